@@ -1,0 +1,226 @@
+"""Plain, slow fp64 CPU oracle for block-sparse long-context decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run this module: only the
+tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no
+code, header, table or helper with the HIP library; the two meet only through the seeded inputs.
+
+What it computes follows the KTransformers long-context sparse-attention article
+("KTransformers 长上下文稀疏注意力实战", lmnt.cn), whose sections are cited per function as
+[KT-LC §n]:
+  * §4.2  the cache is split into Initial (head, always attended), Context (middle, retrieved
+          sparsely) and Local (tail, always attended);
+  * §4.3  Context is cut into fixed-size blocks; each block gets representative ("rep") keys by one of
+          Max (channel-wise max), Mean (channel-wise mean), Quest (channel-wise min and max, two
+          reps), Fix (tokens at a fixed interval) -- Dynamic needs prefill attention scores and is
+          not part of this oracle;
+  * §3.1  Quest's block score: per channel the larger of q*kmax and q*kmin, summed over channels --
+          an upper bound on q.k for every key of the block;
+  * §4.3  other reps are scored by their similarity with the query (the InfLLM equation the article
+          refers to is not printed; reading R7 below);
+  * §4.5  head_select_mode SEPARATE (each KV head selects for itself under GQA) or SHARED (all KV
+          heads select jointly); top ``second_block_count`` blocks are selected;
+  * §4.6  after selection, ordinary attention runs over the retrieved cache; the pseudocode scales
+          logits by 1/sqrt(head_dim).
+
+Readings taken where the pages are silent (each is the spec here):
+  R1  Initial and Local are rounded outward to whole blocks: I_b = B*ceil(I/B),
+      L_loc = max(I_b, B*floor((L-W)/B)); candidates are the full blocks in [I_b, L_loc).
+      If L <= I_b everything is Initial.
+  R3  top-k counts Context blocks only; k_eff = min(k, n_cand) (R4).
+  R5  block scores carry no softmax scale.
+  R7  a multi-rep block (Fix) scores sum over reps of q.rep (parity unpinned by the pages).
+  R8  Fix reps are the block's tokens at offsets r*(B/rep_num), r = 0..rep_num-1.
+  R10 query head j reads KV head j // (Hq/Hkv).
+  R11 SEPARATE group score = sum over the query heads of the group (parity unpinned by the pages).
+  R12 ties in top-k go to the lower block index; the selection is reported in ascending order.
+  R14 attention: softmax of q.k/sqrt(d) over the attended tokens only.
+Pins (tests/test_oracle_pins.py, tests/test_oracle_bruteforce.py): Quest upper-bound invariant in
+exact integer arithmetic; dense/masked attention against torch's scaled_dot_product_attention in
+float64; brute force with Fractions and rank-by-counting top-k on tiny caches; closed forms for Mean
+and Fix; SHARED = sum of SEPARATE; softmax identities.  R7 and R11 stay "parity unpinned" by the
+pages: the readings themselves are what the GPU is held to.
+
+All arithmetic is float64 after an exact widening of the fp16 inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+QUEST, MAX, MEAN, FIX = "quest", "max", "mean", "fix"
+SEPARATE, SHARED = "separate", "shared"
+REP_METHODS = (QUEST, MAX, MEAN, FIX)
+
+
+# ----------------------------------------------------------------------------------------------
+# O1. Regions  [KT-LC §4.2 Initial / Context / Local; §4.3 fixed-size Context blocks]
+# ----------------------------------------------------------------------------------------------
+def regions(L: int, B: int, initial_len: int, local_len: int):
+    """Split a cache of L tokens into Initial / Context candidates / Local (reading R1).
+
+    Returns (init_end, local_start, candidates): Initial = [0, init_end), Local = [local_start, L),
+    candidates = list of logical block ids b whose tokens [b*B, (b+1)*B) form the Context.
+    """
+    I_b = B * math.ceil(initial_len / B)
+    if L <= I_b:
+        return L, L, []
+    L_loc = max(I_b, B * math.floor((L - local_len) / B))
+    return I_b, L_loc, list(range(I_b // B, L_loc // B))
+
+
+# ----------------------------------------------------------------------------------------------
+# O2. Block reps  [KT-LC §4.3 table of rep methods; §3.1 Quest "Reduced Keys"]
+# ----------------------------------------------------------------------------------------------
+def rep_count(method: str, rep_num: int) -> int:
+    """Reps per (block, KV head): Quest keeps a min and a max key (fixed at 2, §4.3), Max and Mean
+    one, Fix ``rep_num``."""
+    if method == QUEST:
+        return 2
+    if method in (MAX, MEAN):
+        return 1
+    if method == FIX:
+        return rep_num
+    raise ValueError(method)
+
+
+def block_reps(K, B: int, method: str, rep_num: int = 1, blocks=None):
+    """Reps of full blocks of one sequence's keys.
+
+    K: [L][Hkv][d] (fp16 or any float), logical token order.
+    blocks: logical block ids to build (default: every full block, b < L // B).
+    Returns float64 array [len(blocks)][Hkv][R][d]; Quest puts the min key at r=0, max key at r=1.
+    """
+    L, Hkv, d = K.shape
+    if blocks is None:
+        blocks = range(L // B)
+    blocks = list(blocks)
+    R = rep_count(method, rep_num)
+    out = np.empty((len(blocks), Hkv, R, d), dtype=np.float64)
+    for i, b in enumerate(blocks):
+        assert (b + 1) * B <= L, "reps are defined for full blocks only"
+        tile = np.asarray(K[b * B:(b + 1) * B], dtype=np.float64)  # [B][Hkv][d]
+        if method == QUEST:
+            out[i, :, 0, :] = tile.min(axis=0)
+            out[i, :, 1, :] = tile.max(axis=0)
+        elif method == MAX:
+            out[i, :, 0, :] = tile.max(axis=0)
+        elif method == MEAN:
+            out[i, :, 0, :] = tile.sum(axis=0) / B
+        elif method == FIX:
+            assert B % rep_num == 0, "Fix needs rep_num | block_size"
+            stride = B // rep_num
+            for r in range(rep_num):
+                out[i, :, r, :] = tile[r * stride]
+        else:
+            raise ValueError(method)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# O3. Per-head block scores  [KT-LC §3.1 Quest bound; §4.3 rep similarity]
+# ----------------------------------------------------------------------------------------------
+def head_scores(q, reps, method: str):
+    """s[i][j] = score of block i for query head j (no softmax scale, reading R5).
+
+    q: [Hq][d]; reps: [nblk][Hkv][R][d] from ``block_reps``.
+    Quest: sum_c max(q_c*kmax_c, q_c*kmin_c).  Max / Mean / Fix: sum_r q.rep_r (R7).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hq, d = q.shape
+    nblk, Hkv, R, _ = reps.shape
+    g = Hq // Hkv
+    s = np.empty((nblk, Hq), dtype=np.float64)
+    for j in range(Hq):
+        h = j // g  # R10: contiguous GQA groups
+        if method == QUEST:
+            kmin, kmax = reps[:, h, 0, :], reps[:, h, 1, :]
+            s[:, j] = np.maximum(q[j] * kmax, q[j] * kmin).sum(axis=1)
+        else:
+            s[:, j] = (reps[:, h, :, :] * q[j]).sum(axis=(1, 2))
+    return s
+
+
+# ----------------------------------------------------------------------------------------------
+# O4. Group scores  [KT-LC §4.5 head_select_mode]
+# ----------------------------------------------------------------------------------------------
+def group_scores(s, Hkv: int, mode: str):
+    """SEPARATE: one score row per KV head, summed over its query heads (R11).
+    SHARED: a single row, summed over all query heads.  Returns [G][nblk]."""
+    nblk, Hq = s.shape
+    g = Hq // Hkv
+    if mode == SEPARATE:
+        return np.stack([s[:, h * g:(h + 1) * g].sum(axis=1) for h in range(Hkv)])
+    if mode == SHARED:
+        return s.sum(axis=1)[None, :]
+    raise ValueError(mode)
+
+
+# ----------------------------------------------------------------------------------------------
+# O5. Top-k  [KT-LC §3.1 "select top-k blocks"; §4.5 second_block_count]
+# ----------------------------------------------------------------------------------------------
+def select_topk(scores_row, cand, k: int):
+    """The k_eff = min(k, len(cand)) best candidates by (score desc, block asc), ascending order."""
+    ranked = sorted(range(len(cand)), key=lambda i: (-scores_row[i], cand[i]))
+    return sorted(cand[i] for i in ranked[:min(k, len(cand))])
+
+
+# ----------------------------------------------------------------------------------------------
+# O6. Exact attention over the retrieved cache  [KT-LC §4.6 attn(query, kvcache_after_retrieval)]
+# ----------------------------------------------------------------------------------------------
+def attended_tokens(L: int, B: int, init_end: int, local_start: int, sel):
+    """Initial tokens, then every token of each selected block, then Local tokens."""
+    toks = list(range(0, min(init_end, L)))
+    for b in sel:
+        toks.extend(range(b * B, (b + 1) * B))
+    toks.extend(range(local_start, L))
+    return toks
+
+
+def attention(q, K, V, tokens_per_head, scale=None):
+    """o_j = softmax_t(q_j.K[t]*scale) @ V[t] over t in tokens_per_head[j]; float64 [Hq][d]."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((Hq, d), dtype=np.float64)
+    for j in range(Hq):
+        h = j // g
+        T = np.asarray(tokens_per_head[j], dtype=np.int64)
+        Kt = np.asarray(K[T, h, :], dtype=np.float64)
+        Vt = np.asarray(V[T, h, :], dtype=np.float64)
+        z = (Kt @ q[j]) * scale
+        w = np.exp(z - z.max())
+        out[j] = (w @ Vt) / w.sum()
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# The whole decode step for one sequence  [KT-LC §4.6: retrieval_kvcache then attn]
+# ----------------------------------------------------------------------------------------------
+def decode_step(q, K, V, *, B, initial_len, local_len, topk, method, rep_num=1,
+                mode=SEPARATE, scale=None, reps=None):
+    """One decode step for one sequence whose cache (current token included) is K, V [L][Hkv][d].
+
+    Returns a dict with regions, candidate ids, reps of the candidates, per-head and group scores,
+    the selection per group (ascending), attended token lists per query head and the fp64 output.
+    ``reps`` may be passed in (from ``block_reps`` over the candidates) to skip rebuilding them.
+    """
+    L, Hkv, d = K.shape
+    Hq = q.shape[0]
+    g = Hq // Hkv
+    init_end, local_start, cand = regions(L, B, initial_len, local_len)
+    if reps is None:
+        reps = block_reps(K, B, method, rep_num, blocks=cand)
+    s = head_scores(q, reps, method) if cand else np.zeros((0, Hq))
+    S = group_scores(s, Hkv, mode) if cand else np.zeros((Hkv if mode == SEPARATE else 1, 0))
+    sel = [select_topk(S[gi], cand, topk) for gi in range(S.shape[0])]
+    toks = []
+    for j in range(Hq):
+        gi = (j // g) if mode == SEPARATE else 0
+        toks.append(attended_tokens(L, B, init_end, local_start, sel[gi]))
+    out = attention(q, K, V, toks, scale)
+    return dict(init_end=init_end, local_start=local_start, cand=cand, reps=reps,
+                head_scores=s, scores=S, sel=sel, tokens=toks, out=out)

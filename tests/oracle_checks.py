@@ -1,0 +1,286 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each ``check_*`` takes the oracle module (so the mutation tests can hand in a deliberately broken
+copy) and raises AssertionError on failure.  What each one rests on:
+  * exact integer arithmetic (every fp16 value is an integer multiple of 2**-24);
+  * torch's scaled_dot_product_attention in float64 (a library routine sharing no code with the oracle);
+  * closed forms and identities of the definitions (Mean linearity, Fix = rows of K, SHARED = sum
+    of SEPARATE, softmax shift invariance, q = 0 gives the mean of V);
+  * hand-worked cases in tests/golden/hand_worked.json;
+  * planted-block recall of the selection.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import kvsynth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def exact_int(x) -> list:
+    """fp16-representable floats -> exact integers in units of 2**-24."""
+    a = np.asarray(x, dtype=np.float64) * (1 << 24)
+    assert np.all(a == np.round(a)), "input is not fp16-representable"
+    return a.astype(np.int64)
+
+
+def small_seq(seed, L=1000, Hq=4, Hkv=2, d=16, B=16, **kw):
+    s = kvsynth.make_sequence(seed, L, Hq, Hkv, d, B, **kw)
+    return s.q.numpy(), s.K.numpy(), s.V.numpy(), s
+
+
+# ------------------------------------------------------------------------------------------ reps
+def check_quest_upper_bound(orc, seeds=(1, 2, 3)):
+    """Quest score >= max_t q.k_t for every block and head, in exact integers (2**-48 units)."""
+    for seed in seeds:
+        q, K, V, _ = small_seq(seed)
+        L, Hkv, d = K.shape
+        B = 16
+        Hq = q.shape[0]
+        g = Hq // Hkv
+        blocks = list(range(L // B))
+        reps = orc.block_reps(K, B, orc.QUEST, blocks=blocks)
+        s = orc.head_scores(q, reps, orc.QUEST)
+        qi = exact_int(q)
+        Ki = exact_int(K)
+        for bi, b in enumerate(blocks):
+            for j in range(Hq):
+                h = j // g
+                dots = [int(np.dot(qi[j].astype(object), Ki[t, h].astype(object)))
+                        for t in range(b * B, (b + 1) * B)]
+                true_max = max(dots) / float(1 << 48)
+                # fp64 rounding of a 16-term sum is far below 1e-9 here
+                assert s[bi, j] >= true_max - 1e-9 * max(1.0, abs(true_max)), (seed, b, j)
+
+
+def check_quest_tight_and_units(orc):
+    """A block whose keys are all equal has Quest score == q.k exactly; a unit query e_c scores
+    kmax_c and -e_c scores -kmin_c (pins channel indexing and which of min/max is which)."""
+    rng = np.random.default_rng(7)
+    B, d, Hkv, Hq = 8, 16, 2, 4
+    g = Hq // Hkv
+    K = np.round(rng.standard_normal((4 * B, Hkv, d)) * 64) / 64  # dyadic: exact everywhere
+    K[B:2 * B] = K[B]                                              # block 1: one repeated row
+    q = np.round(rng.standard_normal((Hq, d)) * 64) / 64
+    reps = orc.block_reps(K, B, orc.QUEST)
+    s = orc.head_scores(q, reps, orc.QUEST)
+    for j in range(Hq):
+        assert s[1, j] == float(np.dot(q[j], K[B, j // g])), j
+    kmax = K.reshape(4, B, Hkv, d).max(axis=1)
+    kmin = K.reshape(4, B, Hkv, d).min(axis=1)
+    for c in range(d):
+        e = np.zeros((Hkv, d))
+        e[:, c] = 1.0
+        se = orc.head_scores(e, reps, orc.QUEST)        # Hq = Hkv: head j reads KV head j
+        assert np.array_equal(se[:, 0], kmax[:, 0, c]) and np.array_equal(se[:, 1], kmax[:, 1, c])
+        sn = orc.head_scores(-e, reps, orc.QUEST)
+        assert np.array_equal(sn[:, 0], -kmin[:, 0, c]) and np.array_equal(sn[:, 1], -kmin[:, 1, c])
+
+
+def check_rep_closed_forms(orc, seed=11):
+    """Mean score = (1/B) sum_t q.k_t (linearity); Quest >= Max-rep score and >= Mean score;
+    kmin <= mean <= kmax; Quest >= every Fix rep's dot; Fix reps are K rows at r*B/rep_num."""
+    q, K, V, _ = small_seq(seed, L=512, Hq=4, Hkv=2, d=16, B=16)
+    B, Hq, Hkv = 16, 4, 2
+    g = Hq // Hkv
+    nb = K.shape[0] // B
+    rq = orc.block_reps(K, B, orc.QUEST)
+    rmax = orc.block_reps(K, B, orc.MAX)
+    rmean = orc.block_reps(K, B, orc.MEAN)
+    rfix = orc.block_reps(K, B, orc.FIX, rep_num=4)
+    sq = orc.head_scores(q, rq, orc.QUEST)
+    smax = orc.head_scores(q, rmax, orc.MAX)
+    smean = orc.head_scores(q, rmean, orc.MEAN)
+    K64 = K.astype(np.float64)
+    q64 = q.astype(np.float64)
+    for b in range(nb):
+        for j in range(Hq):
+            h = j // g
+            direct = sum(float(np.dot(q64[j], K64[t, h])) for t in range(b * B, (b + 1) * B)) / B
+            assert abs(smean[b, j] - direct) <= 1e-12 * max(1.0, abs(direct)), (b, j)
+            assert sq[b, j] >= smax[b, j] - 1e-12 and sq[b, j] >= smean[b, j] - 1e-12
+            for r in range(4):
+                assert np.array_equal(rfix[b, h, r], K64[b * B + r * (B // 4), h])
+                assert sq[b, j] >= float(np.dot(q64[j], rfix[b, h, r])) - 1e-12
+        assert np.all(rq[b, :, 0] <= rmean[b, :, 0] + 1e-15)
+        assert np.all(rmean[b, :, 0] <= rq[b, :, 1] + 1e-15)
+        assert np.array_equal(rmax[b, :, 0], rq[b, :, 1])
+
+
+def check_hand_worked(orc):
+    gd = golden()
+    c = gd["quest_block"]
+    K = np.asarray(c["keys"], dtype=np.float64)[:, None, :]   # [B][Hkv=1][d]
+    q = np.asarray([c["q"]])
+    rq = orc.block_reps(K, c["B"], orc.QUEST)
+    assert np.array_equal(rq[0, 0, 0], c["kmin"]) and np.array_equal(rq[0, 0, 1], c["kmax"])
+    assert np.array_equal(orc.block_reps(K, c["B"], orc.MEAN)[0, 0, 0], c["mean"])
+    assert orc.head_scores(q, rq, orc.QUEST)[0, 0] == c["quest_score"]
+    assert orc.head_scores(q, orc.block_reps(K, 2, orc.MAX), orc.MAX)[0, 0] == c["max_score"]
+    assert orc.head_scores(q, orc.block_reps(K, 2, orc.MEAN), orc.MEAN)[0, 0] == c["mean_score"]
+    assert orc.head_scores(q, orc.block_reps(K, 2, orc.FIX, 1), orc.FIX)[0, 0] == c["fix1_score"]
+    assert orc.head_scores(q, orc.block_reps(K, 2, orc.FIX, 2), orc.FIX)[0, 0] == c["fix2_score"]
+    for key in ("decode_step", "tie"):
+        c = gd[key]
+        K = np.asarray(c["keys"], dtype=np.float64)[:, None, :]
+        V = np.zeros_like(K)
+        q = np.asarray(c["q"], dtype=np.float64)
+        r = orc.decode_step(q, K, V, B=c["B"], initial_len=c["initial_len"],
+                            local_len=c["local_len"], topk=c["topk"], method=orc.QUEST,
+                            mode=orc.SEPARATE)
+        assert r["cand"] == [1, 2]
+        assert np.array_equal(r["scores"][0], c["quest_group_scores"]), (key, r["scores"])
+        assert r["sel"][0] == c["sel"], key
+        if key == "decode_step":
+            assert np.array_equal(r["head_scores"], c["quest_head_scores"])
+            for m, name in ((orc.MAX, "max_group_scores"), (orc.MEAN, "mean_group_scores")):
+                rr = orc.decode_step(q, K, V, B=2, initial_len=2, local_len=2, topk=1, method=m)
+                assert np.array_equal(rr["scores"][0], c[name]), (name, rr["scores"])
+                assert rr["sel"][0] == c["sel"]
+
+
+def check_regions_golden(orc):
+    gd = golden()
+    for c in gd["regions"]["cases"]:
+        ie, ls, cand = orc.regions(c["L"], c["B"], c["I"], c["W"])
+        assert (ie, ls) == (c["init_end"], c["local_start"]), c
+        if "cand" in c:
+            assert cand == c["cand"], c
+        else:
+            assert len(cand) == c["n_cand"] and cand[0] == ie // c["B"], c
+    c = gd["kt_base_config_attended"]
+    ie, ls, cand = orc.regions(c["L"], c["B"], c["I"], c["W"])
+    sel = cand[: c["topk"]]
+    toks = orc.attended_tokens(c["L"], c["B"], ie, ls, sel)
+    assert len(toks) == c["attended_tokens"] == len(set(toks))
+
+
+def check_regions_partition(orc):
+    """Every token is Initial, in exactly one candidate block, or Local; candidates are full
+    blocks; Local holds the partial last block."""
+    for L in (1, 5, 127, 128, 129, 1000, 4096, 5000):
+        for B in (4, 16, 128):
+            for I in (0, 1, 100, 128, 300):
+                for W in (0, 1, 100, 128, 1024):
+                    ie, ls, cand = orc.regions(L, B, I, W)
+                    cover = [0] * L
+                    for t in range(ie):
+                        cover[t] += 1
+                    for b in cand:
+                        assert (b + 1) * B <= L
+                        for t in range(b * B, (b + 1) * B):
+                            cover[t] += 1
+                    for t in range(ls, L):
+                        cover[t] += 1
+                    assert all(c == 1 for c in cover), (L, B, I, W)
+                    assert ie % B == 0 or ie == L
+                    assert ls >= L - W - B + 1 or ls == ie
+                    if L % B and L > ie:
+                        assert ls <= (L // B) * B  # the partial last block is Local
+
+
+# -------------------------------------------------------------------------------------- heads
+def check_shared_is_sum_of_separate(orc, seed=5):
+    q, K, V, _ = small_seq(seed, L=640, Hq=8, Hkv=2, d=16, B=16)
+    for m in orc.REP_METHODS:
+        reps = orc.block_reps(K, 16, m, rep_num=4)
+        s = orc.head_scores(q, reps, m)
+        sep = orc.group_scores(s, 2, orc.SEPARATE)
+        sh = orc.group_scores(s, 2, orc.SHARED)
+        assert sep.shape == (2, 40) and sh.shape == (1, 40)
+        assert np.allclose(sh[0], sep.sum(axis=0), rtol=1e-12, atol=1e-12)
+        # SEPARATE row h only depends on the query heads that read KV head h
+        q2 = q.copy()
+        q2[:4] = 0
+        sep2 = orc.group_scores(orc.head_scores(q2, reps, m), 2, orc.SEPARATE)
+        assert np.array_equal(sep2[1], sep[1]) and np.all(sep2[0] == 0)
+
+
+def check_gqa_mapping_via_sdpa(orc, seed=6):
+    """Dense attention (k >= n_cand) equals torch SDPA with enable_gqa (contiguous head groups)."""
+    for (Hq, Hkv, L) in ((4, 2, 300), (8, 8, 129), (6, 3, 77), (8, 1, 200)):
+        q, K, V, _ = small_seq(seed, L=L, Hq=Hq, Hkv=Hkv, d=16, B=16)
+        r = orc.decode_step(q, K, V, B=16, initial_len=16, local_len=32, topk=10 ** 6,
+                            method=orc.QUEST, mode=orc.SEPARATE)
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q.astype(np.float64))[None, :, None, :],
+            torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2)[None],
+            torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2)[None],
+            enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12), (Hq, Hkv, L)
+
+
+def check_masked_attention_via_sdpa(orc, seed=8):
+    """For an arbitrary selection, O6 equals SDPA with a boolean mask over exactly the attended set."""
+    for mode in (orc.SEPARATE, orc.SHARED):
+        q, K, V, _ = small_seq(seed, L=777, Hq=4, Hkv=2, d=16, B=16)
+        r = orc.decode_step(q, K, V, B=16, initial_len=20, local_len=100, topk=5,
+                            method=orc.MEAN, mode=mode)
+        L = K.shape[0]
+        mask = torch.zeros((1, 4, 1, L), dtype=torch.bool)
+        g = 2
+        for j in range(4):
+            grp = (j // g) if mode == orc.SEPARATE else 0
+            T = list(range(32)) + [t for b in r["sel"][grp] for t in range(16 * b, 16 * b + 16)] \
+                + list(range(r["local_start"], L))
+            mask[0, j, 0, T] = True
+            assert sorted(r["tokens"][j]) == sorted(T)
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q.astype(np.float64))[None, :, None, :],
+            torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2)[None],
+            torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2)[None],
+            attn_mask=mask, enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12), mode
+
+
+def check_softmax_identities(orc, seed=9):
+    """q = 0 -> mean of the attended V rows; L = 1 -> V[0]; K[t] += a*q shifts every logit equally
+    (output unchanged)."""
+    q, K, V, _ = small_seq(seed, L=200, Hq=2, Hkv=1, d=16, B=16)
+    q0 = np.zeros_like(q, dtype=np.float64)
+    r = orc.decode_step(q0, K, V, B=16, initial_len=16, local_len=32, topk=3, method=orc.QUEST)
+    for j in range(2):
+        T = r["tokens"][j]
+        assert np.allclose(r["out"][j], V[T, 0].astype(np.float64).mean(axis=0), atol=1e-13)
+    r1 = orc.decode_step(q, K[:1], V[:1], B=16, initial_len=16, local_len=32, topk=3,
+                         method=orc.QUEST)
+    assert np.array_equal(r1["out"], np.repeat(V[:1, 0].astype(np.float64), 2, axis=0))
+    qs = q[:1].astype(np.float64)
+    Ks = K.astype(np.float64) + 0.75 * qs[0][None, None, :]
+    toks = [list(range(200))]
+    a = orc.attention(qs, K, V, toks)
+    b = orc.attention(qs, Ks, V, toks)
+    assert np.allclose(a, b, atol=1e-12)
+
+
+def check_planted_recall(orc):
+    """Hot blocks planted +2 along the query direction are what the selection picks (c1-like)."""
+    B = 128
+    L, I, W = 8192, 128, 1024
+    for seed in (101, 102):
+        s = kvsynth.make_sequence(seed, L, 8, 8, 128, B, hot_range=(1, 56), n_hot=4)
+        for m in (orc.QUEST, orc.MAX, orc.MEAN):
+            r = orc.decode_step(s.q.numpy(), s.K.numpy(), s.V.numpy(), B=B, initial_len=I,
+                                local_len=W, topk=8, method=m, mode=orc.SEPARATE)
+            for h in range(8):
+                assert set(s.hot[h]) <= set(r["sel"][h]), (seed, m, h)
+
+
+ALL_CHECKS = [
+    check_quest_upper_bound, check_quest_tight_and_units, check_rep_closed_forms,
+    check_hand_worked, check_regions_golden, check_regions_partition,
+    check_shared_is_sum_of_separate, check_gqa_mapping_via_sdpa, check_masked_attention_via_sdpa,
+    check_softmax_identities,
+]

@@ -1,0 +1,133 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle_checks as oc
+from oracle import kvs_oracle as orc
+
+
+@pytest.mark.parametrize("check", oc.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check(orc)
+
+
+def test_planted_recall():
+    oc.check_planted_recall(orc)
+
+
+# ------------------------------------------------------------------------------------------------
+# Mutation tests: plant a plausible mistake in the oracle and show that some pin fails.
+# ------------------------------------------------------------------------------------------------
+def _quest_kmax_only(q, reps, method):
+    s = _orig_head_scores(q, reps, method)
+    if method == orc.QUEST:
+        Hq = q.shape[0]
+        g = Hq // reps.shape[1]
+        for j in range(Hq):
+            s[:, j] = (np.asarray(q[j], np.float64) * reps[:, j // g, 1, :]).sum(axis=1)
+    return s
+
+
+def _quest_min_of_products(q, reps, method):
+    s = _orig_head_scores(q, reps, method)
+    if method == orc.QUEST:
+        Hq = q.shape[0]
+        g = Hq // reps.shape[1]
+        for j in range(Hq):
+            qj = np.asarray(q[j], np.float64)
+            s[:, j] = np.minimum(qj * reps[:, j // g, 1], qj * reps[:, j // g, 0]).sum(axis=1)
+    return s
+
+
+def _dropped_channel(q, reps, method):
+    q = np.array(q, dtype=np.float64)
+    q[:, -1] = 0.0
+    return _orig_head_scores(q, reps, method)
+
+
+def _gqa_modulo(q, reps, method):
+    q = np.asarray(q, dtype=np.float64)
+    Hq, Hkv = q.shape[0], reps.shape[1]
+    s = np.empty((reps.shape[0], Hq))
+    for j in range(Hq):
+        h = j % Hkv  # wrong: interleaved instead of contiguous groups
+        if method == orc.QUEST:
+            s[:, j] = np.maximum(q[j] * reps[:, h, 1], q[j] * reps[:, h, 0]).sum(axis=1)
+        else:
+            s[:, j] = (reps[:, h] * q[j]).sum(axis=(1, 2))
+    return s
+
+
+def _ties_high_index(scores_row, cand, k):
+    ranked = sorted(range(len(cand)), key=lambda i: (-scores_row[i], -cand[i]))
+    return sorted(cand[i] for i in ranked[:min(k, len(cand))])
+
+
+def _local_one_block_short(L, B, initial_len, local_len):
+    ie, ls, cand = _orig_regions(L, B, initial_len, local_len)
+    if cand:
+        return ie, ls + B, cand + [ls // B] if (ls + B) <= L else cand
+    return ie, ls, cand
+
+
+def _attention_no_scale(q, K, V, toks, scale=None):
+    return _orig_attention(q, K, V, toks, scale=1.0)
+
+
+def _mean_wrong_divisor(K, B, method, rep_num=1, blocks=None):
+    r = _orig_block_reps(K, B, method, rep_num, blocks)
+    if method == orc.MEAN:
+        r = r * B / (B - 1)
+    return r
+
+
+def _fix_wrong_offset(K, B, method, rep_num=1, blocks=None):
+    if method != orc.FIX:
+        return _orig_block_reps(K, B, method, rep_num, blocks)
+    L, Hkv, d = K.shape
+    blocks = list(range(L // B)) if blocks is None else list(blocks)
+    stride = B // rep_num
+    out = np.empty((len(blocks), Hkv, rep_num, d))
+    for i, b in enumerate(blocks):
+        for r in range(rep_num):
+            out[i, :, r] = K[b * B + r * stride + stride - 1]
+    return out
+
+
+def _shared_as_mean(s, Hkv, mode):
+    r = _orig_group_scores(s, Hkv, mode)
+    return r / s.shape[1] if mode == orc.SHARED else r
+
+
+_orig_head_scores = orc.head_scores
+_orig_select = orc.select_topk
+_orig_regions = orc.regions
+_orig_attention = orc.attention
+_orig_block_reps = orc.block_reps
+_orig_group_scores = orc.group_scores
+
+MUTANTS = [
+    ("head_scores", _quest_kmax_only),
+    ("head_scores", _quest_min_of_products),
+    ("head_scores", _dropped_channel),
+    ("head_scores", _gqa_modulo),
+    ("select_topk", _ties_high_index),
+    ("regions", _local_one_block_short),
+    ("attention", _attention_no_scale),
+    ("block_reps", _mean_wrong_divisor),
+    ("block_reps", _fix_wrong_offset),
+    ("group_scores", _shared_as_mean),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, mutant):
+    import test_oracle_bruteforce as bf
+    monkeypatch.setattr(orc, name, mutant)
+    failed = []
+    for check in oc.ALL_CHECKS + [bf.check_against_bruteforce]:
+        try:
+            check(orc)
+        except Exception:  # an assertion or a crash both count as caught
+            failed.append(check.__name__)
+    assert failed, f"no pin caught mutant {mutant.__name__}"
