@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Sparse decode benchmark on one MI355X: queries/s and HBM roofline fraction at 128K and 1M tokens.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one pass of the whole hot path -- block scoring, top-k and sparse attention, fused in
+kvs_decode_step -- over one decode token:
+  * 128k-max / 128k-mean: InternLM2.5-7B-shaped layer, 32 query / 8 KV heads, d 128, 131,072 cached
+    tokens, block 128, Max (or Mean) reps, SHARED selection, top-96, Initial 128, Local 4,096;
+    one query = one step of one sequence.  The JSON line's `value` is 128k-max.
+  * 1m: 32 such layers of 1,048,576 tokens each (128 GiB of K/V resident), Quest reps, SEPARATE,
+    top-64; one query = one decode token through all 32 layers (32 kvs_decode_step calls).
+Inputs are seeded synthetic fp16 (kvsynth) and resident in HBM before timing.  To keep repeated
+steps from being served by the 256 MB Infinity Cache, a 128K step cycles through 16 cache replicas
+(8 GiB); a 1M step touches 2.7 GB of distinct memory anyway.  Steps are captured once into a HIP
+graph and replayed; HIP events on the launch stream time exactly K steps.
+
+Roofline: algorithmic bytes per step = q + reps of every candidate block + K and V of every attended
+token of every KV head + out, over the step time, against 8 TB/s.
+cpu_baseline: the fp64 CPU oracle (single thread) on the same inputs, reps prebuilt, timed over a
+bounded number of queries.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+B = 128
+D = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# Workloads
+# ------------------------------------------------------------------------------------------------
+WORKLOADS = {
+    "128k-max": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                     layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002),
+    "128k-mean": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="mean", mode="shared",
+                      layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260012),
+    "1m": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
+               layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003),
+}
+
+
+def regions(L, I, W):
+    ib = B * math.ceil(I / B)
+    if L <= ib:
+        return L, L, 0
+    lloc = max(ib, B * math.floor((L - W) / B))
+    return ib, lloc, (lloc - ib) // B
+
+
+def required_bytes(w):
+    """Algorithmic bytes of one decode step of one layer."""
+    L, Hq, Hkv = w["L"], w["Hq"], w["Hkv"]
+    ie, ls, ncand = regions(L, w["I"], w["W"])
+    k_eff = min(w["k"], ncand)
+    T = min(ie, L) + k_eff * B + (L - ls)
+    R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1)}[w["rep"]]
+    rep_elem = 4 if w["rep"] == "mean" else 2
+    return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * D * 2 * 2,
+                out=Hq * D * 4, tokens=T, ncand=ncand, k_eff=k_eff)
+
+
+class Setup:
+    def __init__(self, name, device):
+        import torch
+
+        import block_sparse_kv_amd as kvs
+        from block_sparse_kv_amd import ops
+        import kvsynth
+
+        w = WORKLOADS[name]
+        self.name, self.w = name, w
+        self.cfg = kvs.Config(num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], initial_len=w["I"],
+                              local_len=w["W"], topk=w["k"], rep_method=w["rep"],
+                              head_select_mode=w["mode"])
+        L = w["L"]
+        nb = math.ceil(L / B)
+        ie, ls, ncand = regions(L, w["I"], w["W"])
+        lo, hi = ie // B, ie // B + ncand
+        self.table = torch.arange(nb, dtype=torch.int32, device=device)[None]
+        self.lens = torch.tensor([L], dtype=torch.int32, device=device)
+        self.units = []  # one per (replica, layer): q, k_pool, v_pool, rep_pool
+        n_units = w["replicas"] * w["layers"]
+        t0 = time.time()
+        for u in range(n_units):
+            q, kp, vp, hot = kvsynth.pool_layer(kvsynth.mix_seed(w["seed"], u), L, w["Hq"], w["Hkv"],
+                                                hot_range=(lo, hi), n_hot=w["n_hot"],
+                                                hot_per_head=w["hot_per_head"], device=device)
+            rp = ops.alloc_rep_pool(self.cfg, nb, device)
+            ops.build_reps(self.cfg, kp, torch.arange(L // B, dtype=torch.int32), rp)
+            self.units.append((q[None].contiguous(), kp, vp, rp))
+        torch.cuda.synchronize()
+        log(f"[setup] {name}: {n_units} cache units of {L} tokens generated in {time.time() - t0:.1f}s")
+        self.out = torch.empty((1, w["Hq"], D), dtype=torch.float32, device=device)
+        self.ws_bytes = kvs.kvs_decode_step_workspace_size(self.cfg, 1, nb)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.sel = torch.empty((1, self.cfg.groups, w["k"]), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((1, self.cfg.groups), dtype=torch.int32, device=device)
+        self.nb = nb
+        self.kvs = kvs
+
+    def step(self, replica):
+        """One decode step (all layers) on cache replica `replica`."""
+        w = self.w
+        for layer in range(w["layers"]):
+            q, kp, vp, rp = self.units[replica * w["layers"] + layer]
+            self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
+                                     self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
+
+
+def time_steps(setup, steps, warmup, use_graph=True):
+    """Returns (seconds for exactly `steps` steps, graph used?)."""
+    import torch
+
+    R = setup.w["replicas"]
+    for i in range(warmup):
+        setup.step(i % R)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            s = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                for r in range(R):
+                    setup.step(r)
+            graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eager launches instead
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graph = None
+    steps = max(R, (steps // R) * R) if graph is not None else steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if graph is not None:
+        for _ in range(steps // R):
+            graph.replay()
+    else:
+        for i in range(steps):
+            setup.step(i % R)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3, steps, graph is not None
+
+
+def copy_bandwidth(device, nbytes=4 << 30):
+    import torch
+
+    a = torch.empty(nbytes // 2, dtype=torch.float16, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    del a, b
+    return 2.0 * nbytes * n / sec / 1e9
+
+
+def cpu_baseline(setup, budget_s=15.0):
+    """The fp64 oracle, one thread, on replica 0 / layer 0 of the same inputs (reps prebuilt)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import kvsynth
+    from oracle import kvs_oracle as orc
+
+    w = setup.w
+    q, kp, vp, _ = setup.units[0]
+    L = w["L"]
+    K = kvsynth.logical_from_pool(kp, setup.table[0].cpu(), L).cpu().numpy()
+    V = kvsynth.logical_from_pool(vp, setup.table[0].cpu(), L).cpu().numpy()
+    qn = q[0].cpu().numpy()
+    ie, ls, cand = orc.regions(L, B, w["I"], w["W"])
+    reps = orc.block_reps(K, B, w["rep"], 1, blocks=cand)
+    n, t0 = 0, time.time()
+    with threadpool_limits(limits=1):
+        while True:
+            orc.decode_step(qn, K, V, B=B, initial_len=w["I"], local_len=w["W"], topk=w["k"],
+                            method=w["rep"], mode=w["mode"], reps=reps)
+            n += 1
+            if time.time() - t0 > budget_s:
+                break
+    sec_per_layer = (time.time() - t0) / n
+    qps = 1.0 / (sec_per_layer * w["layers"])
+    return dict(value=qps, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{n} single-layer decode steps of {setup.name} (replica 0, layer 0), reps "
+                       f"prebuilt, fp64 numpy, 1 thread; queries/s = 1/({w['layers']} x layer time)")
+
+
+def measure(name, steps, warmup, device):
+    import torch
+
+    st = Setup(name, device)
+    sec, steps_done, graphed = time_steps(st, steps, warmup)
+    w = st.w
+    rb = required_bytes(w)
+    per_layer = rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
+    per_step = per_layer * w["layers"]
+    step_s = sec / steps_done
+    gbs = per_step / step_s / 1e9
+    res = dict(workload=name, steps=steps_done, graph=graphed, ms_per_step=step_s * 1e3,
+               queries_per_s=1.0 / step_s, required_bytes_per_step=per_step,
+               required_bytes_per_layer=per_layer, hbm_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
+               attended_tokens=rb["tokens"], candidates=rb["ncand"], k_eff=rb["k_eff"],
+               setup=st)
+    log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
+        f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="all", choices=["all", *WORKLOADS])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the block-sparse decode path is built and timed on a "
+              "single MI355X (sharding is design-only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    copy_gbs = copy_bandwidth(device)
+    log(f"[bench] device copy bandwidth {copy_gbs:.0f} GB/s")
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    results = {}
+    for n in names:
+        st_steps = args.steps if WORKLOADS[n]["layers"] == 1 else max(16, args.steps // 8)
+        results[n] = measure(n, st_steps, args.warmup, device)
+        if n != names[0]:
+            del results[n]["setup"]
+            torch.cuda.empty_cache()
+    head = results[names[0]]
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(head["setup"])
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} queries/s")
+    del head["setup"]
+    w = WORKLOADS[names[0]]
+    line = {
+        "metric": "sparse decode queries/s + achieved HBM GB/s (% roofline) at 128K and 1M ctx",
+        "value": head["queries_per_s"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) fp16 K/V/q with planted hot blocks)",
+        "config": {"workload": names[0], "context": w["L"], "batch": 1, "layers": w["layers"],
+                   "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": D, "block_size": B,
+                   "rep": w["rep"], "head_select_mode": w["mode"], "topk": w["k"],
+                   "initial": w["I"], "local": w["W"], "replicas": w["replicas"]},
+        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": head["frac"],
+                     "traffic": None,
+                     "kernel": "kvs_decode_step (score + top-k + split attention + merge)",
+                     "bytes_per_launch": head["required_bytes_per_layer"]},
+        "cpu_baseline": cpu,
+        "copy_gbs": copy_gbs,
+        "frac_of_copy": head["hbm_gbs"] / copy_gbs,
+        "workloads": {k: {kk: vv for kk, vv in v.items() if kk != "setup"}
+                      for k, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

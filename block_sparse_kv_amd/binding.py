@@ -1,0 +1,188 @@
+"""ctypes binding of libkvs.so: the C entry points under the same names, argument marshalling only.
+
+Tensors are passed as their data pointers, the stream as torch's current HIP stream (or an explicit
+``stream`` handle).  Every computation happens in the library's HIP kernels; nothing here computes.
+A missing library is an ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvs.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m block_sparse_kv_amd.build` "
+                      "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_MISALIGNED, KVS_ERR_WORKSPACE, \
+    KVS_ERR_HIP = 0, -1, -2, -3, -4, -5
+REP_QUEST, REP_MAX, REP_MEAN, REP_FIX = 0, 1, 2, 3
+HEADS_SEPARATE, HEADS_SHARED = 0, 1
+REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FIX}
+MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
+
+EXPORTS = (
+    "kvs_status_string", "kvs_rep_count", "kvs_rep_bytes_per_block", "kvs_build_reps",
+    "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
+    "kvs_decode_step_workspace_size", "kvs_decode_step",
+)
+
+
+class kvs_config(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("initial_len", ctypes.c_int32), ("local_len", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("rep_method", ctypes.c_int32), ("rep_num", ctypes.c_int32),
+        ("head_select_mode", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+@dataclass
+class Config:
+    """Python mirror of kvs_config; rep_method / head_select_mode accept names or codes."""
+    num_q_heads: int
+    num_kv_heads: int
+    initial_len: int
+    local_len: int
+    topk: int
+    rep_method: object = "quest"
+    rep_num: int = 1
+    head_select_mode: object = "separate"
+    head_dim: int = 128
+    block_size: int = 128
+    softmax_scale: float = 0.0
+
+    def c(self) -> kvs_config:
+        rm = REP_NAMES.get(self.rep_method, self.rep_method)
+        hm = MODE_NAMES.get(self.head_select_mode, self.head_select_mode)
+        return kvs_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
+                          self.initial_len, self.local_len, self.topk, int(rm), self.rep_num,
+                          int(hm), float(self.softmax_scale))
+
+    @property
+    def groups(self) -> int:
+        hm = MODE_NAMES.get(self.head_select_mode, self.head_select_mode)
+        return self.num_kv_heads if hm == HEADS_SEPARATE else 1
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_CFG = ctypes.POINTER(kvs_config)
+_lib.kvs_status_string.restype = ctypes.c_char_p
+_lib.kvs_status_string.argtypes = [ctypes.c_int]
+_lib.kvs_rep_count.restype = ctypes.c_int
+_lib.kvs_rep_count.argtypes = [_CFG]
+_lib.kvs_rep_bytes_per_block.restype = _S
+_lib.kvs_rep_bytes_per_block.argtypes = [_CFG]
+_lib.kvs_build_reps.restype = ctypes.c_int
+_lib.kvs_build_reps.argtypes = [_CFG, _P, _P, _I, _P, _P]
+_lib.kvs_score_blocks.restype = ctypes.c_int
+_lib.kvs_score_blocks.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
+_lib.kvs_topk_blocks.restype = ctypes.c_int
+_lib.kvs_topk_blocks.argtypes = [_CFG, _P, _P, _I, _I, _P, _P, _P]
+_lib.kvs_attn_workspace_size.restype = _S
+_lib.kvs_attn_workspace_size.argtypes = [_CFG, _I, _I]
+_lib.kvs_sparse_decode_attn.restype = ctypes.c_int
+_lib.kvs_sparse_decode_attn.argtypes = [_CFG, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
+_lib.kvs_decode_step_workspace_size.restype = _S
+_lib.kvs_decode_step_workspace_size.argtypes = [_CFG, _I, _I]
+_lib.kvs_decode_step.restype = ctypes.c_int
+_lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kvs_status_string(status)} ({status})")
+        self.status = status
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _cfg(cfg):
+    return ctypes.byref(cfg.c() if isinstance(cfg, Config) else cfg)
+
+
+def _check(st: int, where: str) -> int:
+    if st != KVS_OK:
+        raise KvsError(st, where)
+    return st
+
+
+def kvs_status_string(status: int) -> str:
+    return _lib.kvs_status_string(status).decode()
+
+
+def kvs_rep_count(cfg) -> int:
+    return _lib.kvs_rep_count(_cfg(cfg))
+
+
+def kvs_rep_bytes_per_block(cfg) -> int:
+    return _lib.kvs_rep_bytes_per_block(_cfg(cfg))
+
+
+def kvs_build_reps(cfg, k_pool, phys_block_ids, n_blocks, rep_pool, stream=None, check=True):
+    st = _lib.kvs_build_reps(_cfg(cfg), _ptr(k_pool), _ptr(phys_block_ids), n_blocks,
+                             _ptr(rep_pool), _stream(stream))
+    return _check(st, "kvs_build_reps") if check else st
+
+
+def kvs_score_blocks(cfg, q, rep_pool, block_table, max_blocks_per_seq, seq_lens, batch, scores,
+                     stream=None, check=True):
+    st = _lib.kvs_score_blocks(_cfg(cfg), _ptr(q), _ptr(rep_pool), _ptr(block_table),
+                               max_blocks_per_seq, _ptr(seq_lens), batch, _ptr(scores),
+                               _stream(stream))
+    return _check(st, "kvs_score_blocks") if check else st
+
+
+def kvs_topk_blocks(cfg, scores, seq_lens, batch, max_blocks_per_seq, sel, sel_count,
+                    stream=None, check=True):
+    st = _lib.kvs_topk_blocks(_cfg(cfg), _ptr(scores), _ptr(seq_lens), batch,
+                              max_blocks_per_seq, _ptr(sel), _ptr(sel_count), _stream(stream))
+    return _check(st, "kvs_topk_blocks") if check else st
+
+
+def kvs_attn_workspace_size(cfg, batch, max_blocks_per_seq) -> int:
+    return _lib.kvs_attn_workspace_size(_cfg(cfg), batch, max_blocks_per_seq)
+
+
+def kvs_sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+                           batch, sel, sel_count, out, workspace, workspace_bytes, stream=None,
+                           check=True):
+    st = _lib.kvs_sparse_decode_attn(_cfg(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(block_table), max_blocks_per_seq, _ptr(seq_lens), batch,
+                                     _ptr(sel), _ptr(sel_count), _ptr(out), _ptr(workspace),
+                                     workspace_bytes, _stream(stream))
+    return _check(st, "kvs_sparse_decode_attn") if check else st
+
+
+def kvs_decode_step_workspace_size(cfg, batch, max_blocks_per_seq) -> int:
+    return _lib.kvs_decode_step_workspace_size(_cfg(cfg), batch, max_blocks_per_seq)
+
+
+def kvs_decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                    batch, out, sel_out, sel_count_out, workspace, workspace_bytes, stream=None,
+                    check=True):
+    st = _lib.kvs_decode_step(_cfg(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(rep_pool),
+                              _ptr(block_table), max_blocks_per_seq, _ptr(seq_lens), batch,
+                              _ptr(out), _ptr(sel_out), _ptr(sel_count_out), _ptr(workspace),
+                              workspace_bytes, _stream(stream))
+    return _check(st, "kvs_decode_step") if check else st

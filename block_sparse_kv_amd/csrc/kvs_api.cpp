@@ -1,0 +1,228 @@
+// libkvs C ABI: argument validation, workspace sizing and dispatch.  Everything that can be checked
+// on the host is checked before the first HIP call, so a rejected call touches neither the device
+// nor the stream (and works on a machine without a GPU).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+#include "kvs_launch.h"
+
+namespace {
+
+using kvs::Params;
+
+constexpr size_t kAlign = 256;  // sub-buffers of a workspace start on 256-byte boundaries
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2_le16(int x) { return x == 1 || x == 2 || x == 4 || x == 8 || x == 16; }
+
+int rep_count_of(const kvs_config* c) {
+  switch (c->rep_method) {
+    case KVS_REP_QUEST: return 2;
+    case KVS_REP_MAX:
+    case KVS_REP_MEAN: return 1;
+    case KVS_REP_FIX:
+      if (c->rep_num < 1 || c->rep_num > c->block_size || c->block_size % c->rep_num) return -1;
+      return c->rep_num;
+    default: return -1;
+  }
+}
+
+// Validate a config and fill the kernels' Params.
+int make_params(const kvs_config* c, Params* P) {
+  if (!c) return KVS_ERR_INVALID_ARG;
+  if (c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->block_size <= 0)
+    return KVS_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads) return KVS_ERR_INVALID_ARG;
+  if (c->initial_len < 0 || c->local_len < 0 || c->topk < 0) return KVS_ERR_INVALID_ARG;
+  if (c->rep_method < KVS_REP_QUEST || c->rep_method > KVS_REP_FIX) return KVS_ERR_INVALID_ARG;
+  if (c->head_select_mode != KVS_HEADS_SEPARATE && c->head_select_mode != KVS_HEADS_SHARED)
+    return KVS_ERR_INVALID_ARG;
+  if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
+  const int R = rep_count_of(c);
+  if (R < 0) return KVS_ERR_INVALID_ARG;
+  if (c->head_dim != kvs::kDim || c->block_size != kvs::kBlock) return KVS_ERR_UNSUPPORTED;
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (!pow2_le16(c->num_kv_heads) || !(g == 1 || g == 2 || g == 4 || g == 8))
+    return KVS_ERR_UNSUPPORTED;
+  P->Hq = c->num_q_heads;
+  P->Hkv = c->num_kv_heads;
+  P->g = g;
+  P->G = c->head_select_mode == KVS_HEADS_SEPARATE ? c->num_kv_heads : 1;
+  P->initial_len = c->initial_len;
+  P->local_len = c->local_len;
+  P->topk = c->topk;
+  P->method = c->rep_method;
+  P->R = R;
+  P->mode = c->head_select_mode;
+  const float scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf((float)c->head_dim);
+  P->scale_log2 = scale * 1.4426950408889634f;
+  return KVS_OK;
+}
+
+int check_sizes(int32_t batch, int32_t max_blocks) {
+  if (batch <= 0 || max_blocks <= 0) return KVS_ERR_INVALID_ARG;
+  return KVS_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_ERR_HIP; }
+
+struct StepLayout {
+  kvs::AttnPlan plan;
+  size_t scores_off, sel_off, cnt_off, part_o_off, part_ml_off, total;
+};
+
+StepLayout step_layout(const Params& P, int batch, int max_blocks) {
+  StepLayout s;
+  s.plan = kvs::attn_plan(P, batch, max_blocks);
+  size_t off = 0;
+  s.scores_off = off; off += round_up((size_t)batch * P.G * max_blocks * sizeof(float));
+  s.sel_off = off;    off += round_up((size_t)batch * P.G * (P.topk > 0 ? P.topk : 1) * sizeof(int32_t));
+  s.cnt_off = off;    off += round_up((size_t)batch * P.G * sizeof(int32_t));
+  s.part_o_off = off; off += round_up(s.plan.part_o_bytes);
+  s.part_ml_off = off; off += round_up(s.plan.part_ml_bytes);
+  s.total = off;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvs_status_string(int status) {
+  switch (status) {
+    case KVS_OK: return "KVS_OK";
+    case KVS_ERR_INVALID_ARG: return "KVS_ERR_INVALID_ARG: null pointer, negative size or inconsistent shapes";
+    case KVS_ERR_UNSUPPORTED: return "KVS_ERR_UNSUPPORTED: shape outside head_dim=128, block_size=128, Hkv in {1,2,4,8,16}, Hq/Hkv in {1,2,4,8}";
+    case KVS_ERR_MISALIGNED: return "KVS_ERR_MISALIGNED: q, pools and rep_pool need 16-byte alignment, workspace 256-byte";
+    case KVS_ERR_WORKSPACE: return "KVS_ERR_WORKSPACE: workspace null or too small";
+    case KVS_ERR_HIP: return "KVS_ERR_HIP: kernel launch failed";
+    default: return "unknown kvs status";
+  }
+}
+
+int kvs_rep_count(const kvs_config* cfg) {
+  Params P;
+  const int st = make_params(cfg, &P);
+  return st == KVS_OK ? P.R : st;
+}
+
+size_t kvs_rep_bytes_per_block(const kvs_config* cfg) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK) return 0;
+  const size_t elem = P.method == kvs::kMean ? 4 : 2;
+  return (size_t)P.Hkv * P.R * kvs::kDim * elem;
+}
+
+int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
+                   int32_t n_blocks, void* rep_pool, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if (n_blocks < 0) return KVS_ERR_INVALID_ARG;
+  if (n_blocks == 0) return KVS_OK;
+  if (!k_pool || !phys_block_ids || !rep_pool) return KVS_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  return hip_status(kvs::launch_build_reps(P, k_pool, phys_block_ids, n_blocks, cfg->rep_num,
+                                           rep_pool, static_cast<hipStream_t>(stream)));
+}
+
+int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, float* scores, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (!q || !rep_pool || !block_table || !seq_lens || !scores) return KVS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  return hip_status(kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                                      batch, scores, static_cast<hipStream_t>(stream)));
+}
+
+int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* seq_lens,
+                    int32_t batch, int32_t max_blocks_per_seq, int32_t* sel, int32_t* sel_count,
+                    kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (!scores || !seq_lens || !sel_count || (!sel && P.topk > 0)) return KVS_ERR_INVALID_ARG;
+  return hip_status(kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel,
+                                     sel_count, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvs_attn_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
+  const kvs::AttnPlan A = kvs::attn_plan(P, batch, max_blocks_per_seq);
+  return round_up(A.part_o_bytes) + round_up(A.part_ml_bytes);
+}
+
+int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                           const int32_t* sel, const int32_t* sel_count, float* out,
+                           void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_count || !out ||
+      (!sel && P.topk > 0))
+    return KVS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return KVS_ERR_MISALIGNED;
+  const kvs::AttnPlan A = kvs::attn_plan(P, batch, max_blocks_per_seq);
+  const size_t need = round_up(A.part_o_bytes) + round_up(A.part_ml_bytes);
+  if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  char* ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(ws + round_up(A.part_o_bytes));
+  return hip_status(kvs::launch_attn(P, A, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                                     seq_lens, batch, sel, sel_count, out, part_o, part_ml,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
+                                      int32_t max_blocks_per_seq) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
+  return step_layout(P, batch, max_blocks_per_seq).total;
+}
+
+int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                    const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                    int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
+                    kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (!q || !k_pool || !v_pool || !rep_pool || !block_table || !seq_lens || !out)
+    return KVS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
+    return KVS_ERR_MISALIGNED;
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + S.scores_off);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + S.sel_off);
+  int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(ws + S.cnt_off);
+  float* part_o = reinterpret_cast<float*>(ws + S.part_o_off);
+  float* part_ml = reinterpret_cast<float*>(ws + S.part_ml_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                                   batch, scores, s);
+  if (e != hipSuccess) return KVS_ERR_HIP;
+  e = kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel, cnt, s);
+  if (e != hipSuccess) return KVS_ERR_HIP;
+  e = kvs::launch_attn(P, S.plan, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+                       batch, sel, cnt, out, part_o, part_ml, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side helpers shared by the libkvs kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+constexpr int kBlock = 128;  // tokens per KV block
+constexpr int kDim = 128;    // head_dim
+constexpr int kTile = kBlock * kDim;  // fp16 elements in one (block, KV head) tile
+
+enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3 };
+enum Mode { kSeparate = 0, kShared = 1 };
+
+// Launch-time constants of one call (passed by value to every kernel).
+struct Params {
+  int Hq, Hkv, g;       // query heads, KV heads, query heads per KV head
+  int G;                // selection groups: Hkv (SEPARATE) or 1 (SHARED)
+  int initial_len, local_len, topk;
+  int method, R, mode;  // rep method, reps per (block, head), head_select_mode
+  float scale_log2;     // softmax scale * log2(e): logits live in the exp2 domain
+};
+
+// Initial / Context / Local split of a sequence of L tokens, rounded outward to whole blocks:
+// Initial = [0, init_end), candidates = blocks [cand_lo, cand_hi), Local = [local_start, L).
+struct Regions {
+  int init_end, local_start, cand_lo, cand_hi;
+};
+
+__host__ __device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+__host__ __device__ inline Regions regions_of(int L, int initial_len, int local_len) {
+  Regions r;
+  const int ib = ((initial_len + kBlock - 1) / kBlock) * kBlock;
+  if (L <= ib) {
+    r.init_end = L; r.local_start = L; r.cand_lo = 0; r.cand_hi = 0;
+    return r;
+  }
+  const int lloc = max(ib, floor_div(L - local_len, kBlock) * kBlock);
+  r.init_end = ib; r.local_start = lloc; r.cand_lo = ib / kBlock; r.cand_hi = lloc / kBlock;
+  return r;
+}
+
+// Attended tiles of one selection group: nI Initial tiles, then k selected, then nLoc Local tiles.
+struct TileList {
+  int nI, k, nLoc, loc_b0, L;
+  __device__ int count() const { return nI + k + nLoc; }
+};
+
+__device__ inline TileList tiles_of(int L, const Params& P, int k_sel) {
+  const Regions rg = regions_of(L, P.initial_len, P.local_len);
+  TileList t;
+  t.L = L;
+  if (L <= rg.init_end) {  // everything is Initial
+    t.nI = (L + kBlock - 1) / kBlock; t.k = 0; t.nLoc = 0; t.loc_b0 = 0;
+  } else {
+    t.nI = rg.init_end / kBlock;
+    t.k = max(0, min(k_sel, P.topk));  // a selection never names more than topk blocks
+    t.loc_b0 = rg.local_start / kBlock;
+    t.nLoc = (L - rg.local_start + kBlock - 1) / kBlock;
+  }
+  return t;
+}
+
+// ---- wave64 cross-lane helpers (DPP within 16-lane rows) -----------------------------------------
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the total.
+__device__ inline float row_sum16(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror: other quad of the half-row
+  x += dpp_f<0x140>(x);  // row_mirror: other half of the row
+  return x;
+}
+
+__device__ inline float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// ---- fp16 <-> fp32 ----------------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline void unpack8(const uint4& v, float (&f)[8]) {
+  const half8_t h = __builtin_bit_cast(half8_t, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)h[e];
+}
+
+__device__ inline uint16_t f2h_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// 16-byte streaming load (non-temporal hint: K/V tiles are read once per step).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(a - b) that is 0 when a is -inf (an empty stream), never NaN.
+__device__ inline float exp2_diff(float a, float b) { return a == -INFINITY ? 0.f : fast_exp2(a - b); }
+
+}  // namespace kvs

@@ -1,0 +1,100 @@
+// kvs_build_reps kernels: representative keys of full 128-token blocks
+// (KTransformers long-context sparse attention, lmnt.cn, §4.3 rep methods; §3.1 Quest's
+// channel-wise min/max "Reduced Keys").
+//
+// One workgroup (256 lanes) per (listed block, KV head) tile of 128 x 128 fp16 = 32 KiB.  Lane t reads
+// channels 8*(t%16)..+8 of tokens t/16 + 16*i (i = 0..7) with 128-bit loads: each wave-wide load is
+// 4 whole token rows, 1 KiB contiguous.  Per-lane partials are folded across the 4 rows of a wave
+// with lane shuffles and across the 4 waves through LDS.  The kernel streams K once (HBM-bound).
+#include "kvs_device.h"
+#include "kvs_launch.h"
+
+namespace kvs {
+
+template <int METHOD>
+__global__ __launch_bounds__(256) void build_reps_kernel(const uint16_t* __restrict__ k_pool,
+                                                         const int32_t* __restrict__ ids, int Hkv,
+                                                         int rep_num, void* __restrict__ rep_pool) {
+  const int h = blockIdx.y;
+  const size_t p = (size_t)ids[blockIdx.x];
+  const uint16_t* tile = k_pool + (p * Hkv + h) * kTile;
+  const int t = threadIdx.x, c = t & 15, r = t >> 4;
+
+  if constexpr (METHOD == kFix) {  // rows 0, s, 2s, ... copied verbatim
+    const int stride = kBlock / rep_num;
+    uint16_t* out = static_cast<uint16_t*>(rep_pool) + (p * Hkv + h) * (size_t)rep_num * kDim;
+    for (int rr = r; rr < rep_num; rr += 16)
+      *reinterpret_cast<uint4*>(out + rr * kDim + c * 8) =
+          *reinterpret_cast<const uint4*>(tile + (size_t)(rr * stride) * kDim + c * 8);
+    return;
+  } else {
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      raw[i] = ld_stream16(tile + (size_t)(r + 16 * i) * kDim + c * 8);
+    float a[8], b[8];  // Quest: min, max.  Max: -, max.  Mean: sum, -
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { a[e] = METHOD == kMean ? 0.f : INFINITY; b[e] = -INFINITY; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float f[8];
+      unpack8(raw[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (METHOD == kMean) a[e] += f[e];
+        if (METHOD == kQuest) a[e] = fminf(a[e], f[e]);
+        if (METHOD != kMean) b[e] = fmaxf(b[e], f[e]);
+      }
+    }
+    // fold the 4 rows of this wave (lanes l, l^16, l^32, l^48 share the channels)
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = shfl_xor_f(a[e], m), bo = shfl_xor_f(b[e], m);
+        if (METHOD == kMean) a[e] += ao;
+        if (METHOD == kQuest) a[e] = fminf(a[e], ao);
+        if (METHOD != kMean) b[e] = fmaxf(b[e], bo);
+      }
+    }
+    __shared__ float sa[4][kDim], sb[4][kDim];
+    const int w = t >> 6;
+    if ((t & 63) < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sa[w][c * 8 + e] = a[e]; sb[w][c * 8 + e] = b[e]; }
+    }
+    __syncthreads();
+    if (t < kDim) {
+      if constexpr (METHOD == kMean) {
+        const float s = ((sa[0][t] + sa[1][t]) + sa[2][t]) + sa[3][t];
+        float* out = static_cast<float*>(rep_pool) + (p * Hkv + h) * kDim;
+        out[t] = s * (1.0f / kBlock);  // power-of-two scale: exact
+      } else {
+        uint16_t* out = static_cast<uint16_t*>(rep_pool) + (p * Hkv + h) * (size_t)(METHOD == kQuest ? 2 : 1) * kDim;
+        const float mx = fmaxf(fmaxf(sb[0][t], sb[1][t]), fmaxf(sb[2][t], sb[3][t]));
+        if constexpr (METHOD == kQuest) {
+          const float mn = fminf(fminf(sa[0][t], sa[1][t]), fminf(sa[2][t], sa[3][t]));
+          out[t] = f2h_bits(mn);
+          out[kDim + t] = f2h_bits(mx);
+        } else {
+          out[t] = f2h_bits(mx);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
+                             int rep_num, void* rep_pool, hipStream_t s) {
+  const dim3 grid(n, P.Hkv), block(256);
+  const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
+  switch (P.method) {
+    case kQuest: hipLaunchKernelGGL(build_reps_kernel<kQuest>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMax:   hipLaunchKernelGGL(build_reps_kernel<kMax>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMean:  hipLaunchKernelGGL(build_reps_kernel<kMean>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    default:     hipLaunchKernelGGL(build_reps_kernel<kFix>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,71 @@
+"""Torch-facing helpers over the C entry points: allocate outputs and workspaces as torch tensors on
+the inputs' device and call libkvs on torch's current stream.  No arithmetic happens here."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+def _rep_dtype(cfg: B.Config):
+    return torch.float32 if B.REP_NAMES.get(cfg.rep_method, cfg.rep_method) == B.REP_MEAN \
+        else torch.float16
+
+
+def alloc_rep_pool(cfg: B.Config, n_phys: int, device) -> torch.Tensor:
+    """[n_phys][Hkv][R][128] in fp16 (fp32 for Mean)."""
+    R = B.kvs_rep_count(cfg)
+    if R < 0:
+        raise B.KvsError(R, "alloc_rep_pool")
+    return torch.empty((n_phys, cfg.num_kv_heads, R, cfg.head_dim), dtype=_rep_dtype(cfg),
+                       device=device)
+
+
+def build_reps(cfg, k_pool, phys_ids: torch.Tensor, rep_pool: torch.Tensor):
+    ids = phys_ids.to(device=k_pool.device, dtype=torch.int32).contiguous()
+    B.kvs_build_reps(cfg, k_pool, ids, ids.numel(), rep_pool)
+    return rep_pool
+
+
+def score_blocks(cfg, q, rep_pool, block_table, seq_lens):
+    batch, mb = block_table.shape
+    scores = torch.empty((batch, cfg.groups, mb), dtype=torch.float32, device=q.device)
+    B.kvs_score_blocks(cfg, q, rep_pool, block_table, mb, seq_lens, batch, scores)
+    return scores
+
+
+def topk_blocks(cfg, scores, seq_lens):
+    batch, G, mb = scores.shape
+    sel = torch.empty((batch, G, max(cfg.topk, 1)), dtype=torch.int32, device=scores.device)
+    cnt = torch.empty((batch, G), dtype=torch.int32, device=scores.device)
+    B.kvs_topk_blocks(cfg, scores, seq_lens, batch, mb, sel, cnt)
+    return sel[:, :, : cfg.topk], cnt
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, seq_lens, sel, sel_count, ws=None):
+    batch, mb = block_table.shape
+    out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
+    need = B.kvs_attn_workspace_size(cfg, batch, mb)
+    if ws is None:
+        ws = workspace(need, q.device)
+    B.kvs_sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, mb, seq_lens, batch,
+                             sel.contiguous() if cfg.topk > 0 else None, sel_count, out, ws,
+                             ws.numel())
+    return out
+
+
+def decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_lens, ws=None):
+    batch, mb = block_table.shape
+    out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
+    sel = torch.empty((batch, cfg.groups, max(cfg.topk, 1)), dtype=torch.int32, device=q.device)
+    cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=q.device)
+    need = B.kvs_decode_step_workspace_size(cfg, batch, mb)
+    if ws is None:
+        ws = workspace(need, q.device)
+    B.kvs_decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, mb, seq_lens, batch, out,
+                      sel, cnt, ws, ws.numel())
+    return out, sel[:, :, : cfg.topk], cnt

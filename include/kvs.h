@@ -1,0 +1,174 @@
+/*
+ * kvs.h -- block-sparse long-context decode attention over a paged fp16 KV cache, for AMD MI355X
+ * (gfx950).  C ABI of libkvs.so.
+ *
+ * The method is the one the KTransformers long-context sparse-attention article describes
+ * ("KTransformers 长上下文稀疏注意力实战", lmnt.cn; cited below as [KT-LC §n]):
+ *   1. per-block representative keys ("reps") built once per filled block           [§4.3, §3.1]
+ *   2. every Context block scored against the current query                          [§3.1, §4.3]
+ *   3. the top-k Context blocks selected, per KV head or shared by all KV heads      [§4.5]
+ *   4. exact softmax attention over Initial blocks + selected blocks + Local window  [§4.2, §4.6]
+ * Knob names follow the article's configuration list [§4.5] and the operator constructor on
+ * "How to Implement Long Context Inference (Up to 139K Tokens) with KTransformers" (instagit),
+ * step 3: block_size, local_windows_len, topk/second_select_num, anchor_type, anchor_num,
+ * head_select_mode.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns all memory; the library
+ *     never allocates, frees or synchronises, keeps no state between calls and is thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Every argument that can be checked on the host is checked before anything is enqueued; on
+ *     error the call returns a negative status and enqueues nothing.  Contents of device buffers
+ *     (sequence lengths, table entries, selections) are the caller's responsibility: out-of-range
+ *     values there are undefined behaviour.
+ *   - v1 limits: head_dim == 128, block_size == 128, num_kv_heads in {1,2,4,8,16},
+ *     num_q_heads / num_kv_heads in {1,2,4,8}.  Other shapes return KVS_ERR_UNSUPPORTED.
+ *
+ * Layouts (row-major, innermost last)
+ *   q            fp16 [batch][Hq][128]
+ *   out          fp32 [batch][Hq][128]
+ *   k_pool,v_pool fp16 [n_phys][Hkv][128 tokens][128]   one (block, KV head) tile = 32 KiB
+ *   rep_pool     [n_phys][Hkv][R][128]  fp16, except fp32 for KVS_REP_MEAN.
+ *                R = 2 for Quest (r=0 channel-wise min key, r=1 channel-wise max key), 1 for Max
+ *                and Mean, rep_num for Fix (r-th rep = token r*(128/rep_num) of the block).
+ *   block_table  int32 [batch][max_blocks_per_seq]: logical block -> physical block id
+ *   seq_lens     int32 [batch]: cached tokens per sequence, the current token included (>= 1)
+ *   scores       fp32 [batch][G][max_blocks_per_seq], G = Hkv (SEPARATE) or 1 (SHARED);
+ *                -INFINITY at every non-candidate block
+ *   sel          int32 [batch][G][topk]: selected logical block ids in ascending order, -1 padded
+ *   sel_count    int32 [batch][G]
+ *   Query head j reads KV head j / (Hq/Hkv) (contiguous GQA groups).
+ *   q, the pools and rep_pool must be 16-byte aligned (KVS_ERR_MISALIGNED otherwise).
+ *
+ * Regions of a sequence of L tokens (block size B, lengths rounded outward to whole blocks):
+ *   I_b   = B * ceil(initial_len / B)                         Initial = [0, min(I_b, L))
+ *   L_loc = max(I_b, B * floor((L - local_len) / B))          Local   = [L_loc, L)
+ *   candidates = logical blocks b with I_b <= b*B and (b+1)*B <= L_loc; none if L <= I_b.
+ *   k_eff = min(topk, number of candidates).
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* kvs_stream_t; /* hipStream_t */
+
+enum {
+  KVS_OK = 0,
+  KVS_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes     */
+  KVS_ERR_UNSUPPORTED = -2, /* a shape outside the v1 limits above                  */
+  KVS_ERR_MISALIGNED = -3,  /* q / pools / rep_pool not 16-byte aligned             */
+  KVS_ERR_WORKSPACE = -4,   /* workspace null or smaller than the size query        */
+  KVS_ERR_HIP = -5          /* a kernel launch failed                               */
+};
+
+/* Rep methods [KT-LC §4.3]; Dynamic (cumulative prefill attention) is not provided. */
+typedef enum { KVS_REP_QUEST = 0, KVS_REP_MAX = 1, KVS_REP_MEAN = 2, KVS_REP_FIX = 3 } kvs_rep_method;
+
+/* head_select_mode [KT-LC §4.5]: SEPARATE = every KV head selects its own blocks from the scores
+ * of its query heads (summed); SHARED = one selection for all heads from the sum over all
+ * query heads. */
+typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mode;
+
+/* Host struct.  Field order and types are part of the ABI. */
+typedef struct kvs_config {
+  int32_t num_q_heads;      /* Hq                                                           */
+  int32_t num_kv_heads;     /* Hkv, Hq % Hkv == 0                                            */
+  int32_t head_dim;         /* d, must be 128                                                */
+  int32_t block_size;       /* B tokens per block, must be 128 [KT-LC §4.3, §5.1]            */
+  int32_t initial_len;      /* Initial tokens, >= 0 [KT-LC §4.2]                             */
+  int32_t local_len;        /* local_windows_len, >= 0 [KT-LC §4.2, §4.5]                    */
+  int32_t topk;             /* second_block_count: Context blocks selected, >= 0 [KT-LC §4.5] */
+  int32_t rep_method;       /* kvs_rep_method (anchor_type)                                  */
+  int32_t rep_num;          /* anchor_num: Fix only, divides B, 1..B; ignored otherwise      */
+  int32_t head_select_mode; /* kvs_head_select_mode                                          */
+  float softmax_scale;      /* attention logit scale; 0 => 1/sqrt(head_dim) [KT-LC §4.6]     */
+} kvs_config;
+
+/* Human-readable name of a status code (static string). */
+const char* kvs_status_string(int status);
+
+/* Reps per (block, KV head) for this config, or a negative status. */
+int kvs_rep_count(const kvs_config* cfg /* host */);
+
+/* Bytes of one physical block's reps over all KV heads (Hkv * R * 128 * elem), 0 on bad config. */
+size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
+
+/*
+ * kvs_build_reps -- representative keys of full blocks [KT-LC §4.3; Quest's "Reduced Keys" §3.1].
+ * For each of the n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads
+ * the 128x128 key tile and writes its reps into rep_pool at the same physical id:
+ *   Quest: channel-wise min (r=0) and max (r=1);  Max: channel-wise max;
+ *   Mean:  channel-wise mean in fp32;             Fix: rows 0, s, 2s, ... with s = 128/rep_num.
+ * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.
+ */
+int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
+                   int32_t n_blocks, void* rep_pool, kvs_stream_t stream);
+
+/*
+ * kvs_score_blocks -- block relevance [KT-LC §3.1 Quest bound; §4.3 rep similarity; §4.5 modes].
+ * For every candidate block b of every sequence and query head j (KV head h = j/g):
+ *   Quest:        s_j(b) = sum_c max(q_jc * kmax_hbc, q_jc * kmin_hbc)
+ *   Max/Mean/Fix: s_j(b) = sum_r sum_c q_jc * rep_hbrc
+ * (no softmax scale), then SEPARATE: scores[h][b] = sum of s_j over the query heads of h;
+ * SHARED: scores[0][b] = sum over all query heads.  Non-candidates get -INFINITY.
+ * Accumulation is fp32.
+ */
+int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, float* scores, kvs_stream_t stream);
+
+/*
+ * kvs_topk_blocks -- top-k selection [KT-LC §3.1 "top-k blocks"; §4.5 second_block_count].
+ * Per (sequence, group): the k_eff best candidates by score, ties to the lower block index, written
+ * to sel in ascending block order and padded with -1; sel_count = k_eff.  NaN scores are undefined.
+ */
+int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* seq_lens,
+                    int32_t batch, int32_t max_blocks_per_seq, int32_t* sel, int32_t* sel_count,
+                    kvs_stream_t stream);
+
+/* Workspace bytes kvs_sparse_decode_attn needs for these sizes (host query; 0 on bad config). */
+size_t kvs_attn_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq);
+
+/*
+ * kvs_sparse_decode_attn -- exact attention over the retrieved cache [KT-LC §4.2, §4.6].
+ * For query head j of sequence i (group = its KV head in SEPARATE mode, 0 in SHARED):
+ *   T = Initial tokens + every token of the sel_count selected blocks + Local tokens
+ *   out[i][j] = sum_{t in T} softmax_t(scale * q_j . K[t]) V[t], accumulated in fp32.
+ * sel may come from an earlier step (re-selection every token_step tokens / layer_step layers,
+ * [KT-LC §4.6]): Local only grows, so an old selection still names Context blocks.  Selected ids
+ * must be candidates of the current length and distinct.  workspace: device, at least
+ * kvs_attn_workspace_size bytes, 256-byte aligned; its contents are scratch.
+ */
+int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                           const int32_t* sel, const int32_t* sel_count, float* out,
+                           void* workspace, size_t workspace_bytes, kvs_stream_t stream);
+
+/* Workspace bytes kvs_decode_step needs (host query; 0 on bad config). */
+size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
+                                      int32_t max_blocks_per_seq);
+
+/*
+ * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention, enqueued
+ * with no host synchronisation [KT-LC §4.6, retrieval then attention].  Reps must be current for
+ * every candidate block (kvs_build_reps).  sel_out / sel_count_out (nullable) receive the
+ * selection for reuse by later kvs_sparse_decode_attn calls.  workspace as above, at least
+ * kvs_decode_step_workspace_size bytes.
+ */
+int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                    const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                    int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
+                    kvs_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVS_H */

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/kvs.h declares, and
+rejects bad arguments on the host with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_kv_amd as kvs
+from block_sparse_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+ALIGNED = 0x10000        # fake device addresses: never dereferenced, every call below fails first
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    decl = declared_functions()
+    assert len(decl) == 10, decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == decl
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(B.kvs_config) == 44
+    assert B.kvs_config.softmax_scale.offset == 40
+
+
+def cfg(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, initial_len=128, local_len=4096, topk=96,
+                rep_method="quest", head_select_mode="separate")
+    base.update(kw)
+    return kvs.Config(**base)
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert kvs.kvs_status_string(st).startswith("KVS_")
+    assert "unknown" in kvs.kvs_status_string(-99)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_q_heads=0), B.KVS_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), B.KVS_ERR_INVALID_ARG),        # Hq % Hkv
+    (dict(initial_len=-1), B.KVS_ERR_INVALID_ARG),
+    (dict(local_len=-5), B.KVS_ERR_INVALID_ARG),
+    (dict(topk=-1), B.KVS_ERR_INVALID_ARG),
+    (dict(rep_method=7), B.KVS_ERR_INVALID_ARG),
+    (dict(head_select_mode=3), B.KVS_ERR_INVALID_ARG),
+    (dict(rep_method="fix", rep_num=3), B.KVS_ERR_INVALID_ARG),   # must divide 128
+    (dict(rep_method="fix", rep_num=0), B.KVS_ERR_INVALID_ARG),
+    (dict(softmax_scale=-1.0), B.KVS_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), B.KVS_ERR_INVALID_ARG),
+    (dict(head_dim=64), B.KVS_ERR_UNSUPPORTED),
+    (dict(block_size=64), B.KVS_ERR_UNSUPPORTED),
+    (dict(num_q_heads=48, num_kv_heads=3), B.KVS_ERR_UNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=8), B.KVS_ERR_UNSUPPORTED),  # g = 16
+])
+def test_bad_config(kw, expect):
+    c = cfg(**kw)
+    assert kvs.kvs_rep_count(c) == expect
+    assert kvs.kvs_rep_bytes_per_block(c) == 0
+    assert kvs.kvs_attn_workspace_size(c, 1, 10) == 0
+    assert kvs.kvs_decode_step_workspace_size(c, 1, 10) == 0
+    A = ALIGNED
+    assert kvs.kvs_build_reps(c, A, A, 4, A, stream=0, check=False) == expect
+    assert kvs.kvs_score_blocks(c, A, A, A, 10, A, 1, A, stream=0, check=False) == expect
+    assert kvs.kvs_topk_blocks(c, A, A, 1, 10, A, A, stream=0, check=False) == expect
+    assert kvs.kvs_sparse_decode_attn(c, A, A, A, A, 10, A, 1, A, A, A, A, 1 << 30, stream=0,
+                                      check=False) == expect
+    assert kvs.kvs_decode_step(c, A, A, A, A, A, 10, A, 1, A, A, A, A, 1 << 30, stream=0,
+                               check=False) == expect
+
+
+def test_rep_counts_and_bytes():
+    assert kvs.kvs_rep_count(cfg(rep_method="quest")) == 2
+    assert kvs.kvs_rep_count(cfg(rep_method="max")) == 1
+    assert kvs.kvs_rep_count(cfg(rep_method="mean")) == 1
+    assert kvs.kvs_rep_count(cfg(rep_method="fix", rep_num=8)) == 8
+    assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="quest")) == 8 * 2 * 128 * 2
+    assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="mean")) == 8 * 1 * 128 * 4
+    assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="fix", rep_num=8)) == 8 * 8 * 128 * 2
+
+
+def test_null_and_size_errors():
+    c = cfg()
+    A, Z = ALIGNED, None
+    E = B.KVS_ERR_INVALID_ARG
+    assert kvs.kvs_build_reps(c, A, A, -1, A, stream=0, check=False) == E
+    assert kvs.kvs_build_reps(c, Z, A, 3, A, stream=0, check=False) == E
+    assert kvs.kvs_build_reps(c, Z, Z, 0, Z, stream=0, check=False) == B.KVS_OK  # no-op
+    assert kvs.kvs_score_blocks(c, A, A, A, 0, A, 1, A, stream=0, check=False) == E
+    assert kvs.kvs_score_blocks(c, A, A, A, 10, A, 0, A, stream=0, check=False) == E
+    assert kvs.kvs_score_blocks(c, A, Z, A, 10, A, 1, A, stream=0, check=False) == E
+    assert kvs.kvs_topk_blocks(c, A, A, 1, 10, Z, A, stream=0, check=False) == E
+    assert kvs.kvs_sparse_decode_attn(c, A, A, Z, A, 10, A, 1, A, A, A, A, 1 << 30, stream=0,
+                                      check=False) == E
+    assert kvs.kvs_decode_step(c, A, A, A, A, A, 10, A, 1, Z, A, A, A, 1 << 30, stream=0,
+                               check=False) == E
+
+
+def test_alignment_and_workspace_errors():
+    c = cfg()
+    A, M = ALIGNED, MISALIGNED
+    assert kvs.kvs_build_reps(c, M, A, 3, A, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert kvs.kvs_score_blocks(c, M, A, A, 10, A, 1, A, stream=0, check=False) == \
+        B.KVS_ERR_MISALIGNED
+    need = kvs.kvs_attn_workspace_size(c, 2, 1024)
+    assert need > 0 and need % 256 == 0
+    assert kvs.kvs_sparse_decode_attn(c, A, A, A, A, 1024, A, 2, A, A, A, A, need - 1, stream=0,
+                                      check=False) == B.KVS_ERR_WORKSPACE
+    assert kvs.kvs_sparse_decode_attn(c, A, A, A, A, 1024, A, 2, A, A, A, None, need, stream=0,
+                                      check=False) == B.KVS_ERR_WORKSPACE
+    assert kvs.kvs_sparse_decode_attn(c, A, A, A, A, 1024, A, 2, A, A, A, A + 16, need, stream=0,
+                                      check=False) == B.KVS_ERR_MISALIGNED
+    need2 = kvs.kvs_decode_step_workspace_size(c, 2, 1024)
+    assert need2 >= need + 2 * 8 * 1024 * 4
+    assert kvs.kvs_decode_step(c, A, A, A, A, A, 1024, A, 2, A, None, None, A, need2 - 256,
+                               stream=0, check=False) == B.KVS_ERR_WORKSPACE
+    assert kvs.kvs_decode_step(c, A, A, A, M, A, 1024, A, 2, A, None, None, A, need2, stream=0,
+                               check=False) == B.KVS_ERR_MISALIGNED
+
+
+def test_workspace_grows_with_batch():
+    c = cfg()
+    a = kvs.kvs_decode_step_workspace_size(c, 1, 8192)
+    b = kvs.kvs_decode_step_workspace_size(c, 16, 8192)
+    assert 0 < a < b
+
+
+def test_product_path_never_touches_oracle():
+    """Nothing in the package imports or names the oracle; the library has no CPU fallback."""
+    pkg = os.path.join(ROOT, "block_sparse_kv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src, f
+                assert "kvsynth" not in src, f
