@@ -14,8 +14,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvs.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m block_sparse_kv_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built: run `python block_sparse_kv_amd/build.py` "
                       "(or __graft_entry__.build()) first")
+# torch must be loaded first: its bundled HIP runtime has the SONAME libamdhip64.so.7 that libkvs
+# needs, so the loader binds libkvs to that same runtime.  Loading libkvs first would bring in a
+# second HIP runtime, and torch's streams and device memory would mean nothing to it.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_MISALIGNED, KVS_ERR_WORKSPACE, \
@@ -26,7 +31,7 @@ REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FI
 MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
 
 EXPORTS = (
-    "kvs_status_string", "kvs_rep_count", "kvs_rep_bytes_per_block", "kvs_build_reps",
+    "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block", "kvs_build_reps",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step",
 )
@@ -76,6 +81,8 @@ _S = ctypes.c_size_t
 _CFG = ctypes.POINTER(kvs_config)
 _lib.kvs_status_string.restype = ctypes.c_char_p
 _lib.kvs_status_string.argtypes = [ctypes.c_int]
+_lib.kvs_last_error.restype = ctypes.c_char_p
+_lib.kvs_last_error.argtypes = []
 _lib.kvs_rep_count.restype = ctypes.c_int
 _lib.kvs_rep_count.argtypes = [_CFG]
 _lib.kvs_rep_bytes_per_block.restype = _S
@@ -98,7 +105,8 @@ _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _
 
 class KvsError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {kvs_status_string(status)} ({status})")
+        detail = kvs_last_error() if status == KVS_ERR_HIP else ""
+        super().__init__(f"{where}: {kvs_status_string(status)} ({status}) {detail}".rstrip())
         self.status = status
 
 
@@ -129,6 +137,10 @@ def _check(st: int, where: str) -> int:
 
 def kvs_status_string(status: int) -> str:
     return _lib.kvs_status_string(status).decode()
+
+
+def kvs_last_error() -> str:
+    return _lib.kvs_last_error().decode()
 
 
 def kvs_rep_count(cfg) -> int:

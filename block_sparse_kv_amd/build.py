@@ -1,6 +1,6 @@
 """Build libkvs.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_kv_amd.build
+    python block_sparse_kv_amd/build.py
 
 Every .hip / .cpp file under csrc/ goes into one shared library next to this file.  Packed-fp32
 instructions are disabled for the device code (-packed-fp32-ops); the host pass warns that it does

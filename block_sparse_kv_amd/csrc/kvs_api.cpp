@@ -2,6 +2,7 @@
 // on the host is checked before the first HIP call, so a rejected call touches neither the device
 // nor the stream (and works on a machine without a GPU).
 #include <math.h>
+#include <stdio.h>
 #include <stdint.h>
 
 #include "../../include/kvs.h"
@@ -66,7 +67,17 @@ int check_sizes(int32_t batch, int32_t max_blocks) {
   return KVS_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_ERR_HIP; }
+thread_local char g_last_error[512] = "";
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return KVS_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%s)", where, hipGetErrorName(e),
+           hipGetErrorString(e));
+  return KVS_ERR_HIP;
+}
+
+// Clear a launch error left by earlier, unrelated HIP work so it is not reported as ours.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 struct StepLayout {
   kvs::AttnPlan plan;
@@ -89,6 +100,8 @@ StepLayout step_layout(const Params& P, int batch, int max_blocks) {
 }  // namespace
 
 extern "C" {
+
+const char* kvs_last_error(void) { return g_last_error; }
 
 const char* kvs_status_string(int status) {
   switch (status) {
@@ -124,8 +137,10 @@ int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phy
   if (n_blocks == 0) return KVS_OK;
   if (!k_pool || !phys_block_ids || !rep_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
   return hip_status(kvs::launch_build_reps(P, k_pool, phys_block_ids, n_blocks, cfg->rep_num,
-                                           rep_pool, static_cast<hipStream_t>(stream)));
+                                           rep_pool, static_cast<hipStream_t>(stream)),
+                    "kvs_build_reps");
 }
 
 int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,
@@ -137,8 +152,10 @@ int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !rep_pool || !block_table || !seq_lens || !scores) return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
   return hip_status(kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
-                                      batch, scores, static_cast<hipStream_t>(stream)));
+                                      batch, scores, static_cast<hipStream_t>(stream)),
+                    "kvs_score_blocks");
 }
 
 int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* seq_lens,
@@ -149,8 +166,10 @@ int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* s
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!scores || !seq_lens || !sel_count || (!sel && P.topk > 0)) return KVS_ERR_INVALID_ARG;
+  clear_stale_error();
   return hip_status(kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel,
-                                     sel_count, static_cast<hipStream_t>(stream)));
+                                     sel_count, static_cast<hipStream_t>(stream)),
+                    "kvs_topk_blocks");
 }
 
 size_t kvs_attn_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq) {
@@ -180,9 +199,11 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   char* ws = static_cast<char*>(workspace);
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(ws + round_up(A.part_o_bytes));
+  clear_stale_error();
   return hip_status(kvs::launch_attn(P, A, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                                      seq_lens, batch, sel, sel_count, out, part_o, part_ml,
-                                     static_cast<hipStream_t>(stream)));
+                                     static_cast<hipStream_t>(stream)),
+                    "kvs_sparse_decode_attn");
 }
 
 size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
@@ -215,14 +236,15 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
   float* part_o = reinterpret_cast<float*>(ws + S.part_o_off);
   float* part_ml = reinterpret_cast<float*>(ws + S.part_ml_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   hipError_t e = kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
                                    batch, scores, s);
-  if (e != hipSuccess) return KVS_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/score");
   e = kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel, cnt, s);
-  if (e != hipSuccess) return KVS_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/topk");
   e = kvs::launch_attn(P, S.plan, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
                        batch, sel, cnt, out, part_o, part_ml, s);
-  return hip_status(e);
+  return hip_status(e, "kvs_decode_step/attn");
 }
 
 }  // extern "C"

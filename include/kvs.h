@@ -93,6 +93,11 @@ typedef struct kvs_config {
 /* Human-readable name of a status code (static string). */
 const char* kvs_status_string(int status);
 
+/* Detail of the last failed call on the calling thread (for KVS_ERR_HIP: the HIP error name and
+ * message and the launch that failed); "" if no call on this thread has failed.  The string stays
+ * valid until the next failing call on the same thread. */
+const char* kvs_last_error(void);
+
 /* Reps per (block, KV head) for this config, or a negative status. */
 int kvs_rep_count(const kvs_config* cfg /* host */);
 

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 10, decl
+    assert len(decl) == 11, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -147,3 +147,11 @@ def test_product_path_never_touches_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src, f
                 assert "kvsynth" not in src, f
+
+
+def test_one_hip_runtime_in_process():
+    """libkvs is bound to the HIP runtime torch loaded (one runtime per process)."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    hips = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(hips) == 1, hips

