@@ -108,6 +108,7 @@ class Setup:
         self.out = torch.empty((1, w["Hq"], D), dtype=torch.float32, device=device)
         self.ws_bytes = kvs.kvs_decode_step_workspace_size(self.cfg, 1, nb)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        kvs.kvs_decode_step_workspace_init(self.cfg, 1, nb, self.ws, self.ws_bytes)
         self.sel = torch.empty((1, self.cfg.groups, w["k"]), dtype=torch.int32, device=device)
         self.cnt = torch.empty((1, self.cfg.groups), dtype=torch.int32, device=device)
         self.nb = nb
@@ -285,7 +286,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["frac"],
                      "traffic": None,
-                     "kernel": "kvs_decode_step (score + top-k + split attention + merge)",
+                     "kernel": "decode_step_kernel (persistent: score + top-k + attention + merge)",
                      "bytes_per_launch": head["required_bytes_per_layer"]},
         "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,

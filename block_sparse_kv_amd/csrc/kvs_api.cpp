@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <stdint.h>
 
-#include "../../include/kvs.h"
+#include "kvs.h"
 #include "kvs_launch.h"
 
 namespace {
@@ -45,8 +45,7 @@ int make_params(const kvs_config* c, Params* P) {
   if (R < 0) return KVS_ERR_INVALID_ARG;
   if (c->head_dim != kvs::kDim || c->block_size != kvs::kBlock) return KVS_ERR_UNSUPPORTED;
   const int g = c->num_q_heads / c->num_kv_heads;
-  if (!pow2_le16(c->num_kv_heads) || !(g == 1 || g == 2 || g == 4 || g == 8))
-    return KVS_ERR_UNSUPPORTED;
+  if (!pow2_le16(c->num_kv_heads) || !pow2_le16(g)) return KVS_ERR_UNSUPPORTED;
   P->Hq = c->num_q_heads;
   P->Hkv = c->num_kv_heads;
   P->g = g;
@@ -79,23 +78,49 @@ int hip_status(hipError_t e, const char* where) {
 // Clear a launch error left by earlier, unrelated HIP work so it is not reported as ours.
 void clear_stale_error() { (void)hipGetLastError(); }
 
-struct StepLayout {
+// Workspace of the attention: split partials and the tile list.
+struct AttnLayout {
   kvs::AttnPlan plan;
-  size_t scores_off, sel_off, cnt_off, part_o_off, part_ml_off, total;
+  size_t part_o_off, part_ml_off, tiles_off, ntiles_off, total;
 };
 
-StepLayout step_layout(const Params& P, int batch, int max_blocks) {
+AttnLayout attn_layout(const Params& P, int batch, int max_blocks, size_t base = 0) {
+  AttnLayout a;
+  a.plan = kvs::attn_plan(P, batch, max_blocks);
+  size_t off = base;
+  a.part_o_off = off;  off += round_up(a.plan.part_o_bytes);
+  a.part_ml_off = off; off += round_up(a.plan.part_ml_bytes);
+  a.tiles_off = off;   off += round_up(a.plan.tiles_bytes);
+  a.ntiles_off = off;  off += round_up(a.plan.ntiles_bytes);
+  a.total = off;
+  return a;
+}
+
+// Workspace of the fused step: control words first, then scores, selection, selected-tile ids and
+// partials.  Sized for one tile per attention item (the most partials any plan uses).
+struct StepLayout {
+  kvs::StepPlan plan;
+  size_t ctrl_off, scores_off, sel_off, cnt_off, tiles_off, part_o_off, part_ml_off, total;
+};
+
+StepLayout step_layout(const Params& P, int batch, int max_blocks, int resident_wgs) {
   StepLayout s;
-  s.plan = kvs::attn_plan(P, batch, max_blocks);
+  const kvs::StepPlan most = kvs::step_plan(P, batch, max_blocks, 1 << 30);  // tps = 1
+  s.plan = kvs::step_plan(P, batch, max_blocks, resident_wgs);
   size_t off = 0;
+  s.ctrl_off = off;   off += round_up((size_t)most.ctrl_ints * sizeof(int));
   s.scores_off = off; off += round_up((size_t)batch * P.G * max_blocks * sizeof(float));
   s.sel_off = off;    off += round_up((size_t)batch * P.G * (P.topk > 0 ? P.topk : 1) * sizeof(int32_t));
   s.cnt_off = off;    off += round_up((size_t)batch * P.G * sizeof(int32_t));
-  s.part_o_off = off; off += round_up(s.plan.part_o_bytes);
-  s.part_ml_off = off; off += round_up(s.plan.part_ml_bytes);
+  s.tiles_off = off;  off += round_up(most.tiles_bytes);
+  s.part_o_off = off; off += round_up(most.part_o_bytes);
+  s.part_ml_off = off; off += round_up(most.part_ml_bytes);
   s.total = off;
   return s;
 }
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 }  // namespace
 
@@ -107,7 +132,7 @@ const char* kvs_status_string(int status) {
   switch (status) {
     case KVS_OK: return "KVS_OK";
     case KVS_ERR_INVALID_ARG: return "KVS_ERR_INVALID_ARG: null pointer, negative size or inconsistent shapes";
-    case KVS_ERR_UNSUPPORTED: return "KVS_ERR_UNSUPPORTED: shape outside head_dim=128, block_size=128, Hkv in {1,2,4,8,16}, Hq/Hkv in {1,2,4,8}";
+    case KVS_ERR_UNSUPPORTED: return "KVS_ERR_UNSUPPORTED: shape outside head_dim=128, block_size=128, Hkv in {1,2,4,8,16}, Hq/Hkv in {1,2,4,8,16}";
     case KVS_ERR_MISALIGNED: return "KVS_ERR_MISALIGNED: q, pools and rep_pool need 16-byte alignment, workspace 256-byte";
     case KVS_ERR_WORKSPACE: return "KVS_ERR_WORKSPACE: workspace null or too small";
     case KVS_ERR_HIP: return "KVS_ERR_HIP: kernel launch failed";
@@ -175,8 +200,7 @@ int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* s
 size_t kvs_attn_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq) {
   Params P;
   if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
-  const kvs::AttnPlan A = kvs::attn_plan(P, batch, max_blocks_per_seq);
-  return round_up(A.part_o_bytes) + round_up(A.part_ml_bytes);
+  return attn_layout(P, batch, max_blocks_per_seq).total;
 }
 
 int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_pool,
@@ -192,25 +216,40 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
       (!sel && P.topk > 0))
     return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return KVS_ERR_MISALIGNED;
-  const kvs::AttnPlan A = kvs::attn_plan(P, batch, max_blocks_per_seq);
-  const size_t need = round_up(A.part_o_bytes) + round_up(A.part_ml_bytes);
-  if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
+  const AttnLayout A = attn_layout(P, batch, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < A.total) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
-  char* ws = static_cast<char*>(workspace);
-  float* part_o = reinterpret_cast<float*>(ws);
-  float* part_ml = reinterpret_cast<float*>(ws + round_up(A.part_o_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* tiles = at<int32_t>(workspace, A.tiles_off);
+  int32_t* ntiles = at<int32_t>(workspace, A.ntiles_off);
   clear_stale_error();
-  return hip_status(kvs::launch_attn(P, A, q, k_pool, v_pool, block_table, max_blocks_per_seq,
-                                     seq_lens, batch, sel, sel_count, out, part_o, part_ml,
-                                     static_cast<hipStream_t>(stream)),
-                    "kvs_sparse_decode_attn");
+  hipError_t e = kvs::launch_tile_plan(P, A.plan, block_table, max_blocks_per_seq, seq_lens, batch,
+                                       sel, sel_count, tiles, ntiles, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_sparse_decode_attn/plan");
+  e = kvs::launch_attn(P, A.plan, q, k_pool, v_pool, seq_lens, batch, tiles, ntiles, out,
+                       at<float>(workspace, A.part_o_off), at<float>(workspace, A.part_ml_off), s);
+  return hip_status(e, "kvs_sparse_decode_attn");
 }
 
 size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
                                       int32_t max_blocks_per_seq) {
   Params P;
   if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
-  return step_layout(P, batch, max_blocks_per_seq).total;
+  return step_layout(P, batch, max_blocks_per_seq, 1 << 30).total;
+}
+
+int kvs_decode_step_workspace_init(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
+                                   void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq, 1 << 30);
+  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
+  return hip_status(kvs::launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                    "kvs_decode_step_workspace_init");
 }
 
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
@@ -226,25 +265,47 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
     return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
     return KVS_ERR_MISALIGNED;
-  const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
-  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < step_layout(P, batch, max_blocks_per_seq, 1 << 30).total)
+    return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + S.scores_off);
-  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + S.sel_off);
-  int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(ws + S.cnt_off);
-  float* part_o = reinterpret_cast<float*>(ws + S.part_o_off);
-  float* part_ml = reinterpret_cast<float*>(ws + S.part_ml_off);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  hipError_t e = kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
-                                   batch, scores, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/score");
-  e = kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel, cnt, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/topk");
-  e = kvs::launch_attn(P, S.plan, q, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
-                       batch, sel, cnt, out, part_o, part_ml, s);
-  return hip_status(e, "kvs_decode_step/attn");
+  int resident = 0;
+  hipError_t e = kvs::step_resident_wgs(P, &resident);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/occupancy");
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq, resident);
+  const kvs::StepPlan& pl = S.plan;
+  kvs::StepArgs A;
+  A.P = P;
+  A.q = static_cast<const uint16_t*>(q);
+  A.k_pool = static_cast<const uint16_t*>(k_pool);
+  A.v_pool = static_cast<const uint16_t*>(v_pool);
+  A.rep_pool = rep_pool;
+  A.table = block_table;
+  A.seq_lens = seq_lens;
+  A.out = out;
+  A.sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
+  A.sel_count = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
+  A.scores = at<float>(workspace, S.scores_off);
+  A.tiles_sel = at<int32_t>(workspace, S.tiles_off);
+  A.part_o = at<float>(workspace, S.part_o_off);
+  A.part_ml = at<float>(workspace, S.part_ml_off);
+  A.ctrl = at<int>(workspace, S.ctrl_off);
+  A.max_blocks = max_blocks_per_seq;
+  A.batch = batch;
+  A.sb = pl.sb;
+  A.n_score_per_seq = pl.n_score_per_seq;
+  A.tps_il = pl.tps_il;
+  A.n_il_parts = pl.n_il_parts;
+  A.tps_sel = pl.tps_sel;
+  A.n_sel_parts = pl.n_sel_parts;
+  A.n_parts = pl.n_parts;
+  A.off_topk = pl.off_topk;
+  A.off_il = pl.off_il;
+  A.off_sel = pl.off_sel;
+  A.total = pl.total;
+  const int grid = pl.total < resident ? pl.total : resident;
+  e = kvs::launch_step(A, grid, static_cast<hipStream_t>(stream));
+  return hip_status(e, "kvs_decode_step");
 }
 
 }  // extern "C"

@@ -1,0 +1,149 @@
+// Block scoring for one workgroup of 256 lanes (used by kvs_score_blocks and kvs_decode_step).
+// KTransformers long-context sparse attention (lmnt.cn): §3.1 Quest upper bound
+// sum_c max(q_c*kmax_c, q_c*kmin_c); §4.3 similarity of the query with the reps; §4.5 SEPARATE /
+// SHARED head selection.
+//
+// Lane layout: 16 lanes (one DPP row) per (logical block, KV head); lane c owns channels 8c..8c+7 and
+// keeps the matching slice of the g query heads of its KV head in registers.  256 lanes cover
+// 16/Hkv blocks x Hkv heads per pass; up to 4 passes are issued together (table entries first, then
+// all rep loads) so one item pays the memory latency about twice, not once per pass.  Reps are read
+// with 128-bit loads (a 16-lane row reads one 256 B fp16 rep row).  For the linear reps (Max, Mean,
+// Fix) the g query heads are summed first, since sum_j q_j.rep = (sum_j q_j).rep; Quest is per head
+// (the max is not linear).
+#pragma once
+
+#include "kvs_device.h"
+
+namespace kvs {
+
+constexpr int kScorePasses = 4;  // passes whose loads are in flight together
+
+// Scores of logical blocks [b0, b0 + nb) of one sequence (cache length L).  Non-candidates get
+// -INFINITY.  scores_row: SEPARATE -> [Hkv][max_blocks] rows of this sequence, SHARED -> [max_blocks].
+// COH: write the scores with coherent stores (read by another workgroup of the same kernel).
+template <int G, int METHOD, int MODE, bool COH>
+__device__ __forceinline__ void score_blocks_range(const Params& P, const uint16_t* __restrict__ q_seq,
+                                          const void* __restrict__ rep_pool,
+                                          const int32_t* __restrict__ trow, int max_blocks, int L,
+                                          int b0, int nb, float* __restrict__ scores_row,
+                                          float* lds_part /* >= 16 * kScorePasses floats */) {
+  const int Hkv = P.Hkv;
+  const int t = threadIdx.x, c = t & 15;
+  const int h = (t >> 4) % Hkv;
+  const int bpp = 16 / Hkv;  // blocks per pass
+  const int slot = (t >> 4) / Hkv;
+  const Regions rg = regions_of(L, P.initial_len, P.local_len);
+  constexpr int RMAX = METHOD == kQuest ? 2 : (METHOD == kMean ? 2 : 1);  // 16-byte loads per pass
+
+  float qf[G][8];
+  {
+    const uint16_t* qh = q_seq + (size_t)h * G * kDim + c * 8;
+#pragma unroll
+    for (int j = 0; j < G; ++j) unpack8(*reinterpret_cast<const uint4*>(qh + j * kDim), qf[j]);
+  }
+  float qs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    qs[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) qs[e] += qf[j][e];
+  }
+
+  for (int base = b0; base < b0 + nb; base += bpp * kScorePasses) {
+    int blk[kScorePasses];
+    bool inr[kScorePasses], cand[kScorePasses];
+    size_t phys[kScorePasses];
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+      blk[p] = base + p * bpp + slot;
+      inr[p] = blk[p] < b0 + nb && blk[p] < max_blocks;
+      cand[p] = inr[p] && blk[p] >= rg.cand_lo && blk[p] < rg.cand_hi;
+      phys[p] = cand[p] ? (size_t)trow[blk[p]] : 0;
+    }
+    uint4 raw[kScorePasses][RMAX];
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+      if (!cand[p]) continue;
+      if constexpr (METHOD == kQuest) {
+        const uint16_t* rp = static_cast<const uint16_t*>(rep_pool) + (phys[p] * Hkv + h) * 2 * kDim + c * 8;
+        raw[p][0] = ld_stream16(rp);
+        raw[p][1] = ld_stream16(rp + kDim);
+      } else if constexpr (METHOD == kMean) {
+        const float* rp = static_cast<const float*>(rep_pool) + (phys[p] * Hkv + h) * kDim + c * 8;
+        raw[p][0] = ld_stream16(rp);
+        raw[p][RMAX - 1] = ld_stream16(rp + 4);
+      } else {
+        const uint16_t* rp = static_cast<const uint16_t*>(rep_pool) + (phys[p] * Hkv + h) * (size_t)P.R * kDim + c * 8;
+        raw[p][0] = ld_stream16(rp);
+      }
+    }
+    float acc[kScorePasses];
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+      acc[p] = 0.f;
+      if (!cand[p]) continue;
+      if constexpr (METHOD == kQuest) {
+        float kmin[8], kmax[8];
+        unpack8(raw[p][0], kmin);
+        unpack8(raw[p][1], kmax);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[p] += fmaxf(qf[j][e] * kmax[e], qf[j][e] * kmin[e]);
+      } else {
+        float rs[8];
+        if constexpr (METHOD == kMean) {
+          const uint4 x0 = raw[p][0], x1 = raw[p][RMAX - 1];
+          rs[0] = __uint_as_float(x0.x); rs[1] = __uint_as_float(x0.y);
+          rs[2] = __uint_as_float(x0.z); rs[3] = __uint_as_float(x0.w);
+          rs[4] = __uint_as_float(x1.x); rs[5] = __uint_as_float(x1.y);
+          rs[6] = __uint_as_float(x1.z); rs[7] = __uint_as_float(x1.w);
+        } else {
+          unpack8(raw[p][0], rs);
+          const uint16_t* rp = static_cast<const uint16_t*>(rep_pool) + (phys[p] * Hkv + h) * (size_t)P.R * kDim + c * 8;
+          for (int r = 1; r < P.R; ++r) {  // Fix: sum of the rep rows, then one dot
+            float f[8];
+            unpack8(ld_stream16(rp + (size_t)r * kDim), f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rs[e] += f[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[p] += qs[e] * rs[e];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) acc[p] = row_sum16(acc[p]);
+
+    if constexpr (MODE == kSeparate) {
+      if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < kScorePasses; ++p) {
+          if (!inr[p]) continue;
+          float* dst = scores_row + (size_t)h * max_blocks + blk[p];
+          const float v = cand[p] ? acc[p] : -INFINITY;
+          if constexpr (COH) st_coh(dst, v); else *dst = v;
+        }
+      }
+    } else {
+      if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < kScorePasses; ++p) lds_part[p * 16 + slot * Hkv + h] = acc[p];
+      }
+      __syncthreads();
+      if (c == 0 && h == 0) {
+#pragma unroll
+        for (int p = 0; p < kScorePasses; ++p) {
+          if (!inr[p]) continue;
+          float s = 0.f;
+          for (int hh = 0; hh < Hkv; ++hh) s += lds_part[p * 16 + slot * Hkv + hh];
+          const float v = cand[p] ? s : -INFINITY;
+          if constexpr (COH) st_coh(scores_row + blk[p], v); else scores_row[blk[p]] = v;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace kvs

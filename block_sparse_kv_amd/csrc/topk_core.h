@@ -1,0 +1,512 @@
+// Top-k block selection for one (sequence, selection group) by one workgroup of NT lanes
+// (used by kvs_topk_blocks and kvs_decode_step).
+// KTransformers long-context sparse attention (lmnt.cn): §3.1 select the top-k blocks by score;
+// §4.5 second_block_count.  Ties go to the lower block index; the output is in ascending order.
+//
+// Scores become order-preserving 32-bit keys (+0 and -0 share one key).  Finding the k-th largest key
+// T, and how many keys equal to T are still needed, takes two stages:
+//   1. value bins: kBins bins spread linearly over [min, max] of the candidate scores.  The bin index
+//      is a monotone function of the score, so a bin above the boundary bin holds only keys above T.
+//      A histogram (about n/kBins keys per bin, so LDS atomics rarely collide) and a suffix scan find
+//      the bin that holds the k-th largest key.
+//   2. inside that bin: its keys are gathered in LDS.  Up to 64 of them, wave 0 ranks them by
+//      counting (no barriers); a crowded bin (many equal scores) goes through an MSB-first radix select
+//      (4 passes of 8 bits).
+// Each wave then walks a contiguous index segment 64 keys at a time, keeping every key > T and the
+// lowest-indexed keys == T; ballots and popcounts give each kept block its slot, so the selection
+// comes out in ascending block order.
+#pragma once
+
+#include "kvs_device.h"
+
+namespace kvs {
+
+__device__ inline uint32_t order_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (f == 0.f) u = 0u;  // one key for +0 and -0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float key_value(uint32_t u) {
+  return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// A pointer every lane holds the same copy of, made visibly uniform (kept in scalar registers).
+template <typename T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+constexpr int kBins = 1024;     // value bins of stage 1
+constexpr int kSubMax = 1024;   // keys of the boundary bin gathered in LDS for stage 2
+constexpr int kSelLds = 2048;   // selections up to this size are assembled in LDS
+
+// LDS the selection needs besides the staged keys.
+struct TopkLds {
+  int hist[kBins];
+  uint32_t sub[kSubMax];
+  int32_t outsel[kSelLds];
+  int bcast[4];
+  int wgt[16], weq[16];
+  float fmin[16], fmax[16];
+};
+
+// Radix select of the `rem`-th largest among key(i), i < n.  Returns T; `rem` becomes the number of
+// keys equal to T still to take.
+template <int NT, typename KeyFn>
+__device__ inline uint32_t radix_select(KeyFn key, int n, int& rem, TopkLds& S) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = key(i);
+      if ((u & pmask) == prefix) atomicAdd(&S.hist[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {  // lane l owns digits 4l..4l+3; suffix sums from the high digits
+      const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
+                c3 = S.hist[4 * tid + 3];
+      const int own = c0 + c1 + c2 + c3;
+      int suf = own;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_down(suf, d, 64);
+        if (tid + d < 64) suf += y;
+      }
+      const int above_lane = suf - own;  // keys whose digit is above 4*tid+3
+      if (above_lane < rem && suf >= rem) {
+        int digit, above = above_lane;
+        if (above + c3 >= rem) digit = 4 * tid + 3;
+        else if ((above += c3) + c2 >= rem) digit = 4 * tid + 2;
+        else if ((above += c2) + c1 >= rem) digit = 4 * tid + 1;
+        else { above += c1; digit = 4 * tid; }
+        S.bcast[0] = digit;
+        S.bcast[1] = above;
+      }
+    }
+    __syncthreads();
+    rem -= S.bcast[1];
+    prefix |= (uint32_t)S.bcast[0] << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Selects the top k of the n candidate scores row[0..n) (candidate i is logical block cand_lo + i).
+// Writes sel[0..k) ascending; if tiles != nullptr also tiles[i] = trow[sel[i]] (physical ids).
+// IN_LDS: stage the n keys in lkeys (LDS), else read the scores again on every pass.
+// COH: scores were written, and sel / tiles are read, by other workgroups of the same kernel.
+template <int NT, bool COH, bool IN_LDS>
+__device__ __attribute__((noinline)) void topk_select(const float* row, int n, int k, int cand_lo,
+                                                      uint32_t* lkeys, TopkLds& S, int32_t* sel,
+                                                      const int32_t* trow, int32_t* tiles) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  row = uniform_ptr(row);
+  sel = uniform_ptr(sel);
+  trow = uniform_ptr(trow);
+  tiles = uniform_ptr(tiles);
+  n = __builtin_amdgcn_readfirstlane(n);
+  k = __builtin_amdgcn_readfirstlane(k);
+  cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
+  const __amdgpu_buffer_rsrc_t rrow = coh_rsrc(row);
+  auto put = [&](int32_t* p, int32_t v) {
+    if constexpr (COH) st_coh(p, v); else *p = v;
+  };
+  auto score = [&](int i) -> float {
+    if constexpr (COH) return ld_coh_f1(rrow, i * 4); else return row[i];
+  };
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += NT) {
+      put(sel + i, cand_lo + i);
+      if (tiles) put(tiles + i, trow[cand_lo + i]);
+    }
+    return;
+  }
+  if constexpr (IN_LDS) {  // 8 loads in flight per lane
+    for (int base = 0; base < n; base += 8 * NT) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * NT + tid;
+        v[u] = score(i < n ? i : 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * NT + tid;
+        if (i < n) lkeys[i] = order_key(v[u]);
+      }
+    }
+  }
+  auto key = [&](int i) -> uint32_t {
+    if constexpr (IN_LDS) return lkeys[i]; else return order_key(score(i));
+  };
+
+  // ---- stage 1: value bins over [min, max] ----
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = tid; i < n; i += NT) {
+    const float v = key_value(key(i));
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, m, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, m, 64));
+  }
+  if (lane == 0) { S.fmin[wv] = lo; S.fmax[wv] = hi; }
+  for (int i = tid; i < kBins; i += NT) S.hist[i] = 0;
+  __syncthreads();
+  lo = S.fmin[0];
+  hi = S.fmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { lo = fminf(lo, S.fmin[w]); hi = fmaxf(hi, S.fmax[w]); }
+  const float span = hi - lo;
+  const float scale = span > 0.f && span < INFINITY ? (float)kBins / span : 0.f;
+  auto bin_of = [&](uint32_t u) -> int {
+    const float x = (key_value(u) - lo) * scale;  // monotone in the score
+    return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
+  };
+  for (int i = tid; i < n; i += NT) atomicAdd(&S.hist[bin_of(key(i))], 1);
+  __syncthreads();
+  if (tid < 64) {  // boundary bin: lane l sums bins 16l..16l+15, suffix scan across lanes
+    int own = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) own += S.hist[16 * tid + b];
+    int suf = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_down(suf, d, 64);
+      if (tid + d < 64) suf += y;
+    }
+    int above = suf - own;
+    if (above < k && suf >= k) {
+      int b = 16 * tid + 15;
+      for (; b > 16 * tid; --b) {
+        if (above + S.hist[b] >= k) break;
+        above += S.hist[b];
+      }
+      S.bcast[0] = b;          // boundary bin
+      S.bcast[1] = above;      // keys in higher bins (all selected)
+      S.bcast[2] = 0;          // gather cursor of stage 2
+      S.bcast[3] = S.hist[b];  // keys in the boundary bin (hist is reused below)
+    }
+  }
+  __syncthreads();
+  const int bstar = S.bcast[0];
+  int rem = k - S.bcast[1];  // keys still to take from the boundary bin
+  const int m_sub = S.bcast[3];
+
+  // ---- stage 2: exact k-th key inside the boundary bin ----
+  uint32_t T;
+  if (m_sub <= kSubMax) {
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = key(i);
+      if (bin_of(u) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = u;
+    }
+    __syncthreads();
+    if (m_sub <= 64) {  // wave 0 ranks the few keys by counting
+      if (tid < 64) {
+        const uint32_t u = lane < m_sub ? S.sub[lane] : 0u;
+        int gt = 0, ge = 0;
+        for (int x = 0; x < m_sub; ++x) {
+          const uint32_t v = S.sub[x];
+          gt += v > u;
+          ge += v >= u;
+        }
+        const bool is_t = lane < m_sub && gt < rem && ge >= rem;
+        const unsigned long long bm = __ballot(is_t);
+        const int src = __ffsll((long long)bm) - 1;  // some lane holds T (all such lanes agree)
+        const uint32_t t = __shfl(u, src, 64);
+        const int above_t = __shfl(gt, src, 64);
+        if (lane == 0) { S.bcast[2] = (int)t; S.bcast[3] = rem - above_t; }
+      }
+      __syncthreads();
+      T = (uint32_t)S.bcast[2];
+      rem = S.bcast[3];
+    } else {
+      T = radix_select<NT>([&](int i) { return S.sub[i]; }, m_sub, rem, S);
+    }
+  } else {  // a crowded bin: select over all keys of that bin in place
+    T = radix_select<NT>([&](int i) { const uint32_t u = key(i); return bin_of(u) == bstar ? u : 0u; },
+                         n, rem, S);
+  }
+  // T is the k-th largest key; `rem` of the keys equal to T are taken
+
+  // ---- ordered output: wave wv owns the contiguous index segment [s0, s1) ----
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int seg = (n + NW - 1) / NW;
+  const int s0 = min(n, wv * seg), s1 = min(n, s0 + seg);
+  int n_gt = 0, n_eq = 0;
+  for (int base = s0; base < s1; base += 64) {
+    const int i = base + lane;
+    const uint32_t u = i < s1 ? key(i) : 0u;
+    n_gt += __popcll(__ballot(i < s1 && u > T));
+    n_eq += __popcll(__ballot(i < s1 && u == T));
+  }
+  if (lane == 0) { S.wgt[wv] = n_gt; S.weq[wv] = n_eq; }
+  __syncthreads();
+  int eq_before = 0, pos = 0;
+  for (int v = 0; v < wv; ++v) {
+    pos += S.wgt[v] + max(0, min(S.weq[v], rem - eq_before));
+    eq_before += S.weq[v];
+  }
+  const bool in_lds = k <= kSelLds;
+  for (int base = s0; base < s1; base += 64) {
+    const int i = base + lane;
+    const bool in = i < s1;
+    const uint32_t u = in ? key(i) : 0u;
+    const unsigned long long eqm = __ballot(in && u == T);
+    const bool keep = in && (u > T || (u == T && eq_before + __popcll(eqm & lt) < rem));
+    const unsigned long long km = __ballot(keep);
+    if (keep) {
+      const int slot = pos + __popcll(km & lt);
+      if (in_lds) S.outsel[slot] = cand_lo + i;
+      else {
+        put(sel + slot, cand_lo + i);
+        if (tiles) put(tiles + slot, trow[cand_lo + i]);
+      }
+    }
+    pos += __popcll(km);
+    eq_before += __popcll(eqm);
+  }
+  if (in_lds) {
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) {
+      const int b = S.outsel[j];
+      put(sel + j, b);
+      if (tiles) put(tiles + j, trow[b]);
+    }
+  }
+}
+
+
+// Register-resident variant for n <= NT*KPT: lane l of wave w holds the keys of indices
+// w*64*KPT + 64*c + l (c < KPT), so every pass is straight-line code over registers, all the loads of
+// the scores are in flight together, and the ordered output walks a wave's indices in order.
+template <int NT, int KPT, bool COH>
+__device__ __attribute__((noinline)) void topk_select_reg(const float* row, int n, int k, int cand_lo,
+                                                          TopkLds& S, int32_t* sel,
+                                                          const int32_t* trow, int32_t* tiles) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  row = uniform_ptr(row);
+  sel = uniform_ptr(sel);
+  trow = uniform_ptr(trow);
+  tiles = uniform_ptr(tiles);
+  n = __builtin_amdgcn_readfirstlane(n);
+  k = __builtin_amdgcn_readfirstlane(k);
+  cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
+  const __amdgpu_buffer_rsrc_t rrow = coh_rsrc(row);
+  auto put = [&](int32_t* p, int32_t v) {
+    if constexpr (COH) st_coh(p, v); else *p = v;
+  };
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += NT) {
+      put(sel + i, cand_lo + i);
+      if (tiles) put(tiles + i, trow[cand_lo + i]);
+    }
+    return;
+  }
+  const int ibase = wv * 64 * KPT + lane;
+  float v[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const int i = ibase + 64 * c;
+    const int ic = i < n ? i : 0;
+    if constexpr (COH) v[c] = ld_coh_f1(rrow, ic * 4); else v[c] = row[ic];
+  }
+  uint32_t key[KPT];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool ok = ibase + 64 * c < n;
+    key[c] = ok ? order_key(v[c]) : 0u;  // 0 is below every real key
+    const float x = key_value(key[c]);
+    if (ok) { lo = fminf(lo, x); hi = fmaxf(hi, x); }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, m, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, m, 64));
+  }
+  if (lane == 0) { S.fmin[wv] = lo; S.fmax[wv] = hi; }
+  for (int i = tid; i < kBins; i += NT) S.hist[i] = 0;
+  __syncthreads();
+  lo = S.fmin[0];
+  hi = S.fmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { lo = fminf(lo, S.fmin[w]); hi = fmaxf(hi, S.fmax[w]); }
+  const float span = hi - lo;
+  const float scale = span > 0.f && span < INFINITY ? (float)kBins / span : 0.f;
+  auto bin_of = [&](uint32_t u) -> int {
+    const float x = (key_value(u) - lo) * scale;  // monotone in the score
+    return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
+  };
+#pragma unroll
+  for (int c = 0; c < KPT; ++c)
+    if (ibase + 64 * c < n) atomicAdd(&S.hist[bin_of(key[c])], 1);
+  __syncthreads();
+  if (tid < 64) {  // boundary bin: lane l sums bins 16l..16l+15, suffix scan across lanes
+    int own = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) own += S.hist[16 * tid + b];
+    int suf = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_down(suf, d, 64);
+      if (tid + d < 64) suf += y;
+    }
+    int above = suf - own;
+    if (above < k && suf >= k) {
+      int b = 16 * tid + 15;
+      for (; b > 16 * tid; --b) {
+        if (above + S.hist[b] >= k) break;
+        above += S.hist[b];
+      }
+      S.bcast[0] = b;
+      S.bcast[1] = above;
+      S.bcast[2] = 0;
+      S.bcast[3] = S.hist[b];
+    }
+  }
+  __syncthreads();
+  const int bstar = S.bcast[0];
+  int rem = k - S.bcast[1];
+  const int m_sub = S.bcast[3];
+  uint32_t T;
+  if (m_sub <= 64) {  // gather the boundary bin, wave 0 ranks it by counting
+#pragma unroll
+    for (int c = 0; c < KPT; ++c)
+      if (ibase + 64 * c < n && bin_of(key[c]) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = key[c];
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t u = lane < m_sub ? S.sub[lane] : 0u;
+      int gt = 0, ge = 0;
+      for (int x = 0; x < m_sub; ++x) {
+        const uint32_t w2 = S.sub[x];
+        gt += w2 > u;
+        ge += w2 >= u;
+      }
+      const bool is_t = lane < m_sub && gt < rem && ge >= rem;
+      const unsigned long long bm = __ballot(is_t);
+      const int src = __ffsll((long long)bm) - 1;
+      const uint32_t t = __shfl(u, src, 64);
+      const int above_t = __shfl(gt, src, 64);
+      if (lane == 0) { S.bcast[2] = (int)t; S.bcast[3] = rem - above_t; }
+    }
+    __syncthreads();
+    T = (uint32_t)S.bcast[2];
+    rem = S.bcast[3];
+  } else {  // a crowded bin (many equal scores): MSB-first radix select over that bin's keys
+    {
+      uint32_t prefix = 0, pmask = 0;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+          const uint32_t u = key[c];
+          if (ibase + 64 * c < n && bin_of(u) == bstar && (u & pmask) == prefix)
+            atomicAdd(&S.hist[(u >> shift) & 255], 1);
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
+                    c3 = S.hist[4 * tid + 3];
+          const int own = c0 + c1 + c2 + c3;
+          int suf = own;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_down(suf, d, 64);
+            if (tid + d < 64) suf += y;
+          }
+          const int above_lane = suf - own;
+          if (above_lane < rem && suf >= rem) {
+            int digit, above = above_lane;
+            if (above + c3 >= rem) digit = 4 * tid + 3;
+            else if ((above += c3) + c2 >= rem) digit = 4 * tid + 2;
+            else if ((above += c2) + c1 >= rem) digit = 4 * tid + 1;
+            else { above += c1; digit = 4 * tid; }
+            S.bcast[0] = digit;
+            S.bcast[1] = above;
+          }
+        }
+        __syncthreads();
+        rem -= S.bcast[1];
+        prefix |= (uint32_t)S.bcast[0] << shift;
+        pmask |= 255u << shift;
+        __syncthreads();
+      }
+      T = prefix;
+    }
+  }
+  // ordered output over registers
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool ok = ibase + 64 * c < n;
+    n_gt += __popcll(__ballot(ok && key[c] > T));
+    n_eq += __popcll(__ballot(ok && key[c] == T));
+  }
+  if (lane == 0) { S.wgt[wv] = n_gt; S.weq[wv] = n_eq; }
+  __syncthreads();
+  int eq_before = 0, pos = 0;
+  for (int w = 0; w < wv; ++w) {
+    pos += S.wgt[w] + max(0, min(S.weq[w], rem - eq_before));
+    eq_before += S.weq[w];
+  }
+  const bool in_lds = k <= kSelLds;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const int i = ibase + 64 * c;
+    const bool ok = i < n;
+    const unsigned long long eqm = __ballot(ok && key[c] == T);
+    const bool keep = ok && (key[c] > T || (key[c] == T && eq_before + __popcll(eqm & lt) < rem));
+    const unsigned long long km = __ballot(keep);
+    if (keep) {
+      const int slot = pos + __popcll(km & lt);
+      if (in_lds) S.outsel[slot] = cand_lo + i;
+      else {
+        put(sel + slot, cand_lo + i);
+        if (tiles) put(tiles + slot, trow[cand_lo + i]);
+      }
+    }
+    pos += __popcll(km);
+    eq_before += __popcll(eqm);
+  }
+  if (in_lds) {
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) {
+      const int b = S.outsel[j];
+      put(sel + j, b);
+      if (tiles) put(tiles + j, trow[b]);
+    }
+  }
+}
+
+
+// Picks the register-resident variant whenever the candidates fit NT * KMAX keys (KMAX keys per lane),
+// else the LDS-staged (IN_LDS, n <= lds_keys) or re-reading variant.
+template <int NT, int KMAX, bool COH>
+__device__ inline void topk_run(const float* row, int n, int k, int cand_lo, uint32_t* lkeys,
+                                int lds_keys, TopkLds& S, int32_t* sel, const int32_t* trow,
+                                int32_t* tiles) {
+  if (n <= NT * 4) topk_select_reg<NT, 4, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 8 && n <= NT * 8) topk_select_reg<NT, 8, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 16 && n <= NT * 16) topk_select_reg<NT, 16, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 32 && n <= NT * 32) topk_select_reg<NT, 32, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (n <= lds_keys) topk_select<NT, COH, true>(row, n, k, cand_lo, lkeys, S, sel, trow, tiles);
+  else topk_select<NT, COH, false>(row, n, k, cand_lo, nullptr, S, sel, trow, tiles);
+}
+
+}  // namespace kvs

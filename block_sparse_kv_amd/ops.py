@@ -58,14 +58,22 @@ def sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, seq_lens, sel, sel_c
     return out
 
 
+def step_workspace(cfg, batch, max_blocks, device) -> torch.Tensor:
+    """A kvs_decode_step workspace, initialised (its control words zeroed) on the current stream."""
+    need = B.kvs_decode_step_workspace_size(cfg, batch, max_blocks)
+    ws = workspace(need, device)
+    B.kvs_decode_step_workspace_init(cfg, batch, max_blocks, ws, ws.numel())
+    return ws
+
+
 def decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_lens, ws=None):
+    """ws, if given, must come from step_workspace (or have been initialised the same way)."""
     batch, mb = block_table.shape
     out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
     sel = torch.empty((batch, cfg.groups, max(cfg.topk, 1)), dtype=torch.int32, device=q.device)
     cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=q.device)
-    need = B.kvs_decode_step_workspace_size(cfg, batch, mb)
     if ws is None:
-        ws = workspace(need, q.device)
+        ws = step_workspace(cfg, batch, mb, q.device)
     B.kvs_decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, mb, seq_lens, batch, out,
                       sel, cnt, ws, ws.numel())
     return out, sel[:, :, : cfg.topk], cnt

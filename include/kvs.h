@@ -22,7 +22,7 @@
  *     (sequence lengths, table entries, selections) are the caller's responsibility: out-of-range
  *     values there are undefined behaviour.
  *   - v1 limits: head_dim == 128, block_size == 128, num_kv_heads in {1,2,4,8,16},
- *     num_q_heads / num_kv_heads in {1,2,4,8}.  Other shapes return KVS_ERR_UNSUPPORTED.
+ *     num_q_heads / num_kv_heads in {1,2,4,8,16}.  Other shapes return KVS_ERR_UNSUPPORTED.
  *
  * Layouts (row-major, innermost last)
  *   q            fp16 [batch][Hq][128]
@@ -161,11 +161,24 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
                                       int32_t max_blocks_per_seq);
 
 /*
- * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention, enqueued
- * with no host synchronisation [KT-LC §4.6, retrieval then attention].  Reps must be current for
- * every candidate block (kvs_build_reps).  sel_out / sel_count_out (nullable) receive the
- * selection for reuse by later kvs_sparse_decode_attn calls.  workspace as above, at least
- * kvs_decode_step_workspace_size bytes.
+ * kvs_decode_step_workspace_init -- zero a kvs_decode_step workspace (device, the whole
+ * workspace_bytes) on `stream`.  A decode-step workspace holds control words that must be zero when a
+ * call starts; every kvs_decode_step leaves them zero again, so this is needed once after allocation
+ * (a workspace zero-filled by other means is equally valid).
+ */
+int kvs_decode_step_workspace_init(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
+                                   void* workspace, size_t workspace_bytes, kvs_stream_t stream);
+
+/*
+ * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention in a single
+ * persistent kernel, enqueued with no host synchronisation [KT-LC §4.6, retrieval then attention].
+ * Reps must be current for every candidate block (kvs_build_reps).  sel_out / sel_count_out
+ * (nullable) receive the selection for reuse by later kvs_sparse_decode_attn calls.
+ * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned, initialised once by
+ * kvs_decode_step_workspace_init; calls sharing one workspace must not run concurrently (stream order
+ * is enough).  If a dependency wait inside the kernel ever times out (only possible with a workspace
+ * that was not initialised), the kernel still finishes, the results are undefined, and the int at
+ * byte offset 8 of the workspace is non-zero.
  */
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
                     const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,

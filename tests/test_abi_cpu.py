@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 11, decl
+    assert len(decl) == 12, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -64,7 +64,7 @@ def test_status_strings():
     (dict(head_dim=64), B.KVS_ERR_UNSUPPORTED),
     (dict(block_size=64), B.KVS_ERR_UNSUPPORTED),
     (dict(num_q_heads=48, num_kv_heads=3), B.KVS_ERR_UNSUPPORTED),
-    (dict(num_q_heads=128, num_kv_heads=8), B.KVS_ERR_UNSUPPORTED),  # g = 16
+    (dict(num_q_heads=256, num_kv_heads=8), B.KVS_ERR_UNSUPPORTED),  # g = 32
 ])
 def test_bad_config(kw, expect):
     c = cfg(**kw)
