@@ -108,7 +108,6 @@ class Setup:
         self.out = torch.empty((1, w["Hq"], D), dtype=torch.float32, device=device)
         self.ws_bytes = kvs.kvs_decode_step_workspace_size(self.cfg, 1, nb)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
-        kvs.kvs_decode_step_workspace_init(self.cfg, 1, nb, self.ws, self.ws_bytes)
         self.sel = torch.empty((1, self.cfg.groups, w["k"]), dtype=torch.int32, device=device)
         self.cnt = torch.empty((1, self.cfg.groups), dtype=torch.int32, device=device)
         self.nb = nb

@@ -33,7 +33,7 @@ MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
 EXPORTS = (
     "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block", "kvs_build_reps",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
-    "kvs_decode_step_workspace_size", "kvs_decode_step_workspace_init", "kvs_decode_step",
+    "kvs_decode_step_workspace_size", "kvs_decode_step",
 )
 
 
@@ -99,8 +99,6 @@ _lib.kvs_sparse_decode_attn.restype = ctypes.c_int
 _lib.kvs_sparse_decode_attn.argtypes = [_CFG, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
 _lib.kvs_decode_step_workspace_size.restype = _S
 _lib.kvs_decode_step_workspace_size.argtypes = [_CFG, _I, _I]
-_lib.kvs_decode_step_workspace_init.restype = ctypes.c_int
-_lib.kvs_decode_step_workspace_init.argtypes = [_CFG, _I, _I, _P, _S, _P]
 _lib.kvs_decode_step.restype = ctypes.c_int
 _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
 
@@ -190,13 +188,6 @@ def kvs_sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, max_blocks_per_s
 
 def kvs_decode_step_workspace_size(cfg, batch, max_blocks_per_seq) -> int:
     return _lib.kvs_decode_step_workspace_size(_cfg(cfg), batch, max_blocks_per_seq)
-
-
-def kvs_decode_step_workspace_init(cfg, batch, max_blocks_per_seq, workspace, workspace_bytes,
-                                   stream=None, check=True):
-    st = _lib.kvs_decode_step_workspace_init(_cfg(cfg), batch, max_blocks_per_seq, _ptr(workspace),
-                                             workspace_bytes, _stream(stream))
-    return _check(st, "kvs_decode_step_workspace_init") if check else st
 
 
 def kvs_decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq, seq_lens,

@@ -78,49 +78,67 @@ int hip_status(hipError_t e, const char* where) {
 // Clear a launch error left by earlier, unrelated HIP work so it is not reported as ours.
 void clear_stale_error() { (void)hipGetLastError(); }
 
-// Workspace of the attention: split partials and the tile list.
+// Workspace of the attention: the per-tile partials.
 struct AttnLayout {
   kvs::AttnPlan plan;
-  size_t part_o_off, part_ml_off, tiles_off, ntiles_off, total;
+  size_t part_o_off, part_ml_off, total;
 };
 
-AttnLayout attn_layout(const Params& P, int batch, int max_blocks, size_t base = 0) {
+AttnLayout attn_layout(const Params& P, int batch, int max_blocks) {
   AttnLayout a;
   a.plan = kvs::attn_plan(P, batch, max_blocks);
-  size_t off = base;
+  size_t off = 0;
   a.part_o_off = off;  off += round_up(a.plan.part_o_bytes);
   a.part_ml_off = off; off += round_up(a.plan.part_ml_bytes);
-  a.tiles_off = off;   off += round_up(a.plan.tiles_bytes);
-  a.ntiles_off = off;  off += round_up(a.plan.ntiles_bytes);
   a.total = off;
   return a;
 }
 
-// Workspace of the fused step: control words first, then scores, selection, selected-tile ids and
-// partials.  Sized for one tile per attention item (the most partials any plan uses).
+// Workspace of the decode step: scores, the selection (when the caller does not take it), the
+// selected tiles' physical ids, then the attention partials.
 struct StepLayout {
-  kvs::StepPlan plan;
-  size_t ctrl_off, scores_off, sel_off, cnt_off, tiles_off, part_o_off, part_ml_off, total;
+  AttnLayout attn;
+  size_t scores_off, sel_off, cnt_off, tiles_off, attn_off, total;
 };
 
-StepLayout step_layout(const Params& P, int batch, int max_blocks, int resident_wgs) {
+StepLayout step_layout(const Params& P, int batch, int max_blocks) {
   StepLayout s;
-  const kvs::StepPlan most = kvs::step_plan(P, batch, max_blocks, 1 << 30);  // tps = 1
-  s.plan = kvs::step_plan(P, batch, max_blocks, resident_wgs);
+  const size_t nsel = (size_t)batch * P.G * (P.topk > 0 ? P.topk : 1) * sizeof(int32_t);
   size_t off = 0;
-  s.ctrl_off = off;   off += round_up((size_t)most.ctrl_ints * sizeof(int));
   s.scores_off = off; off += round_up((size_t)batch * P.G * max_blocks * sizeof(float));
-  s.sel_off = off;    off += round_up((size_t)batch * P.G * (P.topk > 0 ? P.topk : 1) * sizeof(int32_t));
+  s.sel_off = off;    off += round_up(nsel);
   s.cnt_off = off;    off += round_up((size_t)batch * P.G * sizeof(int32_t));
-  s.tiles_off = off;  off += round_up(most.tiles_bytes);
-  s.part_o_off = off; off += round_up(most.part_o_bytes);
-  s.part_ml_off = off; off += round_up(most.part_ml_bytes);
+  s.tiles_off = off;  off += round_up(nsel);
+  s.attn = attn_layout(P, batch, max_blocks);
+  s.attn_off = off;   off += s.attn.total;
   s.total = off;
   return s;
 }
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+kvs::AttnArgs attn_args(const Params& P, const AttnLayout& L, void* ws, const void* q,
+                        const void* k_pool, const void* v_pool, const int32_t* table, int max_blocks,
+                        const int32_t* seq_lens, const int32_t* sel, const int32_t* sel_count,
+                        float* out) {
+  kvs::AttnArgs a;
+  a.P = P;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.table = table;
+  a.seq_lens = seq_lens;
+  a.sel = sel;
+  a.sel_count = sel_count;
+  a.part_o = at<float>(ws, L.part_o_off);
+  a.part_ml = at<float>(ws, L.part_ml_off);
+  a.out = out;
+  a.max_blocks = max_blocks;
+  a.n_il_max = L.plan.n_il_max;
+  a.max_parts = L.plan.max_parts;
+  return a;
+}
 
 }  // namespace
 
@@ -193,7 +211,7 @@ int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* s
   if (!scores || !seq_lens || !sel_count || (!sel && P.topk > 0)) return KVS_ERR_INVALID_ARG;
   clear_stale_error();
   return hip_status(kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel,
-                                     sel_count, static_cast<hipStream_t>(stream)),
+                                     sel_count, nullptr, nullptr, static_cast<hipStream_t>(stream)),
                     "kvs_topk_blocks");
 }
 
@@ -219,37 +237,20 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   const AttnLayout A = attn_layout(P, batch, max_blocks_per_seq);
   if (!workspace || workspace_bytes < A.total) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  kvs::AttnArgs a = attn_args(P, A, workspace, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                              seq_lens, sel, sel_count, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* tiles = at<int32_t>(workspace, A.tiles_off);
-  int32_t* ntiles = at<int32_t>(workspace, A.ntiles_off);
   clear_stale_error();
-  hipError_t e = kvs::launch_tile_plan(P, A.plan, block_table, max_blocks_per_seq, seq_lens, batch,
-                                       sel, sel_count, tiles, ntiles, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_sparse_decode_attn/plan");
-  e = kvs::launch_attn(P, A.plan, q, k_pool, v_pool, seq_lens, batch, tiles, ntiles, out,
-                       at<float>(workspace, A.part_o_off), at<float>(workspace, A.part_ml_off), s);
-  return hip_status(e, "kvs_sparse_decode_attn");
+  hipError_t e = kvs::launch_attn_tiles(a, batch, true, false, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_sparse_decode_attn/tiles");
+  return hip_status(kvs::launch_merge(a, batch, s), "kvs_sparse_decode_attn/merge");
 }
 
 size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
                                       int32_t max_blocks_per_seq) {
   Params P;
   if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
-  return step_layout(P, batch, max_blocks_per_seq, 1 << 30).total;
-}
-
-int kvs_decode_step_workspace_init(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
-                                   void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
-  Params P;
-  int st = make_params(cfg, &P);
-  if (st != KVS_OK) return st;
-  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
-  const StepLayout S = step_layout(P, batch, max_blocks_per_seq, 1 << 30);
-  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
-  clear_stale_error();
-  return hip_status(kvs::launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
-                    "kvs_decode_step_workspace_init");
+  return step_layout(P, batch, max_blocks_per_seq).total;
 }
 
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
@@ -265,47 +266,26 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
     return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
     return KVS_ERR_MISALIGNED;
-  if (!workspace || workspace_bytes < step_layout(P, batch, max_blocks_per_seq, 1 << 30).total)
-    return KVS_ERR_WORKSPACE;
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
+  int32_t* cnt = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
+  int32_t* tiles = at<int32_t>(workspace, S.tiles_off);
+  float* scores = at<float>(workspace, S.scores_off);
+  void* aws = static_cast<char*>(workspace) + S.attn_off;
+  kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                              seq_lens, tiles, cnt, out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  int resident = 0;
-  hipError_t e = kvs::step_resident_wgs(P, &resident);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/occupancy");
-  const StepLayout S = step_layout(P, batch, max_blocks_per_seq, resident);
-  const kvs::StepPlan& pl = S.plan;
-  kvs::StepArgs A;
-  A.P = P;
-  A.q = static_cast<const uint16_t*>(q);
-  A.k_pool = static_cast<const uint16_t*>(k_pool);
-  A.v_pool = static_cast<const uint16_t*>(v_pool);
-  A.rep_pool = rep_pool;
-  A.table = block_table;
-  A.seq_lens = seq_lens;
-  A.out = out;
-  A.sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
-  A.sel_count = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
-  A.scores = at<float>(workspace, S.scores_off);
-  A.tiles_sel = at<int32_t>(workspace, S.tiles_off);
-  A.part_o = at<float>(workspace, S.part_o_off);
-  A.part_ml = at<float>(workspace, S.part_ml_off);
-  A.ctrl = at<int>(workspace, S.ctrl_off);
-  A.max_blocks = max_blocks_per_seq;
-  A.batch = batch;
-  A.sb = pl.sb;
-  A.n_score_per_seq = pl.n_score_per_seq;
-  A.tps_il = pl.tps_il;
-  A.n_il_parts = pl.n_il_parts;
-  A.tps_sel = pl.tps_sel;
-  A.n_sel_parts = pl.n_sel_parts;
-  A.n_parts = pl.n_parts;
-  A.off_topk = pl.off_topk;
-  A.off_il = pl.off_il;
-  A.off_sel = pl.off_sel;
-  A.total = pl.total;
-  const int grid = pl.total < resident ? pl.total : resident;
-  e = kvs::launch_step(A, grid, static_cast<hipStream_t>(stream));
-  return hip_status(e, "kvs_decode_step");
+  hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/score");
+  e = kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel, cnt, block_table,
+                       P.topk > 0 ? tiles : nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/topk");
+  e = kvs::launch_attn_tiles(a, batch, false, true, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/attention");
+  return hip_status(kvs::launch_merge(a, batch, s), "kvs_decode_step/merge");
 }
 
 }  // extern "C"

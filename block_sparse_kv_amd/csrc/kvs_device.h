@@ -63,6 +63,29 @@ __device__ inline TileList tiles_of(int L, const Params& P, int k_sel) {
   return t;
 }
 
+// Logical block and token count of the t-th Initial/Local tile (t < nI + nLoc).
+__device__ inline int2 il_tile(const TileList& tl, int t) {
+  const int lb = t < tl.nI ? t : tl.loc_b0 + (t - tl.nI);
+  return make_int2(lb, min(kBlock, tl.L - lb * kBlock));
+}
+
+// Arguments of the attention kernels.  Partials: per (sequence, query head) up to max_parts of them;
+// the Initial/Local tiles of a sequence are parts [0, n_il), its selected tiles parts [n_il, n_il + k).
+struct AttnArgs {
+  Params P;
+  const uint16_t* q;         // [batch][Hq][128]
+  const uint16_t* k_pool;    // [n_phys][Hkv][128][128]
+  const uint16_t* v_pool;
+  const int32_t* table;      // [batch][max_blocks]
+  const int32_t* seq_lens;   // [batch]
+  const int32_t* sel;        // [batch][G][topk]: logical ids, or physical ids (sel_phys)
+  const int32_t* sel_count;  // [batch][G]
+  float* part_o;             // [batch][Hq][max_parts][128]
+  float* part_ml;            // [batch][Hq][max_parts][2]
+  float* out;                // [batch][Hq][128]
+  int max_blocks, n_il_max, max_parts;
+};
+
 // ---- wave64 cross-lane helpers (DPP within 16-lane rows) -----------------------------------------
 template <int CTRL>
 __device__ inline float dpp_f(float x) {
@@ -101,38 +124,6 @@ __device__ inline uint4 ld_stream16(const void* p) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Coherent transfer between workgroups of one kernel.  Relaxed device-scope atomic stores and loads
-// bypass the per-XCD L2's non-coherent copies (sc1), so data written this way by one workgroup is seen
-// by another once the writer's stores have completed (vmcnt 0) and a counter says so -- no L2
-// write-back or invalidate of the whole cache is needed.
-template <typename T>
-__device__ inline void st_coh(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline T ld_coh(const T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// Bulk coherent loads/stores: plain (non-atomic) buffer accesses carrying the same sc1 cache policy,
-// so the compiler may keep many of them in flight (it orders atomic loads one by one).
-typedef unsigned int gv2u_t __attribute__((vector_size(8)));
-typedef unsigned int gv4u_t __attribute__((vector_size(16)));
-constexpr int kSc1 = 16;  // cache-policy operand: sc1
-__device__ inline __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
-}
-__device__ inline float ld_coh_f1(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSc1));
-}
-__device__ inline float2 ld_coh_f2(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kSc1));
-}
-__device__ inline void st_coh_f2(__amdgpu_buffer_rsrc_t r, int byte_off, float2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(gv2u_t, v), r, byte_off, 0, kSc1);
-}
-__device__ inline void st_coh_f4(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(gv4u_t, v), r, byte_off, 0, kSc1);
-}
-
-// Wait until this wave's memory operations have completed (vmcnt 0).
-__device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // exp2(a - b) that is 0 when a is -inf (an empty stream), never NaN.
 __device__ inline float exp2_diff(float a, float b) { return a == -INFINITY ? 0.f : fast_exp2(a - b); }

@@ -1,5 +1,5 @@
-// kvs_score_blocks kernel: one workgroup per (chunk of 16/Hkv blocks, sequence); the scoring itself
-// is score_blocks_range (score_core.h).
+// kvs_score_blocks kernel: one workgroup per (chunk of score_blocks_per_wg blocks, sequence); the
+// scoring itself is score_blocks_range (score_core.h).
 #include "kvs_launch.h"
 #include "score_core.h"
 
@@ -13,10 +13,10 @@ __global__ __launch_bounds__(256) void score_kernel(Params P, const uint16_t* __
                                                     float* __restrict__ scores) {
   __shared__ float part[16 * kScorePasses];
   const int seq = blockIdx.y;
-  const int bpp = 16 / P.Hkv;
-  score_blocks_range<G, METHOD, MODE, false>(P, q + (size_t)seq * P.Hq * kDim, rep_pool,
+  const int sb = score_blocks_per_wg(P);
+  score_blocks_range<G, METHOD, MODE>(P, q + (size_t)seq * P.Hq * kDim, rep_pool,
                                       table + (size_t)seq * max_blocks, max_blocks, seq_lens[seq],
-                                      blockIdx.x * bpp, bpp, scores + (size_t)seq * P.G * max_blocks,
+                                      blockIdx.x * sb, sb, scores + (size_t)seq * P.G * max_blocks,
                                       part);
 }
 
@@ -45,8 +45,8 @@ static void launch_score_g(const Params& P, dim3 grid, hipStream_t s, const uint
 hipError_t launch_score(const Params& P, const void* q, const void* rep_pool,
                         const int32_t* table, int max_blocks, const int32_t* seq_lens, int batch,
                         float* scores, hipStream_t s) {
-  const int bpp = 16 / P.Hkv;
-  const dim3 grid((max_blocks + bpp - 1) / bpp, batch);
+  const int sb = score_blocks_per_wg(P);
+  const dim3 grid((max_blocks + sb - 1) / sb, batch);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   switch (P.g) {
     case 1: launch_score_g<1>(P, grid, s, qq, rep_pool, table, max_blocks, seq_lens, scores); break;

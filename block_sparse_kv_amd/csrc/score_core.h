@@ -18,10 +18,12 @@ namespace kvs {
 
 constexpr int kScorePasses = 4;  // passes whose loads are in flight together
 
+// Blocks one scoring workgroup covers: kScorePasses passes of 16/Hkv blocks.
+__host__ __device__ inline int score_blocks_per_wg(const Params& P) { return (16 / P.Hkv) * kScorePasses; }
+
 // Scores of logical blocks [b0, b0 + nb) of one sequence (cache length L).  Non-candidates get
 // -INFINITY.  scores_row: SEPARATE -> [Hkv][max_blocks] rows of this sequence, SHARED -> [max_blocks].
-// COH: write the scores with coherent stores (read by another workgroup of the same kernel).
-template <int G, int METHOD, int MODE, bool COH>
+template <int G, int METHOD, int MODE>
 __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16_t* __restrict__ q_seq,
                                           const void* __restrict__ rep_pool,
                                           const int32_t* __restrict__ trow, int max_blocks, int L,
@@ -120,9 +122,7 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
 #pragma unroll
         for (int p = 0; p < kScorePasses; ++p) {
           if (!inr[p]) continue;
-          float* dst = scores_row + (size_t)h * max_blocks + blk[p];
-          const float v = cand[p] ? acc[p] : -INFINITY;
-          if constexpr (COH) st_coh(dst, v); else *dst = v;
+          scores_row[(size_t)h * max_blocks + blk[p]] = cand[p] ? acc[p] : -INFINITY;
         }
       }
     } else {
@@ -137,8 +137,7 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
           if (!inr[p]) continue;
           float s = 0.f;
           for (int hh = 0; hh < Hkv; ++hh) s += lds_part[p * 16 + slot * Hkv + hh];
-          const float v = cand[p] ? s : -INFINITY;
-          if constexpr (COH) st_coh(scores_row + blk[p], v); else scores_row[blk[p]] = v;
+          scores_row[blk[p]] = cand[p] ? s : -INFINITY;
         }
       }
       __syncthreads();

@@ -1,5 +1,6 @@
-// kvs_topk_blocks kernel: one workgroup of 1024 lanes per (sequence, selection group); the selection
-// itself is topk_run (topk_core.h).
+// Top-k kernel of kvs_topk_blocks and kvs_decode_step: one workgroup of 1024 lanes per (sequence,
+// selection group); the selection itself is topk_run (topk_core.h).  With a table, the physical ids
+// of the selected blocks are written too (for the attention that follows in kvs_decode_step).
 #include "kvs_launch.h"
 #include "topk_core.h"
 
@@ -10,7 +11,9 @@ constexpr int kTopkThreads = 1024;  // up to 16 candidates per lane stay in regi
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params P, const float* __restrict__ scores,
                                                             const int32_t* __restrict__ seq_lens,
                                                             int max_blocks, int32_t* __restrict__ sel,
-                                                            int32_t* __restrict__ sel_count) {
+                                                            int32_t* __restrict__ sel_count,
+                                                            const int32_t* __restrict__ table,
+                                                            int32_t* __restrict__ tiles) {
   __shared__ TopkLds S;
   const int grp = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
   const Regions rg = regions_of(seq_lens[seq], P.initial_len, P.local_len);
@@ -20,14 +23,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params P, const floa
   int32_t* out = sel + row * P.topk;
   if (tid == 0) sel_count[row] = k;
   for (int i = k + tid; i < P.topk; i += kTopkThreads) out[i] = -1;
-  topk_run<kTopkThreads, 16, false>(scores + row * max_blocks + rg.cand_lo, n, k, rg.cand_lo, nullptr, 0,
-                                     S, out, nullptr, nullptr);
+  const int32_t* trow = table ? table + (size_t)seq * max_blocks : nullptr;
+  int32_t* tout = tiles ? tiles + row * P.topk : nullptr;
+  if (tout)
+    for (int i = k + tid; i < P.topk; i += kTopkThreads) tout[i] = -1;
+  topk_run<kTopkThreads, 16>(scores + row * max_blocks + rg.cand_lo, n, k, rg.cand_lo, nullptr, 0, S,
+                             out, trow, tout);
 }
 
 hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_lens, int batch,
-                       int max_blocks, int32_t* sel, int32_t* sel_count, hipStream_t s) {
+                       int max_blocks, int32_t* sel, int32_t* sel_count, const int32_t* table,
+                       int32_t* tiles, hipStream_t s) {
   const dim3 grid(P.G, batch), block(kTopkThreads);
-  hipLaunchKernelGGL(topk_kernel, grid, block, 0, s, P, scores, seq_lens, max_blocks, sel, sel_count);
+  hipLaunchKernelGGL(topk_kernel, grid, block, 0, s, P, scores, seq_lens, max_blocks, sel, sel_count,
+                     table, tiles);
   return hipGetLastError();
 }
 

@@ -101,8 +101,7 @@ __device__ inline uint32_t radix_select(KeyFn key, int n, int& rem, TopkLds& S) 
 // Selects the top k of the n candidate scores row[0..n) (candidate i is logical block cand_lo + i).
 // Writes sel[0..k) ascending; if tiles != nullptr also tiles[i] = trow[sel[i]] (physical ids).
 // IN_LDS: stage the n keys in lkeys (LDS), else read the scores again on every pass.
-// COH: scores were written, and sel / tiles are read, by other workgroups of the same kernel.
-template <int NT, bool COH, bool IN_LDS>
+template <int NT, bool IN_LDS>
 __device__ __attribute__((noinline)) void topk_select(const float* row, int n, int k, int cand_lo,
                                                       uint32_t* lkeys, TopkLds& S, int32_t* sel,
                                                       const int32_t* trow, int32_t* tiles) {
@@ -115,13 +114,8 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
   n = __builtin_amdgcn_readfirstlane(n);
   k = __builtin_amdgcn_readfirstlane(k);
   cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
-  const __amdgpu_buffer_rsrc_t rrow = coh_rsrc(row);
-  auto put = [&](int32_t* p, int32_t v) {
-    if constexpr (COH) st_coh(p, v); else *p = v;
-  };
-  auto score = [&](int i) -> float {
-    if constexpr (COH) return ld_coh_f1(rrow, i * 4); else return row[i];
-  };
+  auto put = [&](int32_t* p, int32_t v) { *p = v; };
+  auto score = [&](int i) -> float { return row[i]; };
   if (k <= 0) return;
   if (k >= n) {
     for (int i = tid; i < n; i += NT) {
@@ -291,7 +285,7 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
 // Register-resident variant for n <= NT*KPT: lane l of wave w holds the keys of indices
 // w*64*KPT + 64*c + l (c < KPT), so every pass is straight-line code over registers, all the loads of
 // the scores are in flight together, and the ordered output walks a wave's indices in order.
-template <int NT, int KPT, bool COH>
+template <int NT, int KPT>
 __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int n, int k, int cand_lo,
                                                           TopkLds& S, int32_t* sel,
                                                           const int32_t* trow, int32_t* tiles) {
@@ -304,10 +298,7 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
   n = __builtin_amdgcn_readfirstlane(n);
   k = __builtin_amdgcn_readfirstlane(k);
   cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
-  const __amdgpu_buffer_rsrc_t rrow = coh_rsrc(row);
-  auto put = [&](int32_t* p, int32_t v) {
-    if constexpr (COH) st_coh(p, v); else *p = v;
-  };
+  auto put = [&](int32_t* p, int32_t v) { *p = v; };
   if (k <= 0) return;
   if (k >= n) {
     for (int i = tid; i < n; i += NT) {
@@ -322,7 +313,7 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
   for (int c = 0; c < KPT; ++c) {
     const int i = ibase + 64 * c;
     const int ic = i < n ? i : 0;
-    if constexpr (COH) v[c] = ld_coh_f1(rrow, ic * 4); else v[c] = row[ic];
+    v[c] = row[ic];
   }
   uint32_t key[KPT];
   float lo = INFINITY, hi = -INFINITY;
@@ -497,16 +488,16 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
 
 // Picks the register-resident variant whenever the candidates fit NT * KMAX keys (KMAX keys per lane),
 // else the LDS-staged (IN_LDS, n <= lds_keys) or re-reading variant.
-template <int NT, int KMAX, bool COH>
+template <int NT, int KMAX>
 __device__ inline void topk_run(const float* row, int n, int k, int cand_lo, uint32_t* lkeys,
                                 int lds_keys, TopkLds& S, int32_t* sel, const int32_t* trow,
                                 int32_t* tiles) {
-  if (n <= NT * 4) topk_select_reg<NT, 4, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 8 && n <= NT * 8) topk_select_reg<NT, 8, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 16 && n <= NT * 16) topk_select_reg<NT, 16, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 32 && n <= NT * 32) topk_select_reg<NT, 32, COH>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (n <= lds_keys) topk_select<NT, COH, true>(row, n, k, cand_lo, lkeys, S, sel, trow, tiles);
-  else topk_select<NT, COH, false>(row, n, k, cand_lo, nullptr, S, sel, trow, tiles);
+  if (n <= NT * 4) topk_select_reg<NT, 4>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 8 && n <= NT * 8) topk_select_reg<NT, 8>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 16 && n <= NT * 16) topk_select_reg<NT, 16>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (KMAX >= 32 && n <= NT * 32) topk_select_reg<NT, 32>(row, n, k, cand_lo, S, sel, trow, tiles);
+  else if (n <= lds_keys) topk_select<NT, true>(row, n, k, cand_lo, lkeys, S, sel, trow, tiles);
+  else topk_select<NT, false>(row, n, k, cand_lo, nullptr, S, sel, trow, tiles);
 }
 
 }  // namespace kvs

@@ -59,15 +59,12 @@ def sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, seq_lens, sel, sel_c
 
 
 def step_workspace(cfg, batch, max_blocks, device) -> torch.Tensor:
-    """A kvs_decode_step workspace, initialised (its control words zeroed) on the current stream."""
-    need = B.kvs_decode_step_workspace_size(cfg, batch, max_blocks)
-    ws = workspace(need, device)
-    B.kvs_decode_step_workspace_init(cfg, batch, max_blocks, ws, ws.numel())
-    return ws
+    """A kvs_decode_step workspace (scratch; no initialisation needed)."""
+    return workspace(B.kvs_decode_step_workspace_size(cfg, batch, max_blocks), device)
 
 
 def decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_lens, ws=None):
-    """ws, if given, must come from step_workspace (or have been initialised the same way)."""
+    """ws, if given, must hold kvs_decode_step_workspace_size bytes (step_workspace)."""
     batch, mb = block_table.shape
     out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
     sel = torch.empty((batch, cfg.groups, max(cfg.topk, 1)), dtype=torch.int32, device=q.device)

@@ -161,24 +161,17 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
                                       int32_t max_blocks_per_seq);
 
 /*
- * kvs_decode_step_workspace_init -- zero a kvs_decode_step workspace (device, the whole
- * workspace_bytes) on `stream`.  A decode-step workspace holds control words that must be zero when a
- * call starts; every kvs_decode_step leaves them zero again, so this is needed once after allocation
- * (a workspace zero-filled by other means is equally valid).
- */
-int kvs_decode_step_workspace_init(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
-                                   void* workspace, size_t workspace_bytes, kvs_stream_t stream);
-
-/*
- * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention in a single
- * persistent kernel, enqueued with no host synchronisation [KT-LC §4.6, retrieval then attention].
+ * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention
+ * [KT-LC §4.6, retrieval then attention], enqueued as four kernels with no host synchronisation:
+ *   1. scoring of every block, together with the Initial/Local tiles' attention (they do not depend
+ *      on the selection, so their K/V gather overlaps the scoring);
+ *   2. top-k per (sequence, group), which also resolves the selected blocks' physical ids;
+ *   3. attention over the selected tiles;  4. the log-sum-exp merge into out.
+ * Results equal kvs_score_blocks + kvs_topk_blocks + kvs_sparse_decode_attn on the same inputs.
  * Reps must be current for every candidate block (kvs_build_reps).  sel_out / sel_count_out
  * (nullable) receive the selection for reuse by later kvs_sparse_decode_attn calls.
- * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned, initialised once by
- * kvs_decode_step_workspace_init; calls sharing one workspace must not run concurrently (stream order
- * is enough).  If a dependency wait inside the kernel ever times out (only possible with a workspace
- * that was not initialised), the kernel still finishes, the results are undefined, and the int at
- * byte offset 8 of the workspace is non-zero.
+ * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned, contents scratch;
+ * calls sharing one workspace must not run concurrently (stream order is enough).
  */
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
                     const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
