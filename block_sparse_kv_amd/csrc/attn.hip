@@ -2,8 +2,9 @@
 //  * attn_tiles_kernel: workgroup (x, h, seq) is one attended tile of KV head h -- the x-th
 //    Initial/Local tile, or a selected one -- and writes one partial per query head of h;
 //  * merge_kernel: workgroup (j, seq) folds the partials of query head j into out.
-// kvs_sparse_decode_attn runs both (Initial/Local and selected tiles in one grid); kvs_decode_step
-// runs the Initial/Local items inside its scoring kernel and the selected ones here.
+// kvs_sparse_decode_attn runs both (Initial/Local and selected tiles in one grid, selections as logical
+// ids); kvs_decode_step runs them with the selections as physical ids, the Initial/Local tiles here
+// or in its top-k launch (step.hip).
 #include "attn_core.h"
 #include "kvs_launch.h"
 
@@ -33,7 +34,9 @@ AttnPlan attn_plan(const Params& P, int batch, int max_blocks) {
 
 template <int G>
 static void launch_tiles_g(const AttnArgs& A, dim3 grid, bool il, bool phys, hipStream_t s) {
-  if (il)
+  if (il && phys)
+    hipLaunchKernelGGL((attn_tiles_kernel<G, true, true>), grid, dim3(256), 0, s, A);
+  else if (il)
     hipLaunchKernelGGL((attn_tiles_kernel<G, true, false>), grid, dim3(256), 0, s, A);
   else if (phys)
     hipLaunchKernelGGL((attn_tiles_kernel<G, false, true>), grid, dim3(256), 0, s, A);

@@ -153,31 +153,55 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 }
 
 constexpr int kMergeChunk = 1024;  // partials whose (max, sum) pairs sit in LDS at once
+constexpr int kMergeFirst = 128;   // partials whose outputs are loaded before their count is known
 constexpr int kMergeLdsFloats = 2 * kMergeChunk + 8 * kDim + 16;
 
-// Log-sum-exp merge of the n partials of one query head into out[128], by 256 lanes:
+// Log-sum-exp merge of the n (<= n_max) partials of one query head into out[128], by 256 lanes:
 //   out = sum_s exp2(m_s - M) o_s / sum_s exp2(m_s - M) l_s,  M = max_s m_s.
-// Chunks of kMergeChunk partials keep a running (M, sum, accumulator) state.  Within a chunk the
-// (max, sum) pairs are loaded in parallel, then each lane owns 4 channels of one of 8 partial groups
-// and keeps 8 float4 loads in flight; the 8 groups fold in LDS.  n == 0 gives zeros.
+// The loads that do not depend on n -- the (max, sum) pairs of the first chunk and the outputs of the
+// first kMergeFirst partials -- are issued first, so they travel with the loads that produce n.
+// Chunks of kMergeChunk partials keep a running (M, sum, accumulator) state; each lane owns 4
+// channels of one of 8 partial groups, and the 8 groups fold in LDS.  n == 0 gives zeros.
 __device__ inline void merge_head(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                  int n, float* __restrict__ out, float* lds) {
+                                  int n_max, int n, float* __restrict__ out, float* lds) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* wts = lds;                  // [kMergeChunk]: max, then weight
   float* sums = wts + kMergeChunk;   // [kMergeChunk]
   float* fold = sums + kMergeChunk;  // [8][128]
   float* red = fold + 8 * kDim;      // [8]
   const int c4 = (tid & 31) * 4, grp = tid >> 5;
+  constexpr int R0 = kMergeChunk / 256, U0 = kMergeFirst / 8;
+  float2 ml0[R0];
+  const int m0 = min(n_max, kMergeChunk);
+#pragma unroll
+  for (int r = 0; r < R0; ++r) {
+    const int s = tid + 256 * r;
+    ml0[r] = s < m0 ? *reinterpret_cast<const float2*>(part_ml + (size_t)s * 2) : make_float2(-INFINITY, 0.f);
+  }
+  float4 o0[U0];
+  const int f0 = min(n_max, kMergeFirst);
+#pragma unroll
+  for (int u = 0; u < U0; ++u) {
+    const int s = grp + 8 * u;
+    o0[u] = s < f0 ? *reinterpret_cast<const float4*>(part_o + (size_t)s * kDim + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float M = -INFINITY, Lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fma4 = [&](const float4& o, float f) {
+    acc.x += o.x * f; acc.y += o.y * f; acc.z += o.z * f; acc.w += o.w * f;
+  };
   for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
     const int cn = min(kMergeChunk, n - c0);
     float cm = -INFINITY;
-    for (int s = tid; s < cn; s += 256) {
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + (size_t)(c0 + s) * 2);
-      wts[s] = ml.x;
-      sums[s] = ml.y;
-      cm = fmaxf(cm, ml.x);
+#pragma unroll
+    for (int r = 0; r < R0; ++r) {
+      const int s = tid + 256 * r;
+      if (s < cn) {
+        const float2 ml = c0 == 0 ? ml0[r] : *reinterpret_cast<const float2*>(part_ml + (size_t)(c0 + s) * 2);
+        wts[s] = ml.x;
+        sums[s] = ml.y;
+        cm = fmaxf(cm, ml.x);
+      }
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) cm = fmaxf(cm, shfl_xor_f(cm, m));
@@ -187,33 +211,41 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
     const float resc = exp2_diff(M, Mn);  // 0 while nothing has been accumulated
     M = Mn;
     float cl = 0.f;
-    for (int s = tid; s < cn; s += 256) {  // each lane rewrites only the entries it loaded
-      const float f = exp2_diff(wts[s], M);
-      wts[s] = f;
-      cl += sums[s] * f;
+#pragma unroll
+    for (int r = 0; r < R0; ++r) {  // each lane rewrites only the entries it wrote
+      const int s = tid + 256 * r;
+      if (s < cn) {
+        const float f = exp2_diff(wts[s], M);
+        wts[s] = f;
+        cl += sums[s] * f;
+      }
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) cl += shfl_xor_f(cl, m);
     if (lane == 0) red[4 + w] = cl;
     __syncthreads();  // weights and chunk sums visible
     acc.x *= resc; acc.y *= resc; acc.z *= resc; acc.w *= resc;
-    for (int s0 = grp; s0 < cn; s0 += 8 * 8) {
+    int s_from = 0;
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < U0; ++u) {
+        const int s = grp + 8 * u;
+        if (s < cn) fma4(o0[u], wts[s]);
+      }
+      s_from = kMergeFirst;
+    }
+    for (int s0 = s_from + grp; s0 < cn; s0 += 8 * 8) {  // the rest, 8 loads in flight
       float4 o[8];
-      float f[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int s = s0 + 8 * u;
-        const bool ok = s < cn;
-        f[u] = ok ? wts[s] : 0.f;
-        o[u] = ok ? *reinterpret_cast<const float4*>(part_o + (size_t)(c0 + s) * kDim + c4)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        o[u] = s < cn ? *reinterpret_cast<const float4*>(part_o + (size_t)(c0 + s) * kDim + c4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        acc.x += o[u].x * f[u];
-        acc.y += o[u].y * f[u];
-        acc.z += o[u].z * f[u];
-        acc.w += o[u].w * f[u];
+        const int s = s0 + 8 * u;
+        if (s < cn) fma4(o[u], wts[s]);
       }
     }
     Lsum = Lsum * resc + red[4] + red[5] + red[6] + red[7];
@@ -228,7 +260,6 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
     out[tid] = Lsum > 0.f ? a / Lsum : 0.f;
   }
 }
-
 
 // Selected blocks attended by (sequence, KV head h): the group's count, clamped to [0, topk], and 0
 // when the sequence is all Initial.
@@ -296,7 +327,8 @@ __device__ inline void merge_item(const AttnArgs& A, int j, int seq, float* lds)
   const TileList tl = tiles_of(L, P, 0);
   const int n = tl.nI + tl.nLoc + sel_k_of(A, seq, j / P.g, L);
   const size_t hp = (size_t)seq * P.Hq + j;
-  merge_head(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, n, A.out + hp * kDim, lds);
+  merge_head(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, A.max_parts, n,
+             A.out + hp * kDim, lds);
 }
 
 }  // namespace kvs

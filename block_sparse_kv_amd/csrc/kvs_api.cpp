@@ -278,14 +278,8 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
                               seq_lens, tiles, cnt, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/score");
-  e = kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel, cnt, block_table,
-                       P.topk > 0 ? tiles : nullptr, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/topk");
-  e = kvs::launch_attn_tiles(a, batch, false, true, s);
-  if (e != hipSuccess) return hip_status(e, "kvs_decode_step/attention");
-  return hip_status(kvs::launch_merge(a, batch, s), "kvs_decode_step/merge");
+  return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles, batch, s),
+                    "kvs_decode_step");
 }
 
 }  // extern "C"

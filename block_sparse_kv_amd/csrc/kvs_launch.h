@@ -29,12 +29,13 @@ hipError_t launch_score(const Params& P, const void* q, const void* rep_pool, co
 hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_lens, int batch,
                        int max_blocks, int32_t* sel, int32_t* sel_count, const int32_t* table,
                        int32_t* tiles, hipStream_t s);
-// Attention work items: with il, the Initial/Local tiles and then the selected ones (A.sel holds
-// logical ids); without, only the selected ones (physical ids if sel_phys).
+// Attention work items: with il, the Initial/Local tiles and then the selected ones, else only the
+// selected ones; A.sel holds physical ids if sel_phys, logical ids otherwise.
 hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s);
-// Scoring of every block together with the Initial/Local tiles (first launch of kvs_decode_step).
-hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* scores, int batch,
-                           hipStream_t s);
+// The whole decode step (step.hip): scores [batch][G][max_blocks], sel / sel_count, and the selected
+// tiles' physical ids (tiles [batch][G][topk]) are its intermediates; A.sel must be `tiles`.
+hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
+                              int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s);
 
 }  // namespace kvs

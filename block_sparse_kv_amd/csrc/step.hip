@@ -1,69 +1,70 @@
-// kvs_decode_step, first launch: block scoring and the Initial/Local attention tiles in one grid.
-// The two need nothing from each other -- Initial and Local are attended whatever the selection
-// [KT-LC §4.2] -- so the gather of Initial/Local K/V overlaps the scoring.  Workgroups
-// [0, n_score) of sequence seq score sb blocks each (score_core.h); the rest are Initial/Local tiles
-// (attn_core.h), the x-th tile of KV head h at x + h * n_il_max.  The step then runs top-k (which
-// also writes the selected tiles' physical ids), the selected tiles and the merge.
+// kvs_decode_step: scoring -> top-k -> attention tiles -> merge, with the Initial/Local tiles -- which
+// do not depend on the selection [KT-LC §4.2] -- placed where their K/V gather costs least:
+//  * short rows (max_blocks <= kStepTopkSmall): in the top-k launch (topk_il_kernel).  Their gather
+//    then runs while the few top-k workgroups -- one per (sequence, group), 256 lanes, keys in
+//    registers -- choose the blocks;
+//  * long rows: in the selected-tile launch, whose stream they lengthen by their bytes only, while
+//    top-k gets 1024-lane workgroups (topk.hip).
+// In every grid an attention tile is one workgroup (attn_core.h).
 #include "attn_core.h"
 #include "kvs_launch.h"
-#include "score_core.h"
+#include "topk_core.h"
 
 namespace kvs {
 
-// 4 workgroups per CU (the attention tiles' occupancy) unless the scoring of 8 or 16 query heads per
-// KV head needs more registers.
-template <int G, int METHOD, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void score_il_kernel(AttnArgs A, const void* __restrict__ rep_pool,
-                                                       float* __restrict__ scores, int sb, int n_score) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kAttnLdsBytes];
-  const int seq = blockIdx.y;
-  const int x = blockIdx.x;
-  if (x < n_score) {
-    const Params& P = A.P;
-    score_blocks_range<G, METHOD, MODE>(P, A.q + (size_t)seq * P.Hq * kDim, rep_pool,
-                                        A.table + (size_t)seq * A.max_blocks, A.max_blocks,
-                                        A.seq_lens[seq], x * sb, sb,
-                                        scores + (size_t)seq * P.G * A.max_blocks,
-                                        reinterpret_cast<float*>(smem));
-  } else {
-    const int y = x - n_score;
-    attn_item<G, true, false>(A, y % A.n_il_max, y / A.n_il_max, seq, smem);
-  }
-}
-
-template <int G, int METHOD>
-static void launch_si_m(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
-                        int sb, int n_score) {
-  if (A.P.mode == kSeparate)
-    hipLaunchKernelGGL((score_il_kernel<G, METHOD, kSeparate>), grid, dim3(256), 0, s, A, reps, scores, sb, n_score);
-  else
-    hipLaunchKernelGGL((score_il_kernel<G, METHOD, kShared>), grid, dim3(256), 0, s, A, reps, scores, sb, n_score);
-}
+constexpr int kStepTopkKeys = 8;  // keys per lane of the 256-lane selections
+constexpr int kStepTopkSmall = 256 * kStepTopkKeys;
+constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
 
 template <int G>
-static void launch_si_g(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
-                        int sb, int n_score) {
-  switch (A.P.method) {
-    case kQuest: launch_si_m<G, kQuest>(A, grid, s, reps, scores, sb, n_score); break;
-    case kMax: launch_si_m<G, kMax>(A, grid, s, reps, scores, sb, n_score); break;
-    case kMean: launch_si_m<G, kMean>(A, grid, s, reps, scores, sb, n_score); break;
-    default: launch_si_m<G, kFix>(A, grid, s, reps, scores, sb, n_score); break;
+__global__ __launch_bounds__(256) void topk_il_kernel(AttnArgs A, const float* __restrict__ scores,
+                                                      int32_t* __restrict__ sel,
+                                                      int32_t* __restrict__ sel_count,
+                                                      int32_t* __restrict__ tiles, int n_topk) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
+  const Params& P = A.P;
+  const int x = blockIdx.x;
+  if (x < n_topk) {
+    topk_group<256, kStepTopkKeys>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles,
+                                   x / P.G, x % P.G, *reinterpret_cast<TopkLds*>(smem));
+  } else {
+    const int y = x - n_topk;
+    const int per_seq = P.Hkv * A.n_il_max;
+    const int r = y % per_seq;
+    attn_item<G, true, false>(A, r % A.n_il_max, r / A.n_il_max, y / per_seq, smem);
   }
 }
 
-hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* scores, int batch,
-                           hipStream_t s) {
-  const int sb = score_blocks_per_wg(A.P);
-  const int n_score = (A.max_blocks + sb - 1) / sb;
-  const dim3 grid(n_score + A.P.Hkv * A.n_il_max, batch);
+hipError_t launch_topk_il(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
+                          int32_t* tiles, int batch, hipStream_t s) {
+  const int n_topk = A.P.G * batch;
+  const dim3 grid(n_topk + batch * A.P.Hkv * A.n_il_max), block(256);
   switch (A.P.g) {
-    case 1: launch_si_g<1>(A, grid, s, rep_pool, scores, sb, n_score); break;
-    case 2: launch_si_g<2>(A, grid, s, rep_pool, scores, sb, n_score); break;
-    case 4: launch_si_g<4>(A, grid, s, rep_pool, scores, sb, n_score); break;
-    case 8: launch_si_g<8>(A, grid, s, rep_pool, scores, sb, n_score); break;
-    default: launch_si_g<16>(A, grid, s, rep_pool, scores, sb, n_score); break;
+    case 1: hipLaunchKernelGGL(topk_il_kernel<1>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
+    case 2: hipLaunchKernelGGL(topk_il_kernel<2>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
+    case 4: hipLaunchKernelGGL(topk_il_kernel<4>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
+    case 8: hipLaunchKernelGGL(topk_il_kernel<8>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
+    default: hipLaunchKernelGGL(topk_il_kernel<16>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
   }
   return hipGetLastError();
+}
+
+
+hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
+                              int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s) {
+  const Params& P = A.P;
+  int32_t* tl = P.topk > 0 ? tiles : nullptr;
+  hipError_t e = launch_score(P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
+  if (A.max_blocks <= kStepTopkSmall) {
+    if (e == hipSuccess) e = launch_topk_il(A, scores, sel, sel_count, tl, batch, s);
+    if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
+  } else {
+    if (e == hipSuccess)
+      e = launch_topk(P, scores, A.seq_lens, batch, A.max_blocks, sel, sel_count, A.table, tl, s);
+    if (e == hipSuccess) e = launch_attn_tiles(A, batch, true, true, s);
+  }
+  if (e == hipSuccess) e = launch_merge(A, batch, s);
+  return e;
 }
 
 }  // namespace kvs

@@ -1,5 +1,5 @@
 // Top-k kernel of kvs_topk_blocks and kvs_decode_step: one workgroup of 1024 lanes per (sequence,
-// selection group); the selection itself is topk_run (topk_core.h).  With a table, the physical ids
+// selection group); the selection itself is topk_group (topk_core.h).  With a table, the physical ids
 // of the selected blocks are written too (for the attention that follows in kvs_decode_step).
 #include "kvs_launch.h"
 #include "topk_core.h"
@@ -15,20 +15,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params P, const floa
                                                             const int32_t* __restrict__ table,
                                                             int32_t* __restrict__ tiles) {
   __shared__ TopkLds S;
-  const int grp = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
-  const Regions rg = regions_of(seq_lens[seq], P.initial_len, P.local_len);
-  const int n = rg.cand_hi - rg.cand_lo;
-  const int k = min(P.topk, n);
-  const size_t row = (size_t)seq * P.G + grp;
-  int32_t* out = sel + row * P.topk;
-  if (tid == 0) sel_count[row] = k;
-  for (int i = k + tid; i < P.topk; i += kTopkThreads) out[i] = -1;
-  const int32_t* trow = table ? table + (size_t)seq * max_blocks : nullptr;
-  int32_t* tout = tiles ? tiles + row * P.topk : nullptr;
-  if (tout)
-    for (int i = k + tid; i < P.topk; i += kTopkThreads) tout[i] = -1;
-  topk_run<kTopkThreads, 16>(scores + row * max_blocks + rg.cand_lo, n, k, rg.cand_lo, nullptr, 0, S,
-                             out, trow, tout);
+  topk_group<kTopkThreads, 16>(P, scores, seq_lens, max_blocks, sel, sel_count, table, tiles,
+                               blockIdx.y, blockIdx.x, S);
 }
 
 hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_lens, int batch,

@@ -9,12 +9,17 @@
 //      is a monotone function of the score, so a bin above the boundary bin holds only keys above T.
 //      A histogram (about n/kBins keys per bin, so LDS atomics rarely collide) and a suffix scan find
 //      the bin that holds the k-th largest key.
-//   2. inside that bin: its keys are gathered in LDS.  Up to 64 of them, wave 0 ranks them by
-//      counting (no barriers); a crowded bin (many equal scores) goes through an MSB-first radix select
-//      (4 passes of 8 bits).
-// Each wave then walks a contiguous index segment 64 keys at a time, keeping every key > T and the
+//   2. inside that bin: up to 64 keys are gathered in LDS and wave 0 ranks them by counting (no
+//      barriers); a crowded bin (many equal scores) goes through an MSB-first radix select (4 passes
+//      of 8 bits).
+// Each wave then walks its indices in ascending order 64 at a time, keeping every key > T and the
 // lowest-indexed keys == T; ballots and popcounts give each kept block its slot, so the selection
 // comes out in ascending block order.
+//
+// Rows of up to NT * KMAX blocks (every size the decode configurations use) keep their keys in
+// registers: the score row, the table row and the sequence length are loaded together, and the
+// candidate range is applied once the length has arrived.  Longer rows re-read their scores from
+// memory on every pass.
 #pragma once
 
 #include "kvs_device.h"
@@ -42,13 +47,11 @@ __device__ inline T* uniform_ptr(T* p) {
 
 constexpr int kBins = 1024;     // value bins of stage 1
 constexpr int kSubMax = 1024;   // keys of the boundary bin gathered in LDS for stage 2
-constexpr int kSelLds = 2048;   // selections up to this size are assembled in LDS
 
 // LDS the selection needs besides the staged keys.
 struct TopkLds {
   int hist[kBins];
   uint32_t sub[kSubMax];
-  int32_t outsel[kSelLds];
   int bcast[4];
   int wgt[16], weq[16];
   float fmin[16], fmax[16];
@@ -98,13 +101,13 @@ __device__ inline uint32_t radix_select(KeyFn key, int n, int& rem, TopkLds& S) 
   return prefix;
 }
 
-// Selects the top k of the n candidate scores row[0..n) (candidate i is logical block cand_lo + i).
-// Writes sel[0..k) ascending; if tiles != nullptr also tiles[i] = trow[sel[i]] (physical ids).
-// IN_LDS: stage the n keys in lkeys (LDS), else read the scores again on every pass.
-template <int NT, bool IN_LDS>
+// Selects the top k of the n candidate scores row[0..n) (candidate i is logical block cand_lo + i),
+// reading the scores again on every pass.  Writes sel[0..k) ascending; if tiles != nullptr also
+// tiles[i] = trow[sel[i]] (physical ids).
+template <int NT>
 __device__ __attribute__((noinline)) void topk_select(const float* row, int n, int k, int cand_lo,
-                                                      uint32_t* lkeys, TopkLds& S, int32_t* sel,
-                                                      const int32_t* trow, int32_t* tiles) {
+                                                      TopkLds& S, int32_t* sel, const int32_t* trow,
+                                                      int32_t* tiles) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   row = uniform_ptr(row);
@@ -124,24 +127,7 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
     }
     return;
   }
-  if constexpr (IN_LDS) {  // 8 loads in flight per lane
-    for (int base = 0; base < n; base += 8 * NT) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * NT + tid;
-        v[u] = score(i < n ? i : 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * NT + tid;
-        if (i < n) lkeys[i] = order_key(v[u]);
-      }
-    }
-  }
-  auto key = [&](int i) -> uint32_t {
-    if constexpr (IN_LDS) return lkeys[i]; else return order_key(score(i));
-  };
+  auto key = [&](int i) -> uint32_t { return order_key(score(i)); };
 
   // ---- stage 1: value bins over [min, max] ----
   float lo = INFINITY, hi = -INFINITY;
@@ -252,7 +238,6 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
     pos += S.wgt[v] + max(0, min(S.weq[v], rem - eq_before));
     eq_before += S.weq[v];
   }
-  const bool in_lds = k <= kSelLds;
   for (int base = s0; base < s1; base += 64) {
     const int i = base + lane;
     const bool in = i < s1;
@@ -262,89 +247,93 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
     const unsigned long long km = __ballot(keep);
     if (keep) {
       const int slot = pos + __popcll(km & lt);
-      if (in_lds) S.outsel[slot] = cand_lo + i;
-      else {
-        put(sel + slot, cand_lo + i);
-        if (tiles) put(tiles + slot, trow[cand_lo + i]);
-      }
+      put(sel + slot, cand_lo + i);
+      if (tiles) put(tiles + slot, trow[cand_lo + i]);
     }
     pos += __popcll(km);
     eq_before += __popcll(eqm);
   }
-  if (in_lds) {
-    __syncthreads();
-    for (int j = tid; j < k; j += NT) {
-      const int b = S.outsel[j];
-      put(sel + j, b);
-      if (tiles) put(tiles + j, trow[b]);
-    }
-  }
 }
 
-
-// Register-resident variant for n <= NT*KPT: lane l of wave w holds the keys of indices
-// w*64*KPT + 64*c + l (c < KPT), so every pass is straight-line code over registers, all the loads of
-// the scores are in flight together, and the ordered output walks a wave's indices in order.
+// Register-resident selection of one (sequence, group) whose score row row[0..m) fits NT * KPT keys:
+// lane l of wave w holds indices w*64*KPT + 64*c + l (c < KPT).  The row, the table row (trow,
+// nullable) and *len are loaded together; candidates are the indices in [cand_lo, cand_hi) of the
+// length's regions.  Writes *cnt = k_eff, sel[0..k_eff) ascending (and tiles[] = their physical ids
+// when trow != nullptr), -1 in sel / tiles [k_eff, topk).
 template <int NT, int KPT>
-__device__ __attribute__((noinline)) void topk_select_reg(const float* row, int n, int k, int cand_lo,
-                                                          TopkLds& S, int32_t* sel,
-                                                          const int32_t* trow, int32_t* tiles) {
+__device__ __forceinline__ void topk_group_reg(const float* row, int m, const int32_t* len,
+                                                         int initial_len, int local_len, int topk,
+                                                         TopkLds& S, int32_t* sel, int32_t* cnt,
+                                                         const int32_t* trow, int32_t* tiles) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   row = uniform_ptr(row);
+  len = uniform_ptr(len);
   sel = uniform_ptr(sel);
+  cnt = uniform_ptr(cnt);
   trow = uniform_ptr(trow);
   tiles = uniform_ptr(tiles);
-  n = __builtin_amdgcn_readfirstlane(n);
-  k = __builtin_amdgcn_readfirstlane(k);
-  cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
-  auto put = [&](int32_t* p, int32_t v) { *p = v; };
-  if (k <= 0) return;
-  if (k >= n) {
-    for (int i = tid; i < n; i += NT) {
-      put(sel + i, cand_lo + i);
-      if (tiles) put(tiles + i, trow[cand_lo + i]);
-    }
-    return;
-  }
+  m = __builtin_amdgcn_readfirstlane(m);
   const int ibase = wv * 64 * KPT + lane;
   float v[KPT];
+  int32_t ph[KPT];
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     const int i = ibase + 64 * c;
-    const int ic = i < n ? i : 0;
+    const int ic = i < m ? i : 0;
     v[c] = row[ic];
+    ph[c] = trow ? trow[ic] : 0;
+  }
+  const Regions rg = regions_of(*len, initial_len, local_len);
+  const int lo = rg.cand_lo, hi = min(rg.cand_hi, m);
+  const int n = max(0, hi - lo);
+  const int k = min(topk, n);
+  if (tid == 0) *cnt = k;
+  for (int i = k + tid; i < topk; i += NT) {
+    sel[i] = -1;
+    if (trow) tiles[i] = -1;
+  }
+  if (k <= 0) return;
+  auto ok = [&](int c) { const int i = ibase + 64 * c; return i >= lo && i < hi; };
+  auto emit = [&](int slot, int c) {
+    sel[slot] = ibase + 64 * c;
+    if (trow) tiles[slot] = ph[c];
+  };
+  if (k >= n) {  // every candidate
+#pragma unroll
+    for (int c = 0; c < KPT; ++c)
+      if (ok(c)) emit(ibase + 64 * c - lo, c);
+    return;
   }
   uint32_t key[KPT];
-  float lo = INFINITY, hi = -INFINITY;
+  float fl = INFINITY, fh = -INFINITY;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    const bool ok = ibase + 64 * c < n;
-    key[c] = ok ? order_key(v[c]) : 0u;  // 0 is below every real key
+    key[c] = ok(c) ? order_key(v[c]) : 0u;  // 0 is below every real key
     const float x = key_value(key[c]);
-    if (ok) { lo = fminf(lo, x); hi = fmaxf(hi, x); }
+    if (ok(c)) { fl = fminf(fl, x); fh = fmaxf(fh, x); }
   }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, m, 64));
-    hi = fmaxf(hi, __shfl_xor(hi, m, 64));
+  for (int mm = 1; mm < 64; mm <<= 1) {
+    fl = fminf(fl, __shfl_xor(fl, mm, 64));
+    fh = fmaxf(fh, __shfl_xor(fh, mm, 64));
   }
-  if (lane == 0) { S.fmin[wv] = lo; S.fmax[wv] = hi; }
+  if (lane == 0) { S.fmin[wv] = fl; S.fmax[wv] = fh; }
   for (int i = tid; i < kBins; i += NT) S.hist[i] = 0;
   __syncthreads();
-  lo = S.fmin[0];
-  hi = S.fmax[0];
+  fl = S.fmin[0];
+  fh = S.fmax[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) { lo = fminf(lo, S.fmin[w]); hi = fmaxf(hi, S.fmax[w]); }
-  const float span = hi - lo;
+  for (int w = 1; w < NW; ++w) { fl = fminf(fl, S.fmin[w]); fh = fmaxf(fh, S.fmax[w]); }
+  const float span = fh - fl;
   const float scale = span > 0.f && span < INFINITY ? (float)kBins / span : 0.f;
   auto bin_of = [&](uint32_t u) -> int {
-    const float x = (key_value(u) - lo) * scale;  // monotone in the score
+    const float x = (key_value(u) - fl) * scale;  // monotone in the score
     return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
   };
 #pragma unroll
   for (int c = 0; c < KPT; ++c)
-    if (ibase + 64 * c < n) atomicAdd(&S.hist[bin_of(key[c])], 1);
+    if (ok(c)) atomicAdd(&S.hist[bin_of(key[c])], 1);
   __syncthreads();
   if (tid < 64) {  // boundary bin: lane l sums bins 16l..16l+15, suffix scan across lanes
     int own = 0;
@@ -363,10 +352,10 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
         if (above + S.hist[b] >= k) break;
         above += S.hist[b];
       }
-      S.bcast[0] = b;
-      S.bcast[1] = above;
-      S.bcast[2] = 0;
-      S.bcast[3] = S.hist[b];
+      S.bcast[0] = b;          // boundary bin
+      S.bcast[1] = above;      // keys in higher bins (all selected)
+      S.bcast[2] = 0;          // gather cursor
+      S.bcast[3] = S.hist[b];  // keys in the boundary bin (hist is reused below)
     }
   }
   __syncthreads();
@@ -377,7 +366,7 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
   if (m_sub <= 64) {  // gather the boundary bin, wave 0 ranks it by counting
 #pragma unroll
     for (int c = 0; c < KPT; ++c)
-      if (ibase + 64 * c < n && bin_of(key[c]) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = key[c];
+      if (ok(c) && bin_of(key[c]) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = key[c];
     __syncthreads();
     if (tid < 64) {
       const uint32_t u = lane < m_sub ? S.sub[lane] : 0u;
@@ -389,7 +378,7 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
       }
       const bool is_t = lane < m_sub && gt < rem && ge >= rem;
       const unsigned long long bm = __ballot(is_t);
-      const int src = __ffsll((long long)bm) - 1;
+      const int src = __ffsll((long long)bm) - 1;  // some lane holds T (all such lanes agree)
       const uint32_t t = __shfl(u, src, 64);
       const int above_t = __shfl(gt, src, 64);
       if (lane == 0) { S.bcast[2] = (int)t; S.bcast[3] = rem - above_t; }
@@ -398,56 +387,52 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
     T = (uint32_t)S.bcast[2];
     rem = S.bcast[3];
   } else {  // a crowded bin (many equal scores): MSB-first radix select over that bin's keys
-    {
-      uint32_t prefix = 0, pmask = 0;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
-        __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
+      __syncthreads();
 #pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-          const uint32_t u = key[c];
-          if (ibase + 64 * c < n && bin_of(u) == bstar && (u & pmask) == prefix)
-            atomicAdd(&S.hist[(u >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (tid < 64) {
-          const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
-                    c3 = S.hist[4 * tid + 3];
-          const int own = c0 + c1 + c2 + c3;
-          int suf = own;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_down(suf, d, 64);
-            if (tid + d < 64) suf += y;
-          }
-          const int above_lane = suf - own;
-          if (above_lane < rem && suf >= rem) {
-            int digit, above = above_lane;
-            if (above + c3 >= rem) digit = 4 * tid + 3;
-            else if ((above += c3) + c2 >= rem) digit = 4 * tid + 2;
-            else if ((above += c2) + c1 >= rem) digit = 4 * tid + 1;
-            else { above += c1; digit = 4 * tid; }
-            S.bcast[0] = digit;
-            S.bcast[1] = above;
-          }
-        }
-        __syncthreads();
-        rem -= S.bcast[1];
-        prefix |= (uint32_t)S.bcast[0] << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
+      for (int c = 0; c < KPT; ++c) {
+        const uint32_t u = key[c];
+        if (ok(c) && bin_of(u) == bstar && (u & pmask) == prefix) atomicAdd(&S.hist[(u >> shift) & 255], 1);
       }
-      T = prefix;
+      __syncthreads();
+      if (tid < 64) {  // lane l owns digits 4l..4l+3; suffix sums from the high digits
+        const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
+                  c3 = S.hist[4 * tid + 3];
+        const int own = c0 + c1 + c2 + c3;
+        int suf = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_down(suf, d, 64);
+          if (tid + d < 64) suf += y;
+        }
+        const int above_lane = suf - own;
+        if (above_lane < rem && suf >= rem) {
+          int digit, above = above_lane;
+          if (above + c3 >= rem) digit = 4 * tid + 3;
+          else if ((above += c3) + c2 >= rem) digit = 4 * tid + 2;
+          else if ((above += c2) + c1 >= rem) digit = 4 * tid + 1;
+          else { above += c1; digit = 4 * tid; }
+          S.bcast[0] = digit;
+          S.bcast[1] = above;
+        }
+      }
+      __syncthreads();
+      rem -= S.bcast[1];
+      prefix |= (uint32_t)S.bcast[0] << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
     }
+    T = prefix;
   }
-  // ordered output over registers
+  // T is the k-th largest key; `rem` of the keys equal to T are taken.  Ordered output:
   const unsigned long long lt = (1ull << lane) - 1ull;
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    const bool ok = ibase + 64 * c < n;
-    n_gt += __popcll(__ballot(ok && key[c] > T));
-    n_eq += __popcll(__ballot(ok && key[c] == T));
+    n_gt += __popcll(__ballot(ok(c) && key[c] > T));
+    n_eq += __popcll(__ballot(ok(c) && key[c] == T));
   }
   if (lane == 0) { S.wgt[wv] = n_gt; S.weq[wv] = n_eq; }
   __syncthreads();
@@ -456,48 +441,50 @@ __device__ __attribute__((noinline)) void topk_select_reg(const float* row, int 
     pos += S.wgt[w] + max(0, min(S.weq[w], rem - eq_before));
     eq_before += S.weq[w];
   }
-  const bool in_lds = k <= kSelLds;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    const int i = ibase + 64 * c;
-    const bool ok = i < n;
-    const unsigned long long eqm = __ballot(ok && key[c] == T);
-    const bool keep = ok && (key[c] > T || (key[c] == T && eq_before + __popcll(eqm & lt) < rem));
+    const unsigned long long eqm = __ballot(ok(c) && key[c] == T);
+    const bool keep = ok(c) && (key[c] > T || (key[c] == T && eq_before + __popcll(eqm & lt) < rem));
     const unsigned long long km = __ballot(keep);
-    if (keep) {
-      const int slot = pos + __popcll(km & lt);
-      if (in_lds) S.outsel[slot] = cand_lo + i;
-      else {
-        put(sel + slot, cand_lo + i);
-        if (tiles) put(tiles + slot, trow[cand_lo + i]);
-      }
-    }
+    if (keep) emit(pos + __popcll(km & lt), c);
     pos += __popcll(km);
     eq_before += __popcll(eqm);
   }
-  if (in_lds) {
-    __syncthreads();
-    for (int j = tid; j < k; j += NT) {
-      const int b = S.outsel[j];
-      put(sel + j, b);
-      if (tiles) put(tiles + j, trow[b]);
-    }
-  }
 }
 
-
-// Picks the register-resident variant whenever the candidates fit NT * KMAX keys (KMAX keys per lane),
-// else the LDS-staged (IN_LDS, n <= lds_keys) or re-reading variant.
+// The selection of group grp of sequence seq from the scores [batch][G][max_blocks]: sel (and, with a
+// table and tiles, the physical ids in tiles) [batch][G][topk] ascending and -1 padded,
+// sel_count [batch][G].  Rows of up to NT * KMAX blocks stay in registers.
 template <int NT, int KMAX>
-__device__ inline void topk_run(const float* row, int n, int k, int cand_lo, uint32_t* lkeys,
-                                int lds_keys, TopkLds& S, int32_t* sel, const int32_t* trow,
-                                int32_t* tiles) {
-  if (n <= NT * 4) topk_select_reg<NT, 4>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 8 && n <= NT * 8) topk_select_reg<NT, 8>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 16 && n <= NT * 16) topk_select_reg<NT, 16>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (KMAX >= 32 && n <= NT * 32) topk_select_reg<NT, 32>(row, n, k, cand_lo, S, sel, trow, tiles);
-  else if (n <= lds_keys) topk_select<NT, true>(row, n, k, cand_lo, lkeys, S, sel, trow, tiles);
-  else topk_select<NT, false>(row, n, k, cand_lo, nullptr, S, sel, trow, tiles);
+__device__ inline void topk_group(const Params& P, const float* __restrict__ scores,
+                                  const int32_t* __restrict__ seq_lens, int max_blocks,
+                                  int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+                                  const int32_t* __restrict__ table, int32_t* __restrict__ tiles,
+                                  int seq, int grp, TopkLds& S) {
+  const size_t row = (size_t)seq * P.G + grp;
+  const float* srow = scores + row * max_blocks;
+  int32_t* out = sel + row * P.topk;
+  int32_t* tout = tiles ? tiles + row * P.topk : nullptr;
+  const int32_t* trow = tiles && table ? table + (size_t)seq * max_blocks : nullptr;
+  const int32_t* len = seq_lens + seq;
+#define KVS_TOPK_REG(KPT)                                                                            \
+  topk_group_reg<NT, KPT>(srow, max_blocks, len, P.initial_len, P.local_len, P.topk, S, out,         \
+                          sel_count + row, trow, tout)
+  if (max_blocks <= NT * 4) { KVS_TOPK_REG(4); return; }
+  if (KMAX >= 8 && max_blocks <= NT * 8) { KVS_TOPK_REG(8); return; }
+  if (KMAX >= 16 && max_blocks <= NT * 16) { KVS_TOPK_REG(16); return; }
+  if (KMAX >= 32 && max_blocks <= NT * 32) { KVS_TOPK_REG(32); return; }
+#undef KVS_TOPK_REG
+  const int tid = threadIdx.x;
+  const Regions rg = regions_of(*len, P.initial_len, P.local_len);
+  const int n = max(0, min(rg.cand_hi, max_blocks) - rg.cand_lo);
+  const int k = min(P.topk, n);
+  if (tid == 0) sel_count[row] = k;
+  for (int i = k + tid; i < P.topk; i += NT) {
+    out[i] = -1;
+    if (trow) tout[i] = -1;
+  }
+  topk_select<NT>(srow + rg.cand_lo, n, k, rg.cand_lo, S, out, trow, trow ? tout : nullptr);
 }
 
 }  // namespace kvs

@@ -163,10 +163,11 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
 /*
  * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention
  * [KT-LC §4.6, retrieval then attention], enqueued as four kernels with no host synchronisation:
- *   1. scoring of every block, together with the Initial/Local tiles' attention (they do not depend
- *      on the selection, so their K/V gather overlaps the scoring);
+ *   1. scoring of every block;
  *   2. top-k per (sequence, group), which also resolves the selected blocks' physical ids;
- *   3. attention over the selected tiles;  4. the log-sum-exp merge into out.
+ *   3. attention, one workgroup per (tile, KV head);  4. the log-sum-exp merge into out.
+ * The Initial/Local tiles do not depend on the selection: for max_blocks_per_seq <= 2048 they run
+ * in launch 2, beside the selections, otherwise in launch 3.
  * Results equal kvs_score_blocks + kvs_topk_blocks + kvs_sparse_decode_attn on the same inputs.
  * Reps must be current for every candidate block (kvs_build_reps).  sel_out / sel_count_out
  * (nullable) receive the selection for reuse by later kvs_sparse_decode_attn calls.
