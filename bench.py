@@ -2,9 +2,12 @@
 """Sparse decode benchmark on one MI355X: queries/s and HBM roofline fraction at 128K and 1M tokens.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --summarize-stats DIR --workload NAME      (rocprofv3 --stats CSVs -> profiles/)
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --workload NAME   (counters -> profiles/)
 
-A step is one pass of the whole hot path -- block scoring, top-k and sparse attention, fused in
-kvs_decode_step -- over one decode token:
+A step is one pass of the whole hot path over one decode token: kvs_decode_step, i.e. block scoring,
+top-k and sparse attention (four launches: scoring; top-k, with the Initial/Local tiles for rows of
+<= 2048 blocks; the attention tiles; the merge):
   * 128k-max / 128k-mean: InternLM2.5-7B-shaped layer, 32 query / 8 KV heads, d 128, 131,072 cached
     tokens, block 128, Max (or Mean) reps, SHARED selection, top-96, Initial 128, Local 4,096;
     one query = one step of one sequence.  The JSON line's `value` is 128k-max.
@@ -12,11 +15,15 @@ kvs_decode_step -- over one decode token:
     top-64; one query = one decode token through all 32 layers (32 kvs_decode_step calls).
 Inputs are seeded synthetic fp16 (kvsynth) and resident in HBM before timing.  To keep repeated
 steps from being served by the 256 MB Infinity Cache, a 128K step cycles through 16 cache replicas
-(8 GiB); a 1M step touches 2.7 GB of distinct memory anyway.  Steps are captured once into a HIP
-graph and replayed; HIP events on the launch stream time exactly K steps.
+(1.1 GB); a 1M step touches 2.7 GB of distinct memory anyway.  Steps are captured once into a HIP
+graph and replayed; HIP events on the replay stream time exactly K steps.
 
 Roofline: algorithmic bytes per step = q + reps of every candidate block + K and V of every attended
-token of every KV head + out, over the step time, against 8 TB/s.
+token of every KV head + out, over the step time, against 8 TB/s.  The unit is one kvs_decode_step
+call (its four kernels); profiles/ holds the per-kernel rocprofv3 averages of the same command.
+traffic: HBM bytes per step from rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/), each scaled by what
+the counter reads for the 4 GiB device copy timed at the start of every run; null when the kernels'
+sources changed since the counters were taken.
 cpu_baseline: the fp64 CPU oracle (single thread) on the same inputs, reps prebuilt, timed over a
 bounded number of queries.
 """
@@ -60,6 +67,47 @@ def regions(L, I, W):
         return L, L, 0
     lloc = max(ib, B * math.floor((L - W) / B))
     return ib, lloc, (lloc - ib) // B
+
+
+STEP_KERNELS = ("score_kernel", "topk_il_kernel", "topk_kernel", "attn_tiles_kernel", "merge_kernel")
+COPY_BYTES = 4 << 30  # the device copy of copy_bandwidth(): read and written once per dispatch
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the C header: the kernels the counters were taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_kv_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    for f in files + [os.path.join(ROOT, "include", "kvs.h")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_kv_file(path):
+    """`key: value` lines of a profiles/ summary (other lines ignored)."""
+    out = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#", "|")):
+                k, v = ln.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
+def traffic_per_step(name):
+    """HBM bytes per step from profiles/decode_step_<name>_traffic.txt, or None if absent or taken
+    on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_step_{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = read_kv_file(path)
+    if kv.get("source_hash") != source_hash():
+        return None
+    return float(kv["hbm_bytes_per_step"])
 
 
 def required_bytes(w):
@@ -225,10 +273,127 @@ def measure(name, steps, warmup, device):
                queries_per_s=1.0 / step_s, required_bytes_per_step=per_step,
                required_bytes_per_layer=per_layer, hbm_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
                attended_tokens=rb["tokens"], candidates=rb["ncand"], k_eff=rb["k_eff"],
-               setup=st)
+               traffic_bytes_per_step=traffic_per_step(name), setup=st)
     log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
         f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
     return res
+
+
+# ------------------------------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ summaries
+# ------------------------------------------------------------------------------------------------
+def _step_kernel(name):
+    base = name.split("(")[0].split("<")[0].replace("void ", "").strip()
+    return base.replace("kvs::", "") if base.replace("kvs::", "") in STEP_KERNELS else None
+
+
+def _bench_line(log_path):
+    if log_path and os.path.exists(log_path):
+        with open(log_path) as f:
+            for ln in f:
+                if ln.startswith("[bench]") and "us/step" in ln:
+                    return ln.strip()
+    return "(bench log not given)"
+
+
+def summarize_stats(d, name, log_path=None):
+    """rocprofv3 --kernel-trace --stats CSV -> profiles/decode_step_<name>_kernel_stats.txt."""
+    import csv
+
+    w = WORKLOADS[name]
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    out, tot = [], 0.0
+    for r in rows:
+        k = _step_kernel(r["Name"])
+        if k is None:
+            continue
+        avg = float(r["AverageNs"]) / 1e3
+        tot += avg
+        out.append(f"| {k:18s} | {r['Name'][:60]:60s} | {int(r['Calls']):6d} | {avg:9.2f} | "
+                   f"{float(r['MinNs']) / 1e3:9.2f} | {float(r['MaxNs']) / 1e3:9.2f} |")
+    steps = "480"
+    txt = [f"# kvs_decode_step kernels, workload {name}",
+           "",
+           "command (repository root on the MI355X box; bench.py times the same calls):",
+           f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{name} -o run "
+           f"-- python3 bench.py --workload {name} --no-cpu --steps {steps}",
+           f"    python bench.py --summarize-stats gpurun_out/prof_{name} --workload {name} "
+           f"--log gpurun_out/prof_{name}.log",
+           "",
+           f"source_hash: {source_hash()}",
+           f"sum_of_kernel_averages_us_per_layer: {tot:.2f}",
+           f"bench_line_under_the_profiler: {_bench_line(log_path)}",
+           "",
+           "| kernel             | name                                                         |  calls |  avg us   |  min us   |  max us   |",
+           "|--------------------|--------------------------------------------------------------|--------|-----------|-----------|-----------|",
+           *out, ""]
+    path = os.path.join(ROOT, "profiles", f"decode_step_{name}_kernel_stats.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(txt))
+    print(path)
+
+
+def summarize_pmc(fetch_dir, write_dir, name):
+    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs -> profiles/decode_step_<name>_traffic.txt.
+    Each counter is scaled by what it reads for the 4 GiB copies of copy_bandwidth()."""
+    import csv
+    import collections
+
+    w = WORKLOADS[name]
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = collections.defaultdict(list)
+        copies = []
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0  # KiB per dispatch
+            if "copyBuffer" in r["Kernel_Name"]:
+                copies.append(v)
+            k = _step_kernel(r["Kernel_Name"])
+            if k is not None:
+                per[k].append(v)
+        big = max(copies)
+        cal = [v for v in copies if v >= 0.5 * big]  # the 4 GiB copies
+        scale = COPY_BYTES / (sum(cal) / len(cal))
+        res[counter] = (scale, {k: sum(v) / len(v) * scale for k, v in per.items()},
+                        {k: len(v) for k, v in per.items()}, len(cal))
+    rb = required_bytes(w)
+    req_layer = rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
+    fetch_layer = sum(res["FETCH_SIZE"][1].values())
+    write_layer = sum(res["WRITE_SIZE"][1].values())
+    steps = "32"
+    lines = [f"# HBM traffic of kvs_decode_step, workload {name}",
+             "",
+             "commands (repository root on the MI355X box), one counter per run:",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{name} -o run "
+             f"-- python3 bench.py --workload {name} --no-cpu --steps {steps} --warmup 2",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{name} -o run "
+             f"-- python3 bench.py --workload {name} --no-cpu --steps {steps} --warmup 2",
+             f"    python bench.py --summarize-pmc gpurun_out/pmc_fetch_{name} gpurun_out/pmc_write_{name} "
+             f"--workload {name}",
+             "",
+             "Calibration: each counter over the 4 GiB device copy that starts every bench.py run "
+             "(read 4 GiB, write 4 GiB).",
+             f"fetch_scale: {res['FETCH_SIZE'][0]:.4f}",
+             f"write_scale: {res['WRITE_SIZE'][0]:.4f}",
+             f"source_hash: {source_hash()}",
+             f"required_bytes_per_layer: {req_layer}",
+             f"fetch_bytes_per_layer: {fetch_layer:.0f}",
+             f"write_bytes_per_layer: {write_layer:.0f}",
+             f"hbm_bytes_per_step: {(fetch_layer + write_layer) * w['layers']:.0f}",
+             f"traffic_over_required: {(fetch_layer + write_layer) / req_layer:.4f}",
+             "",
+             "| kernel             | dispatches | fetch bytes (scaled) | write bytes (scaled) |",
+             "|--------------------|------------|----------------------|----------------------|"]
+    for k in STEP_KERNELS:
+        if k in res["FETCH_SIZE"][1]:
+            lines.append(f"| {k:18s} | {res['FETCH_SIZE'][2][k]:10d} | {res['FETCH_SIZE'][1][k]:20.0f} | "
+                         f"{res['WRITE_SIZE'][1].get(k, 0.0):20.0f} |")
+    path = os.path.join(ROOT, "profiles", f"decode_step_{name}_traffic.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def main():
@@ -238,7 +403,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all", choices=["all", *WORKLOADS])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--summarize-stats", metavar="DIR", help="rocprofv3 --stats output -> profiles/")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs -> profiles/")
+    ap.add_argument("--log", help="bench output captured under the profiler (for --summarize-stats)")
     args = ap.parse_args()
+    if args.summarize_stats or args.summarize_pmc:
+        if args.workload == "all":
+            ap.error("--summarize-* needs --workload")
+        if args.summarize_stats:
+            summarize_stats(args.summarize_stats, args.workload, args.log)
+        if args.summarize_pmc:
+            summarize_pmc(*args.summarize_pmc, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block-sparse decode path is built and timed on a "
               "single MI355X (sharding is design-only); run with --gpus 1", file=sys.stderr)
@@ -284,12 +461,14 @@ def main():
                    "initial": w["I"], "local": w["W"], "replicas": w["replicas"]},
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["frac"],
-                     "traffic": None,
-                     "kernel": "decode_step_kernel (persistent: score + top-k + attention + merge)",
-                     "bytes_per_launch": head["required_bytes_per_layer"]},
+                     "traffic": traffic_per_step(names[0]),
+                     "kernel": "kvs_decode_step (score, top-k + Initial/Local tiles, selected "
+                               "tiles, merge)",
+                     "bytes_per_launch": head["required_bytes_per_step"]},
         "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,
         "frac_of_copy": head["hbm_gbs"] / copy_gbs,
+        "source_hash": source_hash(),
         "workloads": {k: {kk: vv for kk, vv in v.items() if kk != "setup"}
                       for k, v in results.items()},
     }
