@@ -43,27 +43,25 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
   const uint16_t* Kt = k_pool + off;
   const uint16_t* Vt = v_pool + off;
-  // every load is issued up front, in the order the data is needed: Q, K, then V
+  // Every load is issued up front, in the order the data is needed -- Q, K, then V -- and without
+  // branches, so the compiler keeps them all in flight and waits only for what the next step needs.
+  // Rows past ntok are still inside the tile's 32 KiB: their K only feeds logits that are masked,
+  // their V is zeroed after the load (a NaN tail times p = 0 would not be 0).
   half8_t qb[4];  // Q^T B operand: lane l holds head lc, channels 32m + 8*lq .. +8
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (lc < G) v = *reinterpret_cast<const uint4*>(q_h + (size_t)lc * kDim + 32 * m + 8 * lq);
-    qb[m] = __builtin_bit_cast(half8_t, v);
+    const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * m + 8 * lq);
+    qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
   }
   uint4 kr[2][4], vr[8];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int tok = 32 * w + 16 * g + lc;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      kr[g][m] = tok < ntok ? ld_stream16(Kt + tok * kDim + 32 * m + 8 * lq) : make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + tok * kDim + 32 * m + 8 * lq);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tok = 32 * w + 4 * i + lq;
-    vr[i] = tok < ntok ? ld_stream16(Vt + tok * kDim + 8 * lc) : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
   f32x4_t S[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -101,7 +99,10 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   // V to LDS: chunk i holds the wave's tokens 4i..4i+3, row stride 256 B
   unsigned char* vbuf = smem + w * kWaveVBytes;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(vbuf + i * 1056 + lq * 256 + lc * 16) = vr[i];
+  for (int i = 0; i < 8; ++i) {
+    const bool in = 32 * w + 4 * i + lq < ntok;
+    *reinterpret_cast<uint4*>(vbuf + i * 1056 + lq * 256 + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -174,16 +175,16 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
   float2 ml0[R0];
   const int m0 = min(n_max, kMergeChunk);
 #pragma unroll
-  for (int r = 0; r < R0; ++r) {
+  for (int r = 0; r < R0; ++r) {  // clamped indices, no branches: all loads in flight together
     const int s = tid + 256 * r;
-    ml0[r] = s < m0 ? *reinterpret_cast<const float2*>(part_ml + (size_t)s * 2) : make_float2(-INFINITY, 0.f);
+    ml0[r] = *reinterpret_cast<const float2*>(part_ml + (size_t)min(s, m0 - 1) * 2);
   }
   float4 o0[U0];
   const int f0 = min(n_max, kMergeFirst);
 #pragma unroll
   for (int u = 0; u < U0; ++u) {
     const int s = grp + 8 * u;
-    o0[u] = s < f0 ? *reinterpret_cast<const float4*>(part_o + (size_t)s * kDim + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    o0[u] = *reinterpret_cast<const float4*>(part_o + (size_t)min(s, f0 - 1) * kDim + c4);
   }
   float M = -INFINITY, Lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -289,22 +290,28 @@ __device__ inline void empty_partial(float* part_o, float* part_ml, int n_parts,
 template <int G, bool IL, bool PHYS>
 __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int seq, unsigned char* smem) {
   const Params& P = A.P;
+  const bool is_il = IL && x < A.n_il_max;
+  const int i = IL ? x - A.n_il_max : x;  // selected index when !is_il
+  const size_t grow = (size_t)seq * P.G + (P.mode == kSeparate ? h : 0);
+  // the loads that do not depend on the length first
   const int L = A.seq_lens[seq];
+  int cnt = 0, v = -1;
+  if (P.topk > 0) {
+    cnt = A.sel_count[grow];
+    v = A.sel[grow * P.topk + (is_il ? 0 : i)];
+  }
   const TileList tl = tiles_of(L, P, 0);
   const int n_il = tl.nI + tl.nLoc;
   const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
   int phys, ntok, part;
-  if (IL && x < A.n_il_max) {
+  if (is_il) {
     if (x >= n_il) return;
     const int2 t = il_tile(tl, x);
     phys = t.x < A.max_blocks ? trow[t.x] : -1;
     ntok = t.y;
     part = x;
   } else {
-    const int i = IL ? x - A.n_il_max : x;
-    if (i >= sel_k_of(A, seq, h, L)) return;
-    const size_t grow = (size_t)seq * P.G + (P.mode == kSeparate ? h : 0);
-    const int v = A.sel[grow * P.topk + i];
+    if (i >= tiles_of(L, P, cnt).k) return;
     if (PHYS) phys = v;
     else phys = v >= 0 && v < A.max_blocks ? trow[v] : -1;
     ntok = kBlock;

@@ -51,6 +51,9 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
     for (int j = 0; j < G; ++j) qs[e] += qf[j][e];
   }
 
+  // Loads that must be in flight together are issued without branches: indices are clamped to valid
+  // ones (a non-candidate reads physical block 0) and the results are masked afterwards, so the
+  // compiler places no wait between them.
   for (int base = b0; base < b0 + nb; base += bpp * kScorePasses) {
     int blk[kScorePasses];
     bool inr[kScorePasses], cand[kScorePasses];
@@ -60,12 +63,12 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
       blk[p] = base + p * bpp + slot;
       inr[p] = blk[p] < b0 + nb && blk[p] < max_blocks;
       cand[p] = inr[p] && blk[p] >= rg.cand_lo && blk[p] < rg.cand_hi;
-      phys[p] = cand[p] ? (size_t)trow[blk[p]] : 0;
+      const int t = trow[min(blk[p], max_blocks - 1)];
+      phys[p] = cand[p] ? (size_t)t : 0;
     }
     uint4 raw[kScorePasses][RMAX];
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
-      if (!cand[p]) continue;
       if constexpr (METHOD == kQuest) {
         const uint16_t* rp = static_cast<const uint16_t*>(rep_pool) + (phys[p] * Hkv + h) * 2 * kDim + c * 8;
         raw[p][0] = ld_stream16(rp);
@@ -83,7 +86,6 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
       acc[p] = 0.f;
-      if (!cand[p]) continue;
       if constexpr (METHOD == kQuest) {
         float kmin[8], kmax[8];
         unpack8(raw[p][0], kmin);
@@ -103,11 +105,18 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
         } else {
           unpack8(raw[p][0], rs);
           const uint16_t* rp = static_cast<const uint16_t*>(rep_pool) + (phys[p] * Hkv + h) * (size_t)P.R * kDim + c * 8;
-          for (int r = 1; r < P.R; ++r) {  // Fix: sum of the rep rows, then one dot
-            float f[8];
-            unpack8(ld_stream16(rp + (size_t)r * kDim), f);
+          for (int r0 = 1; r0 < P.R; r0 += 8) {  // Fix: sum of the rep rows (8 loads in flight), then one dot
+            uint4 x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rs[e] += f[e];
+            for (int u = 0; u < 8; ++u) x[u] = ld_stream16(rp + (size_t)(r0 + u < P.R ? r0 + u : 0) * kDim);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              float f[8];
+              unpack8(x[u], f);
+              const bool ok = r0 + u < P.R;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) rs[e] += ok ? f[e] : 0.f;
+            }
           }
         }
 #pragma unroll
