@@ -1,7 +1,8 @@
 // Attention kernels over the per-tile work items of attn_core.h:
 //  * attn_tiles_kernel: workgroup (x, h, seq) is one attended tile of KV head h -- the x-th
 //    Initial/Local tile, or a selected one -- and writes one partial per query head of h;
-//  * merge_kernel: workgroup (j, seq) folds the partials of query head j into out.
+//  * merge_kernel: workgroup (j * 4 + q, seq) folds channels [32q, 32q + 32) of query head j's
+//    partials into out.
 // kvs_sparse_decode_attn runs both (Initial/Local and selected tiles in one grid, selections as logical
 // ids); kvs_decode_step runs them with the selections as physical ids, the Initial/Local tiles here
 // or in its top-k launch (step.hip).
@@ -18,7 +19,8 @@ __global__ __launch_bounds__(256) void attn_tiles_kernel(AttnArgs A) {
 
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) float lds[kMergeLdsFloats];
-  merge_item(A, blockIdx.x, blockIdx.y, lds);
+  constexpr int Q = kDim / kMergeCh;
+  merge_item(A, blockIdx.x / Q, blockIdx.x % Q, blockIdx.y, lds);
 }
 
 AttnPlan attn_plan(const Params& P, int batch, int max_blocks) {
@@ -59,7 +61,7 @@ hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phy
 }
 
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(A.P.Hq, batch), dim3(256), 0, s, A);
+  hipLaunchKernelGGL(merge_kernel, dim3(A.P.Hq * (kDim / kMergeCh), batch), dim3(256), 0, s, A);
   return hipGetLastError();
 }
 

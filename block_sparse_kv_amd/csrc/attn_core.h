@@ -155,27 +155,32 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 
 constexpr int kMergeChunk = 1024;  // partials whose (max, sum) pairs sit in LDS at once
 constexpr int kMergeFirst = 128;   // partials whose outputs are loaded before their count is known
-constexpr int kMergeLdsFloats = 2 * kMergeChunk + 8 * kDim + 16;
+constexpr int kMergeCh = 32;       // output channels one merge workgroup covers
+constexpr int kMergeLdsFloats = 2 * kMergeChunk + 256 * 4 + 16;
 
-// Log-sum-exp merge of the n (<= n_max) partials of one query head into out[128], by 256 lanes:
+// Log-sum-exp merge of channels [ch0, ch0 + kMergeCh) of one query head over its n (<= n_max)
+// partials, by 256 lanes:
 //   out = sum_s exp2(m_s - M) o_s / sum_s exp2(m_s - M) l_s,  M = max_s m_s.
-// The loads that do not depend on n -- the (max, sum) pairs of the first chunk and the outputs of the
-// first kMergeFirst partials -- are issued first, so they travel with the loads that produce n.
-// Chunks of kMergeChunk partials keep a running (M, sum, accumulator) state; each lane owns 4
-// channels of one of 8 partial groups, and the 8 groups fold in LDS.  n == 0 gives zeros.
+// Lane t owns 4 channels (t % 8) of partial group t / 8 (32 groups).  The loads that do not depend on
+// n -- the (max, sum) pairs of the first chunk and the first kMergeFirst partials' outputs -- are issued
+// first, with clamped indices and no branches, so they travel with the loads that produce n.  Chunks
+// of kMergeChunk partials keep a running (M, sum, accumulator) state; the 32 groups fold in LDS.
+// n == 0 gives zeros.
 __device__ inline void merge_head(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                  int n_max, int n, float* __restrict__ out, float* lds) {
+                                  int n_max, int n, int ch0, float* __restrict__ out, float* lds) {
+  constexpr int TPR = kMergeCh / 4;  // lanes per partial row
+  constexpr int PG = 256 / TPR;      // partial groups
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* wts = lds;                  // [kMergeChunk]: max, then weight
   float* sums = wts + kMergeChunk;   // [kMergeChunk]
-  float* fold = sums + kMergeChunk;  // [8][128]
-  float* red = fold + 8 * kDim;      // [8]
-  const int c4 = (tid & 31) * 4, grp = tid >> 5;
-  constexpr int R0 = kMergeChunk / 256, U0 = kMergeFirst / 8;
+  float* fold = sums + kMergeChunk;  // [PG][kMergeCh]
+  float* red = fold + 256 * 4;       // [8]
+  const int c4 = ch0 + (tid % TPR) * 4, grp = tid / TPR;
+  constexpr int R0 = kMergeChunk / 256, U0 = kMergeFirst / PG;
   float2 ml0[R0];
   const int m0 = min(n_max, kMergeChunk);
 #pragma unroll
-  for (int r = 0; r < R0; ++r) {  // clamped indices, no branches: all loads in flight together
+  for (int r = 0; r < R0; ++r) {
     const int s = tid + 256 * r;
     ml0[r] = *reinterpret_cast<const float2*>(part_ml + (size_t)min(s, m0 - 1) * 2);
   }
@@ -183,7 +188,7 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
   const int f0 = min(n_max, kMergeFirst);
 #pragma unroll
   for (int u = 0; u < U0; ++u) {
-    const int s = grp + 8 * u;
+    const int s = grp + PG * u;
     o0[u] = *reinterpret_cast<const float4*>(part_o + (size_t)min(s, f0 - 1) * kDim + c4);
   }
   float M = -INFINITY, Lsum = 0.f;
@@ -230,45 +235,35 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
     if (c0 == 0) {
 #pragma unroll
       for (int u = 0; u < U0; ++u) {
-        const int s = grp + 8 * u;
+        const int s = grp + PG * u;
         if (s < cn) fma4(o0[u], wts[s]);
       }
       s_from = kMergeFirst;
     }
-    for (int s0 = s_from + grp; s0 < cn; s0 += 8 * 8) {  // the rest, 8 loads in flight
+    for (int s0 = s_from + grp; s0 < cn; s0 += 8 * PG) {  // the rest, 8 loads in flight
       float4 o[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int s = s0 + 8 * u;
-        o[u] = s < cn ? *reinterpret_cast<const float4*>(part_o + (size_t)(c0 + s) * kDim + c4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int s = min(s0 + PG * u, cn - 1);
+        o[u] = *reinterpret_cast<const float4*>(part_o + (size_t)(c0 + s) * kDim + c4);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int s = s0 + 8 * u;
+        const int s = s0 + PG * u;
         if (s < cn) fma4(o[u], wts[s]);
       }
     }
     Lsum = Lsum * resc + red[4] + red[5] + red[6] + red[7];
     __syncthreads();  // red[] and wts[] are rewritten by the next chunk
   }
-  *reinterpret_cast<float4*>(fold + grp * kDim + c4) = acc;
+  *reinterpret_cast<float4*>(fold + grp * kMergeCh + (c4 - ch0)) = acc;
   __syncthreads();
-  if (tid < kDim) {
+  if (tid < kMergeCh) {
     float a = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) a += fold[g * kDim + tid];
-    out[tid] = Lsum > 0.f ? a / Lsum : 0.f;
+#pragma unroll 8
+    for (int g = 0; g < PG; ++g) a += fold[g * kMergeCh + tid];
+    out[ch0 + tid] = Lsum > 0.f ? a / Lsum : 0.f;
   }
-}
-
-// Selected blocks attended by (sequence, KV head h): the group's count, clamped to [0, topk], and 0
-// when the sequence is all Initial.
-__device__ inline int sel_k_of(const AttnArgs& A, int seq, int h, int L) {
-  const Params& P = A.P;
-  if (P.topk <= 0) return 0;
-  const size_t grow = (size_t)seq * P.G + (P.mode == kSeparate ? h : 0);
-  return tiles_of(L, P, A.sel_count[grow]).k;
 }
 
 // Writes an empty partial (max -inf, sum 0, zero output) for the g query heads of a tile that names
@@ -327,15 +322,16 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
   attn_tile<G>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
 }
 
-// Merge of query head j of sequence seq over its n_il + k partials into out.
-__device__ inline void merge_item(const AttnArgs& A, int j, int seq, float* lds) {
+// Merge of channel quarter q4 of query head j of sequence seq over its n_il + k partials into out.
+__device__ inline void merge_item(const AttnArgs& A, int j, int q4, int seq, float* lds) {
   const Params& P = A.P;
   const int L = A.seq_lens[seq];
-  const TileList tl = tiles_of(L, P, 0);
-  const int n = tl.nI + tl.nLoc + sel_k_of(A, seq, j / P.g, L);
+  const int cnt = P.topk > 0 ? A.sel_count[(size_t)seq * P.G + (P.mode == kSeparate ? j / P.g : 0)] : 0;
+  const TileList tl = tiles_of(L, P, cnt);
+  const int n = tl.nI + tl.nLoc + tl.k;
   const size_t hp = (size_t)seq * P.Hq + j;
   merge_head(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, A.max_parts, n,
-             A.out + hp * kDim, lds);
+             q4 * kMergeCh, A.out + hp * kDim, lds);
 }
 
 }  // namespace kvs
