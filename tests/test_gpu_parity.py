@@ -115,6 +115,14 @@ def test_small_cases(idx):
     run_full_check(case, f"small {rep}/{mode} {Hq}x{Hkv}")
 
 
+def test_batch_odd_counts():
+    """A batch of four 9K-33K sequences (over a thousand attended tiles in one call) with an odd k,
+    odd Initial/Local counts and a partial last block."""
+    c = cfg_of(32, 8, 128, 4096, 31, "quest", "separate")
+    case = Case(c, [32768, 20000, 9000, 30001], seed=kvsynth.mix_seed(7, 99), n_hot=4)
+    run_full_check(case, "batch of 4, odd counts")
+
+
 def test_exact_ties_take_lower_index():
     """Eleven identical blocks planted far above the rest (bitwise-equal scores); k = 5 cuts the tie
     group, so exactly its five lowest ids must be chosen, as the oracle does."""
