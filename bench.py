@@ -155,7 +155,7 @@ class Setup:
         log(f"[setup] {name}: {n_units} cache units of {L} tokens generated in {time.time() - t0:.1f}s")
         self.out = torch.empty((1, w["Hq"], D), dtype=torch.float32, device=device)
         self.ws_bytes = kvs.kvs_decode_step_workspace_size(self.cfg, 1, nb)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)  # counters start at 0
         self.sel = torch.empty((1, self.cfg.groups, w["k"]), dtype=torch.int32, device=device)
         self.cnt = torch.empty((1, self.cfg.groups), dtype=torch.int32, device=device)
         self.nb = nb

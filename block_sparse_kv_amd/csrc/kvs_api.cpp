@@ -13,6 +13,7 @@ namespace {
 using kvs::Params;
 
 constexpr size_t kAlign = 256;  // sub-buffers of a workspace start on 256-byte boundaries
+constexpr size_t kCtrBytes = 65536;  // decode-step hand-off counters: batch * G <= 16384
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -94,17 +95,18 @@ AttnLayout attn_layout(const Params& P, int batch, int max_blocks) {
   return a;
 }
 
-// Workspace of the decode step: scores, the selection (when the caller does not take it), the
-// selected tiles' physical ids, then the attention partials.
+// Workspace of the decode step: hand-off counters (zero between calls), scores, the selection (when
+// the caller does not take it), the selected tiles' physical ids, then the attention partials.
 struct StepLayout {
   AttnLayout attn;
-  size_t scores_off, sel_off, cnt_off, tiles_off, attn_off, total;
+  size_t ctr_off, scores_off, sel_off, cnt_off, tiles_off, attn_off, total;
 };
 
 StepLayout step_layout(const Params& P, int batch, int max_blocks) {
   StepLayout s;
   const size_t nsel = (size_t)batch * P.G * (P.topk > 0 ? P.topk : 1) * sizeof(int32_t);
   size_t off = 0;
+  s.ctr_off = off;    off += kCtrBytes;  // fixed, so every call finds its counters in the zeroed area
   s.scores_off = off; off += round_up((size_t)batch * P.G * max_blocks * sizeof(float));
   s.sel_off = off;    off += round_up(nsel);
   s.cnt_off = off;    off += round_up((size_t)batch * P.G * sizeof(int32_t));
@@ -266,6 +268,7 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
     return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
     return KVS_ERR_MISALIGNED;
+  if ((size_t)batch * P.G * sizeof(int) > kCtrBytes) return KVS_ERR_UNSUPPORTED;
   const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
   if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
@@ -278,7 +281,8 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
                               seq_lens, tiles, cnt, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles, batch, s),
+  return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles,
+                                            at<int>(workspace, S.ctr_off), batch, s),
                     "kvs_decode_step");
 }
 

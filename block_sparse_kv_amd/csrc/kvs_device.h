@@ -125,6 +125,23 @@ __device__ inline uint4 ld_stream16(const void* p) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- hand-off between workgroups of one kernel ----------------------------------------------------
+// The per-XCD L2 caches are not coherent with each other.  Data one workgroup hands to another of the
+// same kernel is written with device-scope stores that write through to the coherence point (sc1),
+// the writer waits for their completion (vmcnt 0) before it bumps a counter, and the reader loads
+// with the same cache policy, so it sees the data whichever XCD it runs on.
+template <typename T>
+__device__ inline void st_coh(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+constexpr int kSc1 = 16;  // cache-policy operand of the raw buffer loads: sc1
+__device__ inline __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ inline float ld_coh_f1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSc1));
+}
+// Wait until this wave's memory operations have completed (vmcnt 0).
+__device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // exp2(a - b) that is 0 when a is -inf (an empty stream), never NaN.
 __device__ inline float exp2_diff(float a, float b) { return a == -INFINITY ? 0.f : fast_exp2(a - b); }
 

@@ -34,8 +34,9 @@ hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_
 hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s);
 // The whole decode step (step.hip): scores [batch][G][max_blocks], sel / sel_count, and the selected
-// tiles' physical ids (tiles [batch][G][topk]) are its intermediates; A.sel must be `tiles`.
+// tiles' physical ids (tiles [batch][G][topk]) are its intermediates; A.sel must be `tiles`.  ctr:
+// [batch][G] ints, zero when the call starts and zero again when it ends.
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                              int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s);
+                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s);
 
 }  // namespace kvs

@@ -5,8 +5,9 @@
 //
 // Lane layout: 16 lanes (one DPP row) per (logical block, KV head); lane c owns channels 8c..8c+7 and
 // keeps the matching slice of the g query heads of its KV head in registers.  256 lanes cover
-// 16/Hkv blocks x Hkv heads per pass; up to 4 passes are issued together (table entries first, then
-// all rep loads) so one item pays the memory latency about twice, not once per pass.  Reps are read
+// 16/Hkv blocks x Hkv heads per pass (or, PER_HEAD, 16 blocks of one KV head); 4 passes are issued
+// together (table entries first, then all rep loads) so one workgroup pays the memory latency about
+// twice, not once per pass.  Reps are read
 // with 128-bit loads (a 16-lane row reads one 256 B fp16 rep row).  For the linear reps (Max, Mean,
 // Fix) the g query heads are summed first, since sum_j q_j.rep = (sum_j q_j).rep; Quest is per head
 // (the max is not linear).
@@ -18,22 +19,28 @@ namespace kvs {
 
 constexpr int kScorePasses = 4;  // passes whose loads are in flight together
 
-// Blocks one scoring workgroup covers: kScorePasses passes of 16/Hkv blocks.
+// Blocks one scoring workgroup covers: kScorePasses passes of 16/Hkv blocks (all KV heads), or of 16
+// blocks (one KV head).
 __host__ __device__ inline int score_blocks_per_wg(const Params& P) { return (16 / P.Hkv) * kScorePasses; }
+constexpr int kScoreBlocksPerHeadWg = 16 * kScorePasses;
 
-// Scores of logical blocks [b0, b0 + nb) of one sequence (cache length L).  Non-candidates get
-// -INFINITY.  scores_row: SEPARATE -> [Hkv][max_blocks] rows of this sequence, SHARED -> [max_blocks].
-template <int G, int METHOD, int MODE>
+// Scores of logical blocks [b0, b0 + nb) of one sequence (cache length L): of every KV head, or with
+// PER_HEAD (SEPARATE only) of KV head h_one.  Non-candidates get -INFINITY.  scores_row: SEPARATE ->
+// [Hkv][max_blocks] rows of this sequence, SHARED -> [max_blocks].  COH: the scores are stored for a
+// workgroup of the same kernel (st_coh).
+template <int G, int METHOD, int MODE, bool PER_HEAD = false, bool COH = false>
 __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16_t* __restrict__ q_seq,
                                           const void* __restrict__ rep_pool,
                                           const int32_t* __restrict__ trow, int max_blocks, int L,
                                           int b0, int nb, float* __restrict__ scores_row,
-                                          float* lds_part /* >= 16 * kScorePasses floats */) {
+                                          float* lds_part /* >= 16 * kScorePasses floats */,
+                                          int h_one = 0) {
+  static_assert(!(PER_HEAD && MODE == kShared), "a SHARED score sums over every KV head");
   const int Hkv = P.Hkv;
   const int t = threadIdx.x, c = t & 15;
-  const int h = (t >> 4) % Hkv;
-  const int bpp = 16 / Hkv;  // blocks per pass
-  const int slot = (t >> 4) / Hkv;
+  const int h = PER_HEAD ? h_one : (t >> 4) % Hkv;
+  const int bpp = PER_HEAD ? 16 : 16 / Hkv;  // blocks per pass
+  const int slot = PER_HEAD ? t >> 4 : (t >> 4) / Hkv;
   const Regions rg = regions_of(L, P.initial_len, P.local_len);
   constexpr int RMAX = METHOD == kQuest ? 2 : (METHOD == kMean ? 2 : 1);  // 16-byte loads per pass
 
@@ -131,7 +138,9 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
 #pragma unroll
         for (int p = 0; p < kScorePasses; ++p) {
           if (!inr[p]) continue;
-          scores_row[(size_t)h * max_blocks + blk[p]] = cand[p] ? acc[p] : -INFINITY;
+          float* dst = scores_row + (size_t)h * max_blocks + blk[p];
+          const float v = cand[p] ? acc[p] : -INFINITY;
+          if constexpr (COH) st_coh(dst, v); else *dst = v;
         }
       }
     } else {
@@ -146,7 +155,8 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
           if (!inr[p]) continue;
           float s = 0.f;
           for (int hh = 0; hh < Hkv; ++hh) s += lds_part[p * 16 + slot * Hkv + hh];
-          scores_row[blk[p]] = cand[p] ? s : -INFINITY;
+          const float v = cand[p] ? s : -INFINITY;
+          if constexpr (COH) st_coh(scores_row + blk[p], v); else scores_row[blk[p]] = v;
         }
       }
       __syncthreads();

@@ -1,13 +1,16 @@
 // kvs_decode_step: scoring -> top-k -> attention tiles -> merge, with the Initial/Local tiles -- which
 // do not depend on the selection [KT-LC §4.2] -- placed where their K/V gather costs least:
-//  * short rows (max_blocks <= kStepTopkSmall): in the top-k launch (topk_il_kernel).  Their gather
-//    then runs while the few top-k workgroups -- one per (sequence, group), 256 lanes, keys in
-//    registers -- choose the blocks;
-//  * long rows: in the selected-tile launch, whose stream they lengthen by their bytes only, while
-//    top-k gets 1024-lane workgroups (topk.hip).
+//  * short rows (max_blocks <= kStepTopkSmall): one launch scores, selects and gathers the
+//    Initial/Local tiles (score_select_kernel).  The scoring workgroups of a (sequence, group) hand
+//    their scores to the one among them that finishes last, which makes the group's selection (256
+//    lanes, keys in registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles
+//    and the merge (attn.hip).
+//  * long rows: scoring (score.hip), top-k in 1024-lane workgroups (topk.hip), then the
+//    Initial/Local and selected tiles together, then the merge.
 // In every grid an attention tile is one workgroup (attn_core.h).
 #include "attn_core.h"
 #include "kvs_launch.h"
+#include "score_core.h"
 #include "topk_core.h"
 
 namespace kvs {
@@ -16,49 +19,98 @@ constexpr int kStepTopkKeys = 8;  // keys per lane of the 256-lane selections
 constexpr int kStepTopkSmall = 256 * kStepTopkKeys;
 constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
 
-template <int G>
-__global__ __launch_bounds__(256) void topk_il_kernel(AttnArgs A, const float* __restrict__ scores,
-                                                      int32_t* __restrict__ sel,
-                                                      int32_t* __restrict__ sel_count,
-                                                      int32_t* __restrict__ tiles, int n_topk) {
+// Workgroups [0, n_il_wg): Initial/Local tiles, tile t of KV head h of sequence seq at
+// (seq * Hkv + h) * n_il_max + t.  Then the scoring workgroups, n_sc per (sequence, group): over every
+// KV head (SHARED) or over one KV head (SEPARATE; group = KV head).  A scoring workgroup stores its
+// scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
+// to n_sc resets it and selects.  Nothing waits on another workgroup.
+template <int G, int METHOD, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void score_select_kernel(
+    AttnArgs A, const void* __restrict__ rep_pool, float* __restrict__ scores, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int n_sc,
+    int n_il_wg) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
+  __shared__ int s_last;
   const Params& P = A.P;
   const int x = blockIdx.x;
-  if (x < n_topk) {
-    topk_group<256, kStepTopkKeys>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles,
-                                   x / P.G, x % P.G, *reinterpret_cast<TopkLds*>(smem));
-  } else {
-    const int y = x - n_topk;
+  if (x < n_il_wg) {
     const int per_seq = P.Hkv * A.n_il_max;
-    const int r = y % per_seq;
-    attn_item<G, true, false>(A, r % A.n_il_max, r / A.n_il_max, y / per_seq, smem);
+    const int r = x % per_seq;
+    attn_item<G, true, false>(A, r % A.n_il_max, r / A.n_il_max, x / per_seq, smem);
+    return;
+  }
+  constexpr bool SEP = MODE == kSeparate;
+  const int y = x - n_il_wg;
+  const int per_seq = P.G * n_sc;
+  const int seq = y / per_seq, grp = (y % per_seq) / n_sc, c = y % n_sc;
+  const int sb = SEP ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
+  score_blocks_range<G, METHOD, MODE, SEP, true>(P, A.q + (size_t)seq * P.Hq * kDim, rep_pool,
+                                                 A.table + (size_t)seq * A.max_blocks, A.max_blocks,
+                                                 A.seq_lens[seq], c * sb, sb,
+                                                 scores + (size_t)seq * P.G * A.max_blocks,
+                                                 reinterpret_cast<float*>(smem), grp);
+  wait_mem();
+  __syncthreads();
+  int* cp = ctr + (size_t)seq * P.G + grp;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_sc - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) st_coh(cp, 0);  // every scoring workgroup of the group has arrived
+  topk_group<256, kStepTopkKeys, true>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table,
+                                       tiles, seq, grp, *reinterpret_cast<TopkLds*>(smem));
+}
+
+template <int G, int METHOD>
+static void launch_ss_m(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
+                        int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
+  if (A.P.mode == kSeparate)
+    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate>), grid, dim3(256), 0, s, A, reps,
+                       scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+  else
+    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kShared>), grid, dim3(256), 0, s, A, reps,
+                       scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+}
+
+template <int G>
+static void launch_ss_g(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
+                        int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
+  switch (A.P.method) {
+    case kQuest: launch_ss_m<G, kQuest>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case kMax: launch_ss_m<G, kMax>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case kMean: launch_ss_m<G, kMean>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    default: launch_ss_m<G, kFix>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
   }
 }
 
-hipError_t launch_topk_il(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
-                          int32_t* tiles, int batch, hipStream_t s) {
-  const int n_topk = A.P.G * batch;
-  const dim3 grid(n_topk + batch * A.P.Hkv * A.n_il_max), block(256);
-  switch (A.P.g) {
-    case 1: hipLaunchKernelGGL(topk_il_kernel<1>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
-    case 2: hipLaunchKernelGGL(topk_il_kernel<2>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
-    case 4: hipLaunchKernelGGL(topk_il_kernel<4>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
-    case 8: hipLaunchKernelGGL(topk_il_kernel<8>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
-    default: hipLaunchKernelGGL(topk_il_kernel<16>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk); break;
+static hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* scores,
+                                      int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int batch,
+                                      hipStream_t s) {
+  const Params& P = A.P;
+  const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
+  const int n_sc = (A.max_blocks + sb - 1) / sb;
+  const int n_il_wg = batch * P.Hkv * A.n_il_max;
+  const dim3 grid(n_il_wg + batch * P.G * n_sc);
+  switch (P.g) {
+    case 1: launch_ss_g<1>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case 2: launch_ss_g<2>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case 4: launch_ss_g<4>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case 8: launch_ss_g<8>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    default: launch_ss_g<16>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
   }
   return hipGetLastError();
 }
 
-
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                              int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s) {
+                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s) {
   const Params& P = A.P;
   int32_t* tl = P.topk > 0 ? tiles : nullptr;
-  hipError_t e = launch_score(P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
+  hipError_t e;
   if (A.max_blocks <= kStepTopkSmall) {
-    if (e == hipSuccess) e = launch_topk_il(A, scores, sel, sel_count, tl, batch, s);
+    e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s);
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   } else {
+    e = launch_score(P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
     if (e == hipSuccess)
       e = launch_topk(P, scores, A.seq_lens, batch, A.max_blocks, sel, sel_count, A.table, tl, s);
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, true, true, s);

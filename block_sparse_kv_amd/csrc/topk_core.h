@@ -259,8 +259,9 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
 // lane l of wave w holds indices w*64*KPT + 64*c + l (c < KPT).  The row, the table row (trow,
 // nullable) and *len are loaded together; candidates are the indices in [cand_lo, cand_hi) of the
 // length's regions.  Writes *cnt = k_eff, sel[0..k_eff) ascending (and tiles[] = their physical ids
-// when trow != nullptr), -1 in sel / tiles [k_eff, topk).
-template <int NT, int KPT>
+// when trow != nullptr), -1 in sel / tiles [k_eff, topk).  COH: the scores were stored by another
+// workgroup of the same kernel (st_coh) and are read with coherent loads.
+template <int NT, int KPT, bool COH = false>
 __device__ __forceinline__ void topk_group_reg(const float* row, int m, const int32_t* len,
                                                          int initial_len, int local_len, int topk,
                                                          TopkLds& S, int32_t* sel, int32_t* cnt,
@@ -281,7 +282,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   for (int c = 0; c < KPT; ++c) {
     const int i = ibase + 64 * c;
     const int ic = i < m ? i : 0;
-    v[c] = row[ic];
+    if constexpr (COH) v[c] = ld_coh_f1(coh_rsrc(row), ic * 4); else v[c] = row[ic];
     ph[c] = trow ? trow[ic] : 0;
   }
   const Regions rg = regions_of(*len, initial_len, local_len);
@@ -454,8 +455,9 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
 
 // The selection of group grp of sequence seq from the scores [batch][G][max_blocks]: sel (and, with a
 // table and tiles, the physical ids in tiles) [batch][G][topk] ascending and -1 padded,
-// sel_count [batch][G].  Rows of up to NT * KMAX blocks stay in registers.
-template <int NT, int KMAX>
+// sel_count [batch][G].  Rows of up to NT * KMAX blocks stay in registers.  COH (rows of up to
+// NT * KMAX blocks only): the scores come from another workgroup of the same kernel.
+template <int NT, int KMAX, bool COH = false>
 __device__ inline void topk_group(const Params& P, const float* __restrict__ scores,
                                   const int32_t* __restrict__ seq_lens, int max_blocks,
                                   int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
@@ -468,13 +470,14 @@ __device__ inline void topk_group(const Params& P, const float* __restrict__ sco
   const int32_t* trow = tiles && table ? table + (size_t)seq * max_blocks : nullptr;
   const int32_t* len = seq_lens + seq;
 #define KVS_TOPK_REG(KPT)                                                                            \
-  topk_group_reg<NT, KPT>(srow, max_blocks, len, P.initial_len, P.local_len, P.topk, S, out,         \
+  topk_group_reg<NT, KPT, COH>(srow, max_blocks, len, P.initial_len, P.local_len, P.topk, S, out,         \
                           sel_count + row, trow, tout)
   if (max_blocks <= NT * 4) { KVS_TOPK_REG(4); return; }
   if (KMAX >= 8 && max_blocks <= NT * 8) { KVS_TOPK_REG(8); return; }
   if (KMAX >= 16 && max_blocks <= NT * 16) { KVS_TOPK_REG(16); return; }
   if (KMAX >= 32 && max_blocks <= NT * 32) { KVS_TOPK_REG(32); return; }
 #undef KVS_TOPK_REG
+  if constexpr (COH) return;  // not reached: callers keep coherent rows within NT * KMAX blocks
   const int tid = threadIdx.x;
   const Regions rg = regions_of(*len, P.initial_len, P.local_len);
   const int n = max(0, min(rg.cand_hi, max_blocks) - rg.cand_lo);

@@ -59,8 +59,9 @@ def sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, seq_lens, sel, sel_c
 
 
 def step_workspace(cfg, batch, max_blocks, device) -> torch.Tensor:
-    """A kvs_decode_step workspace (scratch; no initialisation needed)."""
-    return workspace(B.kvs_decode_step_workspace_size(cfg, batch, max_blocks), device)
+    """A zero-filled kvs_decode_step workspace (its hand-off counters must start at zero)."""
+    n = max(B.kvs_decode_step_workspace_size(cfg, batch, max_blocks), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_lens, ws=None):

@@ -163,16 +163,21 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
 /*
  * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention
  * [KT-LC §4.6, retrieval then attention], enqueued as four kernels with no host synchronisation:
- *   1. scoring of every block;
- *   2. top-k per (sequence, group), which also resolves the selected blocks' physical ids;
- *   3. attention, one workgroup per (tile, KV head);  4. the log-sum-exp merge into out.
- * The Initial/Local tiles do not depend on the selection: for max_blocks_per_seq <= 2048 they run
- * in launch 2, beside the selections, otherwise in launch 3.
+ *   for max_blocks_per_seq <= 2048: 1. scoring, top-k per (sequence, group) by the scoring
+ *   workgroup of the group that finishes last, and the Initial/Local tiles' attention (they do not
+ *   depend on the selection), in one launch;  2. attention over the selected tiles;  3. the
+ *   log-sum-exp merge into out;
+ *   otherwise: 1. scoring;  2. top-k;  3. attention over the Initial/Local and selected tiles;
+ *   4. the merge.
+ * Top-k also resolves the selected blocks' physical ids.
  * Results equal kvs_score_blocks + kvs_topk_blocks + kvs_sparse_decode_attn on the same inputs.
  * Reps must be current for every candidate block (kvs_build_reps).  sel_out / sel_count_out
  * (nullable) receive the selection for reuse by later kvs_sparse_decode_attn calls.
- * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned, contents scratch;
- * calls sharing one workspace must not run concurrently (stream order is enough).
+ * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned.  Its first 64 KiB
+ * hold hand-off counters: zero-fill the workspace once before its first use (e.g. hipMemset); every
+ * call leaves the counters zero again, so the workspace can then be reused by any later call, of any
+ * config and size that fits.  The rest is scratch.  Calls sharing one workspace must not run
+ * concurrently (stream order is enough).  batch * G must not exceed 16384 (KVS_ERR_UNSUPPORTED).
  */
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
                     const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,

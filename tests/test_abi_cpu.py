@@ -131,6 +131,16 @@ def test_alignment_and_workspace_errors():
                                check=False) == B.KVS_ERR_MISALIGNED
 
 
+def test_decode_step_counter_limit():
+    """The decode step keeps one hand-off counter per (sequence, group) in a fixed 64 KiB area:
+    batch * G above 16384 is rejected before anything is enqueued."""
+    c = cfg(head_select_mode="separate")  # G = 8
+    A = ALIGNED
+    assert kvs.kvs_decode_step(c, A, A, A, A, A, 64, A, 2049, A, None, None, A, 1 << 40, stream=0,
+                               check=False) == B.KVS_ERR_UNSUPPORTED
+    assert kvs.kvs_decode_step_workspace_size(c, 2048, 64) >= 65536
+
+
 def test_workspace_grows_with_batch():
     c = cfg()
     a = kvs.kvs_decode_step_workspace_size(c, 1, 8192)

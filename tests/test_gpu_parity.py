@@ -123,6 +123,26 @@ def test_batch_odd_counts():
     run_full_check(case, "batch of 4, odd counts")
 
 
+def test_workspace_reused_across_calls():
+    """One zero-filled workspace serves consecutive decode steps of different configs and batch
+    sizes (its hand-off counters return to zero after every call): results equal those of fresh
+    workspaces, bitwise."""
+    cs = [cfg_of(32, 8, 128, 1024, 12, "max", "shared"), cfg_of(32, 8, 128, 1024, 9, "quest", "separate")]
+    cases = [Case(cs[0], [20000, 7000, 15000], seed=61, n_hot=3), Case(cs[1], [9000], seed=62, n_hot=3)]
+    reps = [build_all_reps(c) for c in cases]
+    size = max(kvs.kvs_decode_step_workspace_size(c.cfg, len(c.lens), c.pb.max_blocks) for c in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    for rnd in range(2):
+        for case, rp in zip(cases, reps):
+            pb, c = case.pb, case.cfg
+            fresh = ops.decode_step(c, pb.q, pb.k_pool, pb.v_pool, rp, pb.block_table, pb.seq_lens)
+            reused = ops.decode_step(c, pb.q, pb.k_pool, pb.v_pool, rp, pb.block_table, pb.seq_lens, ws=ws)
+            torch.cuda.synchronize()
+            for a, b in zip(fresh, reused):
+                assert torch.equal(a, b), (rnd, c.head_select_mode)
+    assert int(ws[:65536].count_nonzero()) == 0, "counters not back to zero"
+
+
 def test_exact_ties_take_lower_index():
     """Eleven identical blocks planted far above the rest (bitwise-equal scores); k = 5 cuts the tie
     group, so exactly its five lowest ids must be chosen, as the oracle does."""
