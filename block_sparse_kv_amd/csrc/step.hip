@@ -19,9 +19,10 @@ constexpr int kStepTopkKeys = 8;  // keys per lane of the 256-lane selections
 constexpr int kStepTopkSmall = 256 * kStepTopkKeys;
 constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
 
-// Workgroups [0, n_il_wg): Initial/Local tiles, tile t of KV head h of sequence seq at
-// (seq * Hkv + h) * n_il_max + t.  Then the scoring workgroups, n_sc per (sequence, group): over every
-// KV head (SHARED) or over one KV head (SEPARATE; group = KV head).  A scoring workgroup stores its
+// First the scoring workgroups, n_sc per (sequence, group), over every KV head (SHARED) or over one KV
+// head (SEPARATE; group = KV head): dispatched first, their few loads are not queued behind the
+// tiles' stream.  Then n_il_wg Initial/Local tiles, tile t of KV head h of sequence seq at
+// (seq * Hkv + h) * n_il_max + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
 template <int G, int METHOD, int MODE>
@@ -32,15 +33,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_last;
   const Params& P = A.P;
+  const int n_score_wg = (int)gridDim.x - n_il_wg;
   const int x = blockIdx.x;
-  if (x < n_il_wg) {
+  if (x >= n_score_wg) {
+    const int xi = x - n_score_wg;
     const int per_seq = P.Hkv * A.n_il_max;
-    const int r = x % per_seq;
-    attn_item<G, true, false>(A, r % A.n_il_max, r / A.n_il_max, x / per_seq, smem);
+    const int r = xi % per_seq;
+    attn_item<G, true, false>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
     return;
   }
   constexpr bool SEP = MODE == kSeparate;
-  const int y = x - n_il_wg;
+  const int y = x;
   const int per_seq = P.G * n_sc;
   const int seq = y / per_seq, grp = (y % per_seq) / n_sc, c = y % n_sc;
   const int sb = SEP ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
