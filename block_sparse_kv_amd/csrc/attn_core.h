@@ -14,9 +14,11 @@
 //     register-resident B operand.
 //   softmax in the exp2 domain per head (the 4 lanes holding one head combine with two shuffles); P is
 //     rounded to fp16 and the row sums use the rounded values.
-//   O = P V: P is already in the A-operand layout (k-slot 8*(l/16)+e holds token 16*(e/4)+4*(l/16)+e%4),
-//     V passes through LDS in rows of 4 tokens padded to 1056 B so the transposed 16-bit reads of the B
-//     operand are free of bank conflicts.
+//   O = P V: P is already in the A-operand layout (k-slot 8*(l/16)+e holds token 16*(e/4)+4*(l/16)+e%4).
+//     V passes through LDS, token rows padded to 288 B, and reaches the B-operand layout (8 tokens of
+//     one channel per lane) through ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+//     element i%4 of the 8-byte chunks addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4, so
+//     lane s of the group points at channels 16nn + 4(s%4) .. +3 of token row s/4 of a 4-token chunk.
 // The 4 waves fold through LDS into one partial (max, sum, unnormalised output) per query head.
 #pragma once
 
@@ -26,8 +28,15 @@ namespace kvs {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaveVBytes = 8 * 1056;           // V staging per wave
+constexpr int kVRow = 288;                      // bytes per staged V token row (256 + 32 bank skew)
+constexpr int kVChunk = 4 * kVRow;              // 4 token rows
+constexpr int kWaveVBytes = 8 * kVChunk;        // V staging per wave (32 tokens)
 constexpr int kAttnLdsBytes = 4 * kWaveVBytes;  // also >= the fold buffers for G <= 16
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(p));
+}
 
 // Partial of query heads h*G .. h*G+G-1 over one tile (physical block `phys`, its first `ntok`
 // tokens, 1 <= ntok <= 128).  Writes part_o[j * n_parts + part][128] and
@@ -96,26 +105,25 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
     }
   ps += shfl_xor_f(ps, 16);
   ps += shfl_xor_f(ps, 32);
-  // V to LDS: chunk i holds the wave's tokens 4i..4i+3, row stride 256 B
+  // V to LDS: chunk i holds the wave's tokens 4i..4i+3, one kVRow row each
   unsigned char* vbuf = smem + w * kWaveVBytes;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool in = 32 * w + 4 * i + lq < ntok;
-    *reinterpret_cast<uint4*>(vbuf + i * 1056 + lq * 256 + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   f32x4_t O[8];
-  const _Float16* vh = reinterpret_cast<const _Float16*>(vbuf);
+  // B operand of k-slots 8*lq + e: V[token 4*lq + e][16nn + lc] from chunk lq (e < 4) and
+  // V[token 16 + 4*lq + e - 4][16nn + lc] from chunk 4 + lq (e >= 4)
+  const unsigned char* vsrc = vbuf + lq * kVChunk + (lc >> 2) * kVRow + (lc & 3) * 8;
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) {
-    half8_t vb;  // B operand: V[token of k-slot 8*lq + e][channel 16nn + lc]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int chunk = e < 4 ? lq : 4 + lq;
-      vb[e] = vh[(chunk * 1056 + (e & 3) * 256) / 2 + 16 * nn + lc];
-    }
+    const v4s_t lo = lds_read_tr16(vsrc + nn * 32);
+    const v4s_t hi = lds_read_tr16(vsrc + 4 * kVChunk + nn * 32);
+    const half8_t vb = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     O[nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
   __syncthreads();  // the V staging area becomes the fold buffer
