@@ -39,16 +39,21 @@ __device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
 }
 
 // Partial of query heads h*G .. h*G+G-1 over one tile (physical block `phys`, its first `ntok`
-// tokens, 1 <= ntok <= 128).  Writes part_o[j * n_parts + part][128] and
+// tokens, 0 <= ntok <= 128).  Writes part_o[j * n_parts + part][128] and
 // part_ml[(j * n_parts + part) * 2 + {0: max, 1: sum}] for j < G (arrays already offset to the first
 // query head of h).
+//
+// The workgroup may be a 256-lane quarter of a larger one (smem then points at the quarter's area):
+// every quarter runs the same barriers.  ntok == 0 gives an empty partial (max -inf); with
+// store == false nothing is written.
 template <int G>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
                                           const uint16_t* __restrict__ v_pool, int h, int phys, int ntok,
                                           float* __restrict__ part_o, float* __restrict__ part_ml,
-                                          int n_parts, int part, unsigned char* smem) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
+                                          int n_parts, int part, unsigned char* smem,
+                                          bool store = true) {
+  const int tid = threadIdx.x & 255, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
   const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
   const uint16_t* Kt = k_pool + off;
   const uint16_t* Vt = v_pool + off;
@@ -140,7 +145,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   }
   __syncthreads();
   // one lane per (head, 4 channels); the (max, sum) pair goes with channel 0
-  for (int idx = tid; idx < G * (kDim / 4); idx += 256) {
+  for (int idx = tid; store && idx < G * (kDim / 4); idx += 256) {
     const int j = idx / (kDim / 4), ch = (idx % (kDim / 4)) * 4;
     const float M = fmaxf(fmaxf(sm[j], sm[16 + j]), fmaxf(sm[32 + j], sm[48 + j]));
     float lsum = 0.f;

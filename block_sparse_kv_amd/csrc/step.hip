@@ -5,8 +5,9 @@
 //    their scores to the one among them that finishes last, which makes the group's selection (256
 //    lanes, keys in registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles
 //    and the merge (attn.hip).
-//  * long rows: scoring (score.hip), top-k in 1024-lane workgroups (topk.hip), then the
-//    Initial/Local and selected tiles together, then the merge.
+//  * long rows: scoring (score.hip); then the top-k selections in 1024-lane workgroups with the
+//    Initial/Local tiles, four per workgroup, in one launch (topk_il_wide_kernel), so their gather
+//    runs while the selections are made; then the selected tiles and the merge.
 // In every grid an attention tile is one workgroup (attn_core.h).
 #include "attn_core.h"
 #include "kvs_launch.h"
@@ -104,6 +105,63 @@ static hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, f
   return hipGetLastError();
 }
 
+// Long rows: the selections, in 1024-lane workgroups, and the Initial/Local tiles in one grid.
+// Workgroups [0, n_topk) are the (sequence, group) selections (keys in registers up to 16 per lane);
+// each later workgroup runs four Initial/Local tiles, one per 256-lane quarter, from the flat index
+// (seq * Hkv + h) * n_il_max + t.  A quarter without a tile (past the sequence's own count or the end)
+// still takes part in the barriers: it computes an empty tile and stores nothing.
+template <int G>
+__global__ __launch_bounds__(1024) void topk_il_wide_kernel(AttnArgs A, const float* __restrict__ scores,
+                                                            int32_t* __restrict__ sel,
+                                                            int32_t* __restrict__ sel_count,
+                                                            int32_t* __restrict__ tiles, int n_topk,
+                                                            int n_il_total) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kAttnLdsBytes];
+  const Params& P = A.P;
+  const int x = blockIdx.x;
+  if (x < n_topk) {
+    topk_group<1024, 16>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles, x / P.G,
+                         x % P.G, *reinterpret_cast<TopkLds*>(smem));
+    return;
+  }
+  const int f = (x - n_topk) * 4 + (threadIdx.x >> 8);  // this quarter's flat tile index
+  const bool in = f < n_il_total;
+  const int fi = in ? f : 0;
+  const int seq = fi / (P.Hkv * A.n_il_max), h = (fi / A.n_il_max) % P.Hkv, t = fi % A.n_il_max;
+  const TileList tl = tiles_of(A.seq_lens[seq], P, 0);
+  const bool have = in && t < tl.nI + tl.nLoc;
+  int phys = 0, ntok = 0;
+  if (have) {
+    const int2 lt = il_tile(tl, t);
+    const int v = lt.x < A.max_blocks ? A.table[(size_t)seq * A.max_blocks + lt.x] : -1;
+    phys = v < 0 ? 0 : v;   // an invalid table entry gives an empty partial
+    ntok = v < 0 ? 0 : lt.y;
+  }
+  const size_t head0 = (size_t)seq * P.Hq + (size_t)h * G;
+  attn_tile<G>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok,
+               A.part_o + head0 * A.max_parts * kDim, A.part_ml + head0 * A.max_parts * 2, A.max_parts,
+               t, smem + (threadIdx.x >> 8) * kAttnLdsBytes, have);
+}
+
+static hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, int32_t* sel,
+                                      int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s) {
+  const int n_topk = A.P.G * batch;
+  const int n_il_total = batch * A.P.Hkv * A.n_il_max;
+  const dim3 grid(n_topk + (n_il_total + 3) / 4), block(1024);
+#define KVS_WIDE(GG)                                                                                 \
+  hipLaunchKernelGGL(topk_il_wide_kernel<GG>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk, \
+                     n_il_total)
+  switch (A.P.g) {
+    case 1: KVS_WIDE(1); break;
+    case 2: KVS_WIDE(2); break;
+    case 4: KVS_WIDE(4); break;
+    case 8: KVS_WIDE(8); break;
+    default: KVS_WIDE(16); break;
+  }
+#undef KVS_WIDE
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
                               int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s) {
   const Params& P = A.P;
@@ -114,9 +172,8 @@ hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* sc
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   } else {
     e = launch_score(P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
-    if (e == hipSuccess)
-      e = launch_topk(P, scores, A.seq_lens, batch, A.max_blocks, sel, sel_count, A.table, tl, s);
-    if (e == hipSuccess) e = launch_attn_tiles(A, batch, true, true, s);
+    if (e == hipSuccess) e = launch_topk_il_wide(A, scores, sel, sel_count, tl, batch, s);
+    if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   }
   if (e == hipSuccess) e = launch_merge(A, batch, s);
   return e;
