@@ -69,7 +69,8 @@ def regions(L, I, W):
     return ib, lloc, (lloc - ib) // B
 
 
-STEP_KERNELS = ("score_kernel", "topk_il_kernel", "topk_kernel", "attn_tiles_kernel", "merge_kernel")
+STEP_KERNELS = ("score_select_kernel", "score_kernel", "topk_il_wide_kernel", "topk_kernel",
+                "attn_tiles_kernel", "merge_kernel")
 COPY_BYTES = 4 << 30  # the device copy of copy_bandwidth(): read and written once per dispatch
 
 
@@ -462,8 +463,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["frac"],
                      "traffic": traffic_per_step(names[0]),
-                     "kernel": "kvs_decode_step (score, top-k + Initial/Local tiles, selected "
-                               "tiles, merge)",
+                     "kernel": "kvs_decode_step (scoring, top-k and Initial/Local tiles, "
+                               "selected tiles, merge: 3 or 4 launches)",
                      "bytes_per_launch": head["required_bytes_per_step"]},
         "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,
