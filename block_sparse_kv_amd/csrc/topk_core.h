@@ -336,44 +336,49 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   for (int c = 0; c < KPT; ++c)
     if (ok(c)) atomicAdd(&S.hist[bin_of(key[c])], 1);
   __syncthreads();
-  if (tid < 64) {  // boundary bin: lane l sums bins 16l..16l+15, suffix scan across lanes
+  if (tid < 64) {  // boundary bin: lane l holds bins 16l..16l+15 in registers, suffix scan across lanes
+    int hb[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 v4 = *reinterpret_cast<const int4*>(&S.hist[16 * tid + 4 * q]);
+      hb[4 * q] = v4.x; hb[4 * q + 1] = v4.y; hb[4 * q + 2] = v4.z; hb[4 * q + 3] = v4.w;
+    }
     int own = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) own += S.hist[16 * tid + b];
+    for (int b = 0; b < 16; ++b) own += hb[b];
     int suf = own;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int y = __shfl_down(suf, d, 64);
       if (tid + d < 64) suf += y;
     }
-    int above = suf - own;
-    if (above < k && suf >= k) {
-      int b = 16 * tid + 15;
-      for (; b > 16 * tid; --b) {
-        if (above + S.hist[b] >= k) break;
-        above += S.hist[b];
+    if (suf - own < k && suf >= k) {  // the boundary bin is one of this lane's
+      int above = suf - own, b = 15, cnt = hb[15];
+#pragma unroll
+      for (int bb = 15; bb >= 1; --bb) {  // highest bb with above + count(bins > bb) + hb[bb] >= k
+        if (b == bb && above + hb[bb] < k) { above += hb[bb]; b = bb - 1; cnt = hb[bb - 1]; }
       }
-      S.bcast[0] = b;          // boundary bin
-      S.bcast[1] = above;      // keys in higher bins (all selected)
-      S.bcast[2] = 0;          // gather cursor
-      S.bcast[3] = S.hist[b];  // keys in the boundary bin (hist is reused below)
+      S.bcast[0] = 16 * tid + b;  // boundary bin
+      S.bcast[1] = above;         // keys in higher bins (all selected)
+      S.bcast[2] = 0;             // gather cursor
+      S.bcast[3] = cnt;           // keys in the boundary bin (hist is reused below)
     }
   }
   __syncthreads();
-  const int bstar = S.bcast[0];
-  int rem = k - S.bcast[1];
-  const int m_sub = S.bcast[3];
+  const int bstar = __builtin_amdgcn_readfirstlane(S.bcast[0]);
+  int rem = k - __builtin_amdgcn_readfirstlane(S.bcast[1]);
+  const int m_sub = __builtin_amdgcn_readfirstlane(S.bcast[3]);
   uint32_t T;
   if (m_sub <= 64) {  // gather the boundary bin, wave 0 ranks it by counting
 #pragma unroll
     for (int c = 0; c < KPT; ++c)
       if (ok(c) && bin_of(key[c]) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = key[c];
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64) {  // rank by counting, the other keys broadcast from their lanes
       const uint32_t u = lane < m_sub ? S.sub[lane] : 0u;
       int gt = 0, ge = 0;
       for (int x = 0; x < m_sub; ++x) {
-        const uint32_t w2 = S.sub[x];
+        const uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)u, x);
         gt += w2 > u;
         ge += w2 >= u;
       }
