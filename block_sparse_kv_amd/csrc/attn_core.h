@@ -43,8 +43,8 @@ __device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
 // part_ml[(j * n_parts + part) * 2 + {0: max, 1: sum}] for j < G (arrays already offset to the first
 // query head of h).
 //
-// The workgroup may be a 256-lane quarter of a larger one (smem then points at the quarter's area):
-// every quarter runs the same barriers.  ntok == 0 gives an empty partial (max -inf); with
+// The workgroup may be a 256-lane part of a larger one (smem then points at the part's area): every
+// part runs the same barriers.  ntok == 0 gives an empty partial (max -inf); with
 // store == false nothing is written.
 template <int G>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,

@@ -104,6 +104,32 @@ __device__ inline float row_sum16(float x) {
 
 __device__ inline float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Minimum / maximum over the 64 lanes of a wave, the same in every lane: DPP within each 16-lane row,
+// then the four row results through readlane (no LDS round trips).
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u<0xB1>(x));
+  x = min(x, dpp_u<0x4E>(x));
+  x = min(x, dpp_u<0x141>(x));
+  x = min(x, dpp_u<0x140>(x));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u<0xB1>(x));
+  x = max(x, dpp_u<0x4E>(x));
+  x = max(x, dpp_u<0x141>(x));
+  x = max(x, dpp_u<0x140>(x));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // ---- fp16 <-> fp32 ----------------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -5,8 +5,8 @@
 //    their scores to the one among them that finishes last, which makes the group's selection (256
 //    lanes, keys in registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles
 //    and the merge (attn.hip).
-//  * long rows: scoring (score.hip); then the top-k selections in 1024-lane workgroups with the
-//    Initial/Local tiles, four per workgroup, in one launch (topk_il_wide_kernel), so their gather
+//  * long rows: scoring (score.hip); then the top-k selections in 512-lane workgroups with the
+//    Initial/Local tiles, two per workgroup, in one launch (topk_il_wide_kernel), so their gather
 //    runs while the selections are made; then the selected tiles and the merge.
 // In every grid an attention tile is one workgroup (attn_core.h).
 #include "attn_core.h"
@@ -105,26 +105,27 @@ static hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, f
   return hipGetLastError();
 }
 
-// Long rows: the selections, in 1024-lane workgroups, and the Initial/Local tiles in one grid.
+// Long rows: the selections, in 512-lane workgroups, and the Initial/Local tiles in one grid.
 // Workgroups [0, n_topk) are the (sequence, group) selections (keys in registers up to 16 per lane);
-// each later workgroup runs four Initial/Local tiles, one per 256-lane quarter, from the flat index
-// (seq * Hkv + h) * n_il_max + t.  A quarter without a tile (past the sequence's own count or the end)
-// still takes part in the barriers: it computes an empty tile and stores nothing.
+// each later workgroup runs two Initial/Local tiles, one per 256-lane half, from the flat index
+// (seq * Hkv + h) * n_il_max + t.  A half without a tile (past the sequence's own count or the end)
+// still takes part in the barriers: it computes an empty tile and stores nothing.  Two halves (73 KiB
+// of LDS) rather than four quarters per workgroup let the tiles spread over twice as many CUs.
 template <int G>
-__global__ __launch_bounds__(1024) void topk_il_wide_kernel(AttnArgs A, const float* __restrict__ scores,
+__global__ __launch_bounds__(512) void topk_il_wide_kernel(AttnArgs A, const float* __restrict__ scores,
                                                             int32_t* __restrict__ sel,
                                                             int32_t* __restrict__ sel_count,
                                                             int32_t* __restrict__ tiles, int n_topk,
                                                             int n_il_total) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kAttnLdsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kAttnLdsBytes];
   const Params& P = A.P;
   const int x = blockIdx.x;
   if (x < n_topk) {
-    topk_group<1024, 16>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles, x / P.G,
+    topk_group<512, 16>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles, x / P.G,
                          x % P.G, *reinterpret_cast<TopkLds*>(smem));
     return;
   }
-  const int f = (x - n_topk) * 4 + (threadIdx.x >> 8);  // this quarter's flat tile index
+  const int f = (x - n_topk) * 2 + (threadIdx.x >> 8);  // this half's flat tile index
   const bool in = f < n_il_total;
   const int fi = in ? f : 0;
   const int seq = fi / (P.Hkv * A.n_il_max), h = (fi / A.n_il_max) % P.Hkv, t = fi % A.n_il_max;
@@ -147,7 +148,7 @@ static hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, in
                                       int32_t* sel_count, int32_t* tiles, int batch, hipStream_t s) {
   const int n_topk = A.P.G * batch;
   const int n_il_total = batch * A.P.Hkv * A.n_il_max;
-  const dim3 grid(n_topk + (n_il_total + 3) / 4), block(1024);
+  const dim3 grid(n_topk + (n_il_total + 1) / 2), block(512);
 #define KVS_WIDE(GG)                                                                                 \
   hipLaunchKernelGGL(topk_il_wide_kernel<GG>, grid, block, 0, s, A, scores, sel, sel_count, tiles, n_topk, \
                      n_il_total)

@@ -307,23 +307,21 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     return;
   }
   uint32_t key[KPT];
-  float fl = INFINITY, fh = -INFINITY;
+  uint32_t kl = 0xFFFFFFFFu, kh = 0u;  // smallest / largest valid key of the lane (keys order as scores)
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     key[c] = ok(c) ? order_key(v[c]) : 0u;  // 0 is below every real key
-    const float x = key_value(key[c]);
-    if (ok(c)) { fl = fminf(fl, x); fh = fmaxf(fh, x); }
+    if (ok(c)) { kl = min(kl, key[c]); kh = max(kh, key[c]); }
   }
-#pragma unroll
-  for (int mm = 1; mm < 64; mm <<= 1) {
-    fl = fminf(fl, __shfl_xor(fl, mm, 64));
-    fh = fmaxf(fh, __shfl_xor(fh, mm, 64));
+  kl = wave_min_u32(kl);
+  kh = wave_max_u32(kh);
+  if (lane == 0) {  // a wave without candidates reports an empty range
+    S.fmin[wv] = kh ? key_value(kl) : INFINITY;
+    S.fmax[wv] = kh ? key_value(kh) : -INFINITY;
   }
-  if (lane == 0) { S.fmin[wv] = fl; S.fmax[wv] = fh; }
   for (int i = tid; i < kBins; i += NT) S.hist[i] = 0;
   __syncthreads();
-  fl = S.fmin[0];
-  fh = S.fmax[0];
+  float fl = S.fmin[0], fh = S.fmax[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) { fl = fminf(fl, S.fmin[w]); fh = fmaxf(fh, S.fmax[w]); }
   const float span = fh - fl;
@@ -442,11 +440,19 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   }
   if (lane == 0) { S.wgt[wv] = n_gt; S.weq[wv] = n_eq; }
   __syncthreads();
-  int eq_before = 0, pos = 0;
-  for (int w = 0; w < wv; ++w) {
-    pos += S.wgt[w] + max(0, min(S.weq[w], rem - eq_before));
-    eq_before += S.weq[w];
+  // keys > T and keys == T of the waves before this one (vector LDS reads, sums in registers); the
+  // T-keys are taken in index order, so min(eq_before, rem) of them precede this wave's
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int q = 0; q < NW / 4; ++q) {
+    const int4 g4 = *reinterpret_cast<const int4*>(&S.wgt[4 * q]);
+    const int4 e4 = *reinterpret_cast<const int4*>(&S.weq[4 * q]);
+    gt_before += (4 * q < wv ? g4.x : 0) + (4 * q + 1 < wv ? g4.y : 0) + (4 * q + 2 < wv ? g4.z : 0) +
+                 (4 * q + 3 < wv ? g4.w : 0);
+    eq_before += (4 * q < wv ? e4.x : 0) + (4 * q + 1 < wv ? e4.y : 0) + (4 * q + 2 < wv ? e4.z : 0) +
+                 (4 * q + 3 < wv ? e4.w : 0);
   }
+  int pos = gt_before + min(eq_before, rem);
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     const unsigned long long eqm = __ballot(ok(c) && key[c] == T);
