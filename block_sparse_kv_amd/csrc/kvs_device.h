@@ -130,6 +130,55 @@ __device__ inline uint32_t wave_max_u32(uint32_t x) {
   return max(max(a, b), max(c, d));
 }
 
+// Float minimum / maximum over the 64 lanes of a wave (NaN lanes are ignored), the same in every lane.
+__device__ inline float rl_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ inline float wave_min_f32(float x) {
+  x = fminf(x, dpp_f<0xB1>(x));
+  x = fminf(x, dpp_f<0x4E>(x));
+  x = fminf(x, dpp_f<0x141>(x));
+  x = fminf(x, dpp_f<0x140>(x));
+  return fminf(fminf(rl_f(x, 0), rl_f(x, 16)), fminf(rl_f(x, 32), rl_f(x, 48)));
+}
+__device__ inline float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return fmaxf(fmaxf(rl_f(x, 0), rl_f(x, 16)), fmaxf(rl_f(x, 32), rl_f(x, 48)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each 16-lane row,
+// then the row totals through the row broadcasts of lanes 15 (into rows 1 and 3) and 31 (into rows
+// 2 and 3).
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// ---- address spaces --------------------------------------------------------------------------------
+// A value every lane reads at a uniform address: loaded through the scalar cache.  Only for data no
+// workgroup of the running kernel writes.
+__device__ inline int ld_uniform_i32(const int32_t* p) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  return *(const cint*)p;
+}
+// The same pointer, marked global (vector memory instructions rather than flat ones).
+template <typename T>
+__device__ inline __attribute__((address_space(1))) T* gptr(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+// Buffer resource over `bytes` bytes from base: loads past the end return 0 (bytes = 0: every load).
+__device__ inline __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // ---- fp16 <-> fp32 ----------------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

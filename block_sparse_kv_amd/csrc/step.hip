@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_sc - 1;
   __syncthreads();
-  if (!s_last) return;
-  if (threadIdx.x == 0) st_coh(cp, 0);  // every scoring workgroup of the group has arrived
+  if (!s_last) return;  // else every scoring workgroup of the group has arrived
   topk_group<256, kStepTopkKeys, true>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table,
                                        tiles, seq, grp, *reinterpret_cast<TopkLds*>(smem));
+  if (threadIdx.x == 0) st_coh(cp, 0);  // stored last: the selection's barriers would wait for it
 }
 
 template <int G, int METHOD>

@@ -48,13 +48,19 @@ __device__ inline T* uniform_ptr(T* p) {
 constexpr int kBins = 1024;     // value bins of stage 1
 constexpr int kSubMax = 1024;   // keys of the boundary bin gathered in LDS for stage 2
 
-// LDS the selection needs besides the staged keys.
+constexpr int kBndMax = 64;     // register path: a boundary bin of up to kBndMax keys is ranked by one wave
+constexpr int kBmapWords = 512; // register path: rows of up to 32 * kBmapWords blocks
+
+// LDS of a selection.
 struct TopkLds {
-  int hist[kBins];
-  uint32_t sub[kSubMax];
+  alignas(16) int hist[kBins + 4];          // value bins; the register path counts non-candidates at [kBins]
+  alignas(16) uint32_t sub[kSubMax];        // keys of the boundary bin (re-read path)
+  alignas(16) unsigned long long bcomp[kBndMax];  // register path: boundary-bin keys, key << 32 | ~index
+  alignas(16) uint32_t bmap[kBmapWords];    //   boundary-bin blocks taken, one bit per block
+  alignas(16) int wgt[16], weq[16], woff[16];
+  alignas(16) float fmin[16], fmax[16];
   int bcast[4];
-  int wgt[16], weq[16];
-  float fmin[16], fmax[16];
+  int cur[2];
 };
 
 // Radix select of the `rem`-th largest among key(i), i < n.  Returns T; `rem` becomes the number of
@@ -261,187 +267,244 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
 // length's regions.  Writes *cnt = k_eff, sel[0..k_eff) ascending (and tiles[] = their physical ids
 // when trow != nullptr), -1 in sel / tiles [k_eff, topk).  COH: the scores were stored by another
 // workgroup of the same kernel (st_coh) and are read with coherent loads.
+//
+// Each candidate's value bin stays in a register, so only the histogram goes through LDS.  Every wave
+// reads the whole histogram and finds the boundary bin itself (DPP prefix sum; no barrier waits on
+// one wave's search).  A boundary bin of at most kBndMax keys -- the usual case -- is gathered and
+// ranked by (key, lower index first) in one wave, which marks the rem it takes in a bitmap and gives
+// every wave its output offset; a crowded one goes through a radix select of the k-th key.  Each wave
+// owns a contiguous index range, so ballots over its columns write the selection in ascending order.
 template <int NT, int KPT, bool COH = false>
 __device__ __forceinline__ void topk_group_reg(const float* row, int m, const int32_t* len,
-                                                         int initial_len, int local_len, int topk,
-                                                         TopkLds& S, int32_t* sel, int32_t* cnt,
-                                                         const int32_t* trow, int32_t* tiles) {
+                                                int initial_len, int local_len, int topk,
+                                                TopkLds& S, int32_t* sel_, int32_t* cnt_,
+                                                const int32_t* trow, int32_t* tiles_) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per block");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  row = uniform_ptr(row);
-  len = uniform_ptr(len);
-  sel = uniform_ptr(sel);
-  cnt = uniform_ptr(cnt);
-  trow = uniform_ptr(trow);
-  tiles = uniform_ptr(tiles);
-  m = __builtin_amdgcn_readfirstlane(m);
+  auto sel = gptr(sel_);
+  auto cnt = gptr(cnt_);
+  auto tiles = gptr(tiles_);
+  const bool with_tiles = trow != nullptr;
   const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc(row, m * 4);
+  const __amdgpu_buffer_rsrc_t rt = span_rsrc(trow, with_tiles ? m * 4 : 0);
   float v[KPT];
   int32_t ph[KPT];
 #pragma unroll
-  for (int c = 0; c < KPT; ++c) {
-    const int i = ibase + 64 * c;
-    const int ic = i < m ? i : 0;
-    if constexpr (COH) v[c] = ld_coh_f1(coh_rsrc(row), ic * 4); else v[c] = row[ic];
-    ph[c] = trow ? trow[ic] : 0;
-  }
-  const Regions rg = regions_of(*len, initial_len, local_len);
+  for (int c = 0; c < KPT; ++c)
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (ibase + 64 * c) * 4, 0,
+                                                                          COH ? kSc1 : 0));
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, (ibase + 64 * c) * 4, 0, 0);
+  const Regions rg = regions_of(ld_uniform_i32(len), initial_len, local_len);
   const int lo = rg.cand_lo, hi = min(rg.cand_hi, m);
   const int n = max(0, hi - lo);
   const int k = min(topk, n);
-  if (tid == 0) *cnt = k;
-  for (int i = k + tid; i < topk; i += NT) {
-    sel[i] = -1;
-    if (trow) tiles[i] = -1;
-  }
-  if (k <= 0) return;
-  auto ok = [&](int c) { const int i = ibase + 64 * c; return i >= lo && i < hi; };
-  auto emit = [&](int slot, int c) {
-    sel[slot] = ibase + 64 * c;
-    if (trow) tiles[slot] = ph[c];
+  // The count and the -1 padding are stored after the last barrier: a barrier waits for every store
+  // the wave has issued.
+  auto finish = [&]() {
+    if (tid == 0) *cnt = k;
+    for (int i = k + tid; i < topk; i += NT) {
+      sel[i] = -1;
+      if (with_tiles) tiles[i] = -1;
+    }
   };
+  if (k <= 0) { finish(); return; }
+  const int d = ibase - lo;  // candidate offset of column 0
+  auto ok = [&](int c) { return (unsigned)(d + 64 * c) < (unsigned)n; };
   if (k >= n) {  // every candidate
+    finish();
 #pragma unroll
     for (int c = 0; c < KPT; ++c)
-      if (ok(c)) emit(ibase + 64 * c - lo, c);
+      if (ok(c)) {
+        sel[d + 64 * c] = ibase + 64 * c;
+        if (with_tiles) tiles[d + 64 * c] = ph[c];
+      }
     return;
   }
-  uint32_t key[KPT];
-  uint32_t kl = 0xFFFFFFFFu, kh = 0u;  // smallest / largest valid key of the lane (keys order as scores)
+
+  // ---- value range of the candidates ----
+  float vl = INFINITY, vh = -INFINITY;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    key[c] = ok(c) ? order_key(v[c]) : 0u;  // 0 is below every real key
-    if (ok(c)) { kl = min(kl, key[c]); kh = max(kh, key[c]); }
+    vl = fminf(vl, ok(c) ? v[c] : INFINITY);
+    vh = fmaxf(vh, ok(c) ? v[c] : -INFINITY);
   }
-  kl = wave_min_u32(kl);
-  kh = wave_max_u32(kh);
-  if (lane == 0) {  // a wave without candidates reports an empty range
-    S.fmin[wv] = kh ? key_value(kl) : INFINITY;
-    S.fmax[wv] = kh ? key_value(kh) : -INFINITY;
-  }
-  for (int i = tid; i < kBins; i += NT) S.hist[i] = 0;
+  vl = wave_min_f32(vl);
+  vh = wave_max_f32(vh);
+  if (lane == 0) { S.fmin[wv] = vl; S.fmax[wv] = vh; }
+  for (int i = tid; i < kBins + 4; i += NT) S.hist[i] = 0;
+  for (int i = tid; i < (m + 31) / 32; i += NT) S.bmap[i] = 0u;
+  if (tid == 0) S.cur[1] = 0;
   __syncthreads();
   float fl = S.fmin[0], fh = S.fmax[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) { fl = fminf(fl, S.fmin[w]); fh = fmaxf(fh, S.fmax[w]); }
   const float span = fh - fl;
-  const float scale = span > 0.f && span < INFINITY ? (float)kBins / span : 0.f;
-  auto bin_of = [&](uint32_t u) -> int {
-    const float x = (key_value(u) - fl) * scale;  // monotone in the score
-    return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
-  };
+  // Any fixed non-negative scale keeps the bins monotone in the score; a range that is empty or not
+  // finite puts every candidate in bin 0.
+  const float scale = span > 0.f && span < INFINITY ? (float)kBins * __builtin_amdgcn_rcpf(span) : 0.f;
+
+  // ---- histogram: bin b of a candidate in a register, -1 for the others (counted in hist[kBins]) ----
+  int b[KPT];
 #pragma unroll
-  for (int c = 0; c < KPT; ++c)
-    if (ok(c)) atomicAdd(&S.hist[bin_of(key[c])], 1);
+  for (int c = 0; c < KPT; ++c) {
+    const float x = fminf(fmaxf((v[c] - fl) * scale, 0.f), (float)(kBins - 1));  // NaN -> 0
+    b[c] = ok(c) ? (int)x : -1;
+    atomicAdd(&S.hist[min((unsigned)b[c], (unsigned)kBins)], 1);
+  }
   __syncthreads();
-  if (tid < 64) {  // boundary bin: lane l holds bins 16l..16l+15 in registers, suffix scan across lanes
+
+  // ---- boundary bin, in every wave: lane l holds bins [kBins - 16(l+1), kBins - 16l), so the prefix
+  // sum over lanes counts keys from the top ----
+  int bstar, above, m_sub;
+  {
+    const int hb0 = kBins - 16 * (lane + 1);
     int hb[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int4 v4 = *reinterpret_cast<const int4*>(&S.hist[16 * tid + 4 * q]);
+      const int4 v4 = *reinterpret_cast<const int4*>(&S.hist[hb0 + 4 * q]);
       hb[4 * q] = v4.x; hb[4 * q + 1] = v4.y; hb[4 * q + 2] = v4.z; hb[4 * q + 3] = v4.w;
     }
     int own = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) own += hb[b];
-    int suf = own;
+    for (int j = 0; j < 16; ++j) own += hb[j];
+    const int incl = wave_incl_scan(own);
+    int cum = incl - own, bb = 0, ab = 0, cb = 0;  // cum: keys in bins above bin j
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_down(suf, d, 64);
-      if (tid + d < 64) suf += y;
+    for (int j = 15; j >= 0; --j) {  // the bin where the count from the top reaches k
+      const int nc = cum + hb[j];
+      const bool hit = cum < k && nc >= k;
+      bb = hit ? j : bb;
+      ab = hit ? cum : ab;
+      cb = hit ? hb[j] : cb;
+      cum = nc;
     }
-    if (suf - own < k && suf >= k) {  // the boundary bin is one of this lane's
-      int above = suf - own, b = 15, cnt = hb[15];
-#pragma unroll
-      for (int bb = 15; bb >= 1; --bb) {  // highest bb with above + count(bins > bb) + hb[bb] >= k
-        if (b == bb && above + hb[bb] < k) { above += hb[bb]; b = bb - 1; cnt = hb[bb - 1]; }
-      }
-      S.bcast[0] = 16 * tid + b;  // boundary bin
-      S.bcast[1] = above;         // keys in higher bins (all selected)
-      S.bcast[2] = 0;             // gather cursor
-      S.bcast[3] = cnt;           // keys in the boundary bin (hist is reused below)
-    }
+    const unsigned long long bl = __ballot(incl - own < k && incl >= k);  // one lane: n > k keys
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bl) - 1);
+    bstar = __builtin_amdgcn_readlane(hb0 + bb, src);
+    above = __builtin_amdgcn_readlane(ab, src);
+    m_sub = __builtin_amdgcn_readlane(cb, src);
   }
-  __syncthreads();
-  const int bstar = __builtin_amdgcn_readfirstlane(S.bcast[0]);
-  int rem = k - __builtin_amdgcn_readfirstlane(S.bcast[1]);
-  const int m_sub = __builtin_amdgcn_readfirstlane(S.bcast[3]);
-  uint32_t T;
-  if (m_sub <= 64) {  // gather the boundary bin, wave 0 ranks it by counting
+  const int rem = k - above;  // keys still to take from the boundary bin, 1..m_sub
+
+  if (m_sub <= kBndMax) {
+    // ---- keys of higher bins are all taken: each wave counts its own; the boundary bin's keys are
+    // gathered for ranking ----
+    int n_above = 0;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      n_above += __popcll(__ballot(b[c] > bstar));
+      if (b[c] == bstar) {
+        const int s = atomicAdd(&S.cur[1], 1);
+        S.bcomp[s] = ((unsigned long long)order_key(v[c]) << 32) | (uint32_t)~(uint32_t)(ibase + 64 * c);
+      }
+    }
+    if (lane == 0) S.wgt[wv] = n_above;
+    __syncthreads();
+    if (wv == 0) {
+      // rank of each boundary key: how many beat it (higher key, or equal and lower index); the best
+      // rem are taken and marked in the bitmap
+      const bool mine = lane < m_sub;
+      const unsigned long long cj = S.bcomp[mine ? lane : 0];
+      int r = 0;
+      for (int x = 0; x < m_sub; x += 2) {
+        const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(&S.bcomp[x]);
+        r += (c2.x > cj) + (x + 1 < m_sub && c2.y > cj);
+      }
+      const bool take = mine && r < rem;
+      const int ij = (int)~(uint32_t)cj;
+      if (take) atomicOr(&S.bmap[ij >> 5], 1u << (ij & 31));
+      // output offset of every wave: the keys the waves before it take
+      const int wj = ij / (64 * KPT);
+      int bsel = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cw = __popcll(__ballot(take && wj == w));
+        bsel = lane == w ? cw : bsel;
+      }
+      const int tot = lane < NW ? S.wgt[lane] + bsel : 0;
+      const int incl = wave_incl_scan(tot);
+      if (lane < NW) S.woff[lane] = incl - tot;
+    }
+    __syncthreads();
+    finish();
+    // ---- ascending order: wave by wave, column by column, lane by lane ----
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int off = S.woff[wv];
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const int i = ibase + 64 * c;
+      bool take = b[c] > bstar;
+      if (__ballot(b[c] == bstar) != 0ull)
+        if (b[c] == bstar) take = (S.bmap[i >> 5] >> (i & 31)) & 1u;
+      const unsigned long long km = __ballot(take);
+      const int slot = off + __popcll(km & lt);
+      if (take && slot < k) {
+        sel[slot] = i;
+        if (with_tiles) tiles[slot] = ph[c];
+      }
+      off += __popcll(km);
+    }
+    return;
+  }
+
+  // ---- a crowded boundary bin: radix select of the k-th key inside the boundary bin ----
+  uint32_t key[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) key[c] = b[c] == bstar ? order_key(v[c]) : 0u;
+  int remT = rem;
+  uint32_t prefix = 0, pmask = 0;
+  __syncthreads();  // every wave has read the value histogram
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
+    __syncthreads();
 #pragma unroll
     for (int c = 0; c < KPT; ++c)
-      if (ok(c) && bin_of(key[c]) == bstar) S.sub[atomicAdd(&S.bcast[2], 1)] = key[c];
+      if (b[c] == bstar && (key[c] & pmask) == prefix) atomicAdd(&S.hist[(key[c] >> shift) & 255], 1);
     __syncthreads();
-    if (tid < 64) {  // rank by counting, the other keys broadcast from their lanes
-      const uint32_t u = lane < m_sub ? S.sub[lane] : 0u;
-      int gt = 0, ge = 0;
-      for (int x = 0; x < m_sub; ++x) {
-        const uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)u, x);
-        gt += w2 > u;
-        ge += w2 >= u;
+    if (tid < 64) {  // lane l owns digits 4l..4l+3; suffix sums from the high digits
+      const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
+                c3 = S.hist[4 * tid + 3];
+      const int own = c0 + c1 + c2 + c3;
+      int suf = own;
+#pragma unroll
+      for (int dd = 1; dd < 64; dd <<= 1) {
+        const int y = __shfl_down(suf, dd, 64);
+        if (tid + dd < 64) suf += y;
       }
-      const bool is_t = lane < m_sub && gt < rem && ge >= rem;
-      const unsigned long long bm = __ballot(is_t);
-      const int src = __ffsll((long long)bm) - 1;  // some lane holds T (all such lanes agree)
-      const uint32_t t = __shfl(u, src, 64);
-      const int above_t = __shfl(gt, src, 64);
-      if (lane == 0) { S.bcast[2] = (int)t; S.bcast[3] = rem - above_t; }
+      const int above_lane = suf - own;
+      if (above_lane < remT && suf >= remT) {
+        int digit, ab = above_lane;
+        if (ab + c3 >= remT) digit = 4 * tid + 3;
+        else if ((ab += c3) + c2 >= remT) digit = 4 * tid + 2;
+        else if ((ab += c2) + c1 >= remT) digit = 4 * tid + 1;
+        else { ab += c1; digit = 4 * tid; }
+        S.bcast[0] = digit;
+        S.bcast[1] = ab;
+      }
     }
     __syncthreads();
-    T = (uint32_t)S.bcast[2];
-    rem = S.bcast[3];
-  } else {  // a crowded bin (many equal scores): MSB-first radix select over that bin's keys
-    uint32_t prefix = 0, pmask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += NT) S.hist[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < KPT; ++c) {
-        const uint32_t u = key[c];
-        if (ok(c) && bin_of(u) == bstar && (u & pmask) == prefix) atomicAdd(&S.hist[(u >> shift) & 255], 1);
-      }
-      __syncthreads();
-      if (tid < 64) {  // lane l owns digits 4l..4l+3; suffix sums from the high digits
-        const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
-                  c3 = S.hist[4 * tid + 3];
-        const int own = c0 + c1 + c2 + c3;
-        int suf = own;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_down(suf, d, 64);
-          if (tid + d < 64) suf += y;
-        }
-        const int above_lane = suf - own;
-        if (above_lane < rem && suf >= rem) {
-          int digit, above = above_lane;
-          if (above + c3 >= rem) digit = 4 * tid + 3;
-          else if ((above += c3) + c2 >= rem) digit = 4 * tid + 2;
-          else if ((above += c2) + c1 >= rem) digit = 4 * tid + 1;
-          else { above += c1; digit = 4 * tid; }
-          S.bcast[0] = digit;
-          S.bcast[1] = above;
-        }
-      }
-      __syncthreads();
-      rem -= S.bcast[1];
-      prefix |= (uint32_t)S.bcast[0] << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
-    }
-    T = prefix;
+    remT -= S.bcast[1];
+    prefix |= (uint32_t)S.bcast[0] << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
   }
-  // T is the k-th largest key; `rem` of the keys equal to T are taken.  Ordered output:
+  const uint32_t T = prefix;  // the k-th largest key: keys of higher bins, keys > T of the boundary
+                              // bin and the remT lowest-indexed keys == T are taken
+  auto gt = [&](int c) { return b[c] > bstar || (b[c] == bstar && key[c] > T); };
+  auto eq = [&](int c) { return b[c] == bstar && key[c] == T; };
   const unsigned long long lt = (1ull << lane) - 1ull;
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    n_gt += __popcll(__ballot(ok(c) && key[c] > T));
-    n_eq += __popcll(__ballot(ok(c) && key[c] == T));
+    n_gt += __popcll(__ballot(gt(c)));
+    n_eq += __popcll(__ballot(eq(c)));
   }
   if (lane == 0) { S.wgt[wv] = n_gt; S.weq[wv] = n_eq; }
   __syncthreads();
-  // keys > T and keys == T of the waves before this one (vector LDS reads, sums in registers); the
-  // T-keys are taken in index order, so min(eq_before, rem) of them precede this wave's
   int gt_before = 0, eq_before = 0;
 #pragma unroll
   for (int q = 0; q < NW / 4; ++q) {
@@ -452,13 +515,18 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     eq_before += (4 * q < wv ? e4.x : 0) + (4 * q + 1 < wv ? e4.y : 0) + (4 * q + 2 < wv ? e4.z : 0) +
                  (4 * q + 3 < wv ? e4.w : 0);
   }
-  int pos = gt_before + min(eq_before, rem);
+  int pos = gt_before + min(eq_before, remT);
+  finish();
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    const unsigned long long eqm = __ballot(ok(c) && key[c] == T);
-    const bool keep = ok(c) && (key[c] > T || (key[c] == T && eq_before + __popcll(eqm & lt) < rem));
+    const unsigned long long eqm = __ballot(eq(c));
+    const bool keep = gt(c) || (eq(c) && eq_before + __popcll(eqm & lt) < remT);
     const unsigned long long km = __ballot(keep);
-    if (keep) emit(pos + __popcll(km & lt), c);
+    const int slot = pos + __popcll(km & lt);
+    if (keep && slot < k) {
+      sel[slot] = ibase + 64 * c;
+      if (with_tiles) tiles[slot] = ph[c];
+    }
     pos += __popcll(km);
     eq_before += __popcll(eqm);
   }
@@ -484,9 +552,8 @@ __device__ inline void topk_group(const Params& P, const float* __restrict__ sco
   topk_group_reg<NT, KPT, COH>(srow, max_blocks, len, P.initial_len, P.local_len, P.topk, S, out,         \
                           sel_count + row, trow, tout)
   if (max_blocks <= NT * 4) { KVS_TOPK_REG(4); return; }
-  if (KMAX >= 8 && max_blocks <= NT * 8) { KVS_TOPK_REG(8); return; }
-  if (KMAX >= 16 && max_blocks <= NT * 16) { KVS_TOPK_REG(16); return; }
-  if (KMAX >= 32 && max_blocks <= NT * 32) { KVS_TOPK_REG(32); return; }
+  if constexpr (KMAX >= 8) if (max_blocks <= NT * 8) { KVS_TOPK_REG(8); return; }
+  if constexpr (KMAX >= 16) if (max_blocks <= NT * 16) { KVS_TOPK_REG(16); return; }
 #undef KVS_TOPK_REG
   if constexpr (COH) return;  // not reached: callers keep coherent rows within NT * KMAX blocks
   const int tid = threadIdx.x;
