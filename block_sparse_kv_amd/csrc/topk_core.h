@@ -452,9 +452,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   }
 
   // ---- a crowded boundary bin: radix select of the k-th key inside the boundary bin ----
-  uint32_t key[KPT];
-#pragma unroll
-  for (int c = 0; c < KPT; ++c) key[c] = b[c] == bstar ? order_key(v[c]) : 0u;
+  auto key = [&](int c) { return order_key(v[c]); };  // recomputed: no register array for the rare case
   int remT = rem;
   uint32_t prefix = 0, pmask = 0;
   __syncthreads();  // every wave has read the value histogram
@@ -463,7 +461,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < KPT; ++c)
-      if (b[c] == bstar && (key[c] & pmask) == prefix) atomicAdd(&S.hist[(key[c] >> shift) & 255], 1);
+      if (b[c] == bstar && (key(c) & pmask) == prefix) atomicAdd(&S.hist[(key(c) >> shift) & 255], 1);
     __syncthreads();
     if (tid < 64) {  // lane l owns digits 4l..4l+3; suffix sums from the high digits
       const int c0 = S.hist[4 * tid], c1 = S.hist[4 * tid + 1], c2 = S.hist[4 * tid + 2],
@@ -494,8 +492,8 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   }
   const uint32_t T = prefix;  // the k-th largest key: keys of higher bins, keys > T of the boundary
                               // bin and the remT lowest-indexed keys == T are taken
-  auto gt = [&](int c) { return b[c] > bstar || (b[c] == bstar && key[c] > T); };
-  auto eq = [&](int c) { return b[c] == bstar && key[c] == T; };
+  auto gt = [&](int c) { return b[c] > bstar || (b[c] == bstar && key(c) > T); };
+  auto eq = [&](int c) { return b[c] == bstar && key(c) == T; };
   const unsigned long long lt = (1ull << lane) - 1ull;
   int n_gt = 0, n_eq = 0;
 #pragma unroll
