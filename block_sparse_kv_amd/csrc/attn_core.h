@@ -167,7 +167,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 }
 
 constexpr int kMergeChunk = 1024;  // partials whose (max, sum) pairs sit in LDS at once
-constexpr int kMergeFirst = 128;   // partials whose outputs are loaded before their count is known
+constexpr int kMergeFirst = 256;   // partials whose outputs are loaded before their count is known
 constexpr int kMergeCh = 32;       // output channels one merge workgroup covers
 constexpr int kMergeLdsFloats = 2 * kMergeChunk + 256 * 4 + 16;
 
@@ -222,8 +222,7 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
         cm = fmaxf(cm, ml.x);
       }
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) cm = fmaxf(cm, shfl_xor_f(cm, m));
+    cm = wave_max_f32(cm);
     if (lane == 0) red[w] = cm;
     __syncthreads();
     const float Mn = fmaxf(M, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
@@ -239,8 +238,7 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
         cl += sums[s] * f;
       }
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) cl += shfl_xor_f(cl, m);
+    cl = wave_sum_f32(cl);
     if (lane == 0) red[4 + w] = cl;
     __syncthreads();  // weights and chunk sums visible
     acc.x *= resc; acc.y *= resc; acc.z *= resc; acc.w *= resc;

@@ -149,6 +149,11 @@ __device__ inline float wave_max_f32(float x) {
   return fmaxf(fmaxf(rl_f(x, 0), rl_f(x, 16)), fmaxf(rl_f(x, 32), rl_f(x, 48)));
 }
 
+__device__ inline float wave_sum_f32(float x) {
+  x = row_sum16(x);
+  return (rl_f(x, 0) + rl_f(x, 16)) + (rl_f(x, 32) + rl_f(x, 48));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each 16-lane row,
 // then the row totals through the row broadcasts of lanes 15 (into rows 1 and 3) and 31 (into rows
 // 2 and 3).
