@@ -60,7 +60,7 @@ struct TopkLds {
   alignas(16) int wgt[16], weq[16], woff[16];
   alignas(16) float fmin[16], fmax[16];
   int bcast[4];
-  int cur[2];
+  int cur;                                  // append cursor of bcomp
 };
 
 // Radix select of the `rem`-th largest among key(i), i < n.  Returns T; `rem` becomes the number of
@@ -337,56 +337,53 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   if (lane == 0) { S.fmin[wv] = vl; S.fmax[wv] = vh; }
   for (int i = tid; i < kBins + 4; i += NT) S.hist[i] = 0;
   for (int i = tid; i < (m + 31) / 32; i += NT) S.bmap[i] = 0u;
-  if (tid == 0) S.cur[1] = 0;
+  if (tid == 0) S.cur = 0;
   __syncthreads();
   float fl = S.fmin[0], fh = S.fmax[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) { fl = fminf(fl, S.fmin[w]); fh = fmaxf(fh, S.fmax[w]); }
   const float span = fh - fl;
-  // Any fixed non-negative scale keeps the bins monotone in the score; a range that is empty or not
-  // finite puts every candidate in bin 0.
+  // bin(v) = min(v * scale - fl * scale, kBins - 1), truncated: monotone in v for any fixed scale >= 0
+  // (a rounding just below 0 truncates to bin 0).  A range that is empty or not finite gives scale 0;
+  // NaN scores land in the top bin.
   const float scale = span > 0.f && span < INFINITY ? (float)kBins * __builtin_amdgcn_rcpf(span) : 0.f;
+  const float boff = -fl * scale;
+  auto bin = [&](float x) { return (int)fminf(fmaf(x, scale, boff), (float)(kBins - 1)); };
 
-  // ---- histogram: bin b of a candidate in a register, -1 for the others (counted in hist[kBins]) ----
+  // ---- histogram: bin of a candidate in a register, -1 for the others (counted in hist[kBins]) ----
   int b[KPT];
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    const float x = fminf(fmaxf((v[c] - fl) * scale, 0.f), (float)(kBins - 1));  // NaN -> 0
-    b[c] = ok(c) ? (int)x : -1;
+    b[c] = ok(c) ? bin(v[c]) : -1;
     atomicAdd(&S.hist[min((unsigned)b[c], (unsigned)kBins)], 1);
   }
   __syncthreads();
 
-  // ---- boundary bin, in every wave: lane l holds bins [kBins - 16(l+1), kBins - 16l), so the prefix
-  // sum over lanes counts keys from the top ----
+  // ---- boundary bin, in every wave.  Lane l sums bins [kBins - 16(l+1), kBins - 16l); a prefix sum
+  // over lanes counts keys from the top and names the lane whose 16 bins hold the k-th key; then
+  // lanes 0..15 take those bins, top bin first, and a prefix sum inside the row names the bin. ----
   int bstar, above, m_sub;
   {
-    const int hb0 = kBins - 16 * (lane + 1);
-    int hb[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int4 v4 = *reinterpret_cast<const int4*>(&S.hist[hb0 + 4 * q]);
-      hb[4 * q] = v4.x; hb[4 * q + 1] = v4.y; hb[4 * q + 2] = v4.z; hb[4 * q + 3] = v4.w;
-    }
-    int own = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) own += hb[j];
+    const int4* h4 = reinterpret_cast<const int4*>(&S.hist[kBins - 16 * (lane + 1)]);
+    const int4 a0 = h4[0], a1 = h4[1], a2 = h4[2], a3 = h4[3];
+    const int own = (a0.x + a0.y + a0.z + a0.w) + (a1.x + a1.y + a1.z + a1.w) +
+                    (a2.x + a2.y + a2.z + a2.w) + (a3.x + a3.y + a3.z + a3.w);
     const int incl = wave_incl_scan(own);
-    int cum = incl - own, bb = 0, ab = 0, cb = 0;  // cum: keys in bins above bin j
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {  // the bin where the count from the top reaches k
-      const int nc = cum + hb[j];
-      const bool hit = cum < k && nc >= k;
-      bb = hit ? j : bb;
-      ab = hit ? cum : ab;
-      cb = hit ? hb[j] : cb;
-      cum = nc;
-    }
     const unsigned long long bl = __ballot(incl - own < k && incl >= k);  // one lane: n > k keys
     const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bl) - 1);
-    bstar = __builtin_amdgcn_readlane(hb0 + bb, src);
-    above = __builtin_amdgcn_readlane(ab, src);
-    m_sub = __builtin_amdgcn_readlane(cb, src);
+    const int above_src = __builtin_amdgcn_readlane(incl - own, src);
+    const int top = kBins - 16 * src - 1;  // the highest of the src lane's bins
+    const int hj = lane < 16 ? S.hist[top - lane] : 0;
+    int cj = hj;  // inclusive prefix over lanes 0..15 of row 0
+    cj += __builtin_amdgcn_update_dpp(0, cj, 0x111, 0xF, 0xF, true);  // row_shr:1
+    cj += __builtin_amdgcn_update_dpp(0, cj, 0x112, 0xF, 0xF, true);  // row_shr:2
+    cj += __builtin_amdgcn_update_dpp(0, cj, 0x114, 0xF, 0xF, true);  // row_shr:4
+    cj += __builtin_amdgcn_update_dpp(0, cj, 0x118, 0xF, 0xF, true);  // row_shr:8
+    const unsigned long long bj = __ballot(lane < 16 && above_src + cj - hj < k && above_src + cj >= k);
+    const int jb = __builtin_amdgcn_readfirstlane(__ffsll((long long)bj) - 1);
+    bstar = top - jb;
+    above = above_src + __builtin_amdgcn_readlane(cj - hj, jb);
+    m_sub = __builtin_amdgcn_readlane(hj, jb);
   }
   const int rem = k - above;  // keys still to take from the boundary bin, 1..m_sub
 
@@ -397,28 +394,27 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       n_above += __popcll(__ballot(b[c] > bstar));
-      if (b[c] == bstar) {
-        const int s = atomicAdd(&S.cur[1], 1);
-        S.bcomp[s] = ((unsigned long long)order_key(v[c]) << 32) | (uint32_t)~(uint32_t)(ibase + 64 * c);
-      }
+      if (b[c] == bstar)
+        S.bcomp[atomicAdd(&S.cur, 1)] =
+            ((unsigned long long)order_key(v[c]) << 32) | (uint32_t)~(uint32_t)(ibase + 64 * c);
     }
     if (lane == 0) S.wgt[wv] = n_above;
     __syncthreads();
     if (wv == 0) {
       // rank of each boundary key: how many beat it (higher key, or equal and lower index); the best
-      // rem are taken and marked in the bitmap
+      // rem are taken and marked in the bitmap, and every wave gets its output offset
       const bool mine = lane < m_sub;
       const unsigned long long cj = S.bcomp[mine ? lane : 0];
       int r = 0;
+#pragma unroll 4
       for (int x = 0; x < m_sub; x += 2) {
         const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(&S.bcomp[x]);
         r += (c2.x > cj) + (x + 1 < m_sub && c2.y > cj);
       }
+      const int wj = (int)(~(uint32_t)cj) / (64 * KPT);
       const bool take = mine && r < rem;
       const int ij = (int)~(uint32_t)cj;
       if (take) atomicOr(&S.bmap[ij >> 5], 1u << (ij & 31));
-      // output offset of every wave: the keys the waves before it take
-      const int wj = ij / (64 * KPT);
       int bsel = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -441,12 +437,14 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
       if (__ballot(b[c] == bstar) != 0ull)
         if (b[c] == bstar) take = (S.bmap[i >> 5] >> (i & 31)) & 1u;
       const unsigned long long km = __ballot(take);
-      const int slot = off + __popcll(km & lt);
-      if (take && slot < k) {
-        sel[slot] = i;
-        if (with_tiles) tiles[slot] = ph[c];
+      if (km != 0ull) {
+        const int slot = off + __popcll(km & lt);
+        if (take && slot < k) {
+          sel[slot] = i;
+          if (with_tiles) tiles[slot] = ph[c];
+        }
+        off += __popcll(km);
       }
-      off += __popcll(km);
     }
     return;
   }
