@@ -1,8 +1,9 @@
 // Attention kernels over the per-tile work items of attn_core.h:
 //  * attn_tiles_kernel: workgroup (x, h, seq) is one attended tile of KV head h -- the x-th
 //    Initial/Local tile, or a selected one -- and writes one partial per query head of h;
-//  * merge_kernel: workgroup (j * 4 + q, seq) folds channels [32q, 32q + 32) of query head j's
-//    partials into out.
+//  * merge_wave_kernel: one wave per (query head, 16 channels) folds that slice of the head's
+//    partials into out; merge_kernel, for partial counts whose weights do not fit the waves' LDS:
+//    workgroup (j * 4 + q, seq) folds channels [32q, 32q + 32).
 // kvs_sparse_decode_attn runs both (Initial/Local and selected tiles in one grid, selections as logical
 // ids); kvs_decode_step runs them with the selections as physical ids, the Initial/Local tiles here
 // or in its top-k launch (step.hip).
@@ -21,6 +22,18 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) float lds[kMergeLdsFloats];
   constexpr int Q = kDim / kMergeCh;
   merge_item(A, blockIdx.x / Q, blockIdx.x % Q, blockIdx.y, lds);
+}
+
+// One wave per (query head, 16 channels), four per workgroup: wave w of workgroup x merges item
+// 4x + w = (seq * Hq + j) * 8 + c.  Used when the waves' LDS (partial weights and the fold) fits.
+constexpr int kMergeWaveLds = 65536;
+__global__ __launch_bounds__(256) void merge_wave_kernel(AttnArgs A, int n_items) {
+  extern __shared__ __attribute__((aligned(16))) float wlds[];
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n_items) return;
+  constexpr int C = kDim / kMergeChWave;
+  const int c = item % C, j = (item / C) % A.P.Hq, seq = item / (C * A.P.Hq);
+  merge_item_wave(A, j, c, seq, wlds + (threadIdx.x >> 6) * (A.max_parts + 256));
 }
 
 AttnPlan attn_plan(const Params& P, int batch, int max_blocks) {
@@ -61,7 +74,13 @@ hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phy
 }
 
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(A.P.Hq * (kDim / kMergeCh), batch), dim3(256), 0, s, A);
+  const size_t lds = (size_t)4 * (A.max_parts + 256) * sizeof(float);
+  if (lds <= (size_t)kMergeWaveLds) {
+    const int n_items = batch * A.P.Hq * (kDim / kMergeChWave);
+    hipLaunchKernelGGL(merge_wave_kernel, dim3((n_items + 3) / 4), dim3(256), lds, s, A, n_items);
+  } else {
+    hipLaunchKernelGGL(merge_kernel, dim3(A.P.Hq * (kDim / kMergeCh), batch), dim3(256), 0, s, A);
+  }
   return hipGetLastError();
 }
 

@@ -277,6 +277,74 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
   }
 }
 
+// Merge of channels [ch0, ch0 + 16) of one query head over its n partials by ONE wave: no workgroup
+// barriers, the reductions go through DPP and the wave's own LDS.  Lane l owns channels
+// ch0 + 4(l % 4) .. +3 of partials l / 4 + 16u; the outputs of the first 16 * kMergeWaveRows partials
+// and the (max, sum) pairs of the first 64 * kMergeWaveMl are requested together, before anything
+// depends on them.  wl: this wave's LDS scratch of >= n + 256 floats.  n == 0 gives zeros.
+constexpr int kMergeChWave = 16;
+constexpr int kMergeWaveRows = 12;
+constexpr int kMergeWaveMl = 3;
+__device__ inline void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                       int n, int ch0, float* __restrict__ out, float* wl) {
+  const int lane = threadIdx.x & 63, cg = lane & 3, pg = lane >> 2;
+  auto ld_ml = [&](int s) { return *reinterpret_cast<const float2*>(part_ml + (size_t)s * 2); };
+  auto ld_o = [&](int s) { return *reinterpret_cast<const float4*>(part_o + (size_t)s * kDim + ch0 + 4 * cg); };
+  const int last = max(n - 1, 0);
+  float2 ml[kMergeWaveMl];
+#pragma unroll
+  for (int r = 0; r < kMergeWaveMl; ++r) ml[r] = ld_ml(min(lane + 64 * r, last));
+  float4 o[kMergeWaveRows];
+#pragma unroll
+  for (int u = 0; u < kMergeWaveRows; ++u) o[u] = ld_o(min(pg + 16 * u, last));
+  float M = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kMergeWaveMl; ++r)
+    if (lane + 64 * r < n) M = fmaxf(M, ml[r].x);
+  for (int s = lane + 64 * kMergeWaveMl; s < n; s += 64) M = fmaxf(M, ld_ml(s).x);
+  M = wave_max_f32(M);
+  float L = 0.f;
+  auto weigh = [&](int s, float2 m) {
+    const float w = exp2_diff(m.x, M);
+    wl[s] = w;
+    L += m.y * w;
+  };
+#pragma unroll
+  for (int r = 0; r < kMergeWaveMl; ++r)
+    if (lane + 64 * r < n) weigh(lane + 64 * r, ml[r]);
+  for (int s = lane + 64 * kMergeWaveMl; s < n; s += 64) weigh(s, ld_ml(s));
+  L = wave_sum_f32(L);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fma4 = [&](const float4& v, float f) {
+    acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
+  };
+#pragma unroll
+  for (int u = 0; u < kMergeWaveRows; ++u)
+    if (pg + 16 * u < n) fma4(o[u], wl[pg + 16 * u]);
+  for (int s = pg + 16 * kMergeWaveRows; s < n; s += 64) {  // the rest, 4 loads in flight
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ld_o(min(s + 16 * u, n - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s + 16 * u < n) fma4(v[u], wl[s + 16 * u]);
+  }
+  float* red = wl + n;  // [16 partial groups][16 channels]
+  *reinterpret_cast<float4*>(red + pg * kMergeChWave + 4 * cg) = acc;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < kMergeChWave) {
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) a += red[g * kMergeChWave + lane];
+    out[ch0 + lane] = L > 0.f ? a / L : 0.f;
+  }
+}
+
 // Writes an empty partial (max -inf, sum 0, zero output) for the g query heads of a tile that names
 // no valid block.
 template <int G>
@@ -331,6 +399,16 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
     return;
   }
   attn_tile<G>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
+}
+
+// Merge of channels [16c, 16c + 16) of query head j of sequence seq by one wave (merge_head_wave).
+__device__ inline void merge_item_wave(const AttnArgs& A, int j, int c, int seq, float* wl) {
+  const Params& P = A.P;
+  const int cnt = P.topk > 0 ? A.sel_count[(size_t)seq * P.G + (P.mode == kSeparate ? j / P.g : 0)] : 0;
+  const TileList tl = tiles_of(A.seq_lens[seq], P, cnt);
+  const size_t hp = (size_t)seq * P.Hq + j;
+  merge_head_wave(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, tl.nI + tl.nLoc + tl.k,
+                  c * kMergeChWave, A.out + hp * kDim, wl);
 }
 
 // Merge of channel quarter q4 of query head j of sequence seq over its n_il + k partials into out.
