@@ -114,3 +114,33 @@ def test_step_all_blocks_equal(nb):
     ref = orc.attention(q[0].cpu().numpy(), Kb[pos], Vb[pos], [list(range(len(toks)))] * Hq)
     err = float(np.abs(out[0].double().cpu().numpy() - ref).max())
     assert err <= 2e-3, err
+
+
+@pytest.mark.parametrize("n", [1000, 4097, 8192])
+def test_topk_nonfinite_rows_stay_well_formed(n):
+    """NaN and infinite scores are outside the contract (their ranking is unspecified), but the
+    output must stay well formed: k_eff entries, distinct candidate ids in ascending order, the rest
+    -1.  Rows with a few NaNs, with +-inf, and with NaN only."""
+    print(f"[case] topk non-finite rows n={n}", flush=True)
+    k = 64
+    c = kvs.Config(num_q_heads=1, num_kv_heads=1, initial_len=0, local_len=0, topk=k,
+                   rep_method="max", head_select_mode="separate")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(kvsynth.mix_seed(303, n))
+    base = torch.randn(4, n, generator=g)
+    base[0, torch.randint(0, n, (17,), generator=g)] = float("nan")
+    base[1, torch.randint(0, n, (9,), generator=g)] = float("inf")
+    base[1, torch.randint(0, n, (9,), generator=g)] = float("-inf")
+    base[2, :] = float("nan")
+    base[3, torch.randint(0, n, (5,), generator=g)] = -float("nan")
+    scores = base[:, None, :].float().to(DEV)
+    lens = torch.full((4,), n * B, dtype=torch.int32, device=DEV)
+    sel, cnt = ops.topk_blocks(c, scores, lens)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu(), cnt.cpu()
+    for i in range(4):
+        got = sel[i, 0].tolist()
+        assert int(cnt[i, 0]) == k, (i, int(cnt[i, 0]))
+        assert all(0 <= x < n for x in got[:k]), (i, got[:k])
+        assert all(a < b for a, b in zip(got[:k], got[1:k])), (i, "not ascending / distinct")
+        assert all(x == -1 for x in got[k:]), (i, "padding")
