@@ -170,14 +170,43 @@ class Setup:
             self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
                                      self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
 
+    def prepare_reuse(self):
+        """Selection reuse (a later token or layer attends with an earlier selection): keep each
+        unit's selection from one decode step, for attention-only steps."""
+        import torch
 
-def time_steps(setup, steps, warmup, use_graph=True):
-    """Returns (seconds for exactly `steps` steps, graph used?)."""
+        w = self.w
+        self.reuse = []
+        for u, (q, kp, vp, rp) in enumerate(self.units):
+            sel = torch.empty_like(self.sel)
+            cnt = torch.empty_like(self.cnt)
+            self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
+                                     self.out, sel, cnt, self.ws, self.ws_bytes)
+            self.reuse.append((sel, cnt))
+        self.attn_ws_bytes = self.kvs.kvs_attn_workspace_size(self.cfg, 1, self.nb)
+        self.attn_ws = torch.empty(self.attn_ws_bytes, dtype=torch.uint8, device=self.out.device)
+        torch.cuda.synchronize()
+
+    def step_attn(self, replica):
+        """One attention-only step (all layers) with the kept selections."""
+        w = self.w
+        for layer in range(w["layers"]):
+            u = replica * w["layers"] + layer
+            q, kp, vp, _ = self.units[u]
+            sel, cnt = self.reuse[u]
+            self.kvs.kvs_sparse_decode_attn(self.cfg, q, kp, vp, self.table, self.nb, self.lens, 1,
+                                            sel, cnt, self.out, self.attn_ws, self.attn_ws_bytes)
+
+
+def time_steps(setup, steps, warmup, use_graph=True, step_fn=None):
+    """Returns (seconds for exactly `steps` steps, graph used?).  step_fn(replica) defaults to the
+    decode step."""
     import torch
 
+    step_fn = step_fn or setup.step
     R = setup.w["replicas"]
     for i in range(warmup):
-        setup.step(i % R)
+        step_fn(i % R)
     torch.cuda.synchronize()
     graph = None
     if use_graph:
@@ -186,7 +215,7 @@ def time_steps(setup, steps, warmup, use_graph=True):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=s):
                 for r in range(R):
-                    setup.step(r)
+                    step_fn(r)
             graph.replay()
             torch.cuda.synchronize()
         except Exception as e:  # capture unsupported: time eager launches instead
@@ -201,7 +230,7 @@ def time_steps(setup, steps, warmup, use_graph=True):
             graph.replay()
     else:
         for i in range(steps):
-            setup.step(i % R)
+            step_fn(i % R)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3, steps, graph is not None
@@ -277,6 +306,17 @@ def measure(name, steps, warmup, device):
                traffic_bytes_per_step=traffic_per_step(name), setup=st)
     log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
         f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+    # selection reuse: attention only, with each unit's kept selection (no scoring, no top-k)
+    st.prepare_reuse()
+    sec_a, steps_a, _ = time_steps(st, steps, warmup, step_fn=st.step_attn)
+    attn_s = sec_a / steps_a
+    attn_bytes = (rb["q"] + rb["kv"] + rb["out"]) * w["layers"]
+    res["reuse_attention_only"] = dict(ms_per_step=attn_s * 1e3, queries_per_s=1.0 / attn_s,
+                                       required_bytes_per_step=attn_bytes,
+                                       hbm_gbs=attn_bytes / attn_s / 1e9,
+                                       frac=attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS)
+    log(f"[bench] {name} attention only (selection reused): {attn_s * 1e6:.1f} us/step, "
+        f"{attn_bytes / attn_s / 1e9:.0f} GB/s = {100 * attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS:.1f}%")
     return res
 
 
