@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Sparse decode benchmark on one MI355X: queries/s and HBM roofline fraction at 128K and 1M tokens.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-reuse]
     python bench.py --summarize-stats DIR --workload NAME      (rocprofv3 --stats CSVs -> profiles/)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --workload NAME   (counters -> profiles/)
 
@@ -69,7 +69,7 @@ def regions(L, I, W):
     return ib, lloc, (lloc - ib) // B
 
 
-STEP_KERNELS = ("score_select_kernel", "score_kernel", "topk_il_wide_kernel", "topk_kernel",
+STEP_KERNELS = ("score_select_kernel", "score_kernel", "topk_il_wide_kernel", "topk_kernel", "merge_wave_kernel",
                 "attn_tiles_kernel", "merge_kernel")
 COPY_BYTES = 4 << 30  # the device copy of copy_bandwidth(): read and written once per dispatch
 
@@ -288,7 +288,7 @@ def cpu_baseline(setup, budget_s=15.0):
                        f"prebuilt, fp64 numpy, 1 thread; queries/s = 1/({w['layers']} x layer time)")
 
 
-def measure(name, steps, warmup, device):
+def measure(name, steps, warmup, device, reuse=True):
     import torch
 
     st = Setup(name, device)
@@ -306,6 +306,8 @@ def measure(name, steps, warmup, device):
                traffic_bytes_per_step=traffic_per_step(name), setup=st)
     log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
         f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+    if not reuse:
+        return res
     # selection reuse: attention only, with each unit's kept selection (no scoring, no top-k)
     st.prepare_reuse()
     sec_a, steps_a, _ = time_steps(st, steps, warmup, step_fn=st.step_attn)
@@ -357,7 +359,7 @@ def summarize_stats(d, name, log_path=None):
            "",
            "command (repository root on the MI355X box; bench.py times the same calls):",
            f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{name} -o run "
-           f"-- python3 bench.py --workload {name} --no-cpu --steps {steps}",
+           f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps}",
            f"    python bench.py --summarize-stats gpurun_out/prof_{name} --workload {name} "
            f"--log gpurun_out/prof_{name}.log",
            "",
@@ -408,9 +410,9 @@ def summarize_pmc(fetch_dir, write_dir, name):
              "",
              "commands (repository root on the MI355X box), one counter per run:",
              f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{name} -o run "
-             f"-- python3 bench.py --workload {name} --no-cpu --steps {steps} --warmup 2",
+             f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps} --warmup 2",
              f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{name} -o run "
-             f"-- python3 bench.py --workload {name} --no-cpu --steps {steps} --warmup 2",
+             f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps} --warmup 2",
              f"    python bench.py --summarize-pmc gpurun_out/pmc_fetch_{name} gpurun_out/pmc_write_{name} "
              f"--workload {name}",
              "",
@@ -444,6 +446,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all", choices=["all", *WORKLOADS])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="skip the attention-only (reused selection) timing, e.g. under the profiler")
     ap.add_argument("--summarize-stats", metavar="DIR", help="rocprofv3 --stats output -> profiles/")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs -> profiles/")
@@ -472,7 +476,7 @@ def main():
     results = {}
     for n in names:
         st_steps = args.steps if WORKLOADS[n]["layers"] == 1 else max(16, args.steps // 8)
-        results[n] = measure(n, st_steps, args.warmup, device)
+        results[n] = measure(n, st_steps, args.warmup, device, reuse=not args.no_reuse)
         if n != names[0]:
             del results[n]["setup"]
             torch.cuda.empty_cache()
