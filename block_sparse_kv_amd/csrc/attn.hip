@@ -24,12 +24,13 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs A) {
   merge_item(A, blockIdx.x / Q, blockIdx.x % Q, blockIdx.y, lds);
 }
 
-// One wave per (query head, 16 channels), four per workgroup: wave w of workgroup x merges item
-// 4x + w = (seq * Hq + j) * 8 + c.  Used when the waves' LDS (partial weights and the fold) fits.
+// One wave per (query head, 16 channels), two per workgroup (spread over many CUs): wave w of
+// workgroup x merges item 2x + w = (seq * Hq + j) * 8 + c.  Used when the waves' LDS (partial
+// weights and the fold) fits.
 constexpr int kMergeWaveLds = 65536;
-__global__ __launch_bounds__(256) void merge_wave_kernel(AttnArgs A, int n_items) {
+__global__ __launch_bounds__(128) void merge_wave_kernel(AttnArgs A, int n_items) {
   extern __shared__ __attribute__((aligned(16))) float wlds[];
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item = blockIdx.x * 2 + (threadIdx.x >> 6);
   if (item >= n_items) return;
   constexpr int C = kDim / kMergeChWave;
   const int c = item % C, j = (item / C) % A.P.Hq, seq = item / (C * A.P.Hq);
@@ -74,10 +75,10 @@ hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phy
 }
 
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s) {
-  const size_t lds = (size_t)4 * (A.max_parts + 256) * sizeof(float);
+  const size_t lds = (size_t)2 * (A.max_parts + 256) * sizeof(float);
   if (lds <= (size_t)kMergeWaveLds) {
     const int n_items = batch * A.P.Hq * (kDim / kMergeChWave);
-    hipLaunchKernelGGL(merge_wave_kernel, dim3((n_items + 3) / 4), dim3(256), lds, s, A, n_items);
+    hipLaunchKernelGGL(merge_wave_kernel, dim3((n_items + 1) / 2), dim3(128), lds, s, A, n_items);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3(A.P.Hq * (kDim / kMergeCh), batch), dim3(256), 0, s, A);
   }

@@ -105,7 +105,7 @@ SMALL = [
     (8, 4, 0, 130, 4, "fix", "separate", 128, [2000]),           # Fix with every token a rep
     (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),       # long rows (> 2048 blocks)
     (16, 1, 128, 1024, 20, "quest", "separate", 1, [280000]),    # long rows, g = 16
-    (8, 8, 128, 1024, 4000, "quest", "separate", 1, [8192, 300]),  # topk past the one-wave merge's LDS
+    (8, 8, 128, 1024, 8000, "quest", "separate", 1, [8192, 300]),  # topk past the one-wave merge's LDS
 ]
 
 
