@@ -386,17 +386,57 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     m_sub = __builtin_amdgcn_readlane(hj, jb);
   }
   const int rem = k - above;  // keys still to take from the boundary bin, 1..m_sub
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
+  if (rem == m_sub) {
+    // ---- the whole boundary bin is taken (typical: value bins are sparse near the k-th key), so the
+    // keys of bin >= bstar are the selection: no ranking ----
+    int n_ge = 0;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) n_ge += __popcll(__ballot(b[c] >= bstar));
+    if (lane == 0) S.wgt[wv] = n_ge;
+    __syncthreads();
+    int off = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) off += w < wv ? S.wgt[w] : 0;
+    finish();
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const bool take = b[c] >= bstar;
+      const unsigned long long km = __ballot(take);
+      if (km != 0ull) {
+        const int slot = off + __popcll(km & lt);
+        if (take && slot < k) {
+          sel[slot] = ibase + 64 * c;
+          if (with_tiles) tiles[slot] = ph[c];
+        }
+        off += __popcll(km);
+      }
+    }
+    return;
+  }
 
   if (m_sub <= kBndMax) {
     // ---- keys of higher bins are all taken: each wave counts its own; the boundary bin's keys are
     // gathered for ranking ----
-    int n_above = 0;
+    // The wave's boundary keys take one range of bcomp: a prefix sum over lanes places each lane's keys,
+    // and one LDS atomic per wave places the wave.
+    int n_above = 0, nb = 0;
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       n_above += __popcll(__ballot(b[c] > bstar));
-      if (b[c] == bstar)
-        S.bcomp[atomicAdd(&S.cur, 1)] =
-            ((unsigned long long)order_key(v[c]) << 32) | (uint32_t)~(uint32_t)(ibase + 64 * c);
+      nb += b[c] == bstar;
+    }
+    const int nb_incl = wave_incl_scan(nb);
+    const int nb_wave = __builtin_amdgcn_readlane(nb_incl, 63);
+    if (nb_wave != 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&S.cur, nb_wave);
+      int at = __builtin_amdgcn_readlane(base, 0) + nb_incl - nb;
+#pragma unroll
+      for (int c = 0; c < KPT; ++c)
+        if (b[c] == bstar)
+          S.bcomp[at++] = ((unsigned long long)order_key(v[c]) << 32) | (uint32_t)~(uint32_t)(ibase + 64 * c);
     }
     if (lane == 0) S.wgt[wv] = n_above;
     __syncthreads();
@@ -428,14 +468,16 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     __syncthreads();
     finish();
     // ---- ascending order: wave by wave, column by column, lane by lane ----
-    const unsigned long long lt = (1ull << lane) - 1ull;
+    // Key ibase + 64c is bit (lane & 31) of bitmap word (ibase >> 5) + 2c: the words are read together,
+    // and nothing below waits inside the loop.
     int off = S.woff[wv];
+    uint32_t wd[KPT];
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) wd[c] = S.bmap[(ibase >> 5) + 2 * c];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int i = ibase + 64 * c;
-      bool take = b[c] > bstar;
-      if (__ballot(b[c] == bstar) != 0ull)
-        if (b[c] == bstar) take = (S.bmap[i >> 5] >> (i & 31)) & 1u;
+      const bool take = b[c] > bstar || (b[c] == bstar && ((wd[c] >> (lane & 31)) & 1u));
       const unsigned long long km = __ballot(take);
       if (km != 0ull) {
         const int slot = off + __popcll(km & lt);
@@ -492,7 +534,6 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
                               // bin and the remT lowest-indexed keys == T are taken
   auto gt = [&](int c) { return b[c] > bstar || (b[c] == bstar && key(c) > T); };
   auto eq = [&](int c) { return b[c] == bstar && key(c) == T; };
-  const unsigned long long lt = (1ull << lane) - 1ull;
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {

@@ -75,7 +75,7 @@ N_VALUES = [1, 2, 63, 64, 65, 1000, 4096, 4097, 8192, 8193, 16384, 16385, 40000]
 @pytest.mark.parametrize("n", N_VALUES)
 def test_topk_crafted_rows(n):
     print(f"[case] topk crafted rows n={n}", flush=True)
-    for j, k in enumerate(sorted({1, 7, 64, max(1, n // 2), max(1, n - 1), n, n + 5})):
+    for j, k in enumerate(sorted({1, 7, 64, 96, 97, max(1, n // 2), max(1, n - 1), n, n + 5})):
         run_rows(n, k, kvsynth.mix_seed(101, n, j))
 
 
