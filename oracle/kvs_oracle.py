@@ -22,6 +22,10 @@ What it computes follows the KTransformers long-context sparse-attention article
   * §4.6  after selection, ordinary attention runs over the retrieved cache; the pseudocode scales
           logits by 1/sqrt(head_dim).
 
+  * the operator's configuration lists kv_type among FP16, FP32, Q4_0 and Q8_0 cache precisions
+    (the article's config list; the instagit page's operator constructor).  Q8_0 is the llama.cpp
+    block format the pages name but do not define; see R22.
+
 Readings taken where the pages are silent (each is the spec here):
   R1  Initial and Local are rounded outward to whole blocks: I_b = B*ceil(I/B),
       L_loc = max(I_b, B*floor((L-W)/B)); candidates are the full blocks in [I_b, L_loc).
@@ -34,6 +38,13 @@ Readings taken where the pages are silent (each is the spec here):
   R11 SEPARATE group score = sum over the query heads of the group (parity unpinned by the pages).
   R12 ties in top-k go to the lower block index; the selection is reported in ascending order.
   R14 attention: softmax of q.k/sqrt(d) over the attended tokens only.
+  R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
+      of one token's key or value row is a block with scale d = max|x| / 127 and codes
+      q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
+      d, 1/d and x * (1/d) are fp32 operations (so the codes are the ones an fp32 implementation
+      takes); an all-zero block has d = 0 and codes 0.  Reps of a Q8_0 cache are taken over the
+      cached (dequantized) keys and stored as fp16 (Mean: fp32), and attention runs over the
+      dequantized keys and values.
 Pins (tests/test_oracle_pins.py, tests/test_oracle_bruteforce.py): Quest upper-bound invariant in
 exact integer arithmetic; dense/masked attention against torch's scaled_dot_product_attention in
 float64; brute force with Fractions and rank-by-counting top-k on tiny caches; closed forms for Mean
@@ -224,3 +235,47 @@ def decode_step(q, K, V, *, B, initial_len, local_len, topk, method, rep_num=1,
     out = attention(q, K, V, toks, scale)
     return dict(init_end=init_end, local_start=local_start, cand=cand, reps=reps,
                 head_scores=s, scores=S, sel=sel, tokens=toks, out=out)
+
+
+# ----------------------------------------------------------------------------------------------
+# O7. Q8_0 cache precision  [the configuration's kv_type: FP16 / FP32 / Q4_0 / Q8_0; reading R22]
+# ----------------------------------------------------------------------------------------------
+Q8_GROUP = 32
+
+
+def quantize_q8_0(x):
+    """Codes and scales of x [..., d] (d a multiple of 32) in the Q8_0 format (reading R22).
+
+    Returns (codes int8 [..., d], scales float16 [..., d // 32]).  The scale, its reciprocal and the
+    scaled values are fp32 operations; the rounding to a code is ties-away-from-zero.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    assert d % Q8_GROUP == 0
+    xg = x.reshape(*lead, d // Q8_GROUP, Q8_GROUP)
+    amax = np.abs(xg).max(axis=-1)                                  # fp32, exact
+    dsc = (amax / np.float32(127.0)).astype(np.float32)             # fp32 division
+    with np.errstate(divide="ignore"):
+        inv = np.where(dsc != 0, np.float32(1.0) / dsc, np.float32(0.0)).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float32)                    # fp32 product
+    v64 = v.astype(np.float64)
+    codes = (np.sign(v64) * np.floor(np.abs(v64) + 0.5)).astype(np.int8)  # ties away from zero
+    return codes.reshape(*lead, d), dsc.astype(np.float16)
+
+
+def dequantize_q8_0(codes, scales):
+    """The cached values fp16(d) * q as float64 [..., d] (exact: 11-bit scale times 8-bit code)."""
+    codes = np.asarray(codes, dtype=np.int8)
+    *lead, d = codes.shape
+    sc = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    cg = codes.astype(np.float64).reshape(*lead, d // Q8_GROUP, Q8_GROUP)
+    return (cg * sc[..., None]).reshape(*lead, d)
+
+
+def stored_reps(reps, method: str):
+    """Reps as the rep pool holds them when they are not copies of fp16 keys (a Q8_0 cache): fp16
+    with round-to-nearest-even, Mean fp32 (reading R22)."""
+    reps = np.asarray(reps, dtype=np.float64)
+    if method == MEAN:
+        return reps.astype(np.float32).astype(np.float64)
+    return reps.astype(np.float16).astype(np.float64)

@@ -6,7 +6,8 @@ copy) and raises AssertionError on failure.  What each one rests on:
   * torch's scaled_dot_product_attention in float64 (a library routine sharing no code with the oracle);
   * closed forms and identities of the definitions (Mean linearity, Fix = rows of K, SHARED = sum
     of SEPARATE, softmax shift invariance, q = 0 gives the mean of V);
-  * hand-worked cases in tests/golden/hand_worked.json;
+  * hand-worked cases in tests/golden/hand_worked.json and tests/golden/q8_0_worked.json;
+  * the rounding bound, code range and block width of the Q8_0 format;
   * planted-block recall of the selection.
 """
 from __future__ import annotations
@@ -278,9 +279,75 @@ def check_planted_recall(orc):
                 assert set(s.hot[h]) <= set(r["sel"][h]), (seed, m, h)
 
 
+# ------------------------------------------------------------------------------------- Q8_0 cache
+GOLDEN_Q8 = os.path.join(os.path.dirname(__file__), "golden", "q8_0_worked.json")
+
+
+def check_q8_golden(orc):
+    """The hand-worked Q8_0 blocks of tests/golden/q8_0_worked.json: scale, codes, cached values."""
+    with open(GOLDEN_Q8) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.zeros(32, dtype=np.float32)
+        for k, v in c["x_nonzero"].items():
+            x[int(k)] = v
+        codes, sc = orc.quantize_q8_0(x[None, :])
+        assert float(sc[0, 0]) == c["d"], (c["why"], float(sc[0, 0]))
+        want = np.zeros(32, dtype=np.int64)
+        for k, v in c["codes_nonzero"].items():
+            want[int(k)] = v
+        assert np.array_equal(codes[0].astype(np.int64), want), (c["why"], codes[0])
+        deq = orc.dequantize_q8_0(codes, sc)[0]
+        wd = np.zeros(32)
+        for k, v in c["deq_nonzero"].items():
+            wd[int(k)] = v
+        assert np.array_equal(deq, wd), (c["why"], deq)
+
+
+def check_q8_error_bound_and_range(orc, seed=21):
+    """On random rows: codes lie in [-127, 127]; each block's largest |x| takes code +-127; the
+    fp32 reconstruction d*q is within d/2 of x (the rounding bound), and the cached value within
+    d/2 + 127 |d - fp16(d)|; blocks are 32 channels wide (a block's scale ignores its neighbours)."""
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((64, 128)) * g.uniform(0.01, 30, (64, 1))).astype(np.float16).astype(np.float32)
+    x[3, 32:64] = 0.0                           # one all-zero block
+    x[5, :32] *= 1000.0                         # a loud block next to quiet ones
+    codes, sc = orc.quantize_q8_0(x)
+    assert codes.shape == x.shape and sc.shape == (64, 4)
+    c = codes.astype(np.int64).reshape(64, 4, 32)
+    xg = x.astype(np.float64).reshape(64, 4, 32)
+    assert c.min() >= -127 and c.max() <= 127
+    amax = np.abs(xg).max(axis=-1)
+    d32 = (amax.astype(np.float32) / np.float32(127)).astype(np.float64)
+    arg = np.abs(xg).argmax(axis=-1)
+    top = np.take_along_axis(c, arg[..., None], -1)[..., 0]
+    nz = amax > 0
+    assert np.all(np.abs(top[nz]) == 127)
+    assert np.all(c[~nz] == 0) and np.all(sc.astype(np.float64)[~nz] == 0)
+    err32 = np.abs(xg - d32[..., None] * c)
+    assert np.all(err32 <= d32[..., None] * (0.5 + 1e-5)), err32.max()
+    deq = orc.dequantize_q8_0(codes, sc).reshape(64, 4, 32)
+    d16 = sc.astype(np.float64)
+    assert np.all(np.abs(xg - deq) <= (d32 * (0.5 + 1e-5) + 127 * np.abs(d32 - d16))[..., None])
+    # the quiet blocks of row 5 keep their own scale
+    assert np.all(sc[5, 1:].astype(np.float64) < sc[5, 0].astype(np.float64) / 100)
+
+
+def check_q8_integer_rows_exact(orc):
+    """Rows of integers whose blocks each hold +-127 are their own codes, with d = 1."""
+    g = np.random.default_rng(22)
+    x = g.integers(-127, 128, (8, 128)).astype(np.float32)
+    x[:, ::32] = 127.0
+    codes, sc = orc.quantize_q8_0(x)
+    assert np.all(sc.astype(np.float64) == 1.0)
+    assert np.array_equal(codes.astype(np.float32), x)
+    assert np.array_equal(orc.dequantize_q8_0(codes, sc), x.astype(np.float64))
+
+
 ALL_CHECKS = [
     check_quest_upper_bound, check_quest_tight_and_units, check_rep_closed_forms,
     check_hand_worked, check_regions_golden, check_regions_partition,
     check_shared_is_sum_of_separate, check_gqa_mapping_via_sdpa, check_masked_attention_via_sdpa,
-    check_softmax_identities,
+    check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
+    check_q8_integer_rows_exact,
 ]

@@ -99,6 +99,46 @@ def _shared_as_mean(s, Hkv, mode):
     return r / s.shape[1] if mode == orc.SHARED else r
 
 
+def _q8_round_half_even(x):
+    codes, sc = _orig_quantize(x)
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    xg = x.reshape(*lead, d // 32, 32)
+    dsc = (np.abs(xg).max(axis=-1) / np.float32(127)).astype(np.float32)
+    inv = np.where(dsc != 0, np.float32(1) / np.where(dsc != 0, dsc, 1), 0).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float32)
+    return np.round(v).astype(np.int8).reshape(*lead, d), sc
+
+
+def _q8_scale_128(x):
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    xg = x.reshape(*lead, d // 32, 32)
+    dsc = (np.abs(xg).max(axis=-1) / np.float32(128)).astype(np.float32)
+    inv = np.where(dsc != 0, np.float32(1) / np.where(dsc != 0, dsc, 1), 0).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float64)
+    codes = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -128, 127)
+    return codes.astype(np.int8).reshape(*lead, d), dsc.astype(np.float16)
+
+
+def _q8_block_16(x):
+    """Codes scaled per 16 channels, reported with the scale of each 32-channel block's first half."""
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    xg = x.reshape(*lead, d // 16, 16)
+    dsc = (np.abs(xg).max(axis=-1) / np.float32(127)).astype(np.float32)
+    inv = np.where(dsc != 0, np.float32(1) / np.where(dsc != 0, dsc, 1), 0).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float64)
+    codes = (np.sign(v) * np.floor(np.abs(v) + 0.5)).astype(np.int8).reshape(*lead, d)
+    return codes, dsc.reshape(*lead, d // 32, 2)[..., 0].astype(np.float16)
+
+
+def _q8_deq_fp32_scale(codes, scales):
+    return _orig_dequantize(codes, scales) * 1.0001
+
+
+_orig_quantize = orc.quantize_q8_0
+_orig_dequantize = orc.dequantize_q8_0
 _orig_head_scores = orc.head_scores
 _orig_select = orc.select_topk
 _orig_regions = orc.regions
@@ -117,6 +157,10 @@ MUTANTS = [
     ("block_reps", _mean_wrong_divisor),
     ("block_reps", _fix_wrong_offset),
     ("group_scores", _shared_as_mean),
+    ("quantize_q8_0", _q8_round_half_even),
+    ("quantize_q8_0", _q8_scale_128),
+    ("quantize_q8_0", _q8_block_16),
+    ("dequantize_q8_0", _q8_deq_fp32_scale),
 ]
 
 
