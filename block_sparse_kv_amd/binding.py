@@ -27,11 +27,14 @@ KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_MISALIGNED, KVS_ERR_WO
     KVS_ERR_HIP = 0, -1, -2, -3, -4, -5
 REP_QUEST, REP_MAX, REP_MEAN, REP_FIX = 0, 1, 2, 3
 HEADS_SEPARATE, HEADS_SHARED = 0, 1
+KV_FP16, KV_Q8_0 = 0, 1
+KV_NAMES = {"fp16": KV_FP16, "q8_0": KV_Q8_0}
 REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FIX}
 MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
 
 EXPORTS = (
-    "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block", "kvs_build_reps",
+    "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block",
+    "kvs_kv_bytes_per_block", "kvs_quantize_kv", "kvs_build_reps",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step",
 )
@@ -44,12 +47,13 @@ class kvs_config(ctypes.Structure):
         ("initial_len", ctypes.c_int32), ("local_len", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("rep_method", ctypes.c_int32), ("rep_num", ctypes.c_int32),
         ("head_select_mode", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("kv_type", ctypes.c_int32),
     ]
 
 
 @dataclass
 class Config:
-    """Python mirror of kvs_config; rep_method / head_select_mode accept names or codes."""
+    """Python mirror of kvs_config; rep_method / head_select_mode / kv_type accept names or codes."""
     num_q_heads: int
     num_kv_heads: int
     initial_len: int
@@ -61,13 +65,15 @@ class Config:
     head_dim: int = 128
     block_size: int = 128
     softmax_scale: float = 0.0
+    kv_type: object = "fp16"
 
     def c(self) -> kvs_config:
         rm = REP_NAMES.get(self.rep_method, self.rep_method)
         hm = MODE_NAMES.get(self.head_select_mode, self.head_select_mode)
+        kt = KV_NAMES.get(self.kv_type, self.kv_type)
         return kvs_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
                           self.initial_len, self.local_len, self.topk, int(rm), self.rep_num,
-                          int(hm), float(self.softmax_scale))
+                          int(hm), float(self.softmax_scale), int(kt))
 
     @property
     def groups(self) -> int:
@@ -87,6 +93,10 @@ _lib.kvs_rep_count.restype = ctypes.c_int
 _lib.kvs_rep_count.argtypes = [_CFG]
 _lib.kvs_rep_bytes_per_block.restype = _S
 _lib.kvs_rep_bytes_per_block.argtypes = [_CFG]
+_lib.kvs_kv_bytes_per_block.restype = _S
+_lib.kvs_kv_bytes_per_block.argtypes = [_CFG]
+_lib.kvs_quantize_kv.restype = ctypes.c_int
+_lib.kvs_quantize_kv.argtypes = [_CFG, _P, _P, _I, _P, _P]
 _lib.kvs_build_reps.restype = ctypes.c_int
 _lib.kvs_build_reps.argtypes = [_CFG, _P, _P, _I, _P, _P]
 _lib.kvs_score_blocks.restype = ctypes.c_int
@@ -149,6 +159,16 @@ def kvs_rep_count(cfg) -> int:
 
 def kvs_rep_bytes_per_block(cfg) -> int:
     return _lib.kvs_rep_bytes_per_block(_cfg(cfg))
+
+
+def kvs_kv_bytes_per_block(cfg) -> int:
+    return _lib.kvs_kv_bytes_per_block(_cfg(cfg))
+
+
+def kvs_quantize_kv(cfg, src_pool, phys_block_ids, n_blocks, dst_pool, stream=None, check=True):
+    st = _lib.kvs_quantize_kv(_cfg(cfg), _ptr(src_pool), _ptr(phys_block_ids), n_blocks,
+                              _ptr(dst_pool), _stream(stream))
+    return _check(st, "kvs_quantize_kv") if check else st
 
 
 def kvs_build_reps(cfg, k_pool, phys_block_ids, n_blocks, rep_pool, stream=None, check=True):

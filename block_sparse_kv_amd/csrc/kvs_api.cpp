@@ -42,6 +42,7 @@ int make_params(const kvs_config* c, Params* P) {
   if (c->head_select_mode != KVS_HEADS_SEPARATE && c->head_select_mode != KVS_HEADS_SHARED)
     return KVS_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
+  if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0) return KVS_ERR_INVALID_ARG;
   const int R = rep_count_of(c);
   if (R < 0) return KVS_ERR_INVALID_ARG;
   if (c->head_dim != kvs::kDim || c->block_size != kvs::kBlock) return KVS_ERR_UNSUPPORTED;
@@ -59,6 +60,7 @@ int make_params(const kvs_config* c, Params* P) {
   P->mode = c->head_select_mode;
   const float scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf((float)c->head_dim);
   P->scale_log2 = scale * 1.4426950408889634f;
+  P->kv = c->kv_type;
   return KVS_OK;
 }
 
@@ -173,6 +175,28 @@ size_t kvs_rep_bytes_per_block(const kvs_config* cfg) {
   return (size_t)P.Hkv * P.R * kvs::kDim * elem;
 }
 
+size_t kvs_kv_bytes_per_block(const kvs_config* cfg) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK) return 0;
+  return (size_t)P.Hkv * (P.kv == kvs::kKvQ8 ? (size_t)kvs::kQ8Record : (size_t)kvs::kTile * 2);
+}
+
+int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,
+                    int32_t n_blocks, void* dst_pool, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if (P.kv != kvs::kKvQ8 || n_blocks < 0) return KVS_ERR_INVALID_ARG;
+  if (n_blocks == 0) return KVS_OK;
+  if (n_blocks > 65535) return KVS_ERR_UNSUPPORTED;  // grid y
+  if (!src_pool || !phys_block_ids || !dst_pool) return KVS_ERR_INVALID_ARG;
+  if (!aligned(src_pool, 16) || !aligned(dst_pool, 16)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
+  return hip_status(kvs::launch_quantize_q8(P, src_pool, phys_block_ids, n_blocks, dst_pool,
+                                            static_cast<hipStream_t>(stream)),
+                    "kvs_quantize_kv");
+}
+
 int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
                    int32_t n_blocks, void* rep_pool, kvs_stream_t stream) {
   Params P;
@@ -231,6 +255,7 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
+  if (P.kv != kvs::kKvFp16) return KVS_ERR_UNSUPPORTED;  // Q8_0 attention: not yet
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_count || !out ||
       (!sel && P.topk > 0))
@@ -263,6 +288,7 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
+  if (P.kv != kvs::kKvFp16) return KVS_ERR_UNSUPPORTED;  // Q8_0 attention: not yet
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !k_pool || !v_pool || !rep_pool || !block_table || !seq_lens || !out)
     return KVS_ERR_INVALID_ARG;

@@ -9,9 +9,15 @@ namespace kvs {
 constexpr int kBlock = 128;  // tokens per KV block
 constexpr int kDim = 128;    // head_dim
 constexpr int kTile = kBlock * kDim;  // fp16 elements in one (block, KV head) tile
+// Q8_0 record of one (block, KV head): int8 codes [128 tokens][128], then fp16 scales [128][4]
+// (scale [t][c / 32] of channel c of token t).
+constexpr int kQ8Group = 32;
+constexpr int kQ8Codes = kBlock * kDim;                                // bytes of codes
+constexpr int kQ8Record = kQ8Codes + kBlock * (kDim / kQ8Group) * 2;  // 17408 bytes
 
 enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3 };
 enum Mode { kSeparate = 0, kShared = 1 };
+enum KvType { kKvFp16 = 0, kKvQ8 = 1 };
 
 // Launch-time constants of one call (passed by value to every kernel).
 struct Params {
@@ -19,6 +25,7 @@ struct Params {
   int G;                // selection groups: Hkv (SEPARATE) or 1 (SHARED)
   int initial_len, local_len, topk;
   int method, R, mode;  // rep method, reps per (block, head), head_select_mode
+  int kv;               // KvType of the K/V pools
   float scale_log2;     // softmax scale * log2(e): logits live in the exp2 domain
 };
 

@@ -19,6 +19,8 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(const Params& P, int batch, int max_blocks);
 
+hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
+                              hipStream_t s);
 hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
                              int rep_num, void* rep_pool, hipStream_t s);
 hipError_t launch_score(const Params& P, const void* q, const void* rep_pool, const int32_t* table,

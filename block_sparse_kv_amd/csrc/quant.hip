@@ -1,0 +1,72 @@
+// kvs_quantize_kv: Q8_0 records of fp16 K or V tiles.  Q8_0 is the published llama.cpp block
+// format that the operator's kv_type list names (KTransformers long-context article, configuration
+// list; the instagit page's operator constructor): per token, blocks of 32 channels with scale
+// d = max|x| / 127 kept in fp16 and int8 codes round(x / d), ties away from zero.
+//
+// One workgroup per (listed block, KV head) tile, 256 lanes: lane t takes token t / 2 and channels
+// 64 (t % 2) .. +63, i.e. two Q8_0 blocks.  Its 128 bytes of fp16 are contiguous and the wave reads
+// 8 KiB in one sweep; codes and scales are written back just as contiguously.  d, 1/d and x * (1/d)
+// are IEEE fp32 operations (correctly rounded division), so the codes are exactly those of any fp32
+// implementation of the format.
+#include "kvs_launch.h"
+
+namespace kvs {
+
+__global__ __launch_bounds__(256) void quantize_q8_kernel(const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ ids, int Hkv,
+                                                          unsigned char* __restrict__ dst) {
+  const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
+  const size_t tile = (size_t)ids[i] * Hkv + h;
+  const int tok = t >> 1, half = t & 1;
+  const uint4* in = reinterpret_cast<const uint4*>(src + tile * kTile + tok * kDim + 64 * half);
+  uint4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) raw[u] = in[u];
+  unsigned char* rec = dst + tile * kQ8Record;
+  uint32_t codes[16];
+  _Float16 sc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {  // Q8_0 block b of this lane: channels 64 half + 32 b .. +31
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 r = raw[4 * b + u];
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * u + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xFFFFu));
+        x[8 * u + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    const float d = amax / 127.0f;
+    const float inv = d != 0.f ? 1.0f / d : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = (int)roundf(x[4 * e + k] * inv);
+        word |= (uint32_t)(c & 0xFF) << (8 * k);
+      }
+      codes[8 * b + e] = word;
+    }
+    sc[b] = (_Float16)d;
+  }
+  uint4* co = reinterpret_cast<uint4*>(rec + tok * kDim + 64 * half);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) co[u] = make_uint4(codes[4 * u], codes[4 * u + 1], codes[4 * u + 2], codes[4 * u + 3]);
+  const uint32_t sw = (uint32_t)__builtin_bit_cast(uint16_t, sc[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, sc[1]) << 16);
+  *reinterpret_cast<uint32_t*>(rec + kQ8Codes + tok * 8 + 4 * half) = sw;
+}
+
+hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(quantize_q8_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
+  return hipGetLastError();
+}
+
+}  // namespace kvs

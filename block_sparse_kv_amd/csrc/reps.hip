@@ -6,39 +6,67 @@
 // channels 8*(t%16)..+8 of tokens t/16 + 16*i (i = 0..7) with 128-bit loads: each wave-wide load is
 // 4 whole token rows, 1 KiB contiguous.  Per-lane partials are folded across the 4 rows of a wave
 // with lane shuffles and across the 4 waves through LDS.  The kernel streams K once (HBM-bound).
+// A Q8_0 cache (kv_type; the llama.cpp block format) is read the same way, 8 codes and the scale of
+// their 32-channel block per token; scale * code is exact in fp32, and the reps are rounded to fp16
+// once, at the store.
 #include "kvs_device.h"
 #include "kvs_launch.h"
 
 namespace kvs {
 
-template <int METHOD>
-__global__ __launch_bounds__(256) void build_reps_kernel(const uint16_t* __restrict__ k_pool,
+// 8 cached values of a Q8_0 record: channels 8c..8c+7 of token `tok` (scale * code, exact in fp32).
+__device__ inline void q8_row8(const unsigned char* rec, int tok, int c, float f[8]) {
+  const uint2 cw = *reinterpret_cast<const uint2*>(rec + tok * kDim + c * 8);
+  const float d = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(
+                      rec + kQ8Codes + tok * (kDim / kQ8Group) * 2 + (c * 8 / kQ8Group) * 2));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = e < 4 ? cw.x : cw.y;
+    f[e] = (float)(int)(signed char)((w >> (8 * (e & 3))) & 0xFF) * d;
+  }
+}
+
+template <int METHOD, bool Q8>
+__global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict__ k_pool,
                                                          const int32_t* __restrict__ ids, int Hkv,
                                                          int rep_num, void* __restrict__ rep_pool) {
   const int h = blockIdx.y;
   const size_t p = (size_t)ids[blockIdx.x];
-  const uint16_t* tile = k_pool + (p * Hkv + h) * kTile;
+  const uint16_t* tile = static_cast<const uint16_t*>(k_pool) + (p * Hkv + h) * kTile;
+  const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + (p * Hkv + h) * (size_t)kQ8Record;
   const int t = threadIdx.x, c = t & 15, r = t >> 4;
 
-  if constexpr (METHOD == kFix) {  // rows 0, s, 2s, ... copied verbatim
+  if constexpr (METHOD == kFix) {  // rows 0, s, 2s, ... (fp16: copied verbatim)
     const int stride = kBlock / rep_num;
     uint16_t* out = static_cast<uint16_t*>(rep_pool) + (p * Hkv + h) * (size_t)rep_num * kDim;
-    for (int rr = r; rr < rep_num; rr += 16)
-      *reinterpret_cast<uint4*>(out + rr * kDim + c * 8) =
-          *reinterpret_cast<const uint4*>(tile + (size_t)(rr * stride) * kDim + c * 8);
+    for (int rr = r; rr < rep_num; rr += 16) {
+      if constexpr (Q8) {
+        float f[8];
+        q8_row8(rec, rr * stride, c, f);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)f2h_bits(f[2 * e]) | ((uint32_t)f2h_bits(f[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(out + rr * kDim + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        *reinterpret_cast<uint4*>(out + rr * kDim + c * 8) =
+            *reinterpret_cast<const uint4*>(tile + (size_t)(rr * stride) * kDim + c * 8);
+      }
+    }
     return;
   } else {
     uint4 raw[8];
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      raw[i] = ld_stream16(tile + (size_t)(r + 16 * i) * kDim + c * 8);
+      for (int i = 0; i < 8; ++i)
+        raw[i] = ld_stream16(tile + (size_t)(r + 16 * i) * kDim + c * 8);
+    }
     float a[8], b[8];  // Quest: min, max.  Max: -, max.  Mean: sum, -
 #pragma unroll
     for (int e = 0; e < 8; ++e) { a[e] = METHOD == kMean ? 0.f : INFINITY; b[e] = -INFINITY; }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float f[8];
-      unpack8(raw[i], f);
+      if constexpr (Q8) q8_row8(rec, r + 16 * i, c, f); else unpack8(raw[i], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (METHOD == kMean) a[e] += f[e];
@@ -84,16 +112,23 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const uint16_t* __restr
   }
 }
 
+template <bool Q8>
+static void launch_reps_q(const Params& P, dim3 grid, const void* kp, const int32_t* ids, int rep_num,
+                          void* rep_pool, hipStream_t s) {
+  const dim3 block(256);
+  switch (P.method) {
+    case kQuest: hipLaunchKernelGGL((build_reps_kernel<kQuest, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMax:   hipLaunchKernelGGL((build_reps_kernel<kMax, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMean:  hipLaunchKernelGGL((build_reps_kernel<kMean, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    default:     hipLaunchKernelGGL((build_reps_kernel<kFix, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+  }
+}
+
 hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
                              int rep_num, void* rep_pool, hipStream_t s) {
-  const dim3 grid(n, P.Hkv), block(256);
-  const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
-  switch (P.method) {
-    case kQuest: hipLaunchKernelGGL(build_reps_kernel<kQuest>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    case kMax:   hipLaunchKernelGGL(build_reps_kernel<kMax>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    case kMean:  hipLaunchKernelGGL(build_reps_kernel<kMean>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    default:     hipLaunchKernelGGL(build_reps_kernel<kFix>, grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-  }
+  const dim3 grid(n, P.Hkv);
+  if (P.kv == kKvQ8) launch_reps_q<true>(P, grid, k_pool, ids, rep_num, rep_pool, s);
+  else launch_reps_q<false>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   return hipGetLastError();
 }
 

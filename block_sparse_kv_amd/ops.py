@@ -21,6 +21,22 @@ def alloc_rep_pool(cfg: B.Config, n_phys: int, device) -> torch.Tensor:
                        device=device)
 
 
+def alloc_q8_pool(cfg: B.Config, n_phys: int, device) -> torch.Tensor:
+    """A Q8_0 K or V pool: [n_phys][Hkv] records of int8 codes [128][128] + fp16 scales [128][4],
+    as bytes [n_phys][Hkv][17408]."""
+    per_block = B.kvs_kv_bytes_per_block(cfg)
+    if per_block == 0:
+        raise B.KvsError(B.KVS_ERR_INVALID_ARG, "alloc_q8_pool")
+    return torch.empty((n_phys, cfg.num_kv_heads, per_block // cfg.num_kv_heads), dtype=torch.uint8,
+                       device=device)
+
+
+def quantize_kv(cfg, src_pool, phys_ids: torch.Tensor, dst_pool: torch.Tensor):
+    ids = phys_ids.to(device=src_pool.device, dtype=torch.int32).contiguous()
+    B.kvs_quantize_kv(cfg, src_pool, ids, ids.numel(), dst_pool)
+    return dst_pool
+
+
 def build_reps(cfg, k_pool, phys_ids: torch.Tensor, rep_pool: torch.Tensor):
     ids = phys_ids.to(device=k_pool.device, dtype=torch.int32).contiguous()
     B.kvs_build_reps(cfg, k_pool, ids, ids.numel(), rep_pool)

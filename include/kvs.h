@@ -27,7 +27,10 @@
  * Layouts (row-major, innermost last)
  *   q            fp16 [batch][Hq][128]
  *   out          fp32 [batch][Hq][128]
- *   k_pool,v_pool fp16 [n_phys][Hkv][128 tokens][128]   one (block, KV head) tile = 32 KiB
+ *   k_pool,v_pool kv_type FP16: fp16 [n_phys][Hkv][128 tokens][128], one (block, KV head) tile = 32 KiB
+ *                kv_type Q8_0: [n_phys][Hkv] records of 17408 bytes, one per (block, KV head):
+ *                int8 codes [128 tokens][128], then fp16 scales [128 tokens][4]; channel c of token
+ *                t holds scale[t][c / 32] * code[t][c] (see kvs_quantize_kv)
  *   rep_pool     [n_phys][Hkv][R][128]  fp16, except fp32 for KVS_REP_MEAN.
  *                R = 2 for Quest (r=0 channel-wise min key, r=1 channel-wise max key), 1 for Max
  *                and Mean, rep_num for Fix (r-th rep = token r*(128/rep_num) of the block).
@@ -75,6 +78,12 @@ typedef enum { KVS_REP_QUEST = 0, KVS_REP_MAX = 1, KVS_REP_MEAN = 2, KVS_REP_FIX
  * query heads. */
 typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mode;
 
+/* Cache precision of k_pool / v_pool: the operator's kv_type [KT-LC §4.5 configuration list; the
+ * instagit page's operator constructor, step 3], which names FP16, FP32, Q4_0 and Q8_0.  FP16 and
+ * Q8_0 are provided; Q8_0 is the published llama.cpp block format: per token and KV head, blocks
+ * of 32 channels with scale d = max|x| / 127 (fp16) and int8 codes round(x / d), ties away from zero. */
+typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1 } kvs_kv_type;
+
 /* Host struct.  Field order and types are part of the ABI. */
 typedef struct kvs_config {
   int32_t num_q_heads;      /* Hq                                                           */
@@ -88,6 +97,7 @@ typedef struct kvs_config {
   int32_t rep_num;          /* anchor_num: Fix only, divides B, 1..B; ignored otherwise      */
   int32_t head_select_mode; /* kvs_head_select_mode                                          */
   float softmax_scale;      /* attention logit scale; 0 => 1/sqrt(head_dim) [KT-LC §4.6]     */
+  int32_t kv_type;          /* kvs_kv_type of k_pool and v_pool                              */
 } kvs_config;
 
 /* Human-readable name of a status code (static string). */
@@ -104,6 +114,22 @@ int kvs_rep_count(const kvs_config* cfg /* host */);
 /* Bytes of one physical block's reps over all KV heads (Hkv * R * 128 * elem), 0 on bad config. */
 size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
 
+/* Bytes of one physical block of k_pool (or v_pool) over all KV heads: Hkv * 32768 for FP16,
+ * Hkv * 17408 for Q8_0; 0 on a bad config. */
+size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
+
+/*
+ * kvs_quantize_kv -- Q8_0 records of fp16 tiles [kv_type, see kvs_kv_type].  For each of the
+ * n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads the fp16 tile
+ * [128 tokens][128] of src_pool (laid out as an FP16 pool) and writes the Q8_0 record at the same id
+ * of dst_pool (laid out as a Q8_0 pool).  Per 32 channels of a token: d = max|x| / 127, codes
+ * round(x * (1/d)) ties away from zero, both in fp32 (an all-zero block: d = 0, codes 0); d is
+ * stored rounded to fp16.  Used for keys and values alike.  cfg->kv_type must be KVS_KV_Q8_0.
+ * n_blocks == 0 is a no-op.  Both pools 16-byte aligned.
+ */
+int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,
+                    int32_t n_blocks, void* dst_pool, kvs_stream_t stream);
+
 /*
  * kvs_build_reps -- representative keys of full blocks [KT-LC §4.3; Quest's "Reduced Keys" §3.1].
  * For each of the n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads
@@ -111,6 +137,8 @@ size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
  *   Quest: channel-wise min (r=0) and max (r=1);  Max: channel-wise max;
  *   Mean:  channel-wise mean in fp32;             Fix: rows 0, s, 2s, ... with s = 128/rep_num.
  * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.
+ * With kv_type Q8_0 the reps are taken over the cached values scale * code (exact in fp32) and stored
+ * rounded to fp16 (Mean: fp32).
  */
 int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
                    int32_t n_blocks, void* rep_pool, kvs_stream_t stream);

@@ -25,15 +25,16 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 11, decl
+    assert len(decl) == 13, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
 
 
 def test_config_struct_layout():
-    assert ctypes.sizeof(B.kvs_config) == 44
+    assert ctypes.sizeof(B.kvs_config) == 48
     assert B.kvs_config.softmax_scale.offset == 40
+    assert B.kvs_config.kv_type.offset == 44
 
 
 def cfg(**kw):
@@ -61,6 +62,8 @@ def test_status_strings():
     (dict(rep_method="fix", rep_num=0), B.KVS_ERR_INVALID_ARG),
     (dict(softmax_scale=-1.0), B.KVS_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), B.KVS_ERR_INVALID_ARG),
+    (dict(kv_type=2), B.KVS_ERR_INVALID_ARG),
+    (dict(kv_type=-1), B.KVS_ERR_INVALID_ARG),
     (dict(head_dim=64), B.KVS_ERR_UNSUPPORTED),
     (dict(block_size=64), B.KVS_ERR_UNSUPPORTED),
     (dict(num_q_heads=48, num_kv_heads=3), B.KVS_ERR_UNSUPPORTED),
@@ -70,10 +73,12 @@ def test_bad_config(kw, expect):
     c = cfg(**kw)
     assert kvs.kvs_rep_count(c) == expect
     assert kvs.kvs_rep_bytes_per_block(c) == 0
+    assert kvs.kvs_kv_bytes_per_block(c) == 0
     assert kvs.kvs_attn_workspace_size(c, 1, 10) == 0
     assert kvs.kvs_decode_step_workspace_size(c, 1, 10) == 0
     A = ALIGNED
     assert kvs.kvs_build_reps(c, A, A, 4, A, stream=0, check=False) == expect
+    assert kvs.kvs_quantize_kv(c, A, A, 4, A, stream=0, check=False) == expect
     assert kvs.kvs_score_blocks(c, A, A, A, 10, A, 1, A, stream=0, check=False) == expect
     assert kvs.kvs_topk_blocks(c, A, A, 1, 10, A, A, stream=0, check=False) == expect
     assert kvs.kvs_sparse_decode_attn(c, A, A, A, A, 10, A, 1, A, A, A, A, 1 << 30, stream=0,
@@ -90,6 +95,22 @@ def test_rep_counts_and_bytes():
     assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="quest")) == 8 * 2 * 128 * 2
     assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="mean")) == 8 * 1 * 128 * 4
     assert kvs.kvs_rep_bytes_per_block(cfg(rep_method="fix", rep_num=8)) == 8 * 8 * 128 * 2
+
+
+def test_kv_bytes_and_quantize_errors():
+    assert kvs.kvs_kv_bytes_per_block(cfg()) == 8 * 128 * 128 * 2
+    q8 = cfg(kv_type="q8_0")
+    assert kvs.kvs_kv_bytes_per_block(q8) == 8 * (128 * 128 + 128 * 4 * 2)
+    A, M, Z = ALIGNED, MISALIGNED, None
+    E = B.KVS_ERR_INVALID_ARG
+    assert kvs.kvs_quantize_kv(cfg(), A, A, 3, A, stream=0, check=False) == E  # needs kv_type Q8_0
+    assert kvs.kvs_quantize_kv(q8, A, A, -1, A, stream=0, check=False) == E
+    assert kvs.kvs_quantize_kv(q8, Z, A, 3, A, stream=0, check=False) == E
+    assert kvs.kvs_quantize_kv(q8, A, A, 3, Z, stream=0, check=False) == E
+    assert kvs.kvs_quantize_kv(q8, Z, Z, 0, Z, stream=0, check=False) == B.KVS_OK  # no-op
+    assert kvs.kvs_quantize_kv(q8, M, A, 3, A, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert kvs.kvs_quantize_kv(q8, A, A, 3, M, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert kvs.kvs_quantize_kv(q8, A, A, 70000, A, stream=0, check=False) == B.KVS_ERR_UNSUPPORTED
 
 
 def test_null_and_size_errors():

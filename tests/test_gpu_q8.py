@@ -1,0 +1,110 @@
+"""The Q8_0 cache precision on the GPU against the oracle (needs an MI355X).
+
+kv_type Q8_0 is the published llama.cpp block format that the operator's kv_type list names: per
+token and KV head, 32-channel blocks with an fp16 scale max|x|/127 and int8 codes, ties away from
+zero.  The codes and scales must match the oracle bit for bit (both take the rounding decisions in
+fp32); reps over the cached values are value-equal (Mean: relative 1e-4).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_sparse_kv_amd as kvs  # noqa: E402
+from block_sparse_kv_amd import ops  # noqa: E402
+
+import kvsynth  # noqa: E402
+from oracle import kvs_oracle as orc  # noqa: E402
+from parity import B, close_rel  # noqa: E402
+
+DEV = "cuda"
+REC = 128 * 128 + 128 * 4 * 2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def q8_cfg(Hkv=8, g=4, **kw):
+    base = dict(num_q_heads=Hkv * g, num_kv_heads=Hkv, initial_len=128, local_len=256, topk=8,
+                rep_method="quest", head_select_mode="separate", kv_type="q8_0")
+    base.update(kw)
+    return kvs.Config(**base)
+
+
+def fp16_pool(n_phys, Hkv, seed):
+    """Random fp16 tiles with the rows a quantizer can get wrong: an all-zero block, integer rows with
+    +-127, exact ties at .5, very loud and very quiet blocks (fp16-subnormal scales)."""
+    x = kvsynth.randn_fp16((n_phys, Hkv, B, 128), seed, DEV).float()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 1)
+    gain = torch.exp(torch.empty(n_phys, Hkv, B, 4).uniform_(-9.0, 7.0, generator=g)).to(DEV)
+    x = (x.view(n_phys, Hkv, B, 4, 32) * gain[..., None]).view(n_phys, Hkv, B, 128)
+    x[0, 0, 0, :32] = 0.0
+    x[0, 0, 1, :] = torch.arange(-64, 64, dtype=torch.float32, device=DEV) * 2.0  # amax 128 in block 0
+    x[0, 0, 2, :32] = torch.tensor([254.0, -127.0, 1.0, 3.0] + [0.0] * 28, device=DEV)  # ties
+    x[0, 0, 3, :] = 127.0
+    return x.to(torch.float16)
+
+
+def split_records(pool_q8):
+    """[n][Hkv][17408] bytes -> codes int8 [n][Hkv][128][128], scales fp16 [n][Hkv][128][4]."""
+    a = pool_q8.cpu().numpy()
+    codes = a[..., : 128 * 128].view(np.int8).reshape(*a.shape[:2], 128, 128)
+    scales = a[..., 128 * 128:].copy().view(np.float16).reshape(*a.shape[:2], 128, 4)
+    return codes, scales
+
+
+@pytest.mark.parametrize("Hkv", [1, 8])
+def test_quantize_bit_exact(Hkv):
+    say(f"[case] q8 quantize Hkv={Hkv}")
+    n_phys = 7
+    c = q8_cfg(Hkv=Hkv, g=1)
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(401, Hkv))
+    dst = ops.alloc_q8_pool(c, n_phys, DEV)
+    dst.fill_(0xAB)
+    ids = torch.tensor([5, 0, 3, 6], dtype=torch.int32)  # not every block, not in order
+    ops.quantize_kv(c, src, ids, dst)
+    torch.cuda.synchronize()
+    got_c, got_s = split_records(dst)
+    want_c, want_s = orc.quantize_q8_0(src.float().cpu().numpy())
+    for p in range(n_phys):
+        if p in ids.tolist():
+            assert np.array_equal(got_c[p], want_c[p]), (p, np.argwhere(got_c[p] != want_c[p])[:4])
+            assert np.array_equal(got_s[p].view(np.uint16), want_s[p].view(np.uint16)), p
+        else:  # untouched
+            assert np.all(dst[p].cpu().numpy() == 0xAB), p
+    assert int(np.abs(want_c[ids.tolist()]).max()) == 127
+
+
+@pytest.mark.parametrize("rep,rep_num", [("quest", 1), ("max", 1), ("mean", 1), ("fix", 8)])
+def test_reps_over_q8_cache(rep, rep_num):
+    say(f"[case] q8 reps {rep}/{rep_num}")
+    n_phys, Hkv = 6, 8
+    c = q8_cfg(Hkv=Hkv, rep_method=rep, rep_num=rep_num)
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(402, rep_num, len(rep)))
+    kq = ops.alloc_q8_pool(c, n_phys, DEV)
+    ids = torch.arange(n_phys, dtype=torch.int32)
+    ops.quantize_kv(c, src, ids, kq)
+    rp = ops.alloc_rep_pool(c, n_phys, DEV)
+    ops.build_reps(c, kq, torch.tensor([4, 1, 2], dtype=torch.int32), rp)
+    torch.cuda.synchronize()
+    codes, scales = split_records(kq)
+    for p in (4, 1, 2):
+        K = orc.dequantize_q8_0(codes[p], scales[p]).transpose(1, 0, 2)  # [B tokens][Hkv][d]
+        want = orc.stored_reps(orc.block_reps(K, B, rep, rep_num), rep)[0]  # [Hkv][R][d]
+        got = rp[p].double().cpu().numpy()
+        if rep == "mean":
+            close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"q8 mean reps {p}")
+        else:
+            assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
