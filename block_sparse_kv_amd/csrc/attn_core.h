@@ -46,7 +46,27 @@ __device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
 // The workgroup may be a 256-lane part of a larger one (smem then points at the part's area): every
 // part runs the same barriers.  ntok == 0 gives an empty partial (max -inf); with
 // store == false nothing is written.
-template <int G>
+// 4 Q8_0 codes (the bytes of w, lowest first) times the fp16 scale d, as 4 fp16 values in 2 words:
+// fp16(code * d), rounded once.  A code c becomes the fp16 1024 + (c + 128) by placing the biased byte
+// under the exponent pattern 0x64 (v_perm_b32), which the packed subtraction of 1152 turns into c
+// exactly; one packed multiply then applies d.
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+__device__ inline uint2 q8_dq4(uint32_t w, half2v_t d2) {
+  const uint32_t u = w ^ 0x80808080u;
+  const half2v_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const half2v_t lo = (__builtin_bit_cast(half2v_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias) * d2;
+  const half2v_t hi = (__builtin_bit_cast(half2v_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias) * d2;
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+// 8 codes (w0 then w1) with the fp16 scale in the low half of sc.
+__device__ inline uint4 q8_dq8(uint32_t w0, uint32_t w1, uint32_t sc) {
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(sc & 0xFFFFu));
+  const half2v_t d2 = {d, d};
+  const uint2 a = q8_dq4(w0, d2), b = q8_dq4(w1, d2);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+template <int G, bool Q8 = false>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
                                           const uint16_t* __restrict__ v_pool, int h, int phys, int ntok,
@@ -54,28 +74,68 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
                                           int n_parts, int part, unsigned char* smem,
                                           bool store = true) {
   const int tid = threadIdx.x & 255, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
-  const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
-  const uint16_t* Kt = k_pool + off;
-  const uint16_t* Vt = v_pool + off;
   // Every load is issued up front, in the order the data is needed -- Q, K, then V -- and without
   // branches, so the compiler keeps them all in flight and waits only for what the next step needs.
-  // Rows past ntok are still inside the tile's 32 KiB: their K only feeds logits that are masked,
-  // their V is zeroed after the load (a NaN tail times p = 0 would not be 0).
-  half8_t qb[4];  // Q^T B operand: lane l holds head lc, channels 32m + 8*lq .. +8
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * m + 8 * lq);
-    qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
-  }
+  // Rows past ntok are still inside the tile: their K only feeds logits that are masked, their V is
+  // zeroed after the load (a NaN tail times p = 0 would not be 0).
+  half8_t qb[4];  // Q^T B operand: lane l holds head lc, 8 channels per MFMA m (below)
   uint4 kr[2][4], vr[8];
+  uint2 vc[8];    // Q8_0: V codes and scales, dequantized when V is staged
+  uint32_t vs[8];
+  if constexpr (!Q8) {
+    // fp16 tile: K rows of MFMA m are channels 32m + 8*lq .. +8
+    const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
+    const uint16_t* Kt = k_pool + off;
+    const uint16_t* Vt = v_pool + off;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int tok = 32 * w + 16 * g + lc;
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * m + 8 * lq);
+      qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
+    }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + tok * kDim + 32 * m + 8 * lq);
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + tok * kDim + 32 * m + 8 * lq);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
+  } else {
+    // Q8_0 record (kv_type; llama.cpp's block format): a lane's K codes are the 32 channels
+    // 32*lq .. +32 of its token -- one Q8_0 block, one scale -- and MFMA m takes channels
+    // 32*lq + 8m .. +8 of them.  The k-slots of the product may be any permutation of the
+    // channels as long as Q^T follows it, so Q^T is loaded in the same order.
+    const size_t rec = ((size_t)phys * P.Hkv + h) * kQ8Record;
+    const unsigned char* Kq = reinterpret_cast<const unsigned char*>(k_pool) + rec;
+    const unsigned char* Vq = reinterpret_cast<const unsigned char*>(v_pool) + rec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
+      qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
+    }
+    uint4 kc[2][2];
+    uint32_t ks[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+      kc[g][0] = ld_stream16(Kq + tok * kDim + 32 * lq);
+      kc[g][1] = ld_stream16(Kq + tok * kDim + 32 * lq + 16);
+      ks[g] = *reinterpret_cast<const uint16_t*>(Kq + kQ8Codes + tok * 8 + 2 * lq);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tok = 32 * w + 4 * i + lq;
+      vc[i] = *reinterpret_cast<const uint2*>(Vq + tok * kDim + 8 * lc);
+      vs[i] = *reinterpret_cast<const uint16_t*>(Vq + kQ8Codes + tok * 8 + 2 * (lc >> 2));
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kr[g][0] = q8_dq8(kc[g][0].x, kc[g][0].y, ks[g]);
+      kr[g][1] = q8_dq8(kc[g][0].z, kc[g][0].w, ks[g]);
+      kr[g][2] = q8_dq8(kc[g][1].x, kc[g][1].y, ks[g]);
+      kr[g][3] = q8_dq8(kc[g][1].z, kc[g][1].w, ks[g]);
+    }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
   f32x4_t S[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -115,7 +175,8 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool in = 32 * w + 4 * i + lq < ntok;
-    *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
+    const uint4 v = Q8 ? q8_dq8(vc[i].x, vc[i].y, vs[i]) : vr[i];
+    *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? v : make_uint4(0, 0, 0, 0);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -361,7 +422,7 @@ __device__ inline void empty_partial(float* part_o, float* part_ml, int n_parts,
 // n_il_max : 0), a logical block id in A.sel, or a physical one when PHYS.  Items past the
 // sequence's own counts do nothing; table entries or selections outside the table give an empty
 // partial instead of a read outside the pools' rows.
-template <int G, bool IL, bool PHYS>
+template <int G, bool IL, bool PHYS, bool Q8 = false>
 __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int seq, unsigned char* smem) {
   const Params& P = A.P;
   const bool is_il = IL && x < A.n_il_max;
@@ -398,7 +459,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
     empty_partial<G>(po, pml, A.max_parts, part);
     return;
   }
-  attn_tile<G>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
+  attn_tile<G, Q8>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
 }
 
 // Merge of channels [16c, 16c + 16) of query head j of sequence seq by one wave (merge_head_wave).

@@ -255,7 +255,6 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
-  if (P.kv != kvs::kKvFp16) return KVS_ERR_UNSUPPORTED;  // Q8_0 attention: not yet
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_count || !out ||
       (!sel && P.topk > 0))
@@ -288,7 +287,6 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
-  if (P.kv != kvs::kKvFp16) return KVS_ERR_UNSUPPORTED;  // Q8_0 attention: not yet
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !k_pool || !v_pool || !rep_pool || !block_table || !seq_lens || !out)
     return KVS_ERR_INVALID_ARG;

@@ -9,6 +9,11 @@ Acceptance (same seeded inputs on both sides):
     blocks scoring at least the (k+1)-th (both within the band) is accepted.
   * Attention: max |gpu - ref| <= 2e-3, where ref is the oracle's attention over the GPU's own
     selection (a different legal selection attends different tokens).
+  * A Q8_0 cache (kv_type): the oracle works on the dequantized keys and values of its own
+    quantization of the same fp16 rows (the codes are bit-exact, tests/test_gpu_q8.py) and on reps
+    stored as the rep pool stores them (fp16, Mean fp32).  The same bounds hold: the kernels round
+    each dequantized value to fp16 once (relative 2**-11 per element), which moves the outputs by
+    about 1e-4 here.
 """
 from __future__ import annotations
 
@@ -68,6 +73,7 @@ class Case:
     def __init__(self, cfg, lens, seed, *, n_hot=0, hot_per_head=False, shuffle=True,
                  device="cuda", spare_blocks=3):
         self.cfg = cfg
+        self.q8 = getattr(cfg, "kv_type", "fp16") in ("q8_0", 1)
         seqs = []
         for i, L in enumerate(lens):
             ie, ls, cand = orc.regions(L, B, cfg.initial_len, cfg.local_len)
@@ -82,14 +88,28 @@ class Case:
         self.host = [(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy()) for s in seqs]
         self.table = self.pb.block_table.cpu().numpy()
         self.lens = list(lens)
+        self.k_pool, self.v_pool = self.pb.k_pool, self.pb.v_pool
+        if self.q8:  # the GPU pools quantized by the library, the host rows by the oracle
+            from block_sparse_kv_amd import ops
+            n_phys = self.pb.k_pool.shape[0]
+            ids = torch.arange(n_phys, dtype=torch.int32)
+            self.k_pool = ops.quantize_kv(cfg, self.pb.k_pool, ids, ops.alloc_q8_pool(cfg, n_phys, device))
+            self.v_pool = ops.quantize_kv(cfg, self.pb.v_pool, ids, ops.alloc_q8_pool(cfg, n_phys, device))
+            self.host = [(q, orc.dequantize_q8_0(*orc.quantize_q8_0(K)),
+                          orc.dequantize_q8_0(*orc.quantize_q8_0(V))) for q, K, V in self.host]
 
     # --- oracle side --------------------------------------------------------------------------
     def oracle(self, i):
         c = self.cfg
         q, K, V = self.host[i]
+        m = method_name(c.rep_method)
+        reps = None
+        if self.q8:
+            cand = orc.regions(K.shape[0], B, c.initial_len, c.local_len)[2]
+            reps = orc.stored_reps(orc.block_reps(K, B, m, c.rep_num, blocks=cand), m)
         return orc.decode_step(q, K, V, B=B, initial_len=c.initial_len, local_len=c.local_len,
-                               topk=c.topk, method=method_name(c.rep_method), rep_num=c.rep_num,
-                               mode=c.head_select_mode, scale=(c.softmax_scale or None))
+                               topk=c.topk, method=m, rep_num=c.rep_num,
+                               mode=c.head_select_mode, scale=(c.softmax_scale or None), reps=reps)
 
     def oracle_attention(self, i, sel_per_group):
         c = self.cfg

@@ -34,19 +34,19 @@ def say(*a):
     sys.stdout.flush()
 
 
-def cfg_of(Hq, Hkv, I, W, k, rep="quest", mode="separate", rep_num=1):
+def cfg_of(Hq, Hkv, I, W, k, rep="quest", mode="separate", rep_num=1, kv="fp16"):
     return kvs.Config(num_q_heads=Hq, num_kv_heads=Hkv, initial_len=I, local_len=W, topk=k,
-                      rep_method=rep, rep_num=rep_num, head_select_mode=mode)
+                      rep_method=rep, rep_num=rep_num, head_select_mode=mode, kv_type=kv)
 
 
 def build_all_reps(case):
     c = case.cfg
-    rp = ops.alloc_rep_pool(c, case.pb.k_pool.shape[0], DEV)
+    rp = ops.alloc_rep_pool(c, case.k_pool.shape[0], DEV)
     ids = []
     for i, L in enumerate(case.lens):
         ids.extend(int(x) for x in case.table[i, : L // B])
     if ids:
-        ops.build_reps(c, case.pb.k_pool, torch.tensor(ids, dtype=torch.int32), rp)
+        ops.build_reps(c, case.k_pool, torch.tensor(ids, dtype=torch.int32), rp)
     case.built_ids = ids
     return rp
 
@@ -56,7 +56,7 @@ def run_full_check(case, label):
     c, pb = case.cfg, case.pb
     say(f"[case] {label}: lens={case.lens[:6]}{'...' if len(case.lens) > 6 else ''} "
         f"Hq/Hkv={c.num_q_heads}/{c.num_kv_heads} I={c.initial_len} W={c.local_len} k={c.topk} "
-        f"rep={c.rep_method}/{c.rep_num} mode={c.head_select_mode}")
+        f"rep={c.rep_method}/{c.rep_num} mode={c.head_select_mode} kv={c.kv_type}")
     rp = build_all_reps(case)
     scores = ops.score_blocks(c, pb.q, rp, pb.block_table, pb.seq_lens)
     sel, cnt = ops.topk_blocks(c, scores, pb.seq_lens)
@@ -69,9 +69,9 @@ def run_full_check(case, label):
         for gi in range(G):
             osel[i, gi, : len(r["sel"][gi])] = torch.tensor(r["sel"][gi], dtype=torch.int32)
             ocnt[i, gi] = len(r["sel"][gi])
-    out_a = ops.sparse_decode_attn(c, pb.q, pb.k_pool, pb.v_pool, pb.block_table, pb.seq_lens,
+    out_a = ops.sparse_decode_attn(c, pb.q, case.k_pool, case.v_pool, pb.block_table, pb.seq_lens,
                                    osel[:, :, : c.topk].to(DEV), ocnt.to(DEV))
-    out_s, sel_s, cnt_s = ops.decode_step(c, pb.q, pb.k_pool, pb.v_pool, rp, pb.block_table,
+    out_s, sel_s, cnt_s = ops.decode_step(c, pb.q, case.k_pool, case.v_pool, rp, pb.block_table,
                                           pb.seq_lens)
     torch.cuda.synchronize()
     kinds, errs = [], []
@@ -107,6 +107,26 @@ SMALL = [
     (16, 1, 128, 1024, 20, "quest", "separate", 1, [280000]),    # long rows, g = 16
     (8, 8, 128, 1024, 8000, "quest", "separate", 1, [8192, 300]),  # topk past the one-wave merge's LDS
 ]
+
+
+# Q8_0 caches: the same path over int8 codes and fp16 scales (kv_type), short and long rows
+SMALL_Q8 = [
+    (32, 8, 128, 512, 12, "quest", "separate", 1, [5000, 129, 1, 7777]),
+    (32, 8, 100, 300, 5, "max", "shared", 1, [4000, 3001]),
+    (16, 16, 0, 0, 7, "fix", "separate", 8, [3000, 2048]),
+    (4, 1, 128, 200, 40, "mean", "separate", 1, [4000]),
+    (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),
+    (32, 8, 128, 1024, 20, "quest", "separate", 1, [280000]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_Q8)),
+                         ids=[f"q8-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_Q8])
+def test_small_cases_q8(idx):
+    Hq, Hkv, I, W, k, rep, mode, rn, lens = SMALL_Q8[idx]
+    c = cfg_of(Hq, Hkv, I, W, k, rep, mode, rn, kv="q8_0")
+    case = Case(c, lens, seed=kvsynth.mix_seed(77, idx), n_hot=3)
+    run_full_check(case, f"small q8 {rep}/{mode} {Hq}x{Hkv}")
 
 
 @pytest.mark.parametrize("idx", range(len(SMALL)),
@@ -239,6 +259,12 @@ def test_full_128k_shared(rep):
     ncand = 991
     case = Case(c, [131072], seed=20260002, n_hot=math.ceil(0.05 * ncand), shuffle=False)
     run_full_check(case, f"full 128K 32/8 {rep} SHARED k96")
+
+
+def test_full_128k_shared_q8():
+    c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="q8_0")
+    case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
+    run_full_check(case, "full 128K 32/8 max SHARED k96, Q8_0 cache")
 
 
 def test_full_mixed_batch_fix():
