@@ -58,6 +58,11 @@ WORKLOADS = {
                       layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260012),
     "1m": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
                layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003),
+    # the same two headline shapes over a Q8_0 cache (kv_type): int8 codes + fp16 scale per 32 channels
+    "128k-max-q8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                        layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="q8_0"),
+    "1m-q8": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
+                  layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003, kv="q8_0"),
 }
 
 
@@ -119,7 +124,8 @@ def required_bytes(w):
     T = min(ie, L) + k_eff * B + (L - ls)
     R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1)}[w["rep"]]
     rep_elem = 4 if w["rep"] == "mean" else 2
-    return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * D * 2 * 2,
+    row = D + (D // 32) * 2 if w.get("kv") == "q8_0" else D * 2  # bytes of one token's K (or V) row
+    return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * row * 2,
                 out=Hq * D * 4, tokens=T, ncand=ncand, k_eff=k_eff)
 
 
@@ -135,7 +141,7 @@ class Setup:
         self.name, self.w = name, w
         self.cfg = kvs.Config(num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], initial_len=w["I"],
                               local_len=w["W"], topk=w["k"], rep_method=w["rep"],
-                              head_select_mode=w["mode"])
+                              head_select_mode=w["mode"], kv_type=w.get("kv", "fp16"))
         L = w["L"]
         nb = math.ceil(L / B)
         ie, ls, ncand = regions(L, w["I"], w["W"])
@@ -149,6 +155,10 @@ class Setup:
             q, kp, vp, hot = kvsynth.pool_layer(kvsynth.mix_seed(w["seed"], u), L, w["Hq"], w["Hkv"],
                                                 hot_range=(lo, hi), n_hot=w["n_hot"],
                                                 hot_per_head=w["hot_per_head"], device=device)
+            if w.get("kv") == "q8_0":  # quantized by the library; the fp16 tiles are dropped
+                ids = torch.arange(nb, dtype=torch.int32)
+                kp = ops.quantize_kv(self.cfg, kp, ids, ops.alloc_q8_pool(self.cfg, nb, device))
+                vp = ops.quantize_kv(self.cfg, vp, ids, ops.alloc_q8_pool(self.cfg, nb, device))
             rp = ops.alloc_rep_pool(self.cfg, nb, device)
             ops.build_reps(self.cfg, kp, torch.arange(L // B, dtype=torch.int32), rp)
             self.units.append((q[None].contiguous(), kp, vp, rp))

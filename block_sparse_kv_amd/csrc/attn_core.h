@@ -80,8 +80,8 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   // zeroed after the load (a NaN tail times p = 0 would not be 0).
   half8_t qb[4];  // Q^T B operand: lane l holds head lc, 8 channels per MFMA m (below)
   uint4 kr[2][4], vr[8];
-  uint2 vc[8];    // Q8_0: V codes and scales, dequantized when V is staged
-  uint32_t vs[8];
+  uint4 vc[4];    // Q8_0: V codes and scales, dequantized when V is staged
+  uint32_t vs[4];
   if constexpr (!Q8) {
     // fp16 tile: K rows of MFMA m are channels 32m + 8*lq .. +8
     const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
@@ -122,11 +122,13 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       kc[g][1] = ld_stream16(Kq + tok * kDim + 32 * lq + 16);
       ks[g] = *reinterpret_cast<const uint16_t*>(Kq + kQ8Codes + tok * 8 + 2 * lq);
     }
+    // V: lane l takes channels 16*(l%8) .. +16 (half a Q8_0 block, one scale) of the wave's tokens
+    // 8i + l/8, i < 4: 16-byte code loads, staged below as two 16-byte rows of fp16
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = 32 * w + 4 * i + lq;
-      vc[i] = *reinterpret_cast<const uint2*>(Vq + tok * kDim + 8 * lc);
-      vs[i] = *reinterpret_cast<const uint16_t*>(Vq + kQ8Codes + tok * 8 + 2 * (lc >> 2));
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * w + 8 * i + (lane >> 3);
+      vc[i] = ld_stream16(Vq + tok * kDim + 16 * (lane & 7));
+      vs[i] = *reinterpret_cast<const uint16_t*>(Vq + kQ8Codes + tok * 8 + 2 * ((lane & 7) >> 1));
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -172,11 +174,22 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   ps += shfl_xor_f(ps, 32);
   // V to LDS: chunk i holds the wave's tokens 4i..4i+3, one kVRow row each
   unsigned char* vbuf = smem + w * kWaveVBytes;
+  if constexpr (Q8) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool in = 32 * w + 4 * i + lq < ntok;
-    const uint4 v = Q8 ? q8_dq8(vc[i].x, vc[i].y, vs[i]) : vr[i];
-    *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? v : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int t = 8 * i + (lane >> 3);  // the wave's token: chunk t / 4, row t % 4
+      const bool in = 32 * w + t < ntok;
+      const uint4 a = q8_dq8(vc[i].x, vc[i].y, vs[i]), b = q8_dq8(vc[i].z, vc[i].w, vs[i]);
+      unsigned char* row = vbuf + (t >> 2) * kVChunk + (t & 3) * kVRow + 32 * (lane & 7);
+      *reinterpret_cast<uint4*>(row) = in ? a : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(row + 16) = in ? b : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool in = 32 * w + 4 * i + lq < ntok;
+      *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
