@@ -38,6 +38,14 @@ Readings taken where the pages are silent (each is the spec here):
   R11 SEPARATE group score = sum over the query heads of the group (parity unpinned by the pages).
   R12 ties in top-k go to the lower block index; the selection is reported in ascending order.
   R14 attention: softmax of q.k/sqrt(d) over the attended tokens only.
+  R23 Dynamic reps (the article's fifth rep method: each token's cumulative attention score, the
+      top tokens of each block become its reps).  The article leaves the scoring method open; here
+      a token's score is the attention it receives from the n_obs observation queries -- the last
+      n_obs tokens of the prompt, at positions L-n_obs .. L-1, each attending causally (keys at
+      positions <= its own) with scale 1/sqrt(d) -- summed over those queries and over the query
+      heads of the selection group (SEPARATE: the g heads of a KV head; SHARED: all heads).  A
+      block's reps are the K rows of its rep_num highest-scoring tokens (ties to the lower token),
+      in ascending token order, and a Dynamic block is scored like Fix (sum over reps of q.rep).
   R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
       of one token's key or value row is a block with scale d = max|x| / 127 and codes
       q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
@@ -279,3 +287,60 @@ def stored_reps(reps, method: str):
     if method == MEAN:
         return reps.astype(np.float32).astype(np.float64)
     return reps.astype(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# O8. Dynamic reps  [KT-LC §4.3 rep table: Dynamic, the block's tokens with the highest cumulative
+#     attention score; reading R23]
+# ----------------------------------------------------------------------------------------------
+def token_importance(q_obs, K, mode: str, scale=None):
+    """Cumulative attention score of every cached token (reading R23).
+
+    q_obs: [n_obs][Hq][d], the queries of the last n_obs tokens of the cache (positions L-n_obs ..
+    L-1); K: [L][Hkv][d].  Returns float64 [G][L] with G = Hkv (SEPARATE) or 1 (SHARED): the sum,
+    over observation queries i and the group's query heads j, of softmax_t(scale * q_ij . K[t]) over
+    t <= L - n_obs + i (zero beyond).
+    """
+    q_obs = np.asarray(q_obs, dtype=np.float64)
+    n_obs, Hq, d = q_obs.shape
+    L, Hkv, _ = K.shape
+    assert 1 <= n_obs <= L
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    imp = np.zeros((Hkv, L))
+    for h in range(Hkv):
+        Kh = np.asarray(K[:, h, :], dtype=np.float64)
+        for i in range(n_obs):
+            p = L - n_obs + i  # position of observation query i
+            for j in range(h * g, (h + 1) * g):
+                z = (Kh[: p + 1] @ q_obs[i, j]) * scale
+                w = np.exp(z - z.max())
+                imp[h, : p + 1] += w / w.sum()
+    if mode == SEPARATE:
+        return imp
+    if mode == SHARED:
+        return imp.sum(axis=0, keepdims=True)
+    raise ValueError(mode)
+
+
+def dynamic_reps(K, imp, B: int, rep_num: int, mode: str, blocks):
+    """Reps of full blocks (reading R23): per block and KV head, the K rows of the rep_num tokens
+    with the largest importance (ties to the lower token), in ascending token order.
+
+    K: [L][Hkv][d]; imp: [G][L] from ``token_importance``.  Returns float64 [len(blocks)][Hkv][rep_num][d]
+    and the chosen token offsets [len(blocks)][Hkv][rep_num].
+    """
+    L, Hkv, d = K.shape
+    blocks = list(blocks)
+    out = np.empty((len(blocks), Hkv, rep_num, d))
+    picked = np.empty((len(blocks), Hkv, rep_num), dtype=np.int64)
+    for n, b in enumerate(blocks):
+        assert (b + 1) * B <= L, "reps are defined for full blocks only"
+        for h in range(Hkv):
+            row = imp[h if mode == SEPARATE else 0, b * B:(b + 1) * B]
+            order = sorted(range(B), key=lambda t: (-row[t], t))[:rep_num]
+            toks = sorted(order)
+            picked[n, h] = toks
+            out[n, h] = np.asarray(K[[b * B + t for t in toks], h, :], dtype=np.float64)
+    return out, picked

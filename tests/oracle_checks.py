@@ -344,10 +344,79 @@ def check_q8_integer_rows_exact(orc):
     assert np.array_equal(orc.dequantize_q8_0(codes, sc), x.astype(np.float64))
 
 
+# ---------------------------------------------------------------------------------- Dynamic reps
+def check_importance_via_sdpa(orc, seed=31):
+    """Token importance = column sums of the attention probabilities, taken from torch's float64
+    scaled_dot_product_attention with V = the identity (its output rows are the probabilities) and a
+    causal mask offset to the observation window's positions."""
+    g = np.random.default_rng(seed)
+    for (L, Hq, Hkv, n, mode) in [(37, 4, 2, 5, "separate"), (50, 6, 3, 50, "shared"), (9, 2, 2, 1, "separate")]:
+        d = 16
+        K = g.standard_normal((L, Hkv, d)).astype(np.float16)
+        q = (2 * g.standard_normal((n, Hq, d))).astype(np.float16)
+        imp = orc.token_importance(q, K, mode)
+        grp = Hq // Hkv
+        eye = torch.eye(L, dtype=torch.float64)
+        pos = torch.arange(L - n, L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos  # [n][L]
+        want = np.zeros((Hkv, L))
+        for j in range(Hq):
+            h = j // grp
+            Q = torch.tensor(q[:, j, :], dtype=torch.float64)[None, None]
+            Kt = torch.tensor(K[:, h, :], dtype=torch.float64)[None, None]
+            P = F.scaled_dot_product_attention(Q, Kt, eye[None, None], attn_mask=mask[None, None])[0, 0]
+            want[h] += P.sum(dim=0).numpy()
+        if mode == "shared":
+            want = want.sum(axis=0, keepdims=True)
+        assert np.allclose(imp, want, rtol=1e-12, atol=1e-12), np.abs(imp - want).max()
+
+
+def check_importance_mass_and_causality(orc, seed=32):
+    """Each observation query spreads one unit of attention per query head over the keys it may see,
+    so a group's importance sums to n_obs times its query heads; SHARED is the sum of SEPARATE; with
+    q = 0 every visible key gets 1/(position + 1) from each query, and a key inside the window only
+    from the queries at or after it."""
+    g = np.random.default_rng(seed)
+    L, Hq, Hkv, n, d = 60, 8, 2, 7, 16
+    K = g.standard_normal((L, Hkv, d)).astype(np.float16)
+    q = g.standard_normal((n, Hq, d)).astype(np.float16)
+    imp = orc.token_importance(q, K, "separate")
+    assert np.allclose(imp.sum(axis=1), n * (Hq // Hkv), rtol=1e-12)
+    shared = orc.token_importance(q, K, "shared")
+    assert np.allclose(shared[0], imp.sum(axis=0), rtol=1e-12)
+    # q = 0: uniform weights, so key t gets sum over the queries that see it of 1/(position+1)
+    z = orc.token_importance(np.zeros_like(q), K, "separate")
+    for t in range(L):
+        want = sum(1.0 / (L - n + i + 1) for i in range(n) if t <= L - n + i) * (Hq // Hkv)
+        assert abs(z[0, t] - want) < 1e-12, (t, z[0, t], want)
+
+
+def check_dynamic_reps_closed_forms(orc, seed=33):
+    """rep_num = B takes every row; uniform importance (q = 0, a block before the window) takes the
+    block's first rep_num rows in order; a key planted along every observation query is taken."""
+    g = np.random.default_rng(seed)
+    L, Hq, Hkv, n, d, B = 64, 4, 2, 4, 16, 8
+    K = g.standard_normal((L, Hkv, d)).astype(np.float16)
+    q = g.standard_normal((n, Hq, d)).astype(np.float16)
+    imp = orc.token_importance(q, K, "separate")
+    allr, picked = orc.dynamic_reps(K, imp, B, B, "separate", [2, 5])
+    assert np.array_equal(allr[0], np.asarray(K[16:24], np.float64).transpose(1, 0, 2))
+    z = orc.token_importance(np.zeros_like(q), K, "shared")
+    r, p = orc.dynamic_reps(K, z, B, 3, "shared", [1, 3])
+    assert p.tolist() == [[[0, 1, 2]] * Hkv] * 2
+    assert np.array_equal(r[0, :, 0], np.asarray(K[8], np.float64))
+    K2 = K.copy()
+    K2[8 * 4 + 5, 1, :] = (8.0 * np.sign(q[:, 2:4, :].astype(np.float64).sum(axis=(0, 1)))).astype(np.float16)
+    imp2 = orc.token_importance(q, K2, "separate")
+    _, p2 = orc.dynamic_reps(K2, imp2, B, 2, "separate", [4])
+    assert 5 in p2[0, 1].tolist(), p2
+
+
 ALL_CHECKS = [
     check_quest_upper_bound, check_quest_tight_and_units, check_rep_closed_forms,
     check_hand_worked, check_regions_golden, check_regions_partition,
     check_shared_is_sum_of_separate, check_gqa_mapping_via_sdpa, check_masked_attention_via_sdpa,
     check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
-    check_q8_integer_rows_exact,
+    check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
+    check_dynamic_reps_closed_forms,
 ]

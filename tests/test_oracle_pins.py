@@ -1,4 +1,6 @@
 """The oracle against what the pages and the mathematics fix (CPU only)."""
+import math
+
 import numpy as np
 import pytest
 
@@ -137,6 +139,36 @@ def _q8_deq_fp32_scale(codes, scales):
     return _orig_dequantize(codes, scales) * 1.0001
 
 
+def _importance_not_causal(q_obs, K, mode, scale=None):
+    n = q_obs.shape[0]
+    Kp = K
+    q64 = np.asarray(q_obs, np.float64)
+    L, Hkv, d = K.shape
+    g = q64.shape[1] // Hkv
+    imp = np.zeros((Hkv, L))
+    for h in range(Hkv):
+        for i in range(n):
+            for j in range(h * g, (h + 1) * g):
+                z = (np.asarray(Kp[:, h], np.float64) @ q64[i, j]) / math.sqrt(d)
+                w = np.exp(z - z.max())
+                imp[h] += w / w.sum()
+    return imp if mode == orc.SEPARATE else imp.sum(axis=0, keepdims=True)
+
+
+def _dynamic_ties_high(K, imp, B, rep_num, mode, blocks):
+    L, Hkv, d = K.shape
+    blocks = list(blocks)
+    out = np.empty((len(blocks), Hkv, rep_num, d))
+    picked = np.empty((len(blocks), Hkv, rep_num), dtype=np.int64)
+    for n, b in enumerate(blocks):
+        for h in range(Hkv):
+            row = imp[h if mode == orc.SEPARATE else 0, b * B:(b + 1) * B]
+            toks = sorted(sorted(range(B), key=lambda t: (-row[t], -t))[:rep_num])
+            picked[n, h] = toks
+            out[n, h] = np.asarray(K[[b * B + t for t in toks], h, :], np.float64)
+    return out, picked
+
+
 _orig_quantize = orc.quantize_q8_0
 _orig_dequantize = orc.dequantize_q8_0
 _orig_head_scores = orc.head_scores
@@ -161,6 +193,8 @@ MUTANTS = [
     ("quantize_q8_0", _q8_scale_128),
     ("quantize_q8_0", _q8_block_16),
     ("dequantize_q8_0", _q8_deq_fp32_scale),
+    ("token_importance", _importance_not_causal),
+    ("dynamic_reps", _dynamic_ties_high),
 ]
 
 
