@@ -25,16 +25,18 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_MISALIGNED, KVS_ERR_WORKSPACE, \
     KVS_ERR_HIP = 0, -1, -2, -3, -4, -5
-REP_QUEST, REP_MAX, REP_MEAN, REP_FIX = 0, 1, 2, 3
+REP_QUEST, REP_MAX, REP_MEAN, REP_FIX, REP_DYNAMIC = 0, 1, 2, 3, 4
 HEADS_SEPARATE, HEADS_SHARED = 0, 1
 KV_FP16, KV_Q8_0 = 0, 1
 KV_NAMES = {"fp16": KV_FP16, "q8_0": KV_Q8_0}
-REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FIX}
+REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FIX,
+             "dynamic": REP_DYNAMIC}
 MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
 
 EXPORTS = (
     "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block",
-    "kvs_kv_bytes_per_block", "kvs_quantize_kv", "kvs_build_reps",
+    "kvs_kv_bytes_per_block", "kvs_quantize_kv", "kvs_build_reps", "kvs_importance_workspace_size",
+    "kvs_token_importance", "kvs_build_dynamic_reps",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step",
 )
@@ -99,6 +101,12 @@ _lib.kvs_quantize_kv.restype = ctypes.c_int
 _lib.kvs_quantize_kv.argtypes = [_CFG, _P, _P, _I, _P, _P]
 _lib.kvs_build_reps.restype = ctypes.c_int
 _lib.kvs_build_reps.argtypes = [_CFG, _P, _P, _I, _P, _P]
+_lib.kvs_importance_workspace_size.restype = _S
+_lib.kvs_importance_workspace_size.argtypes = [_CFG, _I, _I, _I]
+_lib.kvs_token_importance.restype = ctypes.c_int
+_lib.kvs_token_importance.argtypes = [_CFG, _P, _I, _P, _P, _I, _P, _I, _P, _P, _S, _P]
+_lib.kvs_build_dynamic_reps.restype = ctypes.c_int
+_lib.kvs_build_dynamic_reps.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
 _lib.kvs_score_blocks.restype = ctypes.c_int
 _lib.kvs_score_blocks.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
 _lib.kvs_topk_blocks.restype = ctypes.c_int
@@ -175,6 +183,26 @@ def kvs_build_reps(cfg, k_pool, phys_block_ids, n_blocks, rep_pool, stream=None,
     st = _lib.kvs_build_reps(_cfg(cfg), _ptr(k_pool), _ptr(phys_block_ids), n_blocks,
                              _ptr(rep_pool), _stream(stream))
     return _check(st, "kvs_build_reps") if check else st
+
+
+def kvs_importance_workspace_size(cfg, batch, max_blocks_per_seq, n_obs) -> int:
+    return _lib.kvs_importance_workspace_size(_cfg(cfg), batch, max_blocks_per_seq, n_obs)
+
+
+def kvs_token_importance(cfg, q_obs, n_obs, k_pool, block_table, max_blocks_per_seq, seq_lens, batch,
+                         importance, workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvs_token_importance(_cfg(cfg), _ptr(q_obs), n_obs, _ptr(k_pool), _ptr(block_table),
+                                   max_blocks_per_seq, _ptr(seq_lens), batch, _ptr(importance),
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(st, "kvs_token_importance") if check else st
+
+
+def kvs_build_dynamic_reps(cfg, k_pool, importance, block_table, max_blocks_per_seq, seq_lens, batch,
+                           rep_pool, stream=None, check=True):
+    st = _lib.kvs_build_dynamic_reps(_cfg(cfg), _ptr(k_pool), _ptr(importance), _ptr(block_table),
+                                     max_blocks_per_seq, _ptr(seq_lens), batch, _ptr(rep_pool),
+                                     _stream(stream))
+    return _check(st, "kvs_build_dynamic_reps") if check else st
 
 
 def kvs_score_blocks(cfg, q, rep_pool, block_table, max_blocks_per_seq, seq_lens, batch, scores,

@@ -27,6 +27,9 @@ int rep_count_of(const kvs_config* c) {
     case KVS_REP_FIX:
       if (c->rep_num < 1 || c->rep_num > c->block_size || c->block_size % c->rep_num) return -1;
       return c->rep_num;
+    case KVS_REP_DYNAMIC:
+      if (c->rep_num < 1 || c->rep_num > c->block_size) return -1;
+      return c->rep_num;
     default: return -1;
   }
 }
@@ -38,7 +41,7 @@ int make_params(const kvs_config* c, Params* P) {
     return KVS_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads) return KVS_ERR_INVALID_ARG;
   if (c->initial_len < 0 || c->local_len < 0 || c->topk < 0) return KVS_ERR_INVALID_ARG;
-  if (c->rep_method < KVS_REP_QUEST || c->rep_method > KVS_REP_FIX) return KVS_ERR_INVALID_ARG;
+  if (c->rep_method < KVS_REP_QUEST || c->rep_method > KVS_REP_DYNAMIC) return KVS_ERR_INVALID_ARG;
   if (c->head_select_mode != KVS_HEADS_SEPARATE && c->head_select_mode != KVS_HEADS_SHARED)
     return KVS_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
@@ -202,7 +205,7 @@ int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phy
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
-  if (n_blocks < 0) return KVS_ERR_INVALID_ARG;
+  if (n_blocks < 0 || P.method == kvs::kDynamic) return KVS_ERR_INVALID_ARG;
   if (n_blocks == 0) return KVS_OK;
   if (!k_pool || !phys_block_ids || !rep_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
@@ -210,6 +213,54 @@ int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phy
   return hip_status(kvs::launch_build_reps(P, k_pool, phys_block_ids, n_blocks, cfg->rep_num,
                                            rep_pool, static_cast<hipStream_t>(stream)),
                     "kvs_build_reps");
+}
+
+size_t kvs_importance_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
+                                     int32_t n_obs) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
+  if (n_obs < 1 || n_obs > 4096) return 0;
+  return round_up(kvs::token_importance_ws_bytes(P, batch, max_blocks_per_seq, n_obs));
+}
+
+int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs, const void* k_pool,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t batch, float* importance, void* workspace,
+                         size_t workspace_bytes, kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (n_obs < 1) return KVS_ERR_INVALID_ARG;
+  if (n_obs > 4096 || P.kv != kvs::kKvFp16 || batch > 65535 || P.Hkv > 65535) return KVS_ERR_UNSUPPORTED;
+  if (!q_obs || !k_pool || !block_table || !seq_lens || !importance) return KVS_ERR_INVALID_ARG;
+  if (!aligned(q_obs, 16) || !aligned(k_pool, 16)) return KVS_ERR_MISALIGNED;
+  const size_t need = round_up(kvs::token_importance_ws_bytes(P, batch, max_blocks_per_seq, n_obs));
+  if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
+  return hip_status(kvs::launch_token_importance(P, q_obs, n_obs, k_pool, block_table, max_blocks_per_seq,
+                                                 seq_lens, batch, importance, workspace,
+                                                 static_cast<hipStream_t>(stream)),
+                    "kvs_token_importance");
+}
+
+int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const float* importance,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, void* rep_pool,
+                           kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (P.method != kvs::kDynamic) return KVS_ERR_INVALID_ARG;
+  if (P.kv != kvs::kKvFp16 || batch > 65535) return KVS_ERR_UNSUPPORTED;
+  if (!k_pool || !importance || !block_table || !seq_lens || !rep_pool) return KVS_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  clear_stale_error();
+  return hip_status(kvs::launch_dynamic_reps(P, k_pool, importance, block_table, max_blocks_per_seq,
+                                             seq_lens, batch, rep_pool, static_cast<hipStream_t>(stream)),
+                    "kvs_build_dynamic_reps");
 }
 
 int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,

@@ -15,7 +15,7 @@ constexpr int kQ8Group = 32;
 constexpr int kQ8Codes = kBlock * kDim;                                // bytes of codes
 constexpr int kQ8Record = kQ8Codes + kBlock * (kDim / kQ8Group) * 2;  // 17408 bytes
 
-enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3 };
+enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3, kDynamic = 4 };  // Dynamic: scored like Fix
 enum Mode { kSeparate = 0, kShared = 1 };
 enum KvType { kKvFp16 = 0, kKvQ8 = 1 };
 

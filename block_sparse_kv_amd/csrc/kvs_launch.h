@@ -21,6 +21,13 @@ AttnPlan attn_plan(const Params& P, int batch, int max_blocks);
 
 hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
                               hipStream_t s);
+hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs, const void* k_pool,
+                                   const int32_t* table, int max_blocks, const int32_t* seq_lens, int batch,
+                                   float* imp, void* ws, hipStream_t s);
+size_t token_importance_ws_bytes(const Params& P, int batch, int max_blocks, int n_obs);
+hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float* imp, const int32_t* table,
+                               int max_blocks, const int32_t* seq_lens, int batch, void* rep_pool,
+                               hipStream_t s);
 hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
                              int rep_num, void* rep_pool, hipStream_t s);
 hipError_t launch_score(const Params& P, const void* q, const void* rep_pool, const int32_t* table,

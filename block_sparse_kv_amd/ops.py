@@ -43,6 +43,24 @@ def build_reps(cfg, k_pool, phys_ids: torch.Tensor, rep_pool: torch.Tensor):
     return rep_pool
 
 
+def token_importance(cfg, q_obs, k_pool, block_table, seq_lens):
+    """q_obs [batch][n_obs][Hq][128] fp16 -> importance [batch][G][max_blocks * 128] fp32."""
+    batch, mb = block_table.shape
+    n_obs = q_obs.shape[1]
+    imp = torch.empty((batch, cfg.groups, mb * 128), dtype=torch.float32, device=q_obs.device)
+    need = B.kvs_importance_workspace_size(cfg, batch, mb, n_obs)
+    ws = workspace(need, q_obs.device)
+    B.kvs_token_importance(cfg, q_obs.contiguous(), n_obs, k_pool, block_table, mb, seq_lens, batch,
+                           imp, ws, ws.numel())
+    return imp
+
+
+def build_dynamic_reps(cfg, k_pool, importance, block_table, seq_lens, rep_pool):
+    batch, mb = block_table.shape
+    B.kvs_build_dynamic_reps(cfg, k_pool, importance, block_table, mb, seq_lens, batch, rep_pool)
+    return rep_pool
+
+
 def score_blocks(cfg, q, rep_pool, block_table, seq_lens):
     batch, mb = block_table.shape
     scores = torch.empty((batch, cfg.groups, mb), dtype=torch.float32, device=q.device)

@@ -70,8 +70,10 @@ enum {
   KVS_ERR_HIP = -5          /* a kernel launch failed                               */
 };
 
-/* Rep methods [KT-LC §4.3]; Dynamic (cumulative prefill attention) is not provided. */
-typedef enum { KVS_REP_QUEST = 0, KVS_REP_MAX = 1, KVS_REP_MEAN = 2, KVS_REP_FIX = 3 } kvs_rep_method;
+/* Rep methods [KT-LC §4.3].  Dynamic reps are built from token scores (kvs_token_importance,
+ * kvs_build_dynamic_reps) and scored like Fix. */
+typedef enum { KVS_REP_QUEST = 0, KVS_REP_MAX = 1, KVS_REP_MEAN = 2, KVS_REP_FIX = 3,
+               KVS_REP_DYNAMIC = 4 } kvs_rep_method;
 
 /* head_select_mode [KT-LC §4.5]: SEPARATE = every KV head selects its own blocks from the scores
  * of its query heads (summed); SHARED = one selection for all heads from the sum over all
@@ -94,7 +96,7 @@ typedef struct kvs_config {
   int32_t local_len;        /* local_windows_len, >= 0 [KT-LC §4.2, §4.5]                    */
   int32_t topk;             /* second_block_count: Context blocks selected, >= 0 [KT-LC §4.5] */
   int32_t rep_method;       /* kvs_rep_method (anchor_type)                                  */
-  int32_t rep_num;          /* anchor_num: Fix only, divides B, 1..B; ignored otherwise      */
+  int32_t rep_num;          /* anchor_num: Fix (divides B) and Dynamic, 1..B; ignored otherwise */
   int32_t head_select_mode; /* kvs_head_select_mode                                          */
   float softmax_scale;      /* attention logit scale; 0 => 1/sqrt(head_dim) [KT-LC §4.6]     */
   int32_t kv_type;          /* kvs_kv_type of k_pool and v_pool                              */
@@ -136,18 +138,52 @@ int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* 
  * the 128x128 key tile and writes its reps into rep_pool at the same physical id:
  *   Quest: channel-wise min (r=0) and max (r=1);  Max: channel-wise max;
  *   Mean:  channel-wise mean in fp32;             Fix: rows 0, s, 2s, ... with s = 128/rep_num.
- * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.
+ * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.  Dynamic reps come
+ * from kvs_build_dynamic_reps instead (KVS_ERR_INVALID_ARG here).
  * With kv_type Q8_0 the reps are taken over the cached values scale * code (exact in fp32) and stored
  * rounded to fp16 (Mean: fp32).
  */
 int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
                    int32_t n_blocks, void* rep_pool, kvs_stream_t stream);
 
+/* Workspace bytes kvs_token_importance needs (host query; 0 on bad config or sizes). */
+size_t kvs_importance_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq,
+                                     int32_t n_obs);
+
+/*
+ * kvs_token_importance -- cumulative attention score of every cached token, the input of Dynamic
+ * reps [KT-LC §4.3 rep table: Dynamic takes the tokens of a block with the highest accumulated
+ * attention score; the scoring method is left open there and is this one].  q_obs: fp16
+ * [batch][n_obs][Hq][128], the queries of each sequence's last n_obs cached tokens (positions
+ * L-n_obs .. L-1, in order; 1 <= n_obs <= L and n_obs <= 4096).  importance: fp32
+ * [batch][G][max_blocks_per_seq * 128]; for token t of a sequence and group gr (SEPARATE: KV head;
+ * SHARED: 0):
+ *   importance = sum over observation queries i and the group's query heads j of
+ *                softmax_t'(scale * q_ij . K[t']) at t' = t, over the keys t' <= L - n_obs + i,
+ * zero for t >= L.  Accumulation fp32.  kv_type must be FP16 (KVS_ERR_UNSUPPORTED otherwise).
+ * workspace: device, >= kvs_importance_workspace_size bytes, 256-byte aligned, scratch.
+ */
+int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs, const void* k_pool,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t batch, float* importance, void* workspace,
+                         size_t workspace_bytes, kvs_stream_t stream);
+
+/*
+ * kvs_build_dynamic_reps -- Dynamic reps [KT-LC §4.3].  For every full block b of every sequence
+ * (b*128 + 128 <= L) and every KV head h: the K rows of the rep_num tokens of the block with the
+ * highest importance (group of h; ties to the lower token), in ascending token order, written to
+ * rep_pool at the block's physical id.  cfg->rep_method must be KVS_REP_DYNAMIC; kv_type FP16.
+ */
+int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const float* importance,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, void* rep_pool,
+                           kvs_stream_t stream);
+
 /*
  * kvs_score_blocks -- block relevance [KT-LC §3.1 Quest bound; §4.3 rep similarity; §4.5 modes].
  * For every candidate block b of every sequence and query head j (KV head h = j/g):
  *   Quest:        s_j(b) = sum_c max(q_jc * kmax_hbc, q_jc * kmin_hbc)
- *   Max/Mean/Fix: s_j(b) = sum_r sum_c q_jc * rep_hbrc
+ *   Max/Mean/Fix/Dynamic: s_j(b) = sum_r sum_c q_jc * rep_hbrc
  * (no softmax scale), then SEPARATE: scores[h][b] = sum of s_j over the query heads of h;
  * SHARED: scores[0][b] = sum over all query heads.  Non-candidates get -INFINITY.
  * Accumulation is fp32.

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 13, decl
+    assert len(decl) == 16, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -57,6 +57,8 @@ def test_status_strings():
     (dict(local_len=-5), B.KVS_ERR_INVALID_ARG),
     (dict(topk=-1), B.KVS_ERR_INVALID_ARG),
     (dict(rep_method=7), B.KVS_ERR_INVALID_ARG),
+    (dict(rep_method="dynamic", rep_num=0), B.KVS_ERR_INVALID_ARG),
+    (dict(rep_method="dynamic", rep_num=129), B.KVS_ERR_INVALID_ARG),
     (dict(head_select_mode=3), B.KVS_ERR_INVALID_ARG),
     (dict(rep_method="fix", rep_num=3), B.KVS_ERR_INVALID_ARG),   # must divide 128
     (dict(rep_method="fix", rep_num=0), B.KVS_ERR_INVALID_ARG),
@@ -111,6 +113,34 @@ def test_kv_bytes_and_quantize_errors():
     assert kvs.kvs_quantize_kv(q8, M, A, 3, A, stream=0, check=False) == B.KVS_ERR_MISALIGNED
     assert kvs.kvs_quantize_kv(q8, A, A, 3, M, stream=0, check=False) == B.KVS_ERR_MISALIGNED
     assert kvs.kvs_quantize_kv(q8, A, A, 70000, A, stream=0, check=False) == B.KVS_ERR_UNSUPPORTED
+
+
+def test_dynamic_rep_errors():
+    dyn = cfg(rep_method="dynamic", rep_num=3)      # rep_num need not divide the block
+    A, M, Z = ALIGNED, MISALIGNED, None
+    E = B.KVS_ERR_INVALID_ARG
+    assert kvs.kvs_rep_count(dyn) == 3
+    assert kvs.kvs_rep_bytes_per_block(dyn) == 8 * 3 * 128 * 2
+    assert kvs.kvs_build_reps(dyn, A, A, 3, A, stream=0, check=False) == E   # needs the scores
+    assert kvs.kvs_build_dynamic_reps(cfg(), A, A, A, 10, A, 1, A, stream=0, check=False) == E
+    assert kvs.kvs_build_dynamic_reps(dyn, A, Z, A, 10, A, 1, A, stream=0, check=False) == E
+    assert kvs.kvs_build_dynamic_reps(dyn, M, A, A, 10, A, 1, A, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert kvs.kvs_build_dynamic_reps(cfg(rep_method="dynamic", kv_type="q8_0"), A, A, A, 10, A, 1, A,
+                                      stream=0, check=False) == B.KVS_ERR_UNSUPPORTED
+    need = kvs.kvs_importance_workspace_size(dyn, 2, 100, 16)
+    assert need >= 2 * 8 * 16 * 4 * 100 * 8 and need % 256 == 0
+    assert kvs.kvs_importance_workspace_size(dyn, 2, 100, 0) == 0
+    assert kvs.kvs_importance_workspace_size(dyn, 2, 100, 4097) == 0
+    run = lambda c, n, ws, wb, q=A: kvs.kvs_token_importance(c, q, n, A, A, 100, A, 2, A, ws, wb, stream=0,
+                                                           check=False)
+    assert run(dyn, 0, A, need) == E
+    assert run(dyn, 5000, A, need) == B.KVS_ERR_UNSUPPORTED
+    assert run(dyn, 16, A, need, q=Z) == E
+    assert run(dyn, 16, A, need, q=M) == B.KVS_ERR_MISALIGNED
+    assert run(dyn, 16, A, need - 256) == B.KVS_ERR_WORKSPACE
+    assert run(dyn, 16, Z, need) == B.KVS_ERR_WORKSPACE
+    assert run(dyn, 16, A + 16, need) == B.KVS_ERR_MISALIGNED
+    assert run(cfg(kv_type="q8_0"), 16, A, need) == B.KVS_ERR_UNSUPPORTED
 
 
 def test_null_and_size_errors():
