@@ -58,6 +58,10 @@ WORKLOADS = {
                       layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260012),
     "1m": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
                layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003),
+    # the article's base configuration: Dynamic reps, one per block, from 32 observation queries
+    "128k-dynamic": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="dynamic", rep_num=1,
+                         n_obs=32, mode="shared", layers=1, replicas=16, n_hot=50, hot_per_head=False,
+                         seed=20260022),
     # the same two headline shapes over a Q8_0 cache (kv_type): int8 codes + fp16 scale per 32 channels
     "128k-max-q8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
                         layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="q8_0"),
@@ -122,7 +126,7 @@ def required_bytes(w):
     ie, ls, ncand = regions(L, w["I"], w["W"])
     k_eff = min(w["k"], ncand)
     T = min(ie, L) + k_eff * B + (L - ls)
-    R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1)}[w["rep"]]
+    R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1), "dynamic": w.get("rep_num", 1)}[w["rep"]]
     rep_elem = 4 if w["rep"] == "mean" else 2
     row = D + (D // 32) * 2 if w.get("kv") == "q8_0" else D * 2  # bytes of one token's K (or V) row
     return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * row * 2,
@@ -141,7 +145,8 @@ class Setup:
         self.name, self.w = name, w
         self.cfg = kvs.Config(num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], initial_len=w["I"],
                               local_len=w["W"], topk=w["k"], rep_method=w["rep"],
-                              head_select_mode=w["mode"], kv_type=w.get("kv", "fp16"))
+                              rep_num=w.get("rep_num", 1), head_select_mode=w["mode"],
+                              kv_type=w.get("kv", "fp16"))
         L = w["L"]
         nb = math.ceil(L / B)
         ie, ls, ncand = regions(L, w["I"], w["W"])
@@ -160,7 +165,13 @@ class Setup:
                 kp = ops.quantize_kv(self.cfg, kp, ids, ops.alloc_q8_pool(self.cfg, nb, device))
                 vp = ops.quantize_kv(self.cfg, vp, ids, ops.alloc_q8_pool(self.cfg, nb, device))
             rp = ops.alloc_rep_pool(self.cfg, nb, device)
-            ops.build_reps(self.cfg, kp, torch.arange(L // B, dtype=torch.int32), rp)
+            if w["rep"] == "dynamic":  # token scores from the last n_obs queries, then the reps
+                q_obs = kvsynth.randn_fp16((1, w["n_obs"], w["Hq"], D), kvsynth.mix_seed(w["seed"], u, 9), device)
+                self.dyn = (q_obs, kp)
+                imp = ops.token_importance(self.cfg, q_obs, kp, self.table, self.lens)
+                ops.build_dynamic_reps(self.cfg, kp, imp, self.table, self.lens, rp)
+            else:
+                ops.build_reps(self.cfg, kp, torch.arange(L // B, dtype=torch.int32), rp)
             self.units.append((q[None].contiguous(), kp, vp, rp))
         torch.cuda.synchronize()
         log(f"[setup] {name}: {n_units} cache units of {L} tokens generated in {time.time() - t0:.1f}s")
@@ -316,6 +327,24 @@ def measure(name, steps, warmup, device, reuse=True):
                traffic_bytes_per_step=traffic_per_step(name), setup=st)
     log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
         f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+    if w["rep"] == "dynamic":  # the per-prompt cost of Dynamic reps: token scores + reps of one cache
+        from block_sparse_kv_amd import ops
+        q_obs, kp = st.dyn
+        rp = ops.alloc_rep_pool(st.cfg, st.nb, device)
+        times = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            imp = ops.token_importance(st.cfg, q_obs, kp, st.table, st.lens)
+            ops.build_dynamic_reps(st.cfg, kp, imp, st.table, st.lens, rp)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        kbytes = 2 * w["Hkv"] * w["L"] * D * 2  # K read by both passes over the scores
+        res["dynamic_reps_build"] = dict(ms=min(times[1:]), n_obs=w["n_obs"], k_bytes_read=kbytes,
+                                         hbm_gbs=kbytes / (min(times[1:]) * 1e-3) / 1e9)
+        log(f"[bench] {name} token scores + Dynamic reps of one {w['L']}-token cache: "
+            f"{min(times[1:]):.3f} ms ({kbytes / (min(times[1:]) * 1e-3) / 1e9:.0f} GB/s on K)")
     if not reuse:
         return res
     # selection reuse: attention only, with each unit's kept selection (no scoring, no top-k)

@@ -5,15 +5,18 @@
 // observation queries (the last n_obs tokens of the cache, each attending causally, scale
 // 1/sqrt(d)), summed over those queries and the query heads of the selection group.
 //
-// The probabilities need each query row's softmax normaliser over all of its keys, so three passes:
-//  1. imp_stats_kernel, one workgroup per (block, KV head, sequence): S = K Q^T on the matrix cores
-//     for every row (observation query, query head of the KV head), 16 rows at a time, K in the
-//     A-operand layout straight from HBM (loaded once per tile); per row the tile's max and sum of
-//     exp2 in the exp2 domain -> partials [seq][h][row][block].
-//  2. imp_merge_kernel, one wave per (sequence, KV head, row): log-sum-exp of the row's partials.
-//  3. imp_accum_kernel, one workgroup per (block, sequence): for every KV head the same products
-//     again, p = exp2(z - M) / l summed over the rows of a DPP row of 16 lanes, then over row groups
-//     and (SHARED) KV heads in registers, and each token's total stored once.
+// The probabilities need each query row's softmax normaliser over all of its keys, so the scores
+// take three passes over K (the fourth only for SHARED):
+//  1. imp_stats_kernel, one workgroup per (block, KV head, sequence): the K tile in the A-operand
+//     layout straight from HBM and the rows' queries staged in LDS are requested together; then
+//     S = K Q^T on the matrix cores for every row (observation query, query head of the KV head),
+//     16 rows at a time, and each wave keeps its 32 tokens' max and sum of exp2 per row -- a
+//     partial per (row, wave), so no barrier orders the waves.
+//  2. imp_merge_kernel, one workgroup per (sequence, KV head, row): log-sum-exp of the row's partials.
+//  3. imp_accum_kernel, one workgroup per (block, KV head, sequence): the same products again,
+//     p = exp2(z - M) / l summed over the 16 rows of a DPP row and over row groups in registers;
+//     SEPARATE stores the score row of the KV head, SHARED a per-head row that
+//  4. imp_sum_kernel adds over the KV heads.
 // dyn_reps_kernel: one wave per (block, KV head, sequence) ranks the block's 128 scores by counting
 // (higher score, or equal and lower token, beats) and copies the K rows of the rep_num best, in
 // ascending token order, into the rep pool; a Dynamic block is then scored like Fix.
@@ -35,20 +38,43 @@ __device__ inline void load_k_tile(const uint16_t* __restrict__ k_pool, size_t t
     for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + (32 * w + 16 * g + lc) * kDim + 32 * m + 8 * lq);
 }
 
-// Q^T B operand of rows rg*16 .. +16 of KV head h: row r = observation i * g + head j of the group;
-// lane (lc, lq) holds row lc, channels 32m + 8lq .. +8.  Rows past n_rows are zero.
-__device__ inline void load_q_rows(const uint16_t* __restrict__ q_seq, int h, int g, int Hq, int n_rows,
-                                   int rg, half8_t (&qb)[4]) {
-  const int lane = threadIdx.x & 63, lq = lane >> 4, lc = lane & 15;
-  const int r = rg * 16 + lc;
-  const bool ok = r < n_rows;
-  const int rr = ok ? r : 0;
-  const uint16_t* qr = q_seq + ((size_t)(rr / g) * Hq + h * g + rr % g) * kDim;
+constexpr int kImpRows = 128;  // rows (observation query, query head) staged in LDS at a time
+
+// Rows [r0, r0 + kImpRows) of KV head h into LDS, 256 B each: row r = observation r >> gsh, query head
+// (h << gsh) + (r & (g - 1)) (g = 2^gsh query heads per KV head).  Rows past n_rows are zero.  All 8
+// loads of a lane are issued, with clamped rows and no branch, before the first LDS store.
+__device__ inline void stage_q_rows(const uint16_t* __restrict__ q_seq, int h, int gsh, int Hq, int n_rows,
+                                    int r0, uint4* qs) {
+  constexpr int U = kImpRows * 16 / 256;
+  uint4 v[U];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint4 v = *reinterpret_cast<const uint4*>(qr + 32 * m + 8 * lq);
-    qb[m] = __builtin_bit_cast(half8_t, ok ? v : make_uint4(0, 0, 0, 0));
+  for (int u = 0; u < U; ++u) {
+    const int x = threadIdx.x + 256 * u, r = r0 + x / 16, c = x % 16;
+    const int rr = r < n_rows ? r : 0;
+    v[u] = *reinterpret_cast<const uint4*>(
+        q_seq + ((size_t)(rr >> gsh) * Hq + (h << gsh) + (rr & ((1 << gsh) - 1))) * kDim + 8 * c);
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int x = threadIdx.x + 256 * u;
+    qs[x] = r0 + x / 16 < n_rows ? v[u] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Q^T B operand of staged rows rg*16 .. +16: lane (lc, lq) holds row lc, channels 32m + 8lq .. +8.
+__device__ inline void q_rows_from_lds(const uint4* qs, int rg, half8_t (&qb)[4]) {
+  const int lane = threadIdx.x & 63, lq = lane >> 4, lc = lane & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qb[m] = __builtin_bit_cast(half8_t, qs[(rg * 16 + lc) * 16 + 4 * m + lq]);
+}
+
+// S = K Q^T for token group gg of this wave and the 16 rows of qb (lane: tokens 4lq + i, row lc).
+__device__ inline f32x4_t imp_s(const uint4 (&kr)[2][4], const half8_t (&qb)[4], int gg) {
+  f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[gg][m]), qb[m], S, 0, 0, 0);
+  return S;
 }
 
 }  // namespace
@@ -58,132 +84,156 @@ __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t
                                                         const int32_t* __restrict__ table, int max_blocks,
                                                         const int32_t* __restrict__ seq_lens,
                                                         float2* __restrict__ part) {
-  __shared__ float red[4][16];
+  __shared__ uint4 qs[kImpRows * 16];
   const int b = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
-  const int L = seq_lens[seq], g = P.g, n_rows = n_obs * g, n_rg = (n_rows + 15) / 16;
-  float2* out = part + ((size_t)seq * P.Hkv + h) * (size_t)n_rows * max_blocks;
+  const int L = seq_lens[seq], gsh = __builtin_ctz(P.g), n_rows = n_obs * P.g;
+  const int n_sub = max_blocks * 4;  // partials per row: one per (block, wave)
+  float2* out = part + ((size_t)seq * P.Hkv + h) * (size_t)n_rows * n_sub;
   const int v = b * kBlock < L ? table[(size_t)seq * max_blocks + b] : -1;
   if (v < 0) {  // a tile with no keys (past the sequence or unmapped)
-    for (int r = tid; r < n_rows; r += 256) out[(size_t)r * max_blocks + b] = make_float2(-INFINITY, 0.f);
+    for (int x = tid; x < n_rows * 4; x += 256) out[(size_t)(x / 4) * n_sub + b * 4 + x % 4] = make_float2(-INFINITY, 0.f);
     return;
   }
   uint4 kr[2][4];
   load_k_tile(k_pool, (size_t)v * P.Hkv + h, kr);
   const uint16_t* q_seq = q_obs + (size_t)seq * n_obs * P.Hq * kDim;
-  for (int rg = 0; rg < n_rg; ++rg) {
-    half8_t qb[4];
-    load_q_rows(q_seq, h, g, P.Hq, n_rows, rg, qb);
-    const int r = rg * 16 + lc;
-    const int last = L - n_obs + (r < n_rows ? r / g : 0);  // the row's own position: its last key
-    float z[2][4], mx = -INFINITY;
+  for (int r0 = 0; r0 < n_rows; r0 += kImpRows) {
+    if (r0 > 0) __syncthreads();  // every wave is done with the previous rows
+    stage_q_rows(q_seq, h, gsh, P.Hq, n_rows, r0, qs);
+    __syncthreads();
+    const int n_rg = (min(kImpRows, n_rows - r0) + 15) / 16;
+    for (int rg = 0; rg < n_rg; ++rg) {
+      half8_t qb[4];
+      q_rows_from_lds(qs, rg, qb);
+      const int r = r0 + rg * 16 + lc;
+      const int last = L - n_obs + (r < n_rows ? r >> gsh : 0);  // the row's own position: its last key
+      float z[2][4], mx = -INFINITY;
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+      for (int gg = 0; gg < 2; ++gg) {
+        const f32x4_t S = imp_s(kr, qb, gg);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[gg][m]), qb[m], S, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
-        z[gg][i] = r < n_rows && t <= last ? S[i] * P.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[gg][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
+          z[gg][i] = r < n_rows && t <= last ? S[i] * P.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, z[gg][i]);
+        }
       }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));  // the wave's 32 tokens, row lc
+      float sm = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm += exp2_diff(z[gg][i], mx);
+      sm += shfl_xor_f(sm, 16);
+      sm += shfl_xor_f(sm, 32);
+      if (lq == 0 && r < n_rows) out[(size_t)r * n_sub + b * 4 + w] = make_float2(mx, sm);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (lq == 0) red[w][lc] = mx;
-    __syncthreads();
-    const float tm = fmaxf(fmaxf(red[0][lc], red[1][lc]), fmaxf(red[2][lc], red[3][lc]));
-    __syncthreads();
-    float sm = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm += exp2_diff(z[gg][i], tm);
-    sm += shfl_xor_f(sm, 16);
-    sm += shfl_xor_f(sm, 32);
-    if (lq == 0) red[w][lc] = sm;
-    __syncthreads();
-    if (tid < 16 && rg * 16 + tid < n_rows)
-      out[(size_t)(rg * 16 + tid) * max_blocks + b] =
-          make_float2(tm, (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
-    __syncthreads();
   }
 }
 
-// One wave per (sequence, KV head, row): M = max of the partial maxima, l = sum of exp2(m - M) * s.
-__global__ __launch_bounds__(256) void imp_merge_kernel(const float2* __restrict__ part, int n_rows_all,
-                                                        int max_blocks, float2* __restrict__ stats) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= n_rows_all) return;
-  const float2* p = part + (size_t)row * max_blocks;
-  float M = -INFINITY;
-  for (int b = lane; b < max_blocks; b += 64) M = fmaxf(M, p[b].x);
-  M = wave_max_f32(M);
-  float l = 0.f;
-  for (int b = lane; b < max_blocks; b += 64) {
-    const float2 x = p[b];
-    l += x.y * exp2_diff(x.x, M);
-  }
-  l = wave_sum_f32(l);
-  if (lane == 0) stats[row] = make_float2(M, l);
+// One workgroup per (sequence, KV head, row): M = max of the partial maxima, l = sum of
+// exp2(m - M) * s, folded online -- (M, l) absorbs (m, s) as M' = max(M, m),
+// l' = l exp2(M - M') + s exp2(m - M') -- with 8 loads in flight per lane, then across lanes and waves.
+__device__ inline void ml_fold(float& M, float& l, float m, float s2) {
+  const float Mn = fmaxf(M, m);
+  l = l * exp2_diff(M, Mn) + s2 * exp2_diff(m, Mn);
+  M = Mn;
 }
 
+__global__ __launch_bounds__(256) void imp_merge_kernel(const float2* __restrict__ part, int n_sub,
+                                                        float2* __restrict__ stats) {
+  __shared__ float2 red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float2* p = part + (size_t)row * n_sub;
+  float M = -INFINITY, l = 0.f;
+  for (int x0 = tid; x0 < n_sub; x0 += 256 * 8) {
+    float2 y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = p[min(x0 + 256 * u, n_sub - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (x0 + 256 * u < n_sub) ml_fold(M, l, y[u].x, y[u].y);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ml_fold(M, l, shfl_xor_f(M, m), shfl_xor_f(l, m));
+  if (lane == 0) red[w] = make_float2(M, l);
+  __syncthreads();
+  if (tid == 0) {
+    float Mt = red[0].x, lt = red[0].y;
+    for (int k = 1; k < 4; ++k) ml_fold(Mt, lt, red[k].x, red[k].y);
+    stats[row] = make_float2(Mt, lt);
+  }
+}
+
+// dst: SEPARATE the importance itself [batch][Hkv][max_blocks * 128]; SHARED per-head rows of the
+// same shape, summed by imp_sum_kernel.
 __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t* __restrict__ q_obs, int n_obs,
                                                         const uint16_t* __restrict__ k_pool,
                                                         const int32_t* __restrict__ table, int max_blocks,
                                                         const int32_t* __restrict__ seq_lens,
                                                         const float2* __restrict__ stats,
-                                                        float* __restrict__ imp) {
-  const int b = blockIdx.x, seq = blockIdx.y;
+                                                        float* __restrict__ dst) {
+  __shared__ uint4 qs[kImpRows * 16];
+  __shared__ float2 ls[kImpRows];
+  const int b = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
-  const int L = seq_lens[seq], g = P.g, n_rows = n_obs * g, n_rg = (n_rows + 15) / 16;
-  const size_t row_len = (size_t)max_blocks * kBlock;
+  const int L = seq_lens[seq], gsh = __builtin_ctz(P.g), n_rows = n_obs * P.g;
+  float* out = dst + ((size_t)seq * P.Hkv + h) * (size_t)max_blocks * kBlock + (size_t)b * kBlock;
   const int v = b * kBlock < L ? table[(size_t)seq * max_blocks + b] : -1;
+  if (v < 0) {
+    if (tid < kBlock) out[tid] = 0.f;
+    return;
+  }
+  uint4 kr[2][4];
+  load_k_tile(k_pool, (size_t)v * P.Hkv + h, kr);
   const uint16_t* q_seq = q_obs + (size_t)seq * n_obs * P.Hq * kDim;
+  const float2* st = stats + ((size_t)seq * P.Hkv + h) * n_rows;
   float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int h = 0; h < P.Hkv; ++h) {
-    if (v >= 0) {
-      uint4 kr[2][4];
-      load_k_tile(k_pool, (size_t)v * P.Hkv + h, kr);
-      const float2* st = stats + ((size_t)seq * P.Hkv + h) * n_rows;
-      for (int rg = 0; rg < n_rg; ++rg) {
-        half8_t qb[4];
-        load_q_rows(q_seq, h, g, P.Hq, n_rows, rg, qb);
-        const int r = rg * 16 + lc;
-        const float2 ml = st[r < n_rows ? r : 0];
-        const float inv_l = ml.y > 0.f ? 1.0f / ml.y : 0.f;
-        const int last = L - n_obs + (r < n_rows ? r / g : 0);
+  for (int r0 = 0; r0 < n_rows; r0 += kImpRows) {
+    if (r0 > 0) __syncthreads();
+    stage_q_rows(q_seq, h, gsh, P.Hq, n_rows, r0, qs);
+    if (tid < kImpRows) ls[tid] = r0 + tid < n_rows ? st[r0 + tid] : make_float2(-INFINITY, 0.f);
+    __syncthreads();
+    const int n_rg = (min(kImpRows, n_rows - r0) + 15) / 16;
+    for (int rg = 0; rg < n_rg; ++rg) {
+      half8_t qb[4];
+      q_rows_from_lds(qs, rg, qb);
+      const int r = r0 + rg * 16 + lc;
+      const float2 ml = ls[rg * 16 + lc];
+      const float inv_l = ml.y > 0.f ? 1.0f / ml.y : 0.f;
+      const int last = L - n_obs + (r < n_rows ? r >> gsh : 0);
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+      for (int gg = 0; gg < 2; ++gg) {
+        const f32x4_t S = imp_s(kr, qb, gg);
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[gg][m]), qb[m], S, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
-            const float p = r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
-            acc[gg][i] += row_sum16(p);  // the 16 rows of this group (one DPP row = one token)
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
+          const float p = r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
+          acc[gg][i] += row_sum16(p);  // the 16 rows of this group (one DPP row = one token)
         }
       }
     }
-    if (P.mode == kSeparate || h == P.Hkv - 1) {  // one score row per KV head, or one for all
-      if (lc == 0) {
-        float* dst = imp + ((size_t)seq * P.G + (P.mode == kSeparate ? h : 0)) * row_len + (size_t)b * kBlock;
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[32 * w + 16 * gg + 4 * lq + i] = acc[gg][i];
-      }
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[gg][i] = 0.f;
-    }
   }
+  if (lc == 0) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[32 * w + 16 * gg + 4 * lq + i] = acc[gg][i];
+  }
+}
+
+// SHARED: importance[seq][0][t] = sum over KV heads of the per-head rows.
+__global__ __launch_bounds__(256) void imp_sum_kernel(const float* __restrict__ heads, int Hkv, size_t row_len,
+                                                      float* __restrict__ imp) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int seq = blockIdx.y;
+  if (t >= row_len) return;
+  const float* src = heads + (size_t)seq * Hkv * row_len + t;
+  float s = 0.f;
+  for (int h = 0; h < Hkv; ++h) s += src[(size_t)h * row_len];
+  imp[(size_t)seq * row_len + t] = s;
 }
 
 // One wave per (logical block, KV head, sequence): the rep_num best tokens of the block by score.
@@ -230,23 +280,31 @@ __global__ __launch_bounds__(64) void dyn_reps_kernel(Params P, const uint16_t* 
 hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs, const void* k_pool,
                                    const int32_t* table, int max_blocks, const int32_t* seq_lens, int batch,
                                    float* imp, void* ws, hipStream_t s) {
-  const int n_rows = n_obs * P.g;
+  const size_t rows_all = (size_t)batch * P.Hkv * n_obs * P.g;
+  const int n_sub = max_blocks * 4;
   float2* part = static_cast<float2*>(ws);
-  float2* stats = part + (size_t)batch * P.Hkv * n_rows * max_blocks;
+  float2* stats = part + rows_all * n_sub;
+  float* heads = reinterpret_cast<float*>(stats + rows_all);  // SHARED only
   const uint16_t* q = static_cast<const uint16_t*>(q_obs);
   const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
-  hipLaunchKernelGGL(imp_stats_kernel, dim3(max_blocks, P.Hkv, batch), dim3(256), 0, s, P, q, n_obs, kp, table,
-                     max_blocks, seq_lens, part);
-  const int rows_all = batch * P.Hkv * n_rows;
-  hipLaunchKernelGGL(imp_merge_kernel, dim3((rows_all + 3) / 4), dim3(256), 0, s, part, rows_all, max_blocks, stats);
-  hipLaunchKernelGGL(imp_accum_kernel, dim3(max_blocks, batch), dim3(256), 0, s, P, q, n_obs, kp, table,
-                     max_blocks, seq_lens, stats, imp);
+  const dim3 tiles(max_blocks, P.Hkv, batch);
+  hipLaunchKernelGGL(imp_stats_kernel, tiles, dim3(256), 0, s, P, q, n_obs, kp, table, max_blocks, seq_lens, part);
+  hipLaunchKernelGGL(imp_merge_kernel, dim3((unsigned)rows_all), dim3(256), 0, s, part, n_sub, stats);
+  const bool shared = P.mode == kShared;
+  hipLaunchKernelGGL(imp_accum_kernel, tiles, dim3(256), 0, s, P, q, n_obs, kp, table, max_blocks, seq_lens, stats,
+                     shared ? heads : imp);
+  if (shared) {
+    const size_t row_len = (size_t)max_blocks * kBlock;
+    hipLaunchKernelGGL(imp_sum_kernel, dim3((unsigned)((row_len + 255) / 256), batch), dim3(256), 0, s, heads,
+                       P.Hkv, row_len, imp);
+  }
   return hipGetLastError();
 }
 
 size_t token_importance_ws_bytes(const Params& P, int batch, int max_blocks, int n_obs) {
   const size_t rows = (size_t)batch * P.Hkv * n_obs * P.g;
-  return rows * max_blocks * sizeof(float2) + rows * sizeof(float2);
+  return rows * max_blocks * 4 * sizeof(float2) + rows * sizeof(float2) +
+         (size_t)batch * P.Hkv * max_blocks * kBlock * sizeof(float);
 }
 
 hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float* imp, const int32_t* table,
