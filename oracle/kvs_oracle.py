@@ -46,6 +46,12 @@ Readings taken where the pages are silent (each is the spec here):
       heads of the selection group (SEPARATE: the g heads of a KV head; SHARED: all heads).  A
       block's reps are the K rows of its rep_num highest-scoring tokens (ties to the lower token),
       in ascending token order, and a Dynamic block is scored like Fix (sum over reps of q.rep).
+  R24 Preselect (the article's optional module after SnapKV: before decoding, blocks are chosen by
+      the attention the question's tokens pay the context; later selections are confined to them).
+      A block's preselect score is the sum of its tokens' scores (R23's token scores); the
+      preselect_block_count best candidates (ties to the lower block) form the set; a decode step
+      then ranks only the current candidates inside the set, k_eff = min(k, their number) -- so
+      with k >= the set's size the set itself is attended.
   R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
       of one token's key or value row is a block with scale d = max|x| / 127 and codes
       q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
@@ -344,3 +350,40 @@ def dynamic_reps(K, imp, B: int, rep_num: int, mode: str, blocks):
             picked[n, h] = toks
             out[n, h] = np.asarray(K[[b * B + t for t in toks], h, :], dtype=np.float64)
     return out, picked
+
+
+# ----------------------------------------------------------------------------------------------
+# O9. Preselect  [KT-LC §4.4 Preselect (after SnapKV); §4.5 preselect_block_count; reading R24]
+# ----------------------------------------------------------------------------------------------
+def preselect_blocks(imp, L: int, B: int, initial_len: int, local_len: int, n_presel: int):
+    """Per group: the n_presel candidate blocks with the largest summed token score (ties to the
+    lower block), ascending.  imp: [G][L] token scores (``token_importance``)."""
+    _, _, cand = regions(L, B, initial_len, local_len)
+    out = []
+    for row in np.asarray(imp, dtype=np.float64):
+        bs = [row[b * B:(b + 1) * B].sum() for b in cand]
+        out.append(select_topk(bs, cand, n_presel))
+    return out
+
+
+def decode_step_preselected(q, K, V, presel, *, B, initial_len, local_len, topk, method, rep_num=1,
+                            mode=SEPARATE, scale=None, reps=None):
+    """``decode_step`` with each group's selection confined to its preselected blocks that are still
+    candidates (reading R24).  presel: per group, ascending block ids."""
+    r = decode_step(q, K, V, B=B, initial_len=initial_len, local_len=local_len, topk=0,
+                    method=method, rep_num=rep_num, mode=mode, scale=scale, reps=reps)
+    cand = r["cand"]
+    L, Hkv, d = K.shape
+    g = q.shape[0] // Hkv
+    pos = {b: i for i, b in enumerate(cand)}
+    sel = []
+    for gi, ps in enumerate(presel):
+        allowed = [b for b in ps if b in pos]
+        row = [r["scores"][gi][pos[b]] for b in allowed]
+        sel.append(select_topk(row, allowed, topk))
+    toks = []
+    for j in range(q.shape[0]):
+        gi = (j // g) if mode == SEPARATE else 0
+        toks.append(attended_tokens(L, B, r["init_end"], r["local_start"], sel[gi]))
+    r.update(sel=sel, tokens=toks, out=attention(q, K, V, toks, scale))
+    return r

@@ -412,11 +412,46 @@ def check_dynamic_reps_closed_forms(orc, seed=33):
     assert 5 in p2[0, 1].tolist(), p2
 
 
+# ---------------------------------------------------------------------------------------- Preselect
+def check_preselect_identities(orc, seed=34):
+    """A set holding every candidate leaves the decode step as it is; with k >= the set's size the
+    set itself is attended; a block whose tokens all take the largest scores is preselected; the set
+    is the candidates ranked by summed token score (a block-sum reference written as a matrix
+    product)."""
+    g = np.random.default_rng(seed)
+    L, Hq, Hkv, d, B, I, W = 60 * 8 + 5, 4, 2, 16, 8, 8, 24
+    q = g.standard_normal((Hq, d)).astype(np.float16)
+    K = g.standard_normal((L, Hkv, d)).astype(np.float16)
+    V = g.standard_normal((L, Hkv, d)).astype(np.float16)
+    _, _, cand = orc.regions(L, B, I, W)
+    kw = dict(B=B, initial_len=I, local_len=W, method="quest", mode="separate")
+    full = orc.decode_step(q, K, V, topk=6, **kw)
+    allp = orc.decode_step_preselected(q, K, V, [cand] * Hkv, topk=6, **kw)
+    assert allp["sel"] == full["sel"] and np.array_equal(allp["out"], full["out"])
+    presel = [cand[3:9], cand[10:14]]
+    r = orc.decode_step_preselected(q, K, V, presel, topk=10, **kw)
+    assert r["sel"] == presel
+    r2 = orc.decode_step_preselected(q, K, V, presel, topk=2, **kw)
+    for gi in range(Hkv):
+        assert set(r2["sel"][gi]) <= set(presel[gi]) and len(r2["sel"][gi]) == 2
+    imp = np.abs(g.standard_normal((Hkv, L)))
+    imp[1, 20 * B:21 * B] += 50.0
+    ps = orc.preselect_blocks(imp, L, B, I, W, 5)
+    assert 20 in ps[1] and all(len(p) == 5 and p == sorted(p) for p in ps)
+    M = np.zeros((L, len(cand)))
+    for j, b in enumerate(cand):
+        M[b * B:(b + 1) * B, j] = 1.0
+    bs = imp @ M
+    for gi in range(Hkv):
+        order = sorted(range(len(cand)), key=lambda j: (-bs[gi, j], cand[j]))[:5]
+        assert ps[gi] == sorted(cand[j] for j in order)
+
+
 ALL_CHECKS = [
     check_quest_upper_bound, check_quest_tight_and_units, check_rep_closed_forms,
     check_hand_worked, check_regions_golden, check_regions_partition,
     check_shared_is_sum_of_separate, check_gqa_mapping_via_sdpa, check_masked_attention_via_sdpa,
     check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
-    check_dynamic_reps_closed_forms,
+    check_dynamic_reps_closed_forms, check_preselect_identities,
 ]

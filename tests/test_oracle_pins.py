@@ -169,6 +169,16 @@ def _dynamic_ties_high(K, imp, B, rep_num, mode, blocks):
     return out, picked
 
 
+def _presel_max_not_sum(imp, L, B, initial_len, local_len, n_presel):
+    _, _, cand = orc.regions(L, B, initial_len, local_len)
+    return [orc.select_topk([row[b * B:(b + 1) * B].max() for b in cand], cand, n_presel)
+            for row in np.asarray(imp, np.float64)]
+
+
+def _presel_decode_ignores_set(q, K, V, presel, **kw):
+    return orc.decode_step(q, K, V, **kw)
+
+
 _orig_quantize = orc.quantize_q8_0
 _orig_dequantize = orc.dequantize_q8_0
 _orig_head_scores = orc.head_scores
@@ -195,6 +205,8 @@ MUTANTS = [
     ("dequantize_q8_0", _q8_deq_fp32_scale),
     ("token_importance", _importance_not_causal),
     ("dynamic_reps", _dynamic_ties_high),
+    ("preselect_blocks", _presel_max_not_sum),
+    ("decode_step_preselected", _presel_decode_ignores_set),
 ]
 
 
