@@ -36,7 +36,8 @@ MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}
 EXPORTS = (
     "kvs_status_string", "kvs_last_error", "kvs_rep_count", "kvs_rep_bytes_per_block",
     "kvs_kv_bytes_per_block", "kvs_quantize_kv", "kvs_build_reps", "kvs_importance_workspace_size",
-    "kvs_token_importance", "kvs_build_dynamic_reps",
+    "kvs_token_importance", "kvs_build_dynamic_reps", "kvs_preselect_workspace_size",
+    "kvs_preselect_blocks", "kvs_decode_step_preselected_workspace_size", "kvs_decode_step_preselected",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step",
 )
@@ -107,6 +108,14 @@ _lib.kvs_token_importance.restype = ctypes.c_int
 _lib.kvs_token_importance.argtypes = [_CFG, _P, _I, _P, _P, _I, _P, _I, _P, _P, _S, _P]
 _lib.kvs_build_dynamic_reps.restype = ctypes.c_int
 _lib.kvs_build_dynamic_reps.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
+_lib.kvs_preselect_workspace_size.restype = _S
+_lib.kvs_preselect_workspace_size.argtypes = [_CFG, _I, _I]
+_lib.kvs_preselect_blocks.restype = ctypes.c_int
+_lib.kvs_preselect_blocks.argtypes = [_CFG, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+_lib.kvs_decode_step_preselected_workspace_size.restype = _S
+_lib.kvs_decode_step_preselected_workspace_size.argtypes = [_CFG, _I, _I, _I]
+_lib.kvs_decode_step_preselected.restype = ctypes.c_int
+_lib.kvs_decode_step_preselected.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
 _lib.kvs_score_blocks.restype = ctypes.c_int
 _lib.kvs_score_blocks.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
 _lib.kvs_topk_blocks.restype = ctypes.c_int
@@ -203,6 +212,33 @@ def kvs_build_dynamic_reps(cfg, k_pool, importance, block_table, max_blocks_per_
                                      max_blocks_per_seq, _ptr(seq_lens), batch, _ptr(rep_pool),
                                      _stream(stream))
     return _check(st, "kvs_build_dynamic_reps") if check else st
+
+
+def kvs_preselect_workspace_size(cfg, batch, max_blocks_per_seq) -> int:
+    return _lib.kvs_preselect_workspace_size(_cfg(cfg), batch, max_blocks_per_seq)
+
+
+def kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks_per_seq, n_presel, presel,
+                         presel_count, workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvs_preselect_blocks(_cfg(cfg), _ptr(importance), _ptr(seq_lens), batch,
+                                   max_blocks_per_seq, n_presel, _ptr(presel), _ptr(presel_count),
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(st, "kvs_preselect_blocks") if check else st
+
+
+def kvs_decode_step_preselected_workspace_size(cfg, batch, max_blocks_per_seq, n_presel) -> int:
+    return _lib.kvs_decode_step_preselected_workspace_size(_cfg(cfg), batch, max_blocks_per_seq, n_presel)
+
+
+def kvs_decode_step_preselected(cfg, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq,
+                                seq_lens, batch, presel, n_presel, out, sel_out, sel_count_out,
+                                workspace, workspace_bytes, stream=None, check=True):
+    st = _lib.kvs_decode_step_preselected(_cfg(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(rep_pool), _ptr(block_table), max_blocks_per_seq,
+                                          _ptr(seq_lens), batch, _ptr(presel), n_presel, _ptr(out),
+                                          _ptr(sel_out), _ptr(sel_count_out), _ptr(workspace),
+                                          workspace_bytes, _stream(stream))
+    return _check(st, "kvs_decode_step_preselected") if check else st
 
 
 def kvs_score_blocks(cfg, q, rep_pool, block_table, max_blocks_per_seq, seq_lens, batch, scores,

@@ -361,4 +361,119 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
                     "kvs_decode_step");
 }
 
+size_t kvs_preselect_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK) return 0;
+  return round_up((size_t)batch * P.G * max_blocks_per_seq * sizeof(float));
+}
+
+int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel, int32_t* presel,
+                         int32_t* presel_count, void* workspace, size_t workspace_bytes,
+                         kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (n_presel < 1) return KVS_ERR_INVALID_ARG;
+  if (batch > 65535) return KVS_ERR_UNSUPPORTED;
+  if (!importance || !seq_lens || !presel || !presel_count) return KVS_ERR_INVALID_ARG;
+  const size_t need = round_up((size_t)batch * P.G * max_blocks_per_seq * sizeof(float));
+  if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  float* bs = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  hipError_t e = kvs::launch_block_scores(P, importance, seq_lens, batch, max_blocks_per_seq, bs, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_preselect_blocks/scores");
+  Params Q = P;
+  Q.topk = n_presel;
+  return hip_status(kvs::launch_topk(Q, bs, seq_lens, batch, max_blocks_per_seq, presel, presel_count,
+                                     nullptr, nullptr, s),
+                    "kvs_preselect_blocks/top-k");
+}
+
+namespace {
+// Workspace of the confined decode step: scores, the compacted rows (scores, block ids, lengths),
+// their top-k picks, the selection and counts when the caller does not take them, then the partials.
+struct PreselLayout {
+  AttnLayout attn;
+  size_t scores_off, cs_off, cid_off, clen_off, csel_off, sel_off, cnt_off, attn_off, total;
+};
+
+PreselLayout presel_layout(const Params& P, int batch, int max_blocks, int n_presel) {
+  PreselLayout L;
+  const size_t rows = (size_t)batch * P.G, k = P.topk > 0 ? P.topk : 1;
+  size_t off = 0;
+  L.scores_off = off; off += round_up(rows * max_blocks * sizeof(float));
+  L.cs_off = off;     off += round_up(rows * n_presel * sizeof(float));
+  L.cid_off = off;    off += round_up(rows * n_presel * sizeof(int32_t));
+  L.clen_off = off;   off += round_up(rows * sizeof(int32_t));
+  L.csel_off = off;   off += round_up(rows * k * sizeof(int32_t));
+  L.sel_off = off;    off += round_up(rows * k * sizeof(int32_t));
+  L.cnt_off = off;    off += round_up(rows * sizeof(int32_t));
+  L.attn = attn_layout(P, batch, max_blocks);
+  L.attn_off = off;   off += L.attn.total;
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t kvs_decode_step_preselected_workspace_size(const kvs_config* cfg, int32_t batch,
+                                                  int32_t max_blocks_per_seq, int32_t n_presel) {
+  Params P;
+  if (make_params(cfg, &P) != KVS_OK || check_sizes(batch, max_blocks_per_seq) != KVS_OK || n_presel < 1)
+    return 0;
+  return presel_layout(P, batch, max_blocks_per_seq, n_presel).total;
+}
+
+int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void* k_pool,
+                                const void* v_pool, const void* rep_pool, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                const int32_t* presel, int32_t n_presel, float* out, int32_t* sel_out,
+                                int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
+                                kvs_stream_t stream) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (n_presel < 1) return KVS_ERR_INVALID_ARG;
+  if ((size_t)batch * P.G > 65535) return KVS_ERR_UNSUPPORTED;
+  if (!q || !k_pool || !v_pool || !rep_pool || !block_table || !seq_lens || !presel || !out)
+    return KVS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
+    return KVS_ERR_MISALIGNED;
+  const PreselLayout S = presel_layout(P, batch, max_blocks_per_seq, n_presel);
+  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  const int rows = batch * P.G, k = P.topk;
+  float* scores = at<float>(workspace, S.scores_off);
+  float* cs = at<float>(workspace, S.cs_off);
+  int32_t* cid = at<int32_t>(workspace, S.cid_off);
+  int32_t* clen = at<int32_t>(workspace, S.clen_off);
+  int32_t* csel = at<int32_t>(workspace, S.csel_off);
+  int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
+  int32_t* cnt = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  hipError_t e = kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens, batch, scores, s);
+  if (e == hipSuccess)
+    e = kvs::launch_compact(P, scores, max_blocks_per_seq, seq_lens, presel, n_presel, batch, cs, cid, clen, s);
+  // each (sequence, group) row is a sequence of its own: n_eff blocks, all candidates
+  Params C = P;
+  C.G = 1;
+  C.mode = kvs::kShared;
+  C.initial_len = 0;
+  C.local_len = 0;
+  if (e == hipSuccess) e = kvs::launch_topk(C, cs, clen, rows, n_presel, csel, cnt, nullptr, nullptr, s);
+  if (e == hipSuccess) e = kvs::launch_map_back(csel, k, cid, n_presel, rows, sel, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/selection");
+  void* aws = static_cast<char*>(workspace) + S.attn_off;
+  kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                              seq_lens, sel, cnt, out);
+  e = kvs::launch_attn_tiles(a, batch, true, false, s);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/tiles");
+  return hip_status(kvs::launch_merge(a, batch, s), "kvs_decode_step_preselected/merge");
+}
+
 }  // extern "C"

@@ -28,6 +28,13 @@ size_t token_importance_ws_bytes(const Params& P, int batch, int max_blocks, int
 hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float* imp, const int32_t* table,
                                int max_blocks, const int32_t* seq_lens, int batch, void* rep_pool,
                                hipStream_t s);
+hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,
+                               int max_blocks, float* bs, hipStream_t s);
+hipError_t launch_compact(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
+                          const int32_t* presel, int n_presel, int batch, float* cs, int32_t* cid,
+                          int32_t* clen, hipStream_t s);
+hipError_t launch_map_back(const int32_t* csel, int topk, const int32_t* cid, int n_presel, int rows,
+                           int32_t* sel, hipStream_t s);
 hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
                              int rep_num, void* rep_pool, hipStream_t s);
 hipError_t launch_score(const Params& P, const void* q, const void* rep_pool, const int32_t* table,

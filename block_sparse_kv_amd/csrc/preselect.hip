@@ -1,0 +1,107 @@
+// Preselect (KTransformers long-context article §4.4, after SnapKV; §4.5 preselect_block_count):
+// before decoding, a set of blocks is chosen from the attention the question's tokens pay the
+// context, and every later selection is confined to it.
+//  * block_score_kernel: a block's preselect score is the sum of its tokens' scores
+//    (kvs_token_importance), -inf outside the candidates -- the layout of the block scores, so the
+//    set is the ordinary top-k of these rows.
+//  * The confined decode step scores every candidate as usual; compact_kernel then keeps, per
+//    (sequence, group), the scores of the set's blocks that are still candidates, in block order,
+//    as one row of a compacted batch (each row its own "sequence" of n_eff blocks with no Initial or
+//    Local part), the ordinary top-k selects in it, and map_back_kernel turns the picks into block
+//    ids for the attention tiles and the merge.
+#include "kvs_launch.h"
+
+namespace kvs {
+
+// One wave per (candidate block, group, sequence): sum of the block's 128 token scores.
+__global__ __launch_bounds__(256) void block_score_kernel(Params P, const float* __restrict__ imp,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int max_blocks, float* __restrict__ bs) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), gr = blockIdx.y, seq = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  if (b >= max_blocks) return;
+  const Regions rg = regions_of(seq_lens[seq], P.initial_len, P.local_len);
+  const size_t row = (size_t)seq * P.G + gr;
+  float s = 0.f;
+  if (b >= rg.cand_lo && b < rg.cand_hi) {
+    const float2 x = reinterpret_cast<const float2*>(imp + row * (size_t)max_blocks * kBlock + (size_t)b * kBlock)[lane];
+    s = wave_sum_f32(x.x + x.y);
+  } else {
+    s = -INFINITY;
+  }
+  if (lane == 0) bs[row * max_blocks + b] = s;
+}
+
+// One wave per (group, sequence) row: the set's blocks that are current candidates, in order (a
+// ballot prefix places each kept entry).  cs / cid: [batch * G][n_presel] compacted scores and their
+// block ids, -inf / -1 padded; clen: the row's length in tokens (n_eff * 128) for the top-k over the
+// compacted rows.
+__global__ __launch_bounds__(256) void compact_kernel(Params P, const float* __restrict__ scores, int max_blocks,
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      const int32_t* __restrict__ presel, int n_presel,
+                                                      int rows, float* __restrict__ cs, int32_t* __restrict__ cid,
+                                                      int32_t* __restrict__ clen) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int seq = row / P.G;
+  const Regions rg = regions_of(seq_lens[seq], P.initial_len, P.local_len);
+  const int32_t* ps = presel + (size_t)row * n_presel;
+  float* o = cs + (size_t)row * n_presel;
+  int32_t* oi = cid + (size_t)row * n_presel;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int n = 0;
+  for (int i0 = 0; i0 < n_presel; i0 += 64) {
+    const int i = i0 + lane;
+    const int b = i < n_presel ? ps[i] : -1;
+    const bool ok = b >= rg.cand_lo && b < rg.cand_hi && b < max_blocks;
+    const unsigned long long m = __ballot(ok);
+    if (ok) {
+      const int at = n + __popcll(m & lt);
+      o[at] = scores[(size_t)row * max_blocks + b];
+      oi[at] = b;
+    }
+    n += __popcll(m);
+  }
+  for (int i = n + lane; i < n_presel; i += 64) {
+    o[i] = -INFINITY;
+    oi[i] = -1;
+  }
+  if (lane == 0) clen[row] = n * kBlock;
+}
+
+// One thread per (row, pick): compacted index -> block id; -1 stays -1.
+__global__ __launch_bounds__(256) void map_back_kernel(const int32_t* __restrict__ csel, int topk,
+                                                       const int32_t* __restrict__ cid, int n_presel, int total,
+                                                       int32_t* __restrict__ sel) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= total) return;
+  const int row = x / topk, j = csel[x];
+  sel[x] = j >= 0 && j < n_presel ? cid[(size_t)row * n_presel + j] : -1;
+}
+
+hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,
+                               int max_blocks, float* bs, hipStream_t s) {
+  hipLaunchKernelGGL(block_score_kernel, dim3((max_blocks + 3) / 4, P.G, batch), dim3(256), 0, s, P, imp,
+                     seq_lens, max_blocks, bs);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
+                          const int32_t* presel, int n_presel, int batch, float* cs, int32_t* cid,
+                          int32_t* clen, hipStream_t s) {
+  const int rows = batch * P.G;
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, P, scores, max_blocks, seq_lens,
+                     presel, n_presel, rows, cs, cid, clen);
+  return hipGetLastError();
+}
+
+hipError_t launch_map_back(const int32_t* csel, int topk, const int32_t* cid, int n_presel, int rows,
+                           int32_t* sel, hipStream_t s) {
+  const int total = rows * topk;
+  if (total > 0)
+    hipLaunchKernelGGL(map_back_kernel, dim3((total + 255) / 256), dim3(256), 0, s, csel, topk, cid, n_presel,
+                       total, sel);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

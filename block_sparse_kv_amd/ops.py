@@ -61,6 +61,28 @@ def build_dynamic_reps(cfg, k_pool, importance, block_table, seq_lens, rep_pool)
     return rep_pool
 
 
+def preselect_blocks(cfg, importance, seq_lens, n_presel, max_blocks):
+    batch = seq_lens.shape[0]
+    presel = torch.empty((batch, cfg.groups, n_presel), dtype=torch.int32, device=importance.device)
+    cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=importance.device)
+    ws = workspace(B.kvs_preselect_workspace_size(cfg, batch, max_blocks), importance.device)
+    B.kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks, n_presel, presel, cnt, ws,
+                           ws.numel())
+    return presel, cnt
+
+
+def decode_step_preselected(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_lens, presel):
+    batch, mb = block_table.shape
+    n_presel = presel.shape[-1]
+    out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
+    sel = torch.empty((batch, cfg.groups, max(cfg.topk, 1)), dtype=torch.int32, device=q.device)
+    cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=q.device)
+    ws = workspace(B.kvs_decode_step_preselected_workspace_size(cfg, batch, mb, n_presel), q.device)
+    B.kvs_decode_step_preselected(cfg, q, k_pool, v_pool, rep_pool, block_table, mb, seq_lens, batch,
+                                  presel.contiguous(), n_presel, out, sel, cnt, ws, ws.numel())
+    return out, sel[:, :, : cfg.topk], cnt
+
+
 def score_blocks(cfg, q, rep_pool, block_table, seq_lens):
     batch, mb = block_table.shape
     scores = torch.empty((batch, cfg.groups, mb), dtype=torch.float32, device=q.device)

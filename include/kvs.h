@@ -179,6 +179,42 @@ int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const floa
                            const int32_t* seq_lens, int32_t batch, void* rep_pool,
                            kvs_stream_t stream);
 
+/* Workspace bytes kvs_preselect_blocks needs (host query; 0 on bad config or sizes). */
+size_t kvs_preselect_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq);
+
+/*
+ * kvs_preselect_blocks -- the preselected set [KT-LC §4.4 Preselect, after SnapKV; §4.5
+ * preselect_block_count]: before decoding, the blocks the question's tokens attend most.  Per
+ * (sequence, group): a candidate block's preselect score is the sum of its 128 token scores in
+ * importance (kvs_token_importance; same groups); the min(n_presel, candidates) best blocks, ties to
+ * the lower block, are written ascending to presel [batch][G][n_presel], -1 padded, with their number
+ * in presel_count [batch][G].  workspace: >= kvs_preselect_workspace_size bytes, 256-byte aligned.
+ */
+int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel, int32_t* presel,
+                         int32_t* presel_count, void* workspace, size_t workspace_bytes,
+                         kvs_stream_t stream);
+
+/* Workspace bytes kvs_decode_step_preselected needs (host query; 0 on bad config or sizes). */
+size_t kvs_decode_step_preselected_workspace_size(const kvs_config* cfg, int32_t batch,
+                                                  int32_t max_blocks_per_seq, int32_t n_presel);
+
+/*
+ * kvs_decode_step_preselected -- kvs_decode_step with every selection confined to a preselected set
+ * [KT-LC §4.4]: per (sequence, group), only the blocks of presel [batch][G][n_presel] (ascending, -1
+ * padded, e.g. from kvs_preselect_blocks) that are still candidates at the current length compete;
+ * k_eff = min(topk, their number), so with topk >= the set's size the set is attended as it is.
+ * Scores, ties, order and attention as kvs_decode_step.  Enqueued as scoring, compaction, top-k,
+ * mapping, attention tiles and merge; the workspace (>= the size query, 256-byte aligned) is scratch.
+ * sel_out / sel_count_out (nullable) receive the selection.
+ */
+int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void* k_pool,
+                                const void* v_pool, const void* rep_pool, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                const int32_t* presel, int32_t n_presel, float* out, int32_t* sel_out,
+                                int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
+                                kvs_stream_t stream);
+
 /*
  * kvs_score_blocks -- block relevance [KT-LC §3.1 Quest bound; §4.3 rep similarity; §4.5 modes].
  * For every candidate block b of every sequence and query head j (KV head h = j/g):

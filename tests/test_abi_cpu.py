@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 16, decl
+    assert len(decl) == 20, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -141,6 +141,30 @@ def test_dynamic_rep_errors():
     assert run(dyn, 16, Z, need) == B.KVS_ERR_WORKSPACE
     assert run(dyn, 16, A + 16, need) == B.KVS_ERR_MISALIGNED
     assert run(cfg(kv_type="q8_0"), 16, A, need) == B.KVS_ERR_UNSUPPORTED
+
+
+def test_preselect_errors():
+    c = cfg()
+    A, M, Z = ALIGNED, MISALIGNED, None
+    E = B.KVS_ERR_INVALID_ARG
+    need = kvs.kvs_preselect_workspace_size(c, 2, 100)
+    assert need >= 2 * 8 * 100 * 4 and need % 256 == 0
+    pre = lambda n, ws, wb, imp=A: kvs.kvs_preselect_blocks(c, imp, A, 2, 100, n, A, A, ws, wb, stream=0,
+                                                         check=False)
+    assert pre(0, A, need) == E
+    assert pre(8, A, need, imp=Z) == E
+    assert pre(8, A, need - 256) == B.KVS_ERR_WORKSPACE
+    assert pre(8, A + 16, need) == B.KVS_ERR_MISALIGNED
+    need2 = kvs.kvs_decode_step_preselected_workspace_size(c, 2, 100, 32)
+    assert need2 > kvs.kvs_attn_workspace_size(c, 2, 100)
+    assert kvs.kvs_decode_step_preselected_workspace_size(c, 2, 100, 0) == 0
+    step = lambda n, ws, wb, q=A, p=A: kvs.kvs_decode_step_preselected(
+        c, q, A, A, A, A, 100, A, 2, p, n, A, None, None, ws, wb, stream=0, check=False)
+    assert step(0, A, need2) == E
+    assert step(32, A, need2, p=Z) == E
+    assert step(32, A, need2, q=M) == B.KVS_ERR_MISALIGNED
+    assert step(32, A, need2 - 256) == B.KVS_ERR_WORKSPACE
+    assert step(32, Z, need2) == B.KVS_ERR_WORKSPACE
 
 
 def test_null_and_size_errors():
