@@ -62,6 +62,10 @@ WORKLOADS = {
     "128k-dynamic": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="dynamic", rep_num=1,
                          n_obs=32, mode="shared", layers=1, replicas=16, n_hot=50, hot_per_head=False,
                          seed=20260022),
+    # selection confined to a preselected set of 192 blocks (token scores of 32 observation queries)
+    "128k-presel": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                        n_obs=32, presel=192, layers=1, replicas=16, n_hot=50, hot_per_head=False,
+                        seed=20260032),
     # the same two headline shapes over a Q8_0 cache (kv_type): int8 codes + fp16 scale per 32 channels
     "128k-max-q8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
                         layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="q8_0"),
@@ -154,6 +158,7 @@ class Setup:
         self.table = torch.arange(nb, dtype=torch.int32, device=device)[None]
         self.lens = torch.tensor([L], dtype=torch.int32, device=device)
         self.units = []  # one per (replica, layer): q, k_pool, v_pool, rep_pool
+        self.presel = []  # per unit, with "presel" workloads: the preselected set
         n_units = w["replicas"] * w["layers"]
         t0 = time.time()
         for u in range(n_units):
@@ -172,6 +177,11 @@ class Setup:
                 ops.build_dynamic_reps(self.cfg, kp, imp, self.table, self.lens, rp)
             else:
                 ops.build_reps(self.cfg, kp, torch.arange(L // B, dtype=torch.int32), rp)
+            if "presel" in w:  # the unit's preselected set, from its own observation queries
+                q_obs = kvsynth.randn_fp16((1, w["n_obs"], w["Hq"], D), kvsynth.mix_seed(w["seed"], u, 9), device)
+                imp = ops.token_importance(self.cfg, q_obs, kp, self.table, self.lens)
+                ps, _ = ops.preselect_blocks(self.cfg, imp, self.lens, w["presel"], nb)
+                self.presel.append(ps)
             self.units.append((q[None].contiguous(), kp, vp, rp))
         torch.cuda.synchronize()
         log(f"[setup] {name}: {n_units} cache units of {L} tokens generated in {time.time() - t0:.1f}s")
@@ -182,14 +192,23 @@ class Setup:
         self.cnt = torch.empty((1, self.cfg.groups), dtype=torch.int32, device=device)
         self.nb = nb
         self.kvs = kvs
+        if "presel" in w:
+            self.pws_bytes = kvs.kvs_decode_step_preselected_workspace_size(self.cfg, 1, nb, w["presel"])
+            self.pws = torch.empty(self.pws_bytes, dtype=torch.uint8, device=device)
 
     def step(self, replica):
         """One decode step (all layers) on cache replica `replica`."""
         w = self.w
         for layer in range(w["layers"]):
-            q, kp, vp, rp = self.units[replica * w["layers"] + layer]
-            self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
-                                     self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
+            u = replica * w["layers"] + layer
+            q, kp, vp, rp = self.units[u]
+            if self.presel:
+                self.kvs.kvs_decode_step_preselected(self.cfg, q, kp, vp, rp, self.table, self.nb,
+                                                     self.lens, 1, self.presel[u], w["presel"], self.out,
+                                                     self.sel, self.cnt, self.pws, self.pws_bytes)
+            else:
+                self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
+                                         self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
 
     def prepare_reuse(self):
         """Selection reuse (a later token or layer attends with an earlier selection): keep each
