@@ -52,6 +52,10 @@ Readings taken where the pages are silent (each is the spec here):
       preselect_block_count best candidates (ties to the lower block) form the set; a decode step
       then ranks only the current candidates inside the set, k_eff = min(k, their number) -- so
       with k >= the set's size the set itself is attended.
+  R25 kv_type Q4_0 (llama.cpp's other block format the list names, restated): per 32 channels of a
+      token's row, m = the value of largest magnitude (the first one on ties), d = m / -8,
+      codes q = min(15, trunc(x * (1/d) + 8.5)) in 0..15, all fp32; d stored as fp16; the cached
+      value is fp16(d) * (q - 8).  An all-zero block has d = 0 and codes 8.
   R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
       of one token's key or value row is a block with scale d = max|x| / 127 and codes
       q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
@@ -283,6 +287,31 @@ def dequantize_q8_0(codes, scales):
     *lead, d = codes.shape
     sc = np.asarray(scales, dtype=np.float16).astype(np.float64)
     cg = codes.astype(np.float64).reshape(*lead, d // Q8_GROUP, Q8_GROUP)
+    return (cg * sc[..., None]).reshape(*lead, d)
+
+
+def quantize_q4_0(x):
+    """Codes (uint8 0..15) and fp16 scales of x [..., d] in the Q4_0 format (reading R25)."""
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    assert d % Q8_GROUP == 0
+    xg = x.reshape(*lead, d // Q8_GROUP, Q8_GROUP)
+    first = np.abs(xg).argmax(axis=-1)                              # first index of the largest |x|
+    m = np.take_along_axis(xg, first[..., None], -1)[..., 0]
+    dsc = (m / np.float32(-8.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(dsc != 0, np.float32(1.0) / np.where(dsc != 0, dsc, 1), np.float32(0.0)).astype(np.float32)
+    v = ((xg * inv[..., None]).astype(np.float32) + np.float32(8.5)).astype(np.float32)
+    codes = np.minimum(15, np.trunc(v.astype(np.float64))).astype(np.uint8)
+    return codes.reshape(*lead, d), dsc.astype(np.float16)
+
+
+def dequantize_q4_0(codes, scales):
+    """The cached values fp16(d) * (q - 8) as float64 [..., d]."""
+    codes = np.asarray(codes, dtype=np.int64)
+    *lead, d = codes.shape
+    sc = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    cg = (codes - 8).astype(np.float64).reshape(*lead, d // Q8_GROUP, Q8_GROUP)
     return (cg * sc[..., None]).reshape(*lead, d)
 
 

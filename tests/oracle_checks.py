@@ -6,7 +6,7 @@ copy) and raises AssertionError on failure.  What each one rests on:
   * torch's scaled_dot_product_attention in float64 (a library routine sharing no code with the oracle);
   * closed forms and identities of the definitions (Mean linearity, Fix = rows of K, SHARED = sum
     of SEPARATE, softmax shift invariance, q = 0 gives the mean of V);
-  * hand-worked cases in tests/golden/hand_worked.json and tests/golden/q8_0_worked.json;
+  * hand-worked cases in tests/golden/hand_worked.json, q8_0_worked.json and q4_0_worked.json;
   * the rounding bound, code range and block width of the Q8_0 format;
   * planted-block recall of the selection.
 """
@@ -344,6 +344,53 @@ def check_q8_integer_rows_exact(orc):
     assert np.array_equal(orc.dequantize_q8_0(codes, sc), x.astype(np.float64))
 
 
+GOLDEN_Q4 = os.path.join(os.path.dirname(__file__), "golden", "q4_0_worked.json")
+
+
+def check_q4_golden(orc):
+    """The hand-worked Q4_0 blocks of tests/golden/q4_0_worked.json: scale (with its sign), codes,
+    cached values."""
+    with open(GOLDEN_Q4) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.zeros(32, dtype=np.float32)
+        for k, v in c["x_nonzero"].items():
+            x[int(k)] = v
+        codes, sc = orc.quantize_q4_0(x[None, :])
+        d = float(sc[0, 0])
+        assert d == c["d"] and math.copysign(1.0, d) == math.copysign(1.0, c["d"]), (c["why"], d)
+        for k, v in c["codes"].items():
+            assert int(codes[0, int(k)]) == v, (c["why"], k, int(codes[0, int(k)]))
+        deq = orc.dequantize_q4_0(codes, sc)[0]
+        wd = np.zeros(32)
+        for k, v in c["deq_nonzero"].items():
+            wd[int(k)] = v
+        assert np.array_equal(deq, wd), (c["why"], deq)
+
+
+def check_q4_range_and_bound(orc, seed=23):
+    """On random rows: codes in 0..15; each block's first largest-magnitude value takes code 0 and is
+    reproduced up to the fp16 rounding of d; every value lies within |d| of x (within |d|/2 unless
+    clipped at code 15); blocks are 32 channels wide."""
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((64, 128)) * g.uniform(0.01, 30, (64, 1))).astype(np.float16).astype(np.float32)
+    x[5, :32] *= 1000.0
+    codes, sc = orc.quantize_q4_0(x)
+    c = codes.astype(np.int64).reshape(64, 4, 32)
+    xg = x.astype(np.float64).reshape(64, 4, 32)
+    assert c.min() >= 0 and c.max() <= 15
+    first = np.abs(xg).argmax(axis=-1)
+    assert np.all(np.take_along_axis(c, first[..., None], -1) == 0)
+    m = np.take_along_axis(xg, first[..., None], -1)[..., 0]
+    d32 = (m.astype(np.float32) / np.float32(-8)).astype(np.float64)
+    err = np.abs(xg - d32[..., None] * (c - 8))
+    tol = np.abs(d32)[..., None]
+    assert np.all(err <= tol * (1 + 1e-6)), err.max()
+    half = np.broadcast_to(tol / 2 * (1 + 1e-5), err.shape)
+    assert np.all(err[c < 15] <= half[c < 15])
+    assert np.all(np.abs(sc[5, 1:].astype(np.float64)) < np.abs(sc[5, 0].astype(np.float64)) / 100)
+
+
 # ---------------------------------------------------------------------------------- Dynamic reps
 def check_importance_via_sdpa(orc, seed=31):
     """Token importance = column sums of the attention probabilities, taken from torch's float64
@@ -453,5 +500,6 @@ ALL_CHECKS = [
     check_shared_is_sum_of_separate, check_gqa_mapping_via_sdpa, check_masked_attention_via_sdpa,
     check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
-    check_dynamic_reps_closed_forms, check_preselect_identities,
+    check_dynamic_reps_closed_forms, check_preselect_identities, check_q4_golden,
+    check_q4_range_and_bound,
 ]

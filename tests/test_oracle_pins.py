@@ -179,6 +179,33 @@ def _presel_decode_ignores_set(q, K, V, presel, **kw):
     return orc.decode_step(q, K, V, **kw)
 
 
+def _q4_generic(x, last=False, rne=False, clip=True):
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    xg = x.reshape(*lead, d // 32, 32)
+    a = np.abs(xg)
+    idx = (31 - a[..., ::-1].argmax(axis=-1)) if last else a.argmax(axis=-1)
+    m = np.take_along_axis(xg, idx[..., None], -1)[..., 0]
+    dsc = (m / np.float32(-8)).astype(np.float32)
+    inv = np.where(dsc != 0, np.float32(1) / np.where(dsc != 0, dsc, 1), 0).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float32)
+    q = (np.round(v.astype(np.float64)) + 8) if rne else np.trunc((v + np.float32(8.5)).astype(np.float64))
+    q = np.minimum(15, q) if clip else q
+    return q.astype(np.uint8).reshape(*lead, d), dsc.astype(np.float16)
+
+
+def _q4_last_max(x):
+    return _q4_generic(x, last=True)
+
+
+def _q4_round_even(x):
+    return _q4_generic(x, rne=True)
+
+
+def _q4_no_clip(x):
+    return _q4_generic(x, clip=False)
+
+
 _orig_quantize = orc.quantize_q8_0
 _orig_dequantize = orc.dequantize_q8_0
 _orig_head_scores = orc.head_scores
@@ -206,6 +233,9 @@ MUTANTS = [
     ("token_importance", _importance_not_causal),
     ("dynamic_reps", _dynamic_ties_high),
     ("preselect_blocks", _presel_max_not_sum),
+    ("quantize_q4_0", _q4_last_max),
+    ("quantize_q4_0", _q4_round_even),
+    ("quantize_q4_0", _q4_no_clip),
     ("decode_step_preselected", _presel_decode_ignores_set),
 ]
 
