@@ -12,10 +12,10 @@
 
 namespace kvs {
 
-template <int G, bool IL, bool PHYS, bool Q8>
+template <int G, bool IL, bool PHYS, int KV>
 __global__ __launch_bounds__(256) void attn_tiles_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kAttnLdsBytes];
-  attn_item<G, IL, PHYS, Q8>(A, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  attn_item<G, IL, PHYS, KV>(A, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs A) {
@@ -48,22 +48,23 @@ AttnPlan attn_plan(const Params& P, int batch, int max_blocks) {
   return a;
 }
 
-template <int G, bool Q8>
+template <int G, int KV>
 static void launch_tiles_gq(const AttnArgs& A, dim3 grid, bool il, bool phys, hipStream_t s) {
   if (il && phys)
-    hipLaunchKernelGGL((attn_tiles_kernel<G, true, true, Q8>), grid, dim3(256), 0, s, A);
+    hipLaunchKernelGGL((attn_tiles_kernel<G, true, true, KV>), grid, dim3(256), 0, s, A);
   else if (il)
-    hipLaunchKernelGGL((attn_tiles_kernel<G, true, false, Q8>), grid, dim3(256), 0, s, A);
+    hipLaunchKernelGGL((attn_tiles_kernel<G, true, false, KV>), grid, dim3(256), 0, s, A);
   else if (phys)
-    hipLaunchKernelGGL((attn_tiles_kernel<G, false, true, Q8>), grid, dim3(256), 0, s, A);
+    hipLaunchKernelGGL((attn_tiles_kernel<G, false, true, KV>), grid, dim3(256), 0, s, A);
   else
-    hipLaunchKernelGGL((attn_tiles_kernel<G, false, false, Q8>), grid, dim3(256), 0, s, A);
+    hipLaunchKernelGGL((attn_tiles_kernel<G, false, false, KV>), grid, dim3(256), 0, s, A);
 }
 
 template <int G>
 static void launch_tiles_g(const AttnArgs& A, dim3 grid, bool il, bool phys, hipStream_t s) {
-  if (A.P.kv == kKvQ8) launch_tiles_gq<G, true>(A, grid, il, phys, s);
-  else launch_tiles_gq<G, false>(A, grid, il, phys, s);
+  if (A.P.kv == kKvQ8) launch_tiles_gq<G, kKvQ8>(A, grid, il, phys, s);
+  else if (A.P.kv == kKvQ4) launch_tiles_gq<G, kKvQ4>(A, grid, il, phys, s);
+  else launch_tiles_gq<G, kKvFp16>(A, grid, il, phys, s);
 }
 
 hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s) {

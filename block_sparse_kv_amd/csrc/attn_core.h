@@ -66,7 +66,25 @@ __device__ inline uint4 q8_dq8(uint32_t w0, uint32_t w1, uint32_t sc) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-template <int G, bool Q8 = false>
+// 8 Q4_0 codes of one word (channel 2i in bits 4i.., channel 2i+1 in bits 16+4i..) times the fp16 scale
+// in the low half of sc, as 8 fp16 in channel order: (w >> 4i) & 0x000F000F under the exponent pattern
+// 0x6400 is the fp16 pair 1024 + code; subtracting 1032 gives code - 8 exactly, one packed multiply
+// applies d (rounded once).
+__device__ inline uint4 q4_dq8(uint32_t w, uint32_t sc) {
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(sc & 0xFFFFu));
+  const half2v_t d2 = {d, d};
+  const half2v_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    o[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v_t, x) - bias) * d2);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// KV: the pools' KvType (fp16 tiles, Q8_0 or Q4_0 records).
+template <int G, int KV = kKvFp16>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
                                           const uint16_t* __restrict__ v_pool, int h, int phys, int ntok,
@@ -80,9 +98,9 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   // zeroed after the load (a NaN tail times p = 0 would not be 0).
   half8_t qb[4];  // Q^T B operand: lane l holds head lc, 8 channels per MFMA m (below)
   uint4 kr[2][4], vr[8];
-  uint4 vc[4];    // Q8_0: V codes and scales, dequantized when V is staged
+  uint4 vc[4];    // Q8_0 / Q4_0: V codes and scales, dequantized when V is staged
   uint32_t vs[4];
-  if constexpr (!Q8) {
+  if constexpr (KV == kKvFp16) {
     // fp16 tile: K rows of MFMA m are channels 32m + 8*lq .. +8
     const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
     const uint16_t* Kt = k_pool + off;
@@ -100,6 +118,39 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
+  } else if constexpr (KV == kKvQ4) {
+    // Q4_0 record: as for Q8_0 below, a lane's K codes are the 32 channels 32*lq .. +32 of its
+    // token (one block, one scale), here one 16-byte load, and MFMA m takes word m of them; V: lane l
+    // takes one block (channels 32*(l%4) .. +32) of the wave's tokens l/4 and 16 + l/4.
+    const size_t rec = ((size_t)phys * P.Hkv + h) * kQ4Record;
+    const unsigned char* Kq = reinterpret_cast<const unsigned char*>(k_pool) + rec;
+    const unsigned char* Vq = reinterpret_cast<const unsigned char*>(v_pool) + rec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
+      qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
+    }
+    uint4 kc[2];
+    uint32_t ks[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+      kc[g] = ld_stream16(Kq + tok * (kDim / 2) + 16 * lq);
+      ks[g] = *reinterpret_cast<const uint16_t*>(Kq + kQ4Codes + tok * 8 + 2 * lq);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tok = 32 * w + 16 * i + (lane >> 2);
+      vc[i] = ld_stream16(Vq + tok * (kDim / 2) + 16 * (lane & 3));
+      vs[i] = *reinterpret_cast<const uint16_t*>(Vq + kQ4Codes + tok * 8 + 2 * (lane & 3));
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kr[g][0] = q4_dq8(kc[g].x, ks[g]);
+      kr[g][1] = q4_dq8(kc[g].y, ks[g]);
+      kr[g][2] = q4_dq8(kc[g].z, ks[g]);
+      kr[g][3] = q4_dq8(kc[g].w, ks[g]);
+    }
   } else {
     // Q8_0 record (kv_type; llama.cpp's block format): a lane's K codes are the 32 channels
     // 32*lq .. +32 of its token -- one Q8_0 block, one scale -- and MFMA m takes channels
@@ -174,7 +225,18 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   ps += shfl_xor_f(ps, 32);
   // V to LDS: chunk i holds the wave's tokens 4i..4i+3, one kVRow row each
   unsigned char* vbuf = smem + w * kWaveVBytes;
-  if constexpr (Q8) {
+  if constexpr (KV == kKvQ4) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * i + (lane >> 2);  // the wave's token: chunk t / 4, row t % 4
+      const bool in = 32 * w + t < ntok;
+      unsigned char* row = vbuf + (t >> 2) * kVChunk + (t & 3) * kVRow + 64 * (lane & 3);
+      const uint32_t cw[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<uint4*>(row + 16 * u) = in ? q4_dq8(cw[u], vs[i]) : make_uint4(0, 0, 0, 0);
+    }
+  } else if constexpr (KV == kKvQ8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 8 * i + (lane >> 3);  // the wave's token: chunk t / 4, row t % 4
@@ -435,7 +497,7 @@ __device__ inline void empty_partial(float* part_o, float* part_ml, int n_parts,
 // n_il_max : 0), a logical block id in A.sel, or a physical one when PHYS.  Items past the
 // sequence's own counts do nothing; table entries or selections outside the table give an empty
 // partial instead of a read outside the pools' rows.
-template <int G, bool IL, bool PHYS, bool Q8 = false>
+template <int G, bool IL, bool PHYS, int KV = kKvFp16>
 __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int seq, unsigned char* smem) {
   const Params& P = A.P;
   const bool is_il = IL && x < A.n_il_max;
@@ -472,7 +534,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
     empty_partial<G>(po, pml, A.max_parts, part);
     return;
   }
-  attn_tile<G, Q8>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
+  attn_tile<G, KV>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
 }
 
 // Merge of channels [16c, 16c + 16) of query head j of sequence seq by one wave (merge_head_wave).

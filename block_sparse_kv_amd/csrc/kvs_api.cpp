@@ -45,7 +45,8 @@ int make_params(const kvs_config* c, Params* P) {
   if (c->head_select_mode != KVS_HEADS_SEPARATE && c->head_select_mode != KVS_HEADS_SHARED)
     return KVS_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
-  if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0) return KVS_ERR_INVALID_ARG;
+  if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0 && c->kv_type != KVS_KV_Q4_0)
+    return KVS_ERR_INVALID_ARG;
   const int R = rep_count_of(c);
   if (R < 0) return KVS_ERR_INVALID_ARG;
   if (c->head_dim != kvs::kDim || c->block_size != kvs::kBlock) return KVS_ERR_UNSUPPORTED;
@@ -181,7 +182,9 @@ size_t kvs_rep_bytes_per_block(const kvs_config* cfg) {
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg) {
   Params P;
   if (make_params(cfg, &P) != KVS_OK) return 0;
-  return (size_t)P.Hkv * (P.kv == kvs::kKvQ8 ? (size_t)kvs::kQ8Record : (size_t)kvs::kTile * 2);
+  const size_t rec = P.kv == kvs::kKvQ8 ? (size_t)kvs::kQ8Record
+                     : P.kv == kvs::kKvQ4 ? (size_t)kvs::kQ4Record : (size_t)kvs::kTile * 2;
+  return (size_t)P.Hkv * rec;
 }
 
 int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,
@@ -189,7 +192,7 @@ int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* 
   Params P;
   int st = make_params(cfg, &P);
   if (st != KVS_OK) return st;
-  if (P.kv != kvs::kKvQ8 || n_blocks < 0) return KVS_ERR_INVALID_ARG;
+  if (P.kv == kvs::kKvFp16 || n_blocks < 0) return KVS_ERR_INVALID_ARG;
   if (n_blocks == 0) return KVS_OK;
   if (n_blocks > 65535) return KVS_ERR_UNSUPPORTED;  // grid y
   if (!src_pool || !phys_block_ids || !dst_pool) return KVS_ERR_INVALID_ARG;

@@ -14,10 +14,15 @@ constexpr int kTile = kBlock * kDim;  // fp16 elements in one (block, KV head) t
 constexpr int kQ8Group = 32;
 constexpr int kQ8Codes = kBlock * kDim;                                // bytes of codes
 constexpr int kQ8Record = kQ8Codes + kBlock * (kDim / kQ8Group) * 2;  // 17408 bytes
+// Q4_0 record: codes [128 tokens][64 bytes] -- word k of a token row holds channels 8k .. 8k+7,
+// channel 8k + 2i in bits 4i..4i+3 and channel 8k + 2i + 1 in bits 16+4i..19+4i -- then fp16 scales
+// [128][4] as for Q8_0.
+constexpr int kQ4Codes = kBlock * kDim / 2;                            // bytes of codes
+constexpr int kQ4Record = kQ4Codes + kBlock * (kDim / kQ8Group) * 2;  // 9216 bytes
 
 enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3, kDynamic = 4 };  // Dynamic: scored like Fix
 enum Mode { kSeparate = 0, kShared = 1 };
-enum KvType { kKvFp16 = 0, kKvQ8 = 1 };
+enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2 };
 
 // Launch-time constants of one call (passed by value to every kernel).
 struct Params {

@@ -1,4 +1,4 @@
-// kvs_quantize_kv: Q8_0 records of fp16 K or V tiles.  Q8_0 is the published llama.cpp block
+// kvs_quantize_kv: Q8_0 or Q4_0 records of fp16 K or V tiles.  Q8_0 is the published llama.cpp block
 // format that the operator's kv_type list names (KTransformers long-context article, configuration
 // list; the instagit page's operator constructor): per token, blocks of 32 channels with scale
 // d = max|x| / 127 kept in fp16 and int8 codes round(x / d), ties away from zero.
@@ -15,6 +15,7 @@ namespace kvs {
 __global__ __launch_bounds__(256) void quantize_q8_kernel(const uint16_t* __restrict__ src,
                                                           const int32_t* __restrict__ ids, int Hkv,
                                                           unsigned char* __restrict__ dst) {
+#pragma clang fp contract(off)  // x * (1/d) is rounded before it is rounded to a code
   const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
   const size_t tile = (size_t)ids[i] * Hkv + h;
   const int tok = t >> 1, half = t & 1;
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const uint16_t* __rest
       uint32_t word = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int c = (int)roundf(x[4 * e + k] * inv);
+        const float p = x[4 * e + k] * inv;
+        const int c = (int)roundf(p);
         word |= (uint32_t)(c & 0xFF) << (8 * k);
       }
       codes[8 * b + e] = word;
@@ -62,10 +64,79 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const uint16_t* __rest
   *reinterpret_cast<uint32_t*>(rec + kQ8Codes + tok * 8 + 4 * half) = sw;
 }
 
+// Q4_0, the format's other block size-32 variant: m = the first value of largest magnitude, d = m / -8,
+// codes min(15, trunc(x * (1/d) + 8.5)) (x * (1/d) lies in [-8, 8], so the sum is positive and the
+// conversion truncates), all fp32 with IEEE division; d kept in fp16.  Same lane mapping as Q8_0; the
+// codes of 8 channels share a word (channel 2i in bits 4i, channel 2i+1 in bits 16+4i).
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ ids, int Hkv,
+                                                          unsigned char* __restrict__ dst) {
+#pragma clang fp contract(off)
+  const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
+  const size_t tile = (size_t)ids[i] * Hkv + h;
+  const int tok = t >> 1, half = t & 1;
+  const uint4* in = reinterpret_cast<const uint4*>(src + tile * kTile + tok * kDim + 64 * half);
+  uint4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) raw[u] = in[u];
+  unsigned char* rec = dst + tile * kQ4Record;
+  uint32_t words[8];
+  _Float16 sc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 r = raw[4 * b + u];
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * u + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xFFFFu));
+        x[8 * u + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+      }
+    }
+    float amax = 0.f, m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (fabsf(x[e]) > amax) { amax = fabsf(x[e]); m = x[e]; }  // the first of the largest
+    float d = m / -8.0f;  // -0 for an all-zero block
+    // kept as is for the fp16 store: a fused multiply-and-convert adds +0 and would lose the sign of -0
+    __asm__ volatile("" : "+v"(d));
+    const float inv = d != 0.f ? 1.0f / d : 0.f;
+    // x * (1/d) and + 8.5 are two roundings, as the format defines them: no fused multiply-add
+    auto code = [&](float v) {
+#pragma clang fp contract(off)
+      const float p = v * inv;
+      return (uint32_t)min(15, (int)(p + 8.5f));
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const uint32_t c0 = code(x[8 * k + 2 * i2]);
+        const uint32_t c1 = code(x[8 * k + 2 * i2 + 1]);
+        word |= (c0 << (4 * i2)) | (c1 << (16 + 4 * i2));
+      }
+      words[4 * b + k] = word;
+    }
+    sc[b] = (_Float16)d;
+  }
+  uint4* co = reinterpret_cast<uint4*>(rec + tok * (kDim / 2) + 32 * half);
+  co[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  co[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  const uint32_t sw = (uint32_t)__builtin_bit_cast(uint16_t, sc[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, sc[1]) << 16);
+  *reinterpret_cast<uint32_t*>(rec + kQ4Codes + tok * 8 + 4 * half) = sw;
+}
+
 hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
                               hipStream_t s) {
-  hipLaunchKernelGGL(quantize_q8_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
+  if (P.kv == kKvQ4)
+    hipLaunchKernelGGL(quantize_q4_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
+  else
+    hipLaunchKernelGGL(quantize_q8_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
   return hipGetLastError();
 }
 

@@ -26,14 +26,28 @@ __device__ inline void q8_row8(const unsigned char* rec, int tok, int c, float f
   }
 }
 
-template <int METHOD, bool Q8>
+// 8 cached values of a Q4_0 record: channels 8c..8c+7 of token `tok` (word c of its row), d * (code - 8).
+__device__ inline void q4_row8(const unsigned char* rec, int tok, int c, float f[8]) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(rec + tok * (kDim / 2) + c * 4);
+  const float d = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(
+                      rec + kQ4Codes + tok * (kDim / kQ8Group) * 2 + (c * 8 / kQ8Group) * 2));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = (float)((int)((w >> (4 * i)) & 0xF) - 8) * d;
+    f[2 * i + 1] = (float)((int)((w >> (16 + 4 * i)) & 0xF) - 8) * d;
+  }
+}
+
+template <int METHOD, int KV>
 __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict__ k_pool,
                                                          const int32_t* __restrict__ ids, int Hkv,
                                                          int rep_num, void* __restrict__ rep_pool) {
   const int h = blockIdx.y;
   const size_t p = (size_t)ids[blockIdx.x];
   const uint16_t* tile = static_cast<const uint16_t*>(k_pool) + (p * Hkv + h) * kTile;
-  const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + (p * Hkv + h) * (size_t)kQ8Record;
+  const unsigned char* rec = static_cast<const unsigned char*>(k_pool) +
+                             (p * Hkv + h) * (size_t)(KV == kKvQ4 ? kQ4Record : kQ8Record);
+  constexpr bool Q8 = KV != kKvFp16;  // a quantized record
   const int t = threadIdx.x, c = t & 15, r = t >> 4;
 
   if constexpr (METHOD == kFix) {  // rows 0, s, 2s, ... (fp16: copied verbatim)
@@ -42,7 +56,7 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
     for (int rr = r; rr < rep_num; rr += 16) {
       if constexpr (Q8) {
         float f[8];
-        q8_row8(rec, rr * stride, c, f);
+        if constexpr (KV == kKvQ4) q4_row8(rec, rr * stride, c, f); else q8_row8(rec, rr * stride, c, f);
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (uint32_t)f2h_bits(f[2 * e]) | ((uint32_t)f2h_bits(f[2 * e + 1]) << 16);
@@ -66,7 +80,9 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float f[8];
-      if constexpr (Q8) q8_row8(rec, r + 16 * i, c, f); else unpack8(raw[i], f);
+      if constexpr (KV == kKvQ4) q4_row8(rec, r + 16 * i, c, f);
+      else if constexpr (KV == kKvQ8) q8_row8(rec, r + 16 * i, c, f);
+      else unpack8(raw[i], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (METHOD == kMean) a[e] += f[e];
@@ -112,23 +128,24 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
   }
 }
 
-template <bool Q8>
+template <int KV>
 static void launch_reps_q(const Params& P, dim3 grid, const void* kp, const int32_t* ids, int rep_num,
                           void* rep_pool, hipStream_t s) {
   const dim3 block(256);
   switch (P.method) {
-    case kQuest: hipLaunchKernelGGL((build_reps_kernel<kQuest, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    case kMax:   hipLaunchKernelGGL((build_reps_kernel<kMax, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    case kMean:  hipLaunchKernelGGL((build_reps_kernel<kMean, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
-    default:     hipLaunchKernelGGL((build_reps_kernel<kFix, Q8>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kQuest: hipLaunchKernelGGL((build_reps_kernel<kQuest, KV>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMax:   hipLaunchKernelGGL((build_reps_kernel<kMax, KV>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    case kMean:  hipLaunchKernelGGL((build_reps_kernel<kMean, KV>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
+    default:     hipLaunchKernelGGL((build_reps_kernel<kFix, KV>), grid, block, 0, s, kp, ids, P.Hkv, rep_num, rep_pool); break;
   }
 }
 
 hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t* ids, int n,
                              int rep_num, void* rep_pool, hipStream_t s) {
   const dim3 grid(n, P.Hkv);
-  if (P.kv == kKvQ8) launch_reps_q<true>(P, grid, k_pool, ids, rep_num, rep_pool, s);
-  else launch_reps_q<false>(P, grid, k_pool, ids, rep_num, rep_pool, s);
+  if (P.kv == kKvQ8) launch_reps_q<kKvQ8>(P, grid, k_pool, ids, rep_num, rep_pool, s);
+  else if (P.kv == kKvQ4) launch_reps_q<kKvQ4>(P, grid, k_pool, ids, rep_num, rep_pool, s);
+  else launch_reps_q<kKvFp16>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : 
 // (seq * Hkv + h) * n_il_max + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
-template <int G, int METHOD, int MODE, bool Q8>
+template <int G, int METHOD, int MODE, int KV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void score_select_kernel(
     AttnArgs A, const void* __restrict__ rep_pool, float* __restrict__ scores, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int n_sc,
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
     const int xi = x - n_score_wg;
     const int per_seq = P.Hkv * A.n_il_max;
     const int r = xi % per_seq;
-    attn_item<G, true, false, Q8>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
+    attn_item<G, true, false, KV>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
     return;
   }
   constexpr bool SEP = MODE == kSeparate;
@@ -65,22 +65,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   if (threadIdx.x == 0) st_coh(cp, 0);  // stored last: the selection's barriers would wait for it
 }
 
-template <int G, int METHOD, bool Q8>
+template <int G, int METHOD, int KV>
 static void launch_ss_mq(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
                          int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
   if (A.P.mode == kSeparate)
-    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, Q8>), grid, dim3(256), 0, s, A, reps,
+    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, KV>), grid, dim3(256), 0, s, A, reps,
                        scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
   else
-    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kShared, Q8>), grid, dim3(256), 0, s, A, reps,
+    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kShared, KV>), grid, dim3(256), 0, s, A, reps,
                        scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
 }
 
 template <int G, int METHOD>
 static void launch_ss_m(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
                         int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
-  if (A.P.kv == kKvQ8) launch_ss_mq<G, METHOD, true>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
-  else launch_ss_mq<G, METHOD, false>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+  if (A.P.kv == kKvQ8) launch_ss_mq<G, METHOD, kKvQ8>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+  else if (A.P.kv == kKvQ4) launch_ss_mq<G, METHOD, kKvQ4>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+  else launch_ss_mq<G, METHOD, kKvFp16>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
 }
 
 template <int G>
@@ -118,7 +119,7 @@ static hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, f
 // (seq * Hkv + h) * n_il_max + t.  A half without a tile (past the sequence's own count or the end)
 // still takes part in the barriers: it computes an empty tile and stores nothing.  Two halves (73 KiB
 // of LDS) rather than four quarters per workgroup let the tiles spread over twice as many CUs.
-template <int G, bool Q8>
+template <int G, int KV>
 __global__ __launch_bounds__(512) void topk_il_wide_kernel(AttnArgs A, const float* __restrict__ scores,
                                                             int32_t* __restrict__ sel,
                                                             int32_t* __restrict__ sel_count,
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(512) void topk_il_wide_kernel(AttnArgs A, const flo
     ntok = v < 0 ? 0 : lt.y;
   }
   const size_t head0 = (size_t)seq * P.Hq + (size_t)h * G;
-  attn_tile<G, Q8>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok,
+  attn_tile<G, KV>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok,
                A.part_o + head0 * A.max_parts * kDim, A.part_ml + head0 * A.max_parts * 2, A.max_parts,
                t, smem + (threadIdx.x >> 8) * kAttnLdsBytes, have);
 }
@@ -158,10 +159,13 @@ static hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, in
   const dim3 grid(n_topk + (n_il_total + 1) / 2), block(512);
 #define KVS_WIDE(GG)                                                                                 \
   if (A.P.kv == kKvQ8)                                                                               \
-    hipLaunchKernelGGL((topk_il_wide_kernel<GG, true>), grid, block, 0, s, A, scores, sel, sel_count, \
+    hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvQ8>), grid, block, 0, s, A, scores, sel, sel_count, \
+                       tiles, n_topk, n_il_total);                                                  \
+  else if (A.P.kv == kKvQ4)                                                                          \
+    hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvQ4>), grid, block, 0, s, A, scores, sel, sel_count, \
                        tiles, n_topk, n_il_total);                                                  \
   else                                                                                               \
-    hipLaunchKernelGGL((topk_il_wide_kernel<GG, false>), grid, block, 0, s, A, scores, sel, sel_count, \
+    hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvFp16>), grid, block, 0, s, A, scores, sel, sel_count, \
                        tiles, n_topk, n_il_total)
   switch (A.P.g) {
     case 1: KVS_WIDE(1); break;

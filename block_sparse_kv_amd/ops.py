@@ -22,8 +22,8 @@ def alloc_rep_pool(cfg: B.Config, n_phys: int, device) -> torch.Tensor:
 
 
 def alloc_q8_pool(cfg: B.Config, n_phys: int, device) -> torch.Tensor:
-    """A Q8_0 K or V pool: [n_phys][Hkv] records of int8 codes [128][128] + fp16 scales [128][4],
-    as bytes [n_phys][Hkv][17408]."""
+    """A quantized K or V pool of cfg.kv_type as bytes [n_phys][Hkv][record]: Q8_0 records of 17408
+    bytes (int8 codes [128][128] + fp16 scales [128][4]), Q4_0 records of 9216 bytes."""
     per_block = B.kvs_kv_bytes_per_block(cfg)
     if per_block == 0:
         raise B.KvsError(B.KVS_ERR_INVALID_ARG, "alloc_q8_pool")

@@ -31,6 +31,9 @@
  *                kv_type Q8_0: [n_phys][Hkv] records of 17408 bytes, one per (block, KV head):
  *                int8 codes [128 tokens][128], then fp16 scales [128 tokens][4]; channel c of token
  *                t holds scale[t][c / 32] * code[t][c] (see kvs_quantize_kv)
+ *                kv_type Q4_0: [n_phys][Hkv] records of 9216 bytes: codes [128 tokens][64 bytes], word k
+ *                of a row holding channels 8k..8k+7 (channel 8k+2i in bits 4i..4i+3, 8k+2i+1 in bits
+ *                16+4i..19+4i), then fp16 scales [128 tokens][4]; value scale * (code - 8)
  *   rep_pool     [n_phys][Hkv][R][128]  fp16, except fp32 for KVS_REP_MEAN.
  *                R = 2 for Quest (r=0 channel-wise min key, r=1 channel-wise max key), 1 for Max
  *                and Mean, rep_num for Fix (r-th rep = token r*(128/rep_num) of the block).
@@ -81,10 +84,13 @@ typedef enum { KVS_REP_QUEST = 0, KVS_REP_MAX = 1, KVS_REP_MEAN = 2, KVS_REP_FIX
 typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mode;
 
 /* Cache precision of k_pool / v_pool: the operator's kv_type [KT-LC §4.5 configuration list; the
- * instagit page's operator constructor, step 3], which names FP16, FP32, Q4_0 and Q8_0.  FP16 and
- * Q8_0 are provided; Q8_0 is the published llama.cpp block format: per token and KV head, blocks
- * of 32 channels with scale d = max|x| / 127 (fp16) and int8 codes round(x / d), ties away from zero. */
-typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1 } kvs_kv_type;
+ * instagit page's operator constructor, step 3], which names FP16, FP32, Q4_0 and Q8_0.  FP16, Q8_0
+ * and Q4_0 are provided, the last two being llama.cpp's published block formats, per token and KV head
+ * in blocks of 32 channels with an fp16 scale:
+ *   Q8_0: d = max|x| / 127, int8 codes round(x / d) ties away from zero, value d * code;
+ *   Q4_0: m = the first value of largest magnitude, d = m / -8, codes min(15, trunc(x / d + 8.5)) in
+ *         0..15, value d * (code - 8). */
+typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2 } kvs_kv_type;
 
 /* Host struct.  Field order and types are part of the ABI. */
 typedef struct kvs_config {
@@ -117,16 +123,18 @@ int kvs_rep_count(const kvs_config* cfg /* host */);
 size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
 
 /* Bytes of one physical block of k_pool (or v_pool) over all KV heads: Hkv * 32768 for FP16,
- * Hkv * 17408 for Q8_0; 0 on a bad config. */
+ * Hkv * 17408 for Q8_0, Hkv * 9216 for Q4_0; 0 on a bad config. */
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
 
 /*
- * kvs_quantize_kv -- Q8_0 records of fp16 tiles [kv_type, see kvs_kv_type].  For each of the
- * n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads the fp16 tile
- * [128 tokens][128] of src_pool (laid out as an FP16 pool) and writes the Q8_0 record at the same id
- * of dst_pool (laid out as a Q8_0 pool).  Per 32 channels of a token: d = max|x| / 127, codes
- * round(x * (1/d)) ties away from zero, both in fp32 (an all-zero block: d = 0, codes 0); d is
- * stored rounded to fp16.  Used for keys and values alike.  cfg->kv_type must be KVS_KV_Q8_0.
+ * kvs_quantize_kv -- Q8_0 / Q4_0 records of fp16 tiles [kv_type, see kvs_kv_type].  For each of
+ * the n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads the fp16 tile
+ * [128 tokens][128] of src_pool (laid out as an FP16 pool) and writes the record at the same id of
+ * dst_pool (laid out as a pool of cfg->kv_type).  Per 32 channels of a token, in fp32 with IEEE
+ * division: Q8_0 d = max|x| / 127, codes round(x * (1/d)) ties away from zero (an all-zero block:
+ * d = 0, codes 0); Q4_0 d = m / -8 for m the first value of largest magnitude (+0 for an all-zero
+ * block), codes min(15, trunc(x * (1/d) + 8.5)) (all-zero: 8).  d is stored rounded to fp16.  Used
+ * for keys and values alike.  cfg->kv_type must be Q8_0 or Q4_0.
  * n_blocks == 0 is a no-op.  Both pools 16-byte aligned.
  */
 int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,
@@ -140,7 +148,7 @@ int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* 
  *   Mean:  channel-wise mean in fp32;             Fix: rows 0, s, 2s, ... with s = 128/rep_num.
  * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.  Dynamic reps come
  * from kvs_build_dynamic_reps instead (KVS_ERR_INVALID_ARG here).
- * With kv_type Q8_0 the reps are taken over the cached values scale * code (exact in fp32) and stored
+ * With kv_type Q8_0 / Q4_0 the reps are taken over the cached values (exact in fp32) and stored
  * rounded to fp16 (Mean: fp32).
  */
 int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,

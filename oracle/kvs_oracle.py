@@ -298,6 +298,7 @@ def quantize_q4_0(x):
     xg = x.reshape(*lead, d // Q8_GROUP, Q8_GROUP)
     first = np.abs(xg).argmax(axis=-1)                              # first index of the largest |x|
     m = np.take_along_axis(xg, first[..., None], -1)[..., 0]
+    m = np.where(np.abs(xg).max(axis=-1) > 0, m, np.float32(0.0)).astype(np.float32)  # +0 if all zero
     dsc = (m / np.float32(-8.0)).astype(np.float32)
     with np.errstate(divide="ignore"):
         inv = np.where(dsc != 0, np.float32(1.0) / np.where(dsc != 0, dsc, 1), np.float32(0.0)).astype(np.float32)

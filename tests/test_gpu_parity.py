@@ -120,6 +120,22 @@ SMALL_Q8 = [
 ]
 
 
+SMALL_Q4 = [
+    (32, 8, 128, 512, 12, "quest", "separate", 1, [5000, 129, 1, 7777]),
+    (32, 8, 100, 300, 5, "max", "shared", 1, [4000, 3001]),
+    (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_Q4)),
+                         ids=[f"q4-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_Q4])
+def test_small_cases_q4(idx):
+    Hq, Hkv, I, W, k, rep, mode, rn, lens = SMALL_Q4[idx]
+    c = cfg_of(Hq, Hkv, I, W, k, rep, mode, rn, kv="q4_0")
+    case = Case(c, lens, seed=kvsynth.mix_seed(78, idx), n_hot=3)
+    run_full_check(case, f"small q4 {rep}/{mode} {Hq}x{Hkv}")
+
+
 @pytest.mark.parametrize("idx", range(len(SMALL_Q8)),
                          ids=[f"q8-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_Q8])
 def test_small_cases_q8(idx):

@@ -1,9 +1,10 @@
-"""The Q8_0 cache precision on the GPU against the oracle (needs an MI355X).
+"""The Q8_0 and Q4_0 cache precisions on the GPU against the oracle (needs an MI355X).
 
 kv_type Q8_0 is the published llama.cpp block format that the operator's kv_type list names: per
 token and KV head, 32-channel blocks with an fp16 scale max|x|/127 and int8 codes, ties away from
-zero.  The codes and scales must match the oracle bit for bit (both take the rounding decisions in
-fp32); reps over the cached values are value-equal (Mean: relative 1e-4).
+zero; Q4_0 its 4-bit sibling (scale m/-8 for the first largest-magnitude value m, codes
+min(15, trunc(x/d + 8.5))).  The codes and scales must match the oracle bit for bit (both take the
+rounding decisions in fp32); reps over the cached values are value-equal (Mean: relative 1e-4).
 """
 from __future__ import annotations
 
@@ -57,6 +58,18 @@ def fp16_pool(n_phys, Hkv, seed):
     return x.to(torch.float16)
 
 
+def split_q4(pool_q4):
+    """[n][Hkv][9216] bytes -> codes uint8 [n][Hkv][128][128], scales fp16 [n][Hkv][128][4]."""
+    a = pool_q4.cpu().numpy()
+    w = a[..., : 128 * 64].copy().view(np.uint32).reshape(*a.shape[:2], 128, 16)
+    codes = np.zeros((*a.shape[:2], 128, 128), dtype=np.uint8)
+    for i in range(4):
+        codes[..., 2 * i::8] = (w >> (4 * i)) & 0xF
+        codes[..., 2 * i + 1::8] = (w >> (16 + 4 * i)) & 0xF
+    scales = a[..., 128 * 64:].copy().view(np.float16).reshape(*a.shape[:2], 128, 4)
+    return codes, scales
+
+
 def split_records(pool_q8):
     """[n][Hkv][17408] bytes -> codes int8 [n][Hkv][128][128], scales fp16 [n][Hkv][128][4]."""
     a = pool_q8.cpu().numpy()
@@ -106,5 +119,50 @@ def test_reps_over_q8_cache(rep, rep_num):
         got = rp[p].double().cpu().numpy()
         if rep == "mean":
             close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"q8 mean reps {p}")
+        else:
+            assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
+
+
+@pytest.mark.parametrize("Hkv", [1, 8])
+def test_quantize_q4_bit_exact(Hkv):
+    say(f"[case] q4 quantize Hkv={Hkv}")
+    n_phys = 7
+    c = q8_cfg(Hkv=Hkv, g=1, kv_type="q4_0")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(411, Hkv))
+    src[1, 0, 5, :32] = torch.tensor([8.0, -8.0] + [0.0] * 30, dtype=torch.float16, device=DEV)  # tie
+    dst = ops.alloc_q8_pool(c, n_phys, DEV)
+    assert dst.shape[-1] == 9216
+    dst.fill_(0xAB)
+    ids = torch.tensor([5, 0, 1, 6], dtype=torch.int32)
+    ops.quantize_kv(c, src, ids, dst)
+    torch.cuda.synchronize()
+    got_c, got_s = split_q4(dst)
+    want_c, want_s = orc.quantize_q4_0(src.float().cpu().numpy())
+    for p in range(n_phys):
+        if p in ids.tolist():
+            assert np.array_equal(got_c[p], want_c[p]), (p, np.argwhere(got_c[p] != want_c[p])[:4])
+            assert np.array_equal(got_s[p].view(np.uint16), want_s[p].view(np.uint16)), p
+        else:
+            assert np.all(dst[p].cpu().numpy() == 0xAB), p
+
+
+@pytest.mark.parametrize("rep,rep_num", [("quest", 1), ("mean", 1), ("fix", 4)])
+def test_reps_over_q4_cache(rep, rep_num):
+    say(f"[case] q4 reps {rep}/{rep_num}")
+    n_phys, Hkv = 6, 8
+    c = q8_cfg(Hkv=Hkv, rep_method=rep, rep_num=rep_num, kv_type="q4_0")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(412, rep_num, len(rep)))
+    kq = ops.alloc_q8_pool(c, n_phys, DEV)
+    ops.quantize_kv(c, src, torch.arange(n_phys, dtype=torch.int32), kq)
+    rp = ops.alloc_rep_pool(c, n_phys, DEV)
+    ops.build_reps(c, kq, torch.tensor([4, 1, 2], dtype=torch.int32), rp)
+    torch.cuda.synchronize()
+    codes, scales = split_q4(kq)
+    for p in (4, 1, 2):
+        K = orc.dequantize_q4_0(codes[p], scales[p]).transpose(1, 0, 2)
+        want = orc.stored_reps(orc.block_reps(K, B, rep, rep_num), rep)[0]
+        got = rp[p].double().cpu().numpy()
+        if rep == "mean":
+            close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"q4 mean reps {p}")
         else:
             assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
