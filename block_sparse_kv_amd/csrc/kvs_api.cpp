@@ -458,8 +458,12 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
   int32_t* cnt = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  void* aws = static_cast<char*>(workspace) + S.attn_off;
+  kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                              seq_lens, sel, cnt, out);
   clear_stale_error();
-  hipError_t e = kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens, batch, scores, s);
+  bool il_done = false;  // Initial/Local tiles streamed with the scoring (rows of up to 2048 blocks)
+  hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s, &il_done);
   if (e == hipSuccess)
     e = kvs::launch_compact(P, scores, max_blocks_per_seq, seq_lens, presel, n_presel, batch, cs, cid, clen, s);
   // each (sequence, group) row is a sequence of its own: n_eff blocks, all candidates
@@ -471,10 +475,7 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   if (e == hipSuccess) e = kvs::launch_topk(C, cs, clen, rows, n_presel, csel, cnt, nullptr, nullptr, s);
   if (e == hipSuccess) e = kvs::launch_map_back(csel, k, cid, n_presel, rows, sel, s);
   if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/selection");
-  void* aws = static_cast<char*>(workspace) + S.attn_off;
-  kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
-                              seq_lens, sel, cnt, out);
-  e = kvs::launch_attn_tiles(a, batch, true, false, s);
+  e = kvs::launch_attn_tiles(a, batch, !il_done, false, s);
   if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/tiles");
   return hip_status(kvs::launch_merge(a, batch, s), "kvs_decode_step_preselected/merge");
 }

@@ -52,6 +52,10 @@ hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s);
 // The whole decode step (step.hip): scores [batch][G][max_blocks], sel / sel_count, and the selected
 // tiles' physical ids (tiles [batch][G][topk]) are its intermediates; A.sel must be `tiles`.  ctr:
 // [batch][G] ints, zero when the call starts and zero again when it ends.
+// Scores [batch][G][max_blocks] of every candidate, and, for rows the fused step handles in one
+// launch (max_blocks <= 2048), the Initial/Local tiles in the same launch (*il_done = true).
+hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* scores, int batch, hipStream_t s,
+                           bool* il_done);
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
                               int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s);
 

@@ -22,7 +22,8 @@ constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : 
 
 // First the scoring workgroups, n_sc per (sequence, group), over every KV head (SHARED) or over one KV
 // head (SEPARATE; group = KV head): dispatched first, their few loads are not queued behind the
-// tiles' stream.  Then n_il_wg Initial/Local tiles, tile t of KV head h of sequence seq at
+// tiles' stream.  With sel null the kernel only scores and streams the tiles (a selection made by
+// later launches).  Then n_il_wg Initial/Local tiles, tile t of KV head h of sequence seq at
 // (seq * Hkv + h) * n_il_max + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                                                  A.seq_lens[seq], c * sb, sb,
                                                  scores + (size_t)seq * P.G * A.max_blocks,
                                                  reinterpret_cast<float*>(smem), grp);
+  if (sel == nullptr) return;  // scores and Initial/Local tiles only: the selection comes later
   wait_mem();
   __syncthreads();
   int* cp = ctr + (size_t)seq * P.G + grp;
@@ -176,6 +178,13 @@ static hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, in
   }
 #undef KVS_WIDE
   return hipGetLastError();
+}
+
+hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* scores, int batch, hipStream_t s,
+                           bool* il_done) {
+  *il_done = A.max_blocks <= kStepTopkSmall;
+  if (*il_done) return launch_score_select(A, rep_pool, scores, nullptr, nullptr, nullptr, nullptr, batch, s);
+  return launch_score(A.P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
 }
 
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,

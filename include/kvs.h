@@ -212,8 +212,9 @@ size_t kvs_decode_step_preselected_workspace_size(const kvs_config* cfg, int32_t
  * [KT-LC §4.4]: per (sequence, group), only the blocks of presel [batch][G][n_presel] (ascending, -1
  * padded, e.g. from kvs_preselect_blocks) that are still candidates at the current length compete;
  * k_eff = min(topk, their number), so with topk >= the set's size the set is attended as it is.
- * Scores, ties, order and attention as kvs_decode_step.  Enqueued as scoring, compaction, top-k,
- * mapping, attention tiles and merge; the workspace (>= the size query, 256-byte aligned) is scratch.
+ * Scores, ties, order and attention as kvs_decode_step.  Enqueued as scoring (with the Initial/Local
+ * tiles for max_blocks_per_seq <= 2048), compaction, top-k, mapping, attention tiles and merge; the
+ * workspace (>= the size query, 256-byte aligned) is scratch.
  * sel_out / sel_count_out (nullable) receive the selection.
  */
 int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void* k_pool,
