@@ -464,16 +464,20 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   clear_stale_error();
   bool il_done = false;  // Initial/Local tiles streamed with the scoring (rows of up to 2048 blocks)
   hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s, &il_done);
-  if (e == hipSuccess)
-    e = kvs::launch_compact(P, scores, max_blocks_per_seq, seq_lens, presel, n_presel, batch, cs, cid, clen, s);
-  // each (sequence, group) row is a sequence of its own: n_eff blocks, all candidates
-  Params C = P;
-  C.G = 1;
-  C.mode = kvs::kShared;
-  C.initial_len = 0;
-  C.local_len = 0;
-  if (e == hipSuccess) e = kvs::launch_topk(C, cs, clen, rows, n_presel, csel, cnt, nullptr, nullptr, s);
-  if (e == hipSuccess) e = kvs::launch_map_back(csel, k, cid, n_presel, rows, sel, s);
+  if (n_presel <= 256) {  // the set ranked in one launch
+    if (e == hipSuccess)
+      e = kvs::launch_presel_select(P, scores, max_blocks_per_seq, seq_lens, presel, n_presel, batch, sel, cnt, s);
+  } else {  // compacted rows, each a sequence of its own (n_eff blocks, all candidates), and the top-k
+    if (e == hipSuccess)
+      e = kvs::launch_compact(P, scores, max_blocks_per_seq, seq_lens, presel, n_presel, batch, cs, cid, clen, s);
+    Params C = P;
+    C.G = 1;
+    C.mode = kvs::kShared;
+    C.initial_len = 0;
+    C.local_len = 0;
+    if (e == hipSuccess) e = kvs::launch_topk(C, cs, clen, rows, n_presel, csel, cnt, nullptr, nullptr, s);
+    if (e == hipSuccess) e = kvs::launch_map_back(csel, k, cid, n_presel, rows, sel, s);
+  }
   if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/selection");
   e = kvs::launch_attn_tiles(a, batch, !il_done, false, s);
   if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/tiles");

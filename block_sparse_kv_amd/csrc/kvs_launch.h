@@ -30,6 +30,9 @@ hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float*
                                hipStream_t s);
 hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,
                                int max_blocks, float* bs, hipStream_t s);
+hipError_t launch_presel_select(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
+                                const int32_t* presel, int n_presel, int batch, int32_t* sel,
+                                int32_t* sel_count, hipStream_t s);
 hipError_t launch_compact(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
                           const int32_t* presel, int n_presel, int batch, float* cs, int32_t* cid,
                           int32_t* clen, hipStream_t s);

@@ -4,7 +4,9 @@
 //  * block_score_kernel: a block's preselect score is the sum of its tokens' scores
 //    (kvs_token_importance), -inf outside the candidates -- the layout of the block scores, so the
 //    set is the ordinary top-k of these rows.
-//  * The confined decode step scores every candidate as usual; compact_kernel then keeps, per
+//  * The confined decode step scores every candidate as usual.  For sets of up to 256 blocks one
+//    workgroup per (sequence, group) ranks the set's current candidates by counting
+//    (presel_select_kernel).  For larger sets compact_kernel keeps, per
 //    (sequence, group), the scores of the set's blocks that are still candidates, in block order,
 //    as one row of a compacted batch (each row its own "sequence" of n_eff blocks with no Initial or
 //    Local part), the ordinary top-k selects in it, and map_back_kernel turns the picks into block
@@ -77,6 +79,78 @@ __global__ __launch_bounds__(256) void map_back_kernel(const int32_t* __restrict
   if (x >= total) return;
   const int row = x / topk, j = csel[x];
   sel[x] = j >= 0 && j < n_presel ? cid[(size_t)row * n_presel + j] : -1;
+}
+
+// Sets of up to 256 blocks: the whole confined selection of one (sequence, group) row in one
+// workgroup of 1024 lanes.  Entry i's rank among the set's current candidates (higher score, or equal
+// and lower block, beats it) is counted by four lanes, one per quarter of the entries, with 16-byte
+// LDS reads; the k_eff best are kept and a prefix over the (ascending) set gives each its slot.
+constexpr int kPreselFused = 256;
+
+__global__ __launch_bounds__(1024) void presel_select_kernel(Params P, const float* __restrict__ scores,
+                                                             int max_blocks, const int32_t* __restrict__ seq_lens,
+                                                             const int32_t* __restrict__ presel, int n_presel,
+                                                             int32_t* __restrict__ sel,
+                                                             int32_t* __restrict__ sel_count) {
+  __shared__ __attribute__((aligned(16))) float ss[kPreselFused];
+  __shared__ __attribute__((aligned(16))) int sb[kPreselFused];
+  __shared__ int part[4][kPreselFused];
+  __shared__ int wcnt[kPreselFused / 64];
+  const int row = blockIdx.x, tid = threadIdx.x, e = tid & (kPreselFused - 1), q = tid >> 8;
+  const Regions rg = regions_of(seq_lens[row / P.G], P.initial_len, P.local_len);
+  int b = -1;
+  bool ok = false;
+  float v = 0.f;
+  if (q == 0) {
+    b = e < n_presel ? presel[(size_t)row * n_presel + e] : -1;
+    ok = b >= rg.cand_lo && b < rg.cand_hi && b < max_blocks;
+    v = ok ? scores[(size_t)row * max_blocks + b] : 0.f;
+    ss[e] = v;
+    sb[e] = ok ? b : -1;
+  }
+  const int n_ok = __syncthreads_count(ok);
+  const int k = min(P.topk, n_ok);
+  {
+    const float vi = ss[e];
+    const int bi = sb[e];
+    int r = 0;
+#pragma unroll 4
+    for (int j = 64 * q; j < 64 * q + 64; j += 4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&ss[j]);
+      const int4 b4 = *reinterpret_cast<const int4*>(&sb[j]);
+      r += b4.x >= 0 && (v4.x > vi || (v4.x == vi && b4.x < bi));
+      r += b4.y >= 0 && (v4.y > vi || (v4.y == vi && b4.y < bi));
+      r += b4.z >= 0 && (v4.z > vi || (v4.z == vi && b4.z < bi));
+      r += b4.w >= 0 && (v4.w > vi || (v4.w == vi && b4.w < bi));
+    }
+    part[q][e] = r;
+  }
+  __syncthreads();  // partial ranks
+  const int lane = tid & 63, w = tid >> 6;  // waves 0..3 hold the entries (q == 0)
+  bool take = false;
+  unsigned long long m = 0ull;
+  if (q == 0) {
+    take = ok && part[0][e] + part[1][e] + part[2][e] + part[3][e] < k;
+    m = __ballot(take);
+    if (lane == 0) wcnt[w] = __popcll(m);
+  }
+  __syncthreads();  // every wave, the idle ones included
+  if (q == 0) {
+    int slot = __popcll(m & ((1ull << lane) - 1ull));
+    for (int x = 0; x < w; ++x) slot += wcnt[x];
+    int32_t* out = sel + (size_t)row * P.topk;
+    if (take) out[slot] = b;
+    for (int i = k + tid; i < P.topk; i += kPreselFused) out[i] = -1;
+    if (tid == 0) sel_count[row] = k;
+  }
+}
+
+hipError_t launch_presel_select(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
+                                const int32_t* presel, int n_presel, int batch, int32_t* sel,
+                                int32_t* sel_count, hipStream_t s) {
+  hipLaunchKernelGGL(presel_select_kernel, dim3(batch * P.G), dim3(1024), 0, s, P, scores, max_blocks,
+                     seq_lens, presel, n_presel, sel, sel_count);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,

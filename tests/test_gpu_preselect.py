@@ -75,19 +75,22 @@ def test_preselect_blocks(idx):
 
 
 STEP_CASES = [
-    # (Hq, Hkv, mode, rep, k, lens, kv)
-    (32, 8, "shared", "max", 6, [6000, 9000], "fp16"),
-    (8, 2, "separate", "quest", 4, [5000], "fp16"),
-    (16, 4, "separate", "quest", 40, [3000], "fp16"),   # k >= the set: the set itself
-    (32, 8, "shared", "max", 10, [7000], "q8_0"),
-    (16, 2, "shared", "quest", 16, [280000], "fp16"),   # long rows
+    # (Hq, Hkv, mode, rep, k, lens, kv, set size): sets of up to 256 blocks are ranked in one launch,
+    # larger ones through compacted rows and the ordinary top-k
+    (32, 8, "shared", "max", 6, [6000, 9000], "fp16", 18),
+    (8, 2, "separate", "quest", 4, [5000], "fp16", 18),
+    (16, 4, "separate", "quest", 40, [3000], "fp16", 18),   # k >= the set: the set itself
+    (32, 8, "shared", "max", 10, [7000], "q8_0", 18),
+    (16, 2, "shared", "quest", 16, [280000], "fp16", 18),   # long rows
+    (16, 4, "separate", "max", 30, [60000], "q4_0", 248),   # 254 entries: the one-launch path near its limit
+    (16, 2, "shared", "quest", 50, [60000, 40000], "fp16", 300),
 ]
 
 
 @pytest.mark.parametrize("idx", range(len(STEP_CASES)))
 def test_decode_step_preselected(idx):
-    Hq, Hkv, mode, rep, k, lens, kv = STEP_CASES[idx]
-    say(f"[case] confined decode step {Hq}x{Hkv} {mode} {rep} k={k} lens={lens} kv={kv}")
+    Hq, Hkv, mode, rep, k, lens, kv, n_pick = STEP_CASES[idx]
+    say(f"[case] confined decode step {Hq}x{Hkv} {mode} {rep} k={k} lens={lens} kv={kv} set={n_pick}")
     c = kvs.Config(num_q_heads=Hq, num_kv_heads=Hkv, initial_len=128, local_len=1024, topk=k,
                    rep_method=rep, head_select_mode=mode, kv_type=kv)
     case = Case(c, lens, seed=kvsynth.mix_seed(603, idx), n_hot=3)
@@ -96,14 +99,14 @@ def test_decode_step_preselected(idx):
     # a set per group: random candidate blocks, some Local and Initial blocks (no longer candidates)
     # and -1 padding, ascending
     g = np.random.default_rng(kvsynth.mix_seed(604, idx))
-    n_presel = 24
+    n_presel = n_pick + 6
     presel = np.full((len(lens), c.groups, n_presel), -1, dtype=np.int32)
     sets = []
     for i, L in enumerate(lens):
         _, _, cand = orc.regions(L, B, c.initial_len, c.local_len)
         row_sets = []
         for gi in range(c.groups):
-            picks = sorted(set(g.choice(cand, size=min(18, len(cand)), replace=False).tolist())
+            picks = sorted(set(g.choice(cand, size=min(n_pick, len(cand)), replace=False).tolist())
                            | {0, (L - 1) // B})  # an Initial and a Local block
             presel[i, gi, : len(picks)] = picks
             row_sets.append(picks)
