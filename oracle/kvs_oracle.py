@@ -52,6 +52,18 @@ Readings taken where the pages are silent (each is the spec here):
       preselect_block_count best candidates (ties to the lower block) form the set; a decode step
       then ranks only the current candidates inside the set, k_eff = min(k, their number) -- so
       with k >= the set's size the set itself is attended.
+  R26 Pooled preselect (the article's framework pseudocode, §4.6 preselect_block: the window's
+      votes are pooled by pool1d with padding kernel_size // 2 and stride 1, the best tokens are
+      taken, and the set is the blocks they fall in).  The pages contradict themselves here: §4.5
+      says block size 1 with preselect on is SnapKV without pooling, the pseudocode pools.  Both
+      are offered: pool_kernel = 0 is R24; an odd pool_kernel >= 1 is this reading.  The vote is
+      restricted to the Context tokens (the pseudocode slices Initial and Local off before
+      pooling), pooled by an average over pool_kernel tokens centred on each token with zeros
+      beyond the Context (torch's avg_pool1d with count_include_pad), and tokens are taken in
+      descending pooled vote (ties to the lower token) until preselect_block_count distinct blocks
+      are hit.  That is the same as ranking each candidate block by its best pooled token (ties to
+      the lower block), which is how it is computed.  The pooling kind is not named; the average
+      is SnapKV's usual choice.
   R25 kv_type Q4_0 (llama.cpp's other block format the list names, restated): per 32 channels of a
       token's row, m = the value of largest magnitude (the first one on ties), d = m / -8,
       codes q = min(15, trunc(x * (1/d) + 8.5)) in 0..15, all fp32; d stored as fp16; the cached
@@ -383,17 +395,45 @@ def dynamic_reps(K, imp, B: int, rep_num: int, mode: str, blocks):
 
 
 # ----------------------------------------------------------------------------------------------
-# O9. Preselect  [KT-LC §4.4 Preselect (after SnapKV); §4.5 preselect_block_count; reading R24]
+# O9. Preselect  [KT-LC §4.4 Preselect (after SnapKV); §4.5 preselect_block_count; §4.6
+#     preselect_block; readings R24, R26]
 # ----------------------------------------------------------------------------------------------
-def preselect_blocks(imp, L: int, B: int, initial_len: int, local_len: int, n_presel: int):
-    """Per group: the n_presel candidate blocks with the largest summed token score (ties to the
-    lower block), ascending.  imp: [G][L] token scores (``token_importance``)."""
-    _, _, cand = regions(L, B, initial_len, local_len)
-    out = []
-    for row in np.asarray(imp, dtype=np.float64):
-        bs = [row[b * B:(b + 1) * B].sum() for b in cand]
-        out.append(select_topk(bs, cand, n_presel))
+def pooled_votes(row, lo: int, hi: int, pool_kernel: int):
+    """Reading R26: the votes of the Context tokens [lo, hi), each averaged with its pool_kernel // 2
+    neighbours on either side; tokens outside [lo, hi) count as zero, the divisor is always
+    pool_kernel.  Returns float64 [hi - lo]."""
+    h = pool_kernel // 2
+    out = np.zeros(hi - lo)
+    for t in range(lo, hi):
+        acc = 0.0
+        for u in range(t - h, t + h + 1):
+            if lo <= u < hi:
+                acc += row[u]
+        out[t - lo] = acc / pool_kernel
     return out
+
+
+def preselect_scores(imp, L: int, B: int, initial_len: int, local_len: int, pool_kernel: int = 0):
+    """Per group, the preselect score of each candidate block: the sum of its tokens' scores
+    (pool_kernel = 0, reading R24) or its best pooled vote (odd pool_kernel, reading R26).
+    Returns (scores [G][n_cand], candidates)."""
+    lo, hi, cand = regions(L, B, initial_len, local_len)
+    rows = []
+    for row in np.asarray(imp, dtype=np.float64):
+        if pool_kernel == 0:
+            rows.append([row[b * B:(b + 1) * B].sum() for b in cand])
+        else:
+            pv = pooled_votes(row, lo, hi, pool_kernel) if cand else np.zeros(0)
+            rows.append([pv[b * B - lo:(b + 1) * B - lo].max() for b in cand])
+    return rows, cand
+
+
+def preselect_blocks(imp, L: int, B: int, initial_len: int, local_len: int, n_presel: int,
+                     pool_kernel: int = 0):
+    """Per group: the n_presel candidate blocks with the best preselect score (``preselect_scores``;
+    ties to the lower block), ascending.  imp: [G][L] token scores (``token_importance``)."""
+    rows, cand = preselect_scores(imp, L, B, initial_len, local_len, pool_kernel)
+    return [select_topk(bs, cand, n_presel) for bs in rows]
 
 
 def decode_step_preselected(q, K, V, presel, *, B, initial_len, local_len, topk, method, rep_num=1,

@@ -494,6 +494,57 @@ def check_preselect_identities(orc, seed=34):
         assert ps[gi] == sorted(cand[j] for j in order)
 
 
+def _pseudocode_preselect(imp_row, lo, hi, B, pool_kernel, n_presel):
+    """The pooled preselect as the article's pseudocode orders it: torch's avg_pool1d over the
+    Context votes, tokens in descending pooled vote (ties to the lower token), blocks collected in
+    that order until n_presel distinct ones are hit."""
+    import torch
+    v = torch.tensor(imp_row[lo:hi], dtype=torch.float64)[None, None]
+    pv = torch.nn.functional.avg_pool1d(v, pool_kernel, stride=1, padding=pool_kernel // 2,
+                                        count_include_pad=True)[0, 0].numpy()
+    order = sorted(range(hi - lo), key=lambda t: (-pv[t], t))
+    got = []
+    for t in order:
+        b = (lo + t) // B
+        if b not in got:
+            got.append(b)
+        if len(got) == n_presel:
+            break
+    return sorted(got), pv
+
+
+def check_preselect_pooled(orc, seed=35):
+    """Pooled preselect (reading R26): the pooled votes are torch's avg_pool1d of the Context slice;
+    the set is what the pseudocode's token ranking hits first; a vote spike pools into the next
+    block; votes of Initial / Local tokens are not pooled into the Context; pool_kernel = 1 ranks
+    blocks by their largest token score."""
+    g = np.random.default_rng(seed)
+    L, B, I, W = 50 * 8 + 3, 8, 8, 24
+    lo, hi, cand = orc.regions(L, B, I, W)
+    imp = np.abs(g.standard_normal((3, L)))
+    for pk, n in ((5, 7), (7, 3), (3, 12), (9, 1)):
+        got = orc.preselect_blocks(imp, L, B, I, W, n, pool_kernel=pk)
+        for gi in range(3):
+            want, pv = _pseudocode_preselect(imp[gi], lo, hi, B, pk, n)
+            assert got[gi] == want, (pk, n, gi, got[gi], want)
+            assert np.allclose(orc.pooled_votes(imp[gi], lo, hi, pk), pv, rtol=1e-13, atol=0)
+    got1 = orc.preselect_blocks(imp, L, B, I, W, 6, pool_kernel=1)
+    mx = imp[:, lo:hi].reshape(3, -1, B).max(axis=-1)
+    for gi in range(3):
+        order = sorted(range(len(cand)), key=lambda j: (-mx[gi, j], cand[j]))[:6]
+        assert got1[gi] == sorted(cand[j] for j in order)
+    # a spike on the last token of block 20 lifts block 21 through the window, not block 19
+    sp = 1e-3 * np.abs(g.standard_normal((1, L)))
+    sp[0, 21 * B - 1] = 10.0
+    assert orc.preselect_blocks(sp, L, B, I, W, 2, pool_kernel=5) == [[20, 21]]
+    assert orc.preselect_blocks(sp, L, B, I, W, 1, pool_kernel=0) == [[20]]
+    # spikes on the last Initial and first Local tokens stay outside the Context's pooling
+    edge = 1e-3 * np.abs(g.standard_normal((1, L)))
+    edge[0, lo - 1] = edge[0, hi] = 10.0
+    edge[0, 30 * B:31 * B] = 1.0
+    assert orc.preselect_blocks(edge, L, B, I, W, 1, pool_kernel=7) == [[30]]
+
+
 ALL_CHECKS = [
     check_quest_upper_bound, check_quest_tight_and_units, check_rep_closed_forms,
     check_hand_worked, check_regions_golden, check_regions_partition,
@@ -501,5 +552,5 @@ ALL_CHECKS = [
     check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
     check_dynamic_reps_closed_forms, check_preselect_identities, check_q4_golden,
-    check_q4_range_and_bound,
+    check_q4_range_and_bound, check_preselect_pooled,
 ]

@@ -175,6 +175,31 @@ def _presel_max_not_sum(imp, L, B, initial_len, local_len, n_presel):
             for row in np.asarray(imp, np.float64)]
 
 
+_orig_preselect = orc.preselect_blocks
+
+
+def _presel_pooled_variant(kind):
+    """Pooled preselect with one plausible mistake: pooling inside each block only, pooling over the
+    whole row (Initial / Local votes leak in), or a block's pooled votes summed instead of maxed."""
+    def f(imp, L, B, initial_len, local_len, n_presel, pool_kernel=0):
+        if pool_kernel == 0:
+            return _orig_preselect(imp, L, B, initial_len, local_len, n_presel)
+        lo, hi, cand = orc.regions(L, B, initial_len, local_len)
+        h = pool_kernel // 2
+        out = []
+        for row in np.asarray(imp, np.float64):
+            bs = []
+            for b in cand:
+                a, e = (b * B, (b + 1) * B) if kind == "in_block" else ((0, L) if kind == "full_row" else (lo, hi))
+                pv = [sum(row[u] for u in range(t - h, t + h + 1) if a <= u < e) / pool_kernel
+                      for t in range(b * B, (b + 1) * B)]
+                bs.append(sum(pv) if kind == "sum" else max(pv))
+            out.append(orc.select_topk(bs, cand, n_presel))
+        return out
+    f.__name__ = f"_presel_pool_{kind}"
+    return f
+
+
 def _presel_decode_ignores_set(q, K, V, presel, **kw):
     return orc.decode_step(q, K, V, **kw)
 
@@ -237,6 +262,9 @@ MUTANTS = [
     ("quantize_q4_0", _q4_round_even),
     ("quantize_q4_0", _q4_no_clip),
     ("decode_step_preselected", _presel_decode_ignores_set),
+    ("preselect_blocks", _presel_pooled_variant("in_block")),
+    ("preselect_blocks", _presel_pooled_variant("full_row")),
+    ("preselect_blocks", _presel_pooled_variant("sum")),
 ]
 
 
