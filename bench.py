@@ -66,6 +66,10 @@ WORKLOADS = {
     "128k-presel": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
                         n_obs=32, presel=192, layers=1, replicas=16, n_hot=50, hot_per_head=False,
                         seed=20260032),
+    # the same, with the set from pooled votes (average over a centred window of 7 tokens)
+    "128k-presel-pool": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                             n_obs=32, presel=192, pool=7, layers=1, replicas=16, n_hot=50,
+                             hot_per_head=False, seed=20260032),
     # the same two headline shapes over a Q8_0 cache (kv_type): int8 codes + fp16 scale per 32 channels
     "128k-max-q8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
                         layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="q8_0"),
@@ -186,8 +190,9 @@ class Setup:
             if "presel" in w:  # the unit's preselected set, from its own observation queries
                 q_obs = kvsynth.randn_fp16((1, w["n_obs"], w["Hq"], D), kvsynth.mix_seed(w["seed"], u, 9), device)
                 imp = ops.token_importance(self.cfg, q_obs, kp, self.table, self.lens)
-                ps, _ = ops.preselect_blocks(self.cfg, imp, self.lens, w["presel"], nb)
+                ps, _ = ops.preselect_blocks(self.cfg, imp, self.lens, w["presel"], nb, w.get("pool", 0))
                 self.presel.append(ps)
+                self.imp = imp
             self.units.append((q[None].contiguous(), kp, vp, rp))
         torch.cuda.synchronize()
         log(f"[setup] {name}: {n_units} cache units of {L} tokens generated in {time.time() - t0:.1f}s")
@@ -370,6 +375,19 @@ def measure(name, steps, warmup, device, reuse=True):
                                          hbm_gbs=kbytes / (min(times[1:]) * 1e-3) / 1e9)
         log(f"[bench] {name} token scores + Dynamic reps of one {w['L']}-token cache: "
             f"{min(times[1:]):.3f} ms ({kbytes / (min(times[1:]) * 1e-3) / 1e9:.0f} GB/s on K)")
+    if "presel" in w:  # the per-prompt cost of the set: block scores + top-k over one cache's scores
+        from block_sparse_kv_amd import ops
+        times = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ops.preselect_blocks(st.cfg, st.imp, st.lens, w["presel"], st.nb, w.get("pool", 0))
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        res["preselect_build"] = dict(ms=min(times[1:]), pool_kernel=w.get("pool", 0), n_presel=w["presel"])
+        log(f"[bench] {name} preselected set of one {w['L']}-token cache from its token scores: "
+            f"{min(times[1:]):.3f} ms (pool_kernel {w.get('pool', 0)})")
     if not reuse:
         return res
     # selection reuse: attention only, with each unit's kept selection (no scoring, no top-k)

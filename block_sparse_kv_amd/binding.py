@@ -111,7 +111,7 @@ _lib.kvs_build_dynamic_reps.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _P, _P]
 _lib.kvs_preselect_workspace_size.restype = _S
 _lib.kvs_preselect_workspace_size.argtypes = [_CFG, _I, _I]
 _lib.kvs_preselect_blocks.restype = ctypes.c_int
-_lib.kvs_preselect_blocks.argtypes = [_CFG, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+_lib.kvs_preselect_blocks.argtypes = [_CFG, _P, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P]
 _lib.kvs_decode_step_preselected_workspace_size.restype = _S
 _lib.kvs_decode_step_preselected_workspace_size.argtypes = [_CFG, _I, _I, _I]
 _lib.kvs_decode_step_preselected.restype = ctypes.c_int
@@ -218,10 +218,11 @@ def kvs_preselect_workspace_size(cfg, batch, max_blocks_per_seq) -> int:
     return _lib.kvs_preselect_workspace_size(_cfg(cfg), batch, max_blocks_per_seq)
 
 
-def kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks_per_seq, n_presel, presel,
-                         presel_count, workspace, workspace_bytes, stream=None, check=True):
+def kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks_per_seq, n_presel, pool_kernel,
+                         presel, presel_count, workspace, workspace_bytes, stream=None, check=True):
     st = _lib.kvs_preselect_blocks(_cfg(cfg), _ptr(importance), _ptr(seq_lens), batch,
-                                   max_blocks_per_seq, n_presel, _ptr(presel), _ptr(presel_count),
+                                   max_blocks_per_seq, n_presel, pool_kernel, _ptr(presel),
+                                   _ptr(presel_count),
                                    _ptr(workspace), workspace_bytes, _stream(stream))
     return _check(st, "kvs_preselect_blocks") if check else st
 

@@ -371,7 +371,8 @@ size_t kvs_preselect_workspace_size(const kvs_config* cfg, int32_t batch, int32_
 }
 
 int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const int32_t* seq_lens,
-                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel, int32_t* presel,
+                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel,
+                         int32_t pool_kernel, int32_t* presel,
                          int32_t* presel_count, void* workspace, size_t workspace_bytes,
                          kvs_stream_t stream) {
   Params P;
@@ -379,15 +380,19 @@ int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const i
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (n_presel < 1) return KVS_ERR_INVALID_ARG;
+  if (pool_kernel < 0 || pool_kernel > 127 || (pool_kernel > 0 && pool_kernel % 2 == 0))
+    return KVS_ERR_INVALID_ARG;
   if (batch > 65535) return KVS_ERR_UNSUPPORTED;
   if (!importance || !seq_lens || !presel || !presel_count) return KVS_ERR_INVALID_ARG;
+  if (!aligned(importance, 16)) return KVS_ERR_MISALIGNED;
   const size_t need = round_up((size_t)batch * P.G * max_blocks_per_seq * sizeof(float));
   if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
   float* bs = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  hipError_t e = kvs::launch_block_scores(P, importance, seq_lens, batch, max_blocks_per_seq, bs, s);
+  hipError_t e = kvs::launch_block_scores(P, importance, seq_lens, batch, max_blocks_per_seq, pool_kernel,
+                                         bs, s);
   if (e != hipSuccess) return hip_status(e, "kvs_preselect_blocks/scores");
   Params Q = P;
   Q.topk = n_presel;

@@ -28,8 +28,9 @@ size_t token_importance_ws_bytes(const Params& P, int batch, int max_blocks, int
 hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float* imp, const int32_t* table,
                                int max_blocks, const int32_t* seq_lens, int batch, void* rep_pool,
                                hipStream_t s);
+// pool_kernel 0: block sums; odd 1..127: best pooled vote per block.
 hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,
-                               int max_blocks, float* bs, hipStream_t s);
+                               int max_blocks, int pool_kernel, float* bs, hipStream_t s);
 hipError_t launch_presel_select(const Params& P, const float* scores, int max_blocks, const int32_t* seq_lens,
                                 const int32_t* presel, int n_presel, int batch, int32_t* sel,
                                 int32_t* sel_count, hipStream_t s);

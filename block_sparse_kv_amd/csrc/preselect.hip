@@ -4,6 +4,11 @@
 //  * block_score_kernel: a block's preselect score is the sum of its tokens' scores
 //    (kvs_token_importance), -inf outside the candidates -- the layout of the block scores, so the
 //    set is the ordinary top-k of these rows.
+//  * block_pool_score_kernel: the pooled form of the article's preselect pseudocode (§4.6
+//    preselect_block: pool1d over the window's votes, then the best tokens and their blocks).  A
+//    token's pooled vote is the mean of the Context votes in a centred window of pool_kernel
+//    tokens, zero outside the Context; taking tokens in descending pooled vote until enough
+//    distinct blocks are hit ranks each block by its best pooled token, which is the score stored.
 //  * The confined decode step scores every candidate as usual.  For sets of up to 256 blocks one
 //    workgroup per (sequence, group) ranks the set's current candidates by counting
 //    (presel_select_kernel).  For larger sets compact_kernel keeps, per
@@ -32,6 +37,47 @@ __global__ __launch_bounds__(256) void block_score_kernel(Params P, const float*
     s = -INFINITY;
   }
   if (lane == 0) bs[row * max_blocks + b] = s;
+}
+
+// One wave per (candidate block, group, sequence): the largest pooled vote among the block's 128
+// tokens, divided by pool_kernel.  The wave stages the votes of tokens b*128-64 .. b*128+191 (zero
+// outside the Context [cand_lo*128, cand_hi*128)) in LDS; lane l sums the windows of tokens l and
+// l+64 in ascending token order.  pool_kernel is odd and <= 127, so every window stays in the
+// staged span.
+__global__ __launch_bounds__(256) void block_pool_score_kernel(Params P, const float* __restrict__ imp,
+                                                               const int32_t* __restrict__ seq_lens,
+                                                               int max_blocks, int pool_kernel,
+                                                               float* __restrict__ bs) {
+  __shared__ float4 stage[4][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + w, gr = blockIdx.y, seq = blockIdx.z;
+  const Regions rg = regions_of(seq_lens[seq], P.initial_len, P.local_len);
+  const size_t row = (size_t)seq * P.G + gr;
+  const int lo = rg.cand_lo * kBlock, hi = rg.cand_hi * kBlock, n_tok = max_blocks * kBlock;
+  // votes of tokens p .. p+3, loaded from a clamped in-row position and masked to the Context
+  const int p = b * kBlock - 64 + 4 * lane;
+  const int pc = min(max(p, 0), n_tok - 4);
+  const float4 x = reinterpret_cast<const float4*>(imp + row * (size_t)n_tok)[pc >> 2];
+  float4 v;
+  v.x = (p >= lo && p < hi) ? x.x : 0.f;
+  v.y = (p + 1 >= lo && p + 1 < hi) ? x.y : 0.f;
+  v.z = (p + 2 >= lo && p + 2 < hi) ? x.z : 0.f;
+  v.w = (p + 3 >= lo && p + 3 < hi) ? x.w : 0.f;
+  stage[w][lane] = v;
+  __syncthreads();
+  const float* st = reinterpret_cast<const float*>(stage[w]);
+  const int h = pool_kernel >> 1;
+  float best = -INFINITY;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int i = lane + 64 * half;  // token b*128 + i sits at st[64 + i]
+    float acc = 0.f;
+    for (int u = 64 + i - h; u <= 64 + i + h; ++u) acc += st[u];
+    best = fmaxf(best, acc);
+  }
+  best = wave_max_f32(best);
+  if (lane == 0 && b < max_blocks)
+    bs[row * max_blocks + b] = (b >= rg.cand_lo && b < rg.cand_hi) ? best / (float)pool_kernel : -INFINITY;
 }
 
 // One wave per (group, sequence) row: the set's blocks that are current candidates, in order (a
@@ -154,9 +200,13 @@ hipError_t launch_presel_select(const Params& P, const float* scores, int max_bl
 }
 
 hipError_t launch_block_scores(const Params& P, const float* imp, const int32_t* seq_lens, int batch,
-                               int max_blocks, float* bs, hipStream_t s) {
-  hipLaunchKernelGGL(block_score_kernel, dim3((max_blocks + 3) / 4, P.G, batch), dim3(256), 0, s, P, imp,
-                     seq_lens, max_blocks, bs);
+                               int max_blocks, int pool_kernel, float* bs, hipStream_t s) {
+  const dim3 grid((max_blocks + 3) / 4, P.G, batch);
+  if (pool_kernel > 0)
+    hipLaunchKernelGGL(block_pool_score_kernel, grid, dim3(256), 0, s, P, imp, seq_lens, max_blocks,
+                       pool_kernel, bs);
+  else
+    hipLaunchKernelGGL(block_score_kernel, grid, dim3(256), 0, s, P, imp, seq_lens, max_blocks, bs);
   return hipGetLastError();
 }
 

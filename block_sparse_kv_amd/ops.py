@@ -61,13 +61,13 @@ def build_dynamic_reps(cfg, k_pool, importance, block_table, seq_lens, rep_pool)
     return rep_pool
 
 
-def preselect_blocks(cfg, importance, seq_lens, n_presel, max_blocks):
+def preselect_blocks(cfg, importance, seq_lens, n_presel, max_blocks, pool_kernel=0):
     batch = seq_lens.shape[0]
     presel = torch.empty((batch, cfg.groups, n_presel), dtype=torch.int32, device=importance.device)
     cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=importance.device)
     ws = workspace(B.kvs_preselect_workspace_size(cfg, batch, max_blocks), importance.device)
-    B.kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks, n_presel, presel, cnt, ws,
-                           ws.numel())
+    B.kvs_preselect_blocks(cfg, importance, seq_lens, batch, max_blocks, n_presel, pool_kernel, presel,
+                           cnt, ws, ws.numel())
     return presel, cnt
 
 

@@ -192,14 +192,22 @@ size_t kvs_preselect_workspace_size(const kvs_config* cfg, int32_t batch, int32_
 
 /*
  * kvs_preselect_blocks -- the preselected set [KT-LC §4.4 Preselect, after SnapKV; §4.5
- * preselect_block_count]: before decoding, the blocks the question's tokens attend most.  Per
- * (sequence, group): a candidate block's preselect score is the sum of its 128 token scores in
- * importance (kvs_token_importance; same groups); the min(n_presel, candidates) best blocks, ties to
- * the lower block, are written ascending to presel [batch][G][n_presel], -1 padded, with their number
- * in presel_count [batch][G].  workspace: >= kvs_preselect_workspace_size bytes, 256-byte aligned.
+ * preselect_block_count; §4.6 preselect_block]: before decoding, the blocks the question's tokens
+ * attend most.  Per (sequence, group), each candidate block gets a preselect score from importance
+ * (kvs_token_importance; same groups; 16-byte aligned):
+ *   pool_kernel == 0: the sum of its 128 token scores;
+ *   pool_kernel odd, 1..127: its largest pooled vote, a token's pooled vote being the mean of the
+ *     Context token scores in the window of pool_kernel tokens centred on it (tokens outside the
+ *     Context count as zero; the divisor is always pool_kernel).  Ranking blocks so is the same as
+ *     taking tokens in descending pooled vote until n_presel distinct blocks are hit.
+ * The min(n_presel, candidates) best blocks, ties to the lower block, are written ascending to
+ * presel [batch][G][n_presel], -1 padded, with their number in presel_count [batch][G].
+ * workspace: >= kvs_preselect_workspace_size bytes, 256-byte aligned.  Any other pool_kernel:
+ * KVS_ERR_INVALID_ARG.
  */
 int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const int32_t* seq_lens,
-                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel, int32_t* presel,
+                         int32_t batch, int32_t max_blocks_per_seq, int32_t n_presel,
+                         int32_t pool_kernel, int32_t* presel,
                          int32_t* presel_count, void* workspace, size_t workspace_bytes,
                          kvs_stream_t stream);
 

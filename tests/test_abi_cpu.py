@@ -150,10 +150,13 @@ def test_preselect_errors():
     E = B.KVS_ERR_INVALID_ARG
     need = kvs.kvs_preselect_workspace_size(c, 2, 100)
     assert need >= 2 * 8 * 100 * 4 and need % 256 == 0
-    pre = lambda n, ws, wb, imp=A: kvs.kvs_preselect_blocks(c, imp, A, 2, 100, n, A, A, ws, wb, stream=0,
-                                                         check=False)
+    pre = lambda n, ws, wb, imp=A, pk=0: kvs.kvs_preselect_blocks(c, imp, A, 2, 100, n, pk, A, A, ws, wb,
+                                                               stream=0, check=False)
     assert pre(0, A, need) == E
     assert pre(8, A, need, imp=Z) == E
+    for pk in (-1, 2, 8, 128, 129):
+        assert pre(8, A, need, pk=pk) == E
+    assert pre(8, A, need, imp=A + 4, pk=5) == B.KVS_ERR_MISALIGNED
     assert pre(8, A, need - 256) == B.KVS_ERR_WORKSPACE
     assert pre(8, A + 16, need) == B.KVS_ERR_MISALIGNED
     need2 = kvs.kvs_decode_step_preselected_workspace_size(c, 2, 100, 32)

@@ -45,32 +45,36 @@ def build_reps(case):
 
 
 PRE_CASES = [
-    # (Hq, Hkv, mode, rep, n_obs, n_presel, lens)
-    (32, 8, "shared", "max", 16, 20, [6000, 9000]),
-    (8, 2, "separate", "quest", 8, 12, [5000]),
-    (16, 4, "separate", "mean", 4, 200, [3000]),      # n_presel > n_cand: every candidate
-    (16, 2, "shared", "quest", 8, 64, [280000]),      # long rows
+    # (Hq, Hkv, mode, rep, n_obs, n_presel, lens, pool_kernel): 0 ranks block sums, an odd kernel
+    # the blocks' best pooled votes
+    (32, 8, "shared", "max", 16, 20, [6000, 9000], 0),
+    (8, 2, "separate", "quest", 8, 12, [5000], 0),
+    (16, 4, "separate", "mean", 4, 200, [3000], 0),      # n_presel > n_cand: every candidate
+    (16, 2, "shared", "quest", 8, 64, [280000], 0),      # long rows
+    (32, 8, "shared", "max", 16, 20, [6000, 9000], 7),
+    (8, 2, "separate", "quest", 8, 12, [5000, 700], 1),  # 700: no candidates
+    (16, 4, "separate", "mean", 4, 30, [3000], 127),     # the widest window
+    (16, 2, "shared", "quest", 8, 64, [140000], 5),      # long rows
 ]
 
 
 @pytest.mark.parametrize("idx", range(len(PRE_CASES)))
 def test_preselect_blocks(idx):
-    Hq, Hkv, mode, rep, n_obs, n_presel, lens = PRE_CASES[idx]
-    say(f"[case] preselect {Hq}x{Hkv} {mode} n_obs={n_obs} n_presel={n_presel} lens={lens}")
+    Hq, Hkv, mode, rep, n_obs, n_presel, lens, pk = PRE_CASES[idx]
+    say(f"[case] preselect {Hq}x{Hkv} {mode} n_obs={n_obs} n_presel={n_presel} lens={lens} pool={pk}")
     c = kvs.Config(num_q_heads=Hq, num_kv_heads=Hkv, initial_len=128, local_len=1024, topk=8,
                    rep_method=rep, head_select_mode=mode)
     case = Case(c, lens, seed=kvsynth.mix_seed(601, idx), n_hot=3)
     pb = case.pb
     q_obs = kvsynth.randn_fp16((len(lens), n_obs, Hq, 128), kvsynth.mix_seed(602, idx), DEV)
     imp = ops.token_importance(c, q_obs, case.k_pool, pb.block_table, pb.seq_lens)
-    presel, pcnt = ops.preselect_blocks(c, imp, pb.seq_lens, n_presel, pb.max_blocks)
+    presel, pcnt = ops.preselect_blocks(c, imp, pb.seq_lens, n_presel, pb.max_blocks, pk)
     torch.cuda.synchronize()
     for i, L in enumerate(lens):
         ref_imp = orc.token_importance(q_obs[i].cpu().numpy(), case.host[i][1], mode)
-        _, _, cand = orc.regions(L, B, c.initial_len, c.local_len)
+        rows, cand = orc.preselect_scores(ref_imp, L, B, c.initial_len, c.local_len, pk)
         for gi in range(c.groups):
-            bs = [ref_imp[gi, b * B:(b + 1) * B].sum() for b in cand]
-            check_selection(presel[i, gi].cpu().numpy(), pcnt[i, gi].item(), bs, cand, n_presel,
+            check_selection(presel[i, gi].cpu().numpy(), pcnt[i, gi].item(), rows[gi], cand, n_presel,
                             f"preselect seq {i} grp {gi}")
 
 
