@@ -68,6 +68,12 @@ Readings taken where the pages are silent (each is the spec here):
       token's row, m = the value of largest magnitude (the first one on ties), d = m / -8,
       codes q = min(15, trunc(x * (1/d) + 8.5)) in 0..15, all fp32; d stored as fp16; the cached
       value is fp16(d) * (q - 8).  An all-zero block has d = 0 and codes 8.
+  R27 kv_type INT8 per token and head (the int8 cache with one dynamic scale per token and head
+      that the vLLM page lists beside Q8_0-style block formats; it names the granularity and the fp32
+      scale, not the arithmetic, which is read as Q8_0's): per token's K or V row of one KV head,
+      s = max|x| / 127 in fp32, stored as fp32; codes round(x * (1/s)), ties away from zero, all
+      fp32 operations; an all-zero row has s = 0 and codes 0.  The cached value is the fp32
+      product s * code.
   R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
       of one token's key or value row is a block with scale d = max|x| / 127 and codes
       q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
@@ -302,6 +308,27 @@ def dequantize_q8_0(codes, scales):
     return (cg * sc[..., None]).reshape(*lead, d)
 
 
+def quantize_int8_pth(x):
+    """Codes (int8 [..., d]) and fp32 scales ([...]) of x [..., d], one scale per row (reading
+    R27).  The scale, its reciprocal and the scaled values are fp32 operations; codes round ties
+    away from zero."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)                                   # fp32, exact
+    s = (amax / np.float32(127.0)).astype(np.float32)               # fp32 division
+    with np.errstate(divide="ignore"):
+        inv = np.where(s != 0, np.float32(1.0) / np.where(s != 0, s, 1), np.float32(0.0)).astype(np.float32)
+    v = (x * inv[..., None]).astype(np.float32).astype(np.float64)  # fp32 product
+    codes = (np.sign(v) * np.floor(np.abs(v) + 0.5)).astype(np.int8)
+    return codes, s
+
+
+def dequantize_int8_pth(codes, scales):
+    """The cached values fp32(s * q) as float64 [..., d] (reading R27)."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.float32)
+    sc = np.asarray(scales, dtype=np.float32)
+    return (c * sc[..., None]).astype(np.float32).astype(np.float64)
+
+
 def quantize_q4_0(x):
     """Codes (uint8 0..15) and fp16 scales of x [..., d] in the Q4_0 format (reading R25)."""
     x = np.asarray(x, dtype=np.float32)
@@ -329,7 +356,7 @@ def dequantize_q4_0(codes, scales):
 
 
 def stored_reps(reps, method: str):
-    """Reps as the rep pool holds them when they are not copies of fp16 keys (a Q8_0 cache): fp16
+    """Reps as the rep pool holds them when they are not copies of fp16 keys (a quantized cache): fp16
     with round-to-nearest-even, Mean fp32 (reading R22)."""
     reps = np.asarray(reps, dtype=np.float64)
     if method == MEAN:

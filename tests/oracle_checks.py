@@ -6,7 +6,8 @@ copy) and raises AssertionError on failure.  What each one rests on:
   * torch's scaled_dot_product_attention in float64 (a library routine sharing no code with the oracle);
   * closed forms and identities of the definitions (Mean linearity, Fix = rows of K, SHARED = sum
     of SEPARATE, softmax shift invariance, q = 0 gives the mean of V);
-  * hand-worked cases in tests/golden/hand_worked.json, q8_0_worked.json and q4_0_worked.json;
+  * hand-worked cases in tests/golden/hand_worked.json, q8_0_worked.json, q4_0_worked.json and
+    int8_pth_worked.json;
   * the rounding bound, code range and block width of the Q8_0 format;
   * planted-block recall of the selection.
 """
@@ -344,6 +345,49 @@ def check_q8_integer_rows_exact(orc):
     assert np.array_equal(orc.dequantize_q8_0(codes, sc), x.astype(np.float64))
 
 
+GOLDEN_I8 = os.path.join(os.path.dirname(__file__), "golden", "int8_pth_worked.json")
+
+
+def check_int8_pth_golden(orc):
+    """The hand-worked rows of tests/golden/int8_pth_worked.json: fp32 scale, codes, cached values."""
+    with open(GOLDEN_I8) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.zeros(128, dtype=np.float32)
+        for k, v in c["x_nonzero"].items():
+            x[int(k)] = v
+        codes, s = orc.quantize_int8_pth(x[None])
+        assert s.dtype == np.float32 and float(s[0]) == c["s"], (c["why"], float(s[0]))
+        want = np.zeros(128, dtype=np.int64)
+        for k, v in c["codes_nonzero"].items():
+            want[int(k)] = v
+        assert np.array_equal(codes[0].astype(np.int64), want), c["why"]
+        deq = np.zeros(128)
+        for k, v in c["deq_nonzero"].items():
+            deq[int(k)] = v
+        assert np.array_equal(orc.dequantize_int8_pth(codes, s)[0], deq), c["why"]
+
+
+def check_int8_pth_bound_and_range(orc):
+    """On random fp16 rows: codes in [-127, 127], each row's largest |x| takes +-127, the cached
+    value is within s/2 (plus fp32 rounding) of x; integer rows holding +-127 are their own codes."""
+    g = np.random.default_rng(27)
+    x = kvsynth.randn_fp16((16, 4, 128), 27).numpy().astype(np.float32) * np.float32(3.0)
+    x = x.astype(np.float16).astype(np.float32)
+    codes, s = orc.quantize_int8_pth(x)
+    assert codes.shape == x.shape and s.shape == x.shape[:-1]
+    assert np.abs(codes.astype(np.int64)).max() <= 127
+    top = np.take_along_axis(codes, np.abs(x).argmax(axis=-1)[..., None], -1)[..., 0]
+    assert np.all(np.abs(top.astype(np.int64)) == 127)
+    err = np.abs(orc.dequantize_int8_pth(codes, s) - x.astype(np.float64))
+    bound = s.astype(np.float64)[..., None] * (0.5 + 1e-6) + np.abs(x) * 2.0 ** -23
+    assert np.all(err <= bound)
+    xi = g.integers(-127, 128, (8, 128)).astype(np.float32)
+    xi[:, 17] = -127.0
+    ci, si = orc.quantize_int8_pth(xi)
+    assert np.all(si == 1.0) and np.array_equal(ci.astype(np.float32), xi)
+
+
 GOLDEN_Q4 = os.path.join(os.path.dirname(__file__), "golden", "q4_0_worked.json")
 
 
@@ -552,5 +596,6 @@ ALL_CHECKS = [
     check_softmax_identities, check_q8_golden, check_q8_error_bound_and_range,
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
     check_dynamic_reps_closed_forms, check_preselect_identities, check_q4_golden,
-    check_q4_range_and_bound, check_preselect_pooled,
+    check_q4_range_and_bound, check_preselect_pooled, check_int8_pth_golden,
+    check_int8_pth_bound_and_range,
 ]

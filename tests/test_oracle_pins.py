@@ -175,6 +175,36 @@ def _presel_max_not_sum(imp, L, B, initial_len, local_len, n_presel):
             for row in np.asarray(imp, np.float64)]
 
 
+def _i8_generic(x, even=False, div=127.0, group=128, half_scale=False):
+    x = np.asarray(x, dtype=np.float32)
+    *lead, d = x.shape
+    xg = x.reshape(*lead, d // group, group)
+    s = (np.abs(xg).max(axis=-1) / np.float32(div)).astype(np.float32)
+    if half_scale:
+        s = s.astype(np.float16).astype(np.float32)
+    inv = np.where(s != 0, np.float32(1) / np.where(s != 0, s, 1), 0).astype(np.float32)
+    v = (xg * inv[..., None]).astype(np.float32).astype(np.float64)
+    q = np.round(v) if even else np.sign(v) * np.floor(np.abs(v) + 0.5)
+    codes = q.astype(np.int8).reshape(*lead, d)
+    return codes, (s[..., 0] if group == 128 else s.max(axis=-1))
+
+
+def _i8_round_even(x):
+    return _i8_generic(x, even=True)
+
+
+def _i8_div_128(x):
+    return _i8_generic(x, div=128.0)
+
+
+def _i8_block_32(x):
+    return _i8_generic(x, group=32)
+
+
+def _i8_fp16_scale(x):
+    return _i8_generic(x, half_scale=True)
+
+
 _orig_preselect = orc.preselect_blocks
 
 
@@ -265,6 +295,10 @@ MUTANTS = [
     ("preselect_blocks", _presel_pooled_variant("in_block")),
     ("preselect_blocks", _presel_pooled_variant("full_row")),
     ("preselect_blocks", _presel_pooled_variant("sum")),
+    ("quantize_int8_pth", _i8_round_even),
+    ("quantize_int8_pth", _i8_div_128),
+    ("quantize_int8_pth", _i8_block_32),
+    ("quantize_int8_pth", _i8_fp16_scale),
 ]
 
 
