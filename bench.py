@@ -80,6 +80,9 @@ WORKLOADS = {
                         layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="q4_0"),
     "1m-q4": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
                   layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003, kv="q4_0"),
+    # and over an INT8 cache with one fp32 scale per token and KV head
+    "128k-max-i8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                        layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="int8_pth"),
 }
 
 
@@ -142,7 +145,7 @@ def required_bytes(w):
     R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1), "dynamic": w.get("rep_num", 1)}[w["rep"]]
     rep_elem = 4 if w["rep"] == "mean" else 2
     # bytes of one token's K (or V) row: fp16, or codes + one fp16 scale per 32 channels
-    row = {"q8_0": D + (D // 32) * 2, "q4_0": D // 2 + (D // 32) * 2}.get(w.get("kv"), D * 2)
+    row = {"q8_0": D + (D // 32) * 2, "q4_0": D // 2 + (D // 32) * 2, "int8_pth": D + 4}.get(w.get("kv"), D * 2)
     return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * row * 2,
                 out=Hq * D * 4, tokens=T, ncand=ncand, k_eff=k_eff)
 
@@ -175,7 +178,7 @@ class Setup:
             q, kp, vp, hot = kvsynth.pool_layer(kvsynth.mix_seed(w["seed"], u), L, w["Hq"], w["Hkv"],
                                                 hot_range=(lo, hi), n_hot=w["n_hot"],
                                                 hot_per_head=w["hot_per_head"], device=device)
-            if w.get("kv") in ("q8_0", "q4_0"):  # quantized by the library; the fp16 tiles are dropped
+            if w.get("kv", "fp16") != "fp16":  # quantized by the library; the fp16 tiles are dropped
                 ids = torch.arange(nb, dtype=torch.int32)
                 kp = ops.quantize_kv(self.cfg, kp, ids, ops.alloc_q8_pool(self.cfg, nb, device))
                 vp = ops.quantize_kv(self.cfg, vp, ids, ops.alloc_q8_pool(self.cfg, nb, device))

@@ -27,6 +27,9 @@
 namespace kvs {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline f32x4_t ld_stream16f(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+}
 
 constexpr int kVRow = 288;                      // bytes per staged V token row (256 + 32 bank skew)
 constexpr int kVChunk = 4 * kVRow;              // 4 token rows
@@ -83,7 +86,35 @@ __device__ inline uint4 q4_dq8(uint32_t w, uint32_t sc) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// KV: the pools' KvType (fp16 tiles, Q8_0 or Q4_0 records).
+// 8 INT8 codes (w0 then w1, lowest byte first) as 8 fp16 values, exactly: the biased byte under the
+// exponent pattern 0x64 is 1024 + (c + 128), and subtracting 1152 leaves c.
+__device__ inline uint4 i8_codes8(uint32_t w0, uint32_t w1) {
+  const half2v_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = (j < 2 ? w0 : w1) ^ 0x80808080u;
+    const uint32_t sel = (j & 1) ? 0x04030402u : 0x04010400u;
+    o[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v_t, __builtin_amdgcn_perm(0x64646464u, u, sel)) - bias);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// 8 INT8 codes times the token's fp32 scale s, as 8 fp16 values fp16(fp32(s * code)).
+__device__ inline uint4 i8_dq8(uint32_t w0, uint32_t w1, float s) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = (j < 2 ? w0 : w1) ^ 0x80808080u;
+    const int b = 16 * (j & 1);
+    const float a = (float)((w >> b) & 0xFFu) - 128.0f;  // exact
+    const float c = (float)((w >> (b + 8)) & 0xFFu) - 128.0f;
+    const half2v_t hv = {(_Float16)(a * s), (_Float16)(c * s)};
+    o[j] = __builtin_bit_cast(uint32_t, hv);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0 or per-token INT8 records).
 template <int G, int KV = kKvFp16>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
@@ -98,8 +129,10 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   // zeroed after the load (a NaN tail times p = 0 would not be 0).
   half8_t qb[4];  // Q^T B operand: lane l holds head lc, 8 channels per MFMA m (below)
   uint4 kr[2][4], vr[8];
-  uint4 vc[4];    // Q8_0 / Q4_0: V codes and scales, dequantized when V is staged
+  uint4 vc[4];    // Q8_0 / Q4_0 / INT8: V codes and scales, dequantized when V is staged
   uint32_t vs[4];
+  float ksc[2];    // INT8: the fp32 scale of the lane's K token 32w + 16g + lc
+  f32x4_t vsc;     // INT8: the fp32 scales of the lane's 4 V tokens
   if constexpr (KV == kKvFp16) {
     // fp16 tile: K rows of MFMA m are channels 32m + 8*lq .. +8
     const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
@@ -150,6 +183,44 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       kr[g][1] = q4_dq8(kc[g].y, ks[g]);
       kr[g][2] = q4_dq8(kc[g].z, ks[g]);
       kr[g][3] = q4_dq8(kc[g].w, ks[g]);
+    }
+  } else if constexpr (KV == kKvI8) {
+    // INT8 record, one fp32 scale per token: K codes load as for Q8_0 below and enter the product
+    // as exact fp16 integers; the product is scaled per token row afterwards, S = s_t * (code_t . q),
+    // which keeps the scale in fp32 (a lane loads its own K token's scale; the S rows' scales come
+    // from the lanes holding those tokens).  V: lane l takes channels 16*(l%8) .. +16 of the wave's four
+    // consecutive tokens 4*(l/8) .. +3, so their scales are one 16-byte load; scaled when staged.
+    const size_t rec = ((size_t)phys * P.Hkv + h) * kI8Record;
+    const unsigned char* Kq = reinterpret_cast<const unsigned char*>(k_pool) + rec;
+    const unsigned char* Vq = reinterpret_cast<const unsigned char*>(v_pool) + rec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
+      qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
+    }
+    uint4 kc[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+      kc[g][0] = ld_stream16(Kq + tok * kDim + 32 * lq);
+      kc[g][1] = ld_stream16(Kq + tok * kDim + 32 * lq + 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * w + 4 * (lane >> 3) + i;
+      vc[i] = ld_stream16(Vq + tok * kDim + 16 * (lane & 7));
+    }
+    // the scales last: they are needed after the codes (S scaling, V staging)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) ksc[g] = *reinterpret_cast<const float*>(Kq + kQ8Codes + (32 * w + 16 * g + lc) * 4);
+    vsc = ld_stream16f(Vq + kQ8Codes + (32 * w + 4 * (lane >> 3)) * 4);
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the arithmetic below
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kr[g][0] = i8_codes8(kc[g][0].x, kc[g][0].y);
+      kr[g][1] = i8_codes8(kc[g][0].z, kc[g][0].w);
+      kr[g][2] = i8_codes8(kc[g][1].x, kc[g][1].y);
+      kr[g][3] = i8_codes8(kc[g][1].z, kc[g][1].w);
     }
   } else {
     // Q8_0 record (kv_type; llama.cpp's block format): a lane's K codes are the 32 channels
@@ -205,6 +276,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = 32 * w + 16 * g + 4 * lq + i;
+      if constexpr (KV == kKvI8) S[g][i] *= __shfl(ksc[g], 4 * lq + i, 64);  // token 4lq + i's scale
       S[g][i] = tok < ntok ? S[g][i] * sl2 : -INFINITY;
       mx = fmaxf(mx, S[g][i]);
     }
@@ -236,12 +308,20 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       for (int u = 0; u < 4; ++u)
         *reinterpret_cast<uint4*>(row + 16 * u) = in ? q4_dq8(cw[u], vs[i]) : make_uint4(0, 0, 0, 0);
     }
-  } else if constexpr (KV == kKvQ8) {
+  } else if constexpr (KV == kKvQ8 || KV == kKvI8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 8 * i + (lane >> 3);  // the wave's token: chunk t / 4, row t % 4
+      // the wave's token: chunk t / 4, row t % 4
+      const int t = KV == kKvI8 ? 4 * (lane >> 3) + i : 8 * i + (lane >> 3);
       const bool in = 32 * w + t < ntok;
-      const uint4 a = q8_dq8(vc[i].x, vc[i].y, vs[i]), b = q8_dq8(vc[i].z, vc[i].w, vs[i]);
+      uint4 a, b;
+      if constexpr (KV == kKvI8) {
+        a = i8_dq8(vc[i].x, vc[i].y, vsc[i]);
+        b = i8_dq8(vc[i].z, vc[i].w, vsc[i]);
+      } else {
+        a = q8_dq8(vc[i].x, vc[i].y, vs[i]);
+        b = q8_dq8(vc[i].z, vc[i].w, vs[i]);
+      }
       unsigned char* row = vbuf + (t >> 2) * kVChunk + (t & 3) * kVRow + 32 * (lane & 7);
       *reinterpret_cast<uint4*>(row) = in ? a : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(row + 16) = in ? b : make_uint4(0, 0, 0, 0);

@@ -45,7 +45,8 @@ int make_params(const kvs_config* c, Params* P) {
   if (c->head_select_mode != KVS_HEADS_SEPARATE && c->head_select_mode != KVS_HEADS_SHARED)
     return KVS_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
-  if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0 && c->kv_type != KVS_KV_Q4_0)
+  if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0 && c->kv_type != KVS_KV_Q4_0 &&
+      c->kv_type != KVS_KV_INT8_PTH)
     return KVS_ERR_INVALID_ARG;
   const int R = rep_count_of(c);
   if (R < 0) return KVS_ERR_INVALID_ARG;
@@ -182,8 +183,10 @@ size_t kvs_rep_bytes_per_block(const kvs_config* cfg) {
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg) {
   Params P;
   if (make_params(cfg, &P) != KVS_OK) return 0;
-  const size_t rec = P.kv == kvs::kKvQ8 ? (size_t)kvs::kQ8Record
-                     : P.kv == kvs::kKvQ4 ? (size_t)kvs::kQ4Record : (size_t)kvs::kTile * 2;
+  const size_t rec = P.kv == kvs::kKvQ8   ? (size_t)kvs::kQ8Record
+                     : P.kv == kvs::kKvQ4 ? (size_t)kvs::kQ4Record
+                     : P.kv == kvs::kKvI8 ? (size_t)kvs::kI8Record
+                                          : (size_t)kvs::kTile * 2;
   return (size_t)P.Hkv * rec;
 }
 

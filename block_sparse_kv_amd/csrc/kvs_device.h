@@ -19,10 +19,12 @@ constexpr int kQ8Record = kQ8Codes + kBlock * (kDim / kQ8Group) * 2;  // 17408 b
 // [128][4] as for Q8_0.
 constexpr int kQ4Codes = kBlock * kDim / 2;                            // bytes of codes
 constexpr int kQ4Record = kQ4Codes + kBlock * (kDim / kQ8Group) * 2;  // 9216 bytes
+// INT8 with one fp32 scale per token row: codes as Q8_0's, then 128 fp32 scales
+constexpr int kI8Record = kQ8Codes + kBlock * 4;                       // 16896 bytes
 
 enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3, kDynamic = 4 };  // Dynamic: scored like Fix
 enum Mode { kSeparate = 0, kShared = 1 };
-enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2 };
+enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2, kKvI8 = 3 };
 
 // Launch-time constants of one call (passed by value to every kernel).
 struct Params {

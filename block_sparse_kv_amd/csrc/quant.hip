@@ -129,9 +129,60 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
   *reinterpret_cast<uint32_t*>(rec + kQ4Codes + tok * 8 + 4 * half) = sw;
 }
 
+// INT8 with one scale per token and KV head (the per-token-head int8 cache): s = max|x| / 127 over the
+// token's 128 channels, kept in fp32, codes round(x * (1/s)), ties away from zero, as for Q8_0.  Same
+// lane mapping; the two lanes of a token combine their maxima with one lane exchange.
+__global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ ids, int Hkv,
+                                                          unsigned char* __restrict__ dst) {
+#pragma clang fp contract(off)
+  const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
+  const size_t tile = (size_t)ids[i] * Hkv + h;
+  const int tok = t >> 1, half = t & 1;
+  const uint4* in = reinterpret_cast<const uint4*>(src + tile * kTile + tok * kDim + 64 * half);
+  uint4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) raw[u] = in[u];
+  float x[64];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * u + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xFFFFu));
+      x[8 * u + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the token's other half
+  const float sc = amax / 127.0f;
+  const float inv = sc != 0.f ? 1.0f / sc : 0.f;
+  uint32_t codes[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p = x[4 * e + k] * inv;
+      word |= (uint32_t)((int)roundf(p) & 0xFF) << (8 * k);
+    }
+    codes[e] = word;
+  }
+  unsigned char* rec = dst + tile * kI8Record;
+  uint4* co = reinterpret_cast<uint4*>(rec + tok * kDim + 64 * half);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) co[u] = make_uint4(codes[4 * u], codes[4 * u + 1], codes[4 * u + 2], codes[4 * u + 3]);
+  if (half == 0) *reinterpret_cast<float*>(rec + kQ8Codes + tok * 4) = sc;
+}
+
 hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
                               hipStream_t s) {
-  if (P.kv == kKvQ4)
+  if (P.kv == kKvI8)
+    hipLaunchKernelGGL(quantize_i8_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
+  else if (P.kv == kKvQ4)
     hipLaunchKernelGGL(quantize_q4_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
                        static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
   else

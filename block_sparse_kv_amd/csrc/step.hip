@@ -83,6 +83,7 @@ static void launch_ss_m(const AttnArgs& A, dim3 grid, hipStream_t s, const void*
                         int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
   if (A.P.kv == kKvQ8) launch_ss_mq<G, METHOD, kKvQ8>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
   else if (A.P.kv == kKvQ4) launch_ss_mq<G, METHOD, kKvQ4>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+  else if (A.P.kv == kKvI8) launch_ss_mq<G, METHOD, kKvI8>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
   else launch_ss_mq<G, METHOD, kKvFp16>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
 }
 
@@ -165,6 +166,9 @@ static hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, in
                        tiles, n_topk, n_il_total);                                                  \
   else if (A.P.kv == kKvQ4)                                                                          \
     hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvQ4>), grid, block, 0, s, A, scores, sel, sel_count, \
+                       tiles, n_topk, n_il_total);                                                  \
+  else if (A.P.kv == kKvI8)                                                                          \
+    hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvI8>), grid, block, 0, s, A, scores, sel, sel_count, \
                        tiles, n_topk, n_il_total);                                                  \
   else                                                                                               \
     hipLaunchKernelGGL((topk_il_wide_kernel<GG, kKvFp16>), grid, block, 0, s, A, scores, sel, sel_count, \

@@ -34,6 +34,8 @@
  *                kv_type Q4_0: [n_phys][Hkv] records of 9216 bytes: codes [128 tokens][64 bytes], word k
  *                of a row holding channels 8k..8k+7 (channel 8k+2i in bits 4i..4i+3, 8k+2i+1 in bits
  *                16+4i..19+4i), then fp16 scales [128 tokens][4]; value scale * (code - 8)
+ *                kv_type INT8_PTH: [n_phys][Hkv] records of 16896 bytes: int8 codes [128 tokens][128],
+ *                then fp32 scales [128 tokens]; value fp32(scale[t] * code[t][c])
  *   rep_pool     [n_phys][Hkv][R][128]  fp16, except fp32 for KVS_REP_MEAN.
  *                R = 2 for Quest (r=0 channel-wise min key, r=1 channel-wise max key), 1 for Max
  *                and Mean, rep_num for Fix (r-th rep = token r*(128/rep_num) of the block).
@@ -89,8 +91,11 @@ typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mo
  * in blocks of 32 channels with an fp16 scale:
  *   Q8_0: d = max|x| / 127, int8 codes round(x / d) ties away from zero, value d * code;
  *   Q4_0: m = the first value of largest magnitude, d = m / -8, codes min(15, trunc(x / d + 8.5)) in
- *         0..15, value d * (code - 8). */
-typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2 } kvs_kv_type;
+ *         0..15, value d * (code - 8).
+ * INT8_PTH is the int8 cache with one dynamic scale per token and head that the vLLM serving page
+ * lists (its per-token-head cache modes), with Q8_0's arithmetic over a whole 128-channel row:
+ *   s = max|x| / 127 kept in fp32, codes round(x / s) ties away from zero, value fp32(s * code). */
+typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2, KVS_KV_INT8_PTH = 3 } kvs_kv_type;
 
 /* Host struct.  Field order and types are part of the ABI. */
 typedef struct kvs_config {
@@ -133,8 +138,9 @@ size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
  * dst_pool (laid out as a pool of cfg->kv_type).  Per 32 channels of a token, in fp32 with IEEE
  * division: Q8_0 d = max|x| / 127, codes round(x * (1/d)) ties away from zero (an all-zero block:
  * d = 0, codes 0); Q4_0 d = m / -8 for m the first value of largest magnitude (+0 for an all-zero
- * block), codes min(15, trunc(x * (1/d) + 8.5)) (all-zero: 8).  d is stored rounded to fp16.  Used
- * for keys and values alike.  cfg->kv_type must be Q8_0 or Q4_0.
+ * block), codes min(15, trunc(x * (1/d) + 8.5)) (all-zero: 8).  d is stored rounded to fp16.
+ * INT8_PTH: per token, s = max|x| / 127 over its 128 channels, codes as Q8_0's, s stored as fp32.
+ * Used for keys and values alike.  cfg->kv_type must be Q8_0, Q4_0 or INT8_PTH.
  * n_blocks == 0 is a no-op.  Both pools 16-byte aligned.
  */
 int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,
@@ -148,8 +154,8 @@ int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* 
  *   Mean:  channel-wise mean in fp32;             Fix: rows 0, s, 2s, ... with s = 128/rep_num.
  * Every listed block must be full (128 valid tokens).  n_blocks == 0 is a no-op.  Dynamic reps come
  * from kvs_build_dynamic_reps instead (KVS_ERR_INVALID_ARG here).
- * With kv_type Q8_0 / Q4_0 the reps are taken over the cached values (exact in fp32) and stored
- * rounded to fp16 (Mean: fp32).
+ * With a quantized kv_type the reps are taken over the cached values (fp32) and stored rounded to
+ * fp16 (Mean: fp32).
  */
 int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phys_block_ids,
                    int32_t n_blocks, void* rep_pool, kvs_stream_t stream);

@@ -127,6 +127,24 @@ SMALL_Q4 = [
 ]
 
 
+# INT8 caches with one fp32 scale per token and KV head
+SMALL_I8 = [
+    (32, 8, 128, 512, 12, "quest", "separate", 1, [5000, 129, 1, 7777]),
+    (32, 8, 100, 300, 5, "max", "shared", 1, [4000, 3001]),
+    (16, 16, 0, 0, 7, "fix", "separate", 8, [3000, 2048]),
+    (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_I8)),
+                         ids=[f"i8-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_I8])
+def test_small_cases_int8_pth(idx):
+    Hq, Hkv, I, W, k, rep, mode, rn, lens = SMALL_I8[idx]
+    c = cfg_of(Hq, Hkv, I, W, k, rep, mode, rn, kv="int8_pth")
+    case = Case(c, lens, seed=kvsynth.mix_seed(79, idx), n_hot=3)
+    run_full_check(case, f"small int8_pth {rep}/{mode} {Hq}x{Hkv}")
+
+
 @pytest.mark.parametrize("idx", range(len(SMALL_Q4)),
                          ids=[f"q4-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_Q4])
 def test_small_cases_q4(idx):
@@ -281,6 +299,12 @@ def test_full_128k_shared_q8():
     c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="q8_0")
     case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
     run_full_check(case, "full 128K 32/8 max SHARED k96, Q8_0 cache")
+
+
+def test_full_128k_shared_int8_pth():
+    c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="int8_pth")
+    case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
+    run_full_check(case, "full 128K 32/8 max SHARED k96, INT8 per-token-head cache")
 
 
 def test_full_mixed_batch_fix():

@@ -146,6 +146,60 @@ def test_quantize_q4_bit_exact(Hkv):
             assert np.all(dst[p].cpu().numpy() == 0xAB), p
 
 
+def split_i8(pool_i8):
+    """[n][Hkv][16896] bytes -> codes int8 [n][Hkv][128][128], scales fp32 [n][Hkv][128]."""
+    a = pool_i8.cpu().numpy()
+    codes = a[..., : 128 * 128].view(np.int8).reshape(*a.shape[:2], 128, 128)
+    scales = a[..., 128 * 128:].copy().view(np.float32).reshape(*a.shape[:2], 128)
+    return codes, scales
+
+
+@pytest.mark.parametrize("Hkv", [1, 8])
+def test_quantize_int8_pth_bit_exact(Hkv):
+    say(f"[case] int8 per-token-head quantize Hkv={Hkv}")
+    n_phys = 7
+    c = q8_cfg(Hkv=Hkv, g=1, kv_type="int8_pth")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(421, Hkv))
+    src[2, 0, 9, :] = 0.0  # an all-zero row
+    dst = ops.alloc_q8_pool(c, n_phys, DEV)
+    assert dst.shape[-1] == 16896
+    dst.fill_(0xAB)
+    ids = torch.tensor([5, 0, 2, 6], dtype=torch.int32)
+    ops.quantize_kv(c, src, ids, dst)
+    torch.cuda.synchronize()
+    got_c, got_s = split_i8(dst)
+    want_c, want_s = orc.quantize_int8_pth(src.float().cpu().numpy())
+    for p in range(n_phys):
+        if p in ids.tolist():
+            assert np.array_equal(got_c[p], want_c[p]), (p, np.argwhere(got_c[p] != want_c[p])[:4])
+            assert np.array_equal(got_s[p].view(np.uint32), want_s[p].view(np.uint32)), p
+        else:
+            assert np.all(dst[p].cpu().numpy() == 0xAB), p
+    assert float(got_s[2, 0, 9]) == 0.0 and not got_c[2, 0, 9].any()
+
+
+@pytest.mark.parametrize("rep,rep_num", [("quest", 1), ("max", 1), ("mean", 1), ("fix", 8)])
+def test_reps_over_int8_pth_cache(rep, rep_num):
+    say(f"[case] int8 per-token-head reps {rep}/{rep_num}")
+    n_phys, Hkv = 6, 8
+    c = q8_cfg(Hkv=Hkv, rep_method=rep, rep_num=rep_num, kv_type="int8_pth")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(422, rep_num, len(rep)))
+    kq = ops.alloc_q8_pool(c, n_phys, DEV)
+    ops.quantize_kv(c, src, torch.arange(n_phys, dtype=torch.int32), kq)
+    rp = ops.alloc_rep_pool(c, n_phys, DEV)
+    ops.build_reps(c, kq, torch.tensor([4, 1, 2], dtype=torch.int32), rp)
+    torch.cuda.synchronize()
+    codes, scales = split_i8(kq)
+    for p in (4, 1, 2):
+        K = orc.dequantize_int8_pth(codes[p], scales[p]).transpose(1, 0, 2)
+        want = orc.stored_reps(orc.block_reps(K, B, rep, rep_num), rep)[0]
+        got = rp[p].double().cpu().numpy()
+        if rep == "mean":
+            close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"int8 mean reps {p}")
+        else:
+            assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
+
+
 @pytest.mark.parametrize("rep,rep_num", [("quest", 1), ("mean", 1), ("fix", 4)])
 def test_reps_over_q4_cache(rep, rep_num):
     say(f"[case] q4 reps {rep}/{rep_num}")
