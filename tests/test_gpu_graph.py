@@ -5,7 +5,8 @@ replayed.  Here each captured step is replayed several times on different querie
 on the same workspace in between, and every replay must equal the eager call on the same inputs bit
 for bit: output, selection and count.  The step leaves its hand-off counters at zero, so a replay
 needs no clearing node.  Shapes: the 128K headline layer (scoring, top-k and Initial/Local tiles in
-one launch), a 2,400-block row (the wide top-k launch), a Q4_0 cache, and the confined step.
+one launch), a 2,400-block row (the wide top-k launch), Q4_0 and INT8 caches, and the confined
+step.
 """
 from __future__ import annotations
 
@@ -35,6 +36,7 @@ CASES = [
     ("wide-quest", 2400 * 128 + 77, "quest", "separate", 64, "fp16", 0),
     ("128k-max-q4", 131072, "max", "shared", 96, "q4_0", 0),
     ("128k-presel", 131072, "max", "shared", 96, "fp16", 192),
+    ("wide-quest-int8", 2400 * 128 + 77, "quest", "separate", 64, "int8_pth", 0),
 ]
 
 

@@ -1,7 +1,8 @@
 """Preselect on the GPU against the oracle (needs an MI355X).
 
-The set: blocks ranked by the sum of their tokens' scores (token scores as in the Dynamic rep
-tests), checked like any selection (exact, or inside the 1e-4 tie band).  The confined decode step:
+The set: blocks ranked by the sum of their tokens' scores, or by their best vote after pooling over a
+window of tokens (token scores as in the Dynamic rep tests), checked like any selection (exact, or
+inside the 1e-4 tie band).  The confined decode step:
 given a set, only its blocks that are still candidates compete; the selection is checked against the
 oracle on that restricted candidate list, and the output against the oracle's attention over the
 GPU's selection.
@@ -88,6 +89,7 @@ STEP_CASES = [
     (16, 2, "shared", "quest", 16, [280000], "fp16", 18),   # long rows
     (16, 4, "separate", "max", 30, [60000], "q4_0", 248),   # 254 entries: the one-launch path near its limit
     (16, 2, "shared", "quest", 50, [60000, 40000], "fp16", 300),
+    (32, 8, "separate", "mean", 12, [20000], "int8_pth", 40),
 ]
 
 
