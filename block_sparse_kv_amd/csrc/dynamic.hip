@@ -20,22 +20,68 @@
 // dyn_reps_kernel: one wave per (block, KV head, sequence) ranks the block's 128 scores by counting
 // (higher score, or equal and lower token, beats) and copies the K rows of the rep_num best, in
 // ascending token order, into the rep pool; a Dynamic block is then scored like Fix.
+// Over a quantized cache the products take the codes as exact fp16 integers and are scaled in fp32
+// (per 32-channel block, or per token for INT8), and the reps are the chosen rows' cached values
+// rounded to fp16, as the other reps of such a cache.
 #include "attn_core.h"
 #include "kvs_launch.h"
+#include "quant_rows.h"
 
 namespace kvs {
 
 namespace {
 
 // K tile of (phys, h) in the A-operand layout of attn_tile: lane (lc, lq) of wave w, token group g
-// (16 tokens), MFMA m: token 32w + 16g + lc, channels 32m + 8lq .. +8.
-__device__ inline void load_k_tile(const uint16_t* __restrict__ k_pool, size_t tile, uint4 (&kr)[2][4]) {
+// (16 tokens), MFMA m: token 32w + 16g + lc, channels 32m + 8lq .. +8 -- so MFMA m spans channels
+// 32m .. 32m + 31, one quantization block.  A quantized record gives its codes as exact fp16 integers
+// (Q4_0: code - 8) and the scales of the lane's S rows (tokens 32w + 16g + 4lq + i): Q8_0 / Q4_0 the
+// fp16 scales [4 tokens][4 blocks] (32 bytes), INT8 the 4 tokens' fp32 scales (sc[g][0]).  The
+// products are scaled in fp32 (imp_s), so the logits see the cached values without an fp16 rounding.
+template <int KV>
+struct KTile {
+  uint4 kr[2][4];
+  uint4 sc[2][2];
+};
+
+template <int KV>
+__device__ inline void load_k_tile(const void* __restrict__ k_pool, size_t tile, KTile<KV>& T) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
-  const uint16_t* Kt = k_pool + tile * kTile;
+  if constexpr (KV == kKvFp16) {
+    const uint16_t* Kt = static_cast<const uint16_t*>(k_pool) + tile * kTile;
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + (32 * w + 16 * g + lc) * kDim + 32 * m + 8 * lq);
+      for (int m = 0; m < 4; ++m) T.kr[g][m] = ld_stream16(Kt + (32 * w + 16 * g + lc) * kDim + 32 * m + 8 * lq);
+  } else {
+    constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : kQ8Record;
+    constexpr int kCodes = KV == kKvQ4 ? kQ4Codes : kQ8Codes;
+    const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + tile * (size_t)kRec;
+    uint2 raw[2][4];  // every load first, then the conversions
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if constexpr (KV == kKvQ4)
+          raw[g][m].x = *reinterpret_cast<const uint32_t*>(rec + tok * (kDim / 2) + 4 * (4 * m + lq));
+        else
+          raw[g][m] = *reinterpret_cast<const uint2*>(rec + tok * kDim + 32 * m + 8 * lq);
+      }
+      const int t0 = 32 * w + 16 * g + 4 * lq;
+      if constexpr (KV == kKvI8) {
+        T.sc[g][0] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 4);
+      } else {
+        T.sc[g][0] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 8);
+        T.sc[g][1] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 8 + 16);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        T.kr[g][m] = KV == kKvQ4 ? q4_dq8(raw[g][m].x, 0x3C00u)  // fp16 1.0: code - 8 exactly
+                                 : i8_codes8(raw[g][m].x, raw[g][m].y);
+  }
 }
 
 constexpr int kImpRows = 128;  // rows (observation query, query head) staged in LDS at a time
@@ -69,18 +115,43 @@ __device__ inline void q_rows_from_lds(const uint4* qs, int rg, half8_t (&qb)[4]
 }
 
 // S = K Q^T for token group gg of this wave and the 16 rows of qb (lane: tokens 4lq + i, row lc).
-__device__ inline f32x4_t imp_s(const uint4 (&kr)[2][4], const half8_t (&qb)[4], int gg) {
+// Q8_0 / Q4_0: each block's product is scaled by its token's block scale before the sum over blocks;
+// INT8: the sum is scaled by the token's scale.
+template <int KV>
+__device__ inline f32x4_t imp_s(const KTile<KV>& T, const half8_t (&qb)[4], int gg) {
   f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KV == kKvFp16 || KV == kKvI8) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[gg][m]), qb[m], S, 0, 0, 0);
+    for (int m = 0; m < 4; ++m)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, T.kr[gg][m]), qb[m], S, 0, 0, 0);
+    if constexpr (KV == kKvI8) {
+      const f32x4_t s = __builtin_bit_cast(f32x4_t, T.sc[gg][0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] *= s[i];
+    }
+  } else {
+    const uint32_t sw[8] = {T.sc[gg][0].x, T.sc[gg][0].y, T.sc[gg][0].z, T.sc[gg][0].w,
+                            T.sc[gg][1].x, T.sc[gg][1].y, T.sc[gg][1].z, T.sc[gg][1].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4_t Sm = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, T.kr[gg][m]), qb[m],
+                                                                f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // scale of token 4lq + i, block m: halfword 4i + m
+        const uint32_t wv = sw[(4 * i + m) >> 1];
+        const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(((4 * i + m) & 1) ? (wv >> 16) : (wv & 0xFFFFu)));
+        S[i] += d * Sm[i];
+      }
+    }
+  }
   return S;
 }
 
 }  // namespace
 
+template <int KV>
 __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t* __restrict__ q_obs, int n_obs,
-                                                        const uint16_t* __restrict__ k_pool,
+                                                        const void* __restrict__ k_pool,
                                                         const int32_t* __restrict__ table, int max_blocks,
                                                         const int32_t* __restrict__ seq_lens,
                                                         float2* __restrict__ part) {
@@ -95,8 +166,8 @@ __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t
     for (int x = tid; x < n_rows * 4; x += 256) out[(size_t)(x / 4) * n_sub + b * 4 + x % 4] = make_float2(-INFINITY, 0.f);
     return;
   }
-  uint4 kr[2][4];
-  load_k_tile(k_pool, (size_t)v * P.Hkv + h, kr);
+  KTile<KV> kt;
+  load_k_tile<KV>(k_pool, (size_t)v * P.Hkv + h, kt);
   const uint16_t* q_seq = q_obs + (size_t)seq * n_obs * P.Hq * kDim;
   for (int r0 = 0; r0 < n_rows; r0 += kImpRows) {
     if (r0 > 0) __syncthreads();  // every wave is done with the previous rows
@@ -111,7 +182,7 @@ __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t
       float z[2][4], mx = -INFINITY;
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        const f32x4_t S = imp_s(kr, qb, gg);
+        const f32x4_t S = imp_s<KV>(kt, qb, gg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
@@ -169,8 +240,9 @@ __global__ __launch_bounds__(256) void imp_merge_kernel(const float2* __restrict
 
 // dst: SEPARATE the importance itself [batch][Hkv][max_blocks * 128]; SHARED per-head rows of the
 // same shape, summed by imp_sum_kernel.
+template <int KV>
 __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t* __restrict__ q_obs, int n_obs,
-                                                        const uint16_t* __restrict__ k_pool,
+                                                        const void* __restrict__ k_pool,
                                                         const int32_t* __restrict__ table, int max_blocks,
                                                         const int32_t* __restrict__ seq_lens,
                                                         const float2* __restrict__ stats,
@@ -186,8 +258,8 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
     if (tid < kBlock) out[tid] = 0.f;
     return;
   }
-  uint4 kr[2][4];
-  load_k_tile(k_pool, (size_t)v * P.Hkv + h, kr);
+  KTile<KV> kt;
+  load_k_tile<KV>(k_pool, (size_t)v * P.Hkv + h, kt);
   const uint16_t* q_seq = q_obs + (size_t)seq * n_obs * P.Hq * kDim;
   const float2* st = stats + ((size_t)seq * P.Hkv + h) * n_rows;
   float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -206,7 +278,7 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
       const int last = L - n_obs + (r < n_rows ? r >> gsh : 0);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        const f32x4_t S = imp_s(kr, qb, gg);
+        const f32x4_t S = imp_s<KV>(kt, qb, gg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
@@ -237,7 +309,8 @@ __global__ __launch_bounds__(256) void imp_sum_kernel(const float* __restrict__ 
 }
 
 // One wave per (logical block, KV head, sequence): the rep_num best tokens of the block by score.
-__global__ __launch_bounds__(64) void dyn_reps_kernel(Params P, const uint16_t* __restrict__ k_pool,
+template <int KV>
+__global__ __launch_bounds__(64) void dyn_reps_kernel(Params P, const void* __restrict__ k_pool,
                                                       const float* __restrict__ imp,
                                                       const int32_t* __restrict__ table, int max_blocks,
                                                       const int32_t* __restrict__ seq_lens,
@@ -270,11 +343,27 @@ __global__ __launch_bounds__(64) void dyn_reps_kernel(Params P, const uint16_t* 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint16_t* Kt = k_pool + ((size_t)v * P.Hkv + h) * kTile;
   uint16_t* out = rep_pool + ((size_t)v * P.Hkv + h) * (size_t)P.R * kDim;
-  for (int i = lane >> 4; i < P.R; i += 4)  // 16 lanes per row, 16 bytes each
-    *reinterpret_cast<uint4*>(out + (size_t)i * kDim + 8 * (lane & 15)) =
-        *reinterpret_cast<const uint4*>(Kt + (size_t)pick[i] * kDim + 8 * (lane & 15));
+  const size_t tile = (size_t)v * P.Hkv + h;
+  for (int i = lane >> 4; i < P.R; i += 4) {  // 16 lanes per row, 16 bytes each
+    uint4 row8;
+    if constexpr (KV == kKvFp16) {
+      row8 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k_pool) + tile * kTile +
+                                             (size_t)pick[i] * kDim + 8 * (lane & 15));
+    } else {  // a quantized cache: the cached values, rounded to fp16 once
+      constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : kQ8Record;
+      const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + tile * (size_t)kRec;
+      float f[8];
+      if constexpr (KV == kKvQ4) q4_row8(rec, pick[i], lane & 15, f);
+      else if constexpr (KV == kKvI8) i8_row8(rec, pick[i], lane & 15, f);
+      else q8_row8(rec, pick[i], lane & 15, f);
+      uint32_t wd[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wd[e] = (uint32_t)f2h_bits(f[2 * e]) | ((uint32_t)f2h_bits(f[2 * e + 1]) << 16);
+      row8 = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)i * kDim + 8 * (lane & 15)) = row8;
+  }
 }
 
 hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs, const void* k_pool,
@@ -286,13 +375,30 @@ hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs
   float2* stats = part + rows_all * n_sub;
   float* heads = reinterpret_cast<float*>(stats + rows_all);  // SHARED only
   const uint16_t* q = static_cast<const uint16_t*>(q_obs);
-  const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
   const dim3 tiles(max_blocks, P.Hkv, batch);
-  hipLaunchKernelGGL(imp_stats_kernel, tiles, dim3(256), 0, s, P, q, n_obs, kp, table, max_blocks, seq_lens, part);
+#define KVS_IMP_STATS(KV)                                                                                   \
+  hipLaunchKernelGGL(imp_stats_kernel<KV>, tiles, dim3(256), 0, s, P, q, n_obs, k_pool, table, max_blocks, \
+                     seq_lens, part)
+  switch (P.kv) {
+    case kKvQ8: KVS_IMP_STATS(kKvQ8); break;
+    case kKvQ4: KVS_IMP_STATS(kKvQ4); break;
+    case kKvI8: KVS_IMP_STATS(kKvI8); break;
+    default: KVS_IMP_STATS(kKvFp16); break;
+  }
+#undef KVS_IMP_STATS
   hipLaunchKernelGGL(imp_merge_kernel, dim3((unsigned)rows_all), dim3(256), 0, s, part, n_sub, stats);
   const bool shared = P.mode == kShared;
-  hipLaunchKernelGGL(imp_accum_kernel, tiles, dim3(256), 0, s, P, q, n_obs, kp, table, max_blocks, seq_lens, stats,
-                     shared ? heads : imp);
+  float* dst = shared ? heads : imp;
+#define KVS_IMP_ACCUM(KV)                                                                                   \
+  hipLaunchKernelGGL(imp_accum_kernel<KV>, tiles, dim3(256), 0, s, P, q, n_obs, k_pool, table, max_blocks, \
+                     seq_lens, stats, dst)
+  switch (P.kv) {
+    case kKvQ8: KVS_IMP_ACCUM(kKvQ8); break;
+    case kKvQ4: KVS_IMP_ACCUM(kKvQ4); break;
+    case kKvI8: KVS_IMP_ACCUM(kKvI8); break;
+    default: KVS_IMP_ACCUM(kKvFp16); break;
+  }
+#undef KVS_IMP_ACCUM
   if (shared) {
     const size_t row_len = (size_t)max_blocks * kBlock;
     hipLaunchKernelGGL(imp_sum_kernel, dim3((unsigned)((row_len + 255) / 256), batch), dim3(256), 0, s, heads,
@@ -310,9 +416,14 @@ size_t token_importance_ws_bytes(const Params& P, int batch, int max_blocks, int
 hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float* imp, const int32_t* table,
                                int max_blocks, const int32_t* seq_lens, int batch, void* rep_pool,
                                hipStream_t s) {
-  hipLaunchKernelGGL(dyn_reps_kernel, dim3(max_blocks, P.Hkv, batch), dim3(64), 0, s, P,
-                     static_cast<const uint16_t*>(k_pool), imp, table, max_blocks, seq_lens,
-                     static_cast<uint16_t*>(rep_pool));
+  const dim3 grid(max_blocks, P.Hkv, batch);
+  uint16_t* rp = static_cast<uint16_t*>(rep_pool);
+  switch (P.kv) {
+    case kKvQ8: hipLaunchKernelGGL(dyn_reps_kernel<kKvQ8>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
+    case kKvQ4: hipLaunchKernelGGL(dyn_reps_kernel<kKvQ4>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
+    case kKvI8: hipLaunchKernelGGL(dyn_reps_kernel<kKvI8>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
+    default: hipLaunchKernelGGL(dyn_reps_kernel<kKvFp16>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
+  }
   return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (n_obs < 1) return KVS_ERR_INVALID_ARG;
-  if (n_obs > 4096 || P.kv != kvs::kKvFp16 || batch > 65535 || P.Hkv > 65535) return KVS_ERR_UNSUPPORTED;
+  if (n_obs > 4096 || batch > 65535 || P.Hkv > 65535) return KVS_ERR_UNSUPPORTED;
   if (!q_obs || !k_pool || !block_table || !seq_lens || !importance) return KVS_ERR_INVALID_ARG;
   if (!aligned(q_obs, 16) || !aligned(k_pool, 16)) return KVS_ERR_MISALIGNED;
   const size_t need = round_up(kvs::token_importance_ws_bytes(P, batch, max_blocks_per_seq, n_obs));
@@ -260,7 +260,7 @@ int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const floa
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (P.method != kvs::kDynamic) return KVS_ERR_INVALID_ARG;
-  if (P.kv != kvs::kKvFp16 || batch > 65535) return KVS_ERR_UNSUPPORTED;
+  if (batch > 65535) return KVS_ERR_UNSUPPORTED;
   if (!k_pool || !importance || !block_table || !seq_lens || !rep_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
   clear_stale_error();

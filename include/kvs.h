@@ -174,7 +174,8 @@ size_t kvs_importance_workspace_size(const kvs_config* cfg, int32_t batch, int32
  * SHARED: 0):
  *   importance = sum over observation queries i and the group's query heads j of
  *                softmax_t'(scale * q_ij . K[t']) at t' = t, over the keys t' <= L - n_obs + i,
- * zero for t >= L.  Accumulation fp32.  kv_type must be FP16 (KVS_ERR_UNSUPPORTED otherwise).
+ * zero for t >= L.  Accumulation fp32.  With a quantized kv_type the keys are the cached values (the
+ * codes times their scales, applied in fp32).
  * workspace: device, >= kvs_importance_workspace_size bytes, 256-byte aligned, scratch.
  */
 int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs, const void* k_pool,
@@ -186,7 +187,8 @@ int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs
  * kvs_build_dynamic_reps -- Dynamic reps [KT-LC §4.3].  For every full block b of every sequence
  * (b*128 + 128 <= L) and every KV head h: the K rows of the rep_num tokens of the block with the
  * highest importance (group of h; ties to the lower token), in ascending token order, written to
- * rep_pool at the block's physical id.  cfg->rep_method must be KVS_REP_DYNAMIC; kv_type FP16.
+ * rep_pool at the block's physical id.  cfg->rep_method must be KVS_REP_DYNAMIC.  With a quantized
+ * kv_type the reps are those rows' cached values rounded to fp16.
  */
 int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const float* importance,
                            const int32_t* block_table, int32_t max_blocks_per_seq,

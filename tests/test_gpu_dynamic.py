@@ -1,7 +1,8 @@
 """Dynamic reps on the GPU against the oracle (needs an MI355X).
 
 Token importance (the attention the last n_obs queries pay each cached token, summed over the
-group's query heads, causal) is compared within 1e-4 relative to the row scale; the rep tokens a
+group's query heads, causal; over a quantized cache the keys are its cached values) is compared
+within 1e-4 relative to the row scale; the rep tokens a
 block picks must be the oracle's, or differ only inside the tie band of the rep_num-th score; the
 decode step with Dynamic reps is then held to the usual rules, given the reps the GPU built.
 """
@@ -34,9 +35,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def dyn_cfg(Hq, Hkv, mode, rep_num, I=128, W=512, k=8):
+def dyn_cfg(Hq, Hkv, mode, rep_num, I=128, W=512, k=8, kv="fp16"):
     return kvs.Config(num_q_heads=Hq, num_kv_heads=Hkv, initial_len=I, local_len=W, topk=k,
-                      rep_method="dynamic", rep_num=rep_num, head_select_mode=mode)
+                      rep_method="dynamic", rep_num=rep_num, head_select_mode=mode, kv_type=kv)
 
 
 def run_importance(case, n_obs, seed):
@@ -54,20 +55,23 @@ def run_importance(case, n_obs, seed):
 
 
 IMP_CASES = [
-    # (Hq, Hkv, mode, n_obs, lens)
-    (8, 2, "separate", 5, [1000, 300]),
-    (32, 8, "shared", 32, [4000]),
-    (4, 4, "separate", 1, [129, 257]),
-    (16, 1, "shared", 40, [2000]),
-    (8, 8, "separate", 130, [700]),
+    # (Hq, Hkv, mode, n_obs, lens, kv): over a quantized cache the keys are its cached values
+    (8, 2, "separate", 5, [1000, 300], "fp16"),
+    (32, 8, "shared", 32, [4000], "fp16"),
+    (4, 4, "separate", 1, [129, 257], "fp16"),
+    (16, 1, "shared", 40, [2000], "fp16"),
+    (8, 8, "separate", 130, [700], "fp16"),
+    (8, 2, "separate", 5, [1000, 300], "q8_0"),
+    (32, 8, "shared", 32, [4000], "q4_0"),
+    (16, 4, "separate", 8, [2000], "int8_pth"),
 ]
 
 
 @pytest.mark.parametrize("idx", range(len(IMP_CASES)))
 def test_importance(idx):
-    Hq, Hkv, mode, n_obs, lens = IMP_CASES[idx]
-    say(f"[case] importance {Hq}x{Hkv} {mode} n_obs={n_obs} lens={lens}")
-    c = dyn_cfg(Hq, Hkv, mode, 2)
+    Hq, Hkv, mode, n_obs, lens, kv = IMP_CASES[idx]
+    say(f"[case] importance {Hq}x{Hkv} {mode} n_obs={n_obs} lens={lens} kv={kv}")
+    c = dyn_cfg(Hq, Hkv, mode, 2, kv=kv)
     case = Case(c, lens, seed=kvsynth.mix_seed(501, idx))
     run_importance(case, n_obs, kvsynth.mix_seed(502, idx))
 
@@ -83,19 +87,22 @@ def picked_tokens(rep_rows, block_rows):
 
 
 DYN_CASES = [
-    # (Hq, Hkv, mode, rep_num, n_obs, k, lens)
-    (32, 8, "shared", 1, 16, 12, [6000, 3000]),
-    (8, 2, "separate", 4, 8, 6, [5000]),
-    (16, 4, "separate", 3, 4, 40, [1500]),        # rep_num not dividing the block; k >= n_cand
-    (16, 2, "shared", 2, 8, 24, [280000]),        # long rows: the selection launch of > 2048 blocks
+    # (Hq, Hkv, mode, rep_num, n_obs, k, lens, kv)
+    (32, 8, "shared", 1, 16, 12, [6000, 3000], "fp16"),
+    (8, 2, "separate", 4, 8, 6, [5000], "fp16"),
+    (16, 4, "separate", 3, 4, 40, [1500], "fp16"),        # rep_num not dividing the block; k >= n_cand
+    (16, 2, "shared", 2, 8, 24, [280000], "fp16"),        # long rows: the selection launch of > 2048 blocks
+    (32, 8, "shared", 1, 16, 12, [6000, 3000], "q8_0"),   # quantized caches: reps are cached values
+    (8, 2, "separate", 4, 8, 6, [5000], "q4_0"),
+    (16, 4, "separate", 3, 4, 10, [4500], "int8_pth"),
 ]
 
 
 @pytest.mark.parametrize("idx", range(len(DYN_CASES)))
 def test_dynamic_reps_and_step(idx):
-    Hq, Hkv, mode, rn, n_obs, k, lens = DYN_CASES[idx]
-    say(f"[case] dynamic reps {Hq}x{Hkv} {mode} rep_num={rn} n_obs={n_obs} k={k} lens={lens}")
-    c = dyn_cfg(Hq, Hkv, mode, rn, k=k)
+    Hq, Hkv, mode, rn, n_obs, k, lens, kv = DYN_CASES[idx]
+    say(f"[case] dynamic reps {Hq}x{Hkv} {mode} rep_num={rn} n_obs={n_obs} k={k} lens={lens} kv={kv}")
+    c = dyn_cfg(Hq, Hkv, mode, rn, k=k, kv=kv)
     case = Case(c, lens, seed=kvsynth.mix_seed(503, idx), n_hot=3)
     pb = case.pb
     imp, imp_ref = run_importance(case, n_obs, kvsynth.mix_seed(504, idx))
@@ -115,7 +122,8 @@ def test_dynamic_reps_and_step(idx):
         ref_reps, ref_pick = orc.dynamic_reps(K, imp_ref[i], B, rn, mode, cand)
         for n, b in enumerate(cand):
             for h in range(Hkv):
-                rows = np.asarray(K[b * B:(b + 1) * B, h, :], np.float64)
+                # the block's K rows as a rep stores them (fp16; the identity for an fp16 cache)
+                rows = orc.stored_reps(np.asarray(K[b * B:(b + 1) * B, h, :], np.float64), "fix")
                 got = picked_tokens(gpu_reps[n, h], rows)
                 assert got == sorted(got), f"reps not in token order seq {i} block {b} head {h}"
                 want = ref_pick[n, h].tolist()
