@@ -301,6 +301,12 @@ def test_full_128k_shared_q8():
     run_full_check(case, "full 128K 32/8 max SHARED k96, Q8_0 cache")
 
 
+def test_full_128k_shared_q4():
+    c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="q4_0")
+    case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
+    run_full_check(case, "full 128K 32/8 max SHARED k96, Q4_0 cache")
+
+
 def test_full_128k_shared_int8_pth():
     c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="int8_pth")
     case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
