@@ -1,4 +1,4 @@
-// kvs_quantize_kv: Q8_0 or Q4_0 records of fp16 K or V tiles.  Q8_0 is the published llama.cpp block
+// kvs_quantize_kv: Q8_0, Q4_0 or per-token INT8 records of fp16 K or V tiles.  Q8_0 is the published llama.cpp block
 // format that the operator's kv_type list names (KTransformers long-context article, configuration
 // list; the instagit page's operator constructor): per token, blocks of 32 channels with scale
 // d = max|x| / 127 kept in fp16 and int8 codes round(x / d), ties away from zero.

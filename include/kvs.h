@@ -132,7 +132,7 @@ size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
 
 /*
- * kvs_quantize_kv -- Q8_0 / Q4_0 records of fp16 tiles [kv_type, see kvs_kv_type].  For each of
+ * kvs_quantize_kv -- Q8_0 / Q4_0 / INT8_PTH records of fp16 tiles [kv_type, see kvs_kv_type].  For each of
  * the n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads the fp16 tile
  * [128 tokens][128] of src_pool (laid out as an FP16 pool) and writes the record at the same id of
  * dst_pool (laid out as a pool of cfg->kv_type).  Per 32 channels of a token, in fp32 with IEEE

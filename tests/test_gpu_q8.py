@@ -1,9 +1,11 @@
-"""The Q8_0 and Q4_0 cache precisions on the GPU against the oracle (needs an MI355X).
+"""The Q8_0, Q4_0 and INT8 (per token and head) cache precisions on the GPU against the oracle
+(needs an MI355X).
 
 kv_type Q8_0 is the published llama.cpp block format that the operator's kv_type list names: per
 token and KV head, 32-channel blocks with an fp16 scale max|x|/127 and int8 codes, ties away from
 zero; Q4_0 its 4-bit sibling (scale m/-8 for the first largest-magnitude value m, codes
-min(15, trunc(x/d + 8.5))).  The codes and scales must match the oracle bit for bit (both take the
+min(15, trunc(x/d + 8.5))); INT8 one fp32 scale max|x|/127 per token and KV head with Q8_0's
+codes.  The codes and scales must match the oracle bit for bit (both take the
 rounding decisions in fp32); reps over the cached values are value-equal (Mean: relative 1e-4).
 """
 from __future__ import annotations
