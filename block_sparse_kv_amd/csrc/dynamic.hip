@@ -179,6 +179,8 @@ __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t
       q_rows_from_lds(qs, rg, qb);
       const int r = r0 + rg * 16 + lc;
       const int last = L - n_obs + (r < n_rows ? r >> gsh : 0);  // the row's own position: its last key
+      // every key of the block precedes every observation query and all 16 rows exist: no masks
+      const bool open = b * kBlock + kBlock - 1 <= L - n_obs && r0 + rg * 16 + 16 <= n_rows;
       float z[2][4], mx = -INFINITY;
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void imp_stats_kernel(Params P, const uint16_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
-          z[gg][i] = r < n_rows && t <= last ? S[i] * P.scale_log2 : -INFINITY;
+          z[gg][i] = open || (r < n_rows && t <= last) ? S[i] * P.scale_log2 : -INFINITY;
           mx = fmaxf(mx, z[gg][i]);
         }
       }
@@ -276,14 +278,24 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
       const float2 ml = ls[rg * 16 + lc];
       const float inv_l = ml.y > 0.f ? 1.0f / ml.y : 0.f;
       const int last = L - n_obs + (r < n_rows ? r >> gsh : 0);
+      const bool open = b * kBlock + kBlock - 1 <= L - n_obs && r0 + rg * 16 + 16 <= n_rows;
+      if (open) {  // no masks; the row's max is finite, so the logit is too
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const f32x4_t S = imp_s<KV>(kt, qb, gg);
+        for (int gg = 0; gg < 2; ++gg) {
+          const f32x4_t S = imp_s<KV>(kt, qb, gg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
-          const float p = r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
-          acc[gg][i] += row_sum16(p);  // the 16 rows of this group (one DPP row = one token)
+          for (int i = 0; i < 4; ++i) acc[gg][i] += row_sum16(fast_exp2(S[i] * P.scale_log2 - ml.x) * inv_l);
+        }
+      } else {
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const f32x4_t S = imp_s<KV>(kt, qb, gg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
+            const float p = r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
+            acc[gg][i] += row_sum16(p);  // the 16 rows of this group (one DPP row = one token)
+          }
         }
       }
     }
