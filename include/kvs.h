@@ -92,8 +92,9 @@ typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mo
  *   Q8_0: d = max|x| / 127, int8 codes round(x / d) ties away from zero, value d * code;
  *   Q4_0: m = the first value of largest magnitude, d = m / -8, codes min(15, trunc(x / d + 8.5)) in
  *         0..15, value d * (code - 8).
- * INT8_PTH is the int8 cache with one dynamic scale per token and head that the vLLM serving page
- * lists (its per-token-head cache modes), with Q8_0's arithmetic over a whole 128-channel row:
+ * INT8_PTH is the int8 cache with one dynamic scale per token and head of the page "Long context:
+ * 262k with KVarN, and the built-in KV modes" (section "The built-in per-token-head modes"), with
+ * Q8_0's arithmetic over a whole 128-channel row:
  *   s = max|x| / 127 kept in fp32, codes round(x / s) ties away from zero, value fp32(s * code). */
 typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2, KVS_KV_INT8_PTH = 3 } kvs_kv_type;
 

@@ -69,8 +69,9 @@ Readings taken where the pages are silent (each is the spec here):
       codes q = min(15, trunc(x * (1/d) + 8.5)) in 0..15, all fp32; d stored as fp16; the cached
       value is fp16(d) * (q - 8).  An all-zero block has d = 0 and codes 8.
   R27 kv_type INT8 per token and head (the int8 cache with one dynamic scale per token and head
-      that the vLLM page lists beside Q8_0-style block formats; it names the granularity and the fp32
-      scale, not the arithmetic, which is read as Q8_0's): per token's K or V row of one KV head,
+      of the page "Long context: 262k with KVarN, and the built-in KV modes", section "The built-in
+      per-token-head modes"; it names the granularity and the fp32 scale, not the arithmetic, which
+      is read as Q8_0's): per token's K or V row of one KV head,
       s = max|x| / 127 in fp32, stored as fp32; codes round(x * (1/s)), ties away from zero, all
       fp32 operations; an all-zero row has s = 0 and codes 0.  The cached value is the fp32
       product s * code.
