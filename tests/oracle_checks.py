@@ -566,7 +566,7 @@ def check_preselect_pooled(orc, seed=35):
     L, B, I, W = 50 * 8 + 3, 8, 8, 24
     lo, hi, cand = orc.regions(L, B, I, W)
     imp = np.abs(g.standard_normal((3, L)))
-    for pk, n in ((5, 7), (7, 3), (3, 12), (9, 1)):
+    for pk, n in ((5, 7), (7, 3), (3, 12), (9, 1), (127, 4)):  # 127: the widest window the ABI takes
         got = orc.preselect_blocks(imp, L, B, I, W, n, pool_kernel=pk)
         for gi in range(3):
             want, pv = _pseudocode_preselect(imp[gi], lo, hi, B, pk, n)
