@@ -388,6 +388,36 @@ def check_int8_pth_bound_and_range(orc):
     assert np.all(si == 1.0) and np.array_equal(ci.astype(np.float32), xi)
 
 
+GOLDEN_REPS = os.path.join(os.path.dirname(__file__), "golden", "stored_reps_worked.json")
+
+
+def check_stored_reps_golden(orc):
+    """The hand-worked values of tests/golden/stored_reps_worked.json: reps over a quantized cache are
+    stored in fp16 with round-to-nearest-even (ties to even, also in the subnormal range), Mean in
+    fp32; and whole Q8_0 / INT8 key tiles quantized, read back and reduced to those stored reps."""
+    with open(GOLDEN_REPS) as f:
+        gold = json.load(f)
+    for c in gold["direct"]:
+        got = orc.stored_reps(np.array([c["rep"]], dtype=np.float64), c["method"])
+        assert got.shape == (1,) and float(got[0]) == c["stored"], (c["why"], float(got[0]))
+    quant = {"q8_0": (orc.quantize_q8_0, orc.dequantize_q8_0),
+             "int8_pth": (orc.quantize_int8_pth, orc.dequantize_int8_pth)}
+    for c in gold["block"]:
+        x = np.zeros((128, 128), dtype=np.float32)
+        for t, row in c["x"].items():
+            for ch, v in row.items():
+                x[int(t), int(ch)] = v
+        qf, df = quant[c["kv_type"]]
+        K = df(*qf(x))[:, None, :]  # [128 tokens][1 KV head][128]
+        for method, want in (("max", [c["max"]]), ("mean", [c["mean"]]),
+                             ("quest", [c["quest_min"], c["quest_max"]])):
+            got = orc.stored_reps(orc.block_reps(K, 128, method, 1), method)
+            assert got.shape == (1, 1, len(want), 128), (c["kv_type"], method, got.shape)
+            for r, w in enumerate(want):
+                assert got[0, 0, r, :2].tolist() == w, (c["kv_type"], method, r, got[0, 0, r, :2], c["why"])
+            assert np.all(got[0, 0, :, 2:] == 0.0), (c["kv_type"], method)
+
+
 GOLDEN_Q4 = os.path.join(os.path.dirname(__file__), "golden", "q4_0_worked.json")
 
 
@@ -597,5 +627,5 @@ ALL_CHECKS = [
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
     check_dynamic_reps_closed_forms, check_preselect_identities, check_q4_golden,
     check_q4_range_and_bound, check_preselect_pooled, check_int8_pth_golden,
-    check_int8_pth_bound_and_range,
+    check_int8_pth_bound_and_range, check_stored_reps_golden,
 ]

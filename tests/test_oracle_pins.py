@@ -261,6 +261,33 @@ def _q4_no_clip(x):
     return _q4_generic(x, clip=False)
 
 
+def _fp16_toward_zero(x):
+    x = np.asarray(x, dtype=np.float64)
+    h = x.astype(np.float16)
+    over = np.abs(h.astype(np.float64)) > np.abs(x)
+    return np.where(over, np.nextafter(h, np.float16(0)), h).astype(np.float64)
+
+
+def _stored_reps_truncated(reps, method):
+    if method == orc.MEAN:
+        return _orig_stored_reps(reps, method)
+    return _fp16_toward_zero(reps)
+
+
+def _stored_reps_mean_fp16(reps, method):
+    return np.asarray(reps, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _stored_reps_ties_away(reps, method):
+    if method == orc.MEAN:
+        return _orig_stored_reps(reps, method)
+    x = np.asarray(reps, dtype=np.float64)
+    lo = _fp16_toward_zero(x)
+    hi = np.nextafter(lo.astype(np.float16), np.copysign(np.float16(np.inf), x).astype(np.float16)).astype(np.float64)
+    tie = (x - lo) == (hi - x)
+    return np.where(tie & (lo != x), hi, x.astype(np.float16).astype(np.float64))
+
+
 _orig_quantize = orc.quantize_q8_0
 _orig_dequantize = orc.dequantize_q8_0
 _orig_head_scores = orc.head_scores
@@ -269,6 +296,7 @@ _orig_regions = orc.regions
 _orig_attention = orc.attention
 _orig_block_reps = orc.block_reps
 _orig_group_scores = orc.group_scores
+_orig_stored_reps = orc.stored_reps
 
 MUTANTS = [
     ("head_scores", _quest_kmax_only),
@@ -299,6 +327,9 @@ MUTANTS = [
     ("quantize_int8_pth", _i8_div_128),
     ("quantize_int8_pth", _i8_block_32),
     ("quantize_int8_pth", _i8_fp16_scale),
+    ("stored_reps", _stored_reps_truncated),
+    ("stored_reps", _stored_reps_mean_fp16),
+    ("stored_reps", _stored_reps_ties_away),
 ]
 
 
