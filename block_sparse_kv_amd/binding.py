@@ -39,7 +39,7 @@ EXPORTS = (
     "kvs_token_importance", "kvs_build_dynamic_reps", "kvs_preselect_workspace_size",
     "kvs_preselect_blocks", "kvs_decode_step_preselected_workspace_size", "kvs_decode_step_preselected",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
-    "kvs_decode_step_workspace_size", "kvs_decode_step",
+    "kvs_decode_step_workspace_size", "kvs_decode_step", "kvs_validate_contents",
 )
 
 
@@ -128,6 +128,8 @@ _lib.kvs_decode_step_workspace_size.restype = _S
 _lib.kvs_decode_step_workspace_size.argtypes = [_CFG, _I, _I]
 _lib.kvs_decode_step.restype = ctypes.c_int
 _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
+_lib.kvs_validate_contents.restype = ctypes.c_int
+_lib.kvs_validate_contents.argtypes = [_CFG, _P, _I, _P, _I, _P, _P, _P, _I]
 
 
 class KvsError(RuntimeError):
@@ -283,3 +285,15 @@ def kvs_decode_step(cfg, q, k_pool, v_pool, rep_pool, block_table, max_blocks_pe
                               _ptr(out), _ptr(sel_out), _ptr(sel_count_out), _ptr(workspace),
                               workspace_bytes, _stream(stream))
     return _check(st, "kvs_decode_step") if check else st
+
+
+def kvs_validate_contents(cfg, seq_lens, batch, block_table, max_blocks_per_seq, sel=None, sel_count=None,
+                          presel=None, n_presel=0) -> int:
+    """Host arrays (numpy int32, C-contiguous) or raw host addresses; returns the status (no raise)."""
+    def hp(a):
+        if a is None or isinstance(a, int):
+            return a
+        assert a.dtype.name == "int32" and a.flags["C_CONTIGUOUS"], "int32 C-contiguous host array"
+        return a.ctypes.data
+    return _lib.kvs_validate_contents(_cfg(cfg), hp(seq_lens), batch, hp(block_table), max_blocks_per_seq,
+                                      hp(sel), hp(sel_count), hp(presel), n_presel)

@@ -4,6 +4,10 @@
 #include <math.h>
 #include <stdio.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
 
 #include "kvs.h"
 #include "kvs_launch.h"
@@ -149,9 +153,110 @@ kvs::AttnArgs attn_args(const Params& P, const AttnLayout& L, void* ws, const vo
   return a;
 }
 
+// ---- device contents (KVS_DEBUG=1) -------------------------------------------------------------
+// The checks of kvs_validate_contents, on host arrays; each failure names the first bad entry.
+int fail_contents(const char* what, long i, long j, long v) {
+  snprintf(g_last_error, sizeof g_last_error, "kvs contents: %s at [%ld][%ld] = %ld", what, i, j, v);
+  return KVS_ERR_INVALID_ARG;
+}
+
+int validate_host(const Params& P, const int32_t* lens, int batch, const int32_t* table, int max_blocks,
+                  const int32_t* sel, const int32_t* cnt, const int32_t* presel, int n_presel) {
+  for (int i = 0; i < batch; ++i) {
+    const int L = lens[i];
+    if (L < 1 || (long)L > (long)max_blocks * kvs::kBlock) return fail_contents("seq_len out of [1, max_blocks*128]", i, 0, L);
+    const int nb = (L + kvs::kBlock - 1) / kvs::kBlock;
+    if (table)
+      for (int b = 0; b < nb; ++b)
+        if (table[(size_t)i * max_blocks + b] < 0) return fail_contents("block_table entry < 0", i, b, table[(size_t)i * max_blocks + b]);
+    const kvs::Regions rg = kvs::regions_of(L, P.initial_len, P.local_len);
+    const int n_cand = rg.cand_hi - rg.cand_lo;
+    for (int gi = 0; gi < P.G; ++gi) {
+      const size_t row = (size_t)i * P.G + gi;
+      if (cnt) {
+        const int c = cnt[row];
+        if (c < 0 || c > P.topk || c > n_cand) return fail_contents("sel_count out of [0, min(topk, candidates)]", (long)row, 0, c);
+        if (sel) {
+          std::vector<char> seen(max_blocks, 0);
+          for (int e = 0; e < c; ++e) {
+            const int b = sel[row * P.topk + e];
+            if (b < rg.cand_lo || b >= rg.cand_hi) return fail_contents("selected block not a candidate", (long)row, e, b);
+            if (seen[b]) return fail_contents("selected block repeated", (long)row, e, b);
+            seen[b] = 1;
+          }
+        }
+      }
+      if (presel)
+        for (int e = 0; e < n_presel; ++e) {
+          const int b = presel[row * n_presel + e];
+          if (b < -1 || b >= max_blocks) return fail_contents("preselected block out of [-1, max_blocks)", (long)row, e, b);
+        }
+    }
+  }
+  return KVS_OK;
+}
+
+bool debug_on() {
+  const char* e = getenv("KVS_DEBUG");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+// KVS_DEBUG=1: wait for `stream`, copy the device arrays that steer the kernels to the host and
+// validate them before anything is enqueued.  Skipped while the stream is being captured into a graph
+// (nothing can be waited for then).  Null arrays are not checked.
+int debug_check(const Params& P, hipStream_t s, const int32_t* lens_d, int batch, const int32_t* table_d,
+                int max_blocks, const int32_t* sel_d, const int32_t* cnt_d, const int32_t* presel_d,
+                int n_presel) {
+  if (!debug_on()) return KVS_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return KVS_OK;
+  hipError_t e = hipStreamSynchronize(s);
+  const size_t rows = (size_t)batch * P.G;
+  std::vector<int32_t> lens(batch), table(table_d ? (size_t)batch * max_blocks : 0),
+      sel(sel_d ? rows * P.topk : 0), cnt(cnt_d ? rows : 0), presel(presel_d ? rows * n_presel : 0);
+  auto copy = [&](std::vector<int32_t>& h, const int32_t* d) {
+    if (e == hipSuccess && d && !h.empty())
+      e = hipMemcpy(h.data(), d, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  };
+  copy(lens, lens_d);
+  copy(table, table_d);
+  copy(sel, sel_d);
+  copy(cnt, cnt_d);
+  copy(presel, presel_d);
+  if (e != hipSuccess) return hip_status(e, "KVS_DEBUG contents check");
+  return validate_host(P, lens.data(), batch, table_d ? table.data() : nullptr, max_blocks,
+                       sel_d ? sel.data() : nullptr, cnt_d ? cnt.data() : nullptr,
+                       presel_d ? presel.data() : nullptr, n_presel);
+}
+
+// Physical block ids of kvs_build_reps / kvs_quantize_kv must not be negative.
+int debug_check_ids(hipStream_t s, const int32_t* ids_d, int n) {
+  if (!debug_on()) return KVS_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return KVS_OK;
+  std::vector<int32_t> ids(n);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(ids.data(), ids_d, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(e, "KVS_DEBUG contents check");
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0) return fail_contents("physical block id < 0", i, 0, ids[i]);
+  return KVS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int kvs_validate_contents(const kvs_config* cfg, const int32_t* seq_lens, int32_t batch,
+                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* sel,
+                          const int32_t* sel_count, const int32_t* presel, int32_t n_presel) {
+  Params P;
+  int st = make_params(cfg, &P);
+  if (st != KVS_OK) return st;
+  if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
+  if (!seq_lens || (sel && !sel_count) || (presel && n_presel < 1)) return KVS_ERR_INVALID_ARG;
+  return validate_host(P, seq_lens, batch, block_table, max_blocks_per_seq, sel, sel_count, presel, n_presel);
+}
 
 const char* kvs_last_error(void) { return g_last_error; }
 
@@ -200,6 +305,7 @@ int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* 
   if (n_blocks > 65535) return KVS_ERR_UNSUPPORTED;  // grid y
   if (!src_pool || !phys_block_ids || !dst_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(src_pool, 16) || !aligned(dst_pool, 16)) return KVS_ERR_MISALIGNED;
+  if ((st = debug_check_ids(static_cast<hipStream_t>(stream), phys_block_ids, n_blocks)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_quantize_q8(P, src_pool, phys_block_ids, n_blocks, dst_pool,
                                             static_cast<hipStream_t>(stream)),
@@ -215,6 +321,7 @@ int kvs_build_reps(const kvs_config* cfg, const void* k_pool, const int32_t* phy
   if (n_blocks == 0) return KVS_OK;
   if (!k_pool || !phys_block_ids || !rep_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  if ((st = debug_check_ids(static_cast<hipStream_t>(stream), phys_block_ids, n_blocks)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_build_reps(P, k_pool, phys_block_ids, n_blocks, cfg->rep_num,
                                            rep_pool, static_cast<hipStream_t>(stream)),
@@ -244,6 +351,7 @@ int kvs_token_importance(const kvs_config* cfg, const void* q_obs, int32_t n_obs
   const size_t need = round_up(kvs::token_importance_ws_bytes(P, batch, max_blocks_per_seq, n_obs));
   if (!workspace || workspace_bytes < need) return KVS_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  if ((st = debug_check(P, static_cast<hipStream_t>(stream), seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_token_importance(P, q_obs, n_obs, k_pool, block_table, max_blocks_per_seq,
                                                  seq_lens, batch, importance, workspace,
@@ -263,6 +371,7 @@ int kvs_build_dynamic_reps(const kvs_config* cfg, const void* k_pool, const floa
   if (batch > 65535) return KVS_ERR_UNSUPPORTED;
   if (!k_pool || !importance || !block_table || !seq_lens || !rep_pool) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  if ((st = debug_check(P, static_cast<hipStream_t>(stream), seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_dynamic_reps(P, k_pool, importance, block_table, max_blocks_per_seq,
                                              seq_lens, batch, rep_pool, static_cast<hipStream_t>(stream)),
@@ -278,6 +387,7 @@ int kvs_score_blocks(const kvs_config* cfg, const void* q, const void* rep_pool,
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !rep_pool || !block_table || !seq_lens || !scores) return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(rep_pool, 16)) return KVS_ERR_MISALIGNED;
+  if ((st = debug_check(P, static_cast<hipStream_t>(stream), seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_score(P, q, rep_pool, block_table, max_blocks_per_seq, seq_lens,
                                       batch, scores, static_cast<hipStream_t>(stream)),
@@ -292,6 +402,7 @@ int kvs_topk_blocks(const kvs_config* cfg, const float* scores, const int32_t* s
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!scores || !seq_lens || !sel_count || (!sel && P.topk > 0)) return KVS_ERR_INVALID_ARG;
+  if ((st = debug_check(P, static_cast<hipStream_t>(stream), seq_lens, batch, nullptr, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_topk(P, scores, seq_lens, batch, max_blocks_per_seq, sel,
                                      sel_count, nullptr, nullptr, static_cast<hipStream_t>(stream)),
@@ -323,6 +434,7 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   kvs::AttnArgs a = attn_args(P, A, workspace, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                               seq_lens, sel, sel_count, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, P.topk > 0 ? sel : nullptr, sel_count, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   hipError_t e = kvs::launch_attn_tiles(a, batch, true, false, s);
   if (e != hipSuccess) return hip_status(e, "kvs_sparse_decode_attn/tiles");
@@ -361,6 +473,7 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
   kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                               seq_lens, tiles, cnt, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles,
                                             at<int>(workspace, S.ctr_off), batch, s),
@@ -393,6 +506,7 @@ int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const i
   if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
   float* bs = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = debug_check(P, s, seq_lens, batch, nullptr, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   hipError_t e = kvs::launch_block_scores(P, importance, seq_lens, batch, max_blocks_per_seq, pool_kernel,
                                          bs, s);
@@ -469,6 +583,7 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   void* aws = static_cast<char*>(workspace) + S.attn_off;
   kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                               seq_lens, sel, cnt, out);
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, presel, n_presel)) != KVS_OK) return st;
   clear_stale_error();
   bool il_done = false;  // Initial/Local tiles streamed with the scoring (rows of up to 2048 blocks)
   hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s, &il_done);

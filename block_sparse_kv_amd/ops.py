@@ -115,7 +115,8 @@ def sparse_decode_attn(cfg, q, k_pool, v_pool, block_table, seq_lens, sel, sel_c
 
 
 def step_workspace(cfg, batch, max_blocks, device) -> torch.Tensor:
-    """A zero-filled kvs_decode_step workspace (its hand-off counters must start at zero)."""
+    """A zero-filled kvs_decode_step workspace (its hand-off counters must start at zero).  Use it
+    for kvs_decode_step only, and zero it again after a call that failed or did not complete."""
     n = max(B.kvs_decode_step_workspace_size(cfg, batch, max_blocks), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 

@@ -15,12 +15,22 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns all memory; the library
- *     never allocates, frees or synchronises, keeps no state between calls and is thread-safe.
+ *     never allocates, frees or synchronises.  It holds no device state of its own; what carries
+ *     over between calls is (a) the hand-off counters inside a kvs_decode_step workspace (see
+ *     there: such a workspace belongs to kvs_decode_step alone) and (b) the per-thread text behind
+ *     kvs_last_error.  Calls from several host threads are safe when they use distinct
+ *     workspaces and outputs.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *   - Every argument that can be checked on the host is checked before anything is enqueued; on
  *     error the call returns a negative status and enqueues nothing.  Contents of device buffers
  *     (sequence lengths, table entries, selections) are the caller's responsibility: out-of-range
  *     values there are undefined behaviour.
+ *   - Debug mode: with the environment variable KVS_DEBUG set (and not "0") when a call is made,
+ *     every entry point that reads such contents first waits for `stream`, copies them to the host
+ *     and checks them as kvs_validate_contents does (block ids of kvs_build_reps /
+ *     kvs_quantize_kv: >= 0); bad contents return KVS_ERR_INVALID_ARG, with the first bad entry in
+ *     kvs_last_error, and nothing is enqueued.  The check is skipped while the stream is being
+ *     captured into a graph.  This mode synchronises; results are otherwise unchanged.
  *   - v1 limits: head_dim == 128, block_size == 128, num_kv_heads in {1,2,4,8,16},
  *     num_q_heads / num_kv_heads in {1,2,4,8,16}.  Other shapes return KVS_ERR_UNSUPPORTED.
  *
@@ -122,6 +132,23 @@ const char* kvs_status_string(int status);
  * valid until the next failing call on the same thread. */
 const char* kvs_last_error(void);
 
+/*
+ * kvs_validate_contents -- the device-content rules of the entry points, checked on HOST copies
+ * (what KVS_DEBUG=1 runs before each call).  All pointers are host pointers; block_table, sel /
+ * sel_count and presel are nullable (not checked when null).  Rules, per sequence i:
+ *   1 <= seq_lens[i] <= max_blocks_per_seq * 128;
+ *   block_table[i][b] >= 0 for every block b the sequence uses (b < ceil(seq_lens[i] / 128));
+ *   per group gr: 0 <= sel_count[i][gr] <= min(topk, candidates at seq_lens[i]); the first
+ *   sel_count entries of sel[i][gr] are distinct candidate blocks of the current length (what an
+ *   older selection of the same sequence still satisfies: candidates only grow);
+ *   presel[i][gr][e] in [-1, max_blocks_per_seq).
+ * Returns KVS_OK, or KVS_ERR_INVALID_ARG with the first bad entry described in kvs_last_error.
+ * The upper bound of physical ids is not checked: the pools' sizes are not arguments.
+ */
+int kvs_validate_contents(const kvs_config* cfg, const int32_t* seq_lens, int32_t batch,
+                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* sel,
+                          const int32_t* sel_count, const int32_t* presel, int32_t n_presel);
+
 /* Reps per (block, KV head) for this config, or a negative status. */
 int kvs_rep_count(const kvs_config* cfg /* host */);
 
@@ -129,7 +156,7 @@ int kvs_rep_count(const kvs_config* cfg /* host */);
 size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
 
 /* Bytes of one physical block of k_pool (or v_pool) over all KV heads: Hkv * 32768 for FP16,
- * Hkv * 17408 for Q8_0, Hkv * 9216 for Q4_0; 0 on a bad config. */
+ * Hkv * 17408 for Q8_0, Hkv * 9216 for Q4_0, Hkv * 16896 for INT8_PTH; 0 on a bad config. */
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
 
 /*
@@ -288,22 +315,27 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
 
 /*
  * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention
- * [KT-LC §4.6, retrieval then attention], enqueued as four kernels with no host synchronisation:
- *   for max_blocks_per_seq <= 2048: 1. scoring, top-k per (sequence, group) by the scoring
- *   workgroup of the group that finishes last, and the Initial/Local tiles' attention (they do not
- *   depend on the selection), in one launch;  2. attention over the selected tiles;  3. the
- *   log-sum-exp merge into out;
- *   otherwise: 1. scoring;  2. top-k;  3. attention over the Initial/Local and selected tiles;
- *   4. the merge.
+ * [KT-LC §4.6, retrieval then attention], enqueued with no host synchronisation as
+ *   for max_blocks_per_seq <= 2048, three launches: 1. scoring, top-k per (sequence, group) by the
+ *   scoring workgroup of the group that finishes last, and the Initial/Local tiles' attention (they
+ *   do not depend on the selection);  2. attention over the selected tiles;  3. the log-sum-exp
+ *   merge into out;
+ *   otherwise four: 1. scoring;  2. top-k, with the Initial/Local tiles' attention;  3. attention
+ *   over the selected tiles;  4. the merge.
  * Top-k also resolves the selected blocks' physical ids.
  * Results equal kvs_score_blocks + kvs_topk_blocks + kvs_sparse_decode_attn on the same inputs.
  * Reps must be current for every candidate block (kvs_build_reps).  sel_out / sel_count_out
  * (nullable) receive the selection for reuse by later kvs_sparse_decode_attn calls.
  * workspace: device, >= kvs_decode_step_workspace_size bytes, 256-byte aligned.  Its first 64 KiB
  * hold hand-off counters: zero-fill the workspace once before its first use (e.g. hipMemset); every
- * call leaves the counters zero again, so the workspace can then be reused by any later call, of any
- * config and size that fits.  The rest is scratch.  Calls sharing one workspace must not run
- * concurrently (stream order is enough).  batch * G must not exceed 16384 (KVS_ERR_UNSUPPORTED).
+ * call that runs to completion leaves the counters zero again, so the workspace can then be reused
+ * by later kvs_decode_step calls, of any config and size that fits.  Such a workspace belongs to
+ * kvs_decode_step alone: the other entry points write their own data from offset 0 and would leave
+ * non-zero counters, and so would a call that did not complete (a failed launch, an aborted
+ * stream); zero-fill it again after either.  Counters that are not zero leave the selection
+ * unmade and the attention reading stale tile ids.  The rest is scratch.  Calls sharing one
+ * workspace must not run concurrently (stream order is enough).  batch * G must not exceed 16384
+ * (KVS_ERR_UNSUPPORTED).
  */
 int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
                     const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,

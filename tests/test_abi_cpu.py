@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import block_sparse_kv_amd as kvs
@@ -25,7 +27,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 20, decl
+    assert len(decl) == 21, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -246,3 +248,66 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     hips = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(hips) == 1, hips
+
+
+# ------------------------------------------------------------------------------------------------
+# Device-content rules (what KVS_DEBUG=1 checks), on host arrays: no GPU involved.
+# ------------------------------------------------------------------------------------------------
+def _contents_case():
+    import numpy as np
+    c = cfg(topk=4, initial_len=128, local_len=256, head_select_mode="shared")
+    lens = np.array([20 * 128 + 5, 9 * 128], dtype=np.int32)      # candidates [1, 18) and [1, 7)
+    table = np.arange(2 * 24, dtype=np.int32).reshape(2, 24)
+    sel = np.array([[[3, 5, 17, -1]], [[1, 2, 6, -1]]], dtype=np.int32)
+    cnt = np.array([[3], [3]], dtype=np.int32)
+    presel = np.array([[[1, 4, -1]], [[2, 23, -1]]], dtype=np.int32)
+    return c, lens, table, sel, cnt, presel
+
+
+def test_contents_valid():
+    c, lens, table, sel, cnt, presel = _contents_case()
+    assert B.kvs_validate_contents(c, lens, 2, table, 24, sel, cnt, presel, 3) == B.KVS_OK
+    assert B.kvs_validate_contents(c, lens, 2, None, 24) == B.KVS_OK
+
+
+@pytest.mark.parametrize("what", ["len0", "len_over", "table_neg", "cnt_over_k", "cnt_over_cand", "cnt_neg",
+                                  "sel_not_cand_low", "sel_in_local", "sel_repeat", "presel_low", "presel_high"])
+def test_contents_rejected(what):
+    c, lens, table, sel, cnt, presel = _contents_case()
+    if what == "len0":
+        lens[1] = 0
+    elif what == "len_over":
+        lens[0] = 24 * 128 + 1
+    elif what == "table_neg":
+        table[0, 20] = -1                     # block 20 holds the 5 last tokens of sequence 0
+    elif what == "cnt_over_k":
+        cnt[0, 0] = 5
+    elif what == "cnt_over_cand":
+        c = cfg(topk=8, initial_len=128, local_len=256, head_select_mode="shared")
+        sel = np.concatenate([sel, np.full((2, 1, 4), -1, np.int32)], axis=2)
+        sel[1, 0, :7] = [1, 2, 3, 4, 5, 6, 6]
+        cnt[1, 0] = 7                         # sequence 1 has 6 candidates
+    elif what == "cnt_neg":
+        cnt[1, 0] = -1
+    elif what == "sel_not_cand_low":
+        sel[0, 0, 0] = 0                      # the Initial block
+    elif what == "sel_in_local":
+        sel[1, 0, 2] = 7                      # sequence 1's Local starts at block 7
+    elif what == "sel_repeat":
+        sel[0, 0, 1] = 3
+    elif what == "presel_low":
+        presel[0, 0, 2] = -2
+    elif what == "presel_high":
+        presel[1, 0, 0] = 24
+    st = B.kvs_validate_contents(c, np.ascontiguousarray(lens), 2, np.ascontiguousarray(table), 24,
+                                 np.ascontiguousarray(sel), np.ascontiguousarray(cnt),
+                                 np.ascontiguousarray(presel), 3)
+    assert st == B.KVS_ERR_INVALID_ARG, what
+    assert "kvs contents" in kvs.kvs_last_error()
+
+
+def test_contents_bad_arguments():
+    c, lens, table, sel, cnt, presel = _contents_case()
+    assert B.kvs_validate_contents(c, None, 2, table, 24) == B.KVS_ERR_INVALID_ARG
+    assert B.kvs_validate_contents(c, lens, 0, table, 24) == B.KVS_ERR_INVALID_ARG
+    assert B.kvs_validate_contents(c, lens, 2, table, 24, sel, None) == B.KVS_ERR_INVALID_ARG
