@@ -6,26 +6,35 @@
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --workload NAME   (counters -> profiles/)
 
 A step is one pass of the whole hot path over one decode token: kvs_decode_step, i.e. block scoring,
-top-k and sparse attention (four launches: scoring; top-k, with the Initial/Local tiles for rows of
-<= 2048 blocks; the attention tiles; the merge):
+top-k and sparse attention:
   * 128k-max / 128k-mean: InternLM2.5-7B-shaped layer, 32 query / 8 KV heads, d 128, 131,072 cached
     tokens, block 128, Max (or Mean) reps, SHARED selection, top-96, Initial 128, Local 4,096;
     one query = one step of one sequence.  The JSON line's `value` is 128k-max.
   * 1m: 32 such layers of 1,048,576 tokens each (128 GiB of K/V resident), Quest reps, SEPARATE,
     top-64; one query = one decode token through all 32 layers (32 kvs_decode_step calls).
+  * 8k: 8 query / 8 KV heads, 8,192 tokens, Quest, SEPARATE, top-8, Local 1,024.
+  * 32k: Llama-2-70B-shaped GQA, 64 query / 8 KV heads, 32,768 tokens, Quest, SEPARATE, top-32.
+  * mixed: 16 sequences of U[16K, 128K] tokens in one shuffled paged pool, Fix reps (every 16th
+    token), SHARED, top-32, Local 2,048; each step builds the reps of the blocks that fill at it, then
+    decodes the batch (16 queries per step).
+  * the rows beyond the core path: Dynamic reps, preselect, Q8_0 / Q4_0 / INT8 caches.
 Inputs are seeded synthetic fp16 (kvsynth) and resident in HBM before timing.  To keep repeated
 steps from being served by the 256 MB Infinity Cache, a 128K step cycles through 16 cache replicas
-(1.1 GB); a 1M step touches 2.7 GB of distinct memory anyway.  Steps are captured once into a HIP
-graph and replayed; HIP events on the replay stream time exactly K steps.
+(1.1 GB); a 1M step touches 2.7 GB of distinct memory anyway.  Steps are captured into HIP graphs
+and replayed.
 
 Roofline: algorithmic bytes per step = q + reps of every candidate block + K and V of every attended
 token of every KV head + out, over the step time, against 8 TB/s.  The unit is one kvs_decode_step
-call (its four kernels); profiles/ holds the per-kernel rocprofv3 averages of the same command.
+call (its three or four kernels); profiles/ holds the per-kernel rocprofv3 averages of the same command.
 traffic: HBM bytes per step from rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/), each scaled by what
 the counter reads for the 4 GiB device copy timed at the start of every run; null when the kernels'
 sources changed since the counters were taken.
-cpu_baseline: the fp64 CPU oracle (single thread) on the same inputs, reps prebuilt, timed over a
-bounded number of queries.
+cpu_baseline: the fp64 CPU oracle on the same inputs, reps prebuilt, on one thread and on one
+single-threaded process per host core (up to 16), each for a bounded time.
+
+Timing: every workload runs `--trials` timed runs of exactly `--steps` steps (the batched mixed
+workload: whole windows of 128 steps), each bracketed by device synchronisations and HIP events; the
+median run is reported with the fastest and slowest.
 """
 from __future__ import annotations
 
@@ -58,6 +67,18 @@ WORKLOADS = {
                       layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260012),
     "1m": dict(L=1 << 20, Hq=32, Hkv=8, I=128, W=4096, k=64, rep="quest", mode="separate",
                layers=32, replicas=1, n_hot=16, hot_per_head=True, seed=20260003),
+    # 8K tokens, 8 query / 8 KV heads, 4 hot blocks shared by the heads
+    "8k": dict(L=8192, Hq=8, Hkv=8, I=128, W=1024, k=8, rep="quest", mode="separate",
+               layers=1, replicas=40, n_hot=4, hot_per_head=False, seed=20260000),
+    # Llama-2-70B-shaped GQA: 64 query / 8 KV heads, 32K tokens, 8 hot blocks drawn per KV head
+    "32k": dict(L=32768, Hq=64, Hkv=8, I=128, W=4096, k=32, rep="quest", mode="separate",
+                layers=1, replicas=10, n_hot=8, hot_per_head=True, seed=20260001),
+    # 16 sequences of U[16K, 128K] tokens in one shuffled paged pool (two pools alternate), Fix reps
+    # every 16th token, SHARED, k 32, Local 2048: a window of 128 decode steps, each building the reps
+    # of the blocks that fill at that step, then the batched decode step
+    "mixed": dict(batch=16, Lmin=16384, Lmax=131072, Hq=32, Hkv=8, I=128, W=2048, k=32, rep="fix",
+                  rep_num=8, mode="shared", layers=1, replicas=2, window=128, n_hot=8,
+                  hot_per_head=False, seed=20260004),
     # the article's base configuration: Dynamic reps, one per block, from 32 observation queries
     "128k-dynamic": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="dynamic", rep_num=1,
                          n_obs=32, mode="shared", layers=1, replicas=16, n_hot=50, hot_per_head=False,
@@ -136,9 +157,10 @@ def traffic_per_step(name):
     return float(kv["hbm_bytes_per_step"])
 
 
-def required_bytes(w):
-    """Algorithmic bytes of one decode step of one layer."""
-    L, Hq, Hkv = w["L"], w["Hq"], w["Hkv"]
+def required_bytes(w, L=None):
+    """Algorithmic bytes of one decode step of one layer of one sequence of L tokens."""
+    L = w["L"] if L is None else L
+    Hq, Hkv = w["Hq"], w["Hkv"]
     ie, ls, ncand = regions(L, w["I"], w["W"])
     k_eff = min(w["k"], ncand)
     T = min(ie, L) + k_eff * B + (L - ls)
@@ -210,6 +232,35 @@ class Setup:
             self.pws_bytes = kvs.kvs_decode_step_preselected_workspace_size(self.cfg, 1, nb, w["presel"])
             self.pws = torch.empty(self.pws_bytes, dtype=torch.uint8, device=device)
 
+    @property
+    def cycle(self):
+        """Distinct step instances one captured cycle runs through (the cache replicas)."""
+        return self.w["replicas"]
+
+    def bulk_build(self, device, trials=6):
+        """kvs_build_reps over every full block of replica 0 (layer 0): the post-prefill build."""
+        import torch
+
+        w = self.w
+        _, kp, _, rp = self.units[0]
+        nfull = w["L"] // B
+        ids = torch.arange(nfull, dtype=torch.int32, device=device)
+        times = []
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self.kvs.kvs_build_reps(self.cfg, kp, ids, nfull, rp)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1)}[w["rep"]]
+        rep_row = D * (4 if w["rep"] == "mean" else 2)
+        rd = nfull * w["Hkv"] * (B * D * 2 if w["rep"] != "fix" else R * D * 2)
+        wr = nfull * w["Hkv"] * R * rep_row
+        t = sorted(times[1:])[len(times[1:]) // 2]
+        return dict(blocks=nfull, kv_heads=w["Hkv"], bytes_read=rd, bytes_written=wr, ms=t * 1e3,
+                    hbm_gbs=(rd + wr) / t / 1e9, frac=(rd + wr) / t / 1e9 / PEAK_HBM_GBS)
+
     def step(self, replica):
         """One decode step (all layers) on cache replica `replica`."""
         w = self.w
@@ -252,42 +303,138 @@ class Setup:
                                             sel, cnt, self.out, self.attn_ws, self.attn_ws_bytes)
 
 
-def time_steps(setup, steps, warmup, use_graph=True, step_fn=None):
-    """Returns (seconds for exactly `steps` steps, graph used?).  step_fn(replica) defaults to the
-    decode step."""
+class MixedSetup:
+    """The batched mixed-length workload: `batch` sequences of seeded U[Lmin, Lmax] tokens in one
+    shuffled paged pool per replica (two replicas alternate step by step, so the 256 MB Infinity
+    Cache does not serve a step from the one before).  A cycle is a window of `window` decode steps:
+    at step t every sequence holds L_i + t tokens, the pools being filled to L_i + window beforehand;
+    the step first builds the reps of the blocks that become full at t (one per sequence per 128
+    steps), then runs kvs_decode_step on the whole batch."""
+
+    def __init__(self, name, device):
+        import torch
+
+        import block_sparse_kv_amd as kvs
+        from block_sparse_kv_amd import ops
+        import kvsynth
+
+        w = WORKLOADS[name]
+        self.name, self.w, self.kvs = name, w, kvs
+        self.cfg = kvs.Config(num_q_heads=w["Hq"], num_kv_heads=w["Hkv"], initial_len=w["I"],
+                              local_len=w["W"], topk=w["k"], rep_method=w["rep"],
+                              rep_num=w.get("rep_num", 1), head_select_mode=w["mode"])
+        win, bsz = w["window"], w["batch"]
+        self.lens0 = kvsynth.uniform_lengths(kvsynth.mix_seed(w["seed"], 1), bsz, w["Lmin"], w["Lmax"])
+        hot = []
+        for L in self.lens0:
+            ie, _, nc = regions(L, w["I"], w["W"])
+            hot.append((ie // B, ie // B + nc))
+        t0 = time.time()
+        self.units = []
+        for r in range(w["replicas"]):
+            q, kp, vp, table, _ = kvsynth.pool_batch(kvsynth.mix_seed(w["seed"], 2, r),
+                                                     [L + win for L in self.lens0], w["Hq"], w["Hkv"],
+                                                     hot_ranges=hot, n_hot=w["n_hot"], device=device)
+            rp = ops.alloc_rep_pool(self.cfg, kp.shape[0], device)
+            full = torch.cat([table[i, : (L + win - 1) // B] for i, L in enumerate(self.lens0)])
+            ops.build_reps(self.cfg, kp, full, rp)
+            fill = []  # per window step: physical ids of the blocks that become full at that step
+            for t in range(win):
+                ids = [int(table[i, (L + t) // B - 1]) for i, L in enumerate(self.lens0) if (L + t) % B == 0]
+                fill.append(torch.tensor(ids, dtype=torch.int32, device=device))
+            self.units.append((q, kp, vp, rp, table, fill))
+        torch.cuda.synchronize()
+        log(f"[setup] {name}: {w['replicas']} pools of {bsz} sequences ({min(self.lens0)}..{max(self.lens0)} "
+            f"tokens) generated in {time.time() - t0:.1f}s")
+        self.nb = self.units[0][4].shape[1]
+        self.lens_t = [torch.tensor([L + t for L in self.lens0], dtype=torch.int32, device=device)
+                       for t in range(win)]
+        self.out = torch.empty((bsz, w["Hq"], D), dtype=torch.float32, device=device)
+        self.ws_bytes = kvs.kvs_decode_step_workspace_size(self.cfg, bsz, self.nb)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)  # counters start at 0
+        self.sel = torch.empty((bsz, self.cfg.groups, w["k"]), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((bsz, self.cfg.groups), dtype=torch.int32, device=device)
+
+    @property
+    def cycle(self):
+        return self.w["window"]
+
+    def step(self, t):
+        """Window step t: reps of the blocks filling at t, then one decode step of the batch."""
+        q, kp, vp, rp, table, fill = self.units[t % self.w["replicas"]]
+        ids = fill[t]
+        if ids.numel():
+            self.kvs.kvs_build_reps(self.cfg, kp, ids, ids.numel(), rp)
+        self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, table, self.nb, self.lens_t[t], self.w["batch"],
+                                 self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
+
+    def window_bytes(self):
+        """Algorithmic bytes of one window: every step's decode bytes, plus the rows of the reps built
+        (read and written)."""
+        w = self.w
+        tot = 0
+        R = w.get("rep_num", 1)
+        for t in range(w["window"]):
+            for L in self.lens0:
+                rb = required_bytes(w, L + t)
+                tot += rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
+            n_fill = sum(1 for L in self.lens0 if (L + t) % B == 0)
+            tot += n_fill * w["Hkv"] * R * D * 2 * 2
+        return tot
+
+
+def _capture(step_fn, idxs):
+    import torch
+
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in idxs:
+            step_fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(setup, steps, warmup, trials=7, step_fn=None, whole_cycles=False):
+    """Times `trials` runs of exactly `steps` steps (whole cycles when whole_cycles: at least `steps`)
+    replayed from HIP graphs: a cycle (one step per replica, in order) and, when `steps` is not a
+    multiple of it, a graph of the cycle's first `steps % cycle` steps.  Returns (list of seconds per
+    run, steps per run, graph used?).  step_fn(i) defaults to the decode step of cycle position i."""
     import torch
 
     step_fn = step_fn or setup.step
-    R = setup.w["replicas"]
+    C = setup.cycle
+    if whole_cycles:
+        steps = max(C, -(-steps // C) * C)
     for i in range(warmup):
-        step_fn(i % R)
+        step_fn(i % C)
     torch.cuda.synchronize()
-    graph = None
-    if use_graph:
-        try:
-            s = torch.cuda.Stream()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=s):
-                for r in range(R):
-                    step_fn(r)
-            graph.replay()
-            torch.cuda.synchronize()
-        except Exception as e:  # capture unsupported: time eager launches instead
-            log(f"[bench] graph capture failed ({e}); timing eager launches")
-            graph = None
-    steps = max(R, (steps // R) * R) if graph is not None else steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    if graph is not None:
-        for _ in range(steps // R):
-            graph.replay()
-    else:
-        for i in range(steps):
-            step_fn(i % R)
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3, steps, graph is not None
+    full = part = None
+    graphed = True
+    try:
+        full = _capture(step_fn, range(C)) if steps >= C else None
+        part = _capture(step_fn, range(steps % C)) if steps % C else None
+    except Exception as e:  # capture unsupported: time eager launches instead
+        log(f"[bench] graph capture failed ({e}); timing eager launches")
+        graphed = False
+    times = []
+    for _ in range(trials):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        if graphed:
+            for _ in range(steps // C):
+                full.replay()
+            if part is not None:
+                part.replay()
+        else:
+            for i in range(steps):
+                step_fn(i % C)
+        end.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / 1e3)
+    return times, steps, graphed
 
 
 def copy_bandwidth(device, nbytes=4 << 30):
@@ -311,10 +458,49 @@ def copy_bandwidth(device, nbytes=4 << 30):
     return 2.0 * nbytes * n / sec / 1e9
 
 
-def cpu_baseline(setup, budget_s=15.0):
-    """The fp64 oracle, one thread, on replica 0 / layer 0 of the same inputs (reps prebuilt)."""
+def _cpu_worker(args):
+    """One process of the CPU baseline: the oracle's decode step on the saved inputs, repeated for
+    `budget_s` seconds with one BLAS thread; returns the number of steps done."""
+    d, kw, budget_s = args
     import numpy as np
     from threadpoolctl import threadpool_limits
+
+    from oracle import kvs_oracle as orc
+
+    q = np.load(os.path.join(d, "q.npy"))
+    K = np.load(os.path.join(d, "K.npy"), mmap_mode="r")
+    V = np.load(os.path.join(d, "V.npy"), mmap_mode="r")
+    reps = np.load(os.path.join(d, "reps.npy"))
+    n, t0 = 0, time.time()
+    with threadpool_limits(limits=1):
+        while True:
+            orc.decode_step(q, K, V, reps=reps, **kw)
+            n += 1
+            if time.time() - t0 > budget_s:
+                break
+    return n, time.time() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(setup, budget_s=12.0, max_workers=16):
+    """The fp64 oracle on replica 0 / layer 0 of the same inputs (reps prebuilt), untuned: one
+    process with one thread, then one single-threaded process per host core (up to the box's share
+    of 16), each running whole decode steps; queries/s = steps done / wall time / layers."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
 
     import kvsynth
     from oracle import kvs_oracle as orc
@@ -322,44 +508,79 @@ def cpu_baseline(setup, budget_s=15.0):
     w = setup.w
     q, kp, vp, _ = setup.units[0]
     L = w["L"]
-    K = kvsynth.logical_from_pool(kp, setup.table[0].cpu(), L).cpu().numpy()
-    V = kvsynth.logical_from_pool(vp, setup.table[0].cpu(), L).cpu().numpy()
-    qn = q[0].cpu().numpy()
-    ie, ls, cand = orc.regions(L, B, w["I"], w["W"])
-    reps = orc.block_reps(K, B, w["rep"], 1, blocks=cand)
-    n, t0 = 0, time.time()
-    with threadpool_limits(limits=1):
-        while True:
-            orc.decode_step(qn, K, V, B=B, initial_len=w["I"], local_len=w["W"], topk=w["k"],
-                            method=w["rep"], mode=w["mode"], reps=reps)
-            n += 1
-            if time.time() - t0 > budget_s:
-                break
-    sec_per_layer = (time.time() - t0) / n
-    qps = 1.0 / (sec_per_layer * w["layers"])
-    return dict(value=qps, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{n} single-layer decode steps of {setup.name} (replica 0, layer 0), reps "
-                       f"prebuilt, fp64 numpy, 1 thread; queries/s = 1/({w['layers']} x layer time)")
+    d = tempfile.mkdtemp(prefix="kvs_cpu_")
+    try:
+        K = kvsynth.logical_from_pool(kp, setup.table[0].cpu(), L).cpu().numpy()
+        np.save(os.path.join(d, "K.npy"), K)
+        np.save(os.path.join(d, "V.npy"), kvsynth.logical_from_pool(vp, setup.table[0].cpu(), L).cpu().numpy())
+        np.save(os.path.join(d, "q.npy"), q[0].cpu().numpy())
+        _, _, cand = orc.regions(L, B, w["I"], w["W"])
+        np.save(os.path.join(d, "reps.npy"), orc.block_reps(K, B, w["rep"], 1, blocks=cand))
+        del K
+        kw = dict(B=B, initial_len=w["I"], local_len=w["W"], topk=w["k"], method=w["rep"], mode=w["mode"])
+        n1, t1 = _cpu_worker((d, kw, budget_s))
+        avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+        workers = max(1, min(max_workers, avail))
+        ctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
+        t0 = time.time()
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_cpu_worker, [(d, kw, budget_s)] * workers)
+        wall = time.time() - t0
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    n_all = sum(r[0] for r in res)
+    qps1 = n1 / t1 / w["layers"]
+    qps_all = sum(r[0] / r[1] for r in res) / w["layers"]  # the processes ran concurrently
+    return dict(value=qps_all, unit="queries/s", cores=workers, kind="oracle",
+                one_thread=dict(value=qps1, cores=1, steps=n1, seconds=t1),
+                all_cores=dict(value=qps_all, cores=workers, steps=n_all, seconds=wall),
+                nproc=os.cpu_count(), cpu_model=_cpu_model(),
+                sample=f"single-layer decode steps of {setup.name} (replica 0, layer 0; reps prebuilt), "
+                       f"fp64 numpy oracle, ~{budget_s:.0f} s per process: 1 process x 1 thread "
+                       f"({n1} steps), then {workers} single-threaded processes at once ({n_all} steps); "
+                       f"queries/s = sum of each process's steps / its time / {w['layers']} layers")
 
 
-def measure(name, steps, warmup, device, reuse=True):
+def _stats(times, steps):
+    per = sorted(t / steps for t in times)
+    return per[len(per) // 2], per[0], per[-1]
+
+
+def measure(name, steps, warmup, device, trials=7, reuse=True):
     import torch
 
-    st = Setup(name, device)
-    sec, steps_done, graphed = time_steps(st, steps, warmup)
-    w = st.w
-    rb = required_bytes(w)
-    per_layer = rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
-    per_step = per_layer * w["layers"]
-    step_s = sec / steps_done
+    w = WORKLOADS[name]
+    mixed = "batch" in w
+    st = MixedSetup(name, device) if mixed else Setup(name, device)
+    times, steps_done, graphed = time_steps(st, steps, warmup, trials, whole_cycles=mixed)
+    step_s, step_lo, step_hi = _stats(times, steps_done)
+    if mixed:
+        per_step = st.window_bytes() / w["window"]
+        per_layer = per_step
+        qn = w["batch"]
+        rbs = [required_bytes(w, L) for L in st.lens0]
+        extra = dict(batch=qn, lengths=st.lens0, window=w["window"],
+                     attended_tokens_mean=sum(r["tokens"] for r in rbs) / qn,
+                     candidates_mean=sum(r["ncand"] for r in rbs) / qn, k_eff=min(r["k_eff"] for r in rbs))
+    else:
+        rb = required_bytes(w)
+        per_layer = rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
+        per_step = per_layer * w["layers"]
+        qn = 1
+        extra = dict(attended_tokens=rb["tokens"], candidates=rb["ncand"], k_eff=rb["k_eff"])
     gbs = per_step / step_s / 1e9
-    res = dict(workload=name, steps=steps_done, graph=graphed, ms_per_step=step_s * 1e3,
-               queries_per_s=1.0 / step_s, required_bytes_per_step=per_step,
+    res = dict(workload=name, steps=steps_done, trials=trials, graph=graphed, ms_per_step=step_s * 1e3,
+               ms_per_step_min=step_lo * 1e3, ms_per_step_max=step_hi * 1e3, queries_per_step=qn,
+               queries_per_s=qn / step_s, required_bytes_per_step=per_step,
                required_bytes_per_layer=per_layer, hbm_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
-               attended_tokens=rb["tokens"], candidates=rb["ncand"], k_eff=rb["k_eff"],
-               traffic_bytes_per_step=traffic_per_step(name), setup=st)
-    log(f"[bench] {name}: {step_s * 1e6:.1f} us/step, {1 / step_s:.0f} queries/s, "
-        f"{gbs:.0f} GB/s = {100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+               traffic_bytes_per_step=traffic_per_step(name), **extra, setup=st)
+    log(f"[bench] {name}: {step_s * 1e6:.1f} us/step (min {step_lo * 1e6:.1f}, max {step_hi * 1e6:.1f}, "
+        f"{trials} runs of {steps_done} steps), {qn / step_s:.0f} queries/s, {gbs:.0f} GB/s = "
+        f"{100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s (graph={graphed})")
+    if not mixed and "kv" not in w and w["rep"] != "dynamic" and "presel" not in w:
+        res["bulk_build_reps"] = bb = st.bulk_build(device)
+        log(f"[bench] {name} kvs_build_reps over {bb['blocks']} blocks x {bb['kv_heads']} KV heads: "
+            f"{bb['ms']:.3f} ms, {bb['hbm_gbs']:.0f} GB/s = {100 * bb['frac']:.1f}% of 8 TB/s")
     if w["rep"] == "dynamic":  # the per-prompt cost of Dynamic reps: token scores + reps of one cache
         from block_sparse_kv_amd import ops
         q_obs, kp = st.dyn
@@ -391,12 +612,13 @@ def measure(name, steps, warmup, device, reuse=True):
         res["preselect_build"] = dict(ms=min(times[1:]), pool_kernel=w.get("pool", 0), n_presel=w["presel"])
         log(f"[bench] {name} preselected set of one {w['L']}-token cache from its token scores: "
             f"{min(times[1:]):.3f} ms (pool_kernel {w.get('pool', 0)})")
-    if not reuse:
+    if not reuse or mixed:
         return res
     # selection reuse: attention only, with each unit's kept selection (no scoring, no top-k)
     st.prepare_reuse()
-    sec_a, steps_a, _ = time_steps(st, steps, warmup, step_fn=st.step_attn)
-    attn_s = sec_a / steps_a
+    times_a, steps_a, _ = time_steps(st, steps, warmup, trials, step_fn=st.step_attn)
+    attn_s, _, _ = _stats(times_a, steps_a)
+    rb = required_bytes(w)
     attn_bytes = (rb["q"] + rb["kv"] + rb["out"]) * w["layers"]
     res["reuse_attention_only"] = dict(ms_per_step=attn_s * 1e3, queries_per_s=1.0 / attn_s,
                                        required_bytes_per_step=attn_bytes,
@@ -529,6 +751,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--trials", type=int, default=7, help="timed runs of exactly --steps steps; the median is reported")
     ap.add_argument("--workload", default="all", choices=["all", *WORKLOADS])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-reuse", action="store_true",
@@ -560,16 +783,17 @@ def main():
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     results = {}
     for n in names:
-        st_steps = args.steps if WORKLOADS[n]["layers"] == 1 else max(16, args.steps // 8)
-        results[n] = measure(n, st_steps, args.warmup, device, reuse=not args.no_reuse)
+        st_steps = args.steps if (n == names[0] or WORKLOADS[n]["layers"] == 1) else max(16, args.steps // 8)
+        results[n] = measure(n, st_steps, args.warmup, device, trials=args.trials, reuse=not args.no_reuse)
         if n != names[0]:
             del results[n]["setup"]
             torch.cuda.empty_cache()
     head = results[names[0]]
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and "batch" not in WORKLOADS[names[0]]:
         cpu = cpu_baseline(head["setup"])
-        log(f"[bench] cpu oracle: {cpu['value']:.2f} queries/s")
+        log(f"[bench] cpu oracle: {cpu['one_thread']['value']:.2f} queries/s on 1 thread, "
+            f"{cpu['value']:.2f} on {cpu['cores']} processes ({cpu['cpu_model']}, nproc {cpu['nproc']})")
     del head["setup"]
     w = WORKLOADS[names[0]]
     line = {
@@ -580,20 +804,25 @@ def main():
         "steps": head["steps"],
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "trials": head["trials"],
+        "ms_per_step_min": head["ms_per_step_min"],
+        "ms_per_step_max": head["ms_per_step_max"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic (seeded N(0,1) fp16 K/V/q with planted hot blocks)",
-        "config": {"workload": names[0], "context": w["L"], "batch": 1, "layers": w["layers"],
+        "config": {"workload": names[0],
+                   "context": w["L"] if "L" in w else f"U[{w['Lmin']}, {w['Lmax']}] + window {w['window']}",
+                   "batch": w.get("batch", 1), "layers": w["layers"],
                    "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": D, "block_size": B,
                    "rep": w["rep"], "head_select_mode": w["mode"], "topk": w["k"],
                    "initial": w["I"], "local": w["W"], "replicas": w["replicas"]},
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["frac"],
                      "traffic": traffic_per_step(names[0]),
-                     "kernel": "kvs_decode_step (scoring, top-k and Initial/Local tiles, "
-                               "selected tiles, merge: 3 or 4 launches)",
+                     "kernel": "kvs_decode_step (one call: scoring, top-k and Initial/Local tiles, "
+                               "selected tiles, merge)",
                      "bytes_per_launch": head["required_bytes_per_step"]},
         "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,

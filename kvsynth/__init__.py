@@ -191,3 +191,56 @@ def logical_from_pool(pool: torch.Tensor, table_row, L: int) -> torch.Tensor:
     ids = torch.as_tensor(table_row[:nb], dtype=torch.long, device=pool.device)
     x = pool.index_select(0, ids).transpose(1, 2).reshape(nb * B, pool.shape[1], pool.shape[3])
     return x[:L]
+
+
+def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> list[int]:
+    """n sequence lengths drawn uniformly from [lo, hi] (seeded, CPU generator)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
+def pool_batch(seed: int, lens: list[int], Hq: int, Hkv: int, d: int = 128, B: int = 128, *,
+               hot_ranges=None, n_hot: int = 0, shift: float = 2.0, device="cuda", chunk_blocks: int = 256):
+    """A batch of sequences drawn directly into one shared paged pool (for batches too large to hold
+    twice).  Sequence i owns ceil(lens[i] / B) blocks; physical ids are a seeded permutation of all
+    of them.  Keys and values come from per-(sequence, chunk) seeds; the tail of each sequence's
+    last block is NaN.  hot_ranges[i] = (lo, hi): n_hot planted blocks of sequence i drawn from
+    [lo, hi), the same for every KV head, keys shifted by ``shift`` along the sequence's per-head
+    query direction.  Returns (q [batch][Hq][d], k_pool, v_pool, block_table [batch][max_blocks]
+    int32 (-1 past a sequence), hot)."""
+    nbs = [math.ceil(L / B) for L in lens]
+    n_phys = sum(nbs)
+    mb = max(nbs)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(mix_seed(seed, 7))
+    perm = torch.randperm(n_phys, generator=g)
+    table = torch.full((len(lens), mb), -1, dtype=torch.int32)
+    k_pool = torch.empty((n_phys, Hkv, B, d), dtype=torch.float16, device=device)
+    v_pool = torch.empty((n_phys, Hkv, B, d), dtype=torch.float16, device=device)
+    qs, hot, nxt = [], [], 0
+    for i, L in enumerate(lens):
+        ids = perm[nxt:nxt + nbs[i]]
+        nxt += nbs[i]
+        table[i, : nbs[i]] = ids.to(torch.int32)
+        idd = ids.to(device)
+        q = randn_fp16((Hq, d), mix_seed(seed, i, 1), device)
+        qs.append(q)
+        for c0 in range(0, nbs[i], chunk_blocks):
+            c1 = min(nbs[i], c0 + chunk_blocks)
+            k_pool.index_copy_(0, idd[c0:c1], randn_fp16((c1 - c0, Hkv, B, d), mix_seed(seed, i, 12, c0), device))
+            v_pool.index_copy_(0, idd[c0:c1], randn_fp16((c1 - c0, Hkv, B, d), mix_seed(seed, i, 13, c0), device))
+        blocks = []
+        if n_hot > 0 and hot_ranges is not None:
+            u = query_directions(q, Hkv).to(device)
+            blocks = choose_blocks(mix_seed(seed, i, 4), hot_ranges[i][0], hot_ranges[i][1], n_hot)
+            if blocks:
+                pid = idd[torch.tensor(blocks, device=device)]
+                rows = k_pool[pid].float() + shift * u[None, :, None, :]
+                k_pool[pid] = _canon_fp16(rows)
+        hot.append(blocks)
+        tail = nbs[i] * B - L
+        if tail:
+            k_pool[int(ids[-1]), :, B - tail:, :] = float("nan")
+            v_pool[int(ids[-1]), :, B - tail:, :] = float("nan")
+    return torch.stack(qs), k_pool, v_pool, table.to(device), hot
