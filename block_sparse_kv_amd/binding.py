@@ -40,7 +40,9 @@ EXPORTS = (
     "kvs_preselect_blocks", "kvs_decode_step_preselected_workspace_size", "kvs_decode_step_preselected",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step", "kvs_validate_contents",
+    "kvs_decode_step_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20  # KVS_NOALLOC_SCRATCH_BYTES
 
 
 class kvs_config(ctypes.Structure):
@@ -128,6 +130,8 @@ _lib.kvs_decode_step_workspace_size.restype = _S
 _lib.kvs_decode_step_workspace_size.argtypes = [_CFG, _I, _I]
 _lib.kvs_decode_step.restype = ctypes.c_int
 _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
+_lib.kvs_decode_step_noalloc.restype = ctypes.c_int
+_lib.kvs_decode_step_noalloc.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P]
 _lib.kvs_validate_contents.restype = ctypes.c_int
 _lib.kvs_validate_contents.argtypes = [_CFG, _P, _I, _P, _I, _P, _P, _P, _I]
 
@@ -297,3 +301,11 @@ def kvs_validate_contents(cfg, seq_lens, batch, block_table, max_blocks_per_seq,
         return a.ctypes.data
     return _lib.kvs_validate_contents(_cfg(cfg), hp(seq_lens), batch, hp(block_table), max_blocks_per_seq,
                                       hp(sel), hp(sel_count), hp(presel), n_presel)
+
+
+def kvs_decode_step_noalloc(cfg, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                            batch, out, sel_out, sel_count_out, stream=None, check=True):
+    st = _lib.kvs_decode_step_noalloc(_cfg(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(rep_pool),
+                                      _ptr(block_table), max_blocks_per_seq, _ptr(seq_lens), batch,
+                                      _ptr(out), _ptr(sel_out), _ptr(sel_count_out), _stream(stream))
+    return _check(st, "kvs_decode_step_noalloc") if check else st

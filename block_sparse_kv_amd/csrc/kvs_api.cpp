@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "kvs.h"
@@ -243,6 +244,48 @@ int debug_check_ids(hipStream_t s, const int32_t* ids_d, int n) {
   return KVS_OK;
 }
 
+// ---- the allocation-free decode step ----------------------------------------------------------
+// A file-scope device array holds the decode-step workspace for callers that cannot allocate.  Each
+// GPU holds its own copy until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kScratchBytes = KVS_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch sub-buffers are 256-byte aligned");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Zero the hand-off counters (a fill kernel, not a memset node, so a captured first call replays
+// correctly).
+__global__ void zero_ctr_kernel(unsigned* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The scratch address on the current device, set up on the first call there: the symbol's address,
+// and its counters cleared on `s` (the array starts zeroed; a clear also covers a module loaded into
+// a context that reuses memory).
+int scratch_on_device(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_step_noalloc/hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return KVS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                 "kvs_decode_step_noalloc/hipGetSymbolAddress");
+    hipLaunchKernelGGL(zero_ctr_kernel, dim3(16), dim3(256), 0, s, static_cast<unsigned*>(p),
+                       (int)(kCtrBytes / sizeof(unsigned)));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "kvs_decode_step_noalloc/clear");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,23 +491,30 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
   return step_layout(P, batch, max_blocks_per_seq).total;
 }
 
-int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
-                    const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
-                    const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
-                    int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
-                    kvs_stream_t stream) {
-  Params P;
-  int st = make_params(cfg, &P);
+}  // extern "C"
+
+namespace {
+// Host checks of kvs_decode_step's arguments other than the workspace.
+int decode_step_checks(const kvs_config* cfg, Params* P, const void* q, const void* k_pool,
+                       const void* v_pool, const void* rep_pool, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, float* out) {
+  int st = make_params(cfg, P);
   if (st != KVS_OK) return st;
   if ((st = check_sizes(batch, max_blocks_per_seq)) != KVS_OK) return st;
   if (!q || !k_pool || !v_pool || !rep_pool || !block_table || !seq_lens || !out)
     return KVS_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(rep_pool, 16))
     return KVS_ERR_MISALIGNED;
-  if ((size_t)batch * P.G * sizeof(int) > kCtrBytes) return KVS_ERR_UNSUPPORTED;
+  if ((size_t)batch * P->G * sizeof(int) > kCtrBytes) return KVS_ERR_UNSUPPORTED;
+  return KVS_OK;
+}
+
+// The decode step over a checked workspace of at least step_layout(...).total bytes.
+int decode_step_run(const Params& P, const void* q, const void* k_pool, const void* v_pool,
+                    const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                    int32_t* sel_count_out, void* workspace, hipStream_t s, const char* where) {
   const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
-  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
   int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, S.sel_off);
   int32_t* cnt = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
   int32_t* tiles = at<int32_t>(workspace, S.tiles_off);
@@ -472,12 +522,54 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
   void* aws = static_cast<char*>(workspace) + S.attn_off;
   kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                               seq_lens, tiles, cnt, out);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
   clear_stale_error();
   return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles,
                                             at<int>(workspace, S.ctr_off), batch, s),
-                    "kvs_decode_step");
+                    where);
+}
+}  // namespace
+
+extern "C" {
+
+int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                    const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                    int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
+                    kvs_stream_t stream) {
+  Params P;
+  int st = decode_step_checks(cfg, &P, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq,
+                              seq_lens, batch, out);
+  if (st != KVS_OK) return st;
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < S.total) return KVS_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return KVS_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
+  return decode_step_run(P, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                         batch, out, sel_out, sel_count_out, workspace, s, "kvs_decode_step");
+}
+
+int kvs_decode_step_noalloc(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                            const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                            int32_t* sel_count_out, kvs_stream_t stream) {
+  Params P;
+  int st = decode_step_checks(cfg, &P, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq,
+                              seq_lens, batch, out);
+  if (st != KVS_OK) return st;
+  const StepLayout S = step_layout(P, batch, max_blocks_per_seq);
+  if (S.total > kScratchBytes) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "kvs_decode_step_noalloc: these sizes need %zu bytes of scratch; the static scratch holds %zu "
+             "(use kvs_decode_step with a workspace)", S.total, kScratchBytes);
+    return KVS_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, nullptr, 0)) != KVS_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_on_device(s, &ws)) != KVS_OK) return st;
+  return decode_step_run(P, q, k_pool, v_pool, rep_pool, block_table, max_blocks_per_seq, seq_lens,
+                         batch, out, sel_out, sel_count_out, ws, s, "kvs_decode_step_noalloc");
 }
 
 size_t kvs_preselect_workspace_size(const kvs_config* cfg, int32_t batch, int32_t max_blocks_per_seq) {

@@ -343,6 +343,24 @@ int kvs_decode_step(const kvs_config* cfg, const void* q, const void* k_pool, co
                     int32_t* sel_count_out, void* workspace, size_t workspace_bytes,
                     kvs_stream_t stream);
 
+/*
+ * kvs_decode_step_noalloc -- kvs_decode_step for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the workspace taken from a static device scratch area of KVS_NOALLOC_SCRATCH_BYTES
+ * that every GPU the library runs on holds until the process ends.  No allocation is made by this
+ * call or by the library.  The first call on a device looks the area up and enqueues one small
+ * kernel on `stream` that clears its hand-off counters; every completed call leaves them zero.
+ * Sizes whose kvs_decode_step_workspace_size exceeds KVS_NOALLOC_SCRATCH_BYTES return
+ * KVS_ERR_WORKSPACE (the needed size in kvs_last_error) and enqueue nothing.  All calls on one
+ * device share its scratch: calls that may overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  Other arguments and errors as kvs_decode_step.
+ */
+#define KVS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int kvs_decode_step_noalloc(const kvs_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                            const void* rep_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
+                            int32_t* sel_count_out, kvs_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 21, decl
+    assert len(decl) == 22, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -311,3 +311,20 @@ def test_contents_bad_arguments():
     assert B.kvs_validate_contents(c, None, 2, table, 24) == B.KVS_ERR_INVALID_ARG
     assert B.kvs_validate_contents(c, lens, 0, table, 24) == B.KVS_ERR_INVALID_ARG
     assert B.kvs_validate_contents(c, lens, 2, table, 24, sel, None) == B.KVS_ERR_INVALID_ARG
+
+
+def test_noalloc_host_checks():
+    """kvs_decode_step_noalloc rejects bad arguments and sizes beyond its static scratch on the host,
+    before any HIP call."""
+    c = cfg(topk=96, rep_method="max")
+    st = B.kvs_decode_step_noalloc(c, None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1024, ALIGNED, 1,
+                                   ALIGNED, None, None, stream=0, check=False)
+    assert st == B.KVS_ERR_INVALID_ARG
+    st = B.kvs_decode_step_noalloc(c, MISALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1024, ALIGNED, 1,
+                                   ALIGNED, None, None, stream=0, check=False)
+    assert st == B.KVS_ERR_MISALIGNED
+    assert kvs.kvs_decode_step_workspace_size(c, 64, 8192) > B.NOALLOC_SCRATCH_BYTES
+    st = B.kvs_decode_step_noalloc(c, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8192, ALIGNED, 64,
+                                   ALIGNED, None, None, stream=0, check=False)
+    assert st == B.KVS_ERR_WORKSPACE
+    assert "static scratch" in kvs.kvs_last_error()
