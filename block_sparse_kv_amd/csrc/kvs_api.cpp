@@ -18,7 +18,7 @@ namespace {
 using kvs::Params;
 
 constexpr size_t kAlign = 256;  // sub-buffers of a workspace start on 256-byte boundaries
-constexpr size_t kCtrBytes = 65536;  // decode-step hand-off counters: batch * G <= 16384
+constexpr size_t kCtrBytes = kvs::kStepCtrBytes;  // decode-step hand-off counters: batch * G <= 16384
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -111,7 +111,7 @@ AttnLayout attn_layout(const Params& P, int batch, int max_blocks) {
 // the caller does not take it), the selected tiles' physical ids, then the attention partials.
 struct StepLayout {
   AttnLayout attn;
-  size_t ctr_off, scores_off, sel_off, cnt_off, tiles_off, attn_off, total;
+  size_t ctr_off, scores_off, sel_off, cnt_off, tiles_off, summ_off, summ_bytes, attn_off, total;
 };
 
 StepLayout step_layout(const Params& P, int batch, int max_blocks) {
@@ -123,6 +123,8 @@ StepLayout step_layout(const Params& P, int batch, int max_blocks) {
   s.sel_off = off;    off += round_up(nsel);
   s.cnt_off = off;    off += round_up((size_t)batch * P.G * sizeof(int32_t));
   s.tiles_off = off;  off += round_up(nsel);
+  s.summ_bytes = kvs::summaries_bytes(P, batch, max_blocks);  // chunk summaries: scores, ids, physical ids
+  s.summ_off = off;   off += 3 * round_up(s.summ_bytes);
   s.attn = attn_layout(P, batch, max_blocks);
   s.attn_off = off;   off += s.attn.total;
   s.total = off;
@@ -524,7 +526,8 @@ int decode_step_run(const Params& P, const void* q, const void* k_pool, const vo
                               seq_lens, tiles, cnt, out);
   clear_stale_error();
   return hip_status(kvs::launch_decode_step(a, rep_pool, scores, sel, cnt, tiles,
-                                            at<int>(workspace, S.ctr_off), batch, s),
+                                            at<int>(workspace, S.ctr_off), batch, s,
+                                            S.summ_bytes ? at<char>(workspace, S.summ_off) : nullptr),
                     where);
 }
 }  // namespace

@@ -22,6 +22,11 @@ constexpr int kQ4Record = kQ4Codes + kBlock * (kDim / kQ8Group) * 2;  // 9216 by
 // INT8 with one fp32 scale per token row: codes as Q8_0's, then 128 fp32 scales
 constexpr int kI8Record = kQ8Codes + kBlock * 4;                       // 16896 bytes
 
+// Long-row selection from chunk summaries: a chunk is kChunkBlocks consecutive blocks of a score row,
+// summarised by its kChunkTop best candidates.
+constexpr int kChunkBlocks = 64;
+constexpr int kChunkTop = 8;
+
 enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3, kDynamic = 4 };  // Dynamic: scored like Fix
 enum Mode { kSeparate = 0, kShared = 1 };
 enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2, kKvI8 = 3 };

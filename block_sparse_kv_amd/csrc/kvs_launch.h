@@ -53,14 +53,27 @@ hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_
 // selected ones; A.sel holds physical ids if sel_phys, logical ids otherwise.
 hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s);
+// Hand-off counters of the decode step: kStepCtrBytes of ints, one per (sequence, group) at index
+// (seq * G + group) * step_ctr_stride(batch * G), so that counters fall on separate 128-byte lines as
+// far as they fit (agent-scope atomics on one line are serialized where memory performs them).
+constexpr size_t kStepCtrBytes = 65536;
+inline int step_ctr_stride(int n_ctr) {
+  int st = 32;
+  while (st > 1 && (size_t)n_ctr * st * sizeof(int) > kStepCtrBytes) st >>= 1;
+  return st;
+}
 // The whole decode step (step.hip): scores [batch][G][max_blocks], sel / sel_count, and the selected
 // tiles' physical ids (tiles [batch][G][topk]) are its intermediates; A.sel must be `tiles`.  ctr:
-// [batch][G] ints, zero when the call starts and zero again when it ends.
+// the kStepCtrBytes counter area, zero when the call starts and zero again when it ends.
 // Scores [batch][G][max_blocks] of every candidate, and, for rows the fused step handles in one
 // launch (max_blocks <= 2048), the Initial/Local tiles in the same launch (*il_done = true).
 hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* scores, int batch, hipStream_t s,
                            bool* il_done);
+// summ: the chunk summaries of the long-row selection, three arrays of summaries_bytes() each (val,
+// id, phys), nullable (then long rows take the separate top-k launch).
+size_t summaries_bytes(const Params& P, int batch, int max_blocks);
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s);
+                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s,
+                              void* summ);
 
 }  // namespace kvs

@@ -28,13 +28,16 @@ constexpr int kScoreBlocksPerHeadWg = 16 * kScorePasses;
 // PER_HEAD (SEPARATE only) of KV head h_one.  Non-candidates get -INFINITY.  scores_row: SEPARATE ->
 // [Hkv][max_blocks] rows of this sequence, SHARED -> [max_blocks].  COH: the scores are stored for a
 // workgroup of the same kernel (st_coh).
+// lds_chunk (PER_HEAD, nullable): also receives every block's score (-inf for non-candidates and past
+// the row) at [block - b0] and its physical id (0 for non-candidates) as an int at [64 + block - b0],
+// for the workgroup's own use after a barrier (nb <= 64).
 template <int G, int METHOD, int MODE, bool PER_HEAD = false, bool COH = false>
 __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16_t* __restrict__ q_seq,
                                           const void* __restrict__ rep_pool,
                                           const int32_t* __restrict__ trow, int max_blocks, int L,
                                           int b0, int nb, float* __restrict__ scores_row,
                                           float* lds_part /* >= 16 * kScorePasses floats */,
-                                          int h_one = 0) {
+                                          int h_one = 0, float* lds_chunk = nullptr) {
   static_assert(!(PER_HEAD && MODE == kShared), "a SHARED score sums over every KV head");
   const int Hkv = P.Hkv;
   const int t = threadIdx.x, c = t & 15;
@@ -137,6 +140,10 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
       if (c == 0) {
 #pragma unroll
         for (int p = 0; p < kScorePasses; ++p) {
+          if (PER_HEAD && lds_chunk) {
+            lds_chunk[blk[p] - b0] = cand[p] ? acc[p] : -INFINITY;
+            reinterpret_cast<int*>(lds_chunk)[64 + blk[p] - b0] = (int)phys[p];
+          }
           if (!inr[p]) continue;
           float* dst = scores_row + (size_t)h * max_blocks + blk[p];
           const float v = cand[p] ? acc[p] : -INFINITY;

@@ -16,12 +16,13 @@ namespace kvs {
 
 namespace {
 hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                               int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s) {
+                               int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
+                               const Summaries& U = Summaries()) {
   switch (A.P.kv) {
-    case kKvQ8: return launch_score_select_kv<kKvQ8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s);
-    case kKvQ4: return launch_score_select_kv<kKvQ4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s);
-    case kKvI8: return launch_score_select_kv<kKvI8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s);
-    default: return launch_score_select_kv<kKvFp16>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s);
+    case kKvQ8: return launch_score_select_kv<kKvQ8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
+    case kKvQ4: return launch_score_select_kv<kKvQ4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
+    case kKvI8: return launch_score_select_kv<kKvI8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
+    default: return launch_score_select_kv<kKvFp16>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
   }
 }
 
@@ -43,13 +44,27 @@ hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* score
   return launch_score(A.P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
 }
 
+size_t summaries_bytes(const Params& P, int batch, int max_blocks) {
+  if (!(P.mode == kSeparate && max_blocks > kStepTopkSmall && max_blocks <= kStepSummMax)) return 0;
+  return (size_t)batch * P.G * ((max_blocks + kChunkBlocks - 1) / kChunkBlocks) * kChunkTop * 4;
+}
+
 hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s) {
+                              int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s,
+                              void* summ) {
   const Params& P = A.P;
   int32_t* tl = P.topk > 0 ? tiles : nullptr;
   hipError_t e;
+  const size_t ub = summaries_bytes(P, batch, A.max_blocks);
   if (A.max_blocks <= kStepTopkSmall) {
     e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s);
+    if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
+  } else if (ub != 0 && summ != nullptr && P.topk > 0) {  // one launch scores and selects
+    Summaries U;
+    U.val = static_cast<float*>(summ);
+    U.id = reinterpret_cast<int32_t*>(static_cast<char*>(summ) + ub);
+    U.phys = reinterpret_cast<int32_t*>(static_cast<char*>(summ) + 2 * ub);
+    e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s, U);
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   } else {
     e = launch_score(P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);

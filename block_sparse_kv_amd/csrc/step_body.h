@@ -12,6 +12,46 @@ namespace kvs {
 
 constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
 
+// The chunk summary of one SEPARATE scoring workgroup (wave 0; chunk = its kChunkBlocks blocks, whose
+// scores are in lds[0..kChunkBlocks) and physical ids in lds[kChunkBlocks..) as ints): the kChunkTop
+// best by (score desc, block asc), written sorted by block, padded with (-inf, -1, 0), coherently to
+// u*[chunk * kChunkTop ..].  Block b0 + i is lane i.
+__device__ inline void write_chunk_summary(const float* lds, int b0, float* uval, int32_t* uid,
+                                           int32_t* uphys) {
+  static_assert(kChunkBlocks == 64, "one block per lane");
+  const int lane = threadIdx.x & 63;
+  float v = lds[lane];
+  const int phys = reinterpret_cast<const int*>(lds)[kChunkBlocks + lane];
+  float rv = -INFINITY;
+  int rb = 0x7FFFFFFF, rp = 0;  // entry r, held by lane r: score, block (invalid: last), physical id
+#pragma unroll
+  for (int r = 0; r < kChunkTop; ++r) {
+    const float mx = wave_max_f32(v);
+    const unsigned long long hit = __ballot(v == mx);
+    const int w = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+    const bool valid = mx != -INFINITY && hit != 0ull;
+    const int pw = __builtin_amdgcn_readlane(phys, w < 0 ? 0 : w);
+    if (lane == r) {
+      rv = valid ? mx : -INFINITY;
+      rb = valid ? b0 + w : 0x7FFFFFFF;
+      rp = valid ? pw : 0;
+    }
+    if (valid && lane == w) v = -INFINITY;
+  }
+  // position of entry r among the kChunkTop by block (invalid entries after the valid ones, by r)
+  int pos = 0;
+#pragma unroll
+  for (int j = 0; j < kChunkTop; ++j) {
+    const int bj = __builtin_amdgcn_readlane(rb, j);
+    pos += (bj < rb || (bj == rb && j < lane)) ? 1 : 0;
+  }
+  if (lane < kChunkTop) {
+    st_coh(uval + pos, rv);
+    st_coh(uid + pos, rb == 0x7FFFFFFF ? -1 : rb);
+    st_coh(uphys + pos, rp);
+  }
+}
+
 // First the scoring workgroups, n_sc per (sequence, group), over every KV head (SHARED) or over one KV
 // head (SEPARATE; group = KV head): dispatched first, their few loads are not queued behind the
 // tiles' stream.  With sel null the kernel only scores and streams the tiles (a selection made by
@@ -19,11 +59,14 @@ constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : 
 // (seq * Hkv + h) * n_il_max + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
-template <int G, int METHOD, int MODE, int KV>
+// SUMM (SEPARATE rows longer than the register selection holds): each scoring workgroup, one chunk of
+// kChunkBlocks blocks, also writes its chunk summary; the last one selects from the summaries
+// (topk_summary_reg) and, if a chunk holds more than kChunkTop of the selection, from the whole row.
+template <int G, int METHOD, int MODE, int KV, bool SUMM = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void score_select_kernel(
     AttnArgs A, const void* __restrict__ rep_pool, float* __restrict__ scores, int32_t* __restrict__ sel,
-    int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int n_sc,
-    int n_il_wg) {
+    int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int ctr_stride,
+    int n_sc, int n_il_wg, float* __restrict__ uval, int32_t* __restrict__ uid, int32_t* __restrict__ uphys) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_last;
   const Params& P = A.P;
@@ -41,60 +84,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int per_seq = P.G * n_sc;
   const int seq = y / per_seq, grp = (y % per_seq) / n_sc, c = y % n_sc;
   const int sb = SEP ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
-  score_blocks_range<G, METHOD, MODE, SEP, true>(P, A.q + (size_t)seq * P.Hq * kDim, rep_pool,
-                                                 A.table + (size_t)seq * A.max_blocks, A.max_blocks,
-                                                 A.seq_lens[seq], c * sb, sb,
+  static_assert(kScoreBlocksPerHeadWg == kChunkBlocks, "a SEPARATE scoring workgroup is one chunk");
+  const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
+  float* lchunk = reinterpret_cast<float*>(smem) + 64;  // SEPARATE scoring leaves the first floats unused
+  score_blocks_range<G, METHOD, MODE, SEP, true>(P, A.q + (size_t)seq * P.Hq * kDim, rep_pool, trow,
+                                                 A.max_blocks, A.seq_lens[seq], c * sb, sb,
                                                  scores + (size_t)seq * P.G * A.max_blocks,
-                                                 reinterpret_cast<float*>(smem), grp);
+                                                 reinterpret_cast<float*>(smem), grp, SUMM ? lchunk : nullptr);
   if (sel == nullptr) return;  // scores and Initial/Local tiles only: the selection comes later
+  const size_t urow = ((size_t)seq * P.G + grp) * n_sc * kChunkTop;  // this group's summaries
+  if constexpr (SUMM) {
+    __syncthreads();  // the chunk's scores are in LDS
+    if (threadIdx.x < 64)
+      write_chunk_summary(lchunk, c * sb, uval + urow + (size_t)c * kChunkTop,
+                          uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
+  }
   wait_mem();
   __syncthreads();
-  int* cp = ctr + (size_t)seq * P.G + grp;
+  int* cp = ctr + ((size_t)seq * P.G + grp) * ctr_stride;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_sc - 1;
   __syncthreads();
   if (!s_last) return;  // else every scoring workgroup of the group has arrived
-  topk_group<256, kStepTopkKeys, true>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table,
-                                       tiles, seq, grp, *reinterpret_cast<TopkLds*>(smem));
+  if constexpr (SUMM) {
+    const size_t row = (size_t)seq * P.G + grp;
+    const Regions rg = regions_of(A.seq_lens[seq], P.initial_len, P.local_len);
+    const int cand_hi = min(rg.cand_hi, A.max_blocks);
+    const int n = max(0, cand_hi - rg.cand_lo);
+    const int k = min(P.topk, n);
+    int32_t* out = sel + row * P.topk;
+    int32_t* tout = tiles ? tiles + row * P.topk : nullptr;
+    TopkLds& S = *reinterpret_cast<TopkLds*>(smem);
+    if (k >= n) {  // every candidate (or none)
+      for (int i = threadIdx.x; i < n; i += 256) {
+        out[i] = rg.cand_lo + i;
+        if (tout) tout[i] = trow[rg.cand_lo + i];
+      }
+    } else if (!(n_sc * kChunkTop <= 1024
+                     ? topk_summary_reg<256, 4>(uval + urow, uid + urow, uphys + urow, n_sc, rg.cand_lo,
+                                                cand_hi, k, S, out, tout, tout != nullptr)
+                     : topk_summary_reg<256, 8>(uval + urow, uid + urow, uphys + urow, n_sc, rg.cand_lo,
+                                                cand_hi, k, S, out, tout, tout != nullptr))) {
+      __syncthreads();
+      topk_select<256, true>(scores + row * A.max_blocks + rg.cand_lo, n, k, rg.cand_lo, S, out, trow, tout);
+    }
+    if (threadIdx.x == 0) sel_count[row] = k;
+    for (int i = k + (int)threadIdx.x; i < P.topk; i += 256) {
+      out[i] = -1;
+      if (tout) tout[i] = -1;
+    }
+  } else {
+    topk_group<256, kStepTopkKeys, true>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table,
+                                         tiles, seq, grp, *reinterpret_cast<TopkLds*>(smem));
+  }
   if (threadIdx.x == 0) st_coh(cp, 0);  // stored last: the selection's barriers would wait for it
 }
 
 template <int G, int METHOD, int KV>
 static void launch_ss_mq(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
-                         int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
-  if (A.P.mode == kSeparate)
+                         int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int ctr_stride, int n_sc, int n_il_wg,
+                         const Summaries& U) {
+  if (U.val)  // SEPARATE long rows (checked by the caller)
+    hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, KV, true>), grid, dim3(256), 0, s, A, reps,
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
+  else if (A.P.mode == kSeparate)
     hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, KV>), grid, dim3(256), 0, s, A, reps,
-                       scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
   else
     hipLaunchKernelGGL((score_select_kernel<G, METHOD, kShared, KV>), grid, dim3(256), 0, s, A, reps,
-                       scores, sel, cnt, tiles, ctr, n_sc, n_il_wg);
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
 }
 
 template <int G, int KV>
 static void launch_ss_g(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
-                        int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int n_sc, int n_il_wg) {
+                        int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int ctr_stride, int n_sc, int n_il_wg,
+                        const Summaries& U) {
   switch (A.P.method) {
-    case kQuest: launch_ss_mq<G, kQuest, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    case kMax: launch_ss_mq<G, kMax, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    case kMean: launch_ss_mq<G, kMean, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    default: launch_ss_mq<G, kFix, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case kQuest: launch_ss_mq<G, kQuest, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
+    case kMax: launch_ss_mq<G, kMax, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
+    case kMean: launch_ss_mq<G, kMean, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
+    default: launch_ss_mq<G, kFix, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
   }
 }
 
 template <int KV>
 hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                                  int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s) {
+                                  int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
+                                  const Summaries& U) {
   const Params& P = A.P;
   const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
   const int n_sc = (A.max_blocks + sb - 1) / sb;
   const int n_il_wg = batch * P.Hkv * A.n_il_max;
   const dim3 grid(n_il_wg + batch * P.G * n_sc);
+  const int cst = step_ctr_stride(batch * P.G);
   switch (P.g) {
-    case 1: launch_ss_g<1, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    case 2: launch_ss_g<2, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    case 4: launch_ss_g<4, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    case 8: launch_ss_g<8, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
-    default: launch_ss_g<16, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, n_sc, n_il_wg); break;
+    case 1: launch_ss_g<1, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
+    case 2: launch_ss_g<2, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
+    case 4: launch_ss_g<4, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
+    case 8: launch_ss_g<8, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
+    default: launch_ss_g<16, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
   }
   return hipGetLastError();
 }

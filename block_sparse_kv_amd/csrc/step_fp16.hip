@@ -3,7 +3,8 @@
 
 namespace kvs {
 template hipError_t launch_score_select_kv<kKvFp16>(const AttnArgs&, const void*, float*, int32_t*, int32_t*,
-                                                int32_t*, int*, int, hipStream_t);
+                                                int32_t*, int*, int, hipStream_t,
+                                                const Summaries&);
 template hipError_t launch_topk_il_wide_kv<kKvFp16>(const AttnArgs&, const float*, int32_t*, int32_t*, int32_t*,
                                                 int, hipStream_t);
 }  // namespace kvs

@@ -9,11 +9,25 @@ namespace kvs {
 constexpr int kStepTopkKeys = 8;  // keys per lane of the 256-lane selections
 constexpr int kStepTopkSmall = 256 * kStepTopkKeys;  // rows up to this many blocks: one fused launch
 
+// Chunk summaries of the long-row selection: [batch][G][chunks][8] scores, block ids and physical ids
+// (all null for the register selection over whole rows).
+struct Summaries {
+  float* val = nullptr;
+  int32_t* id = nullptr;
+  int32_t* phys = nullptr;
+};
+
+// Rows of SEPARATE selections up to this many blocks take the fused launch through chunk summaries
+// (8 summary entries per 64-block chunk, at most 8 per lane of the 256-lane selection).
+constexpr int kStepSummMax = 256 * 8 * 8;
+
 // Scoring, the top-k by the group's last scoring workgroup (sel != nullptr) and the Initial/Local tiles,
-// in one launch (rows of up to kStepTopkSmall blocks).
+// in one launch: rows of up to kStepTopkSmall blocks from the whole score row, longer SEPARATE rows
+// (up to kStepSummMax) from the chunk summaries U.
 template <int KV>
 hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
-                                  int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s);
+                                  int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
+                                  const Summaries& U);
 // Longer rows: the top-k selections (512-lane workgroups) and the Initial/Local tiles in one launch.
 template <int KV>
 hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,

@@ -109,8 +109,9 @@ __device__ inline uint32_t radix_select(KeyFn key, int n, int& rem, TopkLds& S) 
 
 // Selects the top k of the n candidate scores row[0..n) (candidate i is logical block cand_lo + i),
 // reading the scores again on every pass.  Writes sel[0..k) ascending; if tiles != nullptr also
-// tiles[i] = trow[sel[i]] (physical ids).
-template <int NT>
+// tiles[i] = trow[sel[i]] (physical ids).  COH: the scores were stored by other workgroups of the same
+// kernel (st_coh) and are read with coherent loads.
+template <int NT, bool COH = false>
 __device__ __attribute__((noinline)) void topk_select(const float* row, int n, int k, int cand_lo,
                                                       TopkLds& S, int32_t* sel, const int32_t* trow,
                                                       int32_t* tiles) {
@@ -124,7 +125,11 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
   k = __builtin_amdgcn_readfirstlane(k);
   cand_lo = __builtin_amdgcn_readfirstlane(cand_lo);
   auto put = [&](int32_t* p, int32_t v) { *p = v; };
-  auto score = [&](int i) -> float { return row[i]; };
+  const __amdgpu_buffer_rsrc_t rs = coh_rsrc(row);
+  auto score = [&](int i) -> float {
+    if constexpr (COH) return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4, 0, kSc1));
+    else return row[i];
+  };
   if (k <= 0) return;
   if (k >= n) {
     for (int i = tid; i < n; i += NT) {
@@ -261,69 +266,26 @@ __device__ __attribute__((noinline)) void topk_select(const float* row, int n, i
   }
 }
 
-// Register-resident selection of one (sequence, group) whose score row row[0..m) fits NT * KPT keys:
-// lane l of wave w holds indices w*64*KPT + 64*c + l (c < KPT).  The row, the table row (trow,
-// nullable) and *len are loaded together; candidates are the indices in [cand_lo, cand_hi) of the
-// length's regions.  Writes *cnt = k_eff, sel[0..k_eff) ascending (and tiles[] = their physical ids
-// when trow != nullptr), -1 in sel / tiles [k_eff, topk).  COH: the scores were stored by another
-// workgroup of the same kernel (st_coh) and are read with coherent loads.
+// ---- register-resident selection ------------------------------------------------------------------
+// Keys live in registers: lane l of wave w holds positions w*64*KPT + 64*c + l (c < KPT), so each wave
+// owns a contiguous position range and ballots over its columns, in (column, lane) order, visit its
+// positions in ascending order.
 //
-// Each candidate's value bin stays in a register, so only the histogram goes through LDS.  Every wave
-// reads the whole histogram and finds the boundary bin itself (DPP prefix sum; no barrier waits on
-// one wave's search).  A boundary bin of at most kBndMax keys -- the usual case -- is gathered and
-// ranked by (key, lower index first) in one wave, which marks the rem it takes in a bitmap and gives
-// every wave its output offset; a crowded one goes through a radix select of the k-th key.  Each wave
-// owns a contiguous index range, so ballots over its columns write the selection in ascending order.
-template <int NT, int KPT, bool COH = false>
-__device__ __forceinline__ void topk_group_reg(const float* row, int m, const int32_t* len,
-                                                int initial_len, int local_len, int topk,
-                                                TopkLds& S, int32_t* sel_, int32_t* cnt_,
-                                                const int32_t* trow, int32_t* tiles_) {
-  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
-  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per block");
+// topk_reg_take: the top k (1 <= k < number of candidates) of the candidate positions (bit c of okb
+// set) by (value desc, position asc).  Each candidate's value bin stays in a register, so only the
+// histogram goes through LDS.  Every wave reads the whole histogram and finds the boundary bin itself
+// (DPP prefix sum; no barrier waits on one wave's search).  The keys of the bins above it are taken.
+// When every key of the boundary bin is needed (the usual case: value bins are sparse near the k-th
+// key) they are taken too; a boundary bin of at most kBndMax keys is otherwise gathered and ranked by
+// (key, lower position first) in one wave, which marks the ones it takes in a bitmap; a crowded one
+// goes through a radix select of the k-th key.  Returns the take bits of the lane's keys (bit c) and,
+// in *off, the output slot of the wave's first taken key.
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t topk_reg_take(const float (&v)[KPT], uint32_t okb, int k, int ibase,
+                                                  TopkLds& S, int* off_out) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  auto sel = gptr(sel_);
-  auto cnt = gptr(cnt_);
-  auto tiles = gptr(tiles_);
-  const bool with_tiles = trow != nullptr;
-  const int ibase = wv * 64 * KPT + lane;
-  const __amdgpu_buffer_rsrc_t rs = span_rsrc(row, m * 4);
-  const __amdgpu_buffer_rsrc_t rt = span_rsrc(trow, with_tiles ? m * 4 : 0);
-  float v[KPT];
-  int32_t ph[KPT];
-#pragma unroll
-  for (int c = 0; c < KPT; ++c)
-    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (ibase + 64 * c) * 4, 0,
-                                                                          COH ? kSc1 : 0));
-#pragma unroll
-  for (int c = 0; c < KPT; ++c) ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, (ibase + 64 * c) * 4, 0, 0);
-  const Regions rg = regions_of(ld_uniform_i32(len), initial_len, local_len);
-  const int lo = rg.cand_lo, hi = min(rg.cand_hi, m);
-  const int n = max(0, hi - lo);
-  const int k = min(topk, n);
-  // The count and the -1 padding are stored after the last barrier: a barrier waits for every store
-  // the wave has issued.
-  auto finish = [&]() {
-    if (tid == 0) *cnt = k;
-    for (int i = k + tid; i < topk; i += NT) {
-      sel[i] = -1;
-      if (with_tiles) tiles[i] = -1;
-    }
-  };
-  if (k <= 0) { finish(); return; }
-  const int d = ibase - lo;  // candidate offset of column 0
-  auto ok = [&](int c) { return (unsigned)(d + 64 * c) < (unsigned)n; };
-  if (k >= n) {  // every candidate
-    finish();
-#pragma unroll
-    for (int c = 0; c < KPT; ++c)
-      if (ok(c)) {
-        sel[d + 64 * c] = ibase + 64 * c;
-        if (with_tiles) tiles[d + 64 * c] = ph[c];
-      }
-    return;
-  }
+  auto ok = [&](int c) { return ((okb >> c) & 1u) != 0u; };
 
   // ---- value range of the candidates ----
   float vl = INFINITY, vh = -INFINITY;
@@ -336,7 +298,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   vh = wave_max_f32(vh);
   if (lane == 0) { S.fmin[wv] = vl; S.fmax[wv] = vh; }
   for (int i = tid; i < kBins + 4; i += NT) S.hist[i] = 0;
-  for (int i = tid; i < (m + 31) / 32; i += NT) S.bmap[i] = 0u;
+  for (int i = tid; i < NT * KPT / 32; i += NT) S.bmap[i] = 0u;
   if (tid == 0) S.cur = 0;
   __syncthreads();
   float fl = S.fmin[0], fh = S.fmax[0];
@@ -387,40 +349,29 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   }
   const int rem = k - above;  // keys still to take from the boundary bin, 1..m_sub
   const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t take = 0u;
 
   if (rem == m_sub) {
-    // ---- the whole boundary bin is taken (typical: value bins are sparse near the k-th key), so the
-    // keys of bin >= bstar are the selection: no ranking ----
+    // ---- the whole boundary bin is taken: the keys of bins >= bstar are the selection ----
     int n_ge = 0;
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) n_ge += __popcll(__ballot(b[c] >= bstar));
+    for (int c = 0; c < KPT; ++c) {
+      take |= (b[c] >= bstar ? 1u : 0u) << c;
+      n_ge += __popcll(__ballot(b[c] >= bstar));
+    }
     if (lane == 0) S.wgt[wv] = n_ge;
     __syncthreads();
     int off = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) off += w < wv ? S.wgt[w] : 0;
-    finish();
-#pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const bool take = b[c] >= bstar;
-      const unsigned long long km = __ballot(take);
-      if (km != 0ull) {
-        const int slot = off + __popcll(km & lt);
-        if (take && slot < k) {
-          sel[slot] = ibase + 64 * c;
-          if (with_tiles) tiles[slot] = ph[c];
-        }
-        off += __popcll(km);
-      }
-    }
-    return;
+    *off_out = off;
+    return take;
   }
 
   if (m_sub <= kBndMax) {
     // ---- keys of higher bins are all taken: each wave counts its own; the boundary bin's keys are
-    // gathered for ranking ----
-    // The wave's boundary keys take one range of bcomp: a prefix sum over lanes places each lane's keys,
-    // and one LDS atomic per wave places the wave.
+    // gathered for ranking.  The wave's boundary keys take one range of bcomp: a prefix sum over lanes
+    // places each lane's keys, and one LDS atomic per wave places the wave. ----
     int n_above = 0, nb = 0;
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
@@ -441,7 +392,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     if (lane == 0) S.wgt[wv] = n_above;
     __syncthreads();
     if (wv == 0) {
-      // rank of each boundary key: how many beat it (higher key, or equal and lower index); the best
+      // rank of each boundary key: how many beat it (higher key, or equal and lower position); the best
       // rem are taken and marked in the bitmap, and every wave gets its output offset
       const bool mine = lane < m_sub;
       const unsigned long long cj = S.bcomp[mine ? lane : 0];
@@ -452,13 +403,13 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
         r += (c2.x > cj) + (x + 1 < m_sub && c2.y > cj);
       }
       const int wj = (int)(~(uint32_t)cj) / (64 * KPT);
-      const bool take = mine && r < rem;
+      const bool tk = mine && r < rem;
       const int ij = (int)~(uint32_t)cj;
-      if (take) atomicOr(&S.bmap[ij >> 5], 1u << (ij & 31));
+      if (tk) atomicOr(&S.bmap[ij >> 5], 1u << (ij & 31));
       int bsel = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const int cw = __popcll(__ballot(take && wj == w));
+        const int cw = __popcll(__ballot(tk && wj == w));
         bsel = lane == w ? cw : bsel;
       }
       const int tot = lane < NW ? S.wgt[lane] + bsel : 0;
@@ -466,29 +417,15 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
       if (lane < NW) S.woff[lane] = incl - tot;
     }
     __syncthreads();
-    finish();
-    // ---- ascending order: wave by wave, column by column, lane by lane ----
-    // Key ibase + 64c is bit (lane & 31) of bitmap word (ibase >> 5) + 2c: the words are read together,
-    // and nothing below waits inside the loop.
-    int off = S.woff[wv];
+    // Key ibase + 64c is bit (lane & 31) of bitmap word (ibase >> 5) + 2c: the words are read together.
     uint32_t wd[KPT];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) wd[c] = S.bmap[(ibase >> 5) + 2 * c];
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const int i = ibase + 64 * c;
-      const bool take = b[c] > bstar || (b[c] == bstar && ((wd[c] >> (lane & 31)) & 1u));
-      const unsigned long long km = __ballot(take);
-      if (km != 0ull) {
-        const int slot = off + __popcll(km & lt);
-        if (take && slot < k) {
-          sel[slot] = i;
-          if (with_tiles) tiles[slot] = ph[c];
-        }
-        off += __popcll(km);
-      }
-    }
-    return;
+    for (int c = 0; c < KPT; ++c)
+      take |= (b[c] > bstar || (b[c] == bstar && ((wd[c] >> (lane & 31)) & 1u)) ? 1u : 0u) << c;
+    *off_out = S.woff[wv];
+    return take;
   }
 
   // ---- a crowded boundary bin: radix select of the k-th key inside the boundary bin ----
@@ -531,7 +468,7 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     __syncthreads();
   }
   const uint32_t T = prefix;  // the k-th largest key: keys of higher bins, keys > T of the boundary
-                              // bin and the remT lowest-indexed keys == T are taken
+                              // bin and the remT lowest-positioned keys == T are taken
   auto gt = [&](int c) { return b[c] > bstar || (b[c] == bstar && key(c) > T); };
   auto eq = [&](int c) { return b[c] == bstar && key(c) == T; };
   int n_gt = 0, n_eq = 0;
@@ -552,21 +489,159 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
     eq_before += (4 * q < wv ? e4.x : 0) + (4 * q + 1 < wv ? e4.y : 0) + (4 * q + 2 < wv ? e4.z : 0) +
                  (4 * q + 3 < wv ? e4.w : 0);
   }
-  int pos = gt_before + min(eq_before, remT);
-  finish();
+  *off_out = gt_before + min(eq_before, remT);
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     const unsigned long long eqm = __ballot(eq(c));
-    const bool keep = gt(c) || (eq(c) && eq_before + __popcll(eqm & lt) < remT);
-    const unsigned long long km = __ballot(keep);
-    const int slot = pos + __popcll(km & lt);
-    if (keep && slot < k) {
-      sel[slot] = ibase + 64 * c;
-      if (with_tiles) tiles[slot] = ph[c];
-    }
-    pos += __popcll(km);
+    take |= (gt(c) || (eq(c) && eq_before + __popcll(eqm & lt) < remT) ? 1u : 0u) << c;
     eq_before += __popcll(eqm);
   }
+  return take;
+}
+
+// Writes the taken keys in ascending position order from slot `off` of the wave on: sel[slot] = the
+// key's id (its position, or idv[c]), tiles[slot] = ph[c] when with_tiles.
+template <int KPT>
+__device__ __forceinline__ void topk_reg_write(uint32_t take, int off, int k, int ibase, const int32_t (&idv)[KPT],
+                                               bool use_ids, const int32_t (&ph)[KPT], bool with_tiles,
+                                               __attribute__((address_space(1))) int32_t* sel,
+                                               __attribute__((address_space(1))) int32_t* tiles) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool t = (take >> c) & 1u;
+    const unsigned long long km = __ballot(t);
+    if (km != 0ull) {
+      const int slot = off + __popcll(km & lt);
+      if (t && slot < k) {
+        sel[slot] = use_ids ? idv[c] : ibase + 64 * c;
+        if (with_tiles) tiles[slot] = ph[c];
+      }
+      off += __popcll(km);
+    }
+  }
+}
+
+// Register-resident selection of one (sequence, group) whose score row row[0..m) fits NT * KPT keys.
+// The row, the table row (trow, nullable) and *len are loaded together; candidates are the indices in
+// [cand_lo, cand_hi) of the length's regions.  Writes *cnt = k_eff, sel[0..k_eff) ascending (and
+// tiles[] = their physical ids when trow != nullptr), -1 in sel / tiles [k_eff, topk).  COH: the
+// scores were stored by another workgroup of the same kernel (st_coh) and are read with coherent
+// loads.  The count and the -1 padding are stored after the last barrier (a barrier waits for every
+// store the wave has issued).
+template <int NT, int KPT, bool COH = false>
+__device__ __forceinline__ void topk_group_reg(const float* row, int m, const int32_t* len,
+                                                int initial_len, int local_len, int topk,
+                                                TopkLds& S, int32_t* sel_, int32_t* cnt_,
+                                                const int32_t* trow, int32_t* tiles_) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per block");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto sel = gptr(sel_);
+  auto cnt = gptr(cnt_);
+  auto tiles = gptr(tiles_);
+  const bool with_tiles = trow != nullptr;
+  const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc(row, m * 4);
+  const __amdgpu_buffer_rsrc_t rt = span_rsrc(trow, with_tiles ? m * 4 : 0);
+  float v[KPT];
+  int32_t ph[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c)
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (ibase + 64 * c) * 4, 0,
+                                                                          COH ? kSc1 : 0));
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, (ibase + 64 * c) * 4, 0, 0);
+  const Regions rg = regions_of(ld_uniform_i32(len), initial_len, local_len);
+  const int lo = rg.cand_lo, hi = min(rg.cand_hi, m);
+  const int n = max(0, hi - lo);
+  const int k = min(topk, n);
+  auto finish = [&]() {
+    if (tid == 0) *cnt = k;
+    for (int i = k + tid; i < topk; i += NT) {
+      sel[i] = -1;
+      if (with_tiles) tiles[i] = -1;
+    }
+  };
+  if (k <= 0) { finish(); return; }
+  const int d = ibase - lo;  // candidate offset of column 0
+  uint32_t okb = 0u;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) okb |= ((unsigned)(d + 64 * c) < (unsigned)n ? 1u : 0u) << c;
+  const int32_t none[KPT] = {};
+  if (k >= n) {  // every candidate
+    finish();
+#pragma unroll
+    for (int c = 0; c < KPT; ++c)
+      if ((okb >> c) & 1u) {
+        sel[d + 64 * c] = ibase + 64 * c;
+        if (with_tiles) tiles[d + 64 * c] = ph[c];
+      }
+    return;
+  }
+  int off = 0;
+  const uint32_t take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
+  finish();
+  topk_reg_write<KPT>(take, off, k, ibase, none, false, ph, with_tiles, sel, tiles);
+}
+
+// Selection from chunk summaries.  The candidates of the row are cut into chunks of kChunkBlocks
+// blocks, chunk c covering blocks [c * kChunkBlocks, (c + 1) * kChunkBlocks); each chunk's scorer wrote
+// its kChunkTop best candidates -- (score, block, physical id), best by (score desc, block asc) --
+// sorted by block, padded with (-inf, -1, 0), as uval / uid / uphys[c * kChunkTop + e].  The top k of
+// the row are the top k of these entries unless some chunk holds more than kChunkTop of them: that is
+// the case exactly when every entry of a chunk with more than kChunkTop candidates is taken, which is
+// checked.  The entries are in ascending block order, so the selection is written as it is taken.
+// Returns false, having written nothing, when a chunk overflows (the caller selects from the row).
+template <int NT, int KPT>
+__device__ __forceinline__ bool topk_summary_reg(const float* uval, const int32_t* uid, const int32_t* uphys,
+                                                 int n_chunks, int cand_lo, int cand_hi, int k, TopkLds& S,
+                                                 int32_t* sel_, int32_t* tiles_, bool with_tiles) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per entry");
+  static_assert(kChunkTop == 8, "a chunk is one byte of a ballot");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto sel = gptr(sel_);
+  auto tiles = gptr(tiles_);
+  const int m = n_chunks * kChunkTop;
+  const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rv = span_rsrc(uval, m * 4);
+  const __amdgpu_buffer_rsrc_t ri = span_rsrc(uid, m * 4);
+  const __amdgpu_buffer_rsrc_t rp = span_rsrc(uphys, m * 4);
+  float v[KPT];
+  int32_t id[KPT], ph[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, (ibase + 64 * c) * 4, 0, kSc1));
+    id[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (ibase + 64 * c) * 4, 0, kSc1);
+    ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (ibase + 64 * c) * 4, 0, kSc1);
+  }
+  uint32_t okb = 0u;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) okb |= (ibase + 64 * c < m ? 1u : 0u) << c;
+  int off = 0;
+  const uint32_t take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
+  // overflow: a chunk (8 consecutive lanes of one column) with every entry taken and more than
+  // kChunkTop candidates
+  bool ovf = false;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const unsigned long long km = __ballot((take >> c) & 1u);
+    const int pos = ibase + 64 * c;
+    if ((lane & 7) == 0 && pos < m && ((km >> lane) & 0xFFull) == 0xFFull) {
+      const int ch = pos / kChunkTop;
+      const int n_in = min(cand_hi, (ch + 1) * kChunkBlocks) - max(cand_lo, ch * kChunkBlocks);
+      ovf = ovf || n_in > kChunkTop;
+    }
+  }
+  if (tid == 0) S.bcast[0] = 0;
+  __syncthreads();
+  if (__ballot(ovf) != 0ull && lane == 0) S.bcast[0] = 1;
+  __syncthreads();
+  if (S.bcast[0] != 0) return false;
+  topk_reg_write<KPT>(take, off, k, ibase, id, true, ph, with_tiles, sel, tiles);
+  return true;
 }
 
 // The selection of group grp of sequence seq from the scores [batch][G][max_blocks]: sel (and, with a

@@ -320,6 +320,10 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
  *   scoring workgroup of the group that finishes last, and the Initial/Local tiles' attention (they
  *   do not depend on the selection);  2. attention over the selected tiles;  3. the log-sum-exp
  *   merge into out;
+ *   SEPARATE with 2048 < max_blocks_per_seq <= 16384 and topk > 0, the same three launches, where
+ *   each scoring workgroup (64 blocks of one KV head) also stores its 8 best blocks and the last one
+ *   selects from these summaries; when a chunk of 64 blocks holds more than 8 of the selection
+ *   (the summaries cannot tell which), it selects from the whole score row instead;
  *   otherwise four: 1. scoring;  2. top-k, with the Initial/Local tiles' attention;  3. attention
  *   over the selected tiles;  4. the merge.
  * Top-k also resolves the selected blocks' physical ids.

@@ -106,6 +106,11 @@ SMALL = [
     (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),       # long rows (> 2048 blocks)
     (16, 1, 128, 1024, 20, "quest", "separate", 1, [280000]),    # long rows, g = 16
     (8, 8, 128, 1024, 8000, "quest", "separate", 1, [8192, 300]),  # topk past the one-wave merge's LDS
+    # long SEPARATE rows: selection from the 64-block chunks' summaries in the scoring launch
+    (32, 8, 128, 4096, 64, "quest", "separate", 1, [2200 * 128 + 77, 3000 * 128, 2100 * 128 + 1]),
+    (8, 4, 100, 900, 33, "max", "separate", 1, [4500 * 128 + 3]),
+    (16, 16, 0, 0, 130, "fix", "separate", 8, [2049 * 128, 2600 * 128]),  # chunk 0 holds candidates
+    (8, 8, 128, 2048 * 128, 64, "quest", "separate", 1, [2100 * 128 + 9]),  # k >= candidates
 ]
 
 
@@ -223,6 +228,41 @@ def test_exact_ties_take_lower_index():
         grp = scores[0, h, 10:21]
         assert torch.all(grp == grp[0]), f"tie group not bitwise equal for head {h}"
         assert sel[0, h].tolist() == [10, 11, 12, 13, 14], (h, sel[0, h].tolist())
+
+
+@pytest.mark.parametrize("mode", ["hot", "flat"])
+def test_long_row_chunk_overflow(mode):
+    """A long SEPARATE row whose selection piles into one 64-block chunk (hot: 30 planted blocks inside
+    blocks 128..191 with k = 20; flat: every key of that chunk shifted far above the rest with k = 40),
+    so the chunk summaries cannot hold it and the selection falls back to the whole row: the result
+    still equals the oracle's."""
+    c = cfg_of(16, 4, 128, 1024, 20 if mode == "hot" else 40, "quest", "separate")
+    L = 2300 * B + 11
+    say(f"[case] long-row chunk overflow ({mode}) L={L} k={c.topk}")
+    s = kvsynth.make_sequence(kvsynth.mix_seed(95, mode == "hot"), L, 16, 4, 128, B,
+                              hot_range=(128, 192), n_hot=30 if mode == "hot" else 0, device=DEV)
+    if mode == "flat":
+        u = kvsynth.query_directions(s.q, 4).to(DEV)
+        s.K[128 * B:192 * B] = (s.K[128 * B:192 * B].float() + 3.0 * u[None]).half()
+    pb = kvsynth.page_batch([s], B, shuffle_seed=19, device=DEV)
+    rp = ops.alloc_rep_pool(c, pb.k_pool.shape[0], DEV)
+    ops.build_reps(c, pb.k_pool, pb.block_table[0, : L // B].cpu(), rp)
+    out, sel, cnt = ops.decode_step(c, pb.q, pb.k_pool, pb.v_pool, rp, pb.block_table, pb.seq_lens)
+    torch.cuda.synchronize()
+    r = orc.decode_step(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy(), B=B,
+                        initial_len=128, local_len=1024, topk=c.topk, method="quest")
+    in_chunk = 0
+    for h in range(4):
+        check_selection(sel[0, h].cpu().numpy(), cnt[0, h].item(), r["scores"][h], r["cand"], c.topk,
+                        f"overflow sel h{h}")
+        in_chunk = max(in_chunk, sum(1 for b in r["sel"][h] if 128 <= b < 192))
+    assert in_chunk > 8, f"the case does not overflow a chunk summary ({in_chunk} in the chunk)"
+    gsel = [[int(x) for x in sel[0, h, : int(cnt[0, h])].cpu()] for h in range(4)]
+    toks = [orc.attended_tokens(L, B, r["init_end"], r["local_start"], gsel[j // 4]) for j in range(16)]
+    ref = orc.attention(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy(), toks)
+    err = np.abs(out[0].double().cpu().numpy() - ref).max()
+    say(f"[ok] long-row chunk overflow ({mode}): {in_chunk} selected blocks in one chunk, max err {err:.2e}")
+    assert err <= 2e-3
 
 
 def test_deterministic_and_split_invariant():
