@@ -230,7 +230,7 @@ class Setup:
         self.kvs = kvs
         if "presel" in w:
             self.pws_bytes = kvs.kvs_decode_step_preselected_workspace_size(self.cfg, 1, nb, w["presel"])
-            self.pws = torch.empty(self.pws_bytes, dtype=torch.uint8, device=device)
+            self.pws = torch.zeros(self.pws_bytes, dtype=torch.uint8, device=device)  # counters start at 0
 
     @property
     def cycle(self):
@@ -265,15 +265,19 @@ class Setup:
         """One decode step (all layers) on cache replica `replica`."""
         w = self.w
         for layer in range(w["layers"]):
-            u = replica * w["layers"] + layer
-            q, kp, vp, rp = self.units[u]
-            if self.presel:
-                self.kvs.kvs_decode_step_preselected(self.cfg, q, kp, vp, rp, self.table, self.nb,
-                                                     self.lens, 1, self.presel[u], w["presel"], self.out,
-                                                     self.sel, self.cnt, self.pws, self.pws_bytes)
-            else:
-                self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
-                                         self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
+            self.step_unit(replica * w["layers"] + layer)
+
+    def step_unit(self, u):
+        """The decode step of one layer: cache unit u."""
+        w = self.w
+        q, kp, vp, rp = self.units[u]
+        if self.presel:
+            self.kvs.kvs_decode_step_preselected(self.cfg, q, kp, vp, rp, self.table, self.nb,
+                                                 self.lens, 1, self.presel[u], w["presel"], self.out,
+                                                 self.sel, self.cnt, self.pws, self.pws_bytes)
+        else:
+            self.kvs.kvs_decode_step(self.cfg, q, kp, vp, rp, self.table, self.nb, self.lens, 1,
+                                     self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
 
     def prepare_reuse(self):
         """Selection reuse (a later token or layer attends with an earlier selection): keep each
@@ -746,6 +750,107 @@ def summarize_pmc(fetch_dir, write_dir, name):
     print(path)
 
 
+TL_KINDS = ("scoring+selection: scoring workgroups", "scoring+selection: Initial/Local tiles",
+            "top-k launch: Initial/Local tiles", "attention: selected tiles", "merge",
+            "top-k launch: selections", "scoring launch", "top-k launch (own)", "compaction", "map back")
+TL_LAUNCH = {0: "scoring+selection", 1: "scoring+selection", 2: "top-k", 5: "top-k", 3: "attention",
+             4: "merge", 6: "scoring", 7: "top-k (own)", 8: "compaction", 9: "map back"}
+TL_MARKS = {1: "operands in / scores stored", 2: "done / counter bumped", 3: "selection stored",
+            4: "chunk summary stored"}
+TL_MAX_WG, TL_SLOTS = 16384, 8
+
+
+def timeline(name, device, replays=9, keep=5):
+    """Per-workgroup timeline of the last layer step of `name`'s timed cycle (the same graph-replayed
+    cycle of steps over the cache replicas as the timed runs, so the layer's data is as cold as
+    there), from the timeline library (KVS_LIBRARY=timeline): for each kind of workgroup its start
+    and marks (min / median / max over workgroups, us from the layer's first workgroup start), and
+    per launch its first start, last mark and the gap to the launch before.  Each figure is the
+    median over the last `keep` of `replays` replays.  Returns the summary's text lines."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_amd as kvs
+    from block_sparse_kv_amd import binding
+
+    if not binding.TIMELINE:
+        raise SystemExit("--timeline needs the timeline library: python block_sparse_kv_amd/build.py "
+                         "--timeline, then KVS_LIBRARY=timeline python bench.py --timeline ...")
+    n_kinds = len(TL_KINDS)
+    buf = torch.zeros(n_kinds * TL_MAX_WG * TL_SLOTS, dtype=torch.int64, device=device)
+    kvs.kvs_timeline_set(buf)  # read by every later call's configuration
+    mixed = "batch" in WORKLOADS[name]
+    st = MixedSetup(name, device) if mixed else Setup(name, device)
+    for i in range(st.cycle):
+        st.step(i)
+    torch.cuda.synchronize()
+    g = _capture(st.step, range(st.cycle))
+    per_replay = []
+    for _ in range(replays):
+        buf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rec = buf.view(n_kinds, TL_MAX_WG, TL_SLOTS).cpu().numpy().view(np.uint64).astype(np.float64)
+        t0 = min(rec[k][rec[k][:, 0] > 0, 0].min() for k in range(n_kinds) if (rec[k][:, 0] > 0).any())
+        vals = {}
+        for k in range(n_kinds):
+            r = rec[k][rec[k][:, 0] > 0]
+            if not len(r):
+                continue
+            vals[(k, "n")] = len(r)
+            us = lambda a: (a - t0) / 100.0  # 100 MHz ticks -> us
+            for slot in (0, 1, 2, 3, 4):
+                a = r[:, slot]
+                a = a[a > 0]
+                if len(a):
+                    vals[(k, slot)] = (us(a.min()), us(np.median(a)), us(a.max()))
+            marks = r[:, 1:5]
+            vals[(k, "end")] = us(marks[marks > 0].max()) if (marks > 0).any() else us(r[:, 0].max())
+        per_replay.append(vals)
+    kvs.kvs_timeline_set(None)
+    last = per_replay[-keep:]
+    keys = [k for k in last[-1] if all(k in v for v in last)]
+    med = {}
+    for key in keys:
+        xs = [v[key] for v in last]
+        med[key] = tuple(statistics.median(x[i] for x in xs) for i in range(3)) if isinstance(xs[0], tuple) \
+            else statistics.median(xs)
+    f3 = lambda t: f"{t[0]:6.2f} {t[1]:6.2f} {t[2]:6.2f}"
+    lines = [f"workload: {name}",
+             f"layer_step: the last {'batch step' if mixed else 'layer step'} of a graph-replayed cycle of "
+             f"{st.cycle} steps ({WORKLOADS[name]['layers']} layers each), as in the timed runs",
+             f"replays: {replays} (medians over the last {keep})",
+             f"source_hash: {source_hash()}",
+             "command: python block_sparse_kv_amd/build.py --timeline && "
+             f"KVS_LIBRARY=timeline python bench.py --timeline {name}",
+             "",
+             "# workgroup kinds: start and marks, us from the layer's first workgroup start (min / median / max)"]
+    kinds = sorted({k for k, _ in keys}, key=lambda k: med[(k, 0)][0])
+    for k in kinds:
+        lines.append(f"| {TL_KINDS[k]:40s} | n {int(med[(k, 'n')]):5d} | start {f3(med[(k, 0)])} |")
+        for slot in (1, 4, 2, 3):
+            if (k, slot) in med:
+                lines.append(f"|   {TL_MARKS[slot]:38s} |         | {'':5s} {f3(med[(k, slot)])} |")
+    lines += ["", "# launches: first workgroup start, last mark, span, gap after the launch before (us)"]
+    launches = {}
+    for k in kinds:
+        L = TL_LAUNCH[k]
+        s0, e0 = med[(k, 0)][0], med[(k, "end")]
+        a, b = launches.get(L, (s0, e0))
+        launches[L] = (min(a, s0), max(b, e0))
+    prev_end = None
+    for L, (a, b) in sorted(launches.items(), key=lambda x: x[1][0]):
+        gap = f"{a - prev_end:6.2f}" if prev_end is not None else "     -"
+        lines.append(f"| {L:20s} | start {a:6.2f} | end {b:6.2f} | span {b - a:6.2f} | gap {gap} |")
+        prev_end = b
+    lines.append(f"layer: {prev_end:.2f} us from the first workgroup start to the last mark "
+                 "(the timeline build waits for loads at mark 1, so it runs a little slower than the default build)")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -760,7 +865,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs -> profiles/")
     ap.add_argument("--log", help="bench output captured under the profiler (for --summarize-stats)")
+    ap.add_argument("--timeline", metavar="WORKLOAD", choices=list(WORKLOADS),
+                    help="per-workgroup timeline of one layer's step (timeline library) -> profiles/")
     args = ap.parse_args()
+    if args.timeline:
+        lines = timeline(args.timeline, "cuda:0")
+        path = os.path.join(ROOT, "profiles", f"decode_step_{args.timeline}_timeline.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        print(path)
+        return
     if args.summarize_stats or args.summarize_pmc:
         if args.workload == "all":
             ap.error("--summarize-* needs --workload")

@@ -11,11 +11,17 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvs.so")
+# KVS_LIBRARY=timeline loads the variant with per-workgroup timeline records (build.py --timeline)
+_VARIANTS = {"": ("libkvs.so", ""), "timeline": ("libkvs_timeline.so", " --timeline")}
+_variant = os.environ.get("KVS_LIBRARY", "")
+if _variant not in _VARIANTS:
+    raise ImportError(f"KVS_LIBRARY={_variant!r}: expected unset or 'timeline'")
+LIB_PATH = os.path.join(HERE, _VARIANTS[_variant][0])
+TIMELINE = _variant == "timeline"
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python block_sparse_kv_amd/build.py` "
-                      "(or __graft_entry__.build()) first")
+    raise ImportError(f"{LIB_PATH} is not built: run `python block_sparse_kv_amd/build.py"
+                      f"{_VARIANTS[_variant][1]}` (or __graft_entry__.build()) first")
 # torch must be loaded first: its bundled HIP runtime has the SONAME libamdhip64.so.7 that libkvs
 # needs, so the loader binds libkvs to that same runtime.  Loading libkvs first would bring in a
 # second HIP runtime, and torch's streams and device memory would mean nothing to it.
@@ -309,3 +315,15 @@ def kvs_decode_step_noalloc(cfg, q, k_pool, v_pool, rep_pool, block_table, max_b
                                       _ptr(block_table), max_blocks_per_seq, _ptr(seq_lens), batch,
                                       _ptr(out), _ptr(sel_out), _ptr(sel_count_out), _stream(stream))
     return _check(st, "kvs_decode_step_noalloc") if check else st
+
+
+if TIMELINE:
+    _lib.kvs_timeline_set.restype = None
+    _lib.kvs_timeline_set.argtypes = [_P]
+
+
+def kvs_timeline_set(records):
+    """Timeline library only: the device record array later calls write into (None stops)."""
+    if not TIMELINE:
+        raise RuntimeError("kvs_timeline_set needs the timeline library (KVS_LIBRARY=timeline)")
+    _lib.kvs_timeline_set(_ptr(records))

@@ -1,6 +1,9 @@
 """Build libkvs.so in-tree with hipcc for gfx950.
 
-    python block_sparse_kv_amd/build.py
+    python block_sparse_kv_amd/build.py              # libkvs.so
+    python block_sparse_kv_amd/build.py --timeline   # libkvs_timeline.so: the same library with
+                                                     # per-workgroup timeline records (-DKVS_TIMELINE),
+                                                     # loaded when KVS_LIBRARY=timeline
 
 Every .hip / .cpp file under csrc/ is compiled to an object of its own (in parallel, under _build/)
 and the objects are linked into one shared library next to this file.  Packed-fp32 instructions are
@@ -19,6 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvs.so")
+LIB_TIMELINE = os.path.join(HERE, "libkvs_timeline.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -40,14 +44,18 @@ def _run(cmd):
     return r.returncode, err
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source into libkvs.so (always recompiles); returns the library path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = True, timeline: bool = False) -> str:
+    """Compile every source into libkvs.so, or with timeline into libkvs_timeline.so (always
+    recompiles); returns the library path."""
+    obj_dir = OBJ + ("_timeline" if timeline else "")
+    lib = LIB_TIMELINE if timeline else LIB
+    os.makedirs(obj_dir, exist_ok=True)
     inc = ["-I", os.path.join(HERE, "..", "include")]
+    defs = ["-DKVS_TIMELINE"] if timeline else []
     jobs = []
     for src in sources():
-        obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-        jobs.append((src, obj, [HIPCC, *FLAGS, *inc, "-c", src, "-o", obj]))
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        jobs.append((src, obj, [HIPCC, *FLAGS, *defs, *inc, "-c", src, "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     if verbose:
         print(f"hipcc {' '.join(FLAGS)} -c <each of {len(jobs)} sources> ({workers} jobs)", flush=True)
@@ -58,14 +66,14 @@ def build(verbose: bool = True) -> str:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({rc}):\n{err}")
         if err.strip() and verbose:
             print(err, flush=True)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     rc, err = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[1] for j in jobs]])
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{err}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

@@ -31,10 +31,12 @@ constexpr int kMergeWaveLds = 65536;
 __global__ __launch_bounds__(128) void merge_wave_kernel(AttnArgs A, int n_items) {
   extern __shared__ __attribute__((aligned(16))) float wlds[];
   const int item = blockIdx.x * 2 + (threadIdx.x >> 6);
+  KVS_TL_BEGIN(A.P, kTlMerge, 128)
   if (item >= n_items) return;
   constexpr int C = kDim / kMergeChWave;
   const int c = item % C, j = (item / C) % A.P.Hq, seq = item / (C * A.P.Hq);
   merge_item_wave(A, j, c, seq, wlds + (threadIdx.x >> 6) * (A.max_parts + 256));
+  KVS_TL_MARK(2)
 }
 
 AttnPlan attn_plan(const Params& P, int batch, int max_blocks) {
@@ -68,7 +70,9 @@ static void launch_tiles_g(const AttnArgs& A, dim3 grid, bool il, bool phys, hip
   else launch_tiles_gq<G, kKvFp16>(A, grid, il, phys, s);
 }
 
-hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s) {
+hipError_t launch_attn_tiles(const AttnArgs& A_in, int batch, bool il, bool sel_phys, hipStream_t s) {
+  AttnArgs A = A_in;
+  A.P.tl_kind = kTlAttn;
   const int nx = (il ? A.n_il_max : 0) + A.P.topk;
   if (nx <= 0) return hipGetLastError();
   const dim3 grid(nx, A.P.Hkv, batch);

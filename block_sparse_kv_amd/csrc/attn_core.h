@@ -123,6 +123,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
                                           int n_parts, int part, unsigned char* smem,
                                           bool store = true) {
   const int tid = threadIdx.x & 255, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
+  KVS_TL_BEGIN(P, P.tl_kind, 256)
   // Every load is issued up front, in the order the data is needed -- Q, K, then V -- and without
   // branches, so the compiler keeps them all in flight and waits only for what the next step needs.
   // Rows past ntok are still inside the tile: their K only feeds logits that are masked, their V is
@@ -260,6 +261,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       kr[g][3] = q8_dq8(kc[g][1].z, kc[g][1].w, ks[g]);
     }
   }
+  KVS_TL_MARK_LOADED(1)
   f32x4_t S[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -380,6 +382,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
     *reinterpret_cast<float4*>(part_o + pr * kDim + ch) = acc;
     if (ch == 0) *reinterpret_cast<float2*>(part_ml + pr * 2) = make_float2(M, lsum);
   }
+  KVS_TL_MARK(2)
 }
 
 constexpr int kMergeChunk = 1024;  // partials whose (max, sum) pairs sit in LDS at once

@@ -17,6 +17,13 @@ namespace {
 
 using kvs::Params;
 
+#ifdef KVS_TIMELINE
+unsigned long long* g_timeline = nullptr;  // set by kvs_timeline_set
+unsigned long long* timeline_records() { return g_timeline; }
+#else
+unsigned long long* timeline_records() { return nullptr; }
+#endif
+
 constexpr size_t kAlign = 256;  // sub-buffers of a workspace start on 256-byte boundaries
 constexpr size_t kCtrBytes = kvs::kStepCtrBytes;  // decode-step hand-off counters: batch * G <= 16384
 
@@ -71,6 +78,8 @@ int make_params(const kvs_config* c, Params* P) {
   const float scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf((float)c->head_dim);
   P->scale_log2 = scale * 1.4426950408889634f;
   P->kv = c->kv_type;
+  P->tl = timeline_records();
+  P->tl_kind = 0;
   return KVS_OK;
 }
 
@@ -616,22 +625,29 @@ int kvs_preselect_blocks(const kvs_config* cfg, const float* importance, const i
 namespace {
 // Workspace of the confined decode step: scores, the compacted rows (scores, block ids, lengths),
 // their top-k picks, the selection and counts when the caller does not take them, then the partials.
+// Workspace of the confined step: hand-off counters (zero between calls) at the start, as in the
+// decode step's, then the scores (every candidate, or the sets' entries), the compacted rows, the
+// sets' physical ids, the selection and its tiles, and the attention partials.
 struct PreselLayout {
   AttnLayout attn;
-  size_t scores_off, cs_off, cid_off, clen_off, csel_off, sel_off, cnt_off, attn_off, total;
+  size_t ctr_off, scores_off, cs_off, cid_off, cph_off, clen_off, csel_off, sel_off, cnt_off, tiles_off,
+      attn_off, total;
 };
 
 PreselLayout presel_layout(const Params& P, int batch, int max_blocks, int n_presel) {
   PreselLayout L;
   const size_t rows = (size_t)batch * P.G, k = P.topk > 0 ? P.topk : 1;
   size_t off = 0;
+  L.ctr_off = off;    off += kCtrBytes;
   L.scores_off = off; off += round_up(rows * max_blocks * sizeof(float));
   L.cs_off = off;     off += round_up(rows * n_presel * sizeof(float));
   L.cid_off = off;    off += round_up(rows * n_presel * sizeof(int32_t));
+  L.cph_off = off;    off += round_up(rows * n_presel * sizeof(int32_t));
   L.clen_off = off;   off += round_up(rows * sizeof(int32_t));
   L.csel_off = off;   off += round_up(rows * k * sizeof(int32_t));
   L.sel_off = off;    off += round_up(rows * k * sizeof(int32_t));
   L.cnt_off = off;    off += round_up(rows * sizeof(int32_t));
+  L.tiles_off = off;  off += round_up(rows * k * sizeof(int32_t));
   L.attn = attn_layout(P, batch, max_blocks);
   L.attn_off = off;   off += L.attn.total;
   L.total = off;
@@ -676,9 +692,21 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   int32_t* cnt = sel_count_out ? sel_count_out : at<int32_t>(workspace, S.cnt_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* aws = static_cast<char*>(workspace) + S.attn_off;
+  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, presel, n_presel)) != KVS_OK) return st;
+  if (n_presel <= kvs::presel_step_max() && P.topk > 0 && (size_t)rows * sizeof(int) <= kCtrBytes) {
+    // one launch scores the sets, selects from them and streams the Initial/Local tiles
+    int32_t* tiles = at<int32_t>(workspace, S.tiles_off);
+    kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
+                                seq_lens, tiles, cnt, out);
+    clear_stale_error();
+    hipError_t e = kvs::launch_presel_step(a, rep_pool, presel, n_presel, cs, at<int32_t>(workspace, S.cph_off),
+                                           sel, cnt, tiles, at<int>(workspace, S.ctr_off), batch, s);
+    if (e == hipSuccess) e = kvs::launch_attn_tiles(a, batch, false, true, s);
+    if (e == hipSuccess) e = kvs::launch_merge(a, batch, s);
+    return hip_status(e, "kvs_decode_step_preselected");
+  }
   kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                               seq_lens, sel, cnt, out);
-  if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, presel, n_presel)) != KVS_OK) return st;
   clear_stale_error();
   bool il_done = false;  // Initial/Local tiles streamed with the scoring (rows of up to 2048 blocks)
   hipError_t e = kvs::launch_score_il(a, rep_pool, scores, batch, s, &il_done);
@@ -701,5 +729,11 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   if (e != hipSuccess) return hip_status(e, "kvs_decode_step_preselected/tiles");
   return hip_status(kvs::launch_merge(a, batch, s), "kvs_decode_step_preselected/merge");
 }
+
+#ifdef KVS_TIMELINE
+// Timeline build only: the record array (device, kTlKinds * kTlMaxWg * kTlSlots 64-bit words, zeroed
+// by the caller) that calls configured from now on write into; null stops recording.
+void kvs_timeline_set(void* records) { g_timeline = static_cast<unsigned long long*>(records); }
+#endif
 
 }  // extern "C"

@@ -39,6 +39,8 @@ struct Params {
   int method, R, mode;  // rep method, reps per (block, head), head_select_mode
   int kv;               // KvType of the K/V pools
   float scale_log2;     // softmax scale * log2(e): logits live in the exp2 domain
+  unsigned long long* tl;  // timeline records (timeline build only; null otherwise)
+  int tl_kind;             // TlKind of the tiles of this launch (timeline build only)
 };
 
 // Initial / Context / Local split of a sequence of L tokens, rounded outward to whole blocks:
@@ -226,9 +228,16 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- hand-off between workgroups of one kernel ----------------------------------------------------
 // The per-XCD L2 caches are not coherent with each other.  Data one workgroup hands to another of the
-// same kernel is written with device-scope stores that write through to the coherence point (sc1),
-// the writer waits for their completion (vmcnt 0) before it bumps a counter, and the reader loads
-// with the same cache policy, so it sees the data whichever XCD it runs on.
+// same kernel is written with agent-scope relaxed atomic stores (st_coh: global stores with sc1, which
+// write through to the coherence point), the writer waits for their completion (wait_mem: vmcnt 0)
+// before its relaxed agent-scope fetch_add on the group's counter, and the workgroup that brings the
+// counter to its total reads the data, after a workgroup barrier, with sc1 loads (what agent-scope
+// relaxed atomic loads compile to), so it sees the data whichever XCD it runs on.  The ordering rests
+// on the ISA: a store counted in vmcnt is complete at the coherence point once vmcnt reads 0, and
+// every datum goes through an sc1 access on both sides, so no L2 holds a stale or dirty copy of it.
+// A release/acquire pair on the counter would instead write back and invalidate the whole L2 of the
+// XCD at every hand-off, which costs several microseconds per decode step.  wait_mem also keeps the
+// compiler from moving memory accesses across it (signal fences on both sides).
 template <typename T>
 __device__ inline void st_coh(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 constexpr int kSc1 = 16;  // cache-policy operand of the raw buffer loads: sc1
@@ -238,10 +247,17 @@ __device__ inline __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
 __device__ inline float ld_coh_f1(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSc1));
 }
-// Wait until this wave's memory operations have completed (vmcnt 0).
-__device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until this wave's memory operations have completed (vmcnt 0; 0x0F70 leaves expcnt and lgkmcnt
+// at their maxima, so only vmcnt is waited on).
+__device__ inline void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // exp2(a - b) that is 0 when a is -inf (an empty stream), never NaN.
 __device__ inline float exp2_diff(float a, float b) { return a == -INFINITY ? 0.f : fast_exp2(a - b); }
 
 }  // namespace kvs
+
+#include "timeline.h"

@@ -12,12 +12,14 @@ __global__ __launch_bounds__(256) void score_kernel(Params P, const uint16_t* __
                                                     const int32_t* __restrict__ seq_lens,
                                                     float* __restrict__ scores) {
   __shared__ float part[16 * kScorePasses];
+  KVS_TL_BEGIN(P, kTlScore, 256)
   const int seq = blockIdx.y;
   const int sb = score_blocks_per_wg(P);
   score_blocks_range<G, METHOD, MODE>(P, q + (size_t)seq * P.Hq * kDim, rep_pool,
                                       table + (size_t)seq * max_blocks, max_blocks, seq_lens[seq],
                                       blockIdx.x * sb, sb, scores + (size_t)seq * P.G * max_blocks,
                                       part);
+  KVS_TL_MARK_LOADED(1)
 }
 
 template <int G, int METHOD>

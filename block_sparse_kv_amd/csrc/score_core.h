@@ -31,14 +31,22 @@ constexpr int kScoreBlocksPerHeadWg = 16 * kScorePasses;
 // lds_chunk (PER_HEAD, nullable): also receives every block's score (-inf for non-candidates and past
 // the row) at [block - b0] and its physical id (0 for non-candidates) as an int at [64 + block - b0],
 // for the workgroup's own use after a barrier (nb <= 64).
-template <int G, int METHOD, int MODE, bool PER_HEAD = false, bool COH = false>
+// LIST: [b0, b0 + nb) are positions in the list ids[0..n_list) of logical block ids (-1 or any id
+// outside the candidates: not a candidate); the scores go to position-indexed rows of n_list entries
+// (scores_row[(PER_HEAD ? h : 0) * n_list + position]), and each candidate's physical id, coherently,
+// to phys_row at the same index.
+template <int G, int METHOD, int MODE, bool PER_HEAD = false, bool COH = false, bool LIST = false>
 __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16_t* __restrict__ q_seq,
                                           const void* __restrict__ rep_pool,
                                           const int32_t* __restrict__ trow, int max_blocks, int L,
                                           int b0, int nb, float* __restrict__ scores_row,
                                           float* lds_part /* >= 16 * kScorePasses floats */,
-                                          int h_one = 0, float* lds_chunk = nullptr) {
+                                          int h_one = 0, float* lds_chunk = nullptr,
+                                          const int32_t* __restrict__ ids = nullptr, int n_list = 0,
+                                          int32_t* __restrict__ phys_row = nullptr) {
   static_assert(!(PER_HEAD && MODE == kShared), "a SHARED score sums over every KV head");
+  static_assert(!(LIST && !COH), "list scores are handed to the selecting workgroup");
+  const int n_row = LIST ? n_list : max_blocks;  // entries of a score row
   const int Hkv = P.Hkv;
   const int t = threadIdx.x, c = t & 15;
   const int h = PER_HEAD ? h_one : (t >> 4) % Hkv;
@@ -65,15 +73,26 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
   // ones (a non-candidate reads physical block 0) and the results are masked afterwards, so the
   // compiler places no wait between them.
   for (int base = b0; base < b0 + nb; base += bpp * kScorePasses) {
-    int blk[kScorePasses];
+    int blk[kScorePasses];  // row position: the logical block, or with LIST the list position
+    int lb[kScorePasses];   // logical block
     bool inr[kScorePasses], cand[kScorePasses];
     size_t phys[kScorePasses];
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
       blk[p] = base + p * bpp + slot;
-      inr[p] = blk[p] < b0 + nb && blk[p] < max_blocks;
-      cand[p] = inr[p] && blk[p] >= rg.cand_lo && blk[p] < rg.cand_hi;
-      const int t = trow[min(blk[p], max_blocks - 1)];
+      inr[p] = blk[p] < b0 + nb && blk[p] < n_row;
+    }
+    if constexpr (LIST) {
+#pragma unroll
+      for (int p = 0; p < kScorePasses; ++p) lb[p] = ids[min(blk[p], n_row - 1)];
+    } else {
+#pragma unroll
+      for (int p = 0; p < kScorePasses; ++p) lb[p] = blk[p];
+    }
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+      cand[p] = inr[p] && lb[p] >= rg.cand_lo && lb[p] < rg.cand_hi && lb[p] < max_blocks;
+      const int t = trow[min(max(lb[p], 0), max_blocks - 1)];
       phys[p] = cand[p] ? (size_t)t : 0;
     }
     uint4 raw[kScorePasses][RMAX];
@@ -145,9 +164,10 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
             reinterpret_cast<int*>(lds_chunk)[64 + blk[p] - b0] = (int)phys[p];
           }
           if (!inr[p]) continue;
-          float* dst = scores_row + (size_t)h * max_blocks + blk[p];
+          float* dst = scores_row + (size_t)h * n_row + blk[p];
           const float v = cand[p] ? acc[p] : -INFINITY;
           if constexpr (COH) st_coh(dst, v); else *dst = v;
+          if constexpr (LIST) st_coh(phys_row + (size_t)h * n_row + blk[p], (int32_t)phys[p]);
         }
       }
     } else {
@@ -164,6 +184,7 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
           for (int hh = 0; hh < Hkv; ++hh) s += lds_part[p * 16 + slot * Hkv + hh];
           const float v = cand[p] ? s : -INFINITY;
           if constexpr (COH) st_coh(scores_row + blk[p], v); else scores_row[blk[p]] = v;
+          if constexpr (LIST) st_coh(phys_row + blk[p], (int32_t)phys[p]);
         }
       }
       __syncthreads();

@@ -5,9 +5,14 @@
 //    their scores to the one among them that finishes last, which makes the group's selection (256
 //    lanes, keys in registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles
 //    and the merge (attn.hip).
-//  * long rows: scoring (score.hip); then the top-k selections in 512-lane workgroups with the
+//  * SEPARATE rows of up to kStepSummMax blocks: the same launch, each scoring workgroup (one 64-block
+//    chunk of one KV head) also storing its chunk's best 8; the last one selects from these summaries,
+//    or from the whole row when a chunk holds more than 8 of the selection.
+//  * other long rows: scoring (score.hip); then the top-k selections in 512-lane workgroups with the
 //    Initial/Local tiles, two per workgroup, in one launch (topk_il_wide_kernel), so their gather
 //    runs while the selections are made; then the selected tiles and the merge.
+// The confined step (kvs_decode_step_preselected) scores only the preselected sets and selects from
+// them in the same way (presel_step_kernel), then runs the selected tiles and the merge.
 // In every grid an attention tile is one workgroup (attn_core.h).
 #include "kvs_launch.h"
 #include "step_kv.h"
@@ -42,6 +47,19 @@ hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* score
   *il_done = A.max_blocks <= kStepTopkSmall;
   if (*il_done) return launch_score_select(A, rep_pool, scores, nullptr, nullptr, nullptr, nullptr, batch, s);
   return launch_score(A.P, A.q, rep_pool, A.table, A.max_blocks, A.seq_lens, batch, scores, s);
+}
+
+int presel_step_max() { return kPreselStepMax; }
+
+hipError_t launch_presel_step(const AttnArgs& A, const void* rep_pool, const int32_t* presel, int n_presel,
+                              float* cs, int32_t* cph, int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr,
+                              int batch, hipStream_t s) {
+  switch (A.P.kv) {
+    case kKvQ8: return launch_presel_step_kv<kKvQ8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+    case kKvQ4: return launch_presel_step_kv<kKvQ4>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+    case kKvI8: return launch_presel_step_kv<kKvI8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+    default: return launch_presel_step_kv<kKvFp16>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+  }
 }
 
 size_t summaries_bytes(const Params& P, int batch, int max_blocks) {

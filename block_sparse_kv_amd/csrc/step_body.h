@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
     return;
   }
   constexpr bool SEP = MODE == kSeparate;
+  KVS_TL_BEGIN(P, kTlScoreSel, 256)
   const int y = x;
   const int per_seq = P.G * n_sc;
   const int seq = y / per_seq, grp = (y % per_seq) / n_sc, c = y % n_sc;
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                                                  A.max_blocks, A.seq_lens[seq], c * sb, sb,
                                                  scores + (size_t)seq * P.G * A.max_blocks,
                                                  reinterpret_cast<float*>(smem), grp, SUMM ? lchunk : nullptr);
+  KVS_TL_MARK_LOADED(1)
   if (sel == nullptr) return;  // scores and Initial/Local tiles only: the selection comes later
   const size_t urow = ((size_t)seq * P.G + grp) * n_sc * kChunkTop;  // this group's summaries
   if constexpr (SUMM) {
@@ -100,11 +102,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                           uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
   }
   wait_mem();
+  if constexpr (SUMM) {
+    KVS_TL_MARK(4)
+  }
   __syncthreads();
   int* cp = ctr + ((size_t)seq * P.G + grp) * ctr_stride;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_sc - 1;
   __syncthreads();
+  KVS_TL_MARK(2)
   if (!s_last) return;  // else every scoring workgroup of the group has arrived
   if constexpr (SUMM) {
     const size_t row = (size_t)seq * P.G + grp;
@@ -138,6 +144,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                                          tiles, seq, grp, *reinterpret_cast<TopkLds*>(smem));
   }
   if (threadIdx.x == 0) st_coh(cp, 0);  // stored last: the selection's barriers would wait for it
+  KVS_TL_MARK(3)
 }
 
 template <int G, int METHOD, int KV>
@@ -168,9 +175,11 @@ static void launch_ss_g(const AttnArgs& A, dim3 grid, hipStream_t s, const void*
 }
 
 template <int KV>
-hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
+hipError_t launch_score_select_kv(const AttnArgs& A_in, const void* rep_pool, float* scores, int32_t* sel,
                                   int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
                                   const Summaries& U) {
+  AttnArgs A = A_in;
+  A.P.tl_kind = kTlIlStep;
   const Params& P = A.P;
   const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
   const int n_sc = (A.max_blocks + sb - 1) / sb;
@@ -203,8 +212,10 @@ __global__ __launch_bounds__(512) void topk_il_wide_kernel(AttnArgs A, const flo
   const Params& P = A.P;
   const int x = blockIdx.x;
   if (x < n_topk) {
+    KVS_TL_BEGIN(P, kTlWideTopk, 512)
     topk_group<512, 16>(P, scores, A.seq_lens, A.max_blocks, sel, sel_count, A.table, tiles, x / P.G,
                          x % P.G, *reinterpret_cast<TopkLds*>(smem));
+    KVS_TL_MARK(3)
     return;
   }
   const int f = (x - n_topk) * 2 + (threadIdx.x >> 8);  // this half's flat tile index
@@ -227,8 +238,10 @@ __global__ __launch_bounds__(512) void topk_il_wide_kernel(AttnArgs A, const flo
 }
 
 template <int KV>
-hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
+hipError_t launch_topk_il_wide_kv(const AttnArgs& A_in, const float* scores, int32_t* sel, int32_t* sel_count,
                                   int32_t* tiles, int batch, hipStream_t s) {
+  AttnArgs A = A_in;
+  A.P.tl_kind = kTlIlWide;
   const int n_topk = A.P.G * batch;
   const int n_il_total = batch * A.P.Hkv * A.n_il_max;
   const dim3 grid(n_topk + (n_il_total + 1) / 2), block(512);
@@ -243,6 +256,98 @@ hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_
     default: KVS_WIDE(16); break;
   }
 #undef KVS_WIDE
+  return hipGetLastError();
+}
+
+// The first launch of the confined decode step (kvs_decode_step_preselected) for sets of up to
+// kPreselStepMax entries: n_pc scoring workgroups per (sequence, group) row score the row's
+// preselected blocks -- positions [c * sb, c * sb + sb) of presel[row] -- and store each score and
+// physical id by position, coherently (cs, cph [row][n_presel]); the one that brings the row's
+// counter to n_pc selects from them (topk_list_reg) and resets it.  Then the Initial/Local tiles, as
+// in score_select_kernel.  Rows of any length: only the set is scored.
+template <int G, int METHOD, int MODE, int KV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void presel_step_kernel(
+    AttnArgs A, const void* __restrict__ rep_pool, const int32_t* __restrict__ presel, int n_presel,
+    float* __restrict__ cs, int32_t* __restrict__ cph, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int ctr_stride,
+    int n_pc, int n_il_wg) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
+  __shared__ int s_last;
+  const Params& P = A.P;
+  const int n_score_wg = (int)gridDim.x - n_il_wg;
+  const int x = blockIdx.x;
+  if (x >= n_score_wg) {
+    const int xi = x - n_score_wg;
+    const int per_seq = P.Hkv * A.n_il_max;
+    const int r = xi % per_seq;
+    attn_item<G, true, false, KV>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
+    return;
+  }
+  constexpr bool SEP = MODE == kSeparate;
+  KVS_TL_BEGIN(P, kTlScoreSel, 256)
+  const int row = x / n_pc, c = x % n_pc;
+  const int seq = row / P.G, grp = row % P.G;
+  const int sb = SEP ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
+  const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
+  const int32_t* ids = presel + (size_t)row * n_presel;
+  const size_t rbase = (size_t)seq * P.G * n_presel;  // score rows of the sequence's groups
+  score_blocks_range<G, METHOD, MODE, SEP, true, true>(P, A.q + (size_t)seq * P.Hq * kDim, rep_pool, trow,
+                                                       A.max_blocks, A.seq_lens[seq], c * sb, sb, cs + rbase,
+                                                       reinterpret_cast<float*>(smem), grp, nullptr, ids,
+                                                       n_presel, cph + rbase);
+  KVS_TL_MARK_LOADED(1)
+  wait_mem();
+  __syncthreads();
+  int* cp = ctr + (size_t)row * ctr_stride;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_pc - 1;
+  __syncthreads();
+  KVS_TL_MARK(2)
+  if (!s_last) return;  // else every scoring workgroup of the row has arrived
+  const Regions rg = regions_of(A.seq_lens[seq], P.initial_len, P.local_len);
+  topk_list_reg<256, kPreselStepKeys>(cs + (size_t)row * n_presel, cph + (size_t)row * n_presel, ids,
+                                      n_presel, rg.cand_lo, min(rg.cand_hi, A.max_blocks), P.topk,
+                                      *reinterpret_cast<TopkLds*>(smem), sel + (size_t)row * P.topk,
+                                      sel_count + row, tiles + (size_t)row * P.topk);
+  if (threadIdx.x == 0) st_coh(cp, 0);  // stored last: the selection's barriers would wait for it
+  KVS_TL_MARK(3)
+}
+
+template <int KV>
+hipError_t launch_presel_step_kv(const AttnArgs& A_in, const void* rep_pool, const int32_t* presel,
+                                 int n_presel, float* cs, int32_t* cph, int32_t* sel, int32_t* cnt,
+                                 int32_t* tiles, int* ctr, int batch, hipStream_t s) {
+  AttnArgs A = A_in;
+  A.P.tl_kind = kTlIlStep;
+  const Params& P = A.P;
+  const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
+  const int n_pc = (n_presel + sb - 1) / sb;
+  const int rows = batch * P.G;
+  const int n_il_wg = batch * P.Hkv * A.n_il_max;
+  const dim3 grid(n_il_wg + rows * n_pc);
+  const int cst = step_ctr_stride(rows);
+#define KVS_PS(GG, MM, MO)                                                                            \
+  hipLaunchKernelGGL((presel_step_kernel<GG, MM, MO, KV>), grid, dim3(256), 0, s, A, rep_pool, presel, \
+                     n_presel, cs, cph, sel, cnt, tiles, ctr, cst, n_pc, n_il_wg)
+#define KVS_PS_M(GG, MO)                               \
+  switch (P.method) {                                  \
+    case kQuest: KVS_PS(GG, kQuest, MO); break;        \
+    case kMax: KVS_PS(GG, kMax, MO); break;            \
+    case kMean: KVS_PS(GG, kMean, MO); break;          \
+    default: KVS_PS(GG, kFix, MO); break;              \
+  }
+#define KVS_PS_G(GG)                                                          \
+  if (P.mode == kSeparate) { KVS_PS_M(GG, kSeparate) } else { KVS_PS_M(GG, kShared) }
+  switch (P.g) {
+    case 1: KVS_PS_G(1); break;
+    case 2: KVS_PS_G(2); break;
+    case 4: KVS_PS_G(4); break;
+    case 8: KVS_PS_G(8); break;
+    default: KVS_PS_G(16); break;
+  }
+#undef KVS_PS_G
+#undef KVS_PS_M
+#undef KVS_PS
   return hipGetLastError();
 }
 

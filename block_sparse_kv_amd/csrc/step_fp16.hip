@@ -7,4 +7,7 @@ template hipError_t launch_score_select_kv<kKvFp16>(const AttnArgs&, const void*
                                                 const Summaries&);
 template hipError_t launch_topk_il_wide_kv<kKvFp16>(const AttnArgs&, const float*, int32_t*, int32_t*, int32_t*,
                                                 int, hipStream_t);
+template hipError_t launch_presel_step_kv<kKvFp16>(const AttnArgs&, const void*, const int32_t*, int, float*,
+                                                int32_t*, int32_t*, int32_t*, int32_t*, int*, int,
+                                                hipStream_t);
 }  // namespace kvs

@@ -33,4 +33,14 @@ template <int KV>
 hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
                                   int32_t* tiles, int batch, hipStream_t s);
 
+// The confined step's first launch: scoring of the preselected sets, the selection from them and the
+// Initial/Local tiles (sets of up to kPreselStepMax entries; 256-lane selection, kPreselStepKeys keys
+// per lane).
+constexpr int kPreselStepKeys = 4;
+constexpr int kPreselStepMax = 256 * kPreselStepKeys;
+template <int KV>
+hipError_t launch_presel_step_kv(const AttnArgs& A, const void* rep_pool, const int32_t* presel,
+                                 int n_presel, float* cs, int32_t* cph, int32_t* sel, int32_t* cnt,
+                                 int32_t* tiles, int* ctr, int batch, hipStream_t s);
+
 }  // namespace kvs

@@ -644,6 +644,62 @@ __device__ __forceinline__ bool topk_summary_reg(const float* uval, const int32_
   return true;
 }
 
+// Selection from a list of preselected blocks: ids[0..m) ascending logical block ids (-1 padded), with
+// the score of entry i in vals[i] and its physical id in phys[i], both stored by other workgroups of
+// the same kernel (read coherently).  The candidates are the entries with an id in [cand_lo, cand_hi);
+// the best k = min(topk, their number) by (score desc, id asc) are written to sel[0..k) (ids,
+// ascending) and tiles[0..k) (physical ids), -1 in [k, topk), *cnt = k.
+template <int NT, int KPT>
+__device__ __forceinline__ void topk_list_reg(const float* vals, const int32_t* phys, const int32_t* ids,
+                                              int m, int cand_lo, int cand_hi, int topk, TopkLds& S,
+                                              int32_t* sel_, int32_t* cnt_, int32_t* tiles_) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per entry");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto sel = gptr(sel_);
+  auto cnt = gptr(cnt_);
+  auto tiles = gptr(tiles_);
+  const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rv = span_rsrc(vals, m * 4);
+  const __amdgpu_buffer_rsrc_t rp = span_rsrc(phys, m * 4);
+  const __amdgpu_buffer_rsrc_t ri = span_rsrc(ids, m * 4);
+  float v[KPT];
+  int32_t id[KPT], ph[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, (ibase + 64 * c) * 4, 0, kSc1));
+    ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (ibase + 64 * c) * 4, 0, kSc1);
+    id[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (ibase + 64 * c) * 4, 0, 0);
+  }
+  uint32_t okb = 0u;
+  int n_w = 0;  // candidates of this wave
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool ok = ibase + 64 * c < m && id[c] >= cand_lo && id[c] < cand_hi;
+    okb |= (ok ? 1u : 0u) << c;
+    n_w += __popcll(__ballot(ok));
+  }
+  if (lane == 0) S.woff[wv] = n_w;
+  __syncthreads();
+  int n_ok = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_ok += S.woff[w];
+    before += w < wv ? S.woff[w] : 0;
+  }
+  const int k = min(topk, n_ok);
+  uint32_t take = okb;  // every candidate, written in order from the wave's offset
+  int off = before;
+  if (k < n_ok) take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
+  if (tid == 0) *cnt = k;
+  for (int i = k + tid; i < topk; i += NT) {
+    sel[i] = -1;
+    tiles[i] = -1;
+  }
+  if (k > 0) topk_reg_write<KPT>(take, off, k, ibase, id, true, ph, true, sel, tiles);
+}
+
 // The selection of group grp of sequence seq from the scores [batch][G][max_blocks]: sel (and, with a
 // table and tiles, the physical ids in tiles) [batch][G][topk] ascending and -1 padded,
 // sel_count [batch][G].  Rows of up to NT * KMAX blocks stay in registers.  COH (rows of up to

@@ -77,7 +77,9 @@ def decode_step_preselected(cfg, q, k_pool, v_pool, rep_pool, block_table, seq_l
     out = torch.empty((batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=q.device)
     sel = torch.empty((batch, cfg.groups, max(cfg.topk, 1)), dtype=torch.int32, device=q.device)
     cnt = torch.empty((batch, cfg.groups), dtype=torch.int32, device=q.device)
-    ws = workspace(B.kvs_decode_step_preselected_workspace_size(cfg, batch, mb, n_presel), q.device)
+    # zeroed: its first bytes are the hand-off counters, which every completed call leaves zero
+    ws = torch.zeros(B.kvs_decode_step_preselected_workspace_size(cfg, batch, mb, n_presel), dtype=torch.uint8,
+                     device=q.device)
     B.kvs_decode_step_preselected(cfg, q, k_pool, v_pool, rep_pool, block_table, mb, seq_lens, batch,
                                   presel.contiguous(), n_presel, out, sel, cnt, ws, ws.numel())
     return out, sel[:, :, : cfg.topk], cnt

@@ -256,9 +256,16 @@ size_t kvs_decode_step_preselected_workspace_size(const kvs_config* cfg, int32_t
  * [KT-LC §4.4]: per (sequence, group), only the blocks of presel [batch][G][n_presel] (ascending, -1
  * padded, e.g. from kvs_preselect_blocks) that are still candidates at the current length compete;
  * k_eff = min(topk, their number), so with topk >= the set's size the set is attended as it is.
- * Scores, ties, order and attention as kvs_decode_step.  Enqueued as scoring (with the Initial/Local
- * tiles for max_blocks_per_seq <= 2048), compaction, top-k, mapping, attention tiles and merge; the
- * workspace (>= the size query, 256-byte aligned) is scratch.
+ * Scores, ties, order and attention as kvs_decode_step.  With topk > 0, n_presel <= 1024 and
+ * batch * G <= 16384, enqueued as three launches: 1. scoring of the sets' blocks only, the
+ * selection from them by the scoring workgroup of the (sequence, group) that finishes last, and the
+ * Initial/Local tiles;  2. attention over the selected tiles;  3. the merge.  Otherwise: scoring of
+ * every candidate (with the Initial/Local tiles for max_blocks_per_seq <= 2048), a ranking of the
+ * set (n_presel <= 256) or compaction, top-k and mapping, attention tiles and merge.
+ * workspace: >= the size query, 256-byte aligned.  Like kvs_decode_step's, its first 64 KiB hold
+ * hand-off counters: zero-fill it once before its first use; every call that runs to completion
+ * leaves them zero, a call that did not complete may not, and the workspace must then be zeroed
+ * again.  It belongs to this entry point alone (another call writing into it breaks the counters).
  * sel_out / sel_count_out (nullable) receive the selection.
  */
 int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void* k_pool,

@@ -3,6 +3,7 @@ rejects bad arguments on the host with the documented status before touching the
 import ctypes
 import os
 import re
+import sys
 
 import numpy as np
 
@@ -328,3 +329,27 @@ def test_noalloc_host_checks():
                                    ALIGNED, None, None, stream=0, check=False)
     assert st == B.KVS_ERR_WORKSPACE
     assert "static scratch" in kvs.kvs_last_error()
+
+
+def test_timeline_variant_exports():
+    """The timeline library (build.py --timeline) exports every entry point plus kvs_timeline_set; the
+    default library carries no timeline code."""
+    import ctypes
+    import subprocess
+
+    here = os.path.dirname(B.LIB_PATH)
+    assert not hasattr(ctypes.CDLL(os.path.join(here, "libkvs.so")), "kvs_timeline_set")
+    tl = os.path.join(here, "libkvs_timeline.so")
+    if not os.path.exists(tl):
+        pytest.skip("libkvs_timeline.so not built")
+    code = ("import block_sparse_kv_amd.binding as b; assert b.TIMELINE and b.LIB_PATH.endswith("
+            "'libkvs_timeline.so'); [getattr(b._lib, n) for n in b.EXPORTS]; b._lib.kvs_timeline_set; "
+            "print('ok')")
+    env = dict(os.environ, KVS_LIBRARY="timeline")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=os.path.dirname(here))
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
+    env["KVS_LIBRARY"] = "bogus"
+    r = subprocess.run([sys.executable, "-c", "import block_sparse_kv_amd"], env=env, capture_output=True,
+                       text=True, cwd=os.path.dirname(here))
+    assert r.returncode != 0 and "KVS_LIBRARY" in r.stderr

@@ -80,8 +80,9 @@ def test_preselect_blocks(idx):
 
 
 STEP_CASES = [
-    # (Hq, Hkv, mode, rep, k, lens, kv, set size): sets of up to 256 blocks are ranked in one launch,
-    # larger ones through compacted rows and the ordinary top-k
+    # (Hq, Hkv, mode, rep, k, lens, kv, set size): sets of up to 1024 entries are scored and selected
+    # from in one launch; larger ones through every candidate's score, compacted rows and the
+    # ordinary top-k
     (32, 8, "shared", "max", 6, [6000, 9000], "fp16", 18),
     (8, 2, "separate", "quest", 4, [5000], "fp16", 18),
     (16, 4, "separate", "quest", 40, [3000], "fp16", 18),   # k >= the set: the set itself
@@ -90,6 +91,9 @@ STEP_CASES = [
     (16, 4, "separate", "max", 30, [60000], "q4_0", 248),   # 254 entries: the one-launch path near its limit
     (16, 2, "shared", "quest", 50, [60000, 40000], "fp16", 300),
     (32, 8, "separate", "mean", 12, [20000], "int8_pth", 40),
+    (16, 4, "separate", "quest", 24, [280000], "fp16", 1100),  # 1106 entries: compacted rows
+    (32, 8, "shared", "fix", 20, [150000, 90000], "fp16", 1012),  # 1018 entries: one launch, near its limit
+    (8, 8, "separate", "max", 7, [130000], "q8_0", 300),  # every KV head its own set, g = 1
 ]
 
 
