@@ -115,8 +115,8 @@ def regions(L, I, W):
     return ib, lloc, (lloc - ib) // B
 
 
-STEP_KERNELS = ("score_select_kernel", "score_kernel", "topk_il_wide_kernel", "topk_kernel", "merge_wave_kernel",
-                "attn_tiles_kernel", "merge_kernel")
+STEP_KERNELS = ("build_reps_kernel", "presel_step_kernel", "score_select_kernel", "score_kernel",
+                "topk_il_wide_kernel", "topk_kernel", "merge_wave_kernel", "attn_tiles_kernel", "merge_kernel")
 COPY_BYTES = 4 << 30  # the device copy of copy_bandwidth(): read and written once per dispatch
 
 
@@ -328,7 +328,7 @@ class MixedSetup:
                               local_len=w["W"], topk=w["k"], rep_method=w["rep"],
                               rep_num=w.get("rep_num", 1), head_select_mode=w["mode"])
         win, bsz = w["window"], w["batch"]
-        self.lens0 = kvsynth.uniform_lengths(kvsynth.mix_seed(w["seed"], 1), bsz, w["Lmin"], w["Lmax"])
+        self.lens0 = mixed_lengths(w)
         hot = []
         for L in self.lens0:
             ie, _, nc = regions(L, w["I"], w["W"])
@@ -373,18 +373,37 @@ class MixedSetup:
                                  self.out, self.sel, self.cnt, self.ws, self.ws_bytes)
 
     def window_bytes(self):
-        """Algorithmic bytes of one window: every step's decode bytes, plus the rows of the reps built
-        (read and written)."""
-        w = self.w
-        tot = 0
-        R = w.get("rep_num", 1)
-        for t in range(w["window"]):
-            for L in self.lens0:
-                rb = required_bytes(w, L + t)
-                tot += rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
-            n_fill = sum(1 for L in self.lens0 if (L + t) % B == 0)
-            tot += n_fill * w["Hkv"] * R * D * 2 * 2
-        return tot
+        return mixed_window_bytes(self.w, self.lens0)
+
+
+def mixed_lengths(w):
+    """The batched workload's starting lengths (seeded, CPU)."""
+    import kvsynth
+
+    return kvsynth.uniform_lengths(kvsynth.mix_seed(w["seed"], 1), w["batch"], w["Lmin"], w["Lmax"])
+
+
+def mixed_window_bytes(w, lens0):
+    """Algorithmic bytes of one window of the batched workload: every step's decode bytes, plus the
+    rows of the reps built (read and written)."""
+    tot = 0
+    R = w.get("rep_num", 1)
+    for t in range(w["window"]):
+        for L in lens0:
+            rb = required_bytes(w, L + t)
+            tot += rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
+        n_fill = sum(1 for L in lens0 if (L + t) % B == 0)
+        tot += n_fill * w["Hkv"] * R * D * 2 * 2
+    return tot
+
+
+def required_per_step(name):
+    """Algorithmic bytes of one step of `name` (every layer; the batched workload: a window's mean)."""
+    w = WORKLOADS[name]
+    if "batch" in w:
+        return mixed_window_bytes(w, mixed_lengths(w)) / w["window"]
+    rb = required_bytes(w)
+    return (rb["q"] + rb["reps"] + rb["kv"] + rb["out"]) * w["layers"]
 
 
 def _capture(step_fn, idxs):
@@ -650,46 +669,53 @@ def _bench_line(log_path):
     return "(bench log not given)"
 
 
-def summarize_stats(d, name, log_path=None):
+def summarize_stats(d, name, log_path=None, steps=480):
     """rocprofv3 --kernel-trace --stats CSV -> profiles/decode_step_<name>_kernel_stats.txt."""
     import csv
 
-    w = WORKLOADS[name]
-    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    rows = [r for r in csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv")))
+            if _step_kernel(r["Name"]) is not None]
+    # kernels called at least half as often as the busiest one run every layer step; the others
+    # (the set-up's rep builds and preselection, the batched workload's incremental builds) do not
+    top = max(int(r["Calls"]) for r in rows)
     out, tot = [], 0.0
     for r in rows:
         k = _step_kernel(r["Name"])
-        if k is None:
-            continue
         avg = float(r["AverageNs"]) / 1e3
-        tot += avg
-        out.append(f"| {k:18s} | {r['Name'][:60]:60s} | {int(r['Calls']):6d} | {avg:9.2f} | "
-                   f"{float(r['MinNs']) / 1e3:9.2f} | {float(r['MaxNs']) / 1e3:9.2f} |")
-    steps = "480"
+        every = int(r["Calls"]) >= top // 2
+        if every:
+            tot += avg
+        out.append(f"| {k + ('' if every else ' *'):20s} | {r['Name'][:60]:60s} | {int(r['Calls']):6d} | "
+                   f"{avg:9.2f} | {float(r['MinNs']) / 1e3:9.2f} | {float(r['MaxNs']) / 1e3:9.2f} |")
     txt = [f"# kvs_decode_step kernels, workload {name}",
            "",
            "command (repository root on the MI355X box; bench.py times the same calls):",
            f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{name} -o run "
            f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps}",
-           f"    python bench.py --summarize-stats gpurun_out/prof_{name} --workload {name} "
+           f"    python bench.py --summarize-stats gpurun_out/prof_{name} --workload {name} --steps {steps} "
            f"--log gpurun_out/prof_{name}.log",
            "",
            f"source_hash: {source_hash()}",
            f"sum_of_kernel_averages_us_per_layer: {tot:.2f}",
            f"bench_line_under_the_profiler: {_bench_line(log_path)}",
            "",
-           "| kernel             | name                                                         |  calls |  avg us   |  min us   |  max us   |",
-           "|--------------------|--------------------------------------------------------------|--------|-----------|-----------|-----------|",
-           *out, ""]
+           "| kernel               | name                                                         |  calls |  avg us   |  min us   |  max us   |",
+           "|----------------------|--------------------------------------------------------------|--------|-----------|-----------|-----------|",
+           *out,
+           "",
+           "* not every layer step (set-up, or the batched workload's incremental rep builds): not in the sum",
+           ""]
     path = os.path.join(ROOT, "profiles", f"decode_step_{name}_kernel_stats.txt")
     with open(path, "w") as f:
         f.write("\n".join(txt))
     print(path)
 
 
-def summarize_pmc(fetch_dir, write_dir, name):
+def summarize_pmc(fetch_dir, write_dir, name, steps=32):
     """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs -> profiles/decode_step_<name>_traffic.txt.
-    Each counter is scaled by what it reads for the 4 GiB copies of copy_bandwidth()."""
+    Each counter is scaled by what it reads for the 4 GiB copies of copy_bandwidth().  Per layer:
+    the mean bytes per dispatch of each decode-step kernel, summed (the batched workload's
+    incremental rep builds, not run every step, are listed but not summed)."""
     import csv
     import collections
 
@@ -712,11 +738,12 @@ def summarize_pmc(fetch_dir, write_dir, name):
         scale = COPY_BYTES / (sum(cal) / len(cal))
         res[counter] = (scale, {k: sum(v) / len(v) * scale for k, v in per.items()},
                         {k: len(v) for k, v in per.items()}, len(cal))
-    rb = required_bytes(w)
-    req_layer = rb["q"] + rb["reps"] + rb["kv"] + rb["out"]
-    fetch_layer = sum(res["FETCH_SIZE"][1].values())
-    write_layer = sum(res["WRITE_SIZE"][1].values())
-    steps = "32"
+    # as in summarize_stats: kernels dispatched at least half as often as the busiest run every step
+    top = max(res["FETCH_SIZE"][2].values())
+    every = {k for k, n in res["FETCH_SIZE"][2].items() if n >= top // 2}
+    req_layer = required_per_step(name) / w["layers"]
+    fetch_layer = sum(v for k, v in res["FETCH_SIZE"][1].items() if k in every)
+    write_layer = sum(v for k, v in res["WRITE_SIZE"][1].items() if k in every)
     lines = [f"# HBM traffic of kvs_decode_step, workload {name}",
              "",
              "commands (repository root on the MI355X box), one counter per run:",
@@ -725,7 +752,7 @@ def summarize_pmc(fetch_dir, write_dir, name):
              f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{name} -o run "
              f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps} --warmup 2",
              f"    python bench.py --summarize-pmc gpurun_out/pmc_fetch_{name} gpurun_out/pmc_write_{name} "
-             f"--workload {name}",
+             f"--workload {name} --steps {steps}",
              "",
              "Calibration: each counter over the 4 GiB device copy that starts every bench.py run "
              "(read 4 GiB, write 4 GiB).",
@@ -738,12 +765,14 @@ def summarize_pmc(fetch_dir, write_dir, name):
              f"hbm_bytes_per_step: {(fetch_layer + write_layer) * w['layers']:.0f}",
              f"traffic_over_required: {(fetch_layer + write_layer) / req_layer:.4f}",
              "",
-             "| kernel             | dispatches | fetch bytes (scaled) | write bytes (scaled) |",
-             "|--------------------|------------|----------------------|----------------------|"]
+             "| kernel               | dispatches | fetch bytes (scaled) | write bytes (scaled) |",
+             "|----------------------|------------|----------------------|----------------------|"]
     for k in STEP_KERNELS:
         if k in res["FETCH_SIZE"][1]:
-            lines.append(f"| {k:18s} | {res['FETCH_SIZE'][2][k]:10d} | {res['FETCH_SIZE'][1][k]:20.0f} | "
-                         f"{res['WRITE_SIZE'][1].get(k, 0.0):20.0f} |")
+            lines.append(f"| {k + ('' if k in every else ' *'):20s} | {res['FETCH_SIZE'][2][k]:10d} | "
+                         f"{res['FETCH_SIZE'][1][k]:20.0f} | {res['WRITE_SIZE'][1].get(k, 0.0):20.0f} |")
+    lines += ["", "* not every layer step (set-up, or the batched workload's incremental rep builds): "
+              "not in the per-layer sums"]
     path = os.path.join(ROOT, "profiles", f"decode_step_{name}_traffic.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -756,7 +785,7 @@ TL_KINDS = ("scoring+selection: scoring workgroups", "scoring+selection: Initial
 TL_LAUNCH = {0: "scoring+selection", 1: "scoring+selection", 2: "top-k", 5: "top-k", 3: "attention",
              4: "merge", 6: "scoring", 7: "top-k (own)", 8: "compaction", 9: "map back"}
 TL_MARKS = {1: "operands in / scores stored", 2: "done / counter bumped", 3: "selection stored",
-            4: "chunk summary stored"}
+            4: "chunk summary stored", 5: "chunk summary made"}
 TL_MAX_WG, TL_SLOTS = 16384, 8
 
 
@@ -794,20 +823,23 @@ def timeline(name, device, replays=9, keep=5):
         g.replay()
         torch.cuda.synchronize()
         rec = buf.view(n_kinds, TL_MAX_WG, TL_SLOTS).cpu().numpy().view(np.uint64).astype(np.float64)
-        t0 = min(rec[k][rec[k][:, 0] > 0, 0].min() for k in range(n_kinds) if (rec[k][:, 0] > 0).any())
+        # the step starts with its scoring workgroups (first in their launch's grid); a record that
+        # starts earlier is an earlier step's, left by a workgroup that had nothing to do this time
+        first = [rec[k][rec[k][:, 0] > 0, 0].min() for k in (0, 6) if (rec[k][:, 0] > 0).any()]
+        t0 = min(first) - 100.0  # 1 us of slack (100 MHz ticks)
         vals = {}
         for k in range(n_kinds):
-            r = rec[k][rec[k][:, 0] > 0]
+            r = rec[k][rec[k][:, 0] >= t0]
             if not len(r):
                 continue
             vals[(k, "n")] = len(r)
-            us = lambda a: (a - t0) / 100.0  # 100 MHz ticks -> us
-            for slot in (0, 1, 2, 3, 4):
+            us = lambda a: (a - min(first)) / 100.0  # 100 MHz ticks -> us from the step's start
+            for slot in (0, 1, 2, 3, 4, 5):
                 a = r[:, slot]
                 a = a[a > 0]
                 if len(a):
                     vals[(k, slot)] = (us(a.min()), us(np.median(a)), us(a.max()))
-            marks = r[:, 1:5]
+            marks = r[:, 1:6]
             vals[(k, "end")] = us(marks[marks > 0].max()) if (marks > 0).any() else us(r[:, 0].max())
         per_replay.append(vals)
     kvs.kvs_timeline_set(None)
@@ -831,7 +863,7 @@ def timeline(name, device, replays=9, keep=5):
     kinds = sorted({k for k, _ in keys}, key=lambda k: med[(k, 0)][0])
     for k in kinds:
         lines.append(f"| {TL_KINDS[k]:40s} | n {int(med[(k, 'n')]):5d} | start {f3(med[(k, 0)])} |")
-        for slot in (1, 4, 2, 3):
+        for slot in (1, 5, 4, 2, 3):
             if (k, slot) in med:
                 lines.append(f"|   {TL_MARKS[slot]:38s} |         | {'':5s} {f3(med[(k, slot)])} |")
     lines += ["", "# launches: first workgroup start, last mark, span, gap after the launch before (us)"]
@@ -880,9 +912,9 @@ def main():
         if args.workload == "all":
             ap.error("--summarize-* needs --workload")
         if args.summarize_stats:
-            summarize_stats(args.summarize_stats, args.workload, args.log)
+            summarize_stats(args.summarize_stats, args.workload, args.log, args.steps)
         if args.summarize_pmc:
-            summarize_pmc(*args.summarize_pmc, args.workload)
+            summarize_pmc(*args.summarize_pmc, args.workload, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block-sparse decode path is built and timed on a "

@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
     if (threadIdx.x < 64)
       write_chunk_summary(lchunk, c * sb, uval + urow + (size_t)c * kChunkTop,
                           uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
+    KVS_TL_MARK(5)
   }
   wait_mem();
   if constexpr (SUMM) {

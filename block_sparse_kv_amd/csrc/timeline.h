@@ -11,6 +11,7 @@
 //   2  the workgroup's own work is stored (for a scoring workgroup: it has bumped the counter)
 //   3  the selection made by the workgroup is stored
 //   4  the chunk summary is stored (long-row scoring)
+//   5  the chunk summary is made, its stores issued
 // A workgroup clears its record's marks when it starts, so after several launches of a kind the
 // records hold the last launch's workgroups (and those of earlier launches past its grid).
 #pragma once
