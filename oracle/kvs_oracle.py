@@ -75,6 +75,15 @@ Readings taken where the pages are silent (each is the spec here):
       s = max|x| / 127 in fp32, stored as fp32; codes round(x * (1/s)), ties away from zero, all
       fp32 operations; an all-zero row has s = 0 and codes 0.  The cached value is the fp32
       product s * code.
+  R28 kv_type INT4 per token and head (the page's int4 per-token-head cache: a dynamic scale per
+      token and head, with a rotation and asymmetric zero-points, neither defined there).  Read as
+      the usual asymmetric integer quantization with a zero point, without a rotation: per token's
+      K or V row of one KV head, lo = min(0, min x), hi = max(0, max x) (the range holds 0, so 0 is
+      cached exactly), s = (hi - lo) / 15, inv = 1 / s, the zero point z = rint(-lo * inv) clamped
+      to 0..15 and codes q = clamp(rint(x * inv) + z, 0, 15), rint rounding half to even; every
+      step an fp32 operation; s stored as fp32, z as a byte.  An all-zero row has s = 0, z = 0 and
+      codes 0.  The cached value is the fp32 product s * (q - z).  Parity unpinned by the pages:
+      the pins hold this reading.
   R22 kv_type Q8_0 (the published llama.cpp format, restated): every run of 32 consecutive channels
       of one token's key or value row is a block with scale d = max|x| / 127 and codes
       q = round(x / d) (ties away from zero), d stored as fp16; the cached value is fp16(d) * q.
@@ -328,6 +337,31 @@ def dequantize_int8_pth(codes, scales):
     c = np.asarray(codes, dtype=np.int8).astype(np.float32)
     sc = np.asarray(scales, dtype=np.float32)
     return (c * sc[..., None]).astype(np.float32).astype(np.float64)
+
+
+def quantize_int4_pth(x):
+    """Codes (uint8 0..15 [..., d]), fp32 scales ([...]) and zero points (uint8 [...]) of x [..., d],
+    one scale and zero point per row (reading R28).  Range, scale, reciprocal and scaled values are
+    fp32 operations; rint rounds half to even."""
+    x = np.asarray(x, dtype=np.float32)
+    lo = np.minimum(x.min(axis=-1), np.float32(0.0)).astype(np.float32)   # the range holds 0
+    hi = np.maximum(x.max(axis=-1), np.float32(0.0)).astype(np.float32)
+    s = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32)  # fp32 ops
+    nz = s != 0
+    with np.errstate(divide="ignore"):
+        inv = np.where(nz, np.float32(1.0) / np.where(nz, s, 1), np.float32(0.0)).astype(np.float32)
+    z = np.clip(np.rint((-lo * inv).astype(np.float32).astype(np.float64)), 0, 15)
+    z = np.where(nz, z, 0).astype(np.int64)
+    t = np.rint((x * inv[..., None]).astype(np.float32).astype(np.float64)).astype(np.int64)
+    codes = np.clip(t + z[..., None], 0, 15).astype(np.uint8)
+    return codes, s, z.astype(np.uint8)
+
+
+def dequantize_int4_pth(codes, scales, zeros):
+    """The cached values fp32(s * (q - z)) as float64 [..., d] (reading R28)."""
+    c = np.asarray(codes, dtype=np.int64) - np.asarray(zeros, dtype=np.int64)[..., None]
+    sc = np.asarray(scales, dtype=np.float32)
+    return (c.astype(np.float32) * sc[..., None]).astype(np.float32).astype(np.float64)
 
 
 def quantize_q4_0(x):

@@ -7,7 +7,7 @@ copy) and raises AssertionError on failure.  What each one rests on:
   * closed forms and identities of the definitions (Mean linearity, Fix = rows of K, SHARED = sum
     of SEPARATE, softmax shift invariance, q = 0 gives the mean of V);
   * hand-worked cases in tests/golden/hand_worked.json, q8_0_worked.json, q4_0_worked.json and
-    int8_pth_worked.json;
+    int8_pth_worked.json, int4_pth_worked.json;
   * the rounding bound, code range and block width of the Q8_0 format;
   * planted-block recall of the selection.
 """
@@ -388,6 +388,62 @@ def check_int8_pth_bound_and_range(orc):
     assert np.all(si == 1.0) and np.array_equal(ci.astype(np.float32), xi)
 
 
+GOLDEN_I4 = os.path.join(os.path.dirname(__file__), "golden", "int4_pth_worked.json")
+
+
+def check_int4_pth_golden(orc):
+    """The hand-worked rows of tests/golden/int4_pth_worked.json: fp32 scale, zero point, codes and
+    cached values."""
+    with open(GOLDEN_I4) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.full(128, c.get("fill", 0.0), dtype=np.float32)
+        for k, v in c["x_nonzero"].items():
+            x[int(k)] = v
+        codes, s, z = orc.quantize_int4_pth(x[None])
+        assert s.dtype == np.float32 and float(s[0]) == c["s"], (c["why"], float(s[0]))
+        assert int(z[0]) == c["z"], (c["why"], int(z[0]))
+        want = np.full(128, c["fill_code"], dtype=np.int64)
+        for k, v in c["codes"].items():
+            want[int(k)] = v
+        assert np.array_equal(codes[0].astype(np.int64), want), c["why"]
+        deq = np.full(128, c.get("deq_fill", 0.0))
+        for k, v in c["deq_nonzero"].items():
+            deq[int(k)] = v
+        assert np.array_equal(orc.dequantize_int4_pth(codes, s, z)[0], deq), c["why"]
+
+
+def check_int4_pth_bound_and_range(orc):
+    """On random fp16 rows: codes and zero points in 0..15, every 0 cached as 0, the row's extremes
+    reach the ends of the code range, and each cached value is within s/2 of x (within s where
+    rounding clamped the code), plus fp32 rounding; integer rows of range 15 holding 0 are exact."""
+    g = np.random.default_rng(28)
+    x = kvsynth.randn_fp16((16, 4, 128), 28).numpy().astype(np.float32) * np.float32(3.0)
+    x = x.astype(np.float16).astype(np.float32)
+    x[0, 0, :] = np.abs(x[0, 0, :])  # rows without negative and without positive values
+    x[1, 1, :] = -np.abs(x[1, 1, :])
+    x[2, 2, 5] = 0.0
+    codes, s, z = orc.quantize_int4_pth(x)
+    assert codes.shape == x.shape and s.shape == x.shape[:-1] and z.shape == x.shape[:-1]
+    assert codes.max() <= 15 and z.max() <= 15
+    deq = orc.dequantize_int4_pth(codes, s, z)
+    assert np.all(deq[x == 0] == 0)
+    lo = np.minimum(x.min(axis=-1), 0)
+    hi = np.maximum(x.max(axis=-1), 0)
+    assert np.all(codes[x == hi[..., None]] >= 14) and np.all(codes[x == lo[..., None]] <= 1)
+    t = x.astype(np.float64) / s.astype(np.float64)[..., None] + z.astype(np.float64)[..., None]
+    clamped = (t > 15.5) | (t < -0.5)
+    err = np.abs(deq - x.astype(np.float64))
+    sc = s.astype(np.float64)[..., None]
+    slack = np.abs(x) * 2.0 ** -20 + sc * 1e-6
+    assert np.all(np.where(clamped, err <= sc + slack, err <= 0.5 * sc + slack))
+    xi = g.integers(-7, 9, (8, 128)).astype(np.float32)
+    xi[:, 3], xi[:, 4], xi[:, 5] = -7.0, 8.0, 0.0
+    ci, si, zi = orc.quantize_int4_pth(xi)
+    assert np.all(si == 1.0) and np.all(zi == 7)
+    assert np.array_equal(orc.dequantize_int4_pth(ci, si, zi), xi.astype(np.float64))
+
+
 GOLDEN_REPS = os.path.join(os.path.dirname(__file__), "golden", "stored_reps_worked.json")
 
 
@@ -627,5 +683,6 @@ ALL_CHECKS = [
     check_q8_integer_rows_exact, check_importance_via_sdpa, check_importance_mass_and_causality,
     check_dynamic_reps_closed_forms, check_preselect_identities, check_q4_golden,
     check_q4_range_and_bound, check_preselect_pooled, check_int8_pth_golden,
-    check_int8_pth_bound_and_range, check_stored_reps_golden,
+    check_int8_pth_bound_and_range, check_int4_pth_golden, check_int4_pth_bound_and_range,
+    check_stored_reps_golden,
 ]

@@ -205,6 +205,51 @@ def _i8_fp16_scale(x):
     return _i8_generic(x, half_scale=True)
 
 
+def _i4_generic(x, away=False, zero_in_range=True, clamp=True, symmetric=False, half_scale=False):
+    x = np.asarray(x, dtype=np.float32)
+    lo, hi = x.min(axis=-1), x.max(axis=-1)
+    if zero_in_range:
+        lo, hi = np.minimum(lo, 0).astype(np.float32), np.maximum(hi, 0).astype(np.float32)
+    if symmetric:
+        s = (np.maximum(np.abs(lo), np.abs(hi)) / np.float32(7.0)).astype(np.float32)
+    else:
+        s = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32)
+    if half_scale:
+        s = s.astype(np.float16).astype(np.float32)
+    inv = np.where(s != 0, np.float32(1) / np.where(s != 0, s, 1), 0).astype(np.float32)
+    rnd = (lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)) if away else np.rint
+    z = np.full(s.shape, 8.0) if symmetric else rnd((-lo * inv).astype(np.float32).astype(np.float64))
+    z = np.where(s != 0, np.clip(z, 0, 15), 0).astype(np.int64)
+    t = rnd((x * inv[..., None]).astype(np.float32).astype(np.float64)).astype(np.int64) + z[..., None]
+    codes = (np.clip(t, 0, 15) if clamp else t & 15).astype(np.uint8)
+    return codes, s, z.astype(np.uint8)
+
+
+def _i4_ties_away(x):
+    return _i4_generic(x, away=True)
+
+
+def _i4_range_without_zero(x):
+    return _i4_generic(x, zero_in_range=False)
+
+
+def _i4_wraps_instead_of_clamp(x):
+    return _i4_generic(x, clamp=False)
+
+
+def _i4_symmetric(x):
+    return _i4_generic(x, symmetric=True)
+
+
+def _i4_fp16_scale(x):
+    return _i4_generic(x, half_scale=True)
+
+
+def _i4_dequant_drops_zero_point(codes, scales, zeros):
+    c = np.asarray(codes, dtype=np.int64)
+    return (c.astype(np.float32) * np.asarray(scales, np.float32)[..., None]).astype(np.float32).astype(np.float64)
+
+
 _orig_preselect = orc.preselect_blocks
 
 
@@ -327,6 +372,12 @@ MUTANTS = [
     ("quantize_int8_pth", _i8_div_128),
     ("quantize_int8_pth", _i8_block_32),
     ("quantize_int8_pth", _i8_fp16_scale),
+    ("quantize_int4_pth", _i4_ties_away),
+    ("quantize_int4_pth", _i4_range_without_zero),
+    ("quantize_int4_pth", _i4_wraps_instead_of_clamp),
+    ("quantize_int4_pth", _i4_symmetric),
+    ("quantize_int4_pth", _i4_fp16_scale),
+    ("dequantize_int4_pth", _i4_dequant_drops_zero_point),
     ("stored_reps", _stored_reps_truncated),
     ("stored_reps", _stored_reps_mean_fp16),
     ("stored_reps", _stored_reps_ties_away),
