@@ -104,6 +104,9 @@ WORKLOADS = {
     # and over an INT8 cache with one fp32 scale per token and KV head
     "128k-max-i8": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
                         layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="int8_pth"),
+    # and over an INT4 cache with one fp32 scale and one zero point per token and KV head
+    "128k-max-i4": dict(L=131072, Hq=32, Hkv=8, I=128, W=4096, k=96, rep="max", mode="shared",
+                        layers=1, replicas=16, n_hot=50, hot_per_head=False, seed=20260002, kv="int4_pth"),
 }
 
 
@@ -167,7 +170,8 @@ def required_bytes(w, L=None):
     R = {"quest": 2, "max": 1, "mean": 1, "fix": w.get("rep_num", 1), "dynamic": w.get("rep_num", 1)}[w["rep"]]
     rep_elem = 4 if w["rep"] == "mean" else 2
     # bytes of one token's K (or V) row: fp16, or codes + one fp16 scale per 32 channels
-    row = {"q8_0": D + (D // 32) * 2, "q4_0": D // 2 + (D // 32) * 2, "int8_pth": D + 4}.get(w.get("kv"), D * 2)
+    row = {"q8_0": D + (D // 32) * 2, "q4_0": D // 2 + (D // 32) * 2, "int8_pth": D + 4,
+           "int4_pth": D // 2 + 4 + 1}.get(w.get("kv"), D * 2)
     return dict(q=Hq * D * 2, reps=ncand * Hkv * R * D * rep_elem, kv=Hkv * T * row * 2,
                 out=Hq * D * 4, tokens=T, ncand=ncand, k_eff=k_eff)
 

@@ -33,8 +33,9 @@ KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_MISALIGNED, KVS_ERR_WO
     KVS_ERR_HIP = 0, -1, -2, -3, -4, -5
 REP_QUEST, REP_MAX, REP_MEAN, REP_FIX, REP_DYNAMIC = 0, 1, 2, 3, 4
 HEADS_SEPARATE, HEADS_SHARED = 0, 1
-KV_FP16, KV_Q8_0, KV_Q4_0, KV_INT8_PTH = 0, 1, 2, 3
-KV_NAMES = {"fp16": KV_FP16, "q8_0": KV_Q8_0, "q4_0": KV_Q4_0, "int8_pth": KV_INT8_PTH}
+KV_FP16, KV_Q8_0, KV_Q4_0, KV_INT8_PTH, KV_INT4_PTH = 0, 1, 2, 3, 4
+KV_NAMES = {"fp16": KV_FP16, "q8_0": KV_Q8_0, "q4_0": KV_Q4_0, "int8_pth": KV_INT8_PTH,
+            "int4_pth": KV_INT4_PTH}
 REP_NAMES = {"quest": REP_QUEST, "max": REP_MAX, "mean": REP_MEAN, "fix": REP_FIX,
              "dynamic": REP_DYNAMIC}
 MODE_NAMES = {"separate": HEADS_SEPARATE, "shared": HEADS_SHARED}

@@ -67,6 +67,7 @@ static void launch_tiles_g(const AttnArgs& A, dim3 grid, bool il, bool phys, hip
   if (A.P.kv == kKvQ8) launch_tiles_gq<G, kKvQ8>(A, grid, il, phys, s);
   else if (A.P.kv == kKvQ4) launch_tiles_gq<G, kKvQ4>(A, grid, il, phys, s);
   else if (A.P.kv == kKvI8) launch_tiles_gq<G, kKvI8>(A, grid, il, phys, s);
+  else if (A.P.kv == kKvI4) launch_tiles_gq<G, kKvI4>(A, grid, il, phys, s);
   else launch_tiles_gq<G, kKvFp16>(A, grid, il, phys, s);
 }
 

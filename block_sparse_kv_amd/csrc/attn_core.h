@@ -108,13 +108,45 @@ __device__ inline uint4 i8_dq8(uint32_t w0, uint32_t w1, float s) {
     const int b = 16 * (j & 1);
     const float a = (float)((w >> b) & 0xFFu) - 128.0f;  // exact
     const float c = (float)((w >> (b + 8)) & 0xFFu) - 128.0f;
-    const half2v_t hv = {(_Float16)(a * s), (_Float16)(c * s)};
+    float as = a * s, cs = c * s;
+    keep_fp32(as);  // rounded to fp32 first, then to fp16 (no fused mixed-precision product)
+    keep_fp32(cs);
+    const half2v_t hv = {(_Float16)as, (_Float16)cs};
     o[j] = __builtin_bit_cast(uint32_t, hv);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0 or per-token INT8 records).
+// 8 INT4 codes of one word (Q4_0's layout) less the token's zero point z, as 8 fp16 values, exactly:
+// (w >> 4i) & 0x000F000F under the exponent pattern 0x6400 is the fp16 pair 1024 + code, and
+// subtracting 1024 + z leaves code - z (|code - z| <= 15).
+__device__ inline uint4 i4_codes8(uint32_t w, int z) {
+  const _Float16 b = (_Float16)(float)(1024 + z);
+  const half2v_t bias = {b, b};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v_t, x) - bias);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// 8 INT4 codes of one word as 8 fp16 values fp16(fp32(s * (code - z))).
+__device__ inline uint4 i4_dq8(uint32_t w, float s, int z) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = (float)((int)((w >> (4 * i)) & 0xFu) - z) * s;
+    float c = (float)((int)((w >> (16 + 4 * i)) & 0xFu) - z) * s;
+    keep_fp32(a);  // rounded to fp32 first, then to fp16 (no fused mixed-precision product)
+    keep_fp32(c);
+    const half2v_t hv = {(_Float16)a, (_Float16)c};
+    o[i] = __builtin_bit_cast(uint32_t, hv);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0, or per-token INT8 or INT4 records).
 template <int G, int KV = kKvFp16>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
@@ -132,8 +164,10 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   uint4 kr[2][4], vr[8];
   uint4 vc[4];    // Q8_0 / Q4_0 / INT8: V codes and scales, dequantized when V is staged
   uint32_t vs[4];
-  float ksc[2];    // INT8: the fp32 scale of the lane's K token 32w + 16g + lc
-  f32x4_t vsc;     // INT8: the fp32 scales of the lane's 4 V tokens
+  float ksc[2];    // INT8 / INT4: the fp32 scale of the lane's K token 32w + 16g + lc
+  f32x4_t vsc;     // INT8 / INT4: the fp32 scales of the lane's 4 V tokens
+  uint2 vq4[4];    // INT4: V codes of the lane's 4 tokens (16 channels each)
+  uint32_t vz4 = 0;  // INT4: the zero points of the lane's 4 V tokens, one byte each
   if constexpr (KV == kKvFp16) {
     // fp16 tile: K rows of MFMA m are channels 32m + 8*lq .. +8
     const size_t off = ((size_t)phys * P.Hkv + h) * kTile;
@@ -184,6 +218,47 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       kr[g][1] = q4_dq8(kc[g].y, ks[g]);
       kr[g][2] = q4_dq8(kc[g].z, ks[g]);
       kr[g][3] = q4_dq8(kc[g].w, ks[g]);
+    }
+  } else if constexpr (KV == kKvI4) {
+    // INT4 record, one fp32 scale and one zero point per token: a lane's K codes are the 32 channels
+    // 32*lq .. +32 of its token, as for Q4_0 (one 16-byte load, MFMA m takes word m); they enter the
+    // product as the exact fp16 integers code - z, and the S rows are scaled by their tokens' fp32
+    // scales afterwards, as for INT8.  V: lane l takes channels 16*(l%8) .. +16 (8 bytes of codes) of
+    // the wave's four consecutive tokens 4*(l/8) .. +3, so their scales are one 16-byte load and their
+    // zero points one 4-byte load; scaled when staged.
+    const size_t rec = ((size_t)phys * P.Hkv + h) * kI4Record;
+    const unsigned char* Kq = reinterpret_cast<const unsigned char*>(k_pool) + rec;
+    const unsigned char* Vq = reinterpret_cast<const unsigned char*>(v_pool) + rec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
+      qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
+    }
+    uint4 kc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) kc[g] = ld_stream16(Kq + (32 * w + 16 * g + lc) * (kDim / 2) + 16 * lq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * w + 4 * (lane >> 3) + i;
+      vq4[i] = *reinterpret_cast<const uint2*>(Vq + tok * (kDim / 2) + 8 * (lane & 7));
+    }
+    // the scales and zero points last: they are needed after the codes
+    int kz[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tok = 32 * w + 16 * g + lc;
+      ksc[g] = *reinterpret_cast<const float*>(Kq + kI4Scales + tok * 4);
+      kz[g] = Kq[kI4Zeros + tok];
+    }
+    vsc = ld_stream16f(Vq + kI4Scales + (32 * w + 4 * (lane >> 3)) * 4);
+    vz4 = *reinterpret_cast<const uint32_t*>(Vq + kI4Zeros + 32 * w + 4 * (lane >> 3));
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the arithmetic below
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kr[g][0] = i4_codes8(kc[g].x, kz[g]);
+      kr[g][1] = i4_codes8(kc[g].y, kz[g]);
+      kr[g][2] = i4_codes8(kc[g].z, kz[g]);
+      kr[g][3] = i4_codes8(kc[g].w, kz[g]);
     }
   } else if constexpr (KV == kKvI8) {
     // INT8 record, one fp32 scale per token: K codes load as for Q8_0 below and enter the product
@@ -278,7 +353,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = 32 * w + 16 * g + 4 * lq + i;
-      if constexpr (KV == kKvI8) S[g][i] *= __shfl(ksc[g], 4 * lq + i, 64);  // token 4lq + i's scale
+      if constexpr (KV == kKvI8 || KV == kKvI4) S[g][i] *= __shfl(ksc[g], 4 * lq + i, 64);  // token 4lq + i's scale
       S[g][i] = tok < ntok ? S[g][i] * sl2 : -INFINITY;
       mx = fmaxf(mx, S[g][i]);
     }
@@ -310,14 +385,18 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       for (int u = 0; u < 4; ++u)
         *reinterpret_cast<uint4*>(row + 16 * u) = in ? q4_dq8(cw[u], vs[i]) : make_uint4(0, 0, 0, 0);
     }
-  } else if constexpr (KV == kKvQ8 || KV == kKvI8) {
+  } else if constexpr (KV == kKvQ8 || KV == kKvI8 || KV == kKvI4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // the wave's token: chunk t / 4, row t % 4
-      const int t = KV == kKvI8 ? 4 * (lane >> 3) + i : 8 * i + (lane >> 3);
+      const int t = KV == kKvQ8 ? 8 * i + (lane >> 3) : 4 * (lane >> 3) + i;
       const bool in = 32 * w + t < ntok;
       uint4 a, b;
-      if constexpr (KV == kKvI8) {
+      if constexpr (KV == kKvI4) {
+        const int z = (int)((vz4 >> (8 * i)) & 0xFFu);
+        a = i4_dq8(vq4[i].x, vsc[i], z);
+        b = i4_dq8(vq4[i].y, vsc[i], z);
+      } else if constexpr (KV == kKvI8) {
         a = i8_dq8(vc[i].x, vc[i].y, vsc[i]);
         b = i8_dq8(vc[i].z, vc[i].w, vsc[i]);
       } else {

@@ -53,23 +53,25 @@ __device__ inline void load_k_tile(const void* __restrict__ k_pool, size_t tile,
 #pragma unroll
       for (int m = 0; m < 4; ++m) T.kr[g][m] = ld_stream16(Kt + (32 * w + 16 * g + lc) * kDim + 32 * m + 8 * lq);
   } else {
-    constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : kQ8Record;
-    constexpr int kCodes = KV == kKvQ4 ? kQ4Codes : kQ8Codes;
+    constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : KV == kKvI4 ? kI4Record : kQ8Record;
+    constexpr int kCodes = KV == kKvQ4 || KV == kKvI4 ? kQ4Codes : kQ8Codes;  // INT4: the scales follow
     const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + tile * (size_t)kRec;
     uint2 raw[2][4];  // every load first, then the conversions
+    int kz[2] = {0, 0};  // INT4: the zero point of the lane's K token
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int tok = 32 * w + 16 * g + lc;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        if constexpr (KV == kKvQ4)
+        if constexpr (KV == kKvQ4 || KV == kKvI4)
           raw[g][m].x = *reinterpret_cast<const uint32_t*>(rec + tok * (kDim / 2) + 4 * (4 * m + lq));
         else
           raw[g][m] = *reinterpret_cast<const uint2*>(rec + tok * kDim + 32 * m + 8 * lq);
       }
       const int t0 = 32 * w + 16 * g + 4 * lq;
-      if constexpr (KV == kKvI8) {
+      if constexpr (KV == kKvI8 || KV == kKvI4) {
         T.sc[g][0] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 4);
+        if constexpr (KV == kKvI4) kz[g] = rec[kI4Zeros + tok];
       } else {
         T.sc[g][0] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 8);
         T.sc[g][1] = *reinterpret_cast<const uint4*>(rec + kCodes + t0 * 8 + 16);
@@ -79,8 +81,9 @@ __device__ inline void load_k_tile(const void* __restrict__ k_pool, size_t tile,
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        T.kr[g][m] = KV == kKvQ4 ? q4_dq8(raw[g][m].x, 0x3C00u)  // fp16 1.0: code - 8 exactly
-                                 : i8_codes8(raw[g][m].x, raw[g][m].y);
+        T.kr[g][m] = KV == kKvQ4   ? q4_dq8(raw[g][m].x, 0x3C00u)  // fp16 1.0: code - 8 exactly
+                     : KV == kKvI4 ? i4_codes8(raw[g][m].x, kz[g])   // code - z exactly
+                                   : i8_codes8(raw[g][m].x, raw[g][m].y);
   }
 }
 
@@ -116,15 +119,15 @@ __device__ inline void q_rows_from_lds(const uint4* qs, int rg, half8_t (&qb)[4]
 
 // S = K Q^T for token group gg of this wave and the 16 rows of qb (lane: tokens 4lq + i, row lc).
 // Q8_0 / Q4_0: each block's product is scaled by its token's block scale before the sum over blocks;
-// INT8: the sum is scaled by the token's scale.
+// INT8 / INT4: the sum is scaled by the token's scale.
 template <int KV>
 __device__ inline f32x4_t imp_s(const KTile<KV>& T, const half8_t (&qb)[4], int gg) {
   f32x4_t S = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KV == kKvFp16 || KV == kKvI8) {
+  if constexpr (KV == kKvFp16 || KV == kKvI8 || KV == kKvI4) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       S = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, T.kr[gg][m]), qb[m], S, 0, 0, 0);
-    if constexpr (KV == kKvI8) {
+    if constexpr (KV == kKvI8 || KV == kKvI4) {
       const f32x4_t s = __builtin_bit_cast(f32x4_t, T.sc[gg][0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[i] *= s[i];
@@ -363,11 +366,12 @@ __global__ __launch_bounds__(64) void dyn_reps_kernel(Params P, const void* __re
       row8 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k_pool) + tile * kTile +
                                              (size_t)pick[i] * kDim + 8 * (lane & 15));
     } else {  // a quantized cache: the cached values, rounded to fp16 once
-      constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : kQ8Record;
+      constexpr int kRec = KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : KV == kKvI4 ? kI4Record : kQ8Record;
       const unsigned char* rec = static_cast<const unsigned char*>(k_pool) + tile * (size_t)kRec;
       float f[8];
       if constexpr (KV == kKvQ4) q4_row8(rec, pick[i], lane & 15, f);
       else if constexpr (KV == kKvI8) i8_row8(rec, pick[i], lane & 15, f);
+      else if constexpr (KV == kKvI4) i4_row8(rec, pick[i], lane & 15, f);
       else q8_row8(rec, pick[i], lane & 15, f);
       uint32_t wd[4];
 #pragma unroll
@@ -395,6 +399,7 @@ hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs
     case kKvQ8: KVS_IMP_STATS(kKvQ8); break;
     case kKvQ4: KVS_IMP_STATS(kKvQ4); break;
     case kKvI8: KVS_IMP_STATS(kKvI8); break;
+    case kKvI4: KVS_IMP_STATS(kKvI4); break;
     default: KVS_IMP_STATS(kKvFp16); break;
   }
 #undef KVS_IMP_STATS
@@ -408,6 +413,7 @@ hipError_t launch_token_importance(const Params& P, const void* q_obs, int n_obs
     case kKvQ8: KVS_IMP_ACCUM(kKvQ8); break;
     case kKvQ4: KVS_IMP_ACCUM(kKvQ4); break;
     case kKvI8: KVS_IMP_ACCUM(kKvI8); break;
+    case kKvI4: KVS_IMP_ACCUM(kKvI4); break;
     default: KVS_IMP_ACCUM(kKvFp16); break;
   }
 #undef KVS_IMP_ACCUM
@@ -434,6 +440,7 @@ hipError_t launch_dynamic_reps(const Params& P, const void* k_pool, const float*
     case kKvQ8: hipLaunchKernelGGL(dyn_reps_kernel<kKvQ8>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
     case kKvQ4: hipLaunchKernelGGL(dyn_reps_kernel<kKvQ4>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
     case kKvI8: hipLaunchKernelGGL(dyn_reps_kernel<kKvI8>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
+    case kKvI4: hipLaunchKernelGGL(dyn_reps_kernel<kKvI4>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
     default: hipLaunchKernelGGL(dyn_reps_kernel<kKvFp16>, grid, dim3(64), 0, s, P, k_pool, imp, table, max_blocks, seq_lens, rp); break;
   }
   return hipGetLastError();

@@ -58,7 +58,7 @@ int make_params(const kvs_config* c, Params* P) {
     return KVS_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return KVS_ERR_INVALID_ARG;
   if (c->kv_type != KVS_KV_FP16 && c->kv_type != KVS_KV_Q8_0 && c->kv_type != KVS_KV_Q4_0 &&
-      c->kv_type != KVS_KV_INT8_PTH)
+      c->kv_type != KVS_KV_INT8_PTH && c->kv_type != KVS_KV_INT4_PTH)
     return KVS_ERR_INVALID_ARG;
   const int R = rep_count_of(c);
   if (R < 0) return KVS_ERR_INVALID_ARG;
@@ -345,6 +345,7 @@ size_t kvs_kv_bytes_per_block(const kvs_config* cfg) {
   const size_t rec = P.kv == kvs::kKvQ8   ? (size_t)kvs::kQ8Record
                      : P.kv == kvs::kKvQ4 ? (size_t)kvs::kQ4Record
                      : P.kv == kvs::kKvI8 ? (size_t)kvs::kI8Record
+                     : P.kv == kvs::kKvI4 ? (size_t)kvs::kI4Record
                                           : (size_t)kvs::kTile * 2;
   return (size_t)P.Hkv * rec;
 }

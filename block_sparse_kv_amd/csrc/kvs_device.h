@@ -21,6 +21,11 @@ constexpr int kQ4Codes = kBlock * kDim / 2;                            // bytes 
 constexpr int kQ4Record = kQ4Codes + kBlock * (kDim / kQ8Group) * 2;  // 9216 bytes
 // INT8 with one fp32 scale per token row: codes as Q8_0's, then 128 fp32 scales
 constexpr int kI8Record = kQ8Codes + kBlock * 4;                       // 16896 bytes
+// INT4 with one fp32 scale and one zero point per token row: codes as Q4_0's, then 128 fp32 scales,
+// then 128 zero-point bytes
+constexpr int kI4Scales = kQ4Codes;                                    // offset of the scales
+constexpr int kI4Zeros = kQ4Codes + kBlock * 4;                        // offset of the zero points
+constexpr int kI4Record = kI4Zeros + kBlock;                           // 8832 bytes
 
 // Long-row selection from chunk summaries: a chunk is kChunkBlocks consecutive blocks of a score row,
 // summarised by its kChunkTop best candidates.
@@ -29,7 +34,7 @@ constexpr int kChunkTop = 8;
 
 enum Method { kQuest = 0, kMax = 1, kMean = 2, kFix = 3, kDynamic = 4 };  // Dynamic: scored like Fix
 enum Mode { kSeparate = 0, kShared = 1 };
-enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2, kKvI8 = 3 };
+enum KvType { kKvFp16 = 0, kKvQ8 = 1, kKvQ4 = 2, kKvI8 = 3, kKvI4 = 4 };
 
 // Launch-time constants of one call (passed by value to every kernel).
 struct Params {
@@ -247,6 +252,12 @@ __device__ inline __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
 __device__ inline float ld_coh_f1(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSc1));
 }
+// The per-token-head caches' values are fp32 products that are not exact: keep_fp32 makes one an fp32
+// value in a register, so that a later conversion to fp16 rounds it a second time, as the cached value
+// is defined, instead of the compiler fusing the product and the conversion into one mixed-precision
+// instruction that rounds the exact product once.
+__device__ inline void keep_fp32(float& v) { __asm__ volatile("" : "+v"(v)); }
+
 // Wait until this wave's memory operations have completed (vmcnt 0; 0x0F70 leaves expcnt and lgkmcnt
 // at their maxima, so only vmcnt is waited on).
 __device__ inline void wait_mem() {

@@ -177,9 +177,77 @@ __global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t* __rest
   if (half == 0) *reinterpret_cast<float*>(rec + kQ8Codes + tok * 4) = sc;
 }
 
+// INT4 with one scale and one zero point per token and KV head (the per-token-head int4 cache, read
+// as asymmetric quantization without a rotation): over the token's 128 channels lo = min(0, min x),
+// hi = max(0, max x), s = (hi - lo) / 15 kept in fp32, inv = 1 / s, z = clamp(rint(-lo * inv), 0, 15),
+// codes clamp(rint(x * inv) + z, 0, 15); rint rounds half to even, every step is an fp32 operation
+// (IEEE division, no contraction).  Same lane mapping as Q8_0, the two lanes of a token combining
+// their extremes with one lane exchange; the codes are packed as Q4_0's.
+__global__ __launch_bounds__(256) void quantize_i4_kernel(const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ ids, int Hkv,
+                                                          unsigned char* __restrict__ dst) {
+#pragma clang fp contract(off)
+  const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
+  const size_t tile = (size_t)ids[i] * Hkv + h;
+  const int tok = t >> 1, half = t & 1;
+  const uint4* in = reinterpret_cast<const uint4*>(src + tile * kTile + tok * kDim + 64 * half);
+  uint4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) raw[u] = in[u];
+  float x[64];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * u + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xFFFFu));
+      x[8 * u + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+    }
+  }
+  float lo = 0.f, hi = 0.f;  // the range holds 0
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    lo = fminf(lo, x[e]);
+    hi = fmaxf(hi, x[e]);
+  }
+  lo = fminf(lo, __shfl_xor(lo, 1, 64));  // the token's other half
+  hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
+  const float sc = (hi - lo) / 15.0f;
+  const float inv = sc != 0.f ? 1.0f / sc : 0.f;
+  const float nlo = -lo;
+  const int z = sc != 0.f ? min(15, max(0, (int)rintf(nlo * inv))) : 0;
+  auto code = [&](float v) {
+    const float p = v * inv;
+    return (uint32_t)min(15, max(0, (int)rintf(p) + z));
+  };
+  uint32_t words[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const uint32_t c0 = code(x[8 * k + 2 * i2]);
+      const uint32_t c1 = code(x[8 * k + 2 * i2 + 1]);
+      word |= (c0 << (4 * i2)) | (c1 << (16 + 4 * i2));
+    }
+    words[k] = word;
+  }
+  unsigned char* rec = dst + tile * kI4Record;
+  uint4* co = reinterpret_cast<uint4*>(rec + tok * (kDim / 2) + 32 * half);
+  co[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  co[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  if (half == 0) {
+    *reinterpret_cast<float*>(rec + kI4Scales + tok * 4) = sc;
+    rec[kI4Zeros + tok] = (unsigned char)z;
+  }
+}
+
 hipError_t launch_quantize_q8(const Params& P, const void* src, const int32_t* ids, int n, void* dst,
                               hipStream_t s) {
-  if (P.kv == kKvI8)
+  if (P.kv == kKvI4)
+    hipLaunchKernelGGL(quantize_i4_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
+  else if (P.kv == kKvI8)
     hipLaunchKernelGGL(quantize_i8_kernel, dim3(P.Hkv, n), dim3(256), 0, s,
                        static_cast<const uint16_t*>(src), ids, P.Hkv, static_cast<unsigned char*>(dst));
   else if (P.kv == kKvQ4)

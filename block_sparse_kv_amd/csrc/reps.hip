@@ -8,8 +8,9 @@
 // with lane shuffles and across the 4 waves through LDS.  The kernel streams K once (HBM-bound).
 // A Q8_0 cache (kv_type; the llama.cpp block format) is read the same way, 8 codes and the scale of
 // their 32-channel block per token; scale * code is exact in fp32, and the reps are rounded to fp16
-// once, at the store.  Q4_0 and the per-token INT8 cache likewise (INT8: the cached value is the fp32
-// product of the token's scale and the code).
+// once, at the store.  Q4_0 and the per-token INT8 and INT4 caches likewise (INT8: the cached value is
+// the fp32 product of the token's scale and the code; INT4: of the scale and the code less the token's
+// zero point).
 #include "kvs_device.h"
 #include "kvs_launch.h"
 #include "quant_rows.h"
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
   const size_t p = (size_t)ids[blockIdx.x];
   const uint16_t* tile = static_cast<const uint16_t*>(k_pool) + (p * Hkv + h) * kTile;
   const unsigned char* rec = static_cast<const unsigned char*>(k_pool) +
-                             (p * Hkv + h) * (size_t)(KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : kQ8Record);
+                             (p * Hkv + h) * (size_t)(KV == kKvQ4 ? kQ4Record : KV == kKvI8 ? kI8Record : KV == kKvI4 ? kI4Record : kQ8Record);
   constexpr bool Q8 = KV != kKvFp16;  // a quantized record
   const int t = threadIdx.x, c = t & 15, r = t >> 4;
 
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
         float f[8];
         if constexpr (KV == kKvQ4) q4_row8(rec, rr * stride, c, f);
         else if constexpr (KV == kKvI8) i8_row8(rec, rr * stride, c, f);
+        else if constexpr (KV == kKvI4) i4_row8(rec, rr * stride, c, f);
         else q8_row8(rec, rr * stride, c, f);
         uint32_t w[4];
 #pragma unroll
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(256) void build_reps_kernel(const void* __restrict_
       if constexpr (KV == kKvQ4) q4_row8(rec, r + 16 * i, c, f);
       else if constexpr (KV == kKvQ8) q8_row8(rec, r + 16 * i, c, f);
       else if constexpr (KV == kKvI8) i8_row8(rec, r + 16 * i, c, f);
+      else if constexpr (KV == kKvI4) i4_row8(rec, r + 16 * i, c, f);
       else unpack8(raw[i], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -127,6 +130,7 @@ hipError_t launch_build_reps(const Params& P, const void* k_pool, const int32_t*
   if (P.kv == kKvQ8) launch_reps_q<kKvQ8>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   else if (P.kv == kKvQ4) launch_reps_q<kKvQ4>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   else if (P.kv == kKvI8) launch_reps_q<kKvI8>(P, grid, k_pool, ids, rep_num, rep_pool, s);
+  else if (P.kv == kKvI4) launch_reps_q<kKvI4>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   else launch_reps_q<kKvFp16>(P, grid, k_pool, ids, rep_num, rep_pool, s);
   return hipGetLastError();
 }

@@ -27,6 +27,7 @@ hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* s
     case kKvQ8: return launch_score_select_kv<kKvQ8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
     case kKvQ4: return launch_score_select_kv<kKvQ4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
     case kKvI8: return launch_score_select_kv<kKvI8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
+    case kKvI4: return launch_score_select_kv<kKvI4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
     default: return launch_score_select_kv<kKvFp16>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
   }
 }
@@ -37,6 +38,7 @@ hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, int32_t* 
     case kKvQ8: return launch_topk_il_wide_kv<kKvQ8>(A, scores, sel, sel_count, tiles, batch, s);
     case kKvQ4: return launch_topk_il_wide_kv<kKvQ4>(A, scores, sel, sel_count, tiles, batch, s);
     case kKvI8: return launch_topk_il_wide_kv<kKvI8>(A, scores, sel, sel_count, tiles, batch, s);
+    case kKvI4: return launch_topk_il_wide_kv<kKvI4>(A, scores, sel, sel_count, tiles, batch, s);
     default: return launch_topk_il_wide_kv<kKvFp16>(A, scores, sel, sel_count, tiles, batch, s);
   }
 }
@@ -58,6 +60,7 @@ hipError_t launch_presel_step(const AttnArgs& A, const void* rep_pool, const int
     case kKvQ8: return launch_presel_step_kv<kKvQ8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
     case kKvQ4: return launch_presel_step_kv<kKvQ4>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
     case kKvI8: return launch_presel_step_kv<kKvI8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+    case kKvI4: return launch_presel_step_kv<kKvI4>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
     default: return launch_presel_step_kv<kKvFp16>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
   }
 }

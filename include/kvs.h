@@ -46,6 +46,9 @@
  *                16+4i..19+4i), then fp16 scales [128 tokens][4]; value scale * (code - 8)
  *                kv_type INT8_PTH: [n_phys][Hkv] records of 16896 bytes: int8 codes [128 tokens][128],
  *                then fp32 scales [128 tokens]; value fp32(scale[t] * code[t][c])
+ *                kv_type INT4_PTH: [n_phys][Hkv] records of 8832 bytes: codes as Q4_0's, then fp32
+ *                scales [128 tokens], then uint8 zero points [128 tokens]; value
+ *                fp32(scale[t] * (code[t][c] - zero[t]))
  *   rep_pool     [n_phys][Hkv][R][128]  fp16, except fp32 for KVS_REP_MEAN.
  *                R = 2 for Quest (r=0 channel-wise min key, r=1 channel-wise max key), 1 for Max
  *                and Mean, rep_num for Fix (r-th rep = token r*(128/rep_num) of the block).
@@ -105,8 +108,14 @@ typedef enum { KVS_HEADS_SEPARATE = 0, KVS_HEADS_SHARED = 1 } kvs_head_select_mo
  * INT8_PTH is the int8 cache with one dynamic scale per token and head of the page "Long context:
  * 262k with KVarN, and the built-in KV modes" (section "The built-in per-token-head modes"), with
  * Q8_0's arithmetic over a whole 128-channel row:
- *   s = max|x| / 127 kept in fp32, codes round(x / s) ties away from zero, value fp32(s * code). */
-typedef enum { KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2, KVS_KV_INT8_PTH = 3 } kvs_kv_type;
+ *   s = max|x| / 127 kept in fp32, codes round(x / s) ties away from zero, value fp32(s * code).
+ * INT4_PTH is that page's int4 per-token-head cache (dynamic scales with asymmetric zero points; its
+ * rotation is not defined there and not applied), read as asymmetric quantization per token's row:
+ *   lo = min(0, min x), hi = max(0, max x), s = (hi - lo) / 15 kept in fp32, z = rint(-lo / s) in
+ *   0..15 kept as a byte, codes clamp(rint(x / s) + z, 0, 15), rint to even, value fp32(s * (code - z)). */
+typedef enum {
+  KVS_KV_FP16 = 0, KVS_KV_Q8_0 = 1, KVS_KV_Q4_0 = 2, KVS_KV_INT8_PTH = 3, KVS_KV_INT4_PTH = 4
+} kvs_kv_type;
 
 /* Host struct.  Field order and types are part of the ABI. */
 typedef struct kvs_config {
@@ -156,11 +165,12 @@ int kvs_rep_count(const kvs_config* cfg /* host */);
 size_t kvs_rep_bytes_per_block(const kvs_config* cfg /* host */);
 
 /* Bytes of one physical block of k_pool (or v_pool) over all KV heads: Hkv * 32768 for FP16,
- * Hkv * 17408 for Q8_0, Hkv * 9216 for Q4_0, Hkv * 16896 for INT8_PTH; 0 on a bad config. */
+ * Hkv * 17408 for Q8_0, Hkv * 9216 for Q4_0, Hkv * 16896 for INT8_PTH, Hkv * 8832 for INT4_PTH;
+ * 0 on a bad config. */
 size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
 
 /*
- * kvs_quantize_kv -- Q8_0 / Q4_0 / INT8_PTH records of fp16 tiles [kv_type, see kvs_kv_type].  For each of
+ * kvs_quantize_kv -- Q8_0 / Q4_0 / INT8_PTH / INT4_PTH records of fp16 tiles [kv_type, see kvs_kv_type].  For each of
  * the n_blocks physical ids in phys_block_ids (device int32) and each KV head, reads the fp16 tile
  * [128 tokens][128] of src_pool (laid out as an FP16 pool) and writes the record at the same id of
  * dst_pool (laid out as a pool of cfg->kv_type).  Per 32 channels of a token, in fp32 with IEEE
@@ -168,7 +178,10 @@ size_t kvs_kv_bytes_per_block(const kvs_config* cfg /* host */);
  * d = 0, codes 0); Q4_0 d = m / -8 for m the first value of largest magnitude (+0 for an all-zero
  * block), codes min(15, trunc(x * (1/d) + 8.5)) (all-zero: 8).  d is stored rounded to fp16.
  * INT8_PTH: per token, s = max|x| / 127 over its 128 channels, codes as Q8_0's, s stored as fp32.
- * Used for keys and values alike.  cfg->kv_type must be Q8_0, Q4_0 or INT8_PTH.
+ * INT4_PTH: per token, lo = min(0, min x), hi = max(0, max x), s = (hi - lo) / 15, inv = 1 / s,
+ * z = clamp(rint(-lo * inv), 0, 15), codes clamp(rint(x * inv) + z, 0, 15), rint to even (an all-zero
+ * row: s = 0, z = 0, codes 0); s stored as fp32, z as a byte.
+ * Used for keys and values alike.  cfg->kv_type must be Q8_0, Q4_0, INT8_PTH or INT4_PTH.
  * n_blocks == 0 is a no-op.  Both pools 16-byte aligned.
  */
 int kvs_quantize_kv(const kvs_config* cfg, const void* src_pool, const int32_t* phys_block_ids,

@@ -9,7 +9,7 @@ Acceptance (same seeded inputs on both sides):
     blocks scoring at least the (k+1)-th (both within the band) is accepted.
   * Attention: max |gpu - ref| <= 2e-3, where ref is the oracle's attention over the GPU's own
     selection (a different legal selection attends different tokens).
-  * A Q8_0, Q4_0 or INT8 (per token and head) cache (kv_type): the oracle works on the dequantized
+  * A Q8_0, Q4_0, INT8 or INT4 (per token and head) cache (kv_type): the oracle works on the dequantized
     keys and values of its own
     quantization of the same fp16 rows (the codes are bit-exact, tests/test_gpu_q8.py) and on reps
     stored as the rep pool stores them (fp16, Mean fp32).  The same bounds hold: the kernels round
@@ -75,8 +75,8 @@ class Case:
                  device="cuda", spare_blocks=3):
         self.cfg = cfg
         kv = getattr(cfg, "kv_type", "fp16")
-        self.kv = {1: "q8_0", 2: "q4_0", 3: "int8_pth", 0: "fp16"}.get(kv, kv)
-        self.q8 = self.kv != "fp16"  # a quantized cache (Q8_0, Q4_0 or INT8 per token and head)
+        self.kv = {1: "q8_0", 2: "q4_0", 3: "int8_pth", 4: "int4_pth", 0: "fp16"}.get(kv, kv)
+        self.q8 = self.kv != "fp16"  # a quantized cache (Q8_0, Q4_0, or INT8 / INT4 per token and head)
         seqs = []
         for i, L in enumerate(lens):
             ie, ls, cand = orc.regions(L, B, cfg.initial_len, cfg.local_len)
@@ -100,7 +100,8 @@ class Case:
             self.v_pool = ops.quantize_kv(cfg, self.pb.v_pool, ids, ops.alloc_q8_pool(cfg, n_phys, device))
             qf, df = {"q8_0": (orc.quantize_q8_0, orc.dequantize_q8_0),
                       "q4_0": (orc.quantize_q4_0, orc.dequantize_q4_0),
-                      "int8_pth": (orc.quantize_int8_pth, orc.dequantize_int8_pth)}[self.kv]
+                      "int8_pth": (orc.quantize_int8_pth, orc.dequantize_int8_pth),
+                      "int4_pth": (orc.quantize_int4_pth, orc.dequantize_int4_pth)}[self.kv]
             self.host = [(q, df(*qf(K)), df(*qf(V))) for q, K, V in self.host]
 
     # --- oracle side --------------------------------------------------------------------------

@@ -67,7 +67,7 @@ def test_status_strings():
     (dict(rep_method="fix", rep_num=0), B.KVS_ERR_INVALID_ARG),
     (dict(softmax_scale=-1.0), B.KVS_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), B.KVS_ERR_INVALID_ARG),
-    (dict(kv_type=4), B.KVS_ERR_INVALID_ARG),
+    (dict(kv_type=5), B.KVS_ERR_INVALID_ARG),
     (dict(kv_type=-1), B.KVS_ERR_INVALID_ARG),
     (dict(head_dim=64), B.KVS_ERR_UNSUPPORTED),
     (dict(block_size=64), B.KVS_ERR_UNSUPPORTED),
@@ -108,6 +108,7 @@ def test_kv_bytes_and_quantize_errors():
     assert kvs.kvs_kv_bytes_per_block(q8) == 8 * (128 * 128 + 128 * 4 * 2)
     assert kvs.kvs_kv_bytes_per_block(cfg(kv_type="q4_0")) == 8 * (128 * 64 + 128 * 4 * 2)
     assert kvs.kvs_kv_bytes_per_block(cfg(kv_type="int8_pth")) == 8 * (128 * 128 + 128 * 4)
+    assert kvs.kvs_kv_bytes_per_block(cfg(kv_type="int4_pth")) == 8 * (128 * 64 + 128 * 4 + 128)
     A, M, Z = ALIGNED, MISALIGNED, None
     E = B.KVS_ERR_INVALID_ARG
     assert kvs.kvs_quantize_kv(cfg(), A, A, 3, A, stream=0, check=False) == E  # needs a quantized kv_type

@@ -64,6 +64,7 @@ IMP_CASES = [
     (8, 2, "separate", 5, [1000, 300], "q8_0"),
     (32, 8, "shared", 32, [4000], "q4_0"),
     (16, 4, "separate", 8, [2000], "int8_pth"),
+    (16, 4, "shared", 8, [2000], "int4_pth"),
 ]
 
 
@@ -95,6 +96,7 @@ DYN_CASES = [
     (32, 8, "shared", 1, 16, 12, [6000, 3000], "q8_0"),   # quantized caches: reps are cached values
     (8, 2, "separate", 4, 8, 6, [5000], "q4_0"),
     (16, 4, "separate", 3, 4, 10, [4500], "int8_pth"),
+    (16, 4, "separate", 3, 4, 10, [4500], "int4_pth"),
 ]
 
 

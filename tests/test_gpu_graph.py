@@ -37,6 +37,7 @@ CASES = [
     ("128k-max-q4", 131072, "max", "shared", 96, "q4_0", 0),
     ("128k-presel", 131072, "max", "shared", 96, "fp16", 192),
     ("wide-quest-int8", 2400 * 128 + 77, "quest", "separate", 64, "int8_pth", 0),
+    ("128k-max-int4", 131072, "max", "shared", 96, "int4_pth", 0),
 ]
 
 

@@ -150,6 +150,26 @@ def test_small_cases_int8_pth(idx):
     run_full_check(case, f"small int8_pth {rep}/{mode} {Hq}x{Hkv}")
 
 
+# INT4 caches with one fp32 scale and one zero point per token and KV head (includes a long SEPARATE
+# row through the chunk summaries)
+SMALL_I4 = [
+    (32, 8, 128, 512, 12, "quest", "separate", 1, [5000, 129, 1, 7777]),
+    (32, 8, 100, 300, 5, "max", "shared", 1, [4000, 3001]),
+    (16, 16, 0, 0, 7, "fix", "separate", 8, [3000, 2048]),
+    (16, 2, 128, 2048, 24, "mean", "shared", 1, [290000]),
+    (16, 4, 128, 1024, 40, "quest", "separate", 1, [2300 * 128 + 11]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_I4)),
+                         ids=[f"i4-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_I4])
+def test_small_cases_int4_pth(idx):
+    Hq, Hkv, I, W, k, rep, mode, rn, lens = SMALL_I4[idx]
+    c = cfg_of(Hq, Hkv, I, W, k, rep, mode, rn, kv="int4_pth")
+    case = Case(c, lens, seed=kvsynth.mix_seed(80, idx), n_hot=3)
+    run_full_check(case, f"small int4_pth {rep}/{mode} {Hq}x{Hkv}")
+
+
 @pytest.mark.parametrize("idx", range(len(SMALL_Q4)),
                          ids=[f"q4-{s[5]}-{s[6]}-{s[0]}x{s[1]}-k{s[4]}" for s in SMALL_Q4])
 def test_small_cases_q4(idx):
@@ -351,6 +371,12 @@ def test_full_128k_shared_int8_pth():
     c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="int8_pth")
     case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
     run_full_check(case, "full 128K 32/8 max SHARED k96, INT8 per-token-head cache")
+
+
+def test_full_128k_shared_int4_pth():
+    c = cfg_of(32, 8, 128, 4096, 96, "max", "shared", kv="int4_pth")
+    case = Case(c, [131072], seed=20260012, n_hot=50, shuffle=False)
+    run_full_check(case, "full 128K 32/8 max SHARED k96, INT4 per-token-head cache")
 
 
 def test_full_mixed_batch_fix():

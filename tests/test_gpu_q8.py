@@ -1,11 +1,12 @@
-"""The Q8_0, Q4_0 and INT8 (per token and head) cache precisions on the GPU against the oracle
-(needs an MI355X).
+"""The Q8_0, Q4_0, INT8 and INT4 (per token and head) cache precisions on the GPU against the
+oracle (needs an MI355X).
 
 kv_type Q8_0 is the published llama.cpp block format that the operator's kv_type list names: per
 token and KV head, 32-channel blocks with an fp16 scale max|x|/127 and int8 codes, ties away from
 zero; Q4_0 its 4-bit sibling (scale m/-8 for the first largest-magnitude value m, codes
 min(15, trunc(x/d + 8.5))); INT8 one fp32 scale max|x|/127 per token and KV head with Q8_0's
-codes.  The codes and scales must match the oracle bit for bit (both take the
+codes; INT4 one fp32 scale and one zero point per token and KV head (asymmetric, codes 0..15 packed
+as Q4_0's).  The codes, scales and zero points must match the oracle bit for bit (both take the
 rounding decisions in fp32); reps over the cached values are value-equal (Mean: relative 1e-4).
 """
 from __future__ import annotations
@@ -220,5 +221,77 @@ def test_reps_over_q4_cache(rep, rep_num):
         got = rp[p].double().cpu().numpy()
         if rep == "mean":
             close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"q4 mean reps {p}")
+        else:
+            assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
+
+
+def split_i4(pool_i4):
+    """[n][Hkv][8832] bytes -> codes uint8 [n][Hkv][128][128] (Q4_0's packing), scales fp32
+    [n][Hkv][128], zero points uint8 [n][Hkv][128]."""
+    a = pool_i4.cpu().numpy()
+    w = a[..., : 128 * 64].copy().view(np.uint32).reshape(*a.shape[:2], 128, 16)
+    codes = np.zeros((*a.shape[:2], 128, 128), dtype=np.uint8)
+    for i in range(4):
+        codes[..., 2 * i::8] = (w >> (4 * i)) & 0xF
+        codes[..., 2 * i + 1::8] = (w >> (16 + 4 * i)) & 0xF
+    scales = a[..., 128 * 64: 128 * 68].copy().view(np.float32).reshape(*a.shape[:2], 128)
+    zeros = a[..., 128 * 68:].copy().reshape(*a.shape[:2], 128)
+    return codes, scales, zeros
+
+
+@pytest.mark.parametrize("Hkv", [1, 8])
+def test_quantize_int4_pth_bit_exact(Hkv):
+    say(f"[case] int4 per-token-head quantize Hkv={Hkv}")
+    n_phys = 7
+    c = q8_cfg(Hkv=Hkv, g=1, kv_type="int4_pth")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(431, Hkv))
+    src[2, 0, 9, :] = 0.0  # an all-zero row
+    src[2, 0, 10, :] = torch.arange(128, dtype=torch.float32, device=DEV).to(torch.float16) / 8  # no negatives
+    src[2, 0, 11, :] = -src[2, 0, 10, :]  # no positives
+    row = torch.zeros(128, device=DEV)
+    row[:8] = torch.tensor([20.0, -10.0, 1.0, 3.0, 5.0, -1.0, -3.0, 7.0], device=DEV)  # ties to even
+    src[3, 0, 4, :] = row.to(torch.float16)
+    row[:2] = torch.tensor([27.0, -3.0], device=DEV)  # a clamped code
+    row[2:] = 0.0
+    src[3, 0, 5, :] = row.to(torch.float16)
+    dst = ops.alloc_q8_pool(c, n_phys, DEV)
+    assert dst.shape[-1] == 8832
+    dst.fill_(0xAB)
+    ids = torch.tensor([5, 0, 2, 3, 6], dtype=torch.int32)
+    ops.quantize_kv(c, src, ids, dst)
+    torch.cuda.synchronize()
+    got_c, got_s, got_z = split_i4(dst)
+    want_c, want_s, want_z = orc.quantize_int4_pth(src.float().cpu().numpy())
+    for p in range(n_phys):
+        if p in ids.tolist():
+            assert np.array_equal(got_c[p], want_c[p]), (p, np.argwhere(got_c[p] != want_c[p])[:4])
+            assert np.array_equal(got_s[p].view(np.uint32), want_s[p].view(np.uint32)), p
+            assert np.array_equal(got_z[p], want_z[p]), (p, np.argwhere(got_z[p] != want_z[p])[:4])
+        else:
+            assert np.all(dst[p].cpu().numpy() == 0xAB), p
+    assert float(got_s[2, 0, 9]) == 0.0 and not got_c[2, 0, 9].any() and got_z[2, 0, 9] == 0
+    assert got_z[2, 0, 10] == 0 and got_z[2, 0, 11] == 15
+    assert got_z[3, 0, 4] == 5 and list(got_c[3, 0, 4, :8]) == [15, 0, 5, 7, 7, 5, 3, 9]
+    assert got_z[3, 0, 5] == 2 and list(got_c[3, 0, 5, :2]) == [15, 0]
+
+
+@pytest.mark.parametrize("rep,rep_num", [("quest", 1), ("max", 1), ("mean", 1), ("fix", 8)])
+def test_reps_over_int4_pth_cache(rep, rep_num):
+    say(f"[case] int4 per-token-head reps {rep}/{rep_num}")
+    n_phys, Hkv = 6, 8
+    c = q8_cfg(Hkv=Hkv, rep_method=rep, rep_num=rep_num, kv_type="int4_pth")
+    src = fp16_pool(n_phys, Hkv, kvsynth.mix_seed(432, rep_num, len(rep)))
+    kq = ops.alloc_q8_pool(c, n_phys, DEV)
+    ops.quantize_kv(c, src, torch.arange(n_phys, dtype=torch.int32), kq)
+    rp = ops.alloc_rep_pool(c, n_phys, DEV)
+    ops.build_reps(c, kq, torch.tensor([4, 1, 2], dtype=torch.int32), rp)
+    torch.cuda.synchronize()
+    codes, scales, zeros = split_i4(kq)
+    for p in (4, 1, 2):
+        K = orc.dequantize_int4_pth(codes[p], scales[p], zeros[p]).transpose(1, 0, 2)
+        want = orc.stored_reps(orc.block_reps(K, B, rep, rep_num), rep)[0]
+        got = rp[p].double().cpu().numpy()
+        if rep == "mean":
+            close_rel(got, want, np.abs(want).max(axis=-1, keepdims=True), f"int4 mean reps {p}")
         else:
             assert np.array_equal(got, want), (p, np.argwhere(got != want)[:4])
