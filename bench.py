@@ -673,7 +673,7 @@ def _bench_line(log_path):
     return "(bench log not given)"
 
 
-def summarize_stats(d, name, log_path=None, steps=480):
+def summarize_stats(d, name, log_path=None, steps=480, out_dir=None):
     """rocprofv3 --kernel-trace --stats CSV -> profiles/decode_step_<name>_kernel_stats.txt."""
     import csv
 
@@ -709,13 +709,13 @@ def summarize_stats(d, name, log_path=None, steps=480):
            "",
            "* not every layer step (set-up, or the batched workload's incremental rep builds): not in the sum",
            ""]
-    path = os.path.join(ROOT, "profiles", f"decode_step_{name}_kernel_stats.txt")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"decode_step_{name}_kernel_stats.txt")
     with open(path, "w") as f:
         f.write("\n".join(txt))
     print(path)
 
 
-def summarize_pmc(fetch_dir, write_dir, name, steps=32):
+def summarize_pmc(fetch_dir, write_dir, name, steps=32, out_dir=None):
     """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs -> profiles/decode_step_<name>_traffic.txt.
     Each counter is scaled by what it reads for the 4 GiB copies of copy_bandwidth().  Per layer:
     the mean bytes per dispatch of each decode-step kernel, summed (the batched workload's
@@ -777,7 +777,7 @@ def summarize_pmc(fetch_dir, write_dir, name, steps=32):
                          f"{res['FETCH_SIZE'][1][k]:20.0f} | {res['WRITE_SIZE'][1].get(k, 0.0):20.0f} |")
     lines += ["", "* not every layer step (set-up, or the batched workload's incremental rep builds): "
               "not in the per-layer sums"]
-    path = os.path.join(ROOT, "profiles", f"decode_step_{name}_traffic.txt")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"decode_step_{name}_traffic.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
@@ -793,6 +793,74 @@ TL_MARKS = {1: "operands in / scores stored", 2: "done / counter bumped", 3: "se
 TL_MAX_WG, TL_SLOTS = 16384, 8
 
 
+def timeline_replay_stats(rec):
+    """One replay's records [kinds][TL_MAX_WG][TL_SLOTS] (float64 ticks of the 100 MHz clock) ->
+    {(kind, "n"): workgroups, (kind, slot): (min, median, max) us, (kind, "end"): last mark us}, times
+    from the step's first scoring workgroup start.  The step starts with its scoring workgroups (first
+    in their launch's grid, kinds 0 and 6); a record that starts earlier than 1 us before them is an
+    earlier step's, left by a workgroup that had nothing to do this time, and is dropped."""
+    import numpy as np
+
+    first = [rec[k][rec[k][:, 0] > 0, 0].min() for k in (0, 6) if (rec[k][:, 0] > 0).any()]
+    t_first = min(first)
+    vals = {}
+    for k in range(rec.shape[0]):
+        r = rec[k][rec[k][:, 0] >= t_first - 100.0]
+        if not len(r):
+            continue
+        vals[(k, "n")] = len(r)
+        us = lambda a: (a - t_first) / 100.0
+        for slot in (0, 1, 2, 3, 4, 5):
+            a = r[:, slot]
+            a = a[a > 0]
+            if len(a):
+                vals[(k, slot)] = (us(a.min()), us(np.median(a)), us(a.max()))
+        marks = r[:, 1:6]
+        vals[(k, "end")] = us(marks[marks > 0].max()) if (marks > 0).any() else us(r[:, 0].max())
+    return vals
+
+
+def timeline_medians(per_replay):
+    """The median over replays of every figure present in all of them."""
+    import statistics
+
+    keys = [k for k in per_replay[-1] if all(k in v for v in per_replay)]
+    med = {}
+    for key in keys:
+        xs = [v[key] for v in per_replay]
+        med[key] = tuple(statistics.median(x[i] for x in xs) for i in range(3)) if isinstance(xs[0], tuple) \
+            else statistics.median(xs)
+    return med
+
+
+def timeline_lines(med):
+    """Text tables of timeline_medians(): per workgroup kind, then per launch (kinds grouped by
+    TL_LAUNCH) with its first start, last mark, span and the gap after the launch before."""
+    f3 = lambda t: f"{t[0]:6.2f} {t[1]:6.2f} {t[2]:6.2f}"
+    lines = ["# workgroup kinds: start and marks, us from the layer's first workgroup start (min / median / max)"]
+    kinds = sorted({k for k, _ in med}, key=lambda k: med[(k, 0)][0])
+    for k in kinds:
+        lines.append(f"| {TL_KINDS[k]:40s} | n {int(med[(k, 'n')]):5d} | start {f3(med[(k, 0)])} |")
+        for slot in (1, 5, 4, 2, 3):
+            if (k, slot) in med:
+                lines.append(f"|   {TL_MARKS[slot]:38s} |         | {'':5s} {f3(med[(k, slot)])} |")
+    lines += ["", "# launches: first workgroup start, last mark, span, gap after the launch before (us)"]
+    launches = {}
+    for k in kinds:
+        L = TL_LAUNCH[k]
+        s0, e0 = med[(k, 0)][0], med[(k, "end")]
+        a, b = launches.get(L, (s0, e0))
+        launches[L] = (min(a, s0), max(b, e0))
+    prev_end = None
+    for L, (a, b) in sorted(launches.items(), key=lambda x: x[1][0]):
+        gap = f"{a - prev_end:6.2f}" if prev_end is not None else "     -"
+        lines.append(f"| {L:20s} | start {a:6.2f} | end {b:6.2f} | span {b - a:6.2f} | gap {gap} |")
+        prev_end = b
+    lines.append(f"layer: {prev_end:.2f} us from the first workgroup start to the last mark "
+                 "(the timeline build waits for loads at mark 1, so it runs a little slower than the default build)")
+    return lines
+
+
 def timeline(name, device, replays=9, keep=5):
     """Per-workgroup timeline of the last layer step of `name`'s timed cycle (the same graph-replayed
     cycle of steps over the cache replicas as the timed runs, so the layer's data is as cold as
@@ -800,8 +868,6 @@ def timeline(name, device, replays=9, keep=5):
     and marks (min / median / max over workgroups, us from the layer's first workgroup start), and
     per launch its first start, last mark and the gap to the launch before.  Each figure is the
     median over the last `keep` of `replays` replays.  Returns the summary's text lines."""
-    import statistics
-
     import numpy as np
     import torch
 
@@ -827,64 +893,18 @@ def timeline(name, device, replays=9, keep=5):
         g.replay()
         torch.cuda.synchronize()
         rec = buf.view(n_kinds, TL_MAX_WG, TL_SLOTS).cpu().numpy().view(np.uint64).astype(np.float64)
-        # the step starts with its scoring workgroups (first in their launch's grid); a record that
-        # starts earlier is an earlier step's, left by a workgroup that had nothing to do this time
-        first = [rec[k][rec[k][:, 0] > 0, 0].min() for k in (0, 6) if (rec[k][:, 0] > 0).any()]
-        t0 = min(first) - 100.0  # 1 us of slack (100 MHz ticks)
-        vals = {}
-        for k in range(n_kinds):
-            r = rec[k][rec[k][:, 0] >= t0]
-            if not len(r):
-                continue
-            vals[(k, "n")] = len(r)
-            us = lambda a: (a - min(first)) / 100.0  # 100 MHz ticks -> us from the step's start
-            for slot in (0, 1, 2, 3, 4, 5):
-                a = r[:, slot]
-                a = a[a > 0]
-                if len(a):
-                    vals[(k, slot)] = (us(a.min()), us(np.median(a)), us(a.max()))
-            marks = r[:, 1:6]
-            vals[(k, "end")] = us(marks[marks > 0].max()) if (marks > 0).any() else us(r[:, 0].max())
-        per_replay.append(vals)
+        per_replay.append(timeline_replay_stats(rec))
     kvs.kvs_timeline_set(None)
-    last = per_replay[-keep:]
-    keys = [k for k in last[-1] if all(k in v for v in last)]
-    med = {}
-    for key in keys:
-        xs = [v[key] for v in last]
-        med[key] = tuple(statistics.median(x[i] for x in xs) for i in range(3)) if isinstance(xs[0], tuple) \
-            else statistics.median(xs)
-    f3 = lambda t: f"{t[0]:6.2f} {t[1]:6.2f} {t[2]:6.2f}"
-    lines = [f"workload: {name}",
-             f"layer_step: the last {'batch step' if mixed else 'layer step'} of a graph-replayed cycle of "
-             f"{st.cycle} steps ({WORKLOADS[name]['layers']} layers each), as in the timed runs",
-             f"replays: {replays} (medians over the last {keep})",
-             f"source_hash: {source_hash()}",
-             "command: python block_sparse_kv_amd/build.py --timeline && "
-             f"KVS_LIBRARY=timeline python bench.py --timeline {name}",
-             "",
-             "# workgroup kinds: start and marks, us from the layer's first workgroup start (min / median / max)"]
-    kinds = sorted({k for k, _ in keys}, key=lambda k: med[(k, 0)][0])
-    for k in kinds:
-        lines.append(f"| {TL_KINDS[k]:40s} | n {int(med[(k, 'n')]):5d} | start {f3(med[(k, 0)])} |")
-        for slot in (1, 5, 4, 2, 3):
-            if (k, slot) in med:
-                lines.append(f"|   {TL_MARKS[slot]:38s} |         | {'':5s} {f3(med[(k, slot)])} |")
-    lines += ["", "# launches: first workgroup start, last mark, span, gap after the launch before (us)"]
-    launches = {}
-    for k in kinds:
-        L = TL_LAUNCH[k]
-        s0, e0 = med[(k, 0)][0], med[(k, "end")]
-        a, b = launches.get(L, (s0, e0))
-        launches[L] = (min(a, s0), max(b, e0))
-    prev_end = None
-    for L, (a, b) in sorted(launches.items(), key=lambda x: x[1][0]):
-        gap = f"{a - prev_end:6.2f}" if prev_end is not None else "     -"
-        lines.append(f"| {L:20s} | start {a:6.2f} | end {b:6.2f} | span {b - a:6.2f} | gap {gap} |")
-        prev_end = b
-    lines.append(f"layer: {prev_end:.2f} us from the first workgroup start to the last mark "
-                 "(the timeline build waits for loads at mark 1, so it runs a little slower than the default build)")
-    return lines
+    med = timeline_medians(per_replay[-keep:])
+    head = [f"workload: {name}",
+            f"layer_step: the last {'batch step' if mixed else 'layer step'} of a graph-replayed cycle of "
+            f"{st.cycle} steps ({WORKLOADS[name]['layers']} layers each), as in the timed runs",
+            f"replays: {replays} (medians over the last {keep})",
+            f"source_hash: {source_hash()}",
+            "command: python block_sparse_kv_amd/build.py --timeline && "
+            f"KVS_LIBRARY=timeline python bench.py --timeline {name}",
+            ""]
+    return head + timeline_lines(med)
 
 
 def main():
