@@ -694,10 +694,11 @@ def summarize_stats(d, name, log_path=None, steps=480, out_dir=None):
     txt = [f"# kvs_decode_step kernels, workload {name}",
            "",
            "command (repository root on the MI355X box; bench.py times the same calls):",
-           f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{name} -o run "
-           f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps}",
-           f"    python bench.py --summarize-stats gpurun_out/prof_{name} --workload {name} --steps {steps} "
-           f"--log gpurun_out/prof_{name}.log",
+           f"    rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run "
+           f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps}"
+           + (f" > {log_path} 2>&1" if log_path else ""),
+           f"    python bench.py --summarize-stats {d} --workload {name} --steps {steps}"
+           + (f" --log {log_path}" if log_path else ""),
            "",
            f"source_hash: {source_hash()}",
            f"sum_of_kernel_averages_us_per_layer: {tot:.2f}",
@@ -751,12 +752,11 @@ def summarize_pmc(fetch_dir, write_dir, name, steps=32, out_dir=None):
     lines = [f"# HBM traffic of kvs_decode_step, workload {name}",
              "",
              "commands (repository root on the MI355X box), one counter per run:",
-             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{name} -o run "
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run "
              f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps} --warmup 2",
-             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{name} -o run "
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run "
              f"-- python3 bench.py --workload {name} --no-cpu --no-reuse --steps {steps} --warmup 2",
-             f"    python bench.py --summarize-pmc gpurun_out/pmc_fetch_{name} gpurun_out/pmc_write_{name} "
-             f"--workload {name} --steps {steps}",
+             f"    python bench.py --summarize-pmc {fetch_dir} {write_dir} --workload {name} --steps {steps}",
              "",
              "Calibration: each counter over the 4 GiB device copy that starts every bench.py run "
              "(read 4 GiB, write 4 GiB).",
