@@ -653,7 +653,57 @@ def measure(name, steps, warmup, device, trials=7, reuse=True):
                                        frac=attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS)
     log(f"[bench] {name} attention only (selection reused): {attn_s * 1e6:.1f} us/step, "
         f"{attn_bytes / attn_s / 1e9:.0f} GB/s = {100 * attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS:.1f}%")
+    if "kv" not in w:
+        res["gather_reference"] = g = gather_reference(st, device)
+        log(f"[bench] {name} plain gather of one layer's attended tiles (torch index_select of K and V, "
+            f"{g['tiles']} tiles each): {g['us']:.1f} us, {g['bytes_read'] / 1e6:.1f} MB read and as much "
+            f"written, {g['read_gbs']:.0f} GB/s read")
     return res
+
+
+def gather_reference(st, device, replays=50):
+    """A library gather of the tiles one layer's decode step attends (unit 0: its Initial/Local tiles
+    and the selection kept by prepare_reuse), K and V, by torch.index_select into fresh buffers:
+    what a plain copy of the same scattered 32 KiB tiles costs on this part, for comparison with the
+    attention launch that reads them.  Graph-replayed; the median replay."""
+    import torch
+
+    w = st.w
+    Hkv, nb = w["Hkv"], st.nb
+    ie, ls, _ = regions(w["L"], w["I"], w["W"])
+    il = list(range(ie // B)) + list(range(ls // B, (w["L"] + B - 1) // B))
+    sel, cnt = st.reuse[0]
+    sel, cnt, table = sel.cpu().numpy(), cnt.cpu().numpy(), st.table.cpu().numpy()
+    idx = []
+    for h in range(Hkv):
+        gi = h if st.cfg.groups == Hkv else 0
+        blocks = il + [int(b) for b in sel[0, gi, : int(cnt[0, gi])]]
+        idx += [int(table[0, b]) * Hkv + h for b in blocks]  # (physical block, KV head) tile
+    ix = torch.tensor(idx, dtype=torch.long, device=device)
+    _, kp, vp, _ = st.units[0]
+    kf, vf = kp.view(-1, B * D), vp.view(-1, B * D)
+    ko = torch.empty((len(idx), B * D), dtype=kf.dtype, device=device)
+    vo = torch.empty_like(ko)
+
+    def run(_):
+        torch.index_select(kf, 0, ix, out=ko)
+        torch.index_select(vf, 0, ix, out=vo)
+
+    for _ in range(3):
+        run(0)
+    torch.cuda.synchronize()
+    g = _capture(run, range(1))
+    times = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    nbytes = 2 * len(idx) * B * D * 2
+    return dict(tiles=len(idx), us=t * 1e6, bytes_read=nbytes, read_gbs=nbytes / t / 1e9)
 
 
 # ------------------------------------------------------------------------------------------------
