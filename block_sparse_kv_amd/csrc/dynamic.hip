@@ -267,6 +267,8 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
   load_k_tile<KV>(k_pool, (size_t)v * P.Hkv + h, kt);
   const uint16_t* q_seq = q_obs + (size_t)seq * n_obs * P.Hq * kDim;
   const float2* st = stats + ((size_t)seq * P.Hkv + h) * n_rows;
+  // lane (lc, lq) sums p over the rows lc + 16 * (row group) of token 4lq + i; the 16 lanes of a DPP
+  // row are summed once, after every row group
   float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int r0 = 0; r0 < n_rows; r0 += kImpRows) {
     if (r0 > 0) __syncthreads();
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
         for (int gg = 0; gg < 2; ++gg) {
           const f32x4_t S = imp_s<KV>(kt, qb, gg);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[gg][i] += row_sum16(fast_exp2(S[i] * P.scale_log2 - ml.x) * inv_l);
+          for (int i = 0; i < 4; ++i) acc[gg][i] += fast_exp2(S[i] * P.scale_log2 - ml.x) * inv_l;
         }
       } else {
 #pragma unroll
@@ -296,13 +298,16 @@ __global__ __launch_bounds__(256) void imp_accum_kernel(Params P, const uint16_t
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = b * kBlock + 32 * w + 16 * gg + 4 * lq + i;
-            const float p = r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
-            acc[gg][i] += row_sum16(p);  // the 16 rows of this group (one DPP row = one token)
+            acc[gg][i] += r < n_rows && t <= last ? exp2_diff(S[i] * P.scale_log2, ml.x) * inv_l : 0.f;
           }
         }
       }
     }
   }
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[gg][i] = row_sum16(acc[gg][i]);  // over the rows' lanes
   if (lc == 0) {
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg)
