@@ -119,7 +119,8 @@ def regions(L, I, W):
 
 
 STEP_KERNELS = ("build_reps_kernel", "presel_step_kernel", "score_select_kernel", "score_kernel",
-                "topk_il_wide_kernel", "topk_kernel", "merge_wave_kernel", "attn_tiles_kernel", "merge_kernel")
+                "topk_il_wide_kernel", "topk_kernel", "attn_select_kernel", "merge_wave_kernel",
+                "attn_tiles_kernel", "merge_kernel")
 COPY_BYTES = 4 << 30  # the device copy of copy_bandwidth(): read and written once per dispatch
 
 
@@ -835,9 +836,11 @@ def summarize_pmc(fetch_dir, write_dir, name, steps=32, out_dir=None):
 
 TL_KINDS = ("scoring+selection: scoring workgroups", "scoring+selection: Initial/Local tiles",
             "top-k launch: Initial/Local tiles", "attention: selected tiles", "merge",
-            "top-k launch: selections", "scoring launch", "top-k launch (own)", "compaction", "map back")
+            "top-k launch: selections", "scoring launch", "top-k launch (own)", "compaction", "map back",
+            "attention: selections by the tiles", "attention: Initial/Local tiles")
 TL_LAUNCH = {0: "scoring+selection", 1: "scoring+selection", 2: "top-k", 5: "top-k", 3: "attention",
-             4: "merge", 6: "scoring", 7: "top-k (own)", 8: "compaction", 9: "map back"}
+             4: "merge", 6: "scoring", 7: "top-k (own)", 8: "compaction", 9: "map back", 10: "attention",
+             11: "attention"}
 TL_MARKS = {1: "operands in / scores stored", 2: "done / counter bumped", 3: "selection stored",
             4: "chunk summary stored", 5: "chunk summary made"}
 TL_MAX_WG, TL_SLOTS = 16384, 8
@@ -1042,8 +1045,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["frac"],
                      "traffic": traffic_per_step(names[0]),
-                     "kernel": "kvs_decode_step (one call: scoring, top-k and Initial/Local tiles, "
-                               "selected tiles, merge)",
+                     "kernel": "kvs_decode_step (one call: its scoring, selection, tile and merge "
+                               "launches)",
                      "bytes_per_launch": head["required_bytes_per_step"]},
         "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,

@@ -153,9 +153,9 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
                                           const uint16_t* __restrict__ v_pool, int h, int phys, int ntok,
                                           float* __restrict__ part_o, float* __restrict__ part_ml,
                                           int n_parts, int part, unsigned char* smem,
-                                          bool store = true) {
+                                          bool store = true, int tl_kind = -1) {
   const int tid = threadIdx.x & 255, w = tid >> 6, lane = tid & 63, lq = lane >> 4, lc = lane & 15;
-  KVS_TL_BEGIN(P, P.tl_kind, 256)
+  KVS_TL_BEGIN(P, tl_kind >= 0 ? tl_kind : P.tl_kind, 256)
   // Every load is issued up front, in the order the data is needed -- Q, K, then V -- and without
   // branches, so the compiler keeps them all in flight and waits only for what the next step needs.
   // Rows past ntok are still inside the tile: their K only feeds logits that are masked, their V is
@@ -660,7 +660,8 @@ __device__ inline void empty_partial(float* part_o, float* part_ml, int n_parts,
 // sequence's own counts do nothing; table entries or selections outside the table give an empty
 // partial instead of a read outside the pools' rows.
 template <int G, bool IL, bool PHYS, int KV = kKvFp16>
-__device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int seq, unsigned char* smem) {
+__device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int seq, unsigned char* smem,
+                                          int tl_kind = -1) {
   const Params& P = A.P;
   const bool is_il = IL && x < A.n_il_max;
   const int i = IL ? x - A.n_il_max : x;  // selected index when !is_il
@@ -696,7 +697,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
     empty_partial<G>(po, pml, A.max_parts, part);
     return;
   }
-  attn_tile<G, KV>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem);
+  attn_tile<G, KV>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, phys, ntok, po, pml, A.max_parts, part, smem,
+                   true, tl_kind);
 }
 
 // Merge of channels [16c, 16c + 16) of query head j of sequence seq by one wave (merge_head_wave).

@@ -1,10 +1,14 @@
 // kvs_decode_step: scoring -> top-k -> attention tiles -> merge, with the Initial/Local tiles -- which
 // do not depend on the selection [KT-LC §4.2] -- placed where their K/V gather costs least:
-//  * short rows (max_blocks <= kStepTopkSmall): one launch scores, selects and gathers the
-//    Initial/Local tiles (score_select_kernel).  The scoring workgroups of a (sequence, group) hand
-//    their scores to the one among them that finishes last, which makes the group's selection (256
-//    lanes, keys in registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles
-//    and the merge (attn.hip).
+//  * short rows (max_blocks <= kStepTopkSmall) of small batches (select_plan): a scoring launch
+//    (score_select_kernel without its selection), with some of the Initial/Local tiles; then one
+//    launch in which every selected tile's workgroup makes its group's selection from the score row
+//    itself (all of them make the same one) and gathers its own entry, beside the other Initial/Local
+//    tiles (attn_select_kernel); then the merge (attn.hip).
+//  * other short rows: one launch scores, selects and gathers the Initial/Local tiles
+//    (score_select_kernel).  The scoring workgroups of a (sequence, group) hand their scores to the
+//    one among them that finishes last, which makes the group's selection (256 lanes, keys in
+//    registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles and the merge.
 //  * SEPARATE rows of up to kStepSummMax blocks: the same launch, each scoring workgroup (one 64-block
 //    chunk of one KV head) also storing its chunk's best 8; the last one selects from these summaries,
 //    or from the whole row when a chunk holds more than 8 of the selection.
@@ -22,14 +26,52 @@ namespace kvs {
 namespace {
 hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
                                int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
-                               const Summaries& U = Summaries()) {
+                               const Summaries& U = Summaries(), int il_per = -1) {
   switch (A.P.kv) {
-    case kKvQ8: return launch_score_select_kv<kKvQ8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
-    case kKvQ4: return launch_score_select_kv<kKvQ4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
-    case kKvI8: return launch_score_select_kv<kKvI8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
-    case kKvI4: return launch_score_select_kv<kKvI4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
-    default: return launch_score_select_kv<kKvFp16>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U);
+    case kKvQ8: return launch_score_select_kv<kKvQ8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U, il_per);
+    case kKvQ4: return launch_score_select_kv<kKvQ4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U, il_per);
+    case kKvI8: return launch_score_select_kv<kKvI8>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U, il_per);
+    case kKvI4: return launch_score_select_kv<kKvI4>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U, il_per);
+    default: return launch_score_select_kv<kKvFp16>(A, rep_pool, scores, sel, cnt, tiles, ctr, batch, s, U, il_per);
   }
+}
+
+hipError_t launch_attn_select(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count, int batch,
+                              int il0, hipStream_t s) {
+  switch (A.P.kv) {
+    case kKvQ8: return launch_attn_select_kv<kKvQ8>(A, scores, sel, sel_count, batch, il0, s);
+    case kKvQ4: return launch_attn_select_kv<kKvQ4>(A, scores, sel, sel_count, batch, il0, s);
+    case kKvI8: return launch_attn_select_kv<kKvI8>(A, scores, sel, sel_count, batch, il0, s);
+    case kKvI4: return launch_attn_select_kv<kKvI4>(A, scores, sel, sel_count, batch, il0, s);
+    default: return launch_attn_select_kv<kKvFp16>(A, scores, sel, sel_count, batch, il0, s);
+  }
+}
+
+// Rows of up to kStepTopkSmall blocks: whether every selected tile's workgroup makes its group's
+// selection itself (by_tiles) rather than the scoring launch's last workgroup of the group, and how
+// many of each KV head's Initial/Local tiles stream in the scoring launch (il_first; the rest stream
+// in the tiles' launch while the selections are made).  Chosen by measurement:
+//  * by_tiles while the selected tiles' workgroups number at most kSelByTilesMax, all resident at
+//    once; with more (large batches) the same selections would be made over several waves of
+//    workgroups, and the last scoring workgroup of each group makes each once instead (16 sequences
+//    of 16K to 128K tokens: 109 against 121 us per step);
+//  * rows of up to 256 blocks: up to kIlLate Initial/Local tiles per KV head stream beside the
+//    selections, the others beside the scoring (32K tokens, 8 KV heads: 19.4 us per step, against
+//    20.8 with all of them beside the selections and 20.1 with all beside the scoring); longer rows:
+//    all beside the selections (128K tokens: 23.9 us, against 24.5 with half beside the scoring).
+constexpr int kSelByTilesMax = 1024;
+constexpr int kIlLate = 16;
+struct SelPlan {
+  bool by_tiles;
+  int il_first;
+};
+SelPlan select_plan(const Params& P, int batch, int max_blocks, int n_il_max) {
+  SelPlan p{false, n_il_max};
+  if (P.topk <= 0 || max_blocks > kStepTopkSmall) return p;
+  if ((long long)batch * P.Hkv * P.topk > kSelByTilesMax) return p;
+  p.by_tiles = true;
+  p.il_first = max_blocks <= 256 ? (n_il_max > kIlLate ? n_il_max - kIlLate : 0) : 0;
+  return p;
 }
 
 hipError_t launch_topk_il_wide(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
@@ -77,7 +119,12 @@ hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* sc
   int32_t* tl = P.topk > 0 ? tiles : nullptr;
   hipError_t e;
   const size_t ub = summaries_bytes(P, batch, A.max_blocks);
-  if (A.max_blocks <= kStepTopkSmall) {
+  const SelPlan sp = select_plan(P, batch, A.max_blocks, A.n_il_max);
+  if (sp.by_tiles) {
+    e = launch_score_select(A, rep_pool, scores, nullptr, nullptr, nullptr, nullptr, batch, s, Summaries(),
+                            sp.il_first);
+    if (e == hipSuccess) e = launch_attn_select(A, scores, sel, sel_count, batch, sp.il_first, s);
+  } else if (A.max_blocks <= kStepTopkSmall) {
     e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s);
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   } else if (ub != 0 && summ != nullptr && P.topk > 0) {  // one launch scores and selects

@@ -55,8 +55,8 @@ __device__ inline void write_chunk_summary(const float* lds, int b0, float* uval
 // First the scoring workgroups, n_sc per (sequence, group), over every KV head (SHARED) or over one KV
 // head (SEPARATE; group = KV head): dispatched first, their few loads are not queued behind the
 // tiles' stream.  With sel null the kernel only scores and streams the tiles (a selection made by
-// later launches).  Then n_il_wg Initial/Local tiles, tile t of KV head h of sequence seq at
-// (seq * Hkv + h) * n_il_max + t.  A scoring workgroup stores its
+// later launches).  Then n_il_wg Initial/Local tiles, il_per (<= n_il_max) per KV head: tile t < il_per
+// of KV head h of sequence seq at (seq * Hkv + h) * il_per + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
 // SUMM (SEPARATE rows longer than the register selection holds): each scoring workgroup, one chunk of
@@ -66,7 +66,8 @@ template <int G, int METHOD, int MODE, int KV, bool SUMM = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void score_select_kernel(
     AttnArgs A, const void* __restrict__ rep_pool, float* __restrict__ scores, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int ctr_stride,
-    int n_sc, int n_il_wg, float* __restrict__ uval, int32_t* __restrict__ uid, int32_t* __restrict__ uphys) {
+    int n_sc, int n_il_wg, int il_per, float* __restrict__ uval, int32_t* __restrict__ uid,
+    int32_t* __restrict__ uphys) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_last;
   const Params& P = A.P;
@@ -74,9 +75,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int x = blockIdx.x;
   if (x >= n_score_wg) {
     const int xi = x - n_score_wg;
-    const int per_seq = P.Hkv * A.n_il_max;
+    const int per_seq = P.Hkv * il_per;
     const int r = xi % per_seq;
-    attn_item<G, true, false, KV>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
+    attn_item<G, true, false, KV>(A, r % il_per, r / il_per, xi / per_seq, smem);
     return;
   }
   constexpr bool SEP = MODE == kSeparate;
@@ -151,49 +152,122 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 template <int G, int METHOD, int KV>
 static void launch_ss_mq(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
                          int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int ctr_stride, int n_sc, int n_il_wg,
-                         const Summaries& U) {
+                         int il_per, const Summaries& U) {
   if (U.val)  // SEPARATE long rows (checked by the caller)
     hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, KV, true>), grid, dim3(256), 0, s, A, reps,
-                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U.val, U.id, U.phys);
   else if (A.P.mode == kSeparate)
     hipLaunchKernelGGL((score_select_kernel<G, METHOD, kSeparate, KV>), grid, dim3(256), 0, s, A, reps,
-                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U.val, U.id, U.phys);
   else
     hipLaunchKernelGGL((score_select_kernel<G, METHOD, kShared, KV>), grid, dim3(256), 0, s, A, reps,
-                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U.val, U.id, U.phys);
+                       scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U.val, U.id, U.phys);
 }
 
 template <int G, int KV>
 static void launch_ss_g(const AttnArgs& A, dim3 grid, hipStream_t s, const void* reps, float* scores,
                         int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr, int ctr_stride, int n_sc, int n_il_wg,
-                        const Summaries& U) {
+                        int il_per, const Summaries& U) {
   switch (A.P.method) {
-    case kQuest: launch_ss_mq<G, kQuest, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
-    case kMax: launch_ss_mq<G, kMax, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
-    case kMean: launch_ss_mq<G, kMean, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
-    default: launch_ss_mq<G, kFix, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, U); break;
+    case kQuest: launch_ss_mq<G, kQuest, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U); break;
+    case kMax: launch_ss_mq<G, kMax, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U); break;
+    case kMean: launch_ss_mq<G, kMean, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U); break;
+    default: launch_ss_mq<G, kFix, KV>(A, grid, s, reps, scores, sel, cnt, tiles, ctr, ctr_stride, n_sc, n_il_wg, il_per, U); break;
   }
 }
 
 template <int KV>
 hipError_t launch_score_select_kv(const AttnArgs& A_in, const void* rep_pool, float* scores, int32_t* sel,
                                   int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
-                                  const Summaries& U) {
+                                  const Summaries& U, int il_per) {
   AttnArgs A = A_in;
   A.P.tl_kind = kTlIlStep;
   const Params& P = A.P;
   const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
   const int n_sc = (A.max_blocks + sb - 1) / sb;
-  const int n_il_wg = batch * P.Hkv * A.n_il_max;
+  if (il_per < 0 || il_per > A.n_il_max) il_per = A.n_il_max;
+  const int n_il_wg = batch * P.Hkv * il_per;
   const dim3 grid(n_il_wg + batch * P.G * n_sc);
   const int cst = step_ctr_stride(batch * P.G);
   switch (P.g) {
-    case 1: launch_ss_g<1, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
-    case 2: launch_ss_g<2, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
-    case 4: launch_ss_g<4, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
-    case 8: launch_ss_g<8, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
-    default: launch_ss_g<16, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, U); break;
+    case 1: launch_ss_g<1, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, il_per, U); break;
+    case 2: launch_ss_g<2, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, il_per, U); break;
+    case 4: launch_ss_g<4, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, il_per, U); break;
+    case 8: launch_ss_g<8, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, il_per, U); break;
+    default: launch_ss_g<16, KV>(A, grid, s, rep_pool, scores, sel, cnt, tiles, ctr, cst, n_sc, n_il_wg, il_per, U); break;
   }
+  return hipGetLastError();
+}
+
+// The selected tiles of a step whose score rows an earlier launch stored, and the Initial/Local tiles
+// [il0, n_il_max) of every KV head, in one grid: workgroups [0, n_sel) are the selected tiles, entry i
+// of the selection of KV head h of sequence seq at (seq * Hkv + h) * topk + i -- dispatched first, so
+// their score loads are not queued behind the Initial/Local tiles' stream -- then Initial/Local tile
+// il0 + t at n_sel + (seq * Hkv + h) * (n_il_max - il0) + t.  A selected tile's workgroup makes its
+// group's selection itself from the score row (topk_slot_reg: every workgroup of a group makes the
+// same one) and gathers its entry; the one of entry 0 (of KV head 0 for SHARED) also writes the
+// group's selection and count.  Nothing passes between the workgroups of the launch.
+template <int G, int KV, int KPT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attn_select_kernel(
+    AttnArgs A, const float* __restrict__ scores, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    int n_sel, int il0) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
+  __shared__ int s_slot[2];
+  const Params& P = A.P;
+  const int x = blockIdx.x;
+  if (x >= n_sel) {
+    const int il_n = A.n_il_max - il0, j = x - n_sel;
+    attn_item<G, true, false, KV>(A, il0 + j % il_n, (j / il_n) % P.Hkv, j / (il_n * P.Hkv), smem, kTlAttnIl);
+    return;
+  }
+  KVS_TL_BEGIN(P, kTlTileSel, 256)
+  const int i = x % P.topk, h = (x / P.topk) % P.Hkv, seq = x / (P.topk * P.Hkv);
+  const size_t row = (size_t)seq * P.G + (P.mode == kSeparate ? h : 0);
+  const bool writer = i == 0 && (P.mode == kSeparate || h == 0);
+  const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
+  const int2 e = topk_slot_reg<256, KPT>(scores + row * A.max_blocks, A.max_blocks, A.seq_lens + seq,
+                                         P.initial_len, P.local_len, P.topk, i,
+                                         *reinterpret_cast<TopkLds*>(smem), trow, writer,
+                                         sel + row * P.topk, sel_count + row, s_slot, KVS_TL_REC);
+  KVS_TL_MARK(3)
+  if (e.x < 0) return;
+  const TileList tl = tiles_of(A.seq_lens[seq], P, 0);
+  const int part = tl.nI + tl.nLoc + i;
+  const size_t head0 = (size_t)seq * P.Hq + (size_t)h * G;
+  float* po = A.part_o + head0 * A.max_parts * kDim;
+  float* pml = A.part_ml + head0 * A.max_parts * 2;
+  if (e.y < 0) {  // a table entry that names no block
+    empty_partial<G>(po, pml, A.max_parts, part);
+    return;
+  }
+  __syncthreads();  // the selection's LDS becomes the tile's
+  attn_tile<G, KV>(P, A.q + head0 * kDim, A.k_pool, A.v_pool, h, e.y, kBlock, po, pml, A.max_parts, part, smem);
+}
+
+template <int KV>
+hipError_t launch_attn_select_kv(const AttnArgs& A_in, const float* scores, int32_t* sel, int32_t* sel_count,
+                                 int batch, int il0, hipStream_t s) {
+  AttnArgs A = A_in;
+  A.P.tl_kind = kTlAttn;
+  if (il0 < 0 || il0 > A.n_il_max) il0 = A.n_il_max;
+  const int n_sel = batch * A.P.Hkv * A.P.topk;
+  const dim3 grid(n_sel + batch * A.P.Hkv * (A.n_il_max - il0));
+  const int kpt = A.max_blocks <= 256 ? 1 : (A.max_blocks <= 1024 ? 4 : 8);
+#define KVS_AS(GG, KK) \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK>), grid, dim3(256), 0, s, A, scores, sel, sel_count, n_sel, il0)
+#define KVS_AS_G(GG)                       \
+  if (kpt == 1) KVS_AS(GG, 1);             \
+  else if (kpt == 4) KVS_AS(GG, 4);        \
+  else KVS_AS(GG, 8);
+  switch (A.P.g) {
+    case 1: KVS_AS_G(1); break;
+    case 2: KVS_AS_G(2); break;
+    case 4: KVS_AS_G(4); break;
+    case 8: KVS_AS_G(8); break;
+    default: KVS_AS_G(16); break;
+  }
+#undef KVS_AS_G
+#undef KVS_AS
   return hipGetLastError();
 }
 

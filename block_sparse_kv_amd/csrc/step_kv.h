@@ -21,13 +21,20 @@ struct Summaries {
 // (8 summary entries per 64-block chunk, at most 8 per lane of the 256-lane selection).
 constexpr int kStepSummMax = 256 * 8 * 8;
 
-// Scoring, the top-k by the group's last scoring workgroup (sel != nullptr) and the Initial/Local tiles,
-// in one launch: rows of up to kStepTopkSmall blocks from the whole score row, longer SEPARATE rows
-// (up to kStepSummMax) from the chunk summaries U.
+// Scoring, the top-k by the group's last scoring workgroup (sel != nullptr) and the Initial/Local tiles
+// [0, il_per) of each KV head (every one for il_per < 0), in one launch: rows of up to kStepTopkSmall
+// blocks from the whole score row, longer SEPARATE rows (up to kStepSummMax) from the chunk
+// summaries U.
 template <int KV>
 hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float* scores, int32_t* sel,
                                   int32_t* cnt, int32_t* tiles, int* ctr, int batch, hipStream_t s,
-                                  const Summaries& U);
+                                  const Summaries& U, int il_per = -1);
+// The selected tiles, and the Initial/Local tiles [il0, n_il_max) of each KV head, of a step whose
+// rows (up to kStepTopkSmall blocks) were scored by an earlier launch into scores: each selected
+// tile's workgroup makes its group's selection itself.
+template <int KV>
+hipError_t launch_attn_select_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
+                                 int batch, int il0, hipStream_t s);
 // Longer rows: the top-k selections (512-lane workgroups) and the Initial/Local tiles in one launch.
 template <int KV>
 hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,

@@ -29,7 +29,9 @@ enum TlKind {
   kTlTopk = 7,       // top-k launch of its own
   kTlCompact = 8,    // preselected-set compaction
   kTlMapBack = 9,    // mapping of a confined selection back to block ids
-  kTlKinds = 10
+  kTlTileSel = 10,   // selections made by the selected tiles' workgroups (before their tiles)
+  kTlAttnIl = 11,    // Initial/Local tiles in the selected tiles' launch
+  kTlKinds = 12
 };
 constexpr int kTlMaxWg = 16384;
 constexpr int kTlSlots = 8;
@@ -60,10 +62,12 @@ __device__ inline unsigned long long* tl_begin(unsigned long long* records, int 
     ::kvs::wait_mem();           \
     KVS_TL_MARK(SLOT)            \
   }
+#define KVS_TL_REC kvs_tl_rec
 #else
 #define KVS_TL_BEGIN(P, KIND, PART)
 #define KVS_TL_MARK(SLOT)
 #define KVS_TL_MARK_LOADED(SLOT)
+#define KVS_TL_REC nullptr
 #endif
 
 }  // namespace kvs

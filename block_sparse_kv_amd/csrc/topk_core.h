@@ -586,6 +586,79 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   topk_reg_write<KPT>(take, off, k, ibase, none, false, ph, with_tiles, sel, tiles);
 }
 
+// One entry of the selection of a (sequence, group), made by a workgroup that attends it: the same
+// selection as topk_group_reg's over the score row row[0..m) (stored by an earlier launch), loaded with
+// the table row and *len, keys in registers.  Returns entry `slot` of the ascending selection -- its
+// logical block in .x and physical id (trow) in .y -- or (-1, -1) when slot >= k_eff.  slot_lds: two
+// ints of the workgroup's LDS outside S, through which the entry's owner lane hands it over.  With
+// `writer` the workgroup also writes the whole selection: *cnt = k_eff, sel[0..k_eff) ascending,
+// -1 in [k_eff, topk).  tl_rec: the workgroup's timeline record (timeline build), or null.
+template <int NT, int KPT>
+__device__ __forceinline__ int2 topk_slot_reg(const float* row, int m, const int32_t* len, int initial_len,
+                                              int local_len, int topk, int slot, TopkLds& S,
+                                              const int32_t* trow, bool writer, int32_t* sel_,
+                                              int32_t* cnt_, int* slot_lds, unsigned long long* tl_rec) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per block");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto sel = gptr(sel_);
+  auto cnt = gptr(cnt_);
+  const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc(row, m * 4);
+  const __amdgpu_buffer_rsrc_t rt = span_rsrc(trow, m * 4);
+  float v[KPT];
+  int32_t ph[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c)
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (ibase + 64 * c) * 4, 0, 0));
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, (ibase + 64 * c) * 4, 0, 0);
+  const Regions rg = regions_of(ld_uniform_i32(len), initial_len, local_len);
+  const int lo = rg.cand_lo, hi = min(rg.cand_hi, m);
+  const int n = max(0, hi - lo);
+  const int k = min(topk, n);
+#ifdef KVS_TIMELINE
+  wait_mem();  // the timeline's mark 1: the row has arrived
+  if (tl_rec) tl_rec[1] = __builtin_amdgcn_s_memrealtime();
+#endif
+  if (writer) {
+    if (tid == 0) *cnt = k;
+    for (int i = k + tid; i < topk; i += NT) sel[i] = -1;
+  }
+  if (k <= 0) return make_int2(-1, -1);
+  const int d = ibase - lo;  // candidate offset of column 0
+  uint32_t okb = 0u;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) okb |= ((unsigned)(d + 64 * c) < (unsigned)n ? 1u : 0u) << c;
+  if (k >= n) {  // every candidate: entry j is block lo + j
+#pragma unroll
+    for (int c = 0; c < KPT; ++c)
+      if ((okb >> c) & 1u) {
+        if (writer) sel[d + 64 * c] = ibase + 64 * c;
+        if (d + 64 * c == slot) { slot_lds[0] = ibase + 64 * c; slot_lds[1] = ph[c]; }
+      }
+  } else {
+    int off = 0;
+    const uint32_t take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const bool t = (take >> c) & 1u;
+      const unsigned long long km = __ballot(t);
+      if (km != 0ull) {
+        const int j = off + __popcll(km & lt);
+        if (t && j < k) {
+          if (writer) sel[j] = ibase + 64 * c;
+          if (j == slot) { slot_lds[0] = ibase + 64 * c; slot_lds[1] = ph[c]; }
+        }
+        off += __popcll(km);
+      }
+    }
+  }
+  __syncthreads();
+  return slot < k ? make_int2(slot_lds[0], slot_lds[1]) : make_int2(-1, -1);
+}
+
 // Selection from chunk summaries.  The candidates of the row are cut into chunks of kChunkBlocks
 // blocks, chunk c covering blocks [c * kChunkBlocks, (c + 1) * kChunkBlocks); each chunk's scorer wrote
 // its kChunkTop best candidates -- (score, block, physical id), best by (score desc, block asc) --

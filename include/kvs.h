@@ -336,10 +336,14 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
 /*
  * kvs_decode_step -- one decode step of one layer: score -> top-k -> sparse attention
  * [KT-LC §4.6, retrieval then attention], enqueued with no host synchronisation as
- *   for max_blocks_per_seq <= 2048, three launches: 1. scoring, top-k per (sequence, group) by the
- *   scoring workgroup of the group that finishes last, and the Initial/Local tiles' attention (they
- *   do not depend on the selection);  2. attention over the selected tiles;  3. the log-sum-exp
- *   merge into out;
+ *   for max_blocks_per_seq <= 2048 and batch * num_kv_heads * topk <= 1024, three launches:
+ *   1. scoring (with some of the Initial/Local tiles' attention: they do not depend on the
+ *   selection);  2. attention over the selected tiles, where the workgroup of each selected tile
+ *   makes its (sequence, group)'s top-k itself from the scores (every one of them the same), and
+ *   over the other Initial/Local tiles;  3. the log-sum-exp merge into out;
+ *   for other max_blocks_per_seq <= 2048, three launches: 1. scoring, top-k per (sequence, group) by
+ *   the scoring workgroup of the group that finishes last, and the Initial/Local tiles' attention;
+ *   2. attention over the selected tiles;  3. the merge;
  *   SEPARATE with 2048 < max_blocks_per_seq <= 16384 and topk > 0, the same three launches, where
  *   each scoring workgroup (64 blocks of one KV head) also stores its 8 best blocks and the last one
  *   selects from these summaries; when a chunk of 64 blocks holds more than 8 of the selection
