@@ -9,9 +9,11 @@
 //    (score_select_kernel).  The scoring workgroups of a (sequence, group) hand their scores to the
 //    one among them that finishes last, which makes the group's selection (256 lanes, keys in
 //    registers); the Initial/Local tiles stream meanwhile.  Then the selected tiles and the merge.
-//  * SEPARATE rows of up to kStepSummMax blocks: the same launch, each scoring workgroup (one 64-block
-//    chunk of one KV head) also storing its chunk's best 8; the last one selects from these summaries,
-//    or from the whole row when a chunk holds more than 8 of the selection.
+//  * SEPARATE rows of up to kStepSummMax blocks: each scoring workgroup (one 64-block chunk of one KV
+//    head) also stores its chunk's best 8, and the selection is made from these summaries, or from
+//    the whole row when a chunk holds more than 8 of the selection -- for small batches by every
+//    selected tile's workgroup, as for the short rows above (all Initial/Local tiles in the tiles'
+//    launch), else by the last scoring workgroup of the KV head in the scoring launch.
 //  * other long rows: scoring (score.hip); then the top-k selections in 512-lane workgroups with the
 //    Initial/Local tiles, two per workgroup, in one launch (topk_il_wide_kernel), so their gather
 //    runs while the selections are made; then the selected tiles and the merge.
@@ -37,13 +39,13 @@ hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* s
 }
 
 hipError_t launch_attn_select(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count, int batch,
-                              int il0, hipStream_t s) {
+                              int il0, hipStream_t s, const Summaries& U) {
   switch (A.P.kv) {
-    case kKvQ8: return launch_attn_select_kv<kKvQ8>(A, scores, sel, sel_count, batch, il0, s);
-    case kKvQ4: return launch_attn_select_kv<kKvQ4>(A, scores, sel, sel_count, batch, il0, s);
-    case kKvI8: return launch_attn_select_kv<kKvI8>(A, scores, sel, sel_count, batch, il0, s);
-    case kKvI4: return launch_attn_select_kv<kKvI4>(A, scores, sel, sel_count, batch, il0, s);
-    default: return launch_attn_select_kv<kKvFp16>(A, scores, sel, sel_count, batch, il0, s);
+    case kKvQ8: return launch_attn_select_kv<kKvQ8>(A, scores, sel, sel_count, batch, il0, s, U);
+    case kKvQ4: return launch_attn_select_kv<kKvQ4>(A, scores, sel, sel_count, batch, il0, s, U);
+    case kKvI8: return launch_attn_select_kv<kKvI8>(A, scores, sel, sel_count, batch, il0, s, U);
+    case kKvI4: return launch_attn_select_kv<kKvI4>(A, scores, sel, sel_count, batch, il0, s, U);
+    default: return launch_attn_select_kv<kKvFp16>(A, scores, sel, sel_count, batch, il0, s, U);
   }
 }
 
@@ -59,18 +61,25 @@ hipError_t launch_attn_select(const AttnArgs& A, const float* scores, int32_t* s
 //    selections, the others beside the scoring (32K tokens, 8 KV heads: 19.4 us per step, against
 //    20.8 with all of them beside the selections and 20.1 with all beside the scoring); longer rows:
 //    all beside the selections (128K tokens: 23.9 us, against 24.5 with half beside the scoring).
-constexpr int kSelByTilesMax = 1024;
+// SEPARATE rows of up to kStepSummMax blocks select from chunk summaries (summ): the scoring launch
+// stores them, and the selected tiles' workgroups select from them the same way, with every
+// Initial/Local tile beside the selections (1M tokens, 8 KV heads, k 64: 906 against 952 us per step
+// of 32 layers, where the scoring launch's last workgroups selected and the tiles streamed beside).
 constexpr int kIlLate = 16;
 struct SelPlan {
-  bool by_tiles;
+  bool by_tiles, summ;
   int il_first;
 };
-SelPlan select_plan(const Params& P, int batch, int max_blocks, int n_il_max) {
-  SelPlan p{false, n_il_max};
-  if (P.topk <= 0 || max_blocks > kStepTopkSmall) return p;
-  if ((long long)batch * P.Hkv * P.topk > kSelByTilesMax) return p;
-  p.by_tiles = true;
-  p.il_first = max_blocks <= 256 ? (n_il_max > kIlLate ? n_il_max - kIlLate : 0) : 0;
+SelPlan select_plan(const Params& P, int batch, int max_blocks, int n_il_max, bool summ) {
+  SelPlan p{false, false, n_il_max};
+  if (P.topk <= 0 || (long long)batch * P.Hkv * P.topk > kSelByTilesMax) return p;
+  if (max_blocks <= kStepTopkSmall) {
+    p.by_tiles = true;
+    p.il_first = max_blocks <= 256 ? (n_il_max > kIlLate ? n_il_max - kIlLate : 0) : 0;
+  } else if (summ) {
+    p.by_tiles = p.summ = true;
+    p.il_first = 0;
+  }
   return p;
 }
 
@@ -119,19 +128,21 @@ hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* sc
   int32_t* tl = P.topk > 0 ? tiles : nullptr;
   hipError_t e;
   const size_t ub = summaries_bytes(P, batch, A.max_blocks);
-  const SelPlan sp = select_plan(P, batch, A.max_blocks, A.n_il_max);
-  if (sp.by_tiles) {
-    e = launch_score_select(A, rep_pool, scores, nullptr, nullptr, nullptr, nullptr, batch, s, Summaries(),
-                            sp.il_first);
-    if (e == hipSuccess) e = launch_attn_select(A, scores, sel, sel_count, batch, sp.il_first, s);
-  } else if (A.max_blocks <= kStepTopkSmall) {
-    e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s);
-    if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
-  } else if (ub != 0 && summ != nullptr && P.topk > 0) {  // one launch scores and selects
-    Summaries U;
+  Summaries U;
+  if (ub != 0 && summ != nullptr) {
     U.val = static_cast<float*>(summ);
     U.id = reinterpret_cast<int32_t*>(static_cast<char*>(summ) + ub);
     U.phys = reinterpret_cast<int32_t*>(static_cast<char*>(summ) + 2 * ub);
+  }
+  const SelPlan sp = select_plan(P, batch, A.max_blocks, A.n_il_max, U.val != nullptr);
+  if (sp.by_tiles) {
+    const Summaries Us = sp.summ ? U : Summaries();
+    e = launch_score_select(A, rep_pool, scores, nullptr, nullptr, nullptr, nullptr, batch, s, Us, sp.il_first);
+    if (e == hipSuccess) e = launch_attn_select(A, scores, sel, sel_count, batch, sp.il_first, s, Us);
+  } else if (A.max_blocks <= kStepTopkSmall) {
+    e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s);
+    if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
+  } else if (U.val != nullptr && P.topk > 0) {  // one launch scores and selects
     e = launch_score_select(A, rep_pool, scores, sel, sel_count, tl, ctr, batch, s, U);
     if (e == hipSuccess) e = launch_attn_tiles(A, batch, false, true, s);
   } else {

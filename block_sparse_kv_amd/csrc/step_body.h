@@ -11,6 +11,11 @@
 namespace kvs {
 
 constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
+// attn_select_kernel, SUMM: where a whole-row selection (topk entries, then their physical ids) goes in
+// LDS, after the selection's own TopkLds; kSummSlotMax entries fit.
+constexpr int kSummSlotOff = ((int)sizeof(TopkLds) + 15) / 16 * 16;
+constexpr int kSummSlotMax = (kStepLds - kSummSlotOff) / 8;
+static_assert(kSummSlotMax >= kSelByTilesMax, "every topk the in-tile selections take fits");
 
 // The chunk summary of one SEPARATE scoring workgroup (wave 0; chunk = its kChunkBlocks blocks, whose
 // scores are in lds[0..kChunkBlocks) and physical ids in lds[kChunkBlocks..) as ints): the kChunkTop
@@ -54,8 +59,8 @@ __device__ inline void write_chunk_summary(const float* lds, int b0, float* uval
 
 // First the scoring workgroups, n_sc per (sequence, group), over every KV head (SHARED) or over one KV
 // head (SEPARATE; group = KV head): dispatched first, their few loads are not queued behind the
-// tiles' stream.  With sel null the kernel only scores and streams the tiles (a selection made by
-// later launches).  Then n_il_wg Initial/Local tiles, il_per (<= n_il_max) per KV head: tile t < il_per
+// tiles' stream.  With sel null the kernel only scores (and, SUMM, stores the chunk summaries) and
+// streams the tiles (the selections are made by later launches).  Then n_il_wg Initial/Local tiles, il_per (<= n_il_max) per KV head: tile t < il_per
 // of KV head h of sequence seq at (seq * Hkv + h) * il_per + t.  A scoring workgroup stores its
 // scores coherently, waits for them to complete and bumps the group's counter; the one that brings it
 // to n_sc resets it and selects.  Nothing waits on another workgroup.
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                                                  scores + (size_t)seq * P.G * A.max_blocks,
                                                  reinterpret_cast<float*>(smem), grp, SUMM ? lchunk : nullptr);
   KVS_TL_MARK_LOADED(1)
-  if (sel == nullptr) return;  // scores and Initial/Local tiles only: the selection comes later
+  if (!SUMM && sel == nullptr) return;  // scores and Initial/Local tiles only: the selection comes later
   const size_t urow = ((size_t)seq * P.G + grp) * n_sc * kChunkTop;  // this group's summaries
   if constexpr (SUMM) {
     __syncthreads();  // the chunk's scores are in LDS
@@ -102,6 +107,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
       write_chunk_summary(lchunk, c * sb, uval + urow + (size_t)c * kChunkTop,
                           uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
     KVS_TL_MARK(5)
+    if (sel == nullptr) return;  // scores and summaries only: the selections come later
   }
   wait_mem();
   if constexpr (SUMM) {
@@ -202,15 +208,19 @@ hipError_t launch_score_select_kv(const AttnArgs& A_in, const void* rep_pool, fl
 // The selected tiles of a step whose score rows an earlier launch stored, and the Initial/Local tiles
 // [il0, n_il_max) of every KV head, in one grid: workgroups [0, n_sel) are the selected tiles, entry i
 // of the selection of KV head h of sequence seq at (seq * Hkv + h) * topk + i -- dispatched first, so
-// their score loads are not queued behind the Initial/Local tiles' stream -- then Initial/Local tile
+// their loads are not queued behind the Initial/Local tiles' stream -- then Initial/Local tile
 // il0 + t at n_sel + (seq * Hkv + h) * (n_il_max - il0) + t.  A selected tile's workgroup makes its
-// group's selection itself from the score row (topk_slot_reg: every workgroup of a group makes the
-// same one) and gathers its entry; the one of entry 0 (of KV head 0 for SHARED) also writes the
-// group's selection and count.  Nothing passes between the workgroups of the launch.
-template <int G, int KV, int KPT>
+// group's selection itself (every workgroup of a group makes the same one) and gathers its entry; the
+// one of entry 0 (of KV head 0 for SHARED) also writes the group's selection and count.  Nothing
+// passes between the workgroups of the launch.
+//  * rows of up to kStepTopkSmall blocks: from the score row (topk_slot_reg);
+//  * SUMM (SEPARATE rows up to kStepSummMax blocks): from the chunk summaries U of the scoring launch
+//    (topk_summary_slot, n_sc chunks per row), or, when a chunk holds more than kChunkTop of the
+//    selection, from the whole score row (topk_select into LDS).
+template <int G, int KV, int KPT, bool SUMM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attn_select_kernel(
     AttnArgs A, const float* __restrict__ scores, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    int n_sel, int il0) {
+    int n_sel, int il0, Summaries U, int n_sc) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_slot[2];
   const Params& P = A.P;
@@ -225,10 +235,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const size_t row = (size_t)seq * P.G + (P.mode == kSeparate ? h : 0);
   const bool writer = i == 0 && (P.mode == kSeparate || h == 0);
   const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
-  const int2 e = topk_slot_reg<256, KPT>(scores + row * A.max_blocks, A.max_blocks, A.seq_lens + seq,
-                                         P.initial_len, P.local_len, P.topk, i,
-                                         *reinterpret_cast<TopkLds*>(smem), trow, writer,
-                                         sel + row * P.topk, sel_count + row, s_slot, KVS_TL_REC);
+  TopkLds& S = *reinterpret_cast<TopkLds*>(smem);
+  int2 e;
+  if constexpr (SUMM) {
+    const Regions rg = regions_of(A.seq_lens[seq], P.initial_len, P.local_len);
+    const int lo = rg.cand_lo, hi = min(rg.cand_hi, A.max_blocks);
+    const int n = max(0, hi - lo), k = min(P.topk, n);
+    int32_t* srow = sel + row * P.topk;
+    if (writer) {
+      if (threadIdx.x == 0) sel_count[row] = k;
+      for (int j = k + (int)threadIdx.x; j < P.topk; j += 256) srow[j] = -1;
+    }
+    if (i >= k) return;
+    if (k >= n) {  // every candidate
+      if (writer)
+        for (int j = threadIdx.x; j < n; j += 256) srow[j] = lo + j;
+      e = make_int2(lo + i, trow[lo + i]);
+    } else {
+      const size_t urow = row * n_sc * kChunkTop;
+      if (topk_summary_slot<256, KPT>(U.val + urow, U.id + urow, U.phys + urow, n_sc, lo, hi, k, i, S, s_slot,
+                                      writer, srow)) {
+        e = make_int2(s_slot[0], s_slot[1]);
+      } else {  // a chunk overflows: the whole row, its selection and physical ids into LDS after S
+        int32_t* lsel = reinterpret_cast<int32_t*>(smem + kSummSlotOff);
+        int32_t* ltile = lsel + P.topk;
+        __syncthreads();
+        topk_select<256>(scores + row * A.max_blocks + lo, n, k, lo, S, lsel, trow, ltile);
+        __syncthreads();
+        e = make_int2(lsel[i], ltile[i]);
+        if (writer)
+          for (int j = threadIdx.x; j < k; j += 256) srow[j] = lsel[j];
+      }
+    }
+  } else {
+    e = topk_slot_reg<256, KPT>(scores + row * A.max_blocks, A.max_blocks, A.seq_lens + seq, P.initial_len,
+                                P.local_len, P.topk, i, S, trow, writer, sel + row * P.topk, sel_count + row,
+                                s_slot, KVS_TL_REC);
+  }
   KVS_TL_MARK(3)
   if (e.x < 0) return;
   const TileList tl = tiles_of(A.seq_lens[seq], P, 0);
@@ -246,15 +289,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 
 template <int KV>
 hipError_t launch_attn_select_kv(const AttnArgs& A_in, const float* scores, int32_t* sel, int32_t* sel_count,
-                                 int batch, int il0, hipStream_t s) {
+                                 int batch, int il0, hipStream_t s, const Summaries& U) {
   AttnArgs A = A_in;
   A.P.tl_kind = kTlAttn;
   if (il0 < 0 || il0 > A.n_il_max) il0 = A.n_il_max;
   const int n_sel = batch * A.P.Hkv * A.P.topk;
   const dim3 grid(n_sel + batch * A.P.Hkv * (A.n_il_max - il0));
+  const int n_sc = (A.max_blocks + kChunkBlocks - 1) / kChunkBlocks;
+  if (U.val) {  // summaries of up to 256 * 4 (KPT 4) or 256 * 8 entries per row
+    const int kpt = n_sc * kChunkTop <= 1024 ? 4 : 8;
+#define KVS_ASU(GG, KK)                                                                          \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, true>), grid, dim3(256), 0, s, A, scores, sel, \
+                     sel_count, n_sel, il0, U, n_sc)
+#define KVS_ASU_G(GG)                    \
+  if (kpt == 4) KVS_ASU(GG, 4);          \
+  else KVS_ASU(GG, 8);
+    switch (A.P.g) {
+      case 1: KVS_ASU_G(1); break;
+      case 2: KVS_ASU_G(2); break;
+      case 4: KVS_ASU_G(4); break;
+      case 8: KVS_ASU_G(8); break;
+      default: KVS_ASU_G(16); break;
+    }
+#undef KVS_ASU_G
+#undef KVS_ASU
+    return hipGetLastError();
+  }
   const int kpt = A.max_blocks <= 256 ? 1 : (A.max_blocks <= 1024 ? 4 : 8);
-#define KVS_AS(GG, KK) \
-  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK>), grid, dim3(256), 0, s, A, scores, sel, sel_count, n_sel, il0)
+#define KVS_AS(GG, KK)                                                                            \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, false>), grid, dim3(256), 0, s, A, scores, sel, \
+                     sel_count, n_sel, il0, U, n_sc)
 #define KVS_AS_G(GG)                       \
   if (kpt == 1) KVS_AS(GG, 1);             \
   else if (kpt == 4) KVS_AS(GG, 4);        \

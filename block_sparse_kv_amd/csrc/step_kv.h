@@ -21,6 +21,10 @@ struct Summaries {
 // (8 summary entries per 64-block chunk, at most 8 per lane of the 256-lane selection).
 constexpr int kStepSummMax = 256 * 8 * 8;
 
+// The selected tiles' workgroups make their groups' selections themselves while they number at most
+// this many (batch * num_kv_heads * topk): all of them resident at once.
+constexpr int kSelByTilesMax = 1024;
+
 // Scoring, the top-k by the group's last scoring workgroup (sel != nullptr) and the Initial/Local tiles
 // [0, il_per) of each KV head (every one for il_per < 0), in one launch: rows of up to kStepTopkSmall
 // blocks from the whole score row, longer SEPARATE rows (up to kStepSummMax) from the chunk
@@ -32,9 +36,11 @@ hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float
 // The selected tiles, and the Initial/Local tiles [il0, n_il_max) of each KV head, of a step whose
 // rows (up to kStepTopkSmall blocks) were scored by an earlier launch into scores: each selected
 // tile's workgroup makes its group's selection itself.
+// With U (SEPARATE rows of up to kStepSummMax blocks, topk <= kSummSlotMax), from the chunk summaries
+// the scoring launch stored.
 template <int KV>
 hipError_t launch_attn_select_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
-                                 int batch, int il0, hipStream_t s);
+                                 int batch, int il0, hipStream_t s, const Summaries& U);
 // Longer rows: the top-k selections (512-lane workgroups) and the Initial/Local tiles in one launch.
 template <int KV>
 hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,

@@ -586,6 +586,30 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
   topk_reg_write<KPT>(take, off, k, ibase, none, false, ph, with_tiles, sel, tiles);
 }
 
+// Walks the taken keys as topk_reg_write does (ascending position, slots from `off` of the wave on):
+// the lane holding entry `slot` puts its id (idv) and physical id (ph) into slot_lds[0..1]; with
+// `writer`, sel[j] = the id of entry j for every j < k.
+template <int KPT>
+__device__ __forceinline__ void topk_slot_walk(uint32_t take, int off, int k, const int32_t (&idv)[KPT],
+                                               const int32_t (&ph)[KPT], int slot, int* slot_lds, bool writer,
+                                               __attribute__((address_space(1))) int32_t* sel) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool t = (take >> c) & 1u;
+    const unsigned long long km = __ballot(t);
+    if (km != 0ull) {
+      const int j = off + __popcll(km & lt);
+      if (t && j < k) {
+        if (j == slot) { slot_lds[0] = idv[c]; slot_lds[1] = ph[c]; }
+        if (writer) sel[j] = idv[c];
+      }
+      off += __popcll(km);
+    }
+  }
+}
+
 // One entry of the selection of a (sequence, group), made by a workgroup that attends it: the same
 // selection as topk_group_reg's over the score row row[0..m) (stored by an earlier launch), loaded with
 // the table row and *len, keys in registers.  Returns entry `slot` of the ascending selection -- its
@@ -640,20 +664,10 @@ __device__ __forceinline__ int2 topk_slot_reg(const float* row, int m, const int
   } else {
     int off = 0;
     const uint32_t take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
-    const unsigned long long lt = (1ull << lane) - 1ull;
+    int32_t idv[KPT];
 #pragma unroll
-    for (int c = 0; c < KPT; ++c) {
-      const bool t = (take >> c) & 1u;
-      const unsigned long long km = __ballot(t);
-      if (km != 0ull) {
-        const int j = off + __popcll(km & lt);
-        if (t && j < k) {
-          if (writer) sel[j] = ibase + 64 * c;
-          if (j == slot) { slot_lds[0] = ibase + 64 * c; slot_lds[1] = ph[c]; }
-        }
-        off += __popcll(km);
-      }
-    }
+    for (int c = 0; c < KPT; ++c) idv[c] = ibase + 64 * c;
+    topk_slot_walk<KPT>(take, off, k, idv, ph, slot, slot_lds, writer, sel);
   }
   __syncthreads();
   return slot < k ? make_int2(slot_lds[0], slot_lds[1]) : make_int2(-1, -1);
@@ -665,30 +679,31 @@ __device__ __forceinline__ int2 topk_slot_reg(const float* row, int m, const int
 // sorted by block, padded with (-inf, -1, 0), as uval / uid / uphys[c * kChunkTop + e].  The top k of
 // the row are the top k of these entries unless some chunk holds more than kChunkTop of them: that is
 // the case exactly when every entry of a chunk with more than kChunkTop candidates is taken, which is
-// checked.  The entries are in ascending block order, so the selection is written as it is taken.
-// Returns false, having written nothing, when a chunk overflows (the caller selects from the row).
-template <int NT, int KPT>
-__device__ __forceinline__ bool topk_summary_reg(const float* uval, const int32_t* uid, const int32_t* uphys,
-                                                 int n_chunks, int cand_lo, int cand_hi, int k, TopkLds& S,
-                                                 int32_t* sel_, int32_t* tiles_, bool with_tiles) {
+// checked.  The entries are in ascending block order, so the selection comes out in that order.
+// summary_take loads the entries (COH: stored by other workgroups of the same kernel, read
+// coherently) and finds the taken ones: their bits in *take, the wave's first output slot in *off,
+// their block and physical ids in id / ph.  Returns false when a chunk overflows.
+template <int NT, int KPT, bool COH>
+__device__ __forceinline__ bool summary_take(const float* uval, const int32_t* uid, const int32_t* uphys,
+                                             int n_chunks, int cand_lo, int cand_hi, int k, TopkLds& S,
+                                             int32_t (&id)[KPT], int32_t (&ph)[KPT], uint32_t* take_out,
+                                             int* off_out) {
   static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
   static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per entry");
   static_assert(kChunkTop == 8, "a chunk is one byte of a ballot");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  auto sel = gptr(sel_);
-  auto tiles = gptr(tiles_);
   const int m = n_chunks * kChunkTop;
   const int ibase = wv * 64 * KPT + lane;
   const __amdgpu_buffer_rsrc_t rv = span_rsrc(uval, m * 4);
   const __amdgpu_buffer_rsrc_t ri = span_rsrc(uid, m * 4);
   const __amdgpu_buffer_rsrc_t rp = span_rsrc(uphys, m * 4);
+  constexpr int pol = COH ? kSc1 : 0;
   float v[KPT];
-  int32_t id[KPT], ph[KPT];
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
-    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, (ibase + 64 * c) * 4, 0, kSc1));
-    id[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (ibase + 64 * c) * 4, 0, kSc1);
-    ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (ibase + 64 * c) * 4, 0, kSc1);
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, (ibase + 64 * c) * 4, 0, pol));
+    id[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (ibase + 64 * c) * 4, 0, pol);
+    ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (ibase + 64 * c) * 4, 0, pol);
   }
   uint32_t okb = 0u;
 #pragma unroll
@@ -712,8 +727,43 @@ __device__ __forceinline__ bool topk_summary_reg(const float* uval, const int32_
   __syncthreads();
   if (__ballot(ovf) != 0ull && lane == 0) S.bcast[0] = 1;
   __syncthreads();
-  if (S.bcast[0] != 0) return false;
-  topk_reg_write<KPT>(take, off, k, ibase, id, true, ph, with_tiles, sel, tiles);
+  *take_out = take;
+  *off_out = off;
+  return S.bcast[0] == 0;
+}
+
+// The selection of the chunk summaries of the same kernel, written in full: sel[0..k) and (with_tiles)
+// tiles[0..k).  Returns false, having written nothing, when a chunk overflows (the caller selects from
+// the row).
+template <int NT, int KPT>
+__device__ __forceinline__ bool topk_summary_reg(const float* uval, const int32_t* uid, const int32_t* uphys,
+                                                 int n_chunks, int cand_lo, int cand_hi, int k, TopkLds& S,
+                                                 int32_t* sel_, int32_t* tiles_, bool with_tiles) {
+  int32_t id[KPT], ph[KPT];
+  uint32_t take;
+  int off;
+  if (!summary_take<NT, KPT, true>(uval, uid, uphys, n_chunks, cand_lo, cand_hi, k, S, id, ph, &take, &off))
+    return false;
+  const int ibase = (threadIdx.x >> 6) * 64 * KPT + (threadIdx.x & 63);
+  topk_reg_write<KPT>(take, off, k, ibase, id, true, ph, with_tiles, gptr(sel_), gptr(tiles_));
+  return true;
+}
+
+// Entry `slot` of the selection from chunk summaries stored by an earlier launch, made by a workgroup
+// that attends it (as topk_slot_reg): returns false on a chunk overflow, else true with the entry's
+// block and physical id in slot_lds[0..1] once every lane may read them (-1 when slot >= k); with
+// `writer` the workgroup also writes sel[0..k).
+template <int NT, int KPT>
+__device__ __forceinline__ bool topk_summary_slot(const float* uval, const int32_t* uid, const int32_t* uphys,
+                                                  int n_chunks, int cand_lo, int cand_hi, int k, int slot,
+                                                  TopkLds& S, int* slot_lds, bool writer, int32_t* sel_) {
+  int32_t id[KPT], ph[KPT];
+  uint32_t take;
+  int off;
+  if (!summary_take<NT, KPT, false>(uval, uid, uphys, n_chunks, cand_lo, cand_hi, k, S, id, ph, &take, &off))
+    return false;
+  topk_slot_walk<KPT>(take, off, k, id, ph, slot, slot_lds, writer, gptr(sel_));
+  __syncthreads();
   return true;
 }
 

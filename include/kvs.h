@@ -344,10 +344,13 @@ size_t kvs_decode_step_workspace_size(const kvs_config* cfg, int32_t batch,
  *   for other max_blocks_per_seq <= 2048, three launches: 1. scoring, top-k per (sequence, group) by
  *   the scoring workgroup of the group that finishes last, and the Initial/Local tiles' attention;
  *   2. attention over the selected tiles;  3. the merge;
- *   SEPARATE with 2048 < max_blocks_per_seq <= 16384 and topk > 0, the same three launches, where
- *   each scoring workgroup (64 blocks of one KV head) also stores its 8 best blocks and the last one
- *   selects from these summaries; when a chunk of 64 blocks holds more than 8 of the selection
- *   (the summaries cannot tell which), it selects from the whole score row instead;
+ *   SEPARATE with 2048 < max_blocks_per_seq <= 16384 and topk > 0, three launches in which each
+ *   scoring workgroup (64 blocks of one KV head) also stores its 8 best blocks and the selection is
+ *   made from these summaries -- for batch * num_kv_heads * topk <= 1024 by the workgroup of each
+ *   selected tile (1. scoring;  2. the selected tiles, each making its KV head's top-k, and the
+ *   Initial/Local tiles;  3. the merge), otherwise by the last scoring workgroup of the KV head, in
+ *   the scoring launch with the Initial/Local tiles; when a chunk of 64 blocks holds more than 8 of
+ *   the selection (the summaries cannot tell which), it is made from the whole score row instead;
  *   otherwise four: 1. scoring;  2. top-k, with the Initial/Local tiles' attention;  3. attention
  *   over the selected tiles;  4. the merge.
  * Top-k also resolves the selected blocks' physical ids.
