@@ -695,14 +695,13 @@ int kvs_decode_step_preselected(const kvs_config* cfg, const void* q, const void
   void* aws = static_cast<char*>(workspace) + S.attn_off;
   if ((st = debug_check(P, s, seq_lens, batch, block_table, max_blocks_per_seq, nullptr, nullptr, presel, n_presel)) != KVS_OK) return st;
   if (n_presel <= kvs::presel_step_max() && P.topk > 0 && (size_t)rows * sizeof(int) <= kCtrBytes) {
-    // one launch scores the sets, selects from them and streams the Initial/Local tiles
+    // the sets scored, the selections made from them, and every attended tile, in two launches
     int32_t* tiles = at<int32_t>(workspace, S.tiles_off);
     kvs::AttnArgs a = attn_args(P, S.attn, aws, q, k_pool, v_pool, block_table, max_blocks_per_seq,
                                 seq_lens, tiles, cnt, out);
     clear_stale_error();
     hipError_t e = kvs::launch_presel_step(a, rep_pool, presel, n_presel, cs, at<int32_t>(workspace, S.cph_off),
                                            sel, cnt, tiles, at<int>(workspace, S.ctr_off), batch, s);
-    if (e == hipSuccess) e = kvs::launch_attn_tiles(a, batch, false, true, s);
     if (e == hipSuccess) e = kvs::launch_merge(a, batch, s);
     return hip_status(e, "kvs_decode_step_preselected");
   }

@@ -76,10 +76,10 @@ hipError_t launch_decode_step(const AttnArgs& A, const void* rep_pool, float* sc
                               int32_t* sel_count, int32_t* tiles, int* ctr, int batch, hipStream_t s,
                               void* summ);
 
-// The confined step's first launch (step.hip): the sets presel [batch][G][n_presel] (n_presel <=
+// The confined step up to its merge (step.hip): the sets presel [batch][G][n_presel] (n_presel <=
 // presel_step_max()) scored into cs / cph [batch][G][n_presel] (scores, physical ids), the selection
-// (sel: logical ids, tiles: physical ids, cnt) and the Initial/Local tiles; ctr as for
-// launch_decode_step.
+// (sel: logical ids, cnt; tiles: physical ids, when the scoring launch makes it), and the attention
+// over the Initial/Local and selected tiles into A's partials; ctr as for launch_decode_step.
 int presel_step_max();
 hipError_t launch_presel_step(const AttnArgs& A, const void* rep_pool, const int32_t* presel, int n_presel,
                               float* cs, int32_t* cph, int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr,

@@ -39,13 +39,13 @@ hipError_t launch_score_select(const AttnArgs& A, const void* rep_pool, float* s
 }
 
 hipError_t launch_attn_select(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count, int batch,
-                              int il0, hipStream_t s, const Summaries& U) {
+                              int il0, hipStream_t s, const Summaries& U, int n_list = 0) {
   switch (A.P.kv) {
-    case kKvQ8: return launch_attn_select_kv<kKvQ8>(A, scores, sel, sel_count, batch, il0, s, U);
-    case kKvQ4: return launch_attn_select_kv<kKvQ4>(A, scores, sel, sel_count, batch, il0, s, U);
-    case kKvI8: return launch_attn_select_kv<kKvI8>(A, scores, sel, sel_count, batch, il0, s, U);
-    case kKvI4: return launch_attn_select_kv<kKvI4>(A, scores, sel, sel_count, batch, il0, s, U);
-    default: return launch_attn_select_kv<kKvFp16>(A, scores, sel, sel_count, batch, il0, s, U);
+    case kKvQ8: return launch_attn_select_kv<kKvQ8>(A, scores, sel, sel_count, batch, il0, s, U, n_list);
+    case kKvQ4: return launch_attn_select_kv<kKvQ4>(A, scores, sel, sel_count, batch, il0, s, U, n_list);
+    case kKvI8: return launch_attn_select_kv<kKvI8>(A, scores, sel, sel_count, batch, il0, s, U, n_list);
+    case kKvI4: return launch_attn_select_kv<kKvI4>(A, scores, sel, sel_count, batch, il0, s, U, n_list);
+    default: return launch_attn_select_kv<kKvFp16>(A, scores, sel, sel_count, batch, il0, s, U, n_list);
   }
 }
 
@@ -104,16 +104,35 @@ hipError_t launch_score_il(const AttnArgs& A, const void* rep_pool, float* score
 
 int presel_step_max() { return kPreselStepMax; }
 
+// The confined step's scoring and tiles: as for the decode step's short rows (select_plan), while the
+// selected tiles' workgroups number at most kSelByTilesMax each makes its row's selection from the
+// scored set itself, with up to kIlLate Initial/Local tiles per KV head beside the selections for sets
+// of up to 256 entries (every one beside them for larger sets); otherwise the scoring launch's last
+// workgroup of each row selects, and the selected tiles follow in a launch of their own.
 hipError_t launch_presel_step(const AttnArgs& A, const void* rep_pool, const int32_t* presel, int n_presel,
                               float* cs, int32_t* cph, int32_t* sel, int32_t* cnt, int32_t* tiles, int* ctr,
                               int batch, hipStream_t s) {
+  const bool by_tiles = (long long)batch * A.P.Hkv * A.P.topk <= kSelByTilesMax;
+  const int il_per = !by_tiles ? -1 : n_presel <= 256 ? (A.n_il_max > kIlLate ? A.n_il_max - kIlLate : 0) : 0;
+  int32_t* ssel = by_tiles ? nullptr : sel;
+  hipError_t e;
+#define KVS_PS_ONE(KK) \
+  launch_presel_step_kv<KK>(A, rep_pool, presel, n_presel, cs, cph, ssel, cnt, tiles, ctr, batch, s, il_per)
   switch (A.P.kv) {
-    case kKvQ8: return launch_presel_step_kv<kKvQ8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
-    case kKvQ4: return launch_presel_step_kv<kKvQ4>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
-    case kKvI8: return launch_presel_step_kv<kKvI8>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
-    case kKvI4: return launch_presel_step_kv<kKvI4>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
-    default: return launch_presel_step_kv<kKvFp16>(A, rep_pool, presel, n_presel, cs, cph, sel, cnt, tiles, ctr, batch, s);
+    case kKvQ8: e = KVS_PS_ONE(kKvQ8); break;
+    case kKvQ4: e = KVS_PS_ONE(kKvQ4); break;
+    case kKvI8: e = KVS_PS_ONE(kKvI8); break;
+    case kKvI4: e = KVS_PS_ONE(kKvI4); break;
+    default: e = KVS_PS_ONE(kKvFp16); break;
   }
+#undef KVS_PS_ONE
+  if (e != hipSuccess) return e;
+  if (!by_tiles) return launch_attn_tiles(A, batch, false, true, s);
+  Summaries L;  // the sets, their scores and physical ids by position
+  L.val = cs;
+  L.id = const_cast<int32_t*>(presel);
+  L.phys = cph;
+  return launch_attn_select(A, cs, sel, cnt, batch, il_per, s, L, n_presel);
 }
 
 size_t summaries_bytes(const Params& P, int batch, int max_blocks) {

@@ -11,7 +11,7 @@
 namespace kvs {
 
 constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : (int)sizeof(TopkLds);
-// attn_select_kernel, SUMM: where a whole-row selection (topk entries, then their physical ids) goes in
+// attn_select_kernel, kSrcSumm: where a whole-row selection (topk entries, then their physical ids) goes in
 // LDS, after the selection's own TopkLds; kSummSlotMax entries fit.
 constexpr int kSummSlotOff = ((int)sizeof(TopkLds) + 15) / 16 * 16;
 constexpr int kSummSlotMax = (kStepLds - kSummSlotOff) / 8;
@@ -214,13 +214,17 @@ hipError_t launch_score_select_kv(const AttnArgs& A_in, const void* rep_pool, fl
 // one of entry 0 (of KV head 0 for SHARED) also writes the group's selection and count.  Nothing
 // passes between the workgroups of the launch.
 //  * rows of up to kStepTopkSmall blocks: from the score row (topk_slot_reg);
-//  * SUMM (SEPARATE rows up to kStepSummMax blocks): from the chunk summaries U of the scoring launch
-//    (topk_summary_slot, n_sc chunks per row), or, when a chunk holds more than kChunkTop of the
-//    selection, from the whole score row (topk_select into LDS).
-template <int G, int KV, int KPT, bool SUMM>
+//  * SRC kSrcSumm (SEPARATE rows up to kStepSummMax blocks): from the chunk summaries U of the scoring
+//    launch (topk_summary_slot, n_u chunks per row), or, when a chunk holds more than kChunkTop of
+//    the selection, from the whole score row (topk_select into LDS);
+//  * SRC kSrcList (the confined step): from the preselected set of each row -- U.id = the sets
+//    [rows][n_u] (block ids), U.val / U.phys = their scores and physical ids by position, stored by
+//    the scoring launch (topk_list_slot).
+constexpr int kSrcRow = 0, kSrcSumm = 1, kSrcList = 2;
+template <int G, int KV, int KPT, int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attn_select_kernel(
     AttnArgs A, const float* __restrict__ scores, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    int n_sel, int il0, Summaries U, int n_sc) {
+    int n_sel, int il0, Summaries U, int n_u) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_slot[2];
   const Params& P = A.P;
@@ -237,7 +241,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int32_t* trow = A.table + (size_t)seq * A.max_blocks;
   TopkLds& S = *reinterpret_cast<TopkLds*>(smem);
   int2 e;
-  if constexpr (SUMM) {
+  if constexpr (SRC == kSrcList) {
+    const Regions rg = regions_of(A.seq_lens[seq], P.initial_len, P.local_len);
+    const size_t urow = row * n_u;
+    e = topk_list_slot<256, KPT>(U.val + urow, U.phys + urow, U.id + urow, n_u, rg.cand_lo,
+                                 min(rg.cand_hi, A.max_blocks), P.topk, i, S, s_slot, writer,
+                                 sel + row * P.topk, sel_count + row);
+  } else if constexpr (SRC == kSrcSumm) {
     const Regions rg = regions_of(A.seq_lens[seq], P.initial_len, P.local_len);
     const int lo = rg.cand_lo, hi = min(rg.cand_hi, A.max_blocks);
     const int n = max(0, hi - lo), k = min(P.topk, n);
@@ -252,8 +262,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
         for (int j = threadIdx.x; j < n; j += 256) srow[j] = lo + j;
       e = make_int2(lo + i, trow[lo + i]);
     } else {
-      const size_t urow = row * n_sc * kChunkTop;
-      if (topk_summary_slot<256, KPT>(U.val + urow, U.id + urow, U.phys + urow, n_sc, lo, hi, k, i, S, s_slot,
+      const size_t urow = row * n_u * kChunkTop;
+      if (topk_summary_slot<256, KPT>(U.val + urow, U.id + urow, U.phys + urow, n_u, lo, hi, k, i, S, s_slot,
                                       writer, srow)) {
         e = make_int2(s_slot[0], s_slot[1]);
       } else {  // a chunk overflows: the whole row, its selection and physical ids into LDS after S
@@ -289,17 +299,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 
 template <int KV>
 hipError_t launch_attn_select_kv(const AttnArgs& A_in, const float* scores, int32_t* sel, int32_t* sel_count,
-                                 int batch, int il0, hipStream_t s, const Summaries& U) {
+                                 int batch, int il0, hipStream_t s, const Summaries& U, int n_list) {
   AttnArgs A = A_in;
   A.P.tl_kind = kTlAttn;
   if (il0 < 0 || il0 > A.n_il_max) il0 = A.n_il_max;
   const int n_sel = batch * A.P.Hkv * A.P.topk;
   const dim3 grid(n_sel + batch * A.P.Hkv * (A.n_il_max - il0));
+  if (n_list > 0) {  // preselected sets of up to 256 (KPT 1) or 1024 (KPT 4) entries
+#define KVS_ASL(GG, KK)                                                                              \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, kSrcList>), grid, dim3(256), 0, s, A, scores, sel, \
+                     sel_count, n_sel, il0, U, n_list)
+#define KVS_ASL_G(GG)                    \
+  if (n_list <= 256) KVS_ASL(GG, 1);     \
+  else KVS_ASL(GG, 4);
+    switch (A.P.g) {
+      case 1: KVS_ASL_G(1); break;
+      case 2: KVS_ASL_G(2); break;
+      case 4: KVS_ASL_G(4); break;
+      case 8: KVS_ASL_G(8); break;
+      default: KVS_ASL_G(16); break;
+    }
+#undef KVS_ASL_G
+#undef KVS_ASL
+    return hipGetLastError();
+  }
   const int n_sc = (A.max_blocks + kChunkBlocks - 1) / kChunkBlocks;
   if (U.val) {  // summaries of up to 256 * 4 (KPT 4) or 256 * 8 entries per row
     const int kpt = n_sc * kChunkTop <= 1024 ? 4 : 8;
-#define KVS_ASU(GG, KK)                                                                          \
-  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, true>), grid, dim3(256), 0, s, A, scores, sel, \
+#define KVS_ASU(GG, KK)                                                                              \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, kSrcSumm>), grid, dim3(256), 0, s, A, scores, sel, \
                      sel_count, n_sel, il0, U, n_sc)
 #define KVS_ASU_G(GG)                    \
   if (kpt == 4) KVS_ASU(GG, 4);          \
@@ -316,8 +344,8 @@ hipError_t launch_attn_select_kv(const AttnArgs& A_in, const float* scores, int3
     return hipGetLastError();
   }
   const int kpt = A.max_blocks <= 256 ? 1 : (A.max_blocks <= 1024 ? 4 : 8);
-#define KVS_AS(GG, KK)                                                                            \
-  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, false>), grid, dim3(256), 0, s, A, scores, sel, \
+#define KVS_AS(GG, KK)                                                                             \
+  hipLaunchKernelGGL((attn_select_kernel<GG, KV, KK, kSrcRow>), grid, dim3(256), 0, s, A, scores, sel, \
                      sel_count, n_sel, il0, U, n_sc)
 #define KVS_AS_G(GG)                       \
   if (kpt == 1) KVS_AS(GG, 1);             \
@@ -402,14 +430,15 @@ hipError_t launch_topk_il_wide_kv(const AttnArgs& A_in, const float* scores, int
 // kPreselStepMax entries: n_pc scoring workgroups per (sequence, group) row score the row's
 // preselected blocks -- positions [c * sb, c * sb + sb) of presel[row] -- and store each score and
 // physical id by position, coherently (cs, cph [row][n_presel]); the one that brings the row's
-// counter to n_pc selects from them (topk_list_reg) and resets it.  Then the Initial/Local tiles, as
-// in score_select_kernel.  Rows of any length: only the set is scored.
+// counter to n_pc selects from them (topk_list_reg) and resets it.  With sel null the kernel only
+// scores (the selections are made by the tiles' workgroups).  Then the Initial/Local tiles [0, il_per)
+// of each KV head, as in score_select_kernel.  Rows of any length: only the set is scored.
 template <int G, int METHOD, int MODE, int KV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void presel_step_kernel(
     AttnArgs A, const void* __restrict__ rep_pool, const int32_t* __restrict__ presel, int n_presel,
     float* __restrict__ cs, int32_t* __restrict__ cph, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ tiles, int* __restrict__ ctr, int ctr_stride,
-    int n_pc, int n_il_wg) {
+    int n_pc, int n_il_wg, int il_per) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
   __shared__ int s_last;
   const Params& P = A.P;
@@ -417,9 +446,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int x = blockIdx.x;
   if (x >= n_score_wg) {
     const int xi = x - n_score_wg;
-    const int per_seq = P.Hkv * A.n_il_max;
+    const int per_seq = P.Hkv * il_per;
     const int r = xi % per_seq;
-    attn_item<G, true, false, KV>(A, r % A.n_il_max, r / A.n_il_max, xi / per_seq, smem);
+    attn_item<G, true, false, KV>(A, r % il_per, r / il_per, xi / per_seq, smem);
     return;
   }
   constexpr bool SEP = MODE == kSeparate;
@@ -435,6 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
                                                        reinterpret_cast<float*>(smem), grp, nullptr, ids,
                                                        n_presel, cph + rbase);
   KVS_TL_MARK_LOADED(1)
+  if (sel == nullptr) return;  // scores only: the selections are made by the tiles' workgroups
   wait_mem();
   __syncthreads();
   int* cp = ctr + (size_t)row * ctr_stride;
@@ -455,19 +485,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 template <int KV>
 hipError_t launch_presel_step_kv(const AttnArgs& A_in, const void* rep_pool, const int32_t* presel,
                                  int n_presel, float* cs, int32_t* cph, int32_t* sel, int32_t* cnt,
-                                 int32_t* tiles, int* ctr, int batch, hipStream_t s) {
+                                 int32_t* tiles, int* ctr, int batch, hipStream_t s, int il_per) {
   AttnArgs A = A_in;
   A.P.tl_kind = kTlIlStep;
   const Params& P = A.P;
   const int sb = P.mode == kSeparate ? kScoreBlocksPerHeadWg : score_blocks_per_wg(P);
   const int n_pc = (n_presel + sb - 1) / sb;
   const int rows = batch * P.G;
-  const int n_il_wg = batch * P.Hkv * A.n_il_max;
+  if (il_per < 0 || il_per > A.n_il_max) il_per = A.n_il_max;
+  const int n_il_wg = batch * P.Hkv * il_per;
   const dim3 grid(n_il_wg + rows * n_pc);
   const int cst = step_ctr_stride(rows);
 #define KVS_PS(GG, MM, MO)                                                                            \
   hipLaunchKernelGGL((presel_step_kernel<GG, MM, MO, KV>), grid, dim3(256), 0, s, A, rep_pool, presel, \
-                     n_presel, cs, cph, sel, cnt, tiles, ctr, cst, n_pc, n_il_wg)
+                     n_presel, cs, cph, sel, cnt, tiles, ctr, cst, n_pc, n_il_wg, il_per)
 #define KVS_PS_M(GG, MO)                               \
   switch (P.method) {                                  \
     case kQuest: KVS_PS(GG, kQuest, MO); break;        \

@@ -6,10 +6,10 @@ template hipError_t launch_score_select_kv<kKvI4>(const AttnArgs&, const void*, 
                                                 int32_t*, int*, int, hipStream_t,
                                                 const Summaries&, int);
 template hipError_t launch_attn_select_kv<kKvI4>(const AttnArgs&, const float*, int32_t*, int32_t*, int,
-                                               int, hipStream_t, const Summaries&);
+                                               int, hipStream_t, const Summaries&, int);
 template hipError_t launch_topk_il_wide_kv<kKvI4>(const AttnArgs&, const float*, int32_t*, int32_t*, int32_t*,
                                                 int, hipStream_t);
 template hipError_t launch_presel_step_kv<kKvI4>(const AttnArgs&, const void*, const int32_t*, int, float*,
                                                 int32_t*, int32_t*, int32_t*, int32_t*, int*, int,
-                                                hipStream_t);
+                                                hipStream_t, int);
 }  // namespace kvs

@@ -37,10 +37,11 @@ hipError_t launch_score_select_kv(const AttnArgs& A, const void* rep_pool, float
 // rows (up to kStepTopkSmall blocks) were scored by an earlier launch into scores: each selected
 // tile's workgroup makes its group's selection itself.
 // With U (SEPARATE rows of up to kStepSummMax blocks, topk <= kSummSlotMax), from the chunk summaries
-// the scoring launch stored.
+// the scoring launch stored; with n_list > 0, from the preselected sets U.id [rows][n_list] (at most
+// kPreselStepMax entries) and their scores and physical ids U.val / U.phys stored by the scoring.
 template <int KV>
 hipError_t launch_attn_select_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
-                                 int batch, int il0, hipStream_t s, const Summaries& U);
+                                 int batch, int il0, hipStream_t s, const Summaries& U, int n_list = 0);
 // Longer rows: the top-k selections (512-lane workgroups) and the Initial/Local tiles in one launch.
 template <int KV>
 hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_t* sel, int32_t* sel_count,
@@ -51,9 +52,11 @@ hipError_t launch_topk_il_wide_kv(const AttnArgs& A, const float* scores, int32_
 // per lane).
 constexpr int kPreselStepKeys = 4;
 constexpr int kPreselStepMax = 256 * kPreselStepKeys;
+// With sel null: the scoring only (and the Initial/Local tiles [0, il_per) of each KV head; every one
+// for il_per < 0).
 template <int KV>
 hipError_t launch_presel_step_kv(const AttnArgs& A, const void* rep_pool, const int32_t* presel,
                                  int n_presel, float* cs, int32_t* cph, int32_t* sel, int32_t* cnt,
-                                 int32_t* tiles, int* ctr, int batch, hipStream_t s);
+                                 int32_t* tiles, int* ctr, int batch, hipStream_t s, int il_per = -1);
 
 }  // namespace kvs

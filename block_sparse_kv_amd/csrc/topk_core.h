@@ -823,6 +823,62 @@ __device__ __forceinline__ void topk_list_reg(const float* vals, const int32_t* 
   if (k > 0) topk_reg_write<KPT>(take, off, k, ibase, id, true, ph, true, sel, tiles);
 }
 
+// Entry `slot` of the selection from a preselected list (as topk_list_reg, the list's scores and
+// physical ids stored by an earlier launch), made by a workgroup that attends it: returns its block id
+// in .x and physical id in .y, or (-1, -1) when slot >= k.  With `writer` the workgroup also writes
+// the whole selection: *cnt = k, sel[0..k) ascending, -1 in [k, topk).
+template <int NT, int KPT>
+__device__ __forceinline__ int2 topk_list_slot(const float* vals, const int32_t* phys, const int32_t* ids,
+                                               int m, int cand_lo, int cand_hi, int topk, int slot, TopkLds& S,
+                                               int* slot_lds, bool writer, int32_t* sel_, int32_t* cnt_) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "4 to 16 waves");
+  static_assert(NT * KPT <= 32 * kBmapWords, "one bitmap bit per entry");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto sel = gptr(sel_);
+  auto cnt = gptr(cnt_);
+  const int ibase = wv * 64 * KPT + lane;
+  const __amdgpu_buffer_rsrc_t rv = span_rsrc(vals, m * 4);
+  const __amdgpu_buffer_rsrc_t rp = span_rsrc(phys, m * 4);
+  const __amdgpu_buffer_rsrc_t ri = span_rsrc(ids, m * 4);
+  float v[KPT];
+  int32_t id[KPT], ph[KPT];
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, (ibase + 64 * c) * 4, 0, 0));
+    ph[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (ibase + 64 * c) * 4, 0, 0);
+    id[c] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (ibase + 64 * c) * 4, 0, 0);
+  }
+  uint32_t okb = 0u;
+  int n_w = 0;  // candidates of this wave
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const bool ok = ibase + 64 * c < m && id[c] >= cand_lo && id[c] < cand_hi;
+    okb |= (ok ? 1u : 0u) << c;
+    n_w += __popcll(__ballot(ok));
+  }
+  if (lane == 0) S.woff[wv] = n_w;
+  __syncthreads();
+  int n_ok = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_ok += S.woff[w];
+    before += w < wv ? S.woff[w] : 0;
+  }
+  const int k = min(topk, n_ok);
+  if (writer) {
+    if (tid == 0) *cnt = k;
+    for (int i = k + tid; i < topk; i += NT) sel[i] = -1;
+  }
+  if (k <= 0) return make_int2(-1, -1);
+  uint32_t take = okb;  // every candidate, in order from the wave's offset
+  int off = before;
+  if (k < n_ok) take = topk_reg_take<NT, KPT>(v, okb, k, ibase, S, &off);
+  topk_slot_walk<KPT>(take, off, k, id, ph, slot, slot_lds, writer, sel);
+  __syncthreads();
+  return slot < k ? make_int2(slot_lds[0], slot_lds[1]) : make_int2(-1, -1);
+}
+
 // The selection of group grp of sequence seq from the scores [batch][G][max_blocks]: sel (and, with a
 // table and tiles, the physical ids in tiles) [batch][G][topk] ascending and -1 padded,
 // sel_count [batch][G].  Rows of up to NT * KMAX blocks stay in registers.  COH (rows of up to

@@ -270,9 +270,12 @@ size_t kvs_decode_step_preselected_workspace_size(const kvs_config* cfg, int32_t
  * padded, e.g. from kvs_preselect_blocks) that are still candidates at the current length compete;
  * k_eff = min(topk, their number), so with topk >= the set's size the set is attended as it is.
  * Scores, ties, order and attention as kvs_decode_step.  With topk > 0, n_presel <= 1024 and
- * batch * G <= 16384, enqueued as three launches: 1. scoring of the sets' blocks only, the
- * selection from them by the scoring workgroup of the (sequence, group) that finishes last, and the
- * Initial/Local tiles;  2. attention over the selected tiles;  3. the merge.  Otherwise: scoring of
+ * batch * G <= 16384, enqueued as three launches: 1. scoring of the sets' blocks only (with some of
+ * the Initial/Local tiles);  2. attention over the selected tiles, where the workgroup of each selected
+ * tile makes its (sequence, group)'s selection from the scored set itself, and over the other
+ * Initial/Local tiles (for batch * num_kv_heads * topk <= 1024; otherwise the selection is made in
+ * launch 1 by the scoring workgroup of the (sequence, group) that finishes last, with every
+ * Initial/Local tile);  3. the merge.  Otherwise: scoring of
  * every candidate (with the Initial/Local tiles for max_blocks_per_seq <= 2048), a ranking of the
  * set (n_presel <= 256) or compaction, top-k and mapping, attention tiles and merge.
  * workspace: >= the size query, 256-byte aligned.  Like kvs_decode_step's, its first 64 KiB hold

@@ -94,6 +94,8 @@ STEP_CASES = [
     (16, 4, "separate", "quest", 24, [280000], "fp16", 1100),  # 1106 entries: compacted rows
     (32, 8, "shared", "fix", 20, [150000, 90000], "fp16", 1012),  # 1018 entries: one launch, near its limit
     (8, 8, "separate", "max", 7, [130000], "q8_0", 300),  # every KV head its own set, g = 1
+    # batch * Hkv * k > 1024: the scoring launch's last workgroup of each row selects
+    (32, 8, "shared", "max", 70, [60000, 40000], "fp16", 100),
 ]
 
 
