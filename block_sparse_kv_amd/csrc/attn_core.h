@@ -575,26 +575,31 @@ __device__ inline void merge_head(const float* __restrict__ part_o, const float*
   }
 }
 
-// Merge of channels [ch0, ch0 + 16) of one query head over its n partials by ONE wave: no workgroup
-// barriers, the reductions go through DPP and the wave's own LDS.  Lane l owns channels
+// Merge of channels [ch0, ch0 + 16) of one query head over its n (<= n_max) partials by ONE wave: no
+// workgroup barriers, the reductions go through DPP and the wave's own LDS.  Lane l owns channels
 // ch0 + 4(l % 4) .. +3 of partials l / 4 + 16u; the outputs of the first 16 * kMergeWaveRows partials
-// and the (max, sum) pairs of the first 64 * kMergeWaveMl are requested together, before anything
-// depends on them.  wl: this wave's LDS scratch of >= n + 256 floats.  n == 0 gives zeros.
+// and the (max, sum) pairs of the first 64 * kMergeWaveMl are requested together, with indices clamped
+// to n_max rather than n, so that they travel with the loads that produce n (entries past n are read
+// and not used).  wl: this wave's LDS scratch of >= n + 256 floats.  n == 0 gives zeros.
 constexpr int kMergeChWave = 16;
 constexpr int kMergeWaveRows = 12;
 constexpr int kMergeWaveMl = 3;
+// n_of() gives n; it is called after those requests, so that its own loads' waits (and branches) come
+// after them.
+template <typename NFn>
 __device__ inline void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                       int n, int ch0, float* __restrict__ out, float* wl) {
+                                       int n_max, NFn n_of, int ch0, float* __restrict__ out, float* wl) {
   const int lane = threadIdx.x & 63, cg = lane & 3, pg = lane >> 2;
   auto ld_ml = [&](int s) { return *reinterpret_cast<const float2*>(part_ml + (size_t)s * 2); };
   auto ld_o = [&](int s) { return *reinterpret_cast<const float4*>(part_o + (size_t)s * kDim + ch0 + 4 * cg); };
-  const int last = max(n - 1, 0);
+  const int last = max(n_max - 1, 0);
   float2 ml[kMergeWaveMl];
 #pragma unroll
   for (int r = 0; r < kMergeWaveMl; ++r) ml[r] = ld_ml(min(lane + 64 * r, last));
   float4 o[kMergeWaveRows];
 #pragma unroll
   for (int u = 0; u < kMergeWaveRows; ++u) o[u] = ld_o(min(pg + 16 * u, last));
+  const int n = n_of();
   float M = -INFINITY;
 #pragma unroll
   for (int r = 0; r < kMergeWaveMl; ++r)
@@ -702,12 +707,21 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
 }
 
 // Merge of channels [16c, 16c + 16) of query head j of sequence seq by one wave (merge_head_wave).
+// The sequence's length and the group's selection count are loaded first, without branches (the
+// count through a buffer load that reads 0 when there is no selection), so that they travel with the
+// partials' loads.
 __device__ inline void merge_item_wave(const AttnArgs& A, int j, int c, int seq, float* wl) {
   const Params& P = A.P;
-  const int cnt = P.topk > 0 ? A.sel_count[(size_t)seq * P.G + (P.mode == kSeparate ? j / P.g : 0)] : 0;
-  const TileList tl = tiles_of(A.seq_lens[seq], P, cnt);
+  const int L = A.seq_lens[seq];
+  const __amdgpu_buffer_rsrc_t rc =
+      span_rsrc(A.sel_count + (size_t)seq * P.G + (P.mode == kSeparate ? j / P.g : 0), P.topk > 0 ? 4 : 0);
+  const int cnt = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, 0, 0, 0);
   const size_t hp = (size_t)seq * P.Hq + j;
-  merge_head_wave(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, tl.nI + tl.nLoc + tl.k,
+  merge_head_wave(A.part_o + hp * A.max_parts * kDim, A.part_ml + hp * A.max_parts * 2, A.max_parts,
+                  [&]() {
+                    const TileList tl = tiles_of(L, P, cnt);
+                    return tl.nI + tl.nLoc + tl.k;
+                  },
                   c * kMergeChWave, A.out + hp * kDim, wl);
 }
 
