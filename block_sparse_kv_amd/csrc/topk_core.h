@@ -297,7 +297,8 @@ __device__ __forceinline__ uint32_t topk_reg_take(const float (&v)[KPT], uint32_
   vl = wave_min_f32(vl);
   vh = wave_max_f32(vh);
   if (lane == 0) { S.fmin[wv] = vl; S.fmax[wv] = vh; }
-  for (int i = tid; i < kBins + 4; i += NT) S.hist[i] = 0;
+  static_assert((kBins + 4) % 4 == 0, "the histogram clears in 16-byte stores");
+  for (int i = tid; i < (kBins + 4) / 4; i += NT) reinterpret_cast<int4*>(S.hist)[i] = make_int4(0, 0, 0, 0);
   for (int i = tid; i < NT * KPT / 32; i += NT) S.bmap[i] = 0u;
   if (tid == 0) S.cur = 0;
   __syncthreads();
@@ -588,23 +589,34 @@ __device__ __forceinline__ void topk_group_reg(const float* row, int m, const in
 
 // Walks the taken keys as topk_reg_write does (ascending position, slots from `off` of the wave on):
 // the lane holding entry `slot` puts its id (idv) and physical id (ph) into slot_lds[0..1]; with
-// `writer`, sel[j] = the id of entry j for every j < k.
+// `writer`, sel[j] = the id of entry j for every j < k.  Without branches per column: each column's
+// ballot and the lane's count of lower taken lanes place its key, and one store hands the entry over.
 template <int KPT>
 __device__ __forceinline__ void topk_slot_walk(uint32_t take, int off, int k, const int32_t (&idv)[KPT],
                                                const int32_t (&ph)[KPT], int slot, int* slot_lds, bool writer,
                                                __attribute__((address_space(1))) int32_t* sel) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long lt = (1ull << lane) - 1ull;
+  bool hit = false;
+  int hid = 0, hph = 0;
+  int o = off;
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     const bool t = (take >> c) & 1u;
     const unsigned long long km = __ballot(t);
-    if (km != 0ull) {
-      const int j = off + __popcll(km & lt);
-      if (t && j < k) {
-        if (j == slot) { slot_lds[0] = idv[c]; slot_lds[1] = ph[c]; }
-        if (writer) sel[j] = idv[c];
-      }
+    const int j = o + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+    const bool h = t && j == slot;
+    hid = h ? idv[c] : hid;
+    hph = h ? ph[c] : hph;
+    hit = hit || h;
+    o += __popcll(km);
+  }
+  if (hit) { slot_lds[0] = hid; slot_lds[1] = hph; }
+  if (writer) {
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const bool t = (take >> c) & 1u;
+      const unsigned long long km = __ballot(t);
+      const int j = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+      if (t && j < k) sel[j] = idv[c];
       off += __popcll(km);
     }
   }
