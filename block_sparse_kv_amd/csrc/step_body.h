@@ -213,7 +213,7 @@ hipError_t launch_score_select_kv(const AttnArgs& A_in, const void* rep_pool, fl
 // group's selection itself (every workgroup of a group makes the same one) and gathers its entry; the
 // one of entry 0 (of KV head 0 for SHARED) also writes the group's selection and count.  Nothing
 // passes between the workgroups of the launch.
-//  * rows of up to kStepTopkSmall blocks: from the score row (topk_slot_reg);
+//  * SRC kSrcRow (rows of up to kStepTopkSmall blocks): from the score row (topk_slot_reg);
 //  * SRC kSrcSumm (SEPARATE rows up to kStepSummMax blocks): from the chunk summaries U of the scoring
 //    launch (topk_summary_slot, n_u chunks per row), or, when a chunk holds more than kChunkTop of
 //    the selection, from the whole score row (topk_select into LDS);
