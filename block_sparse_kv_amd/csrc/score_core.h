@@ -10,7 +10,11 @@
 // twice, not once per pass.  Reps are read
 // with 128-bit loads (a 16-lane row reads one 256 B fp16 rep row).  For the linear reps (Max, Mean,
 // Fix) the g query heads are summed first, since sum_j q_j.rep = (sum_j q_j).rep; Quest is per head
-// (the max is not linear).
+// (the max is not linear).  Quest's max(q_c*kmax_c, q_c*kmin_c) is q_c*kmax_c where q_c >= 0 and
+// q_c*kmin_c where q_c < 0 (kmin_c <= kmax_c), so each lane splits its fp16 query pairs once by sign
+// (the other half zeroed) and a block costs two 2-wide fp16 dot products with fp32 accumulation
+// (v_dot2_f32_f16) per channel pair and head: the fp16 products are exact in fp32, and each pair of
+// them is added to the sum with one rounding.
 #pragma once
 
 #include "kvs_device.h"
@@ -55,18 +59,27 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
   const Regions rg = regions_of(L, P.initial_len, P.local_len);
   constexpr int RMAX = METHOD == kQuest ? 2 : (METHOD == kMean ? 2 : 1);  // 16-byte loads per pass
 
-  float qf[G][8];
-  {
-    const uint16_t* qh = q_seq + (size_t)h * G * kDim + c * 8;
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const uint16_t* qh = q_seq + (size_t)h * G * kDim + c * 8;
+  uint32_t qpos[G][4], qneg[G][4];  // Quest: the g query heads' fp16 pairs split by sign
+  float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // linear reps: the g query heads summed
 #pragma unroll
-    for (int j = 0; j < G; ++j) unpack8(*reinterpret_cast<const uint4*>(qh + j * kDim), qf[j]);
-  }
-  float qs[8];
+  for (int j = 0; j < G; ++j) {
+    const uint4 w = *reinterpret_cast<const uint4*>(qh + j * kDim);
+    if constexpr (METHOD == kQuest) {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    qs[e] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t m = ((ws[i] >> 15) & 0x00010001u) * 0xFFFFu;  // the negative halves
+        qneg[j][i] = ws[i] & m;
+        qpos[j][i] = ws[i] & ~m;
+      }
+    } else {
+      float qf[8];
+      unpack8(w, qf);
 #pragma unroll
-    for (int j = 0; j < G; ++j) qs[e] += qf[j][e];
+      for (int e = 0; e < 8; ++e) qs[e] += qf[e];
+    }
   }
 
   // Loads that must be in flight together are issued without branches: indices are clamped to valid
@@ -116,13 +129,17 @@ __device__ __forceinline__ void score_blocks_range(const Params& P, const uint16
     for (int p = 0; p < kScorePasses; ++p) {
       acc[p] = 0.f;
       if constexpr (METHOD == kQuest) {
-        float kmin[8], kmax[8];
-        unpack8(raw[p][0], kmin);
-        unpack8(raw[p][1], kmax);
+        const uint32_t kmin[4] = {raw[p][0].x, raw[p][0].y, raw[p][0].z, raw[p][0].w};
+        const uint32_t kmax[4] = {raw[p][1].x, raw[p][1].y, raw[p][1].z, raw[p][1].w};
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[p] += fmaxf(qf[j][e] * kmax[e], qf[j][e] * kmin[e]);
+          for (int i = 0; i < 4; ++i) {
+            acc[p] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, qpos[j][i]),
+                                            __builtin_bit_cast(h2_t, kmax[i]), acc[p], false);
+            acc[p] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, qneg[j][i]),
+                                            __builtin_bit_cast(h2_t, kmin[i]), acc[p], false);
+          }
       } else {
         float rs[8];
         if constexpr (METHOD == kMean) {

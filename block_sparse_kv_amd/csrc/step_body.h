@@ -25,35 +25,32 @@ __device__ inline void write_chunk_summary(const float* lds, int b0, float* uval
                                            int32_t* uphys) {
   static_assert(kChunkBlocks == 64, "one block per lane");
   const int lane = threadIdx.x & 63;
-  float v = lds[lane];
+  const float v = lds[lane];
   const int phys = reinterpret_cast<const int*>(lds)[kChunkBlocks + lane];
-  float rv = -INFINITY;
-  int rb = 0x7FFFFFFF, rp = 0;  // entry r, held by lane r: score, block (invalid: last), physical id
+  // rank of this lane's block in the chunk by (score desc, block asc): the blocks that come before it
+  int rank = 0;
 #pragma unroll
-  for (int r = 0; r < kChunkTop; ++r) {
-    const float mx = wave_max_f32(v);
-    const unsigned long long hit = __ballot(v == mx);
-    const int w = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
-    const bool valid = mx != -INFINITY && hit != 0ull;
-    const int pw = __builtin_amdgcn_readlane(phys, w < 0 ? 0 : w);
-    if (lane == r) {
-      rv = valid ? mx : -INFINITY;
-      rb = valid ? b0 + w : 0x7FFFFFFF;
-      rp = valid ? pw : 0;
-    }
-    if (valid && lane == w) v = -INFINITY;
+  for (int j = 0; j < kChunkBlocks; j += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(lds + j);
+    rank += (q.x > v || (q.x == v && j < lane)) ? 1 : 0;
+    rank += (q.y > v || (q.y == v && j + 1 < lane)) ? 1 : 0;
+    rank += (q.z > v || (q.z == v && j + 2 < lane)) ? 1 : 0;
+    rank += (q.w > v || (q.w == v && j + 3 < lane)) ? 1 : 0;
   }
-  // position of entry r among the kChunkTop by block (invalid entries after the valid ones, by r)
-  int pos = 0;
-#pragma unroll
-  for (int j = 0; j < kChunkTop; ++j) {
-    const int bj = __builtin_amdgcn_readlane(rb, j);
-    pos += (bj < rb || (bj == rb && j < lane)) ? 1 : 0;
+  // the taken blocks (the first kChunkTop by rank that are candidates) in block order, then padding
+  const bool take = rank < kChunkTop && v > -INFINITY;
+  const unsigned long long tk = __ballot(take);
+  const int n_take = __popcll(tk);
+  const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(tk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tk, 0));
+  if (take) {
+    st_coh(uval + pos, v);
+    st_coh(uid + pos, b0 + lane);
+    st_coh(uphys + pos, phys);
   }
-  if (lane < kChunkTop) {
-    st_coh(uval + pos, rv);
-    st_coh(uid + pos, rb == 0x7FFFFFFF ? -1 : rb);
-    st_coh(uphys + pos, rp);
+  if (lane >= n_take && lane < kChunkTop) {
+    st_coh(uval + lane, -INFINITY);
+    st_coh(uid + lane, -1);
+    st_coh(uphys + lane, 0);
   }
 }
 

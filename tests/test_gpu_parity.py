@@ -250,6 +250,31 @@ def test_exact_ties_take_lower_index():
         assert sel[0, h].tolist() == [10, 11, 12, 13, 14], (h, sel[0, h].tolist())
 
 
+def test_exact_ties_long_row():
+    """A SEPARATE row of 2,200 blocks (selected through the 64-block chunks' summaries) with eleven
+    identical blocks 58..68 planted far above the rest: the tie group spans two chunks and k = 5 cuts
+    it, so exactly blocks 58..62 must be chosen, as the oracle does."""
+    c = cfg_of(32, 8, 128, 512, 5, "quest", "separate")
+    L = 2200 * B
+    say(f"[case] exact ties across a chunk boundary L={L} k=5")
+    s = kvsynth.make_sequence(12, L, 32, 8, 128, B, device=DEV)
+    u = kvsynth.query_directions(s.q, 8).to(DEV)
+    base = (s.K[58 * B:59 * B].float() + 6.0 * u[None]).half()
+    for b in range(58, 69):
+        s.K[b * B:(b + 1) * B] = base
+    r = orc.decode_step(s.q.cpu().numpy(), s.K.cpu().numpy(), s.V.cpu().numpy(), B=B,
+                        initial_len=128, local_len=512, topk=5, method="quest")
+    assert all(x == [58, 59, 60, 61, 62] for x in r["sel"]), r["sel"]
+    pb = kvsynth.page_batch([s], B, shuffle_seed=6, device=DEV)
+    rp = ops.alloc_rep_pool(c, pb.k_pool.shape[0], DEV)
+    ops.build_reps(c, pb.k_pool, pb.block_table[0, : L // B].cpu(), rp)
+    out, sel, cnt = ops.decode_step(c, pb.q, pb.k_pool, pb.v_pool, rp, pb.block_table, pb.seq_lens)
+    torch.cuda.synchronize()
+    for h in range(8):
+        assert int(cnt[0, h]) == 5 and sel[0, h].tolist() == [58, 59, 60, 61, 62], (h, sel[0, h].tolist())
+    say("[ok] exact ties across a chunk boundary")
+
+
 @pytest.mark.parametrize("mode", ["hot", "flat"])
 def test_long_row_chunk_overflow(mode):
     """A long SEPARATE row whose selection piles into one 64-block chunk (hot: 30 planted blocks inside
