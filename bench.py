@@ -657,20 +657,29 @@ def measure(name, steps, warmup, device, trials=7, reuse=True):
     if "kv" not in w:
         res["gather_reference"] = g = gather_reference(st, device)
         log(f"[bench] {name} plain gather of one layer's attended tiles (torch index_select of K and V, "
-            f"{g['tiles']} tiles each): {g['us']:.1f} us, {g['bytes_read'] / 1e6:.1f} MB read and as much "
-            f"written, {g['read_gbs']:.0f} GB/s read")
+            f"{g['tiles']} tiles each, cycling over {g['units']} cache units): {g['us']:.1f} us, "
+            f"{g['bytes_read'] / 1e6:.1f} MB read and as much written, {g['read_gbs']:.0f} GB/s read")
+        log(f"[bench] {name} read floor of the same tiles (kvs_gather_read_floor, reads and sums only): "
+            f"{g['floor_us']:.1f} us = {g['floor_read_gbs']:.0f} GB/s; with 36,864 B of LDS per "
+            f"workgroup as the attention tiles: {g['floor_tile_lds_us']:.1f} us = "
+            f"{g['floor_tile_lds_read_gbs']:.0f} GB/s")
     return res
 
 
-def gather_reference(st, device, replays=50):
-    """A library gather of the tiles one layer's decode step attends (unit 0: its Initial/Local tiles
+def gather_reference(st, device, replays=20):
+    """A library gather of the tiles one layer's decode step attends (unit 0's Initial/Local tiles
     and the selection kept by prepare_reuse), K and V, by torch.index_select into fresh buffers:
     what a plain copy of the same scattered 32 KiB tiles costs on this part, for comparison with the
-    attention launch that reads them.  Graph-replayed; the median replay."""
+    attention launch that reads them.  Then the read floor of the same tiles: the library's
+    read-only kernel (kvs_gather_read_floor), with no LDS reserved and with an attention tile's.
+    Each is captured once per cache unit (the same tile ids in every unit's pools, as the timed
+    steps cycle over the units, so the reads are not served from a cache), graph-replayed; the
+    median replay over the number of units."""
     import torch
+    from block_sparse_kv_amd import binding
 
     w = st.w
-    Hkv, nb = w["Hkv"], st.nb
+    Hkv = w["Hkv"]
     ie, ls, _ = regions(w["L"], w["I"], w["W"])
     il = list(range(ie // B)) + list(range(ls // B, (w["L"] + B - 1) // B))
     sel, cnt = st.reuse[0]
@@ -681,30 +690,46 @@ def gather_reference(st, device, replays=50):
         blocks = il + [int(b) for b in sel[0, gi, : int(cnt[0, gi])]]
         idx += [int(table[0, b]) * Hkv + h for b in blocks]  # (physical block, KV head) tile
     ix = torch.tensor(idx, dtype=torch.long, device=device)
-    _, kp, vp, _ = st.units[0]
-    kf, vf = kp.view(-1, B * D), vp.view(-1, B * D)
-    ko = torch.empty((len(idx), B * D), dtype=kf.dtype, device=device)
+    ix32 = ix.to(torch.int32)
+    pools = [(kp, vp) for _, kp, vp, _ in st.units]
+    ko = torch.empty((len(idx), B * D), dtype=pools[0][0].dtype, device=device)
     vo = torch.empty_like(ko)
+    sums = torch.empty(len(idx), dtype=torch.float32, device=device)
 
-    def run(_):
-        torch.index_select(kf, 0, ix, out=ko)
-        torch.index_select(vf, 0, ix, out=vo)
+    def copy(u):
+        kp, vp = pools[u]
+        torch.index_select(kp.view(-1, B * D), 0, ix, out=ko)
+        torch.index_select(vp.view(-1, B * D), 0, ix, out=vo)
 
-    for _ in range(3):
-        run(0)
-    torch.cuda.synchronize()
-    g = _capture(run, range(1))
-    times = []
-    for _ in range(replays):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
+    def floor(lds):
+        def run(u):
+            kp, vp = pools[u]
+            binding.kvs_gather_read_floor(kp, vp, ix32, len(idx), lds, sums)
+        return run
+
+    def timed(fn):
+        for u in range(len(pools)):
+            fn(u)
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e-3)
-    t = sorted(times)[len(times) // 2]
+        g = _capture(fn, range(len(pools)))
+        times = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3 / len(pools))
+        return sorted(times)[len(times) // 2]
+
     nbytes = 2 * len(idx) * B * D * 2
-    return dict(tiles=len(idx), us=t * 1e6, bytes_read=nbytes, read_gbs=nbytes / t / 1e9)
+    t = timed(copy)
+    res = dict(tiles=len(idx), units=len(pools), us=t * 1e6, bytes_read=nbytes, read_gbs=nbytes / t / 1e9)
+    for lds, key in ((0, "floor"), (36864, "floor_tile_lds")):
+        tf = timed(floor(lds))
+        res[key + "_us"] = tf * 1e6
+        res[key + "_read_gbs"] = nbytes / tf / 1e9
+    return res
 
 
 # ------------------------------------------------------------------------------------------------

@@ -47,7 +47,7 @@ EXPORTS = (
     "kvs_preselect_blocks", "kvs_decode_step_preselected_workspace_size", "kvs_decode_step_preselected",
     "kvs_score_blocks", "kvs_topk_blocks", "kvs_attn_workspace_size", "kvs_sparse_decode_attn",
     "kvs_decode_step_workspace_size", "kvs_decode_step", "kvs_validate_contents",
-    "kvs_decode_step_noalloc",
+    "kvs_decode_step_noalloc", "kvs_gather_read_floor",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20  # KVS_NOALLOC_SCRATCH_BYTES
 
@@ -139,6 +139,8 @@ _lib.kvs_decode_step.restype = ctypes.c_int
 _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P]
 _lib.kvs_decode_step_noalloc.restype = ctypes.c_int
 _lib.kvs_decode_step_noalloc.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P]
+_lib.kvs_gather_read_floor.restype = ctypes.c_int
+_lib.kvs_gather_read_floor.argtypes = [_P, _P, _P, _I, _I, _P, _P]
 _lib.kvs_validate_contents.restype = ctypes.c_int
 _lib.kvs_validate_contents.argtypes = [_CFG, _P, _I, _P, _I, _P, _P, _P, _I]
 
@@ -318,6 +320,12 @@ def kvs_decode_step_noalloc(cfg, q, k_pool, v_pool, rep_pool, block_table, max_b
     return _check(st, "kvs_decode_step_noalloc") if check else st
 
 
+def kvs_gather_read_floor(k_pool, v_pool, tile_ids, n_tiles, lds_bytes, out, stream=None, check=True):
+    st = _lib.kvs_gather_read_floor(_ptr(k_pool), _ptr(v_pool), _ptr(tile_ids), n_tiles, lds_bytes,
+                                    _ptr(out), _stream(stream))
+    return _check(st, "kvs_gather_read_floor") if check else st
+
+
 if TIMELINE:
     _lib.kvs_timeline_set.restype = None
     _lib.kvs_timeline_set.argtypes = [_P]
@@ -328,3 +336,4 @@ def kvs_timeline_set(records):
     if not TIMELINE:
         raise RuntimeError("kvs_timeline_set needs the timeline library (KVS_LIBRARY=timeline)")
     _lib.kvs_timeline_set(_ptr(records))
+

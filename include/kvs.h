@@ -395,6 +395,20 @@ int kvs_decode_step_noalloc(const kvs_config* cfg, const void* q, const void* k_
                             const int32_t* seq_lens, int32_t batch, float* out, int32_t* sel_out,
                             int32_t* sel_count_out, kvs_stream_t stream);
 
+/*
+ * kvs_gather_read_floor -- a measurement, not a step of the method: how long this device takes to
+ * read K/V tiles of the fp16 pools with nothing else done, for comparison with the attention
+ * launches that read the same tiles.  Workgroup x (256 lanes) reads the K tile and the V tile
+ * tile_ids[x] = phys_block * num_kv_heads + kv_head (128 tokens x 128 channels of fp16 each,
+ * contiguous in its pool), every 16-byte load of a lane issued before any is used, and writes the
+ * fp32 sum of the tile's 32,768 values to out[x].  lds_bytes (0 to 65,536) of LDS is reserved per
+ * workgroup and not used: it sets how many workgroups share a CU (an attention tile's workgroup
+ * reserves 36,864 bytes).  tile_ids: device, n_tiles entries, each naming a tile inside both pools
+ * (not checked); out: device, n_tiles floats.  n_tiles == 0 enqueues nothing.
+ */
+int kvs_gather_read_floor(const void* k_pool, const void* v_pool, const int32_t* tile_ids,
+                          int32_t n_tiles, int32_t lds_bytes, float* out, kvs_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

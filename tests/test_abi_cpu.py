@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(B.LIB_PATH)
     decl = declared_functions()
-    assert len(decl) == 22, decl
+    assert len(decl) == 23, decl
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -330,6 +330,18 @@ def test_noalloc_host_checks():
                                    ALIGNED, None, None, stream=0, check=False)
     assert st == B.KVS_ERR_WORKSPACE
     assert "static scratch" in kvs.kvs_last_error()
+
+
+def test_gather_read_floor_host_checks():
+    """kvs_gather_read_floor rejects bad sizes and pointers on the host; no tiles enqueue nothing."""
+    f = B.kvs_gather_read_floor
+    assert f(ALIGNED, ALIGNED, ALIGNED, -1, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, ALIGNED, 4, -1, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, ALIGNED, 4, 65537, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, None, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, None, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(MISALIGNED, ALIGNED, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert f(None, None, None, 0, 0, None, stream=0, check=False) == B.KVS_OK
 
 
 def test_timeline_variant_exports():
