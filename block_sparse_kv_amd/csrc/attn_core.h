@@ -31,10 +31,12 @@ __device__ inline f32x4_t ld_stream16f(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
 }
 
+constexpr int kNtLoad = 2;  // cache-policy operand of the K buffer loads: non-temporal, as ld_stream16
 constexpr int kVRow = 288;                      // bytes per staged V token row (256 + 32 bank skew)
 constexpr int kVChunk = 4 * kVRow;              // 4 token rows
 constexpr int kWaveVBytes = 8 * kVChunk;        // V staging per wave (32 tokens)
 constexpr int kAttnLdsBytes = 4 * kWaveVBytes;  // also >= the fold buffers for G <= 16
+static_assert(kBlock / 4 * kDim * 2 <= kWaveVBytes, "a wave's K rows fit its V staging area");
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 __device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
@@ -178,14 +180,42 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * m + 8 * lq);
       qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
     }
+    // K goes straight into the wave's LDS rows (buffer loads to LDS): load j brings the wave's token
+    // rows 4j .. 4j+3, 1 KiB contiguous in memory as in LDS, lane L's 16 bytes to LDS slot L % 16 of
+    // row 4j + L / 16.  Slot p of row r holds the row's 16-byte chunk p ^ (r % 16), so the A-operand
+    // reads below (16 rows, one chunk) fall on 16 different slots.  A load of 16 token rows x 64 B
+    // in the A-operand layout straight from memory streams about 10% slower than these.
+    {
+      unsigned char* kbuf = smem + w * kWaveVBytes;
+      const __amdgpu_buffer_rsrc_t kres =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kt), (short)0, kTile * 2, 0x00020000);
+      const int rb = (32 * w + (lane >> 4)) * (kDim * 2);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int tok = 32 * w + 16 * g + lc;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) kr[g][m] = ld_stream16(Kt + tok * kDim + 32 * m + 8 * lq);
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kres, (__attribute__((address_space(3))) void*)(kbuf + j * 1024), 16,
+            rb + 16 * ((lane & 15) ^ ((4 * j + (lane >> 4)) & 15)), j * 1024, 0, kNtLoad);
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
+    // The K rows are in LDS once every load of the wave but the 8 V loads issued after them has
+    // completed (vmcnt <= 8; 0x0F78 leaves expcnt and lgkmcnt at their maxima).  The compiler does
+    // not order LDS reads after loads to LDS by itself, and must not move a load across this wait.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    {
+      const unsigned char* kbuf = smem + w * kWaveVBytes;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          kr[g][m] = *reinterpret_cast<const uint4*>(kbuf + (16 * g + lc) * (kDim * 2) + 16 * ((4 * m + lq) ^ lc));
+    }
   } else if constexpr (KV == kKvQ4) {
     // Q4_0 record: as for Q8_0 below, a lane's K codes are the 32 channels 32*lq .. +32 of its
     // token (one block, one scale), here one 16-byte load, and MFMA m takes word m of them; V: lane l
