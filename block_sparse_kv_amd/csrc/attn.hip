@@ -35,7 +35,7 @@ __global__ __launch_bounds__(128) void merge_wave_kernel(AttnArgs A, int n_items
   if (item >= n_items) return;
   constexpr int C = kDim / kMergeChWave;
   const int c = item % C, j = (item / C) % A.P.Hq, seq = item / (C * A.P.Hq);
-  merge_item_wave(A, j, c, seq, wlds + (threadIdx.x >> 6) * (A.max_parts + 256));
+  merge_item_wave(A, j, c, seq, wlds + (threadIdx.x >> 6) * (A.max_parts + 256), KVS_TL_REC);
   KVS_TL_MARK(2)
 }
 

@@ -5,13 +5,14 @@
 // scaled by 1/sqrt(head_dim).
 //
 // Every attended (block, KV head) tile is one workgroup: its 64 KiB of K and V are requested at once,
-// and with 4 such workgroups per CU (128 registers, 33 KiB LDS each) a whole decode step's tiles are
-// in flight together, which is what an HBM-bound gather needs.  A tile covers all g <= 16 query heads
-// of its KV head, padded to the 16 rows of v_mfma_f32_16x16x32_f16.  Each of the 4 waves owns 32
-// token rows:
-//   S = K Q^T: K rows come straight from HBM in the A-operand layout (lane l: token l%16, channels
-//     8*(l/16)..+8 of a 32-channel chunk: each load is 16 tokens x 64 contiguous bytes); Q^T is a
-//     register-resident B operand.
+// and with 4 such workgroups per CU (at most 128 registers and 36 KiB of LDS each) a whole decode
+// step's tiles are in flight together, which is what an HBM-bound gather needs.  A tile covers all
+// g <= 16 query heads of its KV head, padded to the 16 rows of v_mfma_f32_16x16x32_f16.  Each of the
+// 4 waves owns 32 token rows:
+//   S = K Q^T: the A operand is lane l: token l%16, channels 8*(l/16)..+8 of a 32-channel chunk.
+//     fp16 K passes through LDS, loaded by whole token rows (4 rows, 1 KiB, per load) and read back in
+//     that layout; quantized K codes come straight from HBM in it.  Q^T is a register-resident B
+//     operand.
 //   softmax in the exp2 domain per head (the 4 lanes holding one head combine with two shuffles); P is
 //     rounded to fp16 and the row sums use the rounded values.
 //   O = P V: P is already in the A-operand layout (k-slot 8*(l/16)+e holds token 16*(e/4)+4*(l/16)+e%4).
@@ -618,7 +619,8 @@ constexpr int kMergeWaveMl = 3;
 // after them.
 template <typename NFn>
 __device__ inline void merge_head_wave(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                       int n_max, NFn n_of, int ch0, float* __restrict__ out, float* wl) {
+                                       int n_max, NFn n_of, int ch0, float* __restrict__ out, float* wl,
+                                       unsigned long long* tl_rec = nullptr) {
   const int lane = threadIdx.x & 63, cg = lane & 3, pg = lane >> 2;
   auto ld_ml = [&](int s) { return *reinterpret_cast<const float2*>(part_ml + (size_t)s * 2); };
   auto ld_o = [&](int s) { return *reinterpret_cast<const float4*>(part_o + (size_t)s * kDim + ch0 + 4 * cg); };
@@ -630,10 +632,18 @@ __device__ inline void merge_head_wave(const float* __restrict__ part_o, const f
 #pragma unroll
   for (int u = 0; u < kMergeWaveRows; ++u) o[u] = ld_o(min(pg + 16 * u, last));
   const int n = n_of();
+#ifdef KVS_TIMELINE
+  if (tl_rec) {  // the timeline build: the loads above have landed
+    wait_mem();
+    tl_rec[1] = __builtin_amdgcn_s_memrealtime();
+  }
+#endif
+  // The preloaded slots are folded without branches: a slot past n (its load clamped, its value
+  // anything, NaN included) is selected away, so the LDS reads below are issued together instead of
+  // one round trip per branch.
   float M = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < kMergeWaveMl; ++r)
-    if (lane + 64 * r < n) M = fmaxf(M, ml[r].x);
+  for (int r = 0; r < kMergeWaveMl; ++r) M = fmaxf(M, lane + 64 * r < n ? ml[r].x : -INFINITY);
   for (int s = lane + 64 * kMergeWaveMl; s < n; s += 64) M = fmaxf(M, ld_ml(s).x);
   M = wave_max_f32(M);
   float L = 0.f;
@@ -643,8 +653,13 @@ __device__ inline void merge_head_wave(const float* __restrict__ part_o, const f
     L += m.y * w;
   };
 #pragma unroll
-  for (int r = 0; r < kMergeWaveMl; ++r)
-    if (lane + 64 * r < n) weigh(lane + 64 * r, ml[r]);
+  for (int r = 0; r < kMergeWaveMl; ++r) {
+    const int s = lane + 64 * r;
+    const bool ok = s < n;
+    const float w = exp2_diff(ml[r].x, M);
+    if (ok) wl[s] = w;
+    L += ok ? ml[r].y * w : 0.f;
+  }
   for (int s = lane + 64 * kMergeWaveMl; s < n; s += 64) weigh(s, ld_ml(s));
   L = wave_sum_f32(L);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -654,9 +669,17 @@ __device__ inline void merge_head_wave(const float* __restrict__ part_o, const f
   auto fma4 = [&](const float4& v, float f) {
     acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
   };
+  float wu[kMergeWaveRows];  // slots past n read LDS inside the wave's area (it holds n_max + 256)
 #pragma unroll
-  for (int u = 0; u < kMergeWaveRows; ++u)
-    if (pg + 16 * u < n) fma4(o[u], wl[pg + 16 * u]);
+  for (int u = 0; u < kMergeWaveRows; ++u) wu[u] = wl[pg + 16 * u];
+#pragma unroll
+  for (int u = 0; u < kMergeWaveRows; ++u) {
+    const bool ok = pg + 16 * u < n;
+    acc.x += ok ? o[u].x * wu[u] : 0.f;
+    acc.y += ok ? o[u].y * wu[u] : 0.f;
+    acc.z += ok ? o[u].z * wu[u] : 0.f;
+    acc.w += ok ? o[u].w * wu[u] : 0.f;
+  }
   for (int s = pg + 16 * kMergeWaveRows; s < n; s += 64) {  // the rest, 4 loads in flight
     float4 v[4];
 #pragma unroll
@@ -671,10 +694,14 @@ __device__ inline void merge_head_wave(const float* __restrict__ part_o, const f
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < kMergeChWave) {
-    float a = 0.f;
+    float r[16];  // every read issued before the sums
 #pragma unroll
-    for (int g = 0; g < 16; ++g) a += red[g * kMergeChWave + lane];
-    out[ch0 + lane] = L > 0.f ? a / L : 0.f;
+    for (int g = 0; g < 16; ++g) r[g] = red[g * kMergeChWave + lane];
+#pragma unroll
+    for (int step = 1; step < 16; step *= 2)
+#pragma unroll
+      for (int g = 0; g < 16; g += 2 * step) r[g] += r[g + step];
+    out[ch0 + lane] = L > 0.f ? r[0] / L : 0.f;
   }
 }
 
@@ -740,7 +767,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& A, int x, int h, int s
 // The sequence's length and the group's selection count are loaded first, without branches (the
 // count through a buffer load that reads 0 when there is no selection), so that they travel with the
 // partials' loads.
-__device__ inline void merge_item_wave(const AttnArgs& A, int j, int c, int seq, float* wl) {
+__device__ inline void merge_item_wave(const AttnArgs& A, int j, int c, int seq, float* wl,
+                                       unsigned long long* tl_rec = nullptr) {
   const Params& P = A.P;
   const int L = A.seq_lens[seq];
   const __amdgpu_buffer_rsrc_t rc =
@@ -752,7 +780,7 @@ __device__ inline void merge_item_wave(const AttnArgs& A, int j, int c, int seq,
                     const TileList tl = tiles_of(L, P, cnt);
                     return tl.nI + tl.nLoc + tl.k;
                   },
-                  c * kMergeChWave, A.out + hp * kDim, wl);
+                  c * kMergeChWave, A.out + hp * kDim, wl, tl_rec);
 }
 
 // Merge of channel quarter q4 of query head j of sequence seq over its n_il + k partials into out.
