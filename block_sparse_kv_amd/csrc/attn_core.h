@@ -150,6 +150,36 @@ __device__ inline uint4 i4_dq8(uint32_t w, float s, int z) {
 }
 
 // KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0, or per-token INT8 or INT4 records).
+// The wave's 32 K code rows of 128 B (Q8_0, INT8: one byte per channel) into its LDS area, by buffer
+// loads to LDS: load j brings rows 8j .. 8j+7 (1 KiB, contiguous in memory as in LDS), lane L's 16
+// bytes to slot L % 8 of row 8j + L / 8.  Slot p of row r holds the row's chunk p ^ ((r / 2) % 8), so
+// 16 lanes reading one chunk of 16 consecutive rows fall on 16 different 16-byte bank groups.
+__device__ inline void k_rows128_to_lds(const unsigned char* kq, unsigned char* kbuf, int w, int lane) {
+  const __amdgpu_buffer_rsrc_t kres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kq), (short)0, kQ8Codes, 0x00020000);
+  const int rb = (32 * w + (lane >> 3)) * kDim;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)(kbuf + j * 1024), 16,
+                                             rb + 16 * ((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)), j * 1024, 0,
+                                             kNtLoad);
+}
+// Chunk c (16 bytes) of the wave's K code row r, as k_rows128_to_lds placed it.
+__device__ inline uint4 k_row128_chunk(const unsigned char* kbuf, int r, int c) {
+  return *reinterpret_cast<const uint4*>(kbuf + r * kDim + 16 * (c ^ ((r >> 1) & 7)));
+}
+// Wait until this wave's loads, but the `after` it issued last, have completed (vmcnt <= after, with
+// expcnt and lgkmcnt left at their maxima), keeping the compiler from moving memory accesses across.
+template <int after>
+__device__ inline void wait_loads_but() {
+  static_assert(after >= 0 && after < 16, "vmcnt's low field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | after);
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int G, int KV = kKvFp16>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
@@ -202,13 +232,8 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) vr[i] = ld_stream16(Vt + (32 * w + 4 * i + lq) * kDim + 8 * lc);
     // The K rows are in LDS once every load of the wave but the 8 V loads issued after them has
-    // completed (vmcnt <= 8; 0x0F78 leaves expcnt and lgkmcnt at their maxima).  The compiler does
-    // not order LDS reads after loads to LDS by itself, and must not move a load across this wait.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F78);
-    __builtin_amdgcn_sched_barrier(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // completed.  The compiler does not order LDS reads after loads to LDS by itself.
+    wait_loads_but<8>();
     {
       const unsigned char* kbuf = smem + w * kWaveVBytes;
 #pragma unroll
@@ -305,13 +330,11 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
       qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
     }
-    uint4 kc[2][2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int tok = 32 * w + 16 * g + lc;
-      kc[g][0] = ld_stream16(Kq + tok * kDim + 32 * lq);
-      kc[g][1] = ld_stream16(Kq + tok * kDim + 32 * lq + 16);
-    }
+    // K codes through LDS by whole rows (k_rows128_to_lds), then the V codes and the scales
+    unsigned char* kbuf = smem + w * kWaveVBytes;
+    k_rows128_to_lds(Kq, kbuf, w, lane);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = 32 * w + 4 * (lane >> 3) + i;
@@ -321,7 +344,13 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
 #pragma unroll
     for (int g = 0; g < 2; ++g) ksc[g] = *reinterpret_cast<const float*>(Kq + kQ8Codes + (32 * w + 16 * g + lc) * 4);
     vsc = ld_stream16f(Vq + kQ8Codes + (32 * w + 4 * (lane >> 3)) * 4);
-    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the arithmetic below
+    wait_loads_but<7>();  // the K rows have landed; 4 V code loads and 3 scale loads may not have
+    uint4 kc[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kc[g][0] = k_row128_chunk(kbuf, 16 * g + lc, 2 * lq);
+      kc[g][1] = k_row128_chunk(kbuf, 16 * g + lc, 2 * lq + 1);
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       kr[g][0] = i8_codes8(kc[g][0].x, kc[g][0].y);
@@ -342,15 +371,17 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       const uint4 v = *reinterpret_cast<const uint4*>(q_h + (size_t)(lc < G ? lc : 0) * kDim + 32 * lq + 8 * m);
       qb[m] = __builtin_bit_cast(half8_t, lc < G ? v : make_uint4(0, 0, 0, 0));
     }
-    uint4 kc[2][2];
+    // K codes through LDS by whole rows (k_rows128_to_lds); the lane's K scales before them
     uint32_t ks[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int tok = 32 * w + 16 * g + lc;
-      kc[g][0] = ld_stream16(Kq + tok * kDim + 32 * lq);
-      kc[g][1] = ld_stream16(Kq + tok * kDim + 32 * lq + 16);
-      ks[g] = *reinterpret_cast<const uint16_t*>(Kq + kQ8Codes + tok * 8 + 2 * lq);
-    }
+    for (int g = 0; g < 2; ++g)
+      ks[g] = *reinterpret_cast<const uint16_t*>(Kq + kQ8Codes + (32 * w + 16 * g + lc) * 8 + 2 * lq);
+    unsigned char* kbuf = smem + w * kWaveVBytes;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    k_rows128_to_lds(Kq, kbuf, w, lane);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
     // V: lane l takes channels 16*(l%8) .. +16 (half a Q8_0 block, one scale) of the wave's tokens
     // 8i + l/8, i < 4: 16-byte code loads, staged below as two 16-byte rows of fp16
 #pragma unroll
@@ -358,6 +389,13 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
       const int tok = 32 * w + 8 * i + (lane >> 3);
       vc[i] = ld_stream16(Vq + tok * kDim + 16 * (lane & 7));
       vs[i] = *reinterpret_cast<const uint16_t*>(Vq + kQ8Codes + tok * 8 + 2 * ((lane & 7) >> 1));
+    }
+    wait_loads_but<8>();  // the K rows have landed; the 8 V loads may not have
+    uint4 kc[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kc[g][0] = k_row128_chunk(kbuf, 16 * g + lc, 2 * lq);
+      kc[g][1] = k_row128_chunk(kbuf, 16 * g + lc, 2 * lq + 1);
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
