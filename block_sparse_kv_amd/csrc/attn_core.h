@@ -10,9 +10,9 @@
 // g <= 16 query heads of its KV head, padded to the 16 rows of v_mfma_f32_16x16x32_f16.  Each of the
 // 4 waves owns 32 token rows:
 //   S = K Q^T: the A operand is lane l: token l%16, channels 8*(l/16)..+8 of a 32-channel chunk.
-//     fp16 K passes through LDS, loaded by whole token rows (4 rows, 1 KiB, per load) and read back in
-//     that layout; quantized K codes come straight from HBM in it.  Q^T is a register-resident B
-//     operand.
+//     fp16 K, and the 128-B code rows of Q8_0 and INT8 K, pass through LDS, loaded by whole token
+//     rows (1 KiB per load) and read back in that layout; Q4_0 and INT4 K codes (64-B rows, so 16
+//     rows are 1 KiB anyway) come straight from HBM in it.  Q^T is a register-resident B operand.
 //   softmax in the exp2 domain per head (the 4 lanes holding one head combine with two shuffles); P is
 //     rounded to fp16 and the row sums use the rounded values.
 //   O = P V: P is already in the A-operand layout (k-slot 8*(l/16)+e holds token 16*(e/4)+4*(l/16)+e%4).
