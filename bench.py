@@ -704,7 +704,7 @@ def gather_reference(st, device, replays=20):
     def floor(lds):
         def run(u):
             kp, vp = pools[u]
-            binding.kvs_gather_read_floor(kp, vp, ix32, len(idx), lds, sums)
+            binding.kvs_gather_read_floor(kp, vp, kp.numel() // (B * D), ix32, len(idx), lds, sums)
         return run
 
     def timed(fn):

@@ -140,7 +140,7 @@ _lib.kvs_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _
 _lib.kvs_decode_step_noalloc.restype = ctypes.c_int
 _lib.kvs_decode_step_noalloc.argtypes = [_CFG, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P]
 _lib.kvs_gather_read_floor.restype = ctypes.c_int
-_lib.kvs_gather_read_floor.argtypes = [_P, _P, _P, _I, _I, _P, _P]
+_lib.kvs_gather_read_floor.argtypes = [_P, _P, _I, _P, _I, _I, _P, _P]
 _lib.kvs_validate_contents.restype = ctypes.c_int
 _lib.kvs_validate_contents.argtypes = [_CFG, _P, _I, _P, _I, _P, _P, _P, _I]
 
@@ -320,9 +320,10 @@ def kvs_decode_step_noalloc(cfg, q, k_pool, v_pool, rep_pool, block_table, max_b
     return _check(st, "kvs_decode_step_noalloc") if check else st
 
 
-def kvs_gather_read_floor(k_pool, v_pool, tile_ids, n_tiles, lds_bytes, out, stream=None, check=True):
-    st = _lib.kvs_gather_read_floor(_ptr(k_pool), _ptr(v_pool), _ptr(tile_ids), n_tiles, lds_bytes,
-                                    _ptr(out), _stream(stream))
+def kvs_gather_read_floor(k_pool, v_pool, pool_tiles, tile_ids, n_tiles, lds_bytes, out, stream=None,
+                          check=True):
+    st = _lib.kvs_gather_read_floor(_ptr(k_pool), _ptr(v_pool), pool_tiles, _ptr(tile_ids), n_tiles,
+                                    lds_bytes, _ptr(out), _stream(stream))
     return _check(st, "kvs_gather_read_floor") if check else st
 
 

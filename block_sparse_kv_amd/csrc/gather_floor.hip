@@ -9,15 +9,21 @@ namespace kvs {
 // Workgroup x reads tile ids[x] (phys * Hkv + h: kBlock * kDim fp16 values, contiguous in each pool)
 // of K and of V: lane t takes 16 bytes at t * 16 of every 4 KiB, all 16 loads issued before any is
 // used (as an attention tile's), and the workgroup writes the fp32 sum of the tile's values to out[x]
-// so that no load is dead.  The dynamic LDS is only reserved: it sets how many workgroups share a CU.
+// so that no load is dead.  An id outside [0, pool_tiles) reads nothing and writes NaN.  The dynamic
+// LDS is only reserved: it sets how many workgroups share a CU.
 __global__ __launch_bounds__(256) void gather_read_kernel(const uint16_t* __restrict__ k_pool,
                                                           const uint16_t* __restrict__ v_pool,
-                                                          const int32_t* __restrict__ ids,
+                                                          int pool_tiles, const int32_t* __restrict__ ids,
                                                           float* __restrict__ out) {
   __shared__ float part[4];
   constexpr int kTile = kBlock * kDim;       // fp16 values of one tile
   constexpr int kLoads = kTile / (256 * 8);  // 16-byte loads per lane and pool
-  const size_t base = (size_t)ids[blockIdx.x] * kTile + threadIdx.x * 8;
+  const int id = ids[blockIdx.x];
+  if (id < 0 || id >= pool_tiles) {
+    if (threadIdx.x == 0) out[blockIdx.x] = __builtin_nanf("");
+    return;
+  }
+  const size_t base = (size_t)id * kTile + threadIdx.x * 8;
   uint4 kr[kLoads], vr[kLoads];
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
@@ -39,11 +45,12 @@ __global__ __launch_bounds__(256) void gather_read_kernel(const uint16_t* __rest
   if (threadIdx.x == 0) out[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-hipError_t launch_gather_read(const void* k_pool, const void* v_pool, const int32_t* ids, int n,
-                              int lds_bytes, float* out, hipStream_t s) {
+hipError_t launch_gather_read(const void* k_pool, const void* v_pool, int pool_tiles, const int32_t* ids,
+                              int n, int lds_bytes, float* out, hipStream_t s) {
   if (n <= 0) return hipGetLastError();
   hipLaunchKernelGGL(gather_read_kernel, dim3(n), dim3(256), (size_t)lds_bytes, s,
-                     static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), ids, out);
+                     static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), pool_tiles,
+                     ids, out);
   return hipGetLastError();
 }
 

@@ -496,14 +496,15 @@ int kvs_sparse_decode_attn(const kvs_config* cfg, const void* q, const void* k_p
   return hip_status(kvs::launch_merge(a, batch, s), "kvs_sparse_decode_attn/merge");
 }
 
-int kvs_gather_read_floor(const void* k_pool, const void* v_pool, const int32_t* tile_ids,
-                          int32_t n_tiles, int32_t lds_bytes, float* out, kvs_stream_t stream) {
-  if (n_tiles < 0 || lds_bytes < 0 || lds_bytes > 65536) return KVS_ERR_INVALID_ARG;
+int kvs_gather_read_floor(const void* k_pool, const void* v_pool, int32_t pool_tiles,
+                          const int32_t* tile_ids, int32_t n_tiles, int32_t lds_bytes, float* out,
+                          kvs_stream_t stream) {
+  if (n_tiles < 0 || pool_tiles < 0 || lds_bytes < 0 || lds_bytes > 65536) return KVS_ERR_INVALID_ARG;
   if (n_tiles == 0) return KVS_OK;
   if (!k_pool || !v_pool || !tile_ids || !out) return KVS_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return KVS_ERR_MISALIGNED;
   clear_stale_error();
-  return hip_status(kvs::launch_gather_read(k_pool, v_pool, tile_ids, n_tiles, lds_bytes, out,
+  return hip_status(kvs::launch_gather_read(k_pool, v_pool, pool_tiles, tile_ids, n_tiles, lds_bytes, out,
                                             static_cast<hipStream_t>(stream)),
                     "kvs_gather_read_floor");
 }

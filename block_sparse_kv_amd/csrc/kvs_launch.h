@@ -53,10 +53,10 @@ hipError_t launch_topk(const Params& P, const float* scores, const int32_t* seq_
 // selected ones; A.sel holds physical ids if sel_phys, logical ids otherwise.
 hipError_t launch_attn_tiles(const AttnArgs& A, int batch, bool il, bool sel_phys, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& A, int batch, hipStream_t s);
-// The read floor of the tile gather (measurement): n tiles phys * Hkv + h of the fp16 pools, each
-// summed into out[x]; lds_bytes of LDS reserved per workgroup.
-hipError_t launch_gather_read(const void* k_pool, const void* v_pool, const int32_t* ids, int n,
-                              int lds_bytes, float* out, hipStream_t s);
+// The read floor of the tile gather (measurement): n tiles phys * Hkv + h of the fp16 pools (ids
+// outside [0, pool_tiles) give NaN), each summed into out[x]; lds_bytes of LDS reserved per workgroup.
+hipError_t launch_gather_read(const void* k_pool, const void* v_pool, int pool_tiles, const int32_t* ids,
+                              int n, int lds_bytes, float* out, hipStream_t s);
 // Hand-off counters of the decode step: kStepCtrBytes of ints, one per (sequence, group) at index
 // (seq * G + group) * step_ctr_stride(batch * G), so that counters fall on separate 128-byte lines as
 // far as they fit (agent-scope atomics on one line are serialized where memory performs them).

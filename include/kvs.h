@@ -403,11 +403,13 @@ int kvs_decode_step_noalloc(const kvs_config* cfg, const void* q, const void* k_
  * contiguous in its pool), every 16-byte load of a lane issued before any is used, and writes the
  * fp32 sum of the tile's 32,768 values to out[x].  lds_bytes (0 to 65,536) of LDS is reserved per
  * workgroup and not used: it sets how many workgroups share a CU (an attention tile's workgroup
- * reserves 36,864 bytes).  tile_ids: device, n_tiles entries, each naming a tile inside both pools
- * (not checked); out: device, n_tiles floats.  n_tiles == 0 enqueues nothing.
+ * reserves 36,864 bytes).  pool_tiles: the tiles each pool holds (phys blocks x num_kv_heads);
+ * tile_ids: device, n_tiles entries; an entry outside [0, pool_tiles) reads nothing and gives
+ * out[x] = NaN.  out: device, n_tiles floats.  n_tiles == 0 enqueues nothing.
  */
-int kvs_gather_read_floor(const void* k_pool, const void* v_pool, const int32_t* tile_ids,
-                          int32_t n_tiles, int32_t lds_bytes, float* out, kvs_stream_t stream);
+int kvs_gather_read_floor(const void* k_pool, const void* v_pool, int32_t pool_tiles,
+                          const int32_t* tile_ids, int32_t n_tiles, int32_t lds_bytes, float* out,
+                          kvs_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -335,13 +335,14 @@ def test_noalloc_host_checks():
 def test_gather_read_floor_host_checks():
     """kvs_gather_read_floor rejects bad sizes and pointers on the host; no tiles enqueue nothing."""
     f = B.kvs_gather_read_floor
-    assert f(ALIGNED, ALIGNED, ALIGNED, -1, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
-    assert f(ALIGNED, ALIGNED, ALIGNED, 4, -1, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
-    assert f(ALIGNED, ALIGNED, ALIGNED, 4, 65537, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
-    assert f(ALIGNED, ALIGNED, None, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
-    assert f(ALIGNED, None, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
-    assert f(MISALIGNED, ALIGNED, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_MISALIGNED
-    assert f(None, None, None, 0, 0, None, stream=0, check=False) == B.KVS_OK
+    assert f(ALIGNED, ALIGNED, 8, ALIGNED, -1, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, -1, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, 8, ALIGNED, 4, -1, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, 8, ALIGNED, 4, 65537, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, ALIGNED, 8, None, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(ALIGNED, None, 8, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_INVALID_ARG
+    assert f(MISALIGNED, ALIGNED, 8, ALIGNED, 4, 0, ALIGNED, stream=0, check=False) == B.KVS_ERR_MISALIGNED
+    assert f(None, None, 0, None, 0, 0, None, stream=0, check=False) == B.KVS_OK
 
 
 def test_timeline_variant_exports():

@@ -37,16 +37,19 @@ def test_gather_read_floor_sums(lds):
     rng = np.random.default_rng(5)
     ids = rng.integers(0, n_phys * Hkv, size=37).astype(np.int32)
     ids[:3] = [0, n_phys * Hkv - 1, 0]  # first and last tile, and a repeat
+    ids[3:5] = [n_phys * Hkv, -1]       # outside the pools: nothing read, NaN
     tid = torch.from_numpy(ids).to(DEV)
     out = torch.full((len(ids),), float("nan"), dtype=torch.float32, device=DEV)
-    Bd.kvs_gather_read_floor(kp, vp, tid, len(ids), lds, out)
+    Bd.kvs_gather_read_floor(kp, vp, n_phys * Hkv, tid, len(ids), lds, out)
     torch.cuda.synchronize()
     kt = kp.view(-1, B * D).double().cpu().numpy()
     vt = vp.view(-1, B * D).double().cpu().numpy()
-    ref = kt[ids].sum(axis=1) + vt[ids].sum(axis=1)
-    mag = np.abs(kt[ids]).sum(axis=1) + np.abs(vt[ids]).sum(axis=1)
     got = out.double().cpu().numpy()
-    err = np.abs(got - ref)
+    assert np.isnan(got[3]) and np.isnan(got[4])
+    ok = np.r_[0:3, 5:len(ids)]
+    ref = kt[ids[ok]].sum(axis=1) + vt[ids[ok]].sum(axis=1)
+    mag = np.abs(kt[ids[ok]]).sum(axis=1) + np.abs(vt[ids[ok]]).sum(axis=1)
+    err = np.abs(got[ok] - ref)
     assert np.all(err <= 2e-5 * mag + 1e-3), (err.max(), mag.min())
-    assert Bd.kvs_gather_read_floor(kp, vp, tid, 0, lds, out, check=False) == Bd.KVS_OK
+    assert Bd.kvs_gather_read_floor(kp, vp, n_phys * Hkv, tid, 0, lds, out, check=False) == Bd.KVS_OK
     say(f"[ok] gather read floor: max err {err.max():.2e} over {len(ids)} tiles")
