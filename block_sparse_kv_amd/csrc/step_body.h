@@ -17,26 +17,37 @@ constexpr int kSummSlotOff = ((int)sizeof(TopkLds) + 15) / 16 * 16;
 constexpr int kSummSlotMax = (kStepLds - kSummSlotOff) / 8;
 static_assert(kSummSlotMax >= kSelByTilesMax, "every topk the in-tile selections take fits");
 
-// The chunk summary of one SEPARATE scoring workgroup (wave 0; chunk = its kChunkBlocks blocks, whose
-// scores are in lds[0..kChunkBlocks) and physical ids in lds[kChunkBlocks..) as ints): the kChunkTop
-// best by (score desc, block asc), written sorted by block, padded with (-inf, -1, 0), coherently to
-// u*[chunk * kChunkTop ..].  Block b0 + i is lane i.
+// The chunk summary of one SEPARATE scoring workgroup (called by all 256 lanes; chunk = its
+// kChunkBlocks blocks, whose scores are in lds[0..kChunkBlocks) and physical ids in lds[kChunkBlocks..)
+// as ints): the kChunkTop best by (score desc, block asc), written by wave 0 sorted by block, padded
+// with (-inf, -1, 0), coherently to u*[chunk * kChunkTop ..].  Block b0 + i is lane i of each wave;
+// each wave counts the blocks among its 16 of the chunk that come before lane i's (all four waves
+// share the comparisons, so that no one SIMD carries them), the counts meet in LDS after the
+// chunk's ids (lds[2 * kChunkBlocks ..], 4 x 64 ints), and wave 0 adds them.  Waves 1..3 return
+// after the barrier.
 __device__ inline void write_chunk_summary(const float* lds, int b0, float* uval, int32_t* uid,
                                            int32_t* uphys) {
   static_assert(kChunkBlocks == 64, "one block per lane");
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float v = lds[lane];
-  const int phys = reinterpret_cast<const int*>(lds)[kChunkBlocks + lane];
-  // rank of this lane's block in the chunk by (score desc, block asc): the blocks that come before it
-  int rank = 0;
+  int* prank = reinterpret_cast<int*>(const_cast<float*>(lds)) + 2 * kChunkBlocks;  // [wave][block]
+  {
+    int r = 0;
 #pragma unroll
-  for (int j = 0; j < kChunkBlocks; j += 4) {
-    const float4 q = *reinterpret_cast<const float4*>(lds + j);
-    rank += (q.x > v || (q.x == v && j < lane)) ? 1 : 0;
-    rank += (q.y > v || (q.y == v && j + 1 < lane)) ? 1 : 0;
-    rank += (q.z > v || (q.z == v && j + 2 < lane)) ? 1 : 0;
-    rank += (q.w > v || (q.w == v && j + 3 < lane)) ? 1 : 0;
+    for (int jj = 0; jj < 16; jj += 4) {
+      const int j = 16 * wv + jj;
+      const float4 q = *reinterpret_cast<const float4*>(lds + j);
+      r += (q.x > v || (q.x == v && j < lane)) ? 1 : 0;
+      r += (q.y > v || (q.y == v && j + 1 < lane)) ? 1 : 0;
+      r += (q.z > v || (q.z == v && j + 2 < lane)) ? 1 : 0;
+      r += (q.w > v || (q.w == v && j + 3 < lane)) ? 1 : 0;
+    }
+    prank[wv * 64 + lane] = r;
   }
+  __syncthreads();
+  if (wv != 0) return;
+  const int phys = reinterpret_cast<const int*>(lds)[kChunkBlocks + lane];
+  const int rank = (prank[lane] + prank[64 + lane]) + (prank[128 + lane] + prank[192 + lane]);
   // the taken blocks (the first kChunkTop by rank that are candidates) in block order, then padding
   const bool take = rank < kChunkTop && v > -INFINITY;
   const unsigned long long tk = __ballot(take);
@@ -100,9 +111,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const size_t urow = ((size_t)seq * P.G + grp) * n_sc * kChunkTop;  // this group's summaries
   if constexpr (SUMM) {
     __syncthreads();  // the chunk's scores are in LDS
-    if (threadIdx.x < 64)
-      write_chunk_summary(lchunk, c * sb, uval + urow + (size_t)c * kChunkTop,
-                          uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
+    write_chunk_summary(lchunk, c * sb, uval + urow + (size_t)c * kChunkTop,
+                        uid + urow + (size_t)c * kChunkTop, uphys + urow + (size_t)c * kChunkTop);
     KVS_TL_MARK(5)
     if (sel == nullptr) return;  // scores and summaries only: the selections come later
   }
