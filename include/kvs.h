@@ -15,11 +15,11 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns all memory; the library
- *     never allocates, frees or synchronises.  It holds no device state of its own; what carries
- *     over between calls is (a) the hand-off counters inside a kvs_decode_step workspace (see
- *     there: such a workspace belongs to kvs_decode_step alone) and (b) the per-thread text behind
- *     kvs_last_error.  Calls from several host threads are safe when they use distinct
- *     workspaces and outputs.
+ *     never allocates, frees or synchronises.  What carries over between calls is (a) the
+ *     hand-off counters inside a kvs_decode_step workspace (see there: such a workspace belongs to
+ *     kvs_decode_step alone), (b) the per-thread text behind kvs_last_error and (c) the static
+ *     device scratch area of kvs_decode_step_noalloc (one per GPU, see there).  Calls from several
+ *     host threads are safe when they use distinct workspaces and outputs.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *   - Every argument that can be checked on the host is checked before anything is enqueued; on
  *     error the call returns a negative status and enqueues nothing.  Contents of device buffers
