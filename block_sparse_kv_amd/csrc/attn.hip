@@ -14,8 +14,6 @@ namespace kvs {
 
 template <int G, bool IL, bool PHYS, int KV>
 __global__ __launch_bounds__(256) void attn_tiles_kernel(AttnArgs A) {
-  // kAttnLdsBytes for every g: 4 such workgroups per CU (5, with 32 KiB at g <= 8, measured slower
-  // for the batched workload's tiles)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kAttnLdsBytes];
   attn_item<G, IL, PHYS, KV>(A, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }

@@ -33,19 +33,11 @@ __device__ inline f32x4_t ld_stream16f(const void* p) {
 }
 
 constexpr int kNtLoad = 2;  // cache-policy operand of the K buffer loads: non-temporal, as ld_stream16
-constexpr int kVRow = 256;                      // bytes per staged V token row
-constexpr int kWaveVBytes = 32 * kVRow;         // V staging per wave (32 tokens)
+constexpr int kVRow = 288;                      // bytes per staged V token row (256 + 32 bank skew)
+constexpr int kVChunk = 4 * kVRow;              // 4 token rows
+constexpr int kWaveVBytes = 8 * kVChunk;        // V staging per wave (32 tokens)
+constexpr int kAttnLdsBytes = 4 * kWaveVBytes;  // also >= the fold buffers for G <= 16
 static_assert(kBlock / 4 * kDim * 2 <= kWaveVBytes, "a wave's K rows fit its V staging area");
-// Staged V rows are unpadded: the 16-byte chunk c of the wave's token row t sits in slot c ^ 2(t % 4),
-// so the transposed reads (16 lanes: 4 rows x 32 B) fall on 4 different 32-byte bank groups.
-__device__ inline int vslot(int t, int c16) { return t * kVRow + 16 * (c16 ^ (2 * (t & 3))); }
-// LDS of a tile workgroup: the 4 waves' V staging, or the fold of G heads' partials (max and sum of
-// 64 rows, then [4 waves][G][128] outputs), whichever is larger.
-template <int G>
-constexpr int attn_lds_bytes() {
-  return 4 * kWaveVBytes > (128 + 4 * G * kDim) * 4 ? 4 * kWaveVBytes : (128 + 4 * G * kDim) * 4;
-}
-constexpr int kAttnLdsBytes = attn_lds_bytes<16>();  // enough for any G
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 __device__ inline v4s_t lds_read_tr16(const unsigned char* p) {
@@ -449,22 +441,23 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
     }
   ps += shfl_xor_f(ps, 16);
   ps += shfl_xor_f(ps, 32);
-  // V to LDS: one kVRow row per token of the wave, chunks placed by vslot
+  // V to LDS: chunk i holds the wave's tokens 4i..4i+3, one kVRow row each
   unsigned char* vbuf = smem + w * kWaveVBytes;
   if constexpr (KV == kKvQ4) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int t = 16 * i + (lane >> 2);  // the wave's token
+      const int t = 16 * i + (lane >> 2);  // the wave's token: chunk t / 4, row t % 4
       const bool in = 32 * w + t < ntok;
+      unsigned char* row = vbuf + (t >> 2) * kVChunk + (t & 3) * kVRow + 64 * (lane & 3);
       const uint32_t cw[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<uint4*>(vbuf + vslot(t, 4 * (lane & 3) + u)) = in ? q4_dq8(cw[u], vs[i]) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(row + 16 * u) = in ? q4_dq8(cw[u], vs[i]) : make_uint4(0, 0, 0, 0);
     }
   } else if constexpr (KV == kKvQ8 || KV == kKvI8 || KV == kKvI4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // the wave's token
+      // the wave's token: chunk t / 4, row t % 4
       const int t = KV == kKvQ8 ? 8 * i + (lane >> 3) : 4 * (lane >> 3) + i;
       const bool in = 32 * w + t < ntok;
       uint4 a, b;
@@ -479,14 +472,15 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
         a = q8_dq8(vc[i].x, vc[i].y, vs[i]);
         b = q8_dq8(vc[i].z, vc[i].w, vs[i]);
       }
-      *reinterpret_cast<uint4*>(vbuf + vslot(t, 2 * (lane & 7))) = in ? a : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(vbuf + vslot(t, 2 * (lane & 7) + 1)) = in ? b : make_uint4(0, 0, 0, 0);
+      unsigned char* row = vbuf + (t >> 2) * kVChunk + (t & 3) * kVRow + 32 * (lane & 7);
+      *reinterpret_cast<uint4*>(row) = in ? a : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(row + 16) = in ? b : make_uint4(0, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool in = 32 * w + 4 * i + lq < ntok;
-      *reinterpret_cast<uint4*>(vbuf + vslot(4 * i + lq, lc)) = in ? vr[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(vbuf + i * kVChunk + lq * kVRow + lc * 16) = in ? vr[i] : make_uint4(0, 0, 0, 0);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -495,14 +489,11 @@ __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __res
   f32x4_t O[8];
   // B operand of k-slots 8*lq + e: V[token 4*lq + e][16nn + lc] from chunk lq (e < 4) and
   // V[token 16 + 4*lq + e - 4][16nn + lc] from chunk 4 + lq (e >= 4)
-  // lane (lq, lc) points at token 4lq + lc/4 (and 16 more), bytes 32nn + 8(lc%4) .. +7: chunk
-  // 2nn + (lc%4)/2, in slot 2(nn ^ rho) + (lc%4)/2 with rho = lc/4 = the token's row in its 4
-  const int rho = lc >> 2;
-  const unsigned char* vsrc = vbuf + (4 * lq + rho) * kVRow + 8 * (lc & 3);
+  const unsigned char* vsrc = vbuf + lq * kVChunk + (lc >> 2) * kVRow + (lc & 3) * 8;
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) {
-    const v4s_t lo = lds_read_tr16(vsrc + 32 * (nn ^ rho));
-    const v4s_t hi = lds_read_tr16(vsrc + 16 * kVRow + 32 * (nn ^ rho));
+    const v4s_t lo = lds_read_tr16(vsrc + nn * 32);
+    const v4s_t hi = lds_read_tr16(vsrc + 4 * kVChunk + nn * 32);
     const half8_t vb = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     O[nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }

@@ -16,16 +16,6 @@ constexpr int kStepLds = kAttnLdsBytes > (int)sizeof(TopkLds) ? kAttnLdsBytes : 
 constexpr int kSummSlotOff = ((int)sizeof(TopkLds) + 15) / 16 * 16;
 constexpr int kSummSlotMax = (kStepLds - kSummSlotOff) / 8;
 static_assert(kSummSlotMax >= kSelByTilesMax, "every topk the in-tile selections take fits");
-// LDS of an attn_select_kernel workgroup: its tile's (attn_lds_bytes), or the selection's -- TopkLds,
-// a whole-row selection of up to kSelByTilesMax entries at kSummSlotOff, and the two ints through
-// which the owner lane hands its entry over, at the end -- whichever is larger.  For G <= 8 that is
-// 32 KiB, so that 5 such workgroups share a CU.
-template <int G>
-constexpr int select_lds_bytes() {
-  return attn_lds_bytes<G>() > kSummSlotOff + 8 * kSelByTilesMax + 16 ? attn_lds_bytes<G>()
-                                                                       : kSummSlotOff + 8 * kSelByTilesMax + 16;
-}
-static_assert(select_lds_bytes<8>() == 32768, "5 tile workgroups per CU for g <= 8");
 
 // The chunk summary of one SEPARATE scoring workgroup (called by all 256 lanes; chunk = its
 // kChunkBlocks blocks, whose scores are in lds[0..kChunkBlocks) and physical ids in lds[kChunkBlocks..)
@@ -242,8 +232,8 @@ template <int G, int KV, int KPT, int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attn_select_kernel(
     AttnArgs A, const float* __restrict__ scores, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
     int n_sel, int il0, Summaries U, int n_u) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[select_lds_bytes<G>()];
-  int* const s_slot = reinterpret_cast<int*>(smem + select_lds_bytes<G>() - 8);  // outside S and the row
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStepLds];
+  __shared__ int s_slot[2];
   const Params& P = A.P;
   const int x = blockIdx.x;
   if (x >= n_sel) {
