@@ -149,7 +149,6 @@ __device__ inline uint4 i4_dq8(uint32_t w, float s, int z) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0, or per-token INT8 or INT4 records).
 // The wave's 32 K code rows of 128 B (Q8_0, INT8: one byte per channel) into its LDS area, by buffer
 // loads to LDS: load j brings rows 8j .. 8j+7 (1 KiB, contiguous in memory as in LDS), lane L's 16
 // bytes to slot L % 8 of row 8j + L / 8.  Slot p of row r holds the row's chunk p ^ ((r / 2) % 8), so
@@ -180,6 +179,7 @@ __device__ inline void wait_loads_but() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// KV: the pools' KvType (fp16 tiles, Q8_0, Q4_0, or per-token INT8 or INT4 records).
 template <int G, int KV = kKvFp16>
 __device__ __forceinline__ void attn_tile(const Params& P, const uint16_t* __restrict__ q_h,
                                           const uint16_t* __restrict__ k_pool,
